@@ -1,0 +1,50 @@
+"""P10: the 16-bytes-per-parameter state layout and the workload sizes.
+
+The LLMScale fine-tuning VRAM page fixes mixed-precision Adam at 16 bytes per
+trained parameter (bf16 weight 2 + bf16 gradient 2 + fp32 master, m, v 12)
+and prints worked totals; tests/golden/accounting.json holds them.
+"""
+import json
+import os
+
+import pytest
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "accounting.json")
+
+
+def test_page_examples():
+    g = json.load(open(GOLDEN))
+    parts = g["bytes_per_trained_param"]
+    assert parts["total"] == sum(v for k, v in parts.items() if k != "total") == 16
+    f = g["formula_bytes_per_param"]
+    assert f["grads"] + f["adam"] + f["base_bf16"] == parts["total"]
+    for ex in g["examples"]:
+        gib = ex["params"] * ex["bytes_per_param"] / 2 ** 30
+        assert abs(gib - ex["gib"]) <= ex["tol_gib"], ex
+
+
+def test_state_layout_is_16_bytes():
+    # arrays the AdamW path keeps per trained parameter (dtype sizes)
+    layout = {"weight_bf16": 2, "grad_bf16": 2, "master_f32": 4, "m_f32": 4, "v_f32": 4}
+    assert sum(layout.values()) == json.load(open(GOLDEN))["bytes_per_trained_param"]["total"]
+
+
+@pytest.mark.parametrize("name,params,nseg", [
+    ("gpt2_cattn_first2", 3_543_552, 4),
+    ("llama7b_attn_last4", 268_435_456, 16),
+    ("llama7b_layer", 202_383_360, 9),
+    ("llama7b_full", 6_738_415_616, 291),
+])
+def test_workload_sizes(name, params, nseg):
+    w = synth.WORKLOADS[name]
+    assert w.params == params and len(w.segments) == nseg
+
+
+def test_resident_and_slot_footprints():
+    full = synth.WORKLOADS["llama7b_full"].params * 16
+    assert abs(full / 1e9 - 107.81) < 0.01                 # about 108 GB resident
+    slot = synth.WORKLOADS["llama7b_layer"].params * 16
+    assert abs(slot / 1e9 - 3.238) < 0.001                 # one layer slot
+    assert full < 288e9 / 1.3                              # room for orig + delta on one GPU
