@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixed-precision AdamW hot path on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-delta]
+
+A step is one call of lema_adamw_step over the whole workload (constants,
+segment walk, AdamW, bf16 write-back and, by default, the fp32 delta) on
+inputs already resident in HBM.  The default workload is the Llama-2-7B
+q, k, v, o projections of the last 4 decoder layers (16 x [4096 x 4096],
+268,435,456 parameters, bf16 gradient, t = 100), the selection the LEMA
+README's "Selective Full Fine-Tuning" section uses as its example.
+
+Prints one JSON line: parameters updated per second (value), HBM GB/s and
+fraction of the 8 TB/s peak, the roofline of the AdamW kernel (kernel time
+from HIP events on its stream), the plain-copy ceiling of the same GPU, and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
+METRIC = "AdamW params updated/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
+COUNTERS = os.path.join(ROOT, "profiles", "adamw_counters.json")
+KERNEL_SOURCES = ["optimizer_step_lema_amd/csrc/lema_kernels.hip",
+                  "optimizer_step_lema_amd/csrc/lema_internal.h",
+                  "optimizer_step_lema_amd/build.py"]
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def bytes_per_param(grad_f32: bool, delta: bool) -> int:
+    # reads: grad, master, m, v (+ orig); writes: master, m, v, weight (+ delta)
+    read = (4 if grad_f32 else 2) + 12 + (2 if delta else 0)
+    write = 12 + 2 + (4 if delta else 0)
+    return read + write
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="llama7b_attn_last4")
+    ap.add_argument("--no-delta", action="store_true", help="time the step without the delta")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-gib", type=float, default=4.0, help="size of the copy-ceiling test")
+    return ap.parse_args()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: --gpus {a.gpus}: this build runs on one GPU only; the multi-GPU "
+              "(sharded) layout is described but not built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import optimizer_step_lema_amd as L
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(2)
+    dev = "cuda"
+    w = synth.WORKLOADS[a.workload]
+    delta = not a.no_delta
+    hp = synth.HPARAMS
+    P = w.params
+
+    # ---- state resident in HBM; small workloads get rotated copies so the
+    # working set exceeds the 256 MB last-level cache between launches
+    bpp = bytes_per_param(False, delta)
+    per_call = P * bpp
+    nsets = max(1, -(-(1 << 30) // per_call)) if per_call < (1 << 30) else 1
+    sets = []
+    for r in range(nsets):
+        segs = []
+        for i in range(len(w.segments)):
+            st = synth.make_segment_state(w, i, dev, with_orig=delta, grads=1)
+            n = w.numels[i]
+            segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], st["grads"][0],
+                                       torch.empty(n, dtype=torch.bfloat16, device=dev),
+                                       st.get("orig"),
+                                       torch.empty(n, device=dev) if delta else None))
+        sets.append(segs)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    # ---- the copy ceiling (read N + write N bytes)
+    nbytes = int(a.copy_gib * (1 << 30)) // 2 // 4096 * 4096
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    for _ in range(3):
+        L.measure_copy(src, dst, nbytes)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        L.measure_copy(src, dst, nbytes)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = e0.elapsed_time(e1) / reps
+    copy_gbps = 2 * nbytes / (copy_ms * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+
+    # ---- the AdamW step
+    for k in range(a.warmup):
+        L.adamw_step(sets[k % nsets], step=w.step, **hp)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(a.steps):
+        L.adamw_step(sets[k % nsets], step=w.step, **hp)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    ms = start.elapsed_time(stop) / a.steps
+    params_per_s = P / (ms * 1e-3)
+    gbps = per_call / (ms * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(COUNTERS):
+        rec = json.load(open(COUNTERS))
+        entry = rec.get("workloads", {}).get(f"{a.workload}:{'delta' if delta else 'nodelta'}")
+        if entry and rec.get("kernel_digest") == kernel_digest():
+            traffic = entry["traffic_bytes_per_launch"]
+
+    info = L.device_info()
+    line = {
+        "metric": METRIC,
+        "value": params_per_s,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": a.workload,
+            "description": w.description,
+            "params": P,
+            "segments": len(w.segments),
+            "grad": "bf16",
+            "delta": delta,
+            "step_t": w.step,
+            "bytes_per_param": bpp,
+            "bytes_per_call": per_call,
+            "rotated_state_sets": nsets,
+        },
+        "hbm_gbps": gbps,
+        "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "copy_ceiling_gbps": copy_gbps,
+        "pct_copy_ceiling": 100.0 * gbps / copy_gbps,
+        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": "adamw_mta_kernel", "algorithmic_bytes_per_launch": per_call,
+                     "avg_launch_ms": ms},
+        "device": {"compute_units": info["compute_units"],
+                   "blocks_per_cu": info["blocks_per_cu"]},
+        "host_wall_s_timed_region": wall,
+    }
+
+    # ---- the CPU oracle on a bounded sample of the same workload
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(sets[0], w, hp, delta, a.cpu_seconds)
+
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(segs, w, hp, delta, seconds):
+    """Time the oracle (as it stands) on the first tensor of the workload."""
+    import oracle
+    import torch
+
+    def host_copy(t):
+        t = t.detach().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view("uint16").copy()
+        return t.numpy().copy()
+
+    s = segs[0]
+    master, m, v = host_copy(s.master), host_copy(s.exp_avg), host_copy(s.exp_avg_sq)
+    grad = host_copy(s.grad)
+    orig = host_copy(s.orig) if delta else None
+    n = master.shape[0]
+    c = oracle.adamw_constants(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                               hp["weight_decay"], w.step)
+    oracle.adamw_step(master, m, v, grad, c, orig=orig)        # warm-up pass
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.adamw_step(master, m, v, grad, c, orig=orig)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n * reps / el, "unit": "params/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{w.segments[0][0]} ({n} params), {reps} oracle steps in {el:.1f} s, "
+                      f"delta {'on' if delta else 'off'}; C oracle, OpenMP"}
+
+
+if __name__ == "__main__":
+    main()

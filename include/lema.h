@@ -1,0 +1,230 @@
+/*
+ * lema.h -- C ABI of liblema.so: the per-layer mixed-precision AdamW update
+ * of streamed fine-tuning on one AMD Instinct MI355X (gfx950).
+ *
+ * Source of the method (the pages this library implements):
+ *   LEMA README ("LEMA: Layer-wise Efficient Memory Abstraction"),
+ *     "Quick Start": trainable parameters go to torch.optim.AdamW with
+ *       lr = 1e-4 (all other settings at AdamW's defaults);
+ *     "Selective Full Fine-Tuning": the optimizer is a per-layer AdamW whose
+ *       states and gradient accumulators are fp32 and live in host RAM; a
+ *       checkpoint stores an fp32 delta (updated minus original weight);
+ *     "TensorStore: Unified Streaming Core": optimizer states stream through
+ *       a slot-pool address space between RAM and VRAM;
+ *   LLMScale fine-tuning VRAM page, memory note and FAQ: mixed-precision
+ *     Adam holds 16 bytes per trained parameter (bf16 weight, bf16 gradient,
+ *     fp32 master weight, fp32 m, fp32 v).
+ *
+ * Arithmetic (the pages print no formula; this is the fixed reading).  All
+ * operations are IEEE binary32, rounded to nearest even, no fused
+ * multiply-add, correctly rounded sqrt and division, subnormals kept:
+ *   g     = grad (bf16 widened exactly, or the fp32 accumulator)
+ *   w1    = w * decay                     decay     = fp32(1 - lr*wd)
+ *   m'    = b1*m + omb1*g                 b1, omb1  = fp32(beta1), fp32(1-beta1)
+ *   v'    = b2*v + omb2*(g*g)             b2, omb2  = fp32(beta2), fp32(1-beta2)
+ *   d     = sqrt(v')*ibc2 + eps           ibc2      = fp32(1/sqrt(1-beta2^t))
+ *   w'    = w1 - step*(m'/d)              step      = fp32(lr/(1-beta1^t))
+ *   weight_bf16 = round-to-nearest-even bf16 of w'
+ *   delta = w' - f32(orig)                (only when requested)
+ * The constants are computed in double (beta^t by square-and-multiply, low
+ * bit first) and rounded to fp32 once.
+ *
+ * Conventions for every call:
+ *   - Arrays are 1-D, contiguous, little-endian; bf16 values are passed as
+ *     their uint16 bit patterns.  Device pointers must be device memory (or
+ *     memory the GPU can address) of the current HIP device.
+ *   - fp32 pointers must be 4-byte aligned and bf16 pointers 2-byte aligned
+ *     (else LEMA_ERR_ALIGN).  Any further alignment is optional; 16-byte
+ *     aligned fp32 arrays and 8-byte aligned bf16 arrays take the vector path.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Compute calls are
+ *     asynchronous on it; the caller keeps the arrays alive until it is done.
+ *   - Every argument is validated before any HIP call: on any error nothing
+ *     is enqueued and nothing is modified.  HIP failures return LEMA_ERR_HIP
+ *     and lema_last_hip_error() gives the raw hipError_t of this thread.
+ *   - Nothing aborts, throws or prints across this ABI.
+ *   - The caller owns all tensors, streams and the step counter t; the
+ *     library is stateless apart from caches of small launch tables.
+ */
+#ifndef LEMA_H
+#define LEMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ------------------------------------------------------------- statuses */
+
+typedef int32_t lema_status;
+
+#define LEMA_OK              0
+#define LEMA_ERR_NULL       (-1)  /* a required pointer is NULL, or orig/delta unpaired */
+#define LEMA_ERR_SIZE       (-2)  /* negative count/numel, or a size beyond a limit    */
+#define LEMA_ERR_HPARAM     (-3)  /* hyperparameter or step out of range               */
+#define LEMA_ERR_DTYPE      (-4)  /* unknown gradient dtype                            */
+#define LEMA_ERR_OVERLAP    (-5)  /* two arrays overlap where one of them is written   */
+#define LEMA_ERR_NOT_PINNED (-6)  /* host memory is not page-locked                    */
+#define LEMA_ERR_HIP        (-7)  /* the HIP runtime reported an error                 */
+#define LEMA_ERR_ALIGN      (-8)  /* pointer not aligned to its element size           */
+
+/* Static string naming a status (never NULL). */
+const char *lema_status_string(lema_status s);
+
+/* hipError_t of the last LEMA_ERR_HIP returned on the calling thread, else 0. */
+int32_t lema_last_hip_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t lema_version(void);
+
+/* --------------------------------------------------------------- AdamW */
+
+typedef enum {
+    LEMA_GRAD_BF16 = 0,  /* grad is bf16 bit patterns (one micro-batch)   */
+    LEMA_GRAD_FP32 = 1   /* grad is an fp32 accumulator (lema_grad_accum) */
+} lema_grad_dtype;
+
+/*
+ * One trainable tensor (one "addressable segment" of the LEMA README intro).
+ * Every array has `numel` elements.  master, exp_avg and exp_avg_sq are
+ * updated in place; no other two arrays of any segment in a call may
+ * overlap (LEMA_ERR_OVERLAP).
+ */
+typedef struct {
+    float          *master;      /* fp32 master weight, in/out (required)        */
+    float          *exp_avg;     /* m, fp32, in/out (required)                   */
+    float          *exp_avg_sq;  /* v, fp32, in/out (required)                   */
+    const void     *grad;        /* bf16 bits or fp32 accumulator, in (required) */
+    uint16_t       *weight_bf16; /* out: bf16 of the new master (required)       */
+    const uint16_t *orig_bf16;   /* in: base weight; non-NULL iff delta non-NULL */
+    float          *delta;       /* out: new master - f32(orig) (optional)       */
+    int64_t         numel;       /* >= 0; 0 makes the segment a no-op            */
+} lema_adamw_seg;
+
+/* Hyperparameters of one call (one parameter group). */
+typedef struct {
+    double  lr;            /* >= 0                                        */
+    double  beta1;         /* 0 <= beta1 < 1                              */
+    double  beta2;         /* 0 <= beta2 < 1                              */
+    double  eps;           /* > 0                                         */
+    double  weight_decay;  /* >= 0 (decoupled)                            */
+    int64_t step;          /* t >= 1: the number of the step being taken  */
+    int32_t grad_dtype;    /* lema_grad_dtype, one per call               */
+    int32_t reserved;      /* must be 0                                   */
+} lema_adamw_args;
+
+/* The fp32 constants one call uses (see the arithmetic above). */
+typedef struct {
+    float beta1, one_minus_beta1, beta2, one_minus_beta2;
+    float eps, decay, step_size, inv_bias_correction2_root;
+} lema_adamw_consts;
+
+/*
+ * Derive the fp32 constants for `args` (host only, no GPU needed).
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_HPARAM, LEMA_ERR_DTYPE.
+ */
+lema_status lema_adamw_constants(const lema_adamw_args *args, lema_adamw_consts *out);
+
+/*
+ * One AdamW step over `nseg` segments (LEMA README, "Quick Start" and
+ * "Selective Full Fine-Tuning": the per-layer AdamW over fp32 states; the
+ * LLMScale page's 16-byte layout; the checkpoint delta of "Selective Full
+ * Fine-Tuning").  Elementwise and asynchronous on `stream`.
+ *   segs : host array of nseg descriptors holding device pointers; it is
+ *          read during the call only.
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_HPARAM, LEMA_ERR_DTYPE,
+ *         LEMA_ERR_ALIGN, LEMA_ERR_OVERLAP, LEMA_ERR_HIP.
+ */
+lema_status lema_adamw_step(const lema_adamw_seg *segs, int32_t nseg,
+                            const lema_adamw_args *args, void *stream);
+
+/* ------------------------------------------------ gradient accumulation */
+
+/* One accumulator and the bf16 micro-batch gradient added into it. */
+typedef struct {
+    float          *acc;        /* fp32 accumulator, in/out (required) */
+    const uint16_t *grad_bf16;  /* bf16 bits, in (required)            */
+    int64_t         numel;      /* >= 0                                */
+} lema_accum_seg;
+
+/*
+ * fp32 gradient accumulation of one bf16 micro-batch (LEMA README,
+ * "Selective Full Fine-Tuning": gradient accumulation is fp32):
+ *   overwrite = 1 : acc = f32(g)        (first micro-batch; -0 kept)
+ *   overwrite = 0 : acc = acc + f32(g)  (later micro-batches, in order)
+ * A plain sum: any 1/K averaging belongs in the loss scale.  Asynchronous on
+ * `stream`.  Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_ALIGN,
+ * LEMA_ERR_OVERLAP, LEMA_ERR_HIP.
+ */
+lema_status lema_grad_accum(const lema_accum_seg *segs, int32_t nseg,
+                            int32_t overwrite, void *stream);
+
+/* --------------------------------------- slot-pool streaming (host RAM) */
+
+/*
+ * The TensorStore of the LEMA README ("TensorStore: Unified Streaming Core";
+ * "Selective Full Fine-Tuning": fp32 optimizer states live in RAM), reduced
+ * to two tiers: page-locked host RAM and a pool of HBM slots.  Each layer's
+ * master, m, v and bf16 gradient are copied host->HBM into a slot, the AdamW
+ * step runs there, and master, m, v and the bf16 weight are copied back to
+ * the layer's host arrays, with the copy of the next layer overlapping the
+ * step of the current one.
+ */
+typedef struct lema_slot_pool lema_slot_pool;
+
+/*
+ * Create a pool over a caller-owned device region of nslots * slot_bytes
+ * bytes (borrowed, not freed by the library).  copy_stream carries every
+ * host<->HBM copy, compute_stream every kernel; they must differ.  nslots
+ * must be >= 2.  The pool owns only HIP events and small table buffers.
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_HIP.
+ */
+lema_status lema_slot_pool_create(void *device_base, size_t slot_bytes, int32_t nslots,
+                                  void *copy_stream, void *compute_stream,
+                                  lema_slot_pool **out);
+
+/* Destroy a pool (waits for its outstanding work).  NULL is a no-op. */
+lema_status lema_slot_pool_destroy(lema_slot_pool *pool);
+
+/*
+ * One layer of host-resident state.  In each host_segs entry the pointers
+ * are page-locked HOST pointers (lema_host_alloc): master, exp_avg,
+ * exp_avg_sq, grad (bf16 only) are read and master, exp_avg, exp_avg_sq,
+ * weight_bf16 are written back; orig_bf16 and delta must be NULL.
+ */
+typedef struct {
+    const lema_adamw_seg *host_segs;
+    int32_t               nseg;
+} lema_layer;
+
+typedef struct {
+    double h2d_bytes, d2h_bytes;  /* bytes copied in each direction         */
+    double h2d_ms, d2h_ms;        /* summed copy durations                  */
+    double kernel_ms;             /* summed AdamW kernel durations          */
+    double copy_busy_ms;          /* first copy start .. last copy end      */
+    double wall_ms;               /* call start .. last copy end            */
+    double last_kernel_ms;        /* duration of the last layer's kernel    */
+} lema_stream_stats;
+
+/*
+ * Stream `nlayers` layers through the pool with one AdamW step each (bf16
+ * gradients, args->grad_dtype must be LEMA_GRAD_BF16).  Layer i uses slot
+ * i mod nslots.  Blocks until the last copy back has completed.  `stats`
+ * may be NULL.  Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE (a layer does not fit a
+ * slot), LEMA_ERR_HPARAM, LEMA_ERR_DTYPE, LEMA_ERR_ALIGN,
+ * LEMA_ERR_NOT_PINNED, LEMA_ERR_HIP; errors found before the first copy
+ * enqueue nothing.
+ */
+lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int32_t nlayers,
+                             const lema_adamw_args *args, lema_stream_stats *stats);
+
+/* Page-locked host allocation of exactly `bytes` bytes (hipHostMalloc). */
+lema_status lema_host_alloc(void **out, size_t bytes);
+lema_status lema_host_free(void *p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LEMA_H */

@@ -1,0 +1,51 @@
+/*
+ * lema_measure.h -- measurement and self-check aids exported by liblema.so.
+ *
+ * These are not part of the optimizer method.  They exist so that the
+ * AdamW kernel's bandwidth can be put next to the practical ceiling of the
+ * same GPU and so that the arithmetic primitives the kernel is built from
+ * can be checked against IEEE results on the host.  Same conventions as
+ * lema.h: device pointers, `stream` is a hipStream_t, asynchronous, full
+ * validation before any HIP call.
+ */
+#ifndef LEMA_MEASURE_H
+#define LEMA_MEASURE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "lema.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * Plain device-to-device copy of `bytes` bytes with the AdamW kernel's
+ * access width (16 bytes per lane), on a persistent grid of
+ * `blocks_per_cu` x (compute units) workgroups (0 = the AdamW default).
+ * Reads `bytes` and writes `bytes`: the read+write bandwidth ceiling, and the
+ * known-size reference for HBM byte counters.  src and dst must be 16-byte
+ * aligned, bytes a multiple of 16, the ranges disjoint.
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_ALIGN, LEMA_ERR_OVERLAP,
+ * LEMA_ERR_HIP.
+ */
+lema_status lema_measure_copy(const void *src, void *dst, size_t bytes, int32_t blocks_per_cu,
+                              void *stream);
+
+/*
+ * Elementwise a/b, sqrt(a) and bf16 nearest-even of a over n elements,
+ * compiled exactly as inside the AdamW kernel (same file, same flags).
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_HIP.
+ */
+lema_status lema_probe_fp32(const float *a, const float *b, float *quot, float *root,
+                            uint16_t *bf16, int64_t n, void *stream);
+
+/* Compute units of the current device and the AdamW launch's workgroups per CU. */
+lema_status lema_device_info(int32_t *compute_units, int32_t *blocks_per_cu);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LEMA_MEASURE_H */

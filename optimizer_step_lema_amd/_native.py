@@ -1,0 +1,117 @@
+"""ctypes declarations of liblema.so (include/lema.h, include/lema_measure.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation of any step in Python.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblema.so")
+
+# Status codes (include/lema.h)
+LEMA_OK = 0
+LEMA_ERR_NULL = -1
+LEMA_ERR_SIZE = -2
+LEMA_ERR_HPARAM = -3
+LEMA_ERR_DTYPE = -4
+LEMA_ERR_OVERLAP = -5
+LEMA_ERR_NOT_PINNED = -6
+LEMA_ERR_HIP = -7
+LEMA_ERR_ALIGN = -8
+
+LEMA_GRAD_BF16 = 0
+LEMA_GRAD_FP32 = 1
+
+vp = ctypes.c_void_p
+i32 = ctypes.c_int32
+i64 = ctypes.c_int64
+
+
+class AdamwSeg(ctypes.Structure):
+    _fields_ = [("master", vp), ("exp_avg", vp), ("exp_avg_sq", vp), ("grad", vp),
+                ("weight_bf16", vp), ("orig_bf16", vp), ("delta", vp), ("numel", i64)]
+
+
+class AdamwArgs(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double), ("step", i64),
+                ("grad_dtype", i32), ("reserved", i32)]
+
+
+class AdamwConsts(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_float) for n in (
+        "beta1", "one_minus_beta1", "beta2", "one_minus_beta2",
+        "eps", "decay", "step_size", "inv_bias_correction2_root")]
+
+
+class AccumSeg(ctypes.Structure):
+    _fields_ = [("acc", vp), ("grad_bf16", vp), ("numel", i64)]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("host_segs", ctypes.POINTER(AdamwSeg)), ("nseg", i32)]
+
+
+class StreamStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_double) for n in (
+        "h2d_bytes", "d2h_bytes", "h2d_ms", "d2h_ms", "kernel_ms",
+        "copy_busy_ms", "wall_ms", "last_kernel_ms")]
+
+
+# (name, restype, argtypes) of every exported function
+SIGNATURES = [
+    ("lema_status_string", ctypes.c_char_p, [i32]),
+    ("lema_last_hip_error", i32, []),
+    ("lema_version", i32, []),
+    ("lema_adamw_constants", i32, [ctypes.POINTER(AdamwArgs), ctypes.POINTER(AdamwConsts)]),
+    ("lema_adamw_step", i32, [ctypes.POINTER(AdamwSeg), i32, ctypes.POINTER(AdamwArgs), vp]),
+    ("lema_grad_accum", i32, [ctypes.POINTER(AccumSeg), i32, i32, vp]),
+    ("lema_slot_pool_create", i32, [vp, ctypes.c_size_t, i32, vp, vp, ctypes.POINTER(vp)]),
+    ("lema_slot_pool_destroy", i32, [vp]),
+    ("lema_slot_stream", i32, [vp, ctypes.POINTER(Layer), i32, ctypes.POINTER(AdamwArgs),
+                               ctypes.POINTER(StreamStats)]),
+    ("lema_host_alloc", i32, [ctypes.POINTER(vp), ctypes.c_size_t]),
+    ("lema_host_free", i32, [vp]),
+    ("lema_measure_copy", i32, [vp, vp, ctypes.c_size_t, i32, vp]),
+    ("lema_probe_fp32", i32, [vp, vp, vp, vp, vp, i64, vp]),
+    ("lema_device_info", i32, [ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+]
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load liblema.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m optimizer_step_lema_amd.build` "
+            "(or __graft_entry__.build()); there is no non-HIP fallback")
+    import torch  # noqa: F401  -- loads the HIP runtime the library must bind to
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, res, args in SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class LemaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.lema_status_string(status).decode()
+        hip = lib.lema_last_hip_error() if status == LEMA_ERR_HIP else 0
+        super().__init__(f"{where}: {msg}" + (f" (hipError {hip})" if hip else ""))
+        self.status = status
+        self.hip_error = hip
+
+
+def check(status: int, where: str) -> None:
+    if status != LEMA_OK:
+        raise LemaError(status, where)

@@ -1,0 +1,233 @@
+"""Thin torch-facing binding over liblema.so.
+
+Argument marshalling only: tensors are checked for dtype, device, length and
+contiguity, turned into raw pointers and passed to the C ABI of
+include/lema.h together with the current HIP stream.  Every step of the
+optimizer path runs in the library's HIP kernels.
+
+Method (LEMA README "Quick Start" and "Selective Full Fine-Tuning"; LLMScale
+fine-tuning VRAM page): one per-layer AdamW step over fp32 master/m/v with a
+bf16 gradient (or an fp32 accumulator), bf16 weight write-back and an
+optional fp32 delta; fp32 accumulation of bf16 micro-batch gradients;
+streaming of host-resident state through a pool of HBM slots.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _native as N
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _check(t: Optional[torch.Tensor], dtype, n: int, name: str, where: str = "cuda") -> int:
+    if t is None:
+        return 0
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() != n:
+        raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if where == "cuda" and not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if where == "cpu" and t.is_cuda:
+        raise ValueError(f"{name}: must be a host tensor")
+    return t.data_ptr() if n > 0 else 0
+
+
+@dataclass
+class AdamwSegment:
+    """One trainable tensor: fp32 master/m/v, bf16 or fp32 grad, bf16 weight out."""
+    master: torch.Tensor
+    exp_avg: torch.Tensor
+    exp_avg_sq: torch.Tensor
+    grad: torch.Tensor
+    weight: torch.Tensor
+    orig: Optional[torch.Tensor] = None
+    delta: Optional[torch.Tensor] = None
+
+    def to_c(self, where: str = "cuda") -> N.AdamwSeg:
+        n = self.master.numel()
+        gdt = self.grad.dtype
+        if gdt not in (torch.bfloat16, torch.float32):
+            raise TypeError(f"grad: expected bfloat16 or float32, got {gdt}")
+        return N.AdamwSeg(
+            _check(self.master, torch.float32, n, "master", where),
+            _check(self.exp_avg, torch.float32, n, "exp_avg", where),
+            _check(self.exp_avg_sq, torch.float32, n, "exp_avg_sq", where),
+            _check(self.grad, gdt, n, "grad", where),
+            _check(self.weight, torch.bfloat16, n, "weight", where),
+            _check(self.orig, torch.bfloat16, n, "orig", where),
+            _check(self.delta, torch.float32, n, "delta", where),
+            n)
+
+
+def _args(lr, beta1, beta2, eps, weight_decay, step, grad_dtype) -> N.AdamwArgs:
+    return N.AdamwArgs(float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                       int(step), int(grad_dtype), 0)
+
+
+def _grad_dtype(segments: Sequence[AdamwSegment]) -> int:
+    kinds = {s.grad.dtype for s in segments}
+    if len(kinds) > 1:
+        raise TypeError("all segments of one call must share the gradient dtype")
+    return N.LEMA_GRAD_FP32 if kinds == {torch.float32} else N.LEMA_GRAD_BF16
+
+
+def adamw_constants(*, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step,
+                    grad_dtype=N.LEMA_GRAD_BF16) -> dict:
+    """The fp32 constants the kernel uses for this step (host only)."""
+    lib = N.load()
+    out = N.AdamwConsts()
+    N.check(lib.lema_adamw_constants(ctypes.byref(_args(lr, beta1, beta2, eps, weight_decay, step,
+                                                        grad_dtype)), ctypes.byref(out)),
+            "lema_adamw_constants")
+    return {name: np.float32(getattr(out, name)) for name, _ in N.AdamwConsts._fields_}
+
+
+def adamw_step(segments: Sequence[AdamwSegment], *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+               weight_decay=0.01, step, stream=None) -> None:
+    """One AdamW step over `segments` on the GPU (asynchronous on `stream`)."""
+    lib = N.load()
+    segs = (N.AdamwSeg * max(1, len(segments)))(*[s.to_c() for s in segments])
+    args = _args(lr, beta1, beta2, eps, weight_decay, step, _grad_dtype(segments))
+    N.check(lib.lema_adamw_step(segs, len(segments), ctypes.byref(args), _stream_handle(stream)),
+            "lema_adamw_step")
+
+
+@dataclass
+class AccumSegment:
+    acc: torch.Tensor
+    grad: torch.Tensor
+
+
+def grad_accum(segments: Sequence[AccumSegment], *, overwrite: bool, stream=None) -> None:
+    """acc = f32(g) (overwrite) or acc += f32(g) for every segment, on the GPU."""
+    lib = N.load()
+    cs = []
+    for s in segments:
+        n = s.acc.numel()
+        cs.append(N.AccumSeg(_check(s.acc, torch.float32, n, "acc"),
+                             _check(s.grad, torch.bfloat16, n, "grad"), n))
+    arr = (N.AccumSeg * max(1, len(cs)))(*cs)
+    N.check(lib.lema_grad_accum(arr, len(cs), 1 if overwrite else 0, _stream_handle(stream)),
+            "lema_grad_accum")
+
+
+# ------------------------------------------------------------ host memory
+
+class _PinnedBlock:
+    """Page-locked host bytes from lema_host_alloc, freed with the last view."""
+
+    def __init__(self, nbytes: int):
+        lib = N.load()
+        p = ctypes.c_void_p()
+        N.check(lib.lema_host_alloc(ctypes.byref(p), max(1, nbytes)), "lema_host_alloc")
+        self.ptr = p.value
+        self.nbytes = nbytes
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            N.load().lema_host_free(self.ptr)
+            self.ptr = None
+
+
+def pinned_empty(numel: int, dtype: torch.dtype) -> torch.Tensor:
+    """Exact-size page-locked host tensor (no power-of-two rounding)."""
+    itemsize = torch.empty((), dtype=dtype).element_size()
+    block = _PinnedBlock(numel * itemsize)
+    raw = (ctypes.c_uint8 * max(1, numel * itemsize)).from_address(block.ptr)
+    raw._lema_owner = block                       # keeps the block alive with the buffer
+    np_view = np.frombuffer(raw, dtype=np.uint8, count=numel * itemsize)
+    return torch.from_numpy(np_view).view(dtype)
+
+
+# ------------------------------------------------------------ slot stream
+
+class SlotPool:
+    """A pool of `nslots` HBM slots of `slot_bytes` each, with its own copy and
+    compute streams (default priority), for lema_slot_stream."""
+
+    def __init__(self, slot_bytes: int, nslots: int = 2):
+        lib = N.load()
+        slot_bytes = (int(slot_bytes) + 255) // 256 * 256
+        self.region = torch.empty(slot_bytes * nslots, dtype=torch.uint8, device="cuda")
+        self.copy_stream = torch.cuda.Stream()
+        self.compute_stream = torch.cuda.Stream()
+        self.slot_bytes = slot_bytes
+        self.nslots = nslots
+        h = ctypes.c_void_p()
+        torch.cuda.synchronize()
+        N.check(lib.lema_slot_pool_create(self.region.data_ptr(), slot_bytes, nslots,
+                                          self.copy_stream.cuda_stream,
+                                          self.compute_stream.cuda_stream, ctypes.byref(h)),
+                "lema_slot_pool_create")
+        self.handle = h.value
+
+    def stream(self, layers: Sequence[Sequence[AdamwSegment]], *, lr, beta1=0.9, beta2=0.999,
+               eps=1e-8, weight_decay=0.01, step) -> dict:
+        """One AdamW step for every layer, streamed host -> slot -> host.
+        Blocks until done; returns the timing statistics."""
+        lib = N.load()
+        keep = []
+        c_layers = (N.Layer * max(1, len(layers)))()
+        for i, segs in enumerate(layers):
+            arr = (N.AdamwSeg * max(1, len(segs)))(*[s.to_c(where="cpu") for s in segs])
+            keep.append(arr)
+            c_layers[i] = N.Layer(ctypes.cast(arr, ctypes.POINTER(N.AdamwSeg)), len(segs))
+        args = _args(lr, beta1, beta2, eps, weight_decay, step, N.LEMA_GRAD_BF16)
+        st = N.StreamStats()
+        N.check(lib.lema_slot_stream(self.handle, c_layers, len(layers), ctypes.byref(args),
+                                     ctypes.byref(st)), "lema_slot_stream")
+        return {name: getattr(st, name) for name, _ in N.StreamStats._fields_}
+
+    def close(self):
+        if getattr(self, "handle", None):
+            N.check(N.load().lema_slot_pool_destroy(self.handle), "lema_slot_pool_destroy")
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------- measurement aids
+
+def measure_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, blocks_per_cu: int = 0,
+                 stream=None) -> None:
+    N.check(N.load().lema_measure_copy(src.data_ptr(), dst.data_ptr(), int(nbytes),
+                                       int(blocks_per_cu), _stream_handle(stream)),
+            "lema_measure_copy")
+
+
+def probe_fp32(a: torch.Tensor, b: torch.Tensor, stream=None):
+    """(a/b, sqrt(a), bf16(a)) as compiled inside the AdamW kernel."""
+    n = a.numel()
+    _check(a, torch.float32, n, "a")
+    _check(b, torch.float32, n, "b")
+    q = torch.empty_like(a)
+    r = torch.empty_like(a)
+    h = torch.empty(n, dtype=torch.bfloat16, device=a.device)
+    N.check(N.load().lema_probe_fp32(a.data_ptr(), b.data_ptr(), q.data_ptr(), r.data_ptr(),
+                                     h.data_ptr(), n, _stream_handle(stream)), "lema_probe_fp32")
+    return q, r, h
+
+
+def device_info() -> dict:
+    cus, bpc = ctypes.c_int32(), ctypes.c_int32()
+    N.check(N.load().lema_device_info(ctypes.byref(cus), ctypes.byref(bpc)), "lema_device_info")
+    return {"compute_units": cus.value, "blocks_per_cu": bpc.value}

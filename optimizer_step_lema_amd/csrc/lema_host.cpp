@@ -1,0 +1,500 @@
+// lema_host.cpp -- host side of the C ABI in include/lema.h: argument
+// validation, fp32 constant derivation, launch tables and kernel launches.
+//
+// Method: LEMA README, "Quick Start" (torch.optim.AdamW, lr 1e-4) and
+// "Selective Full Fine-Tuning" (per-layer AdamW over fp32 states, fp32
+// gradient accumulation, fp32 delta checkpoint); LLMScale fine-tuning VRAM
+// page (16 bytes per trained parameter).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "lema.h"
+#include "lema_host_internal.h"
+#include "lema_measure.h"
+#include "lema_internal.h"
+
+namespace lema {
+
+// ------------------------------------------------------------ errors
+
+static thread_local int32_t t_last_hip_error = 0;
+
+lema_status hip_failed(hipError_t e) {
+    t_last_hip_error = static_cast<int32_t>(e);
+    return LEMA_ERR_HIP;
+}
+
+// ------------------------------------------------------- constants
+
+// beta^t in double by square-and-multiply, taking the bits of t from the
+// least significant end.
+static double beta_pow(double beta, int64_t t) {
+    double acc = 1.0;
+    double sq = beta;
+    for (int64_t e = t; e != 0; e >>= 1) {
+        if (e & 1) acc *= sq;
+        sq *= sq;
+    }
+    return acc;
+}
+
+lema_status check_hparams(const lema_adamw_args *a) {
+    if (a == nullptr) return LEMA_ERR_NULL;
+    const double vals[] = {a->lr, a->beta1, a->beta2, a->eps, a->weight_decay};
+    for (double x : vals)
+        if (!std::isfinite(x)) return LEMA_ERR_HPARAM;
+    if (a->lr < 0.0 || a->weight_decay < 0.0 || a->eps <= 0.0) return LEMA_ERR_HPARAM;
+    if (a->beta1 < 0.0 || a->beta1 >= 1.0 || a->beta2 < 0.0 || a->beta2 >= 1.0) return LEMA_ERR_HPARAM;
+    if (a->step < 1) return LEMA_ERR_HPARAM;
+    if (a->reserved != 0) return LEMA_ERR_HPARAM;
+    if (a->grad_dtype != LEMA_GRAD_BF16 && a->grad_dtype != LEMA_GRAD_FP32) return LEMA_ERR_DTYPE;
+    return LEMA_OK;
+}
+
+AdamwConsts derive_consts(const lema_adamw_args *a) {
+    // each constant: computed in double, rounded to fp32 once
+    const double bias1 = 1.0 - beta_pow(a->beta1, a->step);
+    const double bias2 = 1.0 - beta_pow(a->beta2, a->step);
+    AdamwConsts c;
+    c.b1 = static_cast<float>(a->beta1);
+    c.omb1 = static_cast<float>(1.0 - a->beta1);
+    c.b2 = static_cast<float>(a->beta2);
+    c.omb2 = static_cast<float>(1.0 - a->beta2);
+    c.eps = static_cast<float>(a->eps);
+    c.decay = static_cast<float>(1.0 - a->lr * a->weight_decay);
+    c.step_size = static_cast<float>(a->lr / bias1);
+    c.inv_bc2_root = static_cast<float>(1.0 / std::sqrt(bias2));
+    return c;
+}
+
+// ------------------------------------------------------- validation
+
+// True if two spans intersect and at least one of them is written.
+bool any_conflict(std::vector<Span> &spans) {
+    std::sort(spans.begin(), spans.end(),
+              [](const Span &x, const Span &y) { return x.lo < y.lo; });
+    uintptr_t reach_any = 0, reach_written = 0;   // max end of spans seen so far
+    bool seen = false;
+    for (const Span &s : spans) {
+        if (seen) {
+            if (reach_written > s.lo) return true;
+            if (s.written && reach_any > s.lo) return true;
+        }
+        seen = true;
+        reach_any = std::max(reach_any, s.hi);
+        if (s.written) reach_written = std::max(reach_written, s.hi);
+    }
+    return false;
+}
+
+static void add_span(std::vector<Span> &spans, const void *p, int64_t numel, size_t elem,
+                     bool written) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    spans.push_back(Span{lo, lo + static_cast<uintptr_t>(numel) * elem, written});
+}
+
+lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_t grad_dtype,
+                                bool delta_allowed, std::vector<Span> *spans) {
+    if (nseg < 0) return LEMA_ERR_SIZE;
+    if (nseg > 0 && segs == nullptr) return LEMA_ERR_NULL;
+    const size_t gsize = grad_dtype == LEMA_GRAD_FP32 ? 4 : 2;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const lema_adamw_seg &s = segs[i];
+        if (s.numel < 0) return LEMA_ERR_SIZE;
+        if ((s.orig_bf16 == nullptr) != (s.delta == nullptr)) return LEMA_ERR_NULL;
+        if (!delta_allowed && s.delta != nullptr) return LEMA_ERR_NULL;
+        if (s.numel == 0) continue;
+        if (!s.master || !s.exp_avg || !s.exp_avg_sq || !s.grad || !s.weight_bf16) return LEMA_ERR_NULL;
+        const uintptr_t f32 = reinterpret_cast<uintptr_t>(s.master) |
+                              reinterpret_cast<uintptr_t>(s.exp_avg) |
+                              reinterpret_cast<uintptr_t>(s.exp_avg_sq) |
+                              reinterpret_cast<uintptr_t>(s.delta) |
+                              (gsize == 4 ? reinterpret_cast<uintptr_t>(s.grad) : 0);
+        const uintptr_t b16 = reinterpret_cast<uintptr_t>(s.weight_bf16) |
+                              reinterpret_cast<uintptr_t>(s.orig_bf16) |
+                              (gsize == 2 ? reinterpret_cast<uintptr_t>(s.grad) : 0);
+        if ((f32 & 3) || (b16 & 1)) return LEMA_ERR_ALIGN;
+        if (spans) {
+            add_span(*spans, s.master, s.numel, 4, true);
+            add_span(*spans, s.exp_avg, s.numel, 4, true);
+            add_span(*spans, s.exp_avg_sq, s.numel, 4, true);
+            add_span(*spans, s.grad, s.numel, gsize, false);
+            add_span(*spans, s.weight_bf16, s.numel, 2, true);
+            if (s.delta) {
+                add_span(*spans, s.orig_bf16, s.numel, 2, false);
+                add_span(*spans, s.delta, s.numel, 4, true);
+            }
+        }
+    }
+    return LEMA_OK;
+}
+
+// ----------------------------------------------- per-device state
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kCacheEntries = 16;
+
+// A launch table kept on the device.  Tables are immutable once uploaded;
+// a call whose table is byte-identical to a cached one launches on it
+// without any copy (the usual case: the same tensors every step).
+struct TableEntry {
+    std::vector<unsigned char> bytes;
+    void *dev = nullptr;
+    size_t dev_cap = 0;
+    void *staging = nullptr;      // page-locked source of the upload
+    size_t staging_cap = 0;
+    hipEvent_t last_use = nullptr;
+    hipStream_t last_stream = nullptr;
+    bool in_use = false;          // last_use has been recorded
+    uint64_t stamp = 0;
+};
+
+struct DeviceState {
+    std::mutex mu;
+    bool ready = false;
+    int cu_count = 0;
+    int blocks_per_cu = 8;
+    uint64_t clock = 0;
+    TableEntry entries[kCacheEntries];
+};
+
+DeviceState g_devices[kMaxDevices];
+
+lema_status device_state(DeviceState **out, int *device) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_failed(e);
+    if (dev < 0 || dev >= kMaxDevices) return LEMA_ERR_SIZE;
+    DeviceState &d = g_devices[dev];
+    std::lock_guard<std::mutex> lock(d.mu);
+    if (!d.ready) {
+        int cus = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return hip_failed(e);
+        d.cu_count = cus > 0 ? cus : 1;
+        if (const char *env = std::getenv("LEMA_BLOCKS_PER_CU")) {
+            const int v = std::atoi(env);
+            if (v >= 1 && v <= 64) d.blocks_per_cu = v;
+        }
+        d.ready = true;
+    }
+    *out = &d;
+    if (device) *device = dev;
+    return LEMA_OK;
+}
+
+// Pick the cache entry for `bytes` (must hold d.mu).  On a hit nothing is
+// copied; on a miss the least recently used entry is reloaded once every
+// launch still reading it has finished.
+lema_status acquire_table(DeviceState &d, const std::vector<unsigned char> &bytes,
+                          hipStream_t stream, TableEntry **out) {
+    hipError_t e;
+    for (TableEntry &t : d.entries) {
+        if (t.in_use && t.bytes == bytes) {
+            if (t.last_stream != stream) {
+                // a later reload must wait for both streams' launches
+                e = hipStreamWaitEvent(stream, t.last_use, 0);
+                if (e != hipSuccess) return hip_failed(e);
+            }
+            *out = &t;
+            return LEMA_OK;
+        }
+    }
+    TableEntry *victim = nullptr;
+    for (TableEntry &t : d.entries) {
+        if (!t.in_use) { victim = &t; break; }
+        if (!victim || t.stamp < victim->stamp) victim = &t;
+    }
+    if (victim->in_use) {
+        e = hipEventSynchronize(victim->last_use);
+        if (e != hipSuccess) return hip_failed(e);
+        victim->in_use = false;
+    }
+    victim->bytes.clear();
+    const size_t n = bytes.size();
+    if (victim->dev_cap < n) {
+        if (victim->dev) (void)hipFree(victim->dev);
+        victim->dev = nullptr;
+        victim->dev_cap = 0;
+        const size_t cap = std::max<size_t>(n, 16384);
+        e = hipMalloc(&victim->dev, cap);
+        if (e != hipSuccess) return hip_failed(e);
+        victim->dev_cap = cap;
+    }
+    if (victim->staging_cap < n) {
+        if (victim->staging) (void)hipHostFree(victim->staging);
+        victim->staging = nullptr;
+        victim->staging_cap = 0;
+        const size_t cap = std::max<size_t>(n, 16384);
+        e = hipHostMalloc(&victim->staging, cap, hipHostMallocDefault);
+        if (e != hipSuccess) return hip_failed(e);
+        victim->staging_cap = cap;
+    }
+    if (!victim->last_use) {
+        e = hipEventCreateWithFlags(&victim->last_use, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_failed(e);
+    }
+    std::memcpy(victim->staging, bytes.data(), n);
+    e = hipMemcpyAsync(victim->dev, victim->staging, n, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_failed(e);
+    victim->bytes = bytes;
+    *out = victim;
+    return LEMA_OK;
+}
+
+lema_status release_table(DeviceState &d, TableEntry *t, hipStream_t stream) {
+    hipError_t e = hipEventRecord(t->last_use, stream);
+    if (e != hipSuccess) return hip_failed(e);
+    t->last_stream = stream;
+    t->in_use = true;
+    t->stamp = ++d.clock;
+    return LEMA_OK;
+}
+
+// Tile prefix sums and records of the non-empty segments.
+struct TableBuild {
+    std::vector<unsigned char> bytes;
+    int nseg = 0;
+    uint64_t total_tiles = 0;
+};
+
+void build_table(const std::vector<SegRec> &recs, TableBuild *tb) {
+    const int n = static_cast<int>(recs.size());
+    tb->nseg = n;
+    tb->bytes.assign(table_bytes(n), 0);
+    uint32_t *tile_begin = reinterpret_cast<uint32_t *>(tb->bytes.data());
+    uint64_t tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        tile_begin[i] = static_cast<uint32_t>(tiles);
+        tiles += static_cast<uint64_t>((recs[i].numel + kTile - 1) / kTile);
+    }
+    tile_begin[n] = static_cast<uint32_t>(tiles);
+    std::memcpy(tb->bytes.data() + table_tiles_bytes(n), recs.data(), sizeof(SegRec) * n);
+    tb->total_tiles = tiles;
+}
+
+// Tile counts must leave room for the grid stride in 32-bit tile indices.
+constexpr uint64_t kMaxTiles = (uint64_t(1) << 32) - (uint64_t(1) << 20);
+
+uint64_t count_tiles(const std::vector<SegRec> &recs) {
+    uint64_t tiles = 0;
+    for (const SegRec &r : recs) tiles += static_cast<uint64_t>((r.numel + kTile - 1) / kTile);
+    return tiles;
+}
+
+int grid_for(const DeviceState &d, uint64_t tiles) {
+    const uint64_t cap = uint64_t(d.cu_count) * uint64_t(d.blocks_per_cu);
+    return static_cast<int>(std::max<uint64_t>(1, std::min(tiles, cap)));
+}
+
+}  // namespace
+
+lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
+                              bool grad_f32, hipStream_t stream) {
+    if (recs.empty()) return LEMA_OK;
+    if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
+    DeviceState *d = nullptr;
+    lema_status st = device_state(&d, nullptr);
+    if (st != LEMA_OK) return st;
+    bool with_delta = false;
+    for (const SegRec &r : recs) with_delta |= r.p[6] != 0;
+
+    TableBuild tb;
+    build_table(recs, &tb);
+    std::lock_guard<std::mutex> lock(d->mu);
+    TableEntry *t = nullptr;
+    st = acquire_table(*d, tb.bytes, stream, &t);
+    if (st != LEMA_OK) return st;
+    hipError_t e = launch_adamw(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_f32,
+                                with_delta, c, grid_for(*d, tb.total_tiles), stream);
+    lema_status rel = release_table(*d, t, stream);
+    if (e != hipSuccess) return hip_failed(e);
+    return rel;
+}
+
+lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
+                              hipStream_t stream) {
+    if (recs.empty()) return LEMA_OK;
+    if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
+    DeviceState *d = nullptr;
+    lema_status st = device_state(&d, nullptr);
+    if (st != LEMA_OK) return st;
+    TableBuild tb;
+    build_table(recs, &tb);
+    std::lock_guard<std::mutex> lock(d->mu);
+    TableEntry *t = nullptr;
+    st = acquire_table(*d, tb.bytes, stream, &t);
+    if (st != LEMA_OK) return st;
+    hipError_t e = launch_accum(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), overwrite,
+                                grid_for(*d, tb.total_tiles), stream);
+    lema_status rel = release_table(*d, t, stream);
+    if (e != hipSuccess) return hip_failed(e);
+    return rel;
+}
+
+void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out) {
+    out->clear();
+    for (int32_t i = 0; i < nseg; ++i) {
+        const lema_adamw_seg &s = segs[i];
+        if (s.numel == 0) continue;
+        SegRec r;
+        r.p[0] = reinterpret_cast<uint64_t>(s.master);
+        r.p[1] = reinterpret_cast<uint64_t>(s.exp_avg);
+        r.p[2] = reinterpret_cast<uint64_t>(s.exp_avg_sq);
+        r.p[3] = reinterpret_cast<uint64_t>(s.grad);
+        r.p[4] = reinterpret_cast<uint64_t>(s.weight_bf16);
+        r.p[5] = reinterpret_cast<uint64_t>(s.orig_bf16);
+        r.p[6] = reinterpret_cast<uint64_t>(s.delta);
+        r.numel = s.numel;
+        out->push_back(r);
+    }
+}
+
+}  // namespace lema
+
+// ==================================================================== C ABI
+
+using namespace lema;
+
+extern "C" {
+
+const char *lema_status_string(lema_status s) {
+    switch (s) {
+    case LEMA_OK: return "LEMA_OK";
+    case LEMA_ERR_NULL: return "LEMA_ERR_NULL: required pointer is NULL or orig/delta unpaired";
+    case LEMA_ERR_SIZE: return "LEMA_ERR_SIZE: negative or too large size";
+    case LEMA_ERR_HPARAM: return "LEMA_ERR_HPARAM: hyperparameter or step out of range";
+    case LEMA_ERR_DTYPE: return "LEMA_ERR_DTYPE: unknown gradient dtype";
+    case LEMA_ERR_OVERLAP: return "LEMA_ERR_OVERLAP: arrays overlap where one is written";
+    case LEMA_ERR_NOT_PINNED: return "LEMA_ERR_NOT_PINNED: host memory is not page-locked";
+    case LEMA_ERR_HIP: return "LEMA_ERR_HIP: HIP runtime error (see lema_last_hip_error)";
+    case LEMA_ERR_ALIGN: return "LEMA_ERR_ALIGN: pointer not aligned to its element size";
+    default: return "unknown lema_status";
+    }
+}
+
+int32_t lema_last_hip_error(void) { return t_last_hip_error; }
+
+int32_t lema_version(void) { return 100; }
+
+lema_status lema_adamw_constants(const lema_adamw_args *args, lema_adamw_consts *out) {
+    if (args == nullptr || out == nullptr) return LEMA_ERR_NULL;
+    lema_status st = check_hparams(args);
+    if (st != LEMA_OK) return st;
+    const AdamwConsts c = derive_consts(args);
+    out->beta1 = c.b1;
+    out->one_minus_beta1 = c.omb1;
+    out->beta2 = c.b2;
+    out->one_minus_beta2 = c.omb2;
+    out->eps = c.eps;
+    out->decay = c.decay;
+    out->step_size = c.step_size;
+    out->inv_bias_correction2_root = c.inv_bc2_root;
+    return LEMA_OK;
+}
+
+lema_status lema_adamw_step(const lema_adamw_seg *segs, int32_t nseg, const lema_adamw_args *args,
+                            void *stream) {
+    lema_status st = check_hparams(args);
+    if (st != LEMA_OK) return st;
+    std::vector<Span> spans;
+    st = validate_adamw_segs(segs, nseg, args->grad_dtype, true, &spans);
+    if (st != LEMA_OK) return st;
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    std::vector<SegRec> recs;
+    adamw_records(segs, nseg, &recs);
+    return launch_adamw_recs(recs, derive_consts(args), args->grad_dtype == LEMA_GRAD_FP32,
+                             static_cast<hipStream_t>(stream));
+}
+
+lema_status lema_grad_accum(const lema_accum_seg *segs, int32_t nseg, int32_t overwrite,
+                            void *stream) {
+    if (nseg < 0) return LEMA_ERR_SIZE;
+    if (nseg > 0 && segs == nullptr) return LEMA_ERR_NULL;
+    std::vector<Span> spans;
+    std::vector<SegRec> recs;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const lema_accum_seg &s = segs[i];
+        if (s.numel < 0) return LEMA_ERR_SIZE;
+        if (s.numel == 0) continue;
+        if (!s.acc || !s.grad_bf16) return LEMA_ERR_NULL;
+        if ((reinterpret_cast<uintptr_t>(s.acc) & 3) || (reinterpret_cast<uintptr_t>(s.grad_bf16) & 1))
+            return LEMA_ERR_ALIGN;
+        add_span(spans, s.acc, s.numel, 4, true);
+        add_span(spans, s.grad_bf16, s.numel, 2, false);
+        SegRec r{};
+        r.p[0] = reinterpret_cast<uint64_t>(s.acc);
+        r.p[1] = reinterpret_cast<uint64_t>(s.grad_bf16);
+        r.numel = s.numel;
+        recs.push_back(r);
+    }
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    return launch_accum_recs(recs, overwrite != 0, static_cast<hipStream_t>(stream));
+}
+
+lema_status lema_host_alloc(void **out, size_t bytes) {
+    if (out == nullptr) return LEMA_ERR_NULL;
+    *out = nullptr;
+    if (bytes == 0) return LEMA_ERR_SIZE;
+    hipError_t e = hipHostMalloc(out, bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+        *out = nullptr;
+        return hip_failed(e);
+    }
+    return LEMA_OK;
+}
+
+lema_status lema_host_free(void *p) {
+    if (p == nullptr) return LEMA_OK;
+    hipError_t e = hipHostFree(p);
+    return e == hipSuccess ? LEMA_OK : hip_failed(e);
+}
+
+// ------------------------------------------------ measurement aids
+
+lema_status lema_measure_copy(const void *src, void *dst, size_t bytes, int32_t blocks_per_cu,
+                              void *stream) {
+    if (src == nullptr || dst == nullptr) return LEMA_ERR_NULL;
+    if (bytes == 0 || (bytes % 16) != 0 || blocks_per_cu < 0 || blocks_per_cu > 64) return LEMA_ERR_SIZE;
+    if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) != 0)
+        return LEMA_ERR_ALIGN;
+    std::vector<Span> spans;
+    add_span(spans, src, static_cast<int64_t>(bytes), 1, false);
+    add_span(spans, dst, static_cast<int64_t>(bytes), 1, true);
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    DeviceState *d = nullptr;
+    lema_status st = device_state(&d, nullptr);
+    if (st != LEMA_OK) return st;
+    const int bpc = blocks_per_cu > 0 ? blocks_per_cu : d->blocks_per_cu;
+    hipError_t e = launch_copy(src, dst, bytes, d->cu_count * bpc, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LEMA_OK : hip_failed(e);
+}
+
+lema_status lema_probe_fp32(const float *a, const float *b, float *quot, float *root,
+                            uint16_t *bf16, int64_t n, void *stream) {
+    if (n < 0) return LEMA_ERR_SIZE;
+    if (n == 0) return LEMA_OK;
+    if (!a || !b || !quot || !root || !bf16) return LEMA_ERR_NULL;
+    hipError_t e = launch_fp32_probe(a, b, quot, root, bf16, n, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LEMA_OK : hip_failed(e);
+}
+
+lema_status lema_device_info(int32_t *compute_units, int32_t *blocks_per_cu) {
+    if (compute_units == nullptr || blocks_per_cu == nullptr) return LEMA_ERR_NULL;
+    DeviceState *d = nullptr;
+    lema_status st = device_state(&d, nullptr);
+    if (st != LEMA_OK) return st;
+    *compute_units = d->cu_count;
+    *blocks_per_cu = d->blocks_per_cu;
+    return LEMA_OK;
+}
+
+}  // extern "C"

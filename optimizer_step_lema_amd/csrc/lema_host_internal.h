@@ -1,0 +1,42 @@
+// lema_host_internal.h -- host helpers shared by the C ABI translation units.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "lema.h"
+#include "lema_internal.h"
+
+namespace lema {
+
+// Address range [lo, hi) of one array in one call; `written` if the call
+// stores into it.
+struct Span {
+    uintptr_t lo, hi;
+    bool written;
+};
+
+// Records hipError_t `e` as this thread's last HIP error; returns LEMA_ERR_HIP.
+lema_status hip_failed(hipError_t e);
+
+lema_status check_hparams(const lema_adamw_args *a);
+AdamwConsts derive_consts(const lema_adamw_args *a);
+
+// Validates segment descriptors (sizes, pairing, required pointers,
+// element alignment) and appends their spans when `spans` is non-null.
+lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_t grad_dtype,
+                                bool delta_allowed, std::vector<Span> *spans);
+bool any_conflict(std::vector<Span> &spans);
+
+// Launch records of the non-empty segments.
+void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out);
+
+// Launch through the per-device table cache on `stream`.
+lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
+                              bool grad_f32, hipStream_t stream);
+lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
+                              hipStream_t stream);
+
+}  // namespace lema

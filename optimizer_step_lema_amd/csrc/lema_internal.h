@@ -1,0 +1,60 @@
+// lema_internal.h -- interface between the host layer and the gfx950 kernels.
+// Not installed; the public ABI is include/lema.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lema {
+
+// Work decomposition.  A tile is the unit a workgroup processes at once:
+// kBlock lanes x kVec contiguous elements x kUnroll accesses per lane.  Each
+// access moves 16 bytes of every fp32 array and 8 bytes of every bf16 array
+// per lane, contiguous across the wavefront.
+constexpr int kBlock = 256;
+constexpr int kVec = 4;
+constexpr int kUnroll = 2;
+constexpr int64_t kTile = int64_t(kBlock) * kVec * kUnroll;   // 2048 elements
+constexpr int kWindow = 64;   // segment records a workgroup stages in LDS at once
+
+// One segment of the launch table: up to seven array pointers and the length.
+//   AdamW : p = {master, m, v, grad, weight_bf16, orig_bf16, delta}
+//   accum : p = {acc, grad_bf16, 0, 0, 0, 0, 0}
+struct SegRec {
+    uint64_t p[7];
+    int64_t numel;
+};
+static_assert(sizeof(SegRec) == 64, "segment record is one 64-byte line");
+
+// The launch table in device memory is
+//   uint32_t tile_begin[nseg + 1]   (prefix sum of tiles per segment)
+//   padding to a multiple of 64 bytes
+//   SegRec   rec[nseg]
+constexpr size_t table_tiles_bytes(int nseg) {
+    return (sizeof(uint32_t) * (size_t(nseg) + 1) + 63) & ~size_t(63);
+}
+constexpr size_t table_bytes(int nseg) {
+    return table_tiles_bytes(nseg) + sizeof(SegRec) * size_t(nseg);
+}
+
+struct AdamwConsts {
+    float b1, omb1, b2, omb2, eps, decay, step_size, inv_bc2_root;
+};
+
+// Kernel launches (asynchronous on `stream`).  `table` is the device copy of
+// the launch table; `grid` workgroups walk tiles 0 .. total_tiles-1.
+hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles,
+                        bool grad_f32, bool with_delta, const AdamwConsts &c,
+                        int grid, hipStream_t stream);
+hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
+                        bool overwrite, int grid, hipStream_t stream);
+
+// Measurement aids (include/lema_measure.h).
+hipError_t launch_copy(const void *src, void *dst, size_t bytes, int grid,
+                       hipStream_t stream);
+hipError_t launch_fp32_probe(const float *a, const float *b, float *quot,
+                             float *root, uint16_t *bf16, int64_t n,
+                             hipStream_t stream);
+
+}  // namespace lema

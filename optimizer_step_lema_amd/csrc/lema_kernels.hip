@@ -1,0 +1,383 @@
+// lema_kernels.hip -- gfx950 kernels of the mixed-precision AdamW path.
+//
+// adamw_mta_kernel : one AdamW step over a list of segments (LEMA README,
+//   "Quick Start": torch.optim.AdamW; "Selective Full Fine-Tuning": per-layer
+//   AdamW over fp32 master, m and v, fp32 delta for checkpoints; LLMScale
+//   fine-tuning VRAM page: bf16 weight and gradient next to fp32 states).
+// accum_mta_kernel : fp32 accumulation of a bf16 micro-batch gradient
+//   (README, "Selective Full Fine-Tuning": fp32 gradient accumulation).
+//
+// Both are elementwise and bound by HBM bandwidth, so there is no MFMA and
+// no LDS tiling of data: each lane streams 4 contiguous elements per access
+// (16-byte fp32 / 8-byte bf16 vector loads and stores, contiguous across the
+// wavefront).  A persistent grid walks the tiles of all segments in order;
+// each workgroup keeps a window of the segment table in LDS and finds the
+// segment of its next tile by a forward walk over the tile prefix sums.
+//
+// Arithmetic: binary32 only, no contraction into FMA (this file is built with
+// -ffp-contract=off and every arithmetic function also carries the pragma),
+// correctly rounded sqrt and division (the compiler's IEEE expansions),
+// subnormals kept, bf16 output rounded to nearest even by gfx950's
+// v_cvt_pk_bf16_f32.
+#include <hip/hip_runtime.h>
+
+#include "lema_internal.h"
+
+namespace lema {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Pointers into global memory (address space 1).  The segment pointers come
+// out of LDS, so without this the compiler could not prove where they point
+// and would emit flat instructions instead of global loads and stores.
+#define LEMA_GLOBAL __attribute__((address_space(1)))
+typedef LEMA_GLOBAL float gfloat;
+typedef LEMA_GLOBAL uint16_t gu16;
+typedef LEMA_GLOBAL f32x4 gf32x4;
+typedef LEMA_GLOBAL u32x2 gu32x2;
+
+template <class T>
+__device__ __forceinline__ T *as_global(uint64_t addr) {
+    return reinterpret_cast<T *>(addr);
+}
+
+// ------------------------------------------------------------- helpers
+
+// A value that is the same in every lane, moved to scalar registers so that
+// address arithmetic on it stays on the scalar unit.
+__device__ __forceinline__ uint64_t wave_uniform(uint64_t x) {
+    uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
+    return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// bf16 is the upper half of an fp32: widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_one(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Two fp32 -> a pair of bf16, nearest-even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t to_bf16_pair(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    bf16x2 b = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+__device__ __forceinline__ uint16_t to_bf16_one(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// One AdamW element (the arithmetic stated in include/lema.h).
+__device__ __forceinline__ void adamw_elem(float &w, float &m, float &v, float g,
+                                           const AdamwConsts &c) {
+#pragma clang fp contract(off)
+    const float w_decayed = w * c.decay;
+    const float m_new = c.b1 * m + c.omb1 * g;
+    const float v_new = c.b2 * v + c.omb2 * (g * g);
+    const float denom = __builtin_sqrtf(v_new) * c.inv_bc2_root + c.eps;
+    w = w_decayed - c.step_size * (m_new / denom);
+    m = m_new;
+    v = v_new;
+}
+
+__device__ __forceinline__ float accum_elem(float acc, float g, bool overwrite) {
+#pragma clang fp contract(off)
+    return overwrite ? g : acc + g;
+}
+
+// ------------------------------------------------------ segment walker
+
+// Walk tiles blockIdx.x, blockIdx.x + gridDim.x, ... of the launch table.
+// Tiles are numbered segment after segment, so the segment of a workgroup's
+// successive tiles never decreases; the walk moves forward through a window
+// of kWindow segment records staged in LDS, restaging when it leaves it.
+// All control flow here is uniform across the workgroup.
+template <class TileFn>
+__device__ __forceinline__ void walk_tiles(const void *table, int nseg,
+                                           uint32_t total_tiles, TileFn &fn) {
+    __shared__ uint32_t s_tile_begin[kWindow + 1];
+    __shared__ SegRec s_rec[kWindow];
+
+    const uint32_t *g_tile_begin = static_cast<const uint32_t *>(table);
+    const SegRec *g_rec = reinterpret_cast<const SegRec *>(
+        static_cast<const char *>(table) + table_tiles_bytes(nseg));
+
+    int win = -1;   // index of the segment held in s_rec[0]; -1 = none staged
+    int seg = 0;
+    for (uint32_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
+        for (;;) {
+            if (win < 0 || seg - win >= kWindow) {
+                __syncthreads();                      // previous window no longer read
+                for (int i = threadIdx.x; i <= kWindow; i += kBlock) {
+                    const int s = seg + i;
+                    s_tile_begin[i] = s <= nseg ? g_tile_begin[s] : 0xFFFFFFFFu;
+                }
+                const int nrec = min(kWindow, nseg - seg);
+                const uint4 *src = reinterpret_cast<const uint4 *>(g_rec + seg);
+                uint4 *dst = reinterpret_cast<uint4 *>(s_rec);
+                for (int i = threadIdx.x; i < nrec * 4; i += kBlock) dst[i] = src[i];
+                __syncthreads();
+                win = seg;
+            }
+            if (t < s_tile_begin[seg - win + 1]) break;
+            ++seg;
+        }
+        fn(s_rec[seg - win], t - s_tile_begin[seg - win]);
+    }
+}
+
+// ------------------------------------------------------------- AdamW
+
+template <bool kGradF32, bool kDelta>
+struct AdamwTile {
+    AdamwConsts c;
+
+    __device__ __forceinline__ void operator()(const SegRec &r, uint32_t local_tile) const {
+        const uint64_t master = wave_uniform(r.p[0]);
+        const uint64_t m = wave_uniform(r.p[1]);
+        const uint64_t v = wave_uniform(r.p[2]);
+        const uint64_t grad = wave_uniform(r.p[3]);
+        const uint64_t weight = wave_uniform(r.p[4]);
+        const uint64_t orig = wave_uniform(r.p[5]);
+        const uint64_t delta = wave_uniform(r.p[6]);
+        const int64_t numel = static_cast<int64_t>(wave_uniform(static_cast<uint64_t>(r.numel)));
+        const int64_t base = int64_t(local_tile) * kTile;
+
+        const bool has_delta = kDelta && delta != 0;
+        const uint64_t fp32_bits = master | m | v | (kGradF32 ? grad : 0) | (has_delta ? delta : 0);
+        const uint64_t bf16_bits = (kGradF32 ? 0 : grad) | weight | (has_delta ? orig : 0);
+        const bool vector_ok = base + kTile <= numel && (fp32_bits & 15) == 0 && (bf16_bits & 7) == 0;
+
+        if (vector_ok) {
+            if (has_delta)
+                vector_tile<true>(master, m, v, grad, weight, orig, delta, base);
+            else
+                vector_tile<false>(master, m, v, grad, weight, orig, delta, base);
+        } else {
+            element_tile(master, m, v, grad, weight, has_delta ? orig : 0, has_delta ? delta : 0,
+                         base, numel);
+        }
+    }
+
+    template <bool kHasDelta>
+    __device__ __forceinline__ void vector_tile(uint64_t master, uint64_t m, uint64_t v,
+                                                uint64_t grad, uint64_t weight, uint64_t orig,
+                                                uint64_t delta, int64_t base) const {
+        f32x4 w4[kUnroll], m4[kUnroll], v4[kUnroll], g4[kUnroll];
+        u32x2 o2[kUnroll];
+        const int64_t lane = int64_t(threadIdx.x) * kVec;
+
+        // all loads of the tile first, so each lane has them in flight together
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;   // vector index
+            w4[u] = as_global<gf32x4>(master)[q];
+            m4[u] = as_global<gf32x4>(m)[q];
+            v4[u] = as_global<gf32x4>(v)[q];
+            if constexpr (kGradF32) {
+                g4[u] = as_global<gf32x4>(grad)[q];
+            } else {
+                const u32x2 gb = as_global<gu32x2>(grad)[q];
+                g4[u] = f32x4{bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
+            }
+            if constexpr (kHasDelta) o2[u] = as_global<gu32x2>(orig)[q];
+        }
+
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
+            f32x4 w = w4[u], mm = m4[u], vv = v4[u];
+            const f32x4 g = g4[u];
+#pragma unroll
+            for (int k = 0; k < kVec; ++k) {
+                float wk = w[k], mk = mm[k], vk = vv[k];
+                adamw_elem(wk, mk, vk, g[k], c);
+                w[k] = wk;
+                mm[k] = mk;
+                vv[k] = vk;
+            }
+            as_global<gf32x4>(master)[q] = w;
+            as_global<gf32x4>(m)[q] = mm;
+            as_global<gf32x4>(v)[q] = vv;
+            as_global<gu32x2>(weight)[q] = u32x2{to_bf16_pair(w.x, w.y), to_bf16_pair(w.z, w.w)};
+            if constexpr (kHasDelta) {
+#pragma clang fp contract(off)
+                const u32x2 o = o2[u];
+                const f32x4 d = {w.x - bf16_lo(o.x), w.y - bf16_hi(o.x),
+                                 w.z - bf16_lo(o.y), w.w - bf16_hi(o.y)};
+                as_global<gf32x4>(delta)[q] = d;
+            }
+        }
+    }
+
+    // Partial tiles and segments whose arrays are not vector-aligned: one
+    // element at a time, same lane-to-element map as the vector path.
+    __device__ __forceinline__ void element_tile(uint64_t master, uint64_t m, uint64_t v,
+                                                 uint64_t grad, uint64_t weight, uint64_t orig,
+                                                 uint64_t delta, int64_t base,
+                                                 int64_t numel) const {
+#pragma clang fp contract(off)
+        const int64_t lane = int64_t(threadIdx.x) * kVec;
+        for (int u = 0; u < kUnroll; ++u) {
+            for (int k = 0; k < kVec; ++k) {
+                const int64_t e = base + u * (kBlock * kVec) + lane + k;
+                if (e >= numel) continue;
+                float g;
+                if constexpr (kGradF32)
+                    g = as_global<gfloat>(grad)[e];
+                else
+                    g = bf16_one(as_global<gu16>(grad)[e]);
+                float w = as_global<gfloat>(master)[e];
+                float mm = as_global<gfloat>(m)[e];
+                float vv = as_global<gfloat>(v)[e];
+                adamw_elem(w, mm, vv, g, c);
+                as_global<gfloat>(master)[e] = w;
+                as_global<gfloat>(m)[e] = mm;
+                as_global<gfloat>(v)[e] = vv;
+                as_global<gu16>(weight)[e] = to_bf16_one(w);
+                if (delta != 0) as_global<gfloat>(delta)[e] = w - bf16_one(as_global<gu16>(orig)[e]);
+            }
+        }
+    }
+};
+
+template <bool kGradF32, bool kDelta>
+__global__ __launch_bounds__(kBlock) void adamw_mta_kernel(const void *table, int nseg,
+                                                           uint32_t total_tiles,
+                                                           AdamwConsts c) {
+    AdamwTile<kGradF32, kDelta> fn{c};
+    walk_tiles(table, nseg, total_tiles, fn);
+}
+
+// ------------------------------------------------------ accumulation
+
+template <bool kOverwrite>
+struct AccumTile {
+    __device__ __forceinline__ void operator()(const SegRec &r, uint32_t local_tile) const {
+        const uint64_t acc = wave_uniform(r.p[0]);
+        const uint64_t g = wave_uniform(r.p[1]);
+        const int64_t numel = static_cast<int64_t>(wave_uniform(static_cast<uint64_t>(r.numel)));
+        const int64_t base = int64_t(local_tile) * kTile;
+        const int64_t lane = int64_t(threadIdx.x) * kVec;
+        const bool vector_ok = base + kTile <= numel && (acc & 15) == 0 && (g & 7) == 0;
+
+        if (vector_ok) {
+            f32x4 a4[kUnroll];
+            u32x2 g2[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
+                if constexpr (!kOverwrite) a4[u] = as_global<gf32x4>(acc)[q];
+                g2[u] = as_global<gu32x2>(g)[q];
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
+                const f32x4 gf = {bf16_lo(g2[u].x), bf16_hi(g2[u].x), bf16_lo(g2[u].y),
+                                  bf16_hi(g2[u].y)};
+                f32x4 out;
+                if constexpr (kOverwrite) {
+                    out = gf;
+                } else {
+#pragma unroll
+                    for (int k = 0; k < kVec; ++k) out[k] = accum_elem(a4[u][k], gf[k], false);
+                }
+                as_global<gf32x4>(acc)[q] = out;
+            }
+        } else {
+            for (int u = 0; u < kUnroll; ++u) {
+                for (int k = 0; k < kVec; ++k) {
+                    const int64_t e = base + u * (kBlock * kVec) + lane + k;
+                    if (e >= numel) continue;
+                    const float ge = bf16_one(as_global<gu16>(g)[e]);
+                    as_global<gfloat>(acc)[e] =
+                        kOverwrite ? ge : accum_elem(as_global<gfloat>(acc)[e], ge, false);
+                }
+            }
+        }
+    }
+};
+
+template <bool kOverwrite>
+__global__ __launch_bounds__(kBlock) void accum_mta_kernel(const void *table, int nseg,
+                                                           uint32_t total_tiles) {
+    AccumTile<kOverwrite> fn;
+    walk_tiles(table, nseg, total_tiles, fn);
+}
+
+// ------------------------------------------------- measurement aids
+
+// Plain 16-byte-per-lane copy: the practical bandwidth ceiling and the
+// reference for HBM byte counters.
+__global__ __launch_bounds__(kBlock) void copy_kernel(const f32x4 *__restrict__ src,
+                                                      f32x4 *__restrict__ dst, size_t n16) {
+    const size_t stride = size_t(gridDim.x) * kBlock;
+    for (size_t i = size_t(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// The division, square root and bf16 rounding exactly as the AdamW kernel
+// compiles them, for checking against IEEE results on the host.
+__global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restrict__ a,
+                                                            const float *__restrict__ b,
+                                                            float *__restrict__ quot,
+                                                            float *__restrict__ root,
+                                                            uint16_t *__restrict__ bf16,
+                                                            int64_t n) {
+#pragma clang fp contract(off)
+    const int64_t stride = int64_t(gridDim.x) * kBlock;
+    for (int64_t i = int64_t(blockIdx.x) * kBlock + threadIdx.x; i < n; i += stride) {
+        quot[i] = a[i] / b[i];
+        root[i] = __builtin_sqrtf(a[i]);
+        bf16[i] = to_bf16_one(a[i]);
+    }
+}
+
+}  // namespace
+
+// Launches go through hipLaunchKernel, which returns the launch status
+// directly instead of through the thread's sticky last-error slot.
+hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, bool grad_f32,
+                        bool with_delta, const AdamwConsts &c, int grid, hipStream_t stream) {
+    const void *fn;
+    if (grad_f32)
+        fn = with_delta ? reinterpret_cast<const void *>(&adamw_mta_kernel<true, true>)
+                        : reinterpret_cast<const void *>(&adamw_mta_kernel<true, false>);
+    else
+        fn = with_delta ? reinterpret_cast<const void *>(&adamw_mta_kernel<false, true>)
+                        : reinterpret_cast<const void *>(&adamw_mta_kernel<false, false>);
+    AdamwConsts consts = c;
+    void *args[] = {&table, &nseg, &total_tiles, &consts};
+    return hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+}
+
+hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles, bool overwrite,
+                        int grid, hipStream_t stream) {
+    const void *fn = overwrite ? reinterpret_cast<const void *>(&accum_mta_kernel<true>)
+                               : reinterpret_cast<const void *>(&accum_mta_kernel<false>);
+    void *args[] = {&table, &nseg, &total_tiles};
+    return hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+}
+
+hipError_t launch_copy(const void *src, void *dst, size_t bytes, int grid, hipStream_t stream) {
+    const f32x4 *s = static_cast<const f32x4 *>(src);
+    f32x4 *d = static_cast<f32x4 *>(dst);
+    size_t n16 = bytes / 16;
+    void *args[] = {&s, &d, &n16};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&copy_kernel), dim3(grid), dim3(kBlock),
+                           args, 0, stream);
+}
+
+hipError_t launch_fp32_probe(const float *a, const float *b, float *quot, float *root,
+                             uint16_t *bf16, int64_t n, hipStream_t stream) {
+    int64_t blocks = (n + kBlock - 1) / kBlock;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    void *args[] = {&a, &b, &quot, &root, &bf16, &n};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&fp32_probe_kernel),
+                           dim3(unsigned(blocks)), dim3(kBlock), args, 0, stream);
+}
+
+}  // namespace lema

@@ -1,0 +1,200 @@
+"""C-ABI checks that need no GPU: exports, constant derivation, validation.
+
+Validation happens before any HIP call, so descriptors with made-up device
+addresses exercise every error path here without touching a GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from optimizer_step_lema_amd import _native as N
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("lema.h", "lema_measure.h")]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return N.load()
+
+
+def declared_functions():
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[\w\s\*]+?\b(lema_\w+)\s*\(", text, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == {s[0] for s in N.SIGNATURES}
+
+
+def test_status_strings(lib):
+    for code in range(-8, 1):
+        assert lib.lema_status_string(code)
+    assert b"unknown" in lib.lema_status_string(-99)
+    assert lib.lema_version() >= 100
+
+
+def args(**kw):
+    base = dict(lr=1e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=10,
+                grad_dtype=N.LEMA_GRAD_BF16, reserved=0)
+    base.update(kw)
+    return N.AdamwArgs(**base)
+
+
+@pytest.mark.parametrize("hp", [
+    dict(), dict(lr=3e-3, weight_decay=0.1), dict(beta1=0.0, beta2=0.0),
+    dict(beta1=0.5, beta2=0.25, eps=1e-6), dict(lr=0.0), dict(weight_decay=0.0)])
+@pytest.mark.parametrize("t", [1, 2, 10, 50, 100, 12345, 2 ** 40 + 1])
+def test_constants_match_oracle(lib, hp, t):
+    """The host derivation (C++) and the oracle's (C) give identical fp32 bits."""
+    a = args(step=t, **hp)
+    out = N.AdamwConsts()
+    assert lib.lema_adamw_constants(ctypes.byref(a), ctypes.byref(out)) == N.LEMA_OK
+    got = np.array([getattr(out, f) for f, _ in N.AdamwConsts._fields_], np.float32)
+    ref = oracle.adamw_constants(a.lr, a.beta1, a.beta2, a.eps, a.weight_decay, t)
+    assert got.view(np.uint32).tolist() == ref.view(np.uint32).tolist()
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(step=0), N.LEMA_ERR_HPARAM), (dict(step=-3), N.LEMA_ERR_HPARAM),
+    (dict(beta1=1.0), N.LEMA_ERR_HPARAM), (dict(beta2=-0.1), N.LEMA_ERR_HPARAM),
+    (dict(eps=0.0), N.LEMA_ERR_HPARAM), (dict(lr=-1e-4), N.LEMA_ERR_HPARAM),
+    (dict(weight_decay=-1.0), N.LEMA_ERR_HPARAM), (dict(lr=float("nan")), N.LEMA_ERR_HPARAM),
+    (dict(eps=float("inf")), N.LEMA_ERR_HPARAM), (dict(reserved=1), N.LEMA_ERR_HPARAM),
+    (dict(grad_dtype=2), N.LEMA_ERR_DTYPE), (dict(grad_dtype=-1), N.LEMA_ERR_DTYPE)])
+def test_hparam_errors(lib, bad, code):
+    a = args(**bad)
+    out = N.AdamwConsts()
+    assert lib.lema_adamw_constants(ctypes.byref(a), ctypes.byref(out)) == code
+    seg = fake_seg(0x10000, 64)
+    assert lib.lema_adamw_step(ctypes.byref(seg), 1, ctypes.byref(a), None) == code
+
+
+def fake_seg(base, n, delta=False, gsize=2):
+    """Descriptor with made-up, disjoint, well-aligned device addresses."""
+    stride = 1 << 24
+    p = [base + k * stride for k in range(7)]
+    return N.AdamwSeg(p[0], p[1], p[2], p[3], p[4], p[5] if delta else 0,
+                      p[6] if delta else 0, n)
+
+
+def call(lib, segs, a=None):
+    arr = (N.AdamwSeg * max(1, len(segs)))(*segs)
+    return lib.lema_adamw_step(arr, len(segs), ctypes.byref(a or args()), None)
+
+
+def test_null_and_size_errors(lib):
+    a = args()
+    assert lib.lema_adamw_step(None, 1, ctypes.byref(a), None) == N.LEMA_ERR_NULL
+    assert lib.lema_adamw_step(None, -1, ctypes.byref(a), None) == N.LEMA_ERR_SIZE
+    seg = fake_seg(1 << 32, 10)
+    assert lib.lema_adamw_step(ctypes.byref(seg), 1, None, None) == N.LEMA_ERR_NULL
+    s = fake_seg(1 << 32, -1)
+    assert call(lib, [s]) == N.LEMA_ERR_SIZE
+    for field in ("master", "exp_avg", "exp_avg_sq", "grad", "weight_bf16"):
+        s = fake_seg(1 << 32, 10)
+        setattr(s, field, 0)
+        assert call(lib, [s]) == N.LEMA_ERR_NULL, field
+    s = fake_seg(1 << 32, 10, delta=True)
+    s.delta = 0
+    assert call(lib, [s]) == N.LEMA_ERR_NULL            # orig without delta
+    s = fake_seg(1 << 32, 10, delta=True)
+    s.orig_bf16 = 0
+    assert call(lib, [s]) == N.LEMA_ERR_NULL            # delta without orig
+    # the error in the second segment is still found before anything runs
+    assert call(lib, [fake_seg(1 << 32, 10), fake_seg(1 << 40, -5)]) == N.LEMA_ERR_SIZE
+
+
+def test_alignment_errors(lib):
+    s = fake_seg(1 << 32, 10)
+    s.master += 2
+    assert call(lib, [s]) == N.LEMA_ERR_ALIGN
+    s = fake_seg(1 << 32, 10)
+    s.weight_bf16 += 1
+    assert call(lib, [s]) == N.LEMA_ERR_ALIGN
+    s = fake_seg(1 << 32, 10)
+    s.grad += 2                                          # bf16 grad: 2-byte aligned is fine
+    assert call(lib, [s]) != N.LEMA_ERR_ALIGN
+    s = fake_seg(1 << 32, 10)
+    s.grad += 2
+    assert call(lib, [s], args(grad_dtype=N.LEMA_GRAD_FP32)) == N.LEMA_ERR_ALIGN
+
+
+def test_overlap_errors(lib):
+    s = fake_seg(1 << 32, 1000)
+    s.exp_avg = s.master + 400                           # m inside master
+    assert call(lib, [s]) == N.LEMA_ERR_OVERLAP
+    s = fake_seg(1 << 32, 1000)
+    s.weight_bf16 = s.grad + 100                         # written over a read array
+    assert call(lib, [s]) == N.LEMA_ERR_OVERLAP
+    a, b = fake_seg(1 << 32, 1000), fake_seg(1 << 32, 1000)
+    b2 = fake_seg((1 << 32) + 8 * 1000, 1000)            # shifted copy: disjoint? no, same stride
+    assert call(lib, [a, b]) == N.LEMA_ERR_OVERLAP       # two segments on the same arrays
+    # two segments may read one gradient buffer (read-only overlap is allowed)
+    c, d = fake_seg(1 << 32, 1000), fake_seg(1 << 40, 1000)
+    d.grad = c.grad
+    assert call(lib, [c, d]) != N.LEMA_ERR_OVERLAP
+    del b2
+
+
+def test_empty_calls_are_noops_without_gpu(lib):
+    assert lib.lema_adamw_step(None, 0, ctypes.byref(args()), None) == N.LEMA_OK
+    z = fake_seg(1 << 32, 0)
+    z.master = 0                                         # numel 0: pointers may be NULL
+    assert call(lib, [z]) == N.LEMA_OK
+    acc0 = N.AccumSeg(0, 0, 0)
+    assert lib.lema_grad_accum(ctypes.byref(acc0), 1, 0, None) == N.LEMA_OK
+
+
+def test_accum_validation(lib):
+    assert lib.lema_grad_accum(None, 2, 1, None) == N.LEMA_ERR_NULL
+    assert lib.lema_grad_accum(None, -2, 1, None) == N.LEMA_ERR_SIZE
+    s = N.AccumSeg(0, 1 << 33, 10)
+    assert lib.lema_grad_accum(ctypes.byref(s), 1, 1, None) == N.LEMA_ERR_NULL
+    s = N.AccumSeg((1 << 32) + 2, 1 << 33, 10)
+    assert lib.lema_grad_accum(ctypes.byref(s), 1, 1, None) == N.LEMA_ERR_ALIGN
+    s = N.AccumSeg(1 << 32, (1 << 32) + 8, 10)
+    assert lib.lema_grad_accum(ctypes.byref(s), 1, 1, None) == N.LEMA_ERR_OVERLAP
+    s = N.AccumSeg(1 << 32, 1 << 33, -1)
+    assert lib.lema_grad_accum(ctypes.byref(s), 1, 1, None) == N.LEMA_ERR_SIZE
+
+
+def test_slot_and_measure_validation(lib):
+    h = ctypes.c_void_p()
+    assert lib.lema_slot_pool_create(None, 1 << 20, 2, 1, 2, ctypes.byref(h)) == N.LEMA_ERR_NULL
+    assert lib.lema_slot_pool_create(1 << 32, 1 << 20, 1, 1, 2, ctypes.byref(h)) == N.LEMA_ERR_SIZE
+    assert lib.lema_slot_pool_create(1 << 32, 1000, 2, 1, 2, ctypes.byref(h)) == N.LEMA_ERR_SIZE
+    assert lib.lema_slot_pool_create(1 << 32, 1 << 20, 2, 1, 1, ctypes.byref(h)) == N.LEMA_ERR_NULL
+    assert lib.lema_slot_pool_destroy(None) == N.LEMA_OK
+    assert lib.lema_slot_stream(None, None, 0, ctypes.byref(args()), None) == N.LEMA_ERR_NULL
+    assert lib.lema_measure_copy(None, 1 << 32, 16, 0, None) == N.LEMA_ERR_NULL
+    assert lib.lema_measure_copy(1 << 32, 1 << 33, 15, 0, None) == N.LEMA_ERR_SIZE
+    assert lib.lema_measure_copy((1 << 32) + 4, 1 << 33, 16, 0, None) == N.LEMA_ERR_ALIGN
+    assert lib.lema_measure_copy(1 << 32, (1 << 32) + 16, 64, 0, None) == N.LEMA_ERR_OVERLAP
+    assert lib.lema_probe_fp32(0, 0, 0, 0, 0, -1, None) == N.LEMA_ERR_SIZE
+    assert lib.lema_probe_fp32(0, 0, 0, 0, 0, 5, None) == N.LEMA_ERR_NULL
+    assert lib.lema_host_alloc(None, 16) == N.LEMA_ERR_NULL
+    assert lib.lema_host_free(None) == N.LEMA_OK
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-GPU error path")
+def test_valid_call_without_gpu_reports_hip_error(lib):
+    s = fake_seg(1 << 32, 10)
+    assert call(lib, [s]) == N.LEMA_ERR_HIP
+    assert lib.lema_last_hip_error() != 0

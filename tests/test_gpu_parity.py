@@ -1,0 +1,469 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every test compares element by element on the same seeded bytes: the inputs
+are drawn on the GPU (synth), copied to the host for the oracle, then the
+GPU runs the step in place.  See tests/parity.py for the bar.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import (compare_bf16, compare_f32, oracle_consts, oracle_segment, to_np)
+
+pytestmark = pytest.mark.gpu
+HP = synth.HPARAMS
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def L():
+    import optimizer_step_lema_amd as lema
+    return lema
+
+
+def _f32(n, sigma, seed, offset=0, square=False):
+    t = synth.normal(n + offset, sigma, seed, DEV)
+    if square:
+        t.mul_(t)
+    return t[offset:]
+
+
+def _bf16(n, sigma, seed, offset=0):
+    return synth.normal(n + offset, sigma, seed, DEV).to(torch.bfloat16)[offset:]
+
+
+def _empty(n, dtype, offset=0):
+    return torch.empty(n + offset, dtype=dtype, device=DEV)[offset:]
+
+
+def build_segments(L, sizes, seed, *, grad_f32=False, delta=(), offset=0, fresh=False,
+                   grad_sigma=1e-3):
+    """Device segments plus host snapshots of their inputs."""
+    segs, snaps = [], []
+    for i, n in enumerate(sizes):
+        s = seed * 1000 + 10 * i
+        master = _f32(n, 0.02, s + 0, offset)
+        if fresh:
+            m = torch.zeros(n + offset, device=DEV)[offset:]
+            v = torch.zeros(n + offset, device=DEV)[offset:]
+        else:
+            m = _f32(n, 1e-4, s + 1, offset)
+            v = _f32(n, 1e-3, s + 2, offset, square=True)
+        grad = _f32(n, 3e-3, s + 3, offset) if grad_f32 else _bf16(n, grad_sigma, s + 3, offset)
+        weight = _empty(n, torch.bfloat16, offset)
+        orig = dl = None
+        if delta == "all" or i in delta:
+            orig = master.to(torch.bfloat16)
+            if offset:
+                o2 = _empty(n, torch.bfloat16, offset)
+                o2.copy_(orig)
+                orig = o2
+            dl = _empty(n, torch.float32, offset)
+        segs.append(L.AdamwSegment(master, m, v, grad, weight, orig, dl))
+        snaps.append({"master": to_np(master), "m": to_np(m), "v": to_np(v), "grad": to_np(grad),
+                      "orig": None if orig is None else to_np(orig)})
+    return segs, snaps
+
+
+def check_segments(segs, snaps, consts, label=""):
+    for i, (s, h) in enumerate(zip(segs, snaps)):
+        ref = oracle_segment(h["master"], h["m"], h["v"], h["grad"], consts, h["orig"])
+        tag = f"{label}seg{i}(n={s.master.numel()})"
+        compare_f32(to_np(s.master), ref["master"], tag + ".master")
+        compare_f32(to_np(s.exp_avg), ref["m"], tag + ".m")
+        compare_f32(to_np(s.exp_avg_sq), ref["v"], tag + ".v")
+        compare_bf16(to_np(s.weight), ref["weight"], tag + ".weight")
+        if s.delta is not None:
+            compare_f32(to_np(s.delta), ref["delta"], tag + ".delta")
+
+
+# ------------------------------------------------------------ primitives
+
+def test_fp32_primitives_are_ieee(L):
+    """Division, sqrt and bf16 rounding as compiled in the kernel vs the host's IEEE ops."""
+    rng = np.random.default_rng(0)
+    n = 1 << 22
+    a_bits = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+    b_bits = rng.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+    # structured cases: subnormals, near-one, powers of two, rounding ties for bf16
+    k = 1 << 16
+    a_bits[:k] = rng.integers(0, 1 << 23, k)                       # positive subnormals
+    b_bits[k:2 * k] = rng.integers(0, 1 << 23, k)                  # subnormal divisors
+    a_bits[2 * k:3 * k] = (0x3F800000 + rng.integers(-4096, 4096, k)).astype(np.uint32)
+    a_bits[3 * k:4 * k] = (rng.integers(0, 1 << 16, k) << 16 | 0x8000).astype(np.uint32)
+    a = a_bits.view(np.float32)
+    b = b_bits.view(np.float32)
+    q, r, h = L.probe_fp32(torch.from_numpy(a).to(DEV), torch.from_numpy(b).to(DEV))
+    with np.errstate(all="ignore"):
+        q_ref = a / b
+        r_ref = np.sqrt(a)
+    compare_f32(to_np(q), q_ref, "a/b")
+    compare_f32(to_np(r), r_ref, "sqrt(a)")
+    compare_bf16(to_np(h), oracle.rne16(a), "bf16(a)")
+
+
+# ---------------------------------------------------------- ragged lists
+
+RAGGED = [0, 1, 3, 4, 5, 7, 8, 9, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097,
+          100003, 3 * 65536 + 17]
+
+
+@pytest.mark.parametrize("offset", [0, 1, 3])
+@pytest.mark.parametrize("grad_f32", [False, True])
+def test_ragged_segments(L, offset, grad_f32):
+    delta = {i for i in range(len(RAGGED)) if i % 2 == 0}
+    segs, snaps = build_segments(L, RAGGED, 7 + offset, grad_f32=grad_f32, delta=delta,
+                                 offset=offset)
+    L.adamw_step(segs, step=37, **HP)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(HP, 37))
+
+
+def test_many_segments_cross_lds_windows(L):
+    """More segments than one LDS window, with empty ones in between."""
+    rng = np.random.default_rng(3)
+    sizes = [int(x) for x in rng.choice([0, 1, 17, 2048, 5000, 40000], size=300)]
+    segs, snaps = build_segments(L, sizes, 11, delta=set(range(0, 300, 3)))
+    L.adamw_step(segs, step=5, **HP)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(HP, 5))
+
+
+@pytest.mark.parametrize("hp", [dict(HP, lr=0.0), dict(HP, beta1=0.0, beta2=0.0),
+                                dict(HP, lr=3e-3, weight_decay=0.1, eps=1e-6)])
+def test_hyperparameter_variants(L, hp):
+    segs, snaps = build_segments(L, [4096 * 3 + 5, 777], 21, delta="all")
+    L.adamw_step(segs, step=3, **hp)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(hp, 3))
+
+
+def test_special_values(L):
+    """NaN, infinities, subnormals and signed zeros flow as in the oracle."""
+    n = 4096 + 19
+    segs, snaps = build_segments(L, [n], 31, delta="all")
+    s = segs[0]
+    specials = torch.tensor([float("nan"), float("inf"), -float("inf"), 0.0, -0.0, 1e-40, -1e-42,
+                             3.4e38], device=DEV)
+    k = len(specials)
+    for t, stride in ((s.master, 3), (s.exp_avg, 5), (s.exp_avg_sq, 7)):
+        t[1:1 + k * stride:stride] = specials
+    s.exp_avg_sq.abs_()                          # the caller keeps v >= 0
+    gb = torch.tensor([0x7FC0, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x8001, 0x7F7F],
+                      dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    s.grad[2:2 + 11 * k:11] = gb
+    snaps[0] = {"master": to_np(s.master), "m": to_np(s.exp_avg), "v": to_np(s.exp_avg_sq),
+                "grad": to_np(s.grad), "orig": to_np(s.orig)}
+    L.adamw_step(segs, step=2, **HP)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(HP, 2))
+
+
+def test_golden_fixture(L):
+    import json
+    import os
+    doc = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "adamw_small.json")))
+    hp = doc["hyperparameters"]
+
+    def arr(hx):
+        if len(hx[0]) == 8:
+            return torch.tensor(np.array([int(h, 16) for h in hx], np.uint32).view(np.int32),
+                                device=DEV).view(torch.float32)
+        return torch.tensor(np.array([int(h, 16) for h in hx], np.uint16).view(np.int16),
+                            device=DEV).view(torch.bfloat16)
+
+    case = doc["cases"][0]
+    ins, exp = case["inputs"], case["expect"]
+    sizes = doc["segment_sizes"]
+    full = {k: arr(v) for k, v in ins.items()}
+    outs_w = torch.empty(sum(sizes), dtype=torch.bfloat16, device=DEV)
+    outs_d = torch.empty(sum(sizes), dtype=torch.float32, device=DEV)
+    segs, o = [], 0
+    for n in sizes:
+        sl = slice(o, o + n)
+        segs.append(L.AdamwSegment(full["master"][sl], full["m"][sl], full["v"][sl],
+                                   full["grad"][sl], outs_w[sl], full["orig"][sl], outs_d[sl]))
+        o += n
+    L.adamw_step(segs, step=case["step"], **hp)
+    torch.cuda.synchronize()
+    for name, t in (("master", full["master"]), ("m", full["m"]), ("v", full["v"]),
+                    ("delta", outs_d)):
+        compare_f32(to_np(t), to_np(arr(exp[name])), name)
+    compare_bf16(to_np(outs_w), to_np(arr(exp["weight"])), "weight")
+
+    # the accumulated-gradient case: three micro-batches then an fp32-grad step
+    case = doc["cases"][1]
+    ins, exp = case["inputs"], case["expect"]
+    acc = torch.empty(sum(sizes), dtype=torch.float32, device=DEV)
+    for k, mb in enumerate(ins["micro_batches"]):
+        L.grad_accum([L.AccumSegment(acc, arr(mb))], overwrite=(k == 0))
+    torch.cuda.synchronize()
+    compare_f32(to_np(acc), to_np(arr(exp["acc"])), "acc")
+    master, m, v = arr(ins["master"]), arr(ins["m"]), arr(ins["v"])
+    w = torch.empty(sum(sizes), dtype=torch.bfloat16, device=DEV)
+    L.adamw_step([L.AdamwSegment(master, m, v, acc, w)], step=case["step"], **hp)
+    torch.cuda.synchronize()
+    for name, t in (("master", master), ("m", m), ("v", v)):
+        compare_f32(to_np(t), to_np(arr(exp[name])), "acc-case " + name)
+    compare_bf16(to_np(w), to_np(arr(exp["weight"])), "acc-case weight")
+
+
+# ------------------------------------------------------------ accumulation
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_accumulation_eight_microbatches(L, offset):
+    sizes = [1, 2048, 2049, 65536 + 3, 0, 300001]
+    accs = [_empty(n, torch.float32, offset) for n in sizes]
+    grads = [[_bf16(n, 1e-3, 500 + 10 * i + k, offset) for i, n in enumerate(sizes)]
+             for k in range(8)]
+    grads[0][1][:4] = torch.tensor([-0.0, 0.0, float("inf"), -1e-40], device=DEV).to(torch.bfloat16)
+    for k in range(8):
+        L.grad_accum([L.AccumSegment(a, g) for a, g in zip(accs, grads[k])], overwrite=(k == 0))
+        if k == 0:
+            torch.cuda.synchronize()
+            assert to_np(accs[1]).view(np.uint32)[0] == 0x80000000      # -0 kept
+    torch.cuda.synchronize()
+    for i, n in enumerate(sizes):
+        ref = np.empty(n, np.float32)
+        oracle.grad_accum(ref, to_np(grads[0][i]), overwrite=True)
+        for k in range(1, 8):
+            oracle.grad_accum(ref, to_np(grads[k][i]), overwrite=False)
+        compare_f32(to_np(accs[i]), ref, f"acc{i}")
+
+
+# ------------------------------------------------------- invariances
+
+def _clone_segs(L, segs):
+    out = []
+    for s in segs:
+        out.append(L.AdamwSegment(s.master.clone(), s.exp_avg.clone(), s.exp_avg_sq.clone(),
+                                  s.grad.clone(), torch.empty_like(s.weight),
+                                  None if s.orig is None else s.orig.clone(),
+                                  None if s.delta is None else torch.empty_like(s.delta)))
+    return out
+
+
+def _same(a, b):
+    return torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a.view(torch.int16),
+                       b.view(torch.int32) if b.dtype == torch.float32 else b.view(torch.int16))
+
+
+def test_resume_invariance(L):
+    """P11: T steps straight == T1 steps, host round trip of the state, T-T1 steps."""
+    sizes = [5000, 2048 * 7, 333]
+    segs, _ = build_segments(L, sizes, 41)
+    twin = _clone_segs(L, segs)
+    grads = [[_bf16(n, 1e-3, 900 + 10 * t + i) for i, n in enumerate(sizes)] for t in range(6)]
+    for t in range(6):
+        for s, g in zip(segs, grads[t]):
+            s.grad.copy_(g)
+        L.adamw_step(segs, step=t + 1, **HP)
+    for t in range(6):
+        if t == 2:   # checkpoint: state to the host and back into fresh buffers
+            torch.cuda.synchronize()
+            host = [(s.master.cpu(), s.exp_avg.cpu(), s.exp_avg_sq.cpu()) for s in twin]
+            twin = [L.AdamwSegment(h[0].to(DEV), h[1].to(DEV), h[2].to(DEV), s.grad,
+                                   torch.empty_like(s.weight)) for h, s in zip(host, twin)]
+        for s, g in zip(twin, grads[t]):
+            s.grad.copy_(g)
+        L.adamw_step(twin, step=t + 1, **HP)
+    torch.cuda.synchronize()
+    for a, b in zip(segs, twin):
+        for x, y in ((a.master, b.master), (a.exp_avg, b.exp_avg), (a.exp_avg_sq, b.exp_avg_sq),
+                     (a.weight, b.weight)):
+            assert _same(x, y)
+
+
+def test_split_permute_pack_invariance(L):
+    """P12: one call == per-segment calls == permuted == split == packed == unaligned views."""
+    sizes = [768 * 2304, 2304, 4099, 1]
+    segs, _ = build_segments(L, sizes, 51, delta="all")
+    variants = {k: _clone_segs(L, segs) for k in ("one", "each", "perm", "split", "packed")}
+    L.adamw_step(variants["one"], step=1, **HP)
+    for s in variants["each"]:
+        L.adamw_step([s], step=1, **HP)
+    L.adamw_step(list(reversed(variants["perm"])), step=1, **HP)
+    halves = []
+    for s in variants["split"]:
+        h = s.master.numel() // 2
+        for sl in (slice(0, h), slice(h, None)):
+            halves.append(L.AdamwSegment(s.master[sl], s.exp_avg[sl], s.exp_avg_sq[sl], s.grad[sl],
+                                         s.weight[sl], s.orig[sl], s.delta[sl]))
+    L.adamw_step([x for x in halves if x.master.numel() > 0], step=1, **HP)
+    # packed: W and b of the first "layer" in one contiguous buffer, one descriptor
+    p = variants["packed"]
+    cat = lambda a, b: torch.cat([a, b])
+    packed = L.AdamwSegment(cat(p[0].master, p[1].master), cat(p[0].exp_avg, p[1].exp_avg),
+                            cat(p[0].exp_avg_sq, p[1].exp_avg_sq), cat(p[0].grad, p[1].grad),
+                            torch.empty(sizes[0] + sizes[1], dtype=torch.bfloat16, device=DEV),
+                            cat(p[0].orig, p[1].orig),
+                            torch.empty(sizes[0] + sizes[1], device=DEV))
+    L.adamw_step([packed] + p[2:], step=1, **HP)
+    torch.cuda.synchronize()
+    ref = variants["one"]
+    for name in ("each", "perm", "split"):
+        for a, b in zip(ref, variants[name]):
+            for f in ("master", "exp_avg", "exp_avg_sq", "weight", "delta"):
+                assert _same(getattr(a, f), getattr(b, f)), (name, f)
+    for f in ("master", "exp_avg", "exp_avg_sq", "weight", "delta"):
+        assert _same(cat(getattr(ref[0], f), getattr(ref[1], f)), getattr(packed, f)), f
+
+
+def test_table_cache_many_lists_and_streams(L):
+    """More distinct segment lists than cached tables, alternating two streams.
+
+    Call j steps a prefix of segment j % 3 whose length shrinks with j, so
+    nearly every call has a table of its own and the cache must evict."""
+    s2 = torch.cuda.Stream()
+    base, snaps = build_segments(L, [3000, 70001, 2048], 61)
+    calls = []
+    for j in range(48):
+        i = j % 3
+        n = base[i].master.numel() - (j % 24)
+        b = base[i]
+        seg = L.AdamwSegment(b.master[:n], b.exp_avg[:n], b.exp_avg_sq[:n], b.grad[:n],
+                             b.weight[:n])
+        extra = [] if j % 5 else [L.AdamwSegment(base[(i + 1) % 3].master[:7],
+                                                 base[(i + 1) % 3].exp_avg[:7],
+                                                 base[(i + 1) % 3].exp_avg_sq[:7],
+                                                 base[(i + 1) % 3].grad[:7],
+                                                 base[(i + 1) % 3].weight[:7])]
+        if j % 2:
+            s2.wait_stream(torch.cuda.current_stream())
+            L.adamw_step([seg] + extra, step=j + 1, stream=s2, **HP)
+            torch.cuda.current_stream().wait_stream(s2)
+        else:
+            L.adamw_step([seg] + extra, step=j + 1, **HP)
+        calls.append(([(i, n)] + ([((i + 1) % 3, 7)] if extra else []), j + 1))
+    torch.cuda.synchronize()
+    state = [{k: h[k].copy() for k in ("master", "m", "v", "grad")} for h in snaps]
+    for w in state:
+        w["w"] = None
+    wout = [np.zeros(len(h["master"]), np.uint16) for h in snaps]
+    touched = [np.zeros(len(h["master"]), bool) for h in snaps]
+    for items, t in calls:
+        c = oracle_consts(HP, t)
+        for i, n in items:
+            st = state[i]
+            out = oracle_segment(st["master"][:n], st["m"][:n], st["v"][:n], st["grad"][:n], c)
+            st["master"][:n], st["m"][:n], st["v"][:n] = out["master"], out["m"], out["v"]
+            wout[i][:n] = out["weight"]
+            touched[i][:n] = True
+    for i, s in enumerate(base):
+        compare_f32(to_np(s.master), state[i]["master"], f"cache seg{i} master")
+        compare_f32(to_np(s.exp_avg_sq), state[i]["v"], f"cache seg{i} v")
+        compare_bf16(to_np(s.weight)[touched[i]], wout[i][touched[i]], f"cache seg{i} weight")
+
+
+# ------------------------------------------------------ full workloads
+
+def _workload_segments(L, w, with_orig, device_grads=1):
+    segs = []
+    for i in range(len(w.segments)):
+        st = synth.make_segment_state(w, i, DEV, with_orig=with_orig, grads=device_grads)
+        n = w.numels[i]
+        segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], st["grads"][0],
+                                   torch.empty(n, dtype=torch.bfloat16, device=DEV),
+                                   st.get("orig"),
+                                   torch.empty(n, device=DEV) if with_orig else None))
+    return segs
+
+
+@pytest.mark.parametrize("with_delta", [False, True])
+def test_gpt2_cattn_full(L, with_delta):
+    """GPT-2-small c_attn, first two layers, t=1 from m=v=0: every element."""
+    w = synth.WORKLOADS["gpt2_cattn_first2"]
+    segs = _workload_segments(L, w, with_delta)
+    snaps = [{"master": to_np(s.master), "m": to_np(s.exp_avg), "v": to_np(s.exp_avg_sq),
+              "grad": to_np(s.grad), "orig": None if s.orig is None else to_np(s.orig)}
+             for s in segs]
+    L.adamw_step(segs, step=w.step, **HP)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(HP, w.step), "gpt2 ")
+
+
+def test_llama7b_attn_last4_full(L):
+    """Llama-2-7B q,k,v,o of the last 4 layers, t=100: all 268M elements."""
+    w = synth.WORKLOADS["llama7b_attn_last4"]
+    segs = _workload_segments(L, w, True)
+    snaps = [{"master": to_np(s.master), "m": to_np(s.exp_avg), "v": to_np(s.exp_avg_sq),
+              "grad": to_np(s.grad), "orig": to_np(s.orig)} for s in segs]
+    L.adamw_step(segs, step=w.step, **HP)
+    torch.cuda.synchronize()
+    consts = oracle_consts(HP, w.step)
+    for i in range(len(segs)):
+        check_segments(segs[i:i + 1], snaps[i:i + 1], consts, f"attn{i} ")
+        snaps[i] = None
+    del segs
+    torch.cuda.empty_cache()
+
+
+def test_llama7b_layer_accumulate_then_step(L):
+    """One Llama-2-7B layer: 8 bf16 micro-batches into fp32, then the step (t=50)."""
+    w = synth.WORKLOADS["llama7b_layer"]
+    accs, segs, snaps = [], [], []
+    for i in range(len(w.segments)):
+        st = synth.make_segment_state(w, i, DEV)
+        n = w.numels[i]
+        acc = torch.empty(n, device=DEV)
+        accs.append((acc, st["grads"]))
+        segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], acc,
+                                   torch.empty(n, dtype=torch.bfloat16, device=DEV)))
+        snaps.append({"master": to_np(st["master"]), "m": to_np(st["m"]), "v": to_np(st["v"])})
+    for k in range(w.microbatches):
+        L.grad_accum([L.AccumSegment(a, g[k]) for a, g in accs], overwrite=(k == 0))
+    torch.cuda.synchronize()
+    for i, (acc, grads) in enumerate(accs):
+        ref = np.empty(acc.numel(), np.float32)
+        for k, g in enumerate(grads):
+            oracle.grad_accum(ref, to_np(g), overwrite=(k == 0))
+        compare_f32(to_np(acc), ref, f"layer acc{i}")
+        snaps[i]["grad"] = ref
+    L.adamw_step(segs, step=w.step, **HP)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(HP, w.step), "layer ")
+    del accs, segs
+    torch.cuda.empty_cache()
+
+
+def test_llama7b_full_resident_sampled(L):
+    """Whole 7B shape resident (291 tensors, ~148 GB with delta): two steps
+    (t=10 with delta, t=11 without), checked on sampled elements of every
+    tensor, including each tensor's first and last 2048."""
+    w = synth.WORKLOADS["llama7b_full"]
+    segs = _workload_segments(L, w, True)
+    rng = np.random.default_rng(4)
+    idx = []
+    for n in w.numels:
+        i = np.unique(np.concatenate([np.arange(min(n, 2048)), np.arange(max(0, n - 2048), n),
+                                      rng.integers(0, n, 8192)]))
+        idx.append(torch.from_numpy(i).to(DEV))
+
+    def gather(s, i, fields):
+        return {f: to_np(getattr(s, f)[i]) for f in fields}
+
+    for step, with_delta in ((w.step, True), (w.step + 1, False)):
+        before = [gather(s, i, ("master", "exp_avg", "exp_avg_sq", "grad", "orig"))
+                  for s, i in zip(segs, idx)]
+        run = segs if with_delta else [L.AdamwSegment(s.master, s.exp_avg, s.exp_avg_sq, s.grad,
+                                                      s.weight) for s in segs]
+        L.adamw_step(run, step=step, **HP)
+        torch.cuda.synchronize()
+        consts = oracle_consts(HP, step)
+        for k, (s, i, b) in enumerate(zip(segs, idx, before)):
+            ref = oracle_segment(b["master"], b["exp_avg"], b["exp_avg_sq"], b["grad"], consts,
+                                 b["orig"] if with_delta else None)
+            after = gather(s, i, ("master", "exp_avg", "exp_avg_sq", "weight", "delta"))
+            tag = f"7b t={step} seg{k}"
+            compare_f32(after["master"], ref["master"], tag + ".master")
+            compare_f32(after["exp_avg"], ref["m"], tag + ".m")
+            compare_f32(after["exp_avg_sq"], ref["v"], tag + ".v")
+            compare_bf16(after["weight"], ref["weight"], tag + ".weight")
+            if with_delta:
+                compare_f32(after["delta"], ref["delta"], tag + ".delta")
+    del segs
+    torch.cuda.empty_cache()
