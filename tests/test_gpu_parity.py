@@ -153,8 +153,8 @@ def test_special_values(L):
     for t, stride in ((s.master, 3), (s.exp_avg, 5), (s.exp_avg_sq, 7)):
         t[1:1 + k * stride:stride] = specials
     s.exp_avg_sq.abs_()                          # the caller keeps v >= 0
-    gb = torch.tensor([0x7FC0, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x8001, 0x7F7F],
-                      dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    pats = np.array([0x7FC0, 0x7F80, 0xFF80, 0x0000, 0x8000, 0x0001, 0x8001, 0x7F7F], np.uint16)
+    gb = torch.from_numpy(pats.view(np.int16)).to(DEV).view(torch.bfloat16)
     s.grad[2:2 + 11 * k:11] = gb
     snaps[0] = {"master": to_np(s.master), "m": to_np(s.exp_avg), "v": to_np(s.exp_avg_sq),
                 "grad": to_np(s.grad), "orig": to_np(s.orig)}
@@ -413,7 +413,8 @@ def test_llama7b_layer_accumulate_then_step(L):
         accs.append((acc, st["grads"]))
         segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], acc,
                                    torch.empty(n, dtype=torch.bfloat16, device=DEV)))
-        snaps.append({"master": to_np(st["master"]), "m": to_np(st["m"]), "v": to_np(st["v"])})
+        snaps.append({"master": to_np(st["master"]), "m": to_np(st["m"]), "v": to_np(st["v"]),
+                      "orig": None})
     for k in range(w.microbatches):
         L.grad_accum([L.AccumSegment(a, g[k]) for a, g in accs], overwrite=(k == 0))
     torch.cuda.synchronize()
