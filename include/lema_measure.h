@@ -21,17 +21,16 @@ extern "C" {
 #endif
 
 /*
- * Plain device-to-device copy of `bytes` bytes with the AdamW kernel's
- * access width (16 bytes per lane), on a persistent grid of
- * `blocks_per_cu` x (compute units) workgroups (0 = the AdamW default).
- * Reads `bytes` and writes `bytes`: the read+write bandwidth ceiling, and the
- * known-size reference for HBM byte counters.  src and dst must be 16-byte
- * aligned, bytes a multiple of 16, the ranges disjoint.
+ * Plain device-to-device copy of `bytes` bytes: one 16-byte vector per lane,
+ * one workgroup per 4 KiB, nontemporal loads and stores (the best plain-copy
+ * shape measured on MI355X).  Reads `bytes` and writes `bytes`: the
+ * read+write bandwidth ceiling, and the known-size reference for HBM byte
+ * counters.  src and dst must be 16-byte aligned, bytes a multiple of 16,
+ * the ranges disjoint.
  * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_ALIGN, LEMA_ERR_OVERLAP,
  * LEMA_ERR_HIP.
  */
-lema_status lema_measure_copy(const void *src, void *dst, size_t bytes, int32_t blocks_per_cu,
-                              void *stream);
+lema_status lema_measure_copy(const void *src, void *dst, size_t bytes, void *stream);
 
 /*
  * Elementwise a/b, sqrt(a) and bf16 nearest-even of a over n elements,
@@ -41,8 +40,9 @@ lema_status lema_measure_copy(const void *src, void *dst, size_t bytes, int32_t 
 lema_status lema_probe_fp32(const float *a, const float *b, float *quot, float *root,
                             uint16_t *bf16, int64_t n, void *stream);
 
-/* Compute units of the current device and the AdamW launch's workgroups per CU. */
-lema_status lema_device_info(int32_t *compute_units, int32_t *blocks_per_cu);
+/* Compute units of the current device and the elements one workgroup takes
+ * per tile in the AdamW and accumulation kernels. */
+lema_status lema_device_info(int32_t *compute_units, int32_t *tile_elements);
 
 #ifdef __cplusplus
 }

@@ -75,7 +75,7 @@ SIGNATURES = [
                                ctypes.POINTER(StreamStats)]),
     ("lema_host_alloc", i32, [ctypes.POINTER(vp), ctypes.c_size_t]),
     ("lema_host_free", i32, [vp]),
-    ("lema_measure_copy", i32, [vp, vp, ctypes.c_size_t, i32, vp]),
+    ("lema_measure_copy", i32, [vp, vp, ctypes.c_size_t, vp]),
     ("lema_probe_fp32", i32, [vp, vp, vp, vp, vp, i64, vp]),
     ("lema_device_info", i32, [ctypes.POINTER(i32), ctypes.POINTER(i32)]),
 ]

@@ -207,11 +207,9 @@ class SlotPool:
 
 # ------------------------------------------------------- measurement aids
 
-def measure_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, blocks_per_cu: int = 0,
-                 stream=None) -> None:
+def measure_copy(src: torch.Tensor, dst: torch.Tensor, nbytes: int, stream=None) -> None:
     N.check(N.load().lema_measure_copy(src.data_ptr(), dst.data_ptr(), int(nbytes),
-                                       int(blocks_per_cu), _stream_handle(stream)),
-            "lema_measure_copy")
+                                       _stream_handle(stream)), "lema_measure_copy")
 
 
 def probe_fp32(a: torch.Tensor, b: torch.Tensor, stream=None):
@@ -228,6 +226,6 @@ def probe_fp32(a: torch.Tensor, b: torch.Tensor, stream=None):
 
 
 def device_info() -> dict:
-    cus, bpc = ctypes.c_int32(), ctypes.c_int32()
-    N.check(N.load().lema_device_info(ctypes.byref(cus), ctypes.byref(bpc)), "lema_device_info")
-    return {"compute_units": cus.value, "blocks_per_cu": bpc.value}
+    cus, tile = ctypes.c_int32(), ctypes.c_int32()
+    N.check(N.load().lema_device_info(ctypes.byref(cus), ctypes.byref(tile)), "lema_device_info")
+    return {"compute_units": cus.value, "tile_elements": tile.value}

@@ -9,7 +9,6 @@
 
 #include <algorithm>
 #include <cmath>
-#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -161,7 +160,6 @@ struct DeviceState {
     std::mutex mu;
     bool ready = false;
     int cu_count = 0;
-    int blocks_per_cu = 8;
     uint64_t clock = 0;
     TableEntry entries[kCacheEntries];
 };
@@ -180,10 +178,6 @@ lema_status device_state(DeviceState **out, int *device) {
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_failed(e);
         d.cu_count = cus > 0 ? cus : 1;
-        if (const char *env = std::getenv("LEMA_BLOCKS_PER_CU")) {
-            const int v = std::atoi(env);
-            if (v >= 1 && v <= 64) d.blocks_per_cu = v;
-        }
         d.ready = true;
     }
     *out = &d;
@@ -290,11 +284,6 @@ uint64_t count_tiles(const std::vector<SegRec> &recs) {
     return tiles;
 }
 
-int grid_for(const DeviceState &d, uint64_t tiles) {
-    const uint64_t cap = uint64_t(d.cu_count) * uint64_t(d.blocks_per_cu);
-    return static_cast<int>(std::max<uint64_t>(1, std::min(tiles, cap)));
-}
-
 }  // namespace
 
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
@@ -314,7 +303,7 @@ lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts
     st = acquire_table(*d, tb.bytes, stream, &t);
     if (st != LEMA_OK) return st;
     hipError_t e = launch_adamw(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_f32,
-                                with_delta, c, grid_for(*d, tb.total_tiles), stream);
+                                with_delta, c, stream);
     lema_status rel = release_table(*d, t, stream);
     if (e != hipSuccess) return hip_failed(e);
     return rel;
@@ -334,7 +323,7 @@ lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
     st = acquire_table(*d, tb.bytes, stream, &t);
     if (st != LEMA_OK) return st;
     hipError_t e = launch_accum(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), overwrite,
-                                grid_for(*d, tb.total_tiles), stream);
+                                stream);
     lema_status rel = release_table(*d, t, stream);
     if (e != hipSuccess) return hip_failed(e);
     return rel;
@@ -460,21 +449,16 @@ lema_status lema_host_free(void *p) {
 
 // ------------------------------------------------ measurement aids
 
-lema_status lema_measure_copy(const void *src, void *dst, size_t bytes, int32_t blocks_per_cu,
-                              void *stream) {
+lema_status lema_measure_copy(const void *src, void *dst, size_t bytes, void *stream) {
     if (src == nullptr || dst == nullptr) return LEMA_ERR_NULL;
-    if (bytes == 0 || (bytes % 16) != 0 || blocks_per_cu < 0 || blocks_per_cu > 64) return LEMA_ERR_SIZE;
+    if (bytes == 0 || (bytes % 16) != 0) return LEMA_ERR_SIZE;
     if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) != 0)
         return LEMA_ERR_ALIGN;
     std::vector<Span> spans;
     add_span(spans, src, static_cast<int64_t>(bytes), 1, false);
     add_span(spans, dst, static_cast<int64_t>(bytes), 1, true);
     if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
-    DeviceState *d = nullptr;
-    lema_status st = device_state(&d, nullptr);
-    if (st != LEMA_OK) return st;
-    const int bpc = blocks_per_cu > 0 ? blocks_per_cu : d->blocks_per_cu;
-    hipError_t e = launch_copy(src, dst, bytes, d->cu_count * bpc, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LEMA_OK : hip_failed(e);
 }
 
@@ -487,13 +471,13 @@ lema_status lema_probe_fp32(const float *a, const float *b, float *quot, float *
     return e == hipSuccess ? LEMA_OK : hip_failed(e);
 }
 
-lema_status lema_device_info(int32_t *compute_units, int32_t *blocks_per_cu) {
-    if (compute_units == nullptr || blocks_per_cu == nullptr) return LEMA_ERR_NULL;
+lema_status lema_device_info(int32_t *compute_units, int32_t *tile_elements) {
+    if (compute_units == nullptr || tile_elements == nullptr) return LEMA_ERR_NULL;
     DeviceState *d = nullptr;
     lema_status st = device_state(&d, nullptr);
     if (st != LEMA_OK) return st;
     *compute_units = d->cu_count;
-    *blocks_per_cu = d->blocks_per_cu;
+    *tile_elements = static_cast<int32_t>(kTile);
     return LEMA_OK;
 }
 

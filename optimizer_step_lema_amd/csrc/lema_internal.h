@@ -16,7 +16,9 @@ constexpr int kBlock = 256;
 constexpr int kVec = 4;
 constexpr int kUnroll = 2;
 constexpr int64_t kTile = int64_t(kBlock) * kVec * kUnroll;   // 2048 elements
-constexpr int kWindow = 64;   // segment records a workgroup stages in LDS at once
+// One workgroup per tile; at most this many workgroups per launch (keeps the
+// grid's work-item count well inside 32 bits).
+constexpr uint32_t kMaxBlocksPerLaunch = 1u << 22;
 
 // One segment of the launch table: up to seven array pointers and the length.
 //   AdamW : p = {master, m, v, grad, weight_bf16, orig_bf16, delta}
@@ -43,16 +45,15 @@ struct AdamwConsts {
 };
 
 // Kernel launches (asynchronous on `stream`).  `table` is the device copy of
-// the launch table; `grid` workgroups walk tiles 0 .. total_tiles-1.
+// the launch table; one workgroup runs per tile 0 .. total_tiles-1.
 hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles,
                         bool grad_f32, bool with_delta, const AdamwConsts &c,
-                        int grid, hipStream_t stream);
+                        hipStream_t stream);
 hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
-                        bool overwrite, int grid, hipStream_t stream);
+                        bool overwrite, hipStream_t stream);
 
 // Measurement aids (include/lema_measure.h).
-hipError_t launch_copy(const void *src, void *dst, size_t bytes, int grid,
-                       hipStream_t stream);
+hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 hipError_t launch_fp32_probe(const float *a, const float *b, float *quot,
                              float *root, uint16_t *bf16, int64_t n,
                              hipStream_t stream);

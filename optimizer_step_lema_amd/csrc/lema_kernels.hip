@@ -1,18 +1,25 @@
 // lema_kernels.hip -- gfx950 kernels of the mixed-precision AdamW path.
 //
-// adamw_mta_kernel : one AdamW step over a list of segments (LEMA README,
+// adamw_tile_kernel : one AdamW step over a list of segments (LEMA README,
 //   "Quick Start": torch.optim.AdamW; "Selective Full Fine-Tuning": per-layer
 //   AdamW over fp32 master, m and v, fp32 delta for checkpoints; LLMScale
 //   fine-tuning VRAM page: bf16 weight and gradient next to fp32 states).
-// accum_mta_kernel : fp32 accumulation of a bf16 micro-batch gradient
+// accum_tile_kernel : fp32 accumulation of a bf16 micro-batch gradient
 //   (README, "Selective Full Fine-Tuning": fp32 gradient accumulation).
 //
 // Both are elementwise and bound by HBM bandwidth, so there is no MFMA and
 // no LDS tiling of data: each lane streams 4 contiguous elements per access
 // (16-byte fp32 / 8-byte bf16 vector loads and stores, contiguous across the
-// wavefront).  A persistent grid walks the tiles of all segments in order;
-// each workgroup keeps a window of the segment table in LDS and finds the
-// segment of its next tile by a forward walk over the tile prefix sums.
+// wavefront), with the nontemporal hint since no byte is touched twice.
+//
+// One workgroup per tile, not a persistent grid: on gfx9 the vector-memory
+// counter also counts stores, so a persistent loop would wait for a tile's
+// stores before its next loads could be waited on; short-lived workgroups
+// leave their stores in flight and a fresh workgroup takes the CU slot.  The
+// tiles of all segments are numbered consecutively; a workgroup finds its
+// segment by a binary search over the tile prefix sums of the launch table
+// (wave-uniform, so it runs on scalar loads that hit the scalar cache) and
+// reads the segment's record with one scalar load.
 //
 // Arithmetic: binary32 only, no contraction into FMA (this file is built with
 // -ffp-contract=off and every arithmetic function also carries the pragma),
@@ -20,6 +27,8 @@
 // subnormals kept, bf16 output rounded to nearest even by gfx950's
 // v_cvt_pk_bf16_f32.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "lema_internal.h"
 
@@ -46,14 +55,6 @@ __device__ __forceinline__ T *as_global(uint64_t addr) {
 }
 
 // ------------------------------------------------------------- helpers
-
-// A value that is the same in every lane, moved to scalar registers so that
-// address arithmetic on it stays on the scalar unit.
-__device__ __forceinline__ uint64_t wave_uniform(uint64_t x) {
-    uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
-    uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x >> 32));
-    return (static_cast<uint64_t>(hi) << 32) | lo;
-}
 
 // bf16 is the upper half of an fp32: widening is a shift.
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
@@ -88,45 +89,43 @@ __device__ __forceinline__ float accum_elem(float acc, float g, bool overwrite) 
     return overwrite ? g : acc + g;
 }
 
-// ------------------------------------------------------ segment walker
+// ---------------------------------------------------------- segment lookup
 
-// Walk tiles blockIdx.x, blockIdx.x + gridDim.x, ... of the launch table.
-// Tiles are numbered segment after segment, so the segment of a workgroup's
-// successive tiles never decreases; the walk moves forward through a window
-// of kWindow segment records staged in LDS, restaging when it leaves it.
-// All control flow here is uniform across the workgroup.
-template <class TileFn>
-__device__ __forceinline__ void walk_tiles(const void *table, int nseg,
-                                           uint32_t total_tiles, TileFn &fn) {
-    __shared__ uint32_t s_tile_begin[kWindow + 1];
-    __shared__ SegRec s_rec[kWindow];
+// Nontemporal vector loads and stores through global-address-space pointers.
+template <class T>
+__device__ __forceinline__ T ld_nt(uint64_t base, int64_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const LEMA_GLOBAL T *>(base) + i);
+}
+template <class T>
+__device__ __forceinline__ void st_nt(uint64_t base, int64_t i, T v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<LEMA_GLOBAL T *>(base) + i);
+}
 
-    const uint32_t *g_tile_begin = static_cast<const uint32_t *>(table);
-    const SegRec *g_rec = reinterpret_cast<const SegRec *>(
-        static_cast<const char *>(table) + table_tiles_bytes(nseg));
-
-    int win = -1;   // index of the segment held in s_rec[0]; -1 = none staged
-    int seg = 0;
-    for (uint32_t t = blockIdx.x; t < total_tiles; t += gridDim.x) {
-        for (;;) {
-            if (win < 0 || seg - win >= kWindow) {
-                __syncthreads();                      // previous window no longer read
-                for (int i = threadIdx.x; i <= kWindow; i += kBlock) {
-                    const int s = seg + i;
-                    s_tile_begin[i] = s <= nseg ? g_tile_begin[s] : 0xFFFFFFFFu;
-                }
-                const int nrec = min(kWindow, nseg - seg);
-                const uint4 *src = reinterpret_cast<const uint4 *>(g_rec + seg);
-                uint4 *dst = reinterpret_cast<uint4 *>(s_rec);
-                for (int i = threadIdx.x; i < nrec * 4; i += kBlock) dst[i] = src[i];
-                __syncthreads();
-                win = seg;
-            }
-            if (t < s_tile_begin[seg - win + 1]) break;
-            ++seg;
-        }
-        fn(s_rec[seg - win], t - s_tile_begin[seg - win]);
+// The segment holding tile t: the last s with tile_begin[s] <= t.  The
+// table guarantees tile_begin[0] = 0 <= t < tile_begin[nseg].
+__device__ __forceinline__ int find_segment(const uint32_t *__restrict__ tile_begin, int nseg,
+                                            uint32_t t) {
+    int lo = 0, hi = nseg;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_begin[mid] <= t)
+            lo = mid;
+        else
+            hi = mid;
     }
+    return lo;
+}
+
+// Run fn(record, tile-within-segment) for the tile of this workgroup.
+template <class TileFn>
+__device__ __forceinline__ void tile_of_block(const void *table, int nseg, uint32_t tile0,
+                                              const TileFn &fn) {
+    const uint32_t *tile_begin = static_cast<const uint32_t *>(table);
+    const SegRec *recs = reinterpret_cast<const SegRec *>(static_cast<const char *>(table) +
+                                                          table_tiles_bytes(nseg));
+    const uint32_t t = tile0 + blockIdx.x;
+    const int s = find_segment(tile_begin, nseg, t);
+    fn(recs[s], t - tile_begin[s]);
 }
 
 // ------------------------------------------------------------- AdamW
@@ -136,14 +135,9 @@ struct AdamwTile {
     AdamwConsts c;
 
     __device__ __forceinline__ void operator()(const SegRec &r, uint32_t local_tile) const {
-        const uint64_t master = wave_uniform(r.p[0]);
-        const uint64_t m = wave_uniform(r.p[1]);
-        const uint64_t v = wave_uniform(r.p[2]);
-        const uint64_t grad = wave_uniform(r.p[3]);
-        const uint64_t weight = wave_uniform(r.p[4]);
-        const uint64_t orig = wave_uniform(r.p[5]);
-        const uint64_t delta = wave_uniform(r.p[6]);
-        const int64_t numel = static_cast<int64_t>(wave_uniform(static_cast<uint64_t>(r.numel)));
+        const uint64_t master = r.p[0], m = r.p[1], v = r.p[2], grad = r.p[3];
+        const uint64_t weight = r.p[4], orig = r.p[5], delta = r.p[6];
+        const int64_t numel = r.numel;
         const int64_t base = int64_t(local_tile) * kTile;
 
         const bool has_delta = kDelta && delta != 0;
@@ -174,16 +168,16 @@ struct AdamwTile {
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;   // vector index
-            w4[u] = as_global<gf32x4>(master)[q];
-            m4[u] = as_global<gf32x4>(m)[q];
-            v4[u] = as_global<gf32x4>(v)[q];
+            w4[u] = ld_nt<f32x4>(master, q);
+            m4[u] = ld_nt<f32x4>(m, q);
+            v4[u] = ld_nt<f32x4>(v, q);
             if constexpr (kGradF32) {
-                g4[u] = as_global<gf32x4>(grad)[q];
+                g4[u] = ld_nt<f32x4>(grad, q);
             } else {
-                const u32x2 gb = as_global<gu32x2>(grad)[q];
+                const u32x2 gb = ld_nt<u32x2>(grad, q);
                 g4[u] = f32x4{bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
             }
-            if constexpr (kHasDelta) o2[u] = as_global<gu32x2>(orig)[q];
+            if constexpr (kHasDelta) o2[u] = ld_nt<u32x2>(orig, q);
         }
 
 #pragma unroll
@@ -199,16 +193,16 @@ struct AdamwTile {
                 mm[k] = mk;
                 vv[k] = vk;
             }
-            as_global<gf32x4>(master)[q] = w;
-            as_global<gf32x4>(m)[q] = mm;
-            as_global<gf32x4>(v)[q] = vv;
-            as_global<gu32x2>(weight)[q] = u32x2{to_bf16_pair(w.x, w.y), to_bf16_pair(w.z, w.w)};
+            st_nt<f32x4>(master, q, w);
+            st_nt<f32x4>(m, q, mm);
+            st_nt<f32x4>(v, q, vv);
+            st_nt<u32x2>(weight, q, u32x2{to_bf16_pair(w.x, w.y), to_bf16_pair(w.z, w.w)});
             if constexpr (kHasDelta) {
 #pragma clang fp contract(off)
                 const u32x2 o = o2[u];
                 const f32x4 d = {w.x - bf16_lo(o.x), w.y - bf16_hi(o.x),
                                  w.z - bf16_lo(o.y), w.w - bf16_hi(o.y)};
-                as_global<gf32x4>(delta)[q] = d;
+                st_nt<f32x4>(delta, q, d);
             }
         }
     }
@@ -245,11 +239,9 @@ struct AdamwTile {
 };
 
 template <bool kGradF32, bool kDelta>
-__global__ __launch_bounds__(kBlock) void adamw_mta_kernel(const void *table, int nseg,
-                                                           uint32_t total_tiles,
-                                                           AdamwConsts c) {
-    AdamwTile<kGradF32, kDelta> fn{c};
-    walk_tiles(table, nseg, total_tiles, fn);
+__global__ __launch_bounds__(kBlock) void adamw_tile_kernel(const void *table, int nseg,
+                                                            uint32_t tile0, AdamwConsts c) {
+    tile_of_block(table, nseg, tile0, AdamwTile<kGradF32, kDelta>{c});
 }
 
 // ------------------------------------------------------ accumulation
@@ -257,9 +249,8 @@ __global__ __launch_bounds__(kBlock) void adamw_mta_kernel(const void *table, in
 template <bool kOverwrite>
 struct AccumTile {
     __device__ __forceinline__ void operator()(const SegRec &r, uint32_t local_tile) const {
-        const uint64_t acc = wave_uniform(r.p[0]);
-        const uint64_t g = wave_uniform(r.p[1]);
-        const int64_t numel = static_cast<int64_t>(wave_uniform(static_cast<uint64_t>(r.numel)));
+        const uint64_t acc = r.p[0], g = r.p[1];
+        const int64_t numel = r.numel;
         const int64_t base = int64_t(local_tile) * kTile;
         const int64_t lane = int64_t(threadIdx.x) * kVec;
         const bool vector_ok = base + kTile <= numel && (acc & 15) == 0 && (g & 7) == 0;
@@ -270,8 +261,8 @@ struct AccumTile {
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
                 const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
-                if constexpr (!kOverwrite) a4[u] = as_global<gf32x4>(acc)[q];
-                g2[u] = as_global<gu32x2>(g)[q];
+                if constexpr (!kOverwrite) a4[u] = ld_nt<f32x4>(acc, q);
+                g2[u] = ld_nt<u32x2>(g, q);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
@@ -285,7 +276,7 @@ struct AccumTile {
 #pragma unroll
                     for (int k = 0; k < kVec; ++k) out[k] = accum_elem(a4[u][k], gf[k], false);
                 }
-                as_global<gf32x4>(acc)[q] = out;
+                st_nt<f32x4>(acc, q, out);
             }
         } else {
             for (int u = 0; u < kUnroll; ++u) {
@@ -302,20 +293,22 @@ struct AccumTile {
 };
 
 template <bool kOverwrite>
-__global__ __launch_bounds__(kBlock) void accum_mta_kernel(const void *table, int nseg,
-                                                           uint32_t total_tiles) {
-    AccumTile<kOverwrite> fn;
-    walk_tiles(table, nseg, total_tiles, fn);
+__global__ __launch_bounds__(kBlock) void accum_tile_kernel(const void *table, int nseg,
+                                                            uint32_t tile0) {
+    tile_of_block(table, nseg, tile0, AccumTile<kOverwrite>{});
 }
 
 // ------------------------------------------------- measurement aids
 
-// Plain 16-byte-per-lane copy: the practical bandwidth ceiling and the
+// Plain copy, one 16-byte vector per lane and one workgroup per 4 KiB, with
+// nontemporal loads and stores: the best plain-copy shape measured on the
+// GPU, used as the practical read+write ceiling and as the known-size
 // reference for HBM byte counters.
 __global__ __launch_bounds__(kBlock) void copy_kernel(const f32x4 *__restrict__ src,
-                                                      f32x4 *__restrict__ dst, size_t n16) {
-    const size_t stride = size_t(gridDim.x) * kBlock;
-    for (size_t i = size_t(blockIdx.x) * kBlock + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+                                                      f32x4 *__restrict__ dst, size_t n16,
+                                                      size_t block0) {
+    const size_t i = (block0 + blockIdx.x) * kBlock + threadIdx.x;
+    if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 // The division, square root and bf16 rounding exactly as the AdamW kernel
@@ -338,36 +331,56 @@ __global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restr
 }  // namespace
 
 // Launches go through hipLaunchKernel, which returns the launch status
-// directly instead of through the thread's sticky last-error slot.
+// directly instead of through the thread's sticky last-error slot.  Grids
+// larger than kMaxBlocksPerLaunch are split into consecutive launches.
 hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, bool grad_f32,
-                        bool with_delta, const AdamwConsts &c, int grid, hipStream_t stream) {
+                        bool with_delta, const AdamwConsts &c, hipStream_t stream) {
     const void *fn;
     if (grad_f32)
-        fn = with_delta ? reinterpret_cast<const void *>(&adamw_mta_kernel<true, true>)
-                        : reinterpret_cast<const void *>(&adamw_mta_kernel<true, false>);
+        fn = with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<true, true>)
+                        : reinterpret_cast<const void *>(&adamw_tile_kernel<true, false>);
     else
-        fn = with_delta ? reinterpret_cast<const void *>(&adamw_mta_kernel<false, true>)
-                        : reinterpret_cast<const void *>(&adamw_mta_kernel<false, false>);
+        fn = with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<false, true>)
+                        : reinterpret_cast<const void *>(&adamw_tile_kernel<false, false>);
     AdamwConsts consts = c;
-    void *args[] = {&table, &nseg, &total_tiles, &consts};
-    return hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+    for (uint32_t tile0 = 0; tile0 < total_tiles;) {
+        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
+        void *args[] = {&table, &nseg, &tile0, &consts};
+        hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, 0, stream);
+        if (e != hipSuccess) return e;
+        tile0 += n;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles, bool overwrite,
-                        int grid, hipStream_t stream) {
-    const void *fn = overwrite ? reinterpret_cast<const void *>(&accum_mta_kernel<true>)
-                               : reinterpret_cast<const void *>(&accum_mta_kernel<false>);
-    void *args[] = {&table, &nseg, &total_tiles};
-    return hipLaunchKernel(fn, dim3(grid), dim3(kBlock), args, 0, stream);
+                        hipStream_t stream) {
+    const void *fn = overwrite ? reinterpret_cast<const void *>(&accum_tile_kernel<true>)
+                               : reinterpret_cast<const void *>(&accum_tile_kernel<false>);
+    for (uint32_t tile0 = 0; tile0 < total_tiles;) {
+        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
+        void *args[] = {&table, &nseg, &tile0};
+        hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, 0, stream);
+        if (e != hipSuccess) return e;
+        tile0 += n;
+    }
+    return hipSuccess;
 }
 
-hipError_t launch_copy(const void *src, void *dst, size_t bytes, int grid, hipStream_t stream) {
+hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t stream) {
     const f32x4 *s = static_cast<const f32x4 *>(src);
     f32x4 *d = static_cast<f32x4 *>(dst);
     size_t n16 = bytes / 16;
-    void *args[] = {&s, &d, &n16};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&copy_kernel), dim3(grid), dim3(kBlock),
-                           args, 0, stream);
+    const size_t blocks = (n16 + kBlock - 1) / kBlock;
+    for (size_t block0 = 0; block0 < blocks;) {
+        const size_t n = std::min<size_t>(blocks - block0, kMaxBlocksPerLaunch);
+        void *args[] = {&s, &d, &n16, &block0};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&copy_kernel),
+                                       dim3(unsigned(n)), dim3(kBlock), args, 0, stream);
+        if (e != hipSuccess) return e;
+        block0 += n;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_fp32_probe(const float *a, const float *b, float *quot, float *root,

@@ -183,10 +183,10 @@ def test_slot_and_measure_validation(lib):
     assert lib.lema_slot_pool_create(1 << 32, 1 << 20, 2, 1, 1, ctypes.byref(h)) == N.LEMA_ERR_NULL
     assert lib.lema_slot_pool_destroy(None) == N.LEMA_OK
     assert lib.lema_slot_stream(None, None, 0, ctypes.byref(args()), None) == N.LEMA_ERR_NULL
-    assert lib.lema_measure_copy(None, 1 << 32, 16, 0, None) == N.LEMA_ERR_NULL
-    assert lib.lema_measure_copy(1 << 32, 1 << 33, 15, 0, None) == N.LEMA_ERR_SIZE
-    assert lib.lema_measure_copy((1 << 32) + 4, 1 << 33, 16, 0, None) == N.LEMA_ERR_ALIGN
-    assert lib.lema_measure_copy(1 << 32, (1 << 32) + 16, 64, 0, None) == N.LEMA_ERR_OVERLAP
+    assert lib.lema_measure_copy(None, 1 << 32, 16, None) == N.LEMA_ERR_NULL
+    assert lib.lema_measure_copy(1 << 32, 1 << 33, 15, None) == N.LEMA_ERR_SIZE
+    assert lib.lema_measure_copy((1 << 32) + 4, 1 << 33, 16, None) == N.LEMA_ERR_ALIGN
+    assert lib.lema_measure_copy(1 << 32, (1 << 32) + 16, 64, None) == N.LEMA_ERR_OVERLAP
     assert lib.lema_probe_fp32(0, 0, 0, 0, 0, -1, None) == N.LEMA_ERR_SIZE
     assert lib.lema_probe_fp32(0, 0, 0, 0, 0, 5, None) == N.LEMA_ERR_NULL
     assert lib.lema_host_alloc(None, 16) == N.LEMA_ERR_NULL

@@ -1,0 +1,141 @@
+"""GPU tests of the slot-pool streaming engine (lema_slot_stream).
+
+Host-resident fp32 master/m/v and bf16 gradients in page-locked memory are
+streamed through two HBM slots; every layer's results, copied back to the
+host, must equal the oracle's on the same bytes.  Delays injected on the
+copy and compute streams from the host must not change a single bit.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from parity import compare_bf16, compare_f32, oracle_consts, oracle_segment, to_np
+
+pytestmark = pytest.mark.gpu
+HP = synth.HPARAMS
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def L():
+    import optimizer_step_lema_amd as lema
+    return lema
+
+
+def host_layer(L, sizes, seed):
+    """One layer of pinned host state plus numpy snapshots of its inputs."""
+    segs, snaps = [], []
+    for i, n in enumerate(sizes):
+        s = 100 * seed + 10 * i
+        dev = {"master": synth.normal(n, 0.02, s, DEV), "m": synth.normal(n, 1e-4, s + 1, DEV),
+               "v": synth.normal(n, 1e-3, s + 2, DEV).square_(),
+               "g": synth.bf16_normal(n, 1e-3, s + 3, DEV)}
+        host = {k: L.pinned_empty(n, t.dtype) for k, t in dev.items()}
+        for k in dev:
+            host[k].copy_(dev[k])
+        w = L.pinned_empty(n, torch.bfloat16)
+        segs.append(L.AdamwSegment(host["master"], host["m"], host["v"], host["g"], w))
+        # copies: to_np of a host tensor is a view, and the stream writes back into it
+        snaps.append({"master": to_np(host["master"]).copy(), "m": to_np(host["m"]).copy(),
+                      "v": to_np(host["v"]).copy(), "grad": to_np(host["g"]).copy()})
+    return segs, snaps
+
+
+def check_layers(layers, snaps, step, sample=None):
+    consts = oracle_consts(HP, step)
+    rng = np.random.default_rng(0)
+    for li, (segs, sn) in enumerate(zip(layers, snaps)):
+        for si, (s, h) in enumerate(zip(segs, sn)):
+            n = s.master.numel()
+            idx = slice(None) if sample is None or n <= sample else np.unique(
+                np.concatenate([np.arange(1024), np.arange(n - 1024, n), rng.integers(0, n, sample)]))
+            ref = oracle_segment(h["master"][idx], h["m"][idx], h["v"][idx], h["grad"][idx], consts)
+            tag = f"layer{li}.seg{si}"
+            compare_f32(to_np(s.master)[idx], ref["master"], tag + ".master")
+            compare_f32(to_np(s.exp_avg)[idx], ref["m"], tag + ".m")
+            compare_f32(to_np(s.exp_avg_sq)[idx], ref["v"], tag + ".v")
+            compare_bf16(to_np(s.weight)[idx], ref["weight"], tag + ".weight")
+
+
+def layer_bytes(sizes):
+    a = lambda x: (x + 255) // 256 * 256
+    return sum(a(4 * n) * 3 + a(2 * n) * 2 for n in sizes)
+
+
+def test_slot_stream_small_layers(L):
+    shapes = [[100003, 4096, 2048 * 3 + 1], [777, 65536], [1, 2, 3, 300000], [5000]]
+    layers, snaps = zip(*[host_layer(L, s, 10 + i) for i, s in enumerate(shapes)])
+    pool = L.SlotPool(max(layer_bytes(s) for s in shapes), nslots=2)
+    stats = pool.stream(layers, step=7, **HP)
+    check_layers(layers, snaps, 7)
+    P = sum(sum(s) for s in shapes)
+    assert stats["h2d_bytes"] == 14 * P and stats["d2h_bytes"] == 14 * P
+    assert stats["wall_ms"] > 0 and stats["kernel_ms"] > 0
+    # a second streamed step on the evolved state, with three slots
+    snaps2 = [[{"master": to_np(s.master).copy(), "m": to_np(s.exp_avg).copy(),
+                "v": to_np(s.exp_avg_sq).copy(), "grad": to_np(s.grad).copy()} for s in segs]
+              for segs in layers]
+    pool3 = L.SlotPool(max(layer_bytes(s) for s in shapes), nslots=3)
+    pool3.stream(layers, step=8, **HP)
+    check_layers(layers, snaps2, 8)
+    pool.close()
+    pool3.close()
+
+
+def test_slot_stream_with_injected_delays(L):
+    """Long work queued on the pool's copy stream and on its compute stream
+    before the call must not change any result (ordering is by events)."""
+    shapes = [[1 << 20, 4097], [1 << 20, 4097], [1 << 20, 4097], [1 << 20, 4097]]
+    layers, snaps = zip(*[host_layer(L, s, 30 + i) for i, s in enumerate(shapes)])
+    pool = L.SlotPool(layer_bytes(shapes[0]), nslots=2)
+    big_a = torch.empty(1 << 28, device=DEV)
+    big_b = torch.empty(1 << 28, device=DEV)
+    x = torch.randn(4096, 4096, device=DEV)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(pool.copy_stream):
+        for _ in range(20):
+            big_b.copy_(big_a)                       # ~20 ms of copy-stream work
+    with torch.cuda.stream(pool.compute_stream):
+        for _ in range(10):
+            x = x @ x                                # compute-stream work
+            x = x / x.norm()
+    pool.stream(layers, step=3, **HP)
+    check_layers(layers, snaps, 3)
+    pool.close()
+
+
+def test_slot_stream_rejects_pageable_and_oversize(L):
+    n = 4096
+    pageable = L.AdamwSegment(torch.zeros(n), torch.zeros(n), torch.zeros(n),
+                              torch.zeros(n, dtype=torch.bfloat16),
+                              torch.zeros(n, dtype=torch.bfloat16))
+    pool = L.SlotPool(layer_bytes([n]), nslots=2)
+    with pytest.raises(L.LemaError) as e:
+        pool.stream([[pageable]], step=1, **HP)
+    assert e.value.status == -6                      # LEMA_ERR_NOT_PINNED
+    assert torch.count_nonzero(pageable.master) == 0  # nothing ran
+    segs, _ = host_layer(L, [2 * n], 77)
+    with pytest.raises(L.LemaError) as e:
+        pool.stream([segs], step=1, **HP)
+    assert e.value.status == -2                      # LEMA_ERR_SIZE: layer exceeds a slot
+    pool.close()
+
+
+def test_slot_stream_llama_layers_sampled(L):
+    """Three real Llama-2-7B decoder layers (202M params each, 3.24 GB slots)."""
+    w = synth.WORKLOADS["llama7b_layer"]
+    sizes = w.numels
+    layers, snaps = zip(*[host_layer(L, sizes, 50 + i) for i in range(3)])
+    pool = L.SlotPool(layer_bytes(sizes), nslots=2)
+    stats = pool.stream(layers, step=10, **HP)
+    check_layers(layers, snaps, 10, sample=20000)
+    h2d_gbps = stats["h2d_bytes"] / (stats["h2d_ms"] * 1e-3) / 1e9
+    d2h_gbps = stats["d2h_bytes"] / (stats["d2h_ms"] * 1e-3) / 1e9
+    print(f"slot stream 3 Llama layers: H2D {h2d_gbps:.1f} GB/s, D2H {d2h_gbps:.1f} GB/s, "
+          f"kernel {stats['kernel_ms']:.2f} ms, wall {stats['wall_ms']:.1f} ms, "
+          f"copy busy {stats['copy_busy_ms']:.1f} ms, last kernel {stats['last_kernel_ms']:.3f} ms")
+    assert stats["wall_ms"] - stats["copy_busy_ms"] <= 1.05 * stats["last_kernel_ms"] + 1.0
+    pool.close()
