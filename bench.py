@@ -2,18 +2,25 @@
 """Benchmark of the mixed-precision AdamW hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-delta]
+    python bench.py --slot-stream [--layers L]
 
-A step is one call of lema_adamw_step over the whole workload (constants,
-segment walk, AdamW, bf16 write-back and, by default, the fp32 delta) on
-inputs already resident in HBM.  The default workload is the Llama-2-7B
-q, k, v, o projections of the last 4 decoder layers (16 x [4096 x 4096],
-268,435,456 parameters, bf16 gradient, t = 100), the selection the LEMA
-README's "Selective Full Fine-Tuning" section uses as its example.
+A step is one pass of the hot path over the whole workload on inputs already
+resident in HBM: for one micro-batch, one lema_adamw_step call (constants,
+segment walk, AdamW, bf16 write-back and, by default, the fp32 delta); for
+the one-layer workload, 8 lema_grad_accum calls then the step on the fp32
+accumulator.  The default workload is the Llama-2-7B q, k, v, o projections
+of the last 4 decoder layers (16 x [4096 x 4096], 268,435,456 parameters,
+bf16 gradient, t = 100), the selection the LEMA README's "Selective Full
+Fine-Tuning" section uses as its example.
+
+--slot-stream streams the whole Llama-2-7B shape from page-locked host
+memory through two HBM slots (README "TensorStore", "Features") and reports
+copy GB/s next to kernel time.
 
 Prints one JSON line: parameters updated per second (value), HBM GB/s and
-fraction of the 8 TB/s peak, the roofline of the AdamW kernel (kernel time
-from HIP events on its stream), the plain-copy ceiling of the same GPU, and
-the CPU oracle timed on a bounded sample of the same workload.
+fraction of the 8 TB/s peak, the roofline of the AdamW kernel (per-launch
+time from HIP events on its stream), the plain-copy ceiling of the same GPU,
+and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -43,11 +50,15 @@ def kernel_digest() -> str:
     return h.hexdigest()
 
 
-def bytes_per_param(grad_f32: bool, delta: bool) -> int:
+def adamw_bytes_per_param(grad_f32: bool, delta: bool) -> int:
     # reads: grad, master, m, v (+ orig); writes: master, m, v, weight (+ delta)
     read = (4 if grad_f32 else 2) + 12 + (2 if delta else 0)
     write = 12 + 2 + (4 if delta else 0)
     return read + write
+
+
+ACCUM_BYTES_OVERWRITE = 6      # read bf16 g, write fp32 acc
+ACCUM_BYTES = 10               # read bf16 g and fp32 acc, write fp32 acc
 
 
 def parse():
@@ -60,7 +71,52 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-gib", type=float, default=4.0, help="size of the copy-ceiling test")
+    ap.add_argument("--slot-stream", action="store_true",
+                    help="stream the whole 7B shape from pinned host memory through 2 HBM slots")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="with --slot-stream: stream only the first L loads (0 = all 34)")
+    ap.add_argument("--duplex", action="store_true",
+                    help="with --slot-stream: slot -> host copies on a stream of their own")
     return ap.parse_args()
+
+
+def timed_events(torch, stream, fn, n):
+    """Run fn(k) n times, each bracketed by its own event pair; returns ms list."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for k in range(n):
+        evs[k][0].record(stream)
+        fn(k)
+        evs[k][1].record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def copy_ceiling(torch, L, gib):
+    """Read+write GB/s of the library's plain copy kernel (nbytes each way)."""
+    nbytes = int(gib * (1 << 30)) // 2 // 4096 * 4096
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    for _ in range(3):
+        L.measure_copy(src, dst, nbytes)
+    torch.cuda.synchronize()
+    ms = timed_events(torch, torch.cuda.current_stream(),
+                      lambda k: L.measure_copy(src, dst, nbytes), 10)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (sum(ms) / len(ms) * 1e-3) / 1e9
+
+
+def traffic_for(key):
+    """Counter-measured HBM bytes per launch, if recorded for this kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    rec = json.load(open(COUNTERS))
+    entry = rec.get("workloads", {}).get(key)
+    if entry and rec.get("kernel_digest") == kernel_digest():
+        return entry["traffic_bytes_per_launch"]
+    return None
 
 
 def main():
@@ -77,90 +133,96 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(2)
+    if a.slot_stream:
+        line = slot_stream_bench(torch, L, synth, a)
+    else:
+        line = resident_bench(torch, L, synth, a)
+    print(json.dumps(line), flush=True)
+
+
+# ------------------------------------------------------------- resident
+
+def resident_bench(torch, L, synth, a):
     dev = "cuda"
     w = synth.WORKLOADS[a.workload]
     delta = not a.no_delta
     hp = synth.HPARAMS
     P = w.params
+    K = w.microbatches
+    grad_f32 = K > 1
+    step_bytes = adamw_bytes_per_param(grad_f32, delta)
+    accum_bytes = (ACCUM_BYTES_OVERWRITE + (K - 1) * ACCUM_BYTES) if K > 1 else 0
+    per_step = P * (step_bytes + accum_bytes)
 
-    # ---- state resident in HBM; small workloads get rotated copies so the
+    # state resident in HBM; small workloads get rotated copies so that the
     # working set exceeds the 256 MB last-level cache between launches
-    bpp = bytes_per_param(False, delta)
-    per_call = P * bpp
-    nsets = max(1, -(-(1 << 30) // per_call)) if per_call < (1 << 30) else 1
+    nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
     sets = []
-    for r in range(nsets):
-        segs = []
+    for _ in range(nsets):
+        segs, accs = [], []
         for i in range(len(w.segments)):
-            st = synth.make_segment_state(w, i, dev, with_orig=delta, grads=1)
+            st = synth.make_segment_state(w, i, dev, with_orig=delta)
             n = w.numels[i]
-            segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], st["grads"][0],
+            grad = torch.empty(n, device=dev) if grad_f32 else st["grads"][0]
+            if grad_f32:
+                accs.append((grad, st["grads"]))
+            segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], grad,
                                        torch.empty(n, dtype=torch.bfloat16, device=dev),
                                        st.get("orig"),
                                        torch.empty(n, device=dev) if delta else None))
-        sets.append(segs)
+        sets.append((segs, accs))
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
+    copy_gbps = copy_ceiling(torch, L, a.copy_gib)
 
-    # ---- the copy ceiling (read N + write N bytes)
-    nbytes = int(a.copy_gib * (1 << 30)) // 2 // 4096 * 4096
-    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    dst = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    src.fill_(1)
-    for _ in range(3):
-        L.measure_copy(src, dst, nbytes)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 10
-    e0.record(stream)
-    for _ in range(reps):
-        L.measure_copy(src, dst, nbytes)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = e0.elapsed_time(e1) / reps
-    copy_gbps = 2 * nbytes / (copy_ms * 1e-3) / 1e9
-    del src, dst
-    torch.cuda.empty_cache()
+    def accumulate(k):
+        _, accs = sets[k % nsets]
+        for j in range(K):
+            L.grad_accum([L.AccumSegment(acc, g[j]) for acc, g in accs], overwrite=(j == 0))
 
-    # ---- the AdamW step.  Each launch is bracketed by its own pair of HIP
-    # events on the launch stream, so launches do not overlap one another
-    # (the same isolation the kernel trace sees); the back-to-back rate, where
-    # one launch's tail overlaps the next launch's start, is reported beside it.
+    def step(k):
+        L.adamw_step(sets[k % nsets][0], step=w.step, **hp)
+
+    def whole(k):
+        if K > 1:
+            accumulate(k)
+        step(k)
+
+    # Each step is bracketed by its own pair of HIP events on the launch
+    # stream, so steps do not overlap one another (the isolation the kernel
+    # trace sees); the back-to-back rate, where one launch's tail overlaps the
+    # next launch's start, is reported beside it as "pipelined".
     for k in range(a.warmup):
-        L.adamw_step(sets[k % nsets], step=w.step, **hp)
+        whole(k)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(a.steps)]
     t_wall0 = time.perf_counter()
-    for k in range(a.steps):
-        evs[k][0].record(stream)
-        L.adamw_step(sets[k % nsets], step=w.step, **hp)
-        evs[k][1].record(stream)
-    torch.cuda.synchronize()
+    step_ms = timed_events(torch, stream, whole, a.steps)
     wall = time.perf_counter() - t_wall0
-    per_launch = [e0.elapsed_time(e1) for e0, e1 in evs]
-    ms = sum(per_launch) / len(per_launch)
-    params_per_s = P / (ms * 1e-3)
-    gbps = per_call / (ms * 1e-3) / 1e9
+    ms = sum(step_ms) / len(step_ms)
+
+    # the AdamW kernel alone, one launch per event pair
+    if K > 1:
+        adamw_ms_list = timed_events(torch, stream, step, a.steps)
+        accum_ms_list = timed_events(torch, stream, accumulate, a.steps)
+    else:
+        adamw_ms_list, accum_ms_list = step_ms, []
+    adamw_ms = sum(adamw_ms_list) / len(adamw_ms_list)
+    adamw_gbps = P * step_bytes / (adamw_ms * 1e-3) / 1e9
 
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for k in range(a.steps):
-        L.adamw_step(sets[k % nsets], step=w.step, **hp)
+        whole(k)
     stop.record(stream)
     torch.cuda.synchronize()
     pipelined_ms = start.elapsed_time(stop) / a.steps
 
-    traffic = None
-    if os.path.exists(COUNTERS):
-        rec = json.load(open(COUNTERS))
-        entry = rec.get("workloads", {}).get(f"{a.workload}:{'delta' if delta else 'nodelta'}")
-        if entry and rec.get("kernel_digest") == kernel_digest():
-            traffic = entry["traffic_bytes_per_launch"]
-
+    gbps = per_step / (ms * 1e-3) / 1e9
+    key = f"{a.workload}:{'delta' if delta else 'nodelta'}"
     info = L.device_info()
     line = {
         "metric": METRIC,
-        "value": params_per_s,
+        "value": P / (ms * 1e-3),
         "unit": "params/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -176,35 +238,40 @@ def main():
             "description": w.description,
             "params": P,
             "segments": len(w.segments),
-            "grad": "bf16",
+            "grad": "fp32 accumulator of 8 bf16 micro-batches" if K > 1 else "bf16",
             "delta": delta,
             "step_t": w.step,
-            "bytes_per_param": bpp,
-            "bytes_per_call": per_call,
+            "bytes_per_param": step_bytes + accum_bytes,
+            "bytes_per_step": per_step,
             "rotated_state_sets": nsets,
         },
         "hbm_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
         "copy_ceiling_gbps": copy_gbps,
         "pct_copy_ceiling": 100.0 * gbps / copy_gbps,
-        "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": traffic,
-                     "kernel": "adamw_tile_kernel", "algorithmic_bytes_per_launch": per_call,
-                     "avg_launch_ms": ms, "min_launch_ms": min(per_launch),
-                     "max_launch_ms": max(per_launch)},
+        "roofline": {"bound": "hbm", "achieved": adamw_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": adamw_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic_for(key), "kernel": "adamw_tile_kernel",
+                     "algorithmic_bytes_per_launch": P * step_bytes,
+                     "avg_launch_ms": adamw_ms, "min_launch_ms": min(adamw_ms_list),
+                     "max_launch_ms": max(adamw_ms_list)},
         "pipelined": {"ms_per_step": pipelined_ms,
-                      "hbm_gbps": per_call / (pipelined_ms * 1e-3) / 1e9,
+                      "hbm_gbps": per_step / (pipelined_ms * 1e-3) / 1e9,
                       "params_per_s": P / (pipelined_ms * 1e-3)},
         "device": {"compute_units": info["compute_units"],
                    "tile_elements": info["tile_elements"]},
         "host_wall_s_timed_region": wall,
     }
-
-    # ---- the CPU oracle on a bounded sample of the same workload
+    if accum_ms_list:
+        acc_ms = sum(accum_ms_list) / len(accum_ms_list)
+        acc_gbps = P * accum_bytes / (acc_ms * 1e-3) / 1e9
+        line["accumulation"] = {"kernel": "accum_tile_kernel", "launches_per_step": K,
+                                "ms_per_step": acc_ms, "hbm_gbps": acc_gbps,
+                                "frac": acc_gbps / HBM_PEAK_GBPS,
+                                "algorithmic_bytes_per_step": P * accum_bytes}
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(sets[0], w, hp, delta, a.cpu_seconds)
-
-    print(json.dumps(line), flush=True)
+        line["cpu_baseline"] = cpu_baseline(sets[0][0], w, hp, delta, a.cpu_seconds)
+    return line
 
 
 def cpu_baseline(segs, w, hp, delta, seconds):
@@ -237,6 +304,91 @@ def cpu_baseline(segs, w, hp, delta, seconds):
             "kind": "oracle",
             "sample": f"{w.segments[0][0]} ({n} params), {reps} oracle steps in {el:.1f} s, "
                       f"delta {'on' if delta else 'off'}; C oracle, OpenMP"}
+
+
+# ------------------------------------------------------------ streamed
+
+def slot_stream_bench(torch, L, synth, a):
+    """The whole 7B shape in page-locked host memory, streamed per layer."""
+    w = synth.WORKLOADS["llama7b_full"]
+    hp = synth.HPARAMS
+    # the 34 loads: embedding, 32 decoder layers, final norm + LM head
+    loads = [[0]] + [list(range(1 + 9 * l, 10 + 9 * l)) for l in range(32)] + [[289, 290]]
+    if a.layers:
+        loads = loads[:a.layers]
+    align = lambda x: (x + 255) // 256 * 256
+    slot_bytes = max(sum(align(4 * w.numels[i]) * 3 + align(2 * w.numels[i]) * 2 for i in ld)
+                     for ld in loads)
+    t0 = time.perf_counter()
+    layers = []
+    for li, ld in enumerate(loads):
+        segs = []
+        for i in ld:
+            st = synth.make_segment_state(w, i, "cuda")
+            n = w.numels[i]
+            host = {}
+            for k, t in (("master", st["master"]), ("m", st["m"]), ("v", st["v"]),
+                         ("g", st["grads"][0])):
+                host[k] = L.pinned_empty(n, t.dtype)
+                host[k].copy_(t)
+            segs.append(L.AdamwSegment(host["master"], host["m"], host["v"], host["g"],
+                                       L.pinned_empty(n, torch.bfloat16)))
+            del st
+        layers.append(segs)
+        print(f"bench.py: staged load {li + 1}/{len(loads)} in pinned host memory "
+              f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    P = sum(w.numels[i] for ld in loads for i in ld)
+    pool = L.SlotPool(slot_bytes, nslots=2, duplex=a.duplex)
+
+    # standalone pinned copy ceilings (half a slot each way)
+    hbuf = L.pinned_empty(slot_bytes // 2, torch.uint8)
+    dbuf = torch.empty(slot_bytes // 2, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    h2d = timed_events(torch, stream, lambda k: dbuf.copy_(hbuf, non_blocking=True), 3)
+    d2h = timed_events(torch, stream, lambda k: hbuf.copy_(dbuf, non_blocking=True), 3)
+    h2d_gbps = hbuf.numel() / (min(h2d) * 1e-3) / 1e9
+    d2h_gbps = hbuf.numel() / (min(d2h) * 1e-3) / 1e9
+    del hbuf, dbuf
+
+    steps = max(1, min(a.steps, 3))
+    stats = []
+    pool.stream(layers, step=w.step, **hp)                  # warm-up step
+    print("bench.py: warm-up streamed step done", file=sys.stderr, flush=True)
+    for k in range(steps):
+        stats.append(pool.stream(layers, step=w.step + 1 + k, **hp))
+        print(f"bench.py: streamed step {k + 1}/{steps}: {stats[-1]['wall_ms']:.0f} ms",
+              file=sys.stderr, flush=True)
+    pool.close()
+    wall = sum(s["wall_ms"] for s in stats) / steps
+    s0 = stats[-1]
+    line = {
+        "metric": METRIC,
+        "value": P / (wall * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 1,
+        "ms_per_step": wall,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama7b_full_streamed", "loads": len(loads), "params": P,
+                   "slots": 2, "slot_bytes": slot_bytes, "grad": "bf16", "delta": False,
+                   "copy_streams": 2 if a.duplex else 1,
+                   "step_t": w.step, "host_state_bytes": 16 * P, "setup_s": setup_s},
+        "stream": {"h2d_gbps": s0["h2d_bytes"] / (s0["h2d_ms"] * 1e-3) / 1e9,
+                   "d2h_gbps": s0["d2h_bytes"] / (s0["d2h_ms"] * 1e-3) / 1e9,
+                   "standalone_h2d_gbps": h2d_gbps, "standalone_d2h_gbps": d2h_gbps,
+                   "kernel_ms": s0["kernel_ms"], "copy_busy_ms": s0["copy_busy_ms"],
+                   "wall_ms": s0["wall_ms"], "last_kernel_ms": s0["last_kernel_ms"],
+                   "exposed_ms": s0["wall_ms"] - s0["copy_busy_ms"],
+                   "kernel_hbm_gbps": 28 * P / (s0["kernel_ms"] * 1e-3) / 1e9},
+    }
+    return line
 
 
 if __name__ == "__main__":

@@ -184,6 +184,14 @@ lema_status lema_slot_pool_create(void *device_base, size_t slot_bytes, int32_t 
                                   void *copy_stream, void *compute_stream,
                                   lema_slot_pool **out);
 
+/*
+ * Optional: carry the slot -> host copies on their own stream, so that both
+ * PCIe directions are busy at once (the upload of layer i+1 runs beside the
+ * write-back of layer i).  NULL restores the single copy stream.  The stream
+ * must differ from the pool's copy and compute streams (else LEMA_ERR_NULL).
+ */
+lema_status lema_slot_pool_set_writeback_stream(lema_slot_pool *pool, void *stream);
+
 /* Destroy a pool (waits for its outstanding work).  NULL is a no-op. */
 lema_status lema_slot_pool_destroy(lema_slot_pool *pool);
 
@@ -202,8 +210,8 @@ typedef struct {
     double h2d_bytes, d2h_bytes;  /* bytes copied in each direction         */
     double h2d_ms, d2h_ms;        /* summed copy durations                  */
     double kernel_ms;             /* summed AdamW kernel durations          */
-    double copy_busy_ms;          /* first copy start .. last copy end      */
-    double wall_ms;               /* call start .. last copy end            */
+    double copy_busy_ms;          /* time at least one copy was running     */
+    double wall_ms;               /* first copy start .. last copy end      */
     double last_kernel_ms;        /* duration of the last layer's kernel    */
 } lema_stream_stats;
 

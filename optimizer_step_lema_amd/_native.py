@@ -71,6 +71,7 @@ SIGNATURES = [
     ("lema_grad_accum", i32, [ctypes.POINTER(AccumSeg), i32, i32, vp]),
     ("lema_slot_pool_create", i32, [vp, ctypes.c_size_t, i32, vp, vp, ctypes.POINTER(vp)]),
     ("lema_slot_pool_destroy", i32, [vp]),
+    ("lema_slot_pool_set_writeback_stream", i32, [vp, vp]),
     ("lema_slot_stream", i32, [vp, ctypes.POINTER(Layer), i32, ctypes.POINTER(AdamwArgs),
                                ctypes.POINTER(StreamStats)]),
     ("lema_host_alloc", i32, [ctypes.POINTER(vp), ctypes.c_size_t]),

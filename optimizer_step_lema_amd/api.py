@@ -158,9 +158,10 @@ def pinned_empty(numel: int, dtype: torch.dtype) -> torch.Tensor:
 
 class SlotPool:
     """A pool of `nslots` HBM slots of `slot_bytes` each, with its own copy and
-    compute streams (default priority), for lema_slot_stream."""
+    compute streams (default priority), for lema_slot_stream.  With
+    duplex=True the slot -> host copies get a third stream of their own."""
 
-    def __init__(self, slot_bytes: int, nslots: int = 2):
+    def __init__(self, slot_bytes: int, nslots: int = 2, duplex: bool = False):
         lib = N.load()
         slot_bytes = (int(slot_bytes) + 255) // 256 * 256
         self.region = torch.empty(slot_bytes * nslots, dtype=torch.uint8, device="cuda")
@@ -175,6 +176,12 @@ class SlotPool:
                                           self.compute_stream.cuda_stream, ctypes.byref(h)),
                 "lema_slot_pool_create")
         self.handle = h.value
+        self.writeback_stream = None
+        if duplex:
+            self.writeback_stream = torch.cuda.Stream()
+            N.check(lib.lema_slot_pool_set_writeback_stream(self.handle,
+                                                            self.writeback_stream.cuda_stream),
+                    "lema_slot_pool_set_writeback_stream")
 
     def stream(self, layers: Sequence[Sequence[AdamwSegment]], *, lr, beta1=0.9, beta2=0.999,
                eps=1e-8, weight_decay=0.01, step) -> dict:

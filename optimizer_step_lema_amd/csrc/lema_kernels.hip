@@ -300,14 +300,16 @@ __global__ __launch_bounds__(kBlock) void accum_tile_kernel(const void *table, i
 
 // ------------------------------------------------- measurement aids
 
-// Plain copy, one 16-byte vector per lane and one workgroup per 4 KiB, with
-// nontemporal loads and stores: the best plain-copy shape measured on the
-// GPU, used as the practical read+write ceiling and as the known-size
-// reference for HBM byte counters.
-__global__ __launch_bounds__(kBlock) void copy_kernel(const f32x4 *__restrict__ src,
-                                                      f32x4 *__restrict__ dst, size_t n16,
-                                                      size_t block0) {
-    const size_t i = (block0 + blockIdx.x) * kBlock + threadIdx.x;
+// Plain copy, one 16-byte vector per lane and one 256-lane workgroup per
+// 4 KiB, with nontemporal loads and stores: the best plain-copy shape
+// measured on MI355X, used as the practical read+write ceiling and as the
+// known-size reference for HBM byte counters.
+constexpr int kCopyBlock = 256;
+
+__global__ __launch_bounds__(kCopyBlock) void copy_kernel(const f32x4 *__restrict__ src,
+                                                          f32x4 *__restrict__ dst, size_t n16,
+                                                          size_t block0) {
+    const size_t i = (block0 + blockIdx.x) * kCopyBlock + threadIdx.x;
     if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
@@ -371,12 +373,12 @@ hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t str
     const f32x4 *s = static_cast<const f32x4 *>(src);
     f32x4 *d = static_cast<f32x4 *>(dst);
     size_t n16 = bytes / 16;
-    const size_t blocks = (n16 + kBlock - 1) / kBlock;
+    const size_t blocks = (n16 + kCopyBlock - 1) / kCopyBlock;
     for (size_t block0 = 0; block0 < blocks;) {
-        const size_t n = std::min<size_t>(blocks - block0, kMaxBlocksPerLaunch);
+        const size_t n = std::min<size_t>(blocks - block0, kMaxBlocksPerLaunch / 4);
         void *args[] = {&s, &d, &n16, &block0};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&copy_kernel),
-                                       dim3(unsigned(n)), dim3(kBlock), args, 0, stream);
+                                       dim3(unsigned(n)), dim3(kCopyBlock), args, 0, stream);
         if (e != hipSuccess) return e;
         block0 += n;
     }

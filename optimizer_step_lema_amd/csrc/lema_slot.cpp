@@ -13,9 +13,17 @@
 // rewritten by H2D(i) only after D2H(i - nslots), which precedes it on the
 // copy stream, so no slot is overwritten while still in use.  The host
 // enqueues everything without waiting and synchronizes once at the end.
+//
+// With a separate write-back stream (lema_slot_pool_set_writeback_stream)
+// the D2H copies move there, so the two PCIe directions run at once:
+//
+//   copy stream     : H2D(0) H2D(1) H2D(2) ...      (H2D(i) waits for D2H(i - nslots))
+//   write-back      :        D2H(0) D2H(1) ...      (D2H(i) waits for K(i))
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "lema.h"
@@ -31,6 +39,7 @@ struct lema_slot_pool {
     int nslots = 0;
     hipStream_t copy = nullptr;
     hipStream_t compute = nullptr;
+    hipStream_t writeback = nullptr;  // NULL: D2H copies share the copy stream
     std::vector<hipEvent_t> events;   // 6 per layer, grown on demand, reused
     std::mutex mu;
 };
@@ -136,6 +145,15 @@ lema_status lema_slot_pool_create(void *device_base, size_t slot_bytes, int32_t 
     return LEMA_OK;
 }
 
+lema_status lema_slot_pool_set_writeback_stream(lema_slot_pool *pool, void *stream) {
+    if (pool == nullptr) return LEMA_ERR_NULL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (s != nullptr && (s == pool->copy || s == pool->compute)) return LEMA_ERR_NULL;
+    std::lock_guard<std::mutex> lock(pool->mu);
+    pool->writeback = s;
+    return LEMA_OK;
+}
+
 lema_status lema_slot_pool_destroy(lema_slot_pool *pool) {
     if (pool == nullptr) return LEMA_OK;
     lema_status st = LEMA_OK;
@@ -191,23 +209,24 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
     std::vector<std::vector<lema_adamw_seg>> dev_segs(nlayers);
     double h2d_bytes = 0, d2h_bytes = 0;
 
+    hipStream_t d2h_stream = pool->writeback ? pool->writeback : pool->copy;
     auto copy_back = [&](int j) -> lema_status {
         const lema_layer &L = layers[j];
-        hipError_t err = hipStreamWaitEvent(pool->copy, ev(j, EV_K_END), 0);
-        if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_BEGIN), pool->copy);
+        hipError_t err = hipStreamWaitEvent(d2h_stream, ev(j, EV_K_END), 0);
+        if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_BEGIN), d2h_stream);
         size_t k = 0;
         for (int32_t s = 0; s < L.nseg && err == hipSuccess; ++s) {
             const lema_adamw_seg &h = L.host_segs[s];
             if (h.numel == 0) continue;
             const lema_adamw_seg &d = dev_segs[j][k++];
             const size_t n = size_t(h.numel);
-            err = hipMemcpyAsync(h.master, d.master, 4 * n, hipMemcpyDeviceToHost, pool->copy);
-            if (err == hipSuccess) err = hipMemcpyAsync(h.exp_avg, d.exp_avg, 4 * n, hipMemcpyDeviceToHost, pool->copy);
-            if (err == hipSuccess) err = hipMemcpyAsync(h.exp_avg_sq, d.exp_avg_sq, 4 * n, hipMemcpyDeviceToHost, pool->copy);
-            if (err == hipSuccess) err = hipMemcpyAsync(h.weight_bf16, d.weight_bf16, 2 * n, hipMemcpyDeviceToHost, pool->copy);
+            err = hipMemcpyAsync(h.master, d.master, 4 * n, hipMemcpyDeviceToHost, d2h_stream);
+            if (err == hipSuccess) err = hipMemcpyAsync(h.exp_avg, d.exp_avg, 4 * n, hipMemcpyDeviceToHost, d2h_stream);
+            if (err == hipSuccess) err = hipMemcpyAsync(h.exp_avg_sq, d.exp_avg_sq, 4 * n, hipMemcpyDeviceToHost, d2h_stream);
+            if (err == hipSuccess) err = hipMemcpyAsync(h.weight_bf16, d.weight_bf16, 2 * n, hipMemcpyDeviceToHost, d2h_stream);
             d2h_bytes += 14.0 * double(n);
         }
-        if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_END), pool->copy);
+        if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_END), d2h_stream);
         return err == hipSuccess ? LEMA_OK : hip_failed(err);
     };
 
@@ -216,8 +235,12 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
         char *slot = pool->base + size_t(i % pool->nslots) * pool->slot_bytes;
         slot_segments(L, slot, &dev_segs[i]);
 
-        // host -> slot
-        e = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
+        // host -> slot; with a separate write-back stream the slot must first
+        // have been copied back from its previous occupant
+        e = hipSuccess;
+        if (pool->writeback && i >= pool->nslots)
+            e = hipStreamWaitEvent(pool->copy, ev(i - pool->nslots, EV_D2H_END), 0);
+        if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
         size_t k = 0;
         for (int32_t s = 0; s < L.nseg && e == hipSuccess; ++s) {
             const lema_adamw_seg &h = L.host_segs[s];
@@ -259,18 +282,39 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
         lema_stream_stats s{};
         s.h2d_bytes = h2d_bytes;
         s.d2h_bytes = d2h_bytes;
-        float ms = 0.f;
+        // copy intervals relative to the first upload, then their union
+        std::vector<std::pair<float, float>> busy;
+        const hipEvent_t t0 = ev(0, EV_H2D_BEGIN);
+        float ms = 0.f, b = 0.f, en = 0.f;
         for (int32_t i = 0; i < nlayers; ++i) {
-            if (hipEventElapsedTime(&ms, ev(i, EV_H2D_BEGIN), ev(i, EV_H2D_END)) == hipSuccess) s.h2d_ms += ms;
-            if (hipEventElapsedTime(&ms, ev(i, EV_D2H_BEGIN), ev(i, EV_D2H_END)) == hipSuccess) s.d2h_ms += ms;
+            if (hipEventElapsedTime(&b, t0, ev(i, EV_H2D_BEGIN)) == hipSuccess &&
+                hipEventElapsedTime(&en, t0, ev(i, EV_H2D_END)) == hipSuccess) {
+                s.h2d_ms += en - b;
+                busy.emplace_back(b, en);
+            }
+            if (hipEventElapsedTime(&b, t0, ev(i, EV_D2H_BEGIN)) == hipSuccess &&
+                hipEventElapsedTime(&en, t0, ev(i, EV_D2H_END)) == hipSuccess) {
+                s.d2h_ms += en - b;
+                busy.emplace_back(b, en);
+            }
             if (hipEventElapsedTime(&ms, ev(i, EV_K_BEGIN), ev(i, EV_K_END)) == hipSuccess) {
                 s.kernel_ms += ms;
                 if (i == nlayers - 1) s.last_kernel_ms = ms;
             }
         }
-        s.copy_busy_ms = s.h2d_ms + s.d2h_ms;
-        if (hipEventElapsedTime(&ms, ev(0, EV_H2D_BEGIN), ev(nlayers - 1, EV_D2H_END)) == hipSuccess)
-            s.wall_ms = ms;
+        std::sort(busy.begin(), busy.end());
+        float lo = 0.f, hi = -1.f;
+        for (const auto &iv : busy) {
+            if (iv.first > hi) {
+                if (hi > lo) s.copy_busy_ms += hi - lo;
+                lo = iv.first;
+                hi = iv.second;
+            } else if (iv.second > hi) {
+                hi = iv.second;
+            }
+        }
+        if (hi > lo) s.copy_busy_ms += hi - lo;
+        if (hipEventElapsedTime(&ms, t0, ev(nlayers - 1, EV_D2H_END)) == hipSuccess) s.wall_ms = ms;
         *stats = s;
     }
     return LEMA_OK;

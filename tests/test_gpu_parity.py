@@ -22,6 +22,7 @@ DEV = "cuda"
 @pytest.fixture(scope="module")
 def L():
     import optimizer_step_lema_amd as lema
+    lema.load()
     return lema
 
 
@@ -108,8 +109,8 @@ def test_fp32_primitives_are_ieee(L):
 
 # ---------------------------------------------------------- ragged lists
 
-RAGGED = [0, 1, 3, 4, 5, 7, 8, 9, 1023, 1024, 1025, 2047, 2048, 2049, 4095, 4096, 4097,
-          100003, 3 * 65536 + 17]
+RAGGED = [0, 1, 3, 4, 5, 7, 8, 9, 255, 256, 257, 1023, 1024, 1025, 2047, 2048, 2049, 4095,
+          4096, 4097, 100003, 3 * 65536 + 17]
 
 
 @pytest.mark.parametrize("offset", [0, 1, 3])

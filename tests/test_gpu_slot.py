@@ -22,6 +22,7 @@ DEV = "cuda"
 @pytest.fixture(scope="module")
 def L():
     import optimizer_step_lema_amd as lema
+    lema.load()
     return lema
 
 
@@ -135,6 +136,38 @@ def test_slot_stream_llama_layers_sampled(L):
     h2d_gbps = stats["h2d_bytes"] / (stats["h2d_ms"] * 1e-3) / 1e9
     d2h_gbps = stats["d2h_bytes"] / (stats["d2h_ms"] * 1e-3) / 1e9
     print(f"slot stream 3 Llama layers: H2D {h2d_gbps:.1f} GB/s, D2H {d2h_gbps:.1f} GB/s, "
+          f"kernel {stats['kernel_ms']:.2f} ms, wall {stats['wall_ms']:.1f} ms, "
+          f"copy busy {stats['copy_busy_ms']:.1f} ms, last kernel {stats['last_kernel_ms']:.3f} ms")
+    assert stats["wall_ms"] - stats["copy_busy_ms"] <= 1.05 * stats["last_kernel_ms"] + 1.0
+    pool.close()
+
+
+@pytest.mark.parametrize("nslots", [2, 3])
+def test_slot_stream_duplex_writeback(L, nslots):
+    """Slot -> host copies on their own stream: both PCIe directions at once.
+    Slot reuse then hangs on events alone; results must not change."""
+    shapes = [[1 << 20, 4097, 3], [1 << 20, 4097, 3], [5000], [1 << 20, 4097, 3], [1 << 19]]
+    layers, snaps = zip(*[host_layer(L, s, 70 + i) for i, s in enumerate(shapes)])
+    pool = L.SlotPool(max(layer_bytes(s) for s in shapes), nslots=nslots, duplex=True)
+    stats = pool.stream(layers, step=4, **HP)
+    check_layers(layers, snaps, 4)
+    P = sum(sum(s) for s in shapes)
+    assert stats["h2d_bytes"] == 14 * P and stats["d2h_bytes"] == 14 * P
+    assert stats["copy_busy_ms"] <= stats["wall_ms"] + 1e-3
+    pool.close()
+
+
+def test_slot_stream_duplex_llama_layers(L):
+    """Four real Llama-2-7B layers through 2 slots with the duplex write-back."""
+    w = synth.WORKLOADS["llama7b_layer"]
+    sizes = w.numels
+    layers, snaps = zip(*[host_layer(L, sizes, 90 + i) for i in range(4)])
+    pool = L.SlotPool(layer_bytes(sizes), nslots=2, duplex=True)
+    stats = pool.stream(layers, step=10, **HP)
+    check_layers(layers, snaps, 10, sample=20000)
+    h2d_gbps = stats["h2d_bytes"] / (stats["h2d_ms"] * 1e-3) / 1e9
+    d2h_gbps = stats["d2h_bytes"] / (stats["d2h_ms"] * 1e-3) / 1e9
+    print(f"duplex slot stream 4 Llama layers: H2D {h2d_gbps:.1f} GB/s, D2H {d2h_gbps:.1f} GB/s, "
           f"kernel {stats['kernel_ms']:.2f} ms, wall {stats['wall_ms']:.1f} ms, "
           f"copy busy {stats['copy_busy_ms']:.1f} ms, last kernel {stats['last_kernel_ms']:.3f} ms")
     assert stats["wall_ms"] - stats["copy_busy_ms"] <= 1.05 * stats["last_kernel_ms"] + 1.0
