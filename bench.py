@@ -77,6 +77,8 @@ def parse():
                     help="with --slot-stream: stream only the first L loads (0 = all 34)")
     ap.add_argument("--duplex", action="store_true",
                     help="with --slot-stream: slot -> host copies on a stream of their own")
+    ap.add_argument("--host-gib", type=float, default=56.0,
+                    help="with --slot-stream: page-locked host memory to stage at most")
     return ap.parse_args()
 
 
@@ -314,43 +316,61 @@ def slot_stream_bench(torch, L, synth, a):
     hp = synth.HPARAMS
     # the 34 loads: embedding, 32 decoder layers, final norm + LM head
     loads = [[0]] + [list(range(1 + 9 * l, 10 + 9 * l)) for l in range(32)] + [[289, 290]]
+    requested = len(loads)
     if a.layers:
         loads = loads[:a.layers]
     align = lambda x: (x + 255) // 256 * 256
     slot_bytes = max(sum(align(4 * w.numels[i]) * 3 + align(2 * w.numels[i]) * 2 for i in ld)
                      for ld in loads)
-    t0 = time.perf_counter()
-    layers = []
-    for li, ld in enumerate(loads):
-        segs = []
-        for i in ld:
-            st = synth.make_segment_state(w, i, "cuda")
-            n = w.numels[i]
-            host = {}
-            for k, t in (("master", st["master"]), ("m", st["m"]), ("v", st["v"]),
-                         ("g", st["grads"][0])):
-                host[k] = L.pinned_empty(n, t.dtype)
-                host[k].copy_(t)
-            segs.append(L.AdamwSegment(host["master"], host["m"], host["v"], host["g"],
-                                       L.pinned_empty(n, torch.bfloat16)))
-            del st
-        layers.append(segs)
-        print(f"bench.py: staged load {li + 1}/{len(loads)} in pinned host memory "
-              f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    setup_s = time.perf_counter() - t0
-    P = sum(w.numels[i] for ld in loads for i in ld)
-    pool = L.SlotPool(slot_bytes, nslots=2, duplex=a.duplex)
 
-    # standalone pinned copy ceilings (half a slot each way)
+    # device side first: the pool's slots, then the standalone pinned copy
+    # ceilings (half a slot each way); host staging comes last because the
+    # GPU-mappable page-locked memory of a host is bounded
+    pool = L.SlotPool(slot_bytes, nslots=2, duplex=a.duplex)
+    stream = torch.cuda.current_stream()
     hbuf = L.pinned_empty(slot_bytes // 2, torch.uint8)
     dbuf = torch.empty(slot_bytes // 2, dtype=torch.uint8, device="cuda")
-    stream = torch.cuda.current_stream()
     h2d = timed_events(torch, stream, lambda k: dbuf.copy_(hbuf, non_blocking=True), 3)
     d2h = timed_events(torch, stream, lambda k: hbuf.copy_(dbuf, non_blocking=True), 3)
     h2d_gbps = hbuf.numel() / (min(h2d) * 1e-3) / 1e9
     d2h_gbps = hbuf.numel() / (min(d2h) * 1e-3) / 1e9
     del hbuf, dbuf
+
+    t0 = time.perf_counter()
+    layers, staged_bytes = [], 0
+    budget = a.host_gib * (1 << 30)
+    for li, ld in enumerate(loads):
+        need = 16 * sum(w.numels[i] for i in ld)
+        if staged_bytes + need > budget:
+            print(f"bench.py: host budget {a.host_gib} GiB reached after {len(layers)} loads",
+                  file=sys.stderr, flush=True)
+            break
+        segs = []
+        try:
+            for i in ld:
+                st = synth.make_segment_state(w, i, "cuda")
+                n = w.numels[i]
+                host = {}
+                for k, t in (("master", st["master"]), ("m", st["m"]), ("v", st["v"]),
+                             ("g", st["grads"][0])):
+                    host[k] = L.pinned_empty(n, t.dtype)
+                    host[k].copy_(t)
+                segs.append(L.AdamwSegment(host["master"], host["m"], host["v"], host["g"],
+                                           L.pinned_empty(n, torch.bfloat16)))
+                del st
+        except L.LemaError as e:
+            del segs
+            print(f"bench.py: page-locked allocation failed at load {li + 1} ({e}); "
+                  f"streaming {len(layers)} of {requested} loads", file=sys.stderr, flush=True)
+            break
+        layers.append(segs)
+        staged_bytes += need
+        print(f"bench.py: staged load {li + 1}/{len(loads)} in pinned host memory "
+              f"({time.perf_counter() - t0:.1f} s)", file=sys.stderr, flush=True)
+    loads = loads[:len(layers)]
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    P = sum(w.numels[i] for ld in loads for i in ld)
 
     steps = max(1, min(a.steps, 3))
     stats = []
@@ -363,6 +383,7 @@ def slot_stream_bench(torch, L, synth, a):
     pool.close()
     wall = sum(s["wall_ms"] for s in stats) / steps
     s0 = stats[-1]
+    full_params = w.params
     line = {
         "metric": METRIC,
         "value": P / (wall * 1e-3),
@@ -376,17 +397,20 @@ def slot_stream_bench(torch, L, synth, a):
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": "llama7b_full_streamed", "loads": len(loads), "params": P,
-                   "slots": 2, "slot_bytes": slot_bytes, "grad": "bf16", "delta": False,
-                   "copy_streams": 2 if a.duplex else 1,
-                   "step_t": w.step, "host_state_bytes": 16 * P, "setup_s": setup_s},
+        "config": {"workload": "llama7b_full_streamed", "loads": len(loads),
+                   "loads_requested": requested, "params": P, "slots": 2,
+                   "slot_bytes": slot_bytes, "grad": "bf16", "delta": False,
+                   "copy_streams": 2 if a.duplex else 1, "step_t": w.step,
+                   "host_state_bytes": 16 * P, "setup_s": setup_s},
         "stream": {"h2d_gbps": s0["h2d_bytes"] / (s0["h2d_ms"] * 1e-3) / 1e9,
                    "d2h_gbps": s0["d2h_bytes"] / (s0["d2h_ms"] * 1e-3) / 1e9,
                    "standalone_h2d_gbps": h2d_gbps, "standalone_d2h_gbps": d2h_gbps,
                    "kernel_ms": s0["kernel_ms"], "copy_busy_ms": s0["copy_busy_ms"],
                    "wall_ms": s0["wall_ms"], "last_kernel_ms": s0["last_kernel_ms"],
                    "exposed_ms": s0["wall_ms"] - s0["copy_busy_ms"],
-                   "kernel_hbm_gbps": 28 * P / (s0["kernel_ms"] * 1e-3) / 1e9},
+                   "kernel_hbm_gbps": 28 * P / (s0["kernel_ms"] * 1e-3) / 1e9,
+                   "ms_per_param_billion": wall / (P / 1e9),
+                   "projected_full_7b_ms": wall * full_params / P},
     }
     return line
 
