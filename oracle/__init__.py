@@ -72,6 +72,8 @@ def _load():
     lib.oracle_adamw.restype = None
     lib.oracle_accum.argtypes = [i64, vp, vp, i32]
     lib.oracle_accum.restype = None
+    lib.oracle_merge_delta.argtypes = [i64, vp, vp, vp]
+    lib.oracle_merge_delta.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -166,3 +168,13 @@ def grad_accum(acc: np.ndarray, grad_bf16: np.ndarray, overwrite: bool):
     _check(acc, np.float32, n, "acc", True)
     _check(grad_bf16, np.uint16, n, "grad_bf16")
     _load().oracle_accum(n, _ptr(acc), _ptr(grad_bf16), 1 if overwrite else 0)
+
+
+def merge_delta(base_bf16: np.ndarray, delta: np.ndarray) -> np.ndarray:
+    """Servable bf16 weight: rne16(f32(base) + delta) (README merge_delta)."""
+    n = base_bf16.shape[0]
+    _check(base_bf16, np.uint16, n, "base")
+    _check(delta, np.float32, n, "delta")
+    out = np.empty(n, dtype=np.uint16)
+    _load().oracle_merge_delta(n, _ptr(base_bf16), _ptr(delta), _ptr(out))
+    return out

@@ -103,3 +103,12 @@ def accumulate(grads_bf16):
                 s = F(s + from_bf16_bits(grads_bf16[k][i]))
             acc[i] = s
     return acc
+
+
+def merge_delta(base_bf16, delta):
+    """Loop version of the bf16 merge: rne16(f32(base) + delta) per element."""
+    out = np.empty(len(base_bf16), np.uint16)
+    with np.errstate(all="ignore"):
+        for i in range(len(base_bf16)):
+            out[i] = to_bf16_bits(F(from_bf16_bits(base_bf16[i]) + F(delta[i])))
+    return out

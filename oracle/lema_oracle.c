@@ -203,6 +203,23 @@ void oracle_accum(int64_t n, float *acc, const uint16_t *g, int overwrite)
     }
 }
 
+/* ---------------------------------------------------------- merge delta */
+
+/*
+ * A servable bf16 weight from a base checkpoint and a saved delta (LEMA
+ * README, "Selective Full Fine-Tuning": merge_delta(base, delta, merged)
+ * produces a full model from the base weights and the fp32 delta):
+ *   merged = rne16(f32(base) + delta)      one binary32 addition, then bf16
+ */
+void oracle_merge_delta(int64_t n, const uint16_t *base, const float *delta, uint16_t *merged)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) {
+        float sum = oracle_bf16_to_f32(base[i]) + delta[i];
+        merged[i] = oracle_rne16(sum);
+    }
+}
+
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_num_threads(void)
 {

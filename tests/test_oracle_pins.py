@@ -474,3 +474,45 @@ def test_nan_and_inf_propagate():
     assert np.isnan(master[3]) and master[4] == np.inf
     assert np.isfinite(master[5]) and master[6] == np.float32(0.5) * np.float32(1 - 1e-6)
     assert ((wb[:4] & 0x7FFF) > 0x7F80).all()
+
+
+# ---------------------------------------------------------------- merge delta
+
+def test_merge_delta_reproduces_step_weight():
+    """README merge_delta: base + saved delta gives the servable weight back.
+
+    The delta a step writes is w' - f32(base), exact wherever w' and the base
+    are within a factor of two (Sterbenz), so merging it reproduces
+    rne16(w'), the bf16 weight of the same step, bit for bit there.
+    """
+    n = 200000
+    master, m, v, grad = rng_state(n, 41)
+    base = oracle.rne16(master)
+    wb, delta = oracle.adamw_step(master, m, v, grad, consts(100), orig=base)
+    merged = oracle.merge_delta(base, delta)
+    b = oracle.bf16_to_f32(base).astype(np.float64)
+    w = master.astype(np.float64)
+    same = (np.sign(w) == np.sign(b)) & (np.abs(w) <= 2 * np.abs(b)) & (np.abs(b) <= 2 * np.abs(w))
+    assert same.mean() > 0.99
+    assert np.array_equal(merged[same], wb[same])
+
+
+def test_merge_delta_zero_delta_and_bruteforce():
+    rng = np.random.default_rng(8)
+    base = oracle.rne16((rng.standard_normal(5000) * 0.02).astype(np.float32))
+    base[:4] = [0x0000, 0x8000, 0x7F80, 0x7FC0]
+    zero = np.zeros(5000, np.float32)
+    merged = oracle.merge_delta(base, zero)
+    assert np.array_equal(merged[4:], base[4:])                     # exact
+    assert merged[0] == 0 and merged[1] == 0 and merged[2] == 0x7F80  # -0 + 0 = +0
+    assert (merged[3] & 0x7FFF) > 0x7F80
+    delta = (rng.standard_normal(5000) * 1e-4).astype(np.float32)
+    got = oracle.merge_delta(base, delta)
+    ref = bruteforce.merge_delta(base, delta)
+    nan = (ref & 0x7FFF) > 0x7F80
+    assert np.array_equal(got[~nan], ref[~nan])
+    # against float64 arithmetic: the merged value is the bf16 nearest to base+delta
+    exact = oracle.bf16_to_f32(base[4:]).astype(np.float64) + delta[4:].astype(np.float64)
+    mval = oracle.bf16_to_f32(got[4:]).astype(np.float64)
+    ulp16 = np.spacing(np.abs(mval).astype(np.float32)).astype(np.float64) * 65536
+    assert np.all(np.abs(mval - exact) <= 0.5 * ulp16 + np.spacing(np.abs(exact).astype(np.float32)))
