@@ -139,6 +139,23 @@ lema_status lema_adamw_constants(const lema_adamw_args *args, lema_adamw_consts 
 lema_status lema_adamw_step(const lema_adamw_seg *segs, int32_t nseg,
                             const lema_adamw_args *args, void *stream);
 
+/*
+ * The step on an fp32 accumulator with the last micro-batch folded in:
+ * per element g = acc + f32(last), the same fp32 addition lema_grad_accum
+ * performs, so the results are bit-identical to lema_grad_accum(last) followed
+ * by lema_adamw_step on the accumulator, while the accumulator is only read
+ * (it is not updated).  It saves one pass over the accumulator (LEMA README,
+ * "Selective Full Fine-Tuning": fp32 gradient accumulation feeding the
+ * per-layer AdamW step).
+ *   segs        : as for lema_adamw_step; segs[i].grad is the fp32 accumulator
+ *   last_bf16   : host array of nseg device pointers; last_bf16[i] holds the
+ *                 bf16 bits of segment i's last micro-batch (numel elements)
+ *   args        : args->grad_dtype must be LEMA_GRAD_FP32 (else LEMA_ERR_DTYPE)
+ * Errors: as lema_adamw_step.
+ */
+lema_status lema_adamw_step_accum(const lema_adamw_seg *segs, const uint16_t *const *last_bf16,
+                                  int32_t nseg, const lema_adamw_args *args, void *stream);
+
 /* ------------------------------------------------ gradient accumulation */
 
 /* One accumulator and the bf16 micro-batch gradient added into it. */
@@ -159,6 +176,28 @@ typedef struct {
  */
 lema_status lema_grad_accum(const lema_accum_seg *segs, int32_t nseg,
                             int32_t overwrite, void *stream);
+
+/* ----------------------------------------------------------- merge delta */
+
+/* One tensor of a merge: base checkpoint weight, saved delta, output. */
+typedef struct {
+    const uint16_t *base_bf16;    /* bf16 bits of the base weight, in (required) */
+    const float    *delta;        /* fp32 delta (updated - original), in (required) */
+    uint16_t       *merged_bf16;  /* out: the servable bf16 weight (required)     */
+    int64_t         numel;        /* >= 0                                         */
+} lema_merge_seg;
+
+/*
+ * Servable weights from a base checkpoint and a saved delta (LEMA README,
+ * "Selective Full Fine-Tuning": merge_delta(base, delta, merged)):
+ *   merged = bf16 round-to-nearest-even of (f32(base) + delta)
+ * one binary32 addition per element.  Merging the delta a step wrote next to
+ * its bf16 weight reproduces that weight.  The file I/O of the original tool
+ * is the caller's.  Asynchronous on `stream`.
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_ALIGN, LEMA_ERR_OVERLAP,
+ * LEMA_ERR_HIP.
+ */
+lema_status lema_merge_delta(const lema_merge_seg *segs, int32_t nseg, void *stream);
 
 /* --------------------------------------- slot-pool streaming (host RAM) */
 

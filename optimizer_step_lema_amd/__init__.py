@@ -6,6 +6,6 @@ thin Python binding.  The library is loaded on first use (``load()``), which
 raises ImportError if it has not been built: no step has a non-HIP fallback.
 """
 from ._native import LemaError, load  # noqa: F401
-from .api import (AccumSegment, AdamwSegment, SlotPool, adamw_constants,  # noqa: F401
-                  adamw_step, device_info, grad_accum, measure_copy, pinned_empty,
-                  probe_fp32)
+from .api import (AccumPlan, AccumSegment, AdamwPlan, AdamwSegment, MergeSegment, SlotPool,  # noqa: F401
+                  adamw_constants, adamw_step, device_info, grad_accum, measure_copy,
+                  merge_delta, pinned_empty, probe_fp32)

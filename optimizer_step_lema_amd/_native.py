@@ -51,6 +51,10 @@ class AccumSeg(ctypes.Structure):
     _fields_ = [("acc", vp), ("grad_bf16", vp), ("numel", i64)]
 
 
+class MergeSeg(ctypes.Structure):
+    _fields_ = [("base_bf16", vp), ("delta", vp), ("merged_bf16", vp), ("numel", i64)]
+
+
 class Layer(ctypes.Structure):
     _fields_ = [("host_segs", ctypes.POINTER(AdamwSeg)), ("nseg", i32)]
 
@@ -68,7 +72,10 @@ SIGNATURES = [
     ("lema_version", i32, []),
     ("lema_adamw_constants", i32, [ctypes.POINTER(AdamwArgs), ctypes.POINTER(AdamwConsts)]),
     ("lema_adamw_step", i32, [ctypes.POINTER(AdamwSeg), i32, ctypes.POINTER(AdamwArgs), vp]),
+    ("lema_adamw_step_accum", i32, [ctypes.POINTER(AdamwSeg), ctypes.POINTER(vp), i32,
+                                    ctypes.POINTER(AdamwArgs), vp]),
     ("lema_grad_accum", i32, [ctypes.POINTER(AccumSeg), i32, i32, vp]),
+    ("lema_merge_delta", i32, [ctypes.POINTER(MergeSeg), i32, vp]),
     ("lema_slot_pool_create", i32, [vp, ctypes.c_size_t, i32, vp, vp, ctypes.POINTER(vp)]),
     ("lema_slot_pool_destroy", i32, [vp]),
     ("lema_slot_pool_set_writeback_stream", i32, [vp, vp]),

@@ -98,13 +98,65 @@ def adamw_constants(*, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, 
 
 
 def adamw_step(segments: Sequence[AdamwSegment], *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
-               weight_decay=0.01, step, stream=None) -> None:
-    """One AdamW step over `segments` on the GPU (asynchronous on `stream`)."""
+               weight_decay=0.01, step, stream=None,
+               last_grads: Optional[Sequence[torch.Tensor]] = None) -> None:
+    """One AdamW step over `segments` on the GPU (asynchronous on `stream`).
+
+    With `last_grads` (one bf16 tensor per segment) each segment's grad is an
+    fp32 accumulator and the step adds the last micro-batch to it on the fly
+    (lema_adamw_step_accum); the accumulator is not updated.
+    """
     lib = N.load()
     segs = (N.AdamwSeg * max(1, len(segments)))(*[s.to_c() for s in segments])
     args = _args(lr, beta1, beta2, eps, weight_decay, step, _grad_dtype(segments))
-    N.check(lib.lema_adamw_step(segs, len(segments), ctypes.byref(args), _stream_handle(stream)),
-            "lema_adamw_step")
+    if last_grads is None:
+        N.check(lib.lema_adamw_step(segs, len(segments), ctypes.byref(args),
+                                    _stream_handle(stream)), "lema_adamw_step")
+        return
+    if len(last_grads) != len(segments):
+        raise ValueError("one last-micro-batch gradient per segment is required")
+    ptrs = (ctypes.c_void_p * max(1, len(segments)))(
+        *[_check(g, torch.bfloat16, s.master.numel(), f"last_grads[{i}]")
+          for i, (g, s) in enumerate(zip(last_grads, segments))])
+    N.check(lib.lema_adamw_step_accum(segs, ptrs, len(segments), ctypes.byref(args),
+                                      _stream_handle(stream)), "lema_adamw_step_accum")
+
+
+class AdamwPlan:
+    """A segment list marshalled once for repeated steps.
+
+    A training loop steps the same tensors every iteration; the plan keeps
+    the C descriptor array (and, for the fused mode, the last-micro-batch
+    pointer array) so that each step is one call into the library.  The
+    tensors must stay alive and in place while the plan is used.
+    """
+
+    def __init__(self, segments: Sequence[AdamwSegment],
+                 last_grads: Optional[Sequence[torch.Tensor]] = None):
+        self.lib = N.load()
+        self.segments = list(segments)
+        self.n = len(self.segments)
+        self.c_segs = (N.AdamwSeg * max(1, self.n))(*[s.to_c() for s in self.segments])
+        self.grad_dtype = _grad_dtype(self.segments)
+        self.last_grads = None if last_grads is None else list(last_grads)
+        self.c_last = None
+        if self.last_grads is not None:
+            if len(self.last_grads) != self.n:
+                raise ValueError("one last-micro-batch gradient per segment is required")
+            self.c_last = (ctypes.c_void_p * max(1, self.n))(
+                *[_check(g, torch.bfloat16, s.master.numel(), f"last_grads[{i}]")
+                  for i, (g, s) in enumerate(zip(self.last_grads, self.segments))])
+
+    def step(self, *, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step,
+             stream=None) -> None:
+        args = _args(lr, beta1, beta2, eps, weight_decay, step, self.grad_dtype)
+        if self.c_last is None:
+            N.check(self.lib.lema_adamw_step(self.c_segs, self.n, ctypes.byref(args),
+                                             _stream_handle(stream)), "lema_adamw_step")
+        else:
+            N.check(self.lib.lema_adamw_step_accum(self.c_segs, self.c_last, self.n,
+                                                   ctypes.byref(args), _stream_handle(stream)),
+                    "lema_adamw_step_accum")
 
 
 @dataclass
@@ -124,6 +176,45 @@ def grad_accum(segments: Sequence[AccumSegment], *, overwrite: bool, stream=None
     arr = (N.AccumSeg * max(1, len(cs)))(*cs)
     N.check(lib.lema_grad_accum(arr, len(cs), 1 if overwrite else 0, _stream_handle(stream)),
             "lema_grad_accum")
+
+
+@dataclass
+class MergeSegment:
+    base: torch.Tensor       # bf16
+    delta: torch.Tensor      # fp32
+    merged: torch.Tensor     # bf16 output
+
+
+def merge_delta(segments: Sequence[MergeSegment], stream=None) -> None:
+    """merged = bf16(f32(base) + delta) for every segment, on the GPU."""
+    lib = N.load()
+    cs = []
+    for s in segments:
+        n = s.base.numel()
+        cs.append(N.MergeSeg(_check(s.base, torch.bfloat16, n, "base"),
+                             _check(s.delta, torch.float32, n, "delta"),
+                             _check(s.merged, torch.bfloat16, n, "merged"), n))
+    arr = (N.MergeSeg * max(1, len(cs)))(*cs)
+    N.check(lib.lema_merge_delta(arr, len(cs), _stream_handle(stream)), "lema_merge_delta")
+
+
+class AccumPlan:
+    """An accumulation segment list marshalled once for repeated calls."""
+
+    def __init__(self, segments: Sequence[AccumSegment]):
+        self.lib = N.load()
+        self.segments = list(segments)
+        cs = []
+        for s in self.segments:
+            n = s.acc.numel()
+            cs.append(N.AccumSeg(_check(s.acc, torch.float32, n, "acc"),
+                                 _check(s.grad, torch.bfloat16, n, "grad"), n))
+        self.n = len(cs)
+        self.c_segs = (N.AccumSeg * max(1, self.n))(*cs)
+
+    def run(self, *, overwrite: bool, stream=None) -> None:
+        N.check(self.lib.lema_grad_accum(self.c_segs, self.n, 1 if overwrite else 0,
+                                         _stream_handle(stream)), "lema_grad_accum")
 
 
 # ------------------------------------------------------------ host memory

@@ -287,7 +287,7 @@ uint64_t count_tiles(const std::vector<SegRec> &recs) {
 }  // namespace
 
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
-                              bool grad_f32, hipStream_t stream) {
+                              GradMode grad_mode, hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
     DeviceState *d = nullptr;
@@ -302,7 +302,7 @@ lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts
     TableEntry *t = nullptr;
     st = acquire_table(*d, tb.bytes, stream, &t);
     if (st != LEMA_OK) return st;
-    hipError_t e = launch_adamw(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_f32,
+    hipError_t e = launch_adamw(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_mode,
                                 with_delta, c, stream);
     lema_status rel = release_table(*d, t, stream);
     if (e != hipSuccess) return hip_failed(e);
@@ -329,12 +329,31 @@ lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
     return rel;
 }
 
-void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out) {
+lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t stream) {
+    if (recs.empty()) return LEMA_OK;
+    if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
+    DeviceState *d = nullptr;
+    lema_status st = device_state(&d, nullptr);
+    if (st != LEMA_OK) return st;
+    TableBuild tb;
+    build_table(recs, &tb);
+    std::lock_guard<std::mutex> lock(d->mu);
+    TableEntry *t = nullptr;
+    st = acquire_table(*d, tb.bytes, stream, &t);
+    if (st != LEMA_OK) return st;
+    hipError_t e = launch_merge(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), stream);
+    lema_status rel = release_table(*d, t, stream);
+    if (e != hipSuccess) return hip_failed(e);
+    return rel;
+}
+
+void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out,
+                   const uint16_t *const *last_bf16) {
     out->clear();
     for (int32_t i = 0; i < nseg; ++i) {
         const lema_adamw_seg &s = segs[i];
         if (s.numel == 0) continue;
-        SegRec r;
+        SegRec r{};
         r.p[0] = reinterpret_cast<uint64_t>(s.master);
         r.p[1] = reinterpret_cast<uint64_t>(s.exp_avg);
         r.p[2] = reinterpret_cast<uint64_t>(s.exp_avg_sq);
@@ -342,6 +361,7 @@ void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec>
         r.p[4] = reinterpret_cast<uint64_t>(s.weight_bf16);
         r.p[5] = reinterpret_cast<uint64_t>(s.orig_bf16);
         r.p[6] = reinterpret_cast<uint64_t>(s.delta);
+        r.p[7] = last_bf16 ? reinterpret_cast<uint64_t>(last_bf16[i]) : 0;
         r.numel = s.numel;
         out->push_back(r);
     }
@@ -399,8 +419,31 @@ lema_status lema_adamw_step(const lema_adamw_seg *segs, int32_t nseg, const lema
     if (st != LEMA_OK) return st;
     if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
     std::vector<SegRec> recs;
-    adamw_records(segs, nseg, &recs);
-    return launch_adamw_recs(recs, derive_consts(args), args->grad_dtype == LEMA_GRAD_FP32,
+    adamw_records(segs, nseg, &recs, nullptr);
+    return launch_adamw_recs(recs, derive_consts(args),
+                             args->grad_dtype == LEMA_GRAD_FP32 ? kGradF32 : kGradBf16,
+                             static_cast<hipStream_t>(stream));
+}
+
+lema_status lema_adamw_step_accum(const lema_adamw_seg *segs, const uint16_t *const *last_bf16,
+                                  int32_t nseg, const lema_adamw_args *args, void *stream) {
+    lema_status st = check_hparams(args);
+    if (st != LEMA_OK) return st;
+    if (args->grad_dtype != LEMA_GRAD_FP32) return LEMA_ERR_DTYPE;
+    std::vector<Span> spans;
+    st = validate_adamw_segs(segs, nseg, args->grad_dtype, true, &spans);
+    if (st != LEMA_OK) return st;
+    if (nseg > 0 && last_bf16 == nullptr) return LEMA_ERR_NULL;
+    for (int32_t i = 0; i < nseg; ++i) {
+        if (segs[i].numel == 0) continue;
+        if (last_bf16[i] == nullptr) return LEMA_ERR_NULL;
+        if (reinterpret_cast<uintptr_t>(last_bf16[i]) & 1) return LEMA_ERR_ALIGN;
+        add_span(spans, last_bf16[i], segs[i].numel, 2, false);
+    }
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    std::vector<SegRec> recs;
+    adamw_records(segs, nseg, &recs, last_bf16);
+    return launch_adamw_recs(recs, derive_consts(args), kGradF32PlusBf16,
                              static_cast<hipStream_t>(stream));
 }
 
@@ -427,6 +470,34 @@ lema_status lema_grad_accum(const lema_accum_seg *segs, int32_t nseg, int32_t ov
     }
     if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
     return launch_accum_recs(recs, overwrite != 0, static_cast<hipStream_t>(stream));
+}
+
+lema_status lema_merge_delta(const lema_merge_seg *segs, int32_t nseg, void *stream) {
+    if (nseg < 0) return LEMA_ERR_SIZE;
+    if (nseg > 0 && segs == nullptr) return LEMA_ERR_NULL;
+    std::vector<Span> spans;
+    std::vector<SegRec> recs;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const lema_merge_seg &s = segs[i];
+        if (s.numel < 0) return LEMA_ERR_SIZE;
+        if (s.numel == 0) continue;
+        if (!s.base_bf16 || !s.delta || !s.merged_bf16) return LEMA_ERR_NULL;
+        if ((reinterpret_cast<uintptr_t>(s.base_bf16) & 1) ||
+            (reinterpret_cast<uintptr_t>(s.merged_bf16) & 1) ||
+            (reinterpret_cast<uintptr_t>(s.delta) & 3))
+            return LEMA_ERR_ALIGN;
+        add_span(spans, s.base_bf16, s.numel, 2, false);
+        add_span(spans, s.delta, s.numel, 4, false);
+        add_span(spans, s.merged_bf16, s.numel, 2, true);
+        SegRec r{};
+        r.p[0] = reinterpret_cast<uint64_t>(s.base_bf16);
+        r.p[1] = reinterpret_cast<uint64_t>(s.delta);
+        r.p[2] = reinterpret_cast<uint64_t>(s.merged_bf16);
+        r.numel = s.numel;
+        recs.push_back(r);
+    }
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    return launch_merge_recs(recs, static_cast<hipStream_t>(stream));
 }
 
 lema_status lema_host_alloc(void **out, size_t bytes) {

@@ -30,13 +30,16 @@ lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_
                                 bool delta_allowed, std::vector<Span> *spans);
 bool any_conflict(std::vector<Span> &spans);
 
-// Launch records of the non-empty segments.
-void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out);
+// Launch records of the non-empty segments; last_bf16 (may be NULL) gives
+// each segment's last micro-batch for the fused accumulate-and-step mode.
+void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out,
+                   const uint16_t *const *last_bf16);
 
 // Launch through the per-device table cache on `stream`.
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
-                              bool grad_f32, hipStream_t stream);
+                              GradMode grad_mode, hipStream_t stream);
 lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
                               hipStream_t stream);
+lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t stream);
 
 }  // namespace lema

@@ -22,14 +22,23 @@ constexpr int64_t kTile = int64_t(kBlock) * kVec * kUnroll;   // 256 elements
 // grid's work-item count well inside 32 bits).
 constexpr uint32_t kMaxBlocksPerLaunch = 1u << 24;
 
-// One segment of the launch table: up to seven array pointers and the length.
-//   AdamW : p = {master, m, v, grad, weight_bf16, orig_bf16, delta}
-//   accum : p = {acc, grad_bf16, 0, 0, 0, 0, 0}
+// One segment of the launch table: up to eight array pointers and the length.
+//   AdamW : p = {master, m, v, grad, weight_bf16, orig_bf16, delta, last_bf16}
+//   accum : p = {acc, grad_bf16, 0, 0, 0, 0, 0, 0}
+//   merge : p = {base_bf16, delta, merged_bf16, 0, 0, 0, 0, 0}
 struct SegRec {
-    uint64_t p[7];
+    uint64_t p[8];
     int64_t numel;
+    int64_t reserved;
 };
-static_assert(sizeof(SegRec) == 64, "segment record is one 64-byte line");
+static_assert(sizeof(SegRec) == 80, "segment record is 80 bytes");
+
+// How the AdamW kernel reads the gradient.
+enum GradMode : int {
+    kGradBf16 = 0,         // grad: bf16 bits of one micro-batch
+    kGradF32 = 1,          // grad: the fp32 accumulator
+    kGradF32PlusBf16 = 2,  // grad: fp32 accumulator + f32(last bf16 micro-batch)
+};
 
 // The launch table in device memory is
 //   uint32_t tile_begin[nseg + 1]   (prefix sum of tiles per segment)
@@ -49,10 +58,11 @@ struct AdamwConsts {
 // Kernel launches (asynchronous on `stream`).  `table` is the device copy of
 // the launch table; one workgroup runs per tile 0 .. total_tiles-1.
 hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles,
-                        bool grad_f32, bool with_delta, const AdamwConsts &c,
+                        GradMode grad_mode, bool with_delta, const AdamwConsts &c,
                         hipStream_t stream);
 hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
                         bool overwrite, hipStream_t stream);
+hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream);
 
 // Measurement aids (include/lema_measure.h).
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);

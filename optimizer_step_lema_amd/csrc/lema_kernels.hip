@@ -6,6 +6,8 @@
 //   fine-tuning VRAM page: bf16 weight and gradient next to fp32 states).
 // accum_tile_kernel : fp32 accumulation of a bf16 micro-batch gradient
 //   (README, "Selective Full Fine-Tuning": fp32 gradient accumulation).
+// merge_tile_kernel : servable bf16 weight from base + saved fp32 delta
+//   (README, "Selective Full Fine-Tuning": merge_delta).
 //
 // Both are elementwise and bound by HBM bandwidth, so there is no MFMA and
 // no LDS tiling of data: each lane streams 4 contiguous elements per access
@@ -130,36 +132,55 @@ __device__ __forceinline__ void tile_of_block(const void *table, int nseg, uint3
 
 // ------------------------------------------------------------- AdamW
 
-template <bool kGradF32, bool kDelta>
+template <GradMode kMode, bool kDelta>
 struct AdamwTile {
     AdamwConsts c;
 
     __device__ __forceinline__ void operator()(const SegRec &r, uint32_t local_tile) const {
         const uint64_t master = r.p[0], m = r.p[1], v = r.p[2], grad = r.p[3];
-        const uint64_t weight = r.p[4], orig = r.p[5], delta = r.p[6];
+        const uint64_t weight = r.p[4], orig = r.p[5], delta = r.p[6], last = r.p[7];
         const int64_t numel = r.numel;
         const int64_t base = int64_t(local_tile) * kTile;
 
+        constexpr bool kGradIsF32 = kMode != kGradBf16;
         const bool has_delta = kDelta && delta != 0;
-        const uint64_t fp32_bits = master | m | v | (kGradF32 ? grad : 0) | (has_delta ? delta : 0);
-        const uint64_t bf16_bits = (kGradF32 ? 0 : grad) | weight | (has_delta ? orig : 0);
+        const uint64_t fp32_bits = master | m | v | (kGradIsF32 ? grad : 0) | (has_delta ? delta : 0);
+        const uint64_t bf16_bits = (kGradIsF32 ? 0 : grad) | weight | (has_delta ? orig : 0) |
+                                   (kMode == kGradF32PlusBf16 ? last : 0);
         const bool vector_ok = base + kTile <= numel && (fp32_bits & 15) == 0 && (bf16_bits & 7) == 0;
 
         if (vector_ok) {
             if (has_delta)
-                vector_tile<true>(master, m, v, grad, weight, orig, delta, base);
+                vector_tile<true>(master, m, v, grad, last, weight, orig, delta, base);
             else
-                vector_tile<false>(master, m, v, grad, weight, orig, delta, base);
+                vector_tile<false>(master, m, v, grad, last, weight, orig, delta, base);
         } else {
-            element_tile(master, m, v, grad, weight, has_delta ? orig : 0, has_delta ? delta : 0,
-                         base, numel);
+            element_tile(master, m, v, grad, last, weight, has_delta ? orig : 0,
+                         has_delta ? delta : 0, base, numel);
+        }
+    }
+
+    // The gradient of 4 consecutive elements starting at vector index q.
+    __device__ __forceinline__ f32x4 load_grad4(uint64_t grad, uint64_t last, int64_t q) const {
+#pragma clang fp contract(off)
+        if constexpr (kMode == kGradBf16) {
+            const u32x2 gb = ld_nt<u32x2>(grad, q);
+            return f32x4{bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
+        } else if constexpr (kMode == kGradF32) {
+            return ld_nt<f32x4>(grad, q);
+        } else {
+            // the last micro-batch's fp32 addition, as lema_grad_accum does it
+            const f32x4 acc = ld_nt<f32x4>(grad, q);
+            const u32x2 lb = ld_nt<u32x2>(last, q);
+            return f32x4{accum_elem(acc.x, bf16_lo(lb.x), false), accum_elem(acc.y, bf16_hi(lb.x), false),
+                         accum_elem(acc.z, bf16_lo(lb.y), false), accum_elem(acc.w, bf16_hi(lb.y), false)};
         }
     }
 
     template <bool kHasDelta>
     __device__ __forceinline__ void vector_tile(uint64_t master, uint64_t m, uint64_t v,
-                                                uint64_t grad, uint64_t weight, uint64_t orig,
-                                                uint64_t delta, int64_t base) const {
+                                                uint64_t grad, uint64_t last, uint64_t weight,
+                                                uint64_t orig, uint64_t delta, int64_t base) const {
         f32x4 w4[kUnroll], m4[kUnroll], v4[kUnroll], g4[kUnroll];
         u32x2 o2[kUnroll];
         const int64_t lane = int64_t(threadIdx.x) * kVec;
@@ -171,12 +192,7 @@ struct AdamwTile {
             w4[u] = ld_nt<f32x4>(master, q);
             m4[u] = ld_nt<f32x4>(m, q);
             v4[u] = ld_nt<f32x4>(v, q);
-            if constexpr (kGradF32) {
-                g4[u] = ld_nt<f32x4>(grad, q);
-            } else {
-                const u32x2 gb = ld_nt<u32x2>(grad, q);
-                g4[u] = f32x4{bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
-            }
+            g4[u] = load_grad4(grad, last, q);
             if constexpr (kHasDelta) o2[u] = ld_nt<u32x2>(orig, q);
         }
 
@@ -210,8 +226,8 @@ struct AdamwTile {
     // Partial tiles and segments whose arrays are not vector-aligned: one
     // element at a time, same lane-to-element map as the vector path.
     __device__ __forceinline__ void element_tile(uint64_t master, uint64_t m, uint64_t v,
-                                                 uint64_t grad, uint64_t weight, uint64_t orig,
-                                                 uint64_t delta, int64_t base,
+                                                 uint64_t grad, uint64_t last, uint64_t weight,
+                                                 uint64_t orig, uint64_t delta, int64_t base,
                                                  int64_t numel) const {
 #pragma clang fp contract(off)
         const int64_t lane = int64_t(threadIdx.x) * kVec;
@@ -220,10 +236,12 @@ struct AdamwTile {
                 const int64_t e = base + u * (kBlock * kVec) + lane + k;
                 if (e >= numel) continue;
                 float g;
-                if constexpr (kGradF32)
+                if constexpr (kMode == kGradBf16)
+                    g = bf16_one(as_global<gu16>(grad)[e]);
+                else if constexpr (kMode == kGradF32)
                     g = as_global<gfloat>(grad)[e];
                 else
-                    g = bf16_one(as_global<gu16>(grad)[e]);
+                    g = accum_elem(as_global<gfloat>(grad)[e], bf16_one(as_global<gu16>(last)[e]), false);
                 float w = as_global<gfloat>(master)[e];
                 float mm = as_global<gfloat>(m)[e];
                 float vv = as_global<gfloat>(v)[e];
@@ -238,10 +256,10 @@ struct AdamwTile {
     }
 };
 
-template <bool kGradF32, bool kDelta>
+template <GradMode kMode, bool kDelta>
 __global__ __launch_bounds__(kBlock) void adamw_tile_kernel(const void *table, int nseg,
                                                             uint32_t tile0, AdamwConsts c) {
-    tile_of_block(table, nseg, tile0, AdamwTile<kGradF32, kDelta>{c});
+    tile_of_block(table, nseg, tile0, AdamwTile<kMode, kDelta>{c});
 }
 
 // ------------------------------------------------------ accumulation
@@ -298,6 +316,52 @@ __global__ __launch_bounds__(kBlock) void accum_tile_kernel(const void *table, i
     tile_of_block(table, nseg, tile0, AccumTile<kOverwrite>{});
 }
 
+// ------------------------------------------------------------ merge delta
+
+// merged = bf16 nearest-even of (f32(base) + delta): one binary32 addition.
+struct MergeTile {
+    __device__ __forceinline__ void operator()(const SegRec &r, uint32_t local_tile) const {
+#pragma clang fp contract(off)
+        const uint64_t base_w = r.p[0], delta = r.p[1], merged = r.p[2];
+        const int64_t numel = r.numel;
+        const int64_t base = int64_t(local_tile) * kTile;
+        const int64_t lane = int64_t(threadIdx.x) * kVec;
+        const bool vector_ok = base + kTile <= numel && ((base_w | merged) & 7) == 0 &&
+                               (delta & 15) == 0;
+        if (vector_ok) {
+            u32x2 b2[kUnroll];
+            f32x4 d4[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
+                b2[u] = ld_nt<u32x2>(base_w, q);
+                d4[u] = ld_nt<f32x4>(delta, q);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
+                const float s0 = bf16_lo(b2[u].x) + d4[u].x, s1 = bf16_hi(b2[u].x) + d4[u].y;
+                const float s2 = bf16_lo(b2[u].y) + d4[u].z, s3 = bf16_hi(b2[u].y) + d4[u].w;
+                st_nt<u32x2>(merged, q, u32x2{to_bf16_pair(s0, s1), to_bf16_pair(s2, s3)});
+            }
+        } else {
+            for (int u = 0; u < kUnroll; ++u) {
+                for (int k = 0; k < kVec; ++k) {
+                    const int64_t e = base + u * (kBlock * kVec) + lane + k;
+                    if (e >= numel) continue;
+                    const float sum = bf16_one(as_global<gu16>(base_w)[e]) + as_global<gfloat>(delta)[e];
+                    as_global<gu16>(merged)[e] = to_bf16_one(sum);
+                }
+            }
+        }
+    }
+};
+
+__global__ __launch_bounds__(kBlock) void merge_tile_kernel(const void *table, int nseg,
+                                                            uint32_t tile0) {
+    tile_of_block(table, nseg, tile0, MergeTile{});
+}
+
 // ------------------------------------------------- measurement aids
 
 // Plain copy, one 16-byte vector per lane and one 256-lane workgroup per
@@ -335,15 +399,18 @@ __global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restr
 // Launches go through hipLaunchKernel, which returns the launch status
 // directly instead of through the thread's sticky last-error slot.  Grids
 // larger than kMaxBlocksPerLaunch are split into consecutive launches.
-hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, bool grad_f32,
+hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradMode grad_mode,
                         bool with_delta, const AdamwConsts &c, hipStream_t stream) {
     const void *fn;
-    if (grad_f32)
-        fn = with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<true, true>)
-                        : reinterpret_cast<const void *>(&adamw_tile_kernel<true, false>);
-    else
-        fn = with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<false, true>)
-                        : reinterpret_cast<const void *>(&adamw_tile_kernel<false, false>);
+#define LEMA_PICK(M) with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<M, true>) \
+                                : reinterpret_cast<const void *>(&adamw_tile_kernel<M, false>)
+    switch (grad_mode) {
+    case kGradBf16: fn = LEMA_PICK(kGradBf16); break;
+    case kGradF32: fn = LEMA_PICK(kGradF32); break;
+    case kGradF32PlusBf16: fn = LEMA_PICK(kGradF32PlusBf16); break;
+    default: return hipErrorInvalidValue;
+    }
+#undef LEMA_PICK
     AdamwConsts consts = c;
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
         const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
@@ -363,6 +430,18 @@ hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles, bool 
         const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
         void *args[] = {&table, &nseg, &tile0};
         hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, 0, stream);
+        if (e != hipSuccess) return e;
+        tile0 += n;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream) {
+    for (uint32_t tile0 = 0; tile0 < total_tiles;) {
+        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
+        void *args[] = {&table, &nseg, &tile0};
+        hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&merge_tile_kernel), dim3(n),
+                                       dim3(kBlock), args, 0, stream);
         if (e != hipSuccess) return e;
         tile0 += n;
     }

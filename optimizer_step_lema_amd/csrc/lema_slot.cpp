@@ -261,8 +261,8 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
         if (e == hipSuccess) e = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
         if (e != hipSuccess) return hip_failed(e);
         std::vector<SegRec> recs;
-        adamw_records(dev_segs[i].data(), int32_t(dev_segs[i].size()), &recs);
-        st = launch_adamw_recs(recs, consts, false, pool->compute);
+        adamw_records(dev_segs[i].data(), int32_t(dev_segs[i].size()), &recs, nullptr);
+        st = launch_adamw_recs(recs, consts, kGradBf16, pool->compute);
         if (st != LEMA_OK) return st;
         e = hipEventRecord(ev(i, EV_K_END), pool->compute);
         if (e != hipSuccess) return hip_failed(e);

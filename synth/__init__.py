@@ -20,6 +20,10 @@ Workloads (tensor shapes from the models the LEMA README trains):
 * ``llama7b_full``  -- the whole Llama-2-7B shape: embedding [32000 x 4096],
   32 decoder layers as above, final RMSNorm [4096], LM head [32000 x 4096];
   291 segments, 6,738,415,616 parameters; t = 10.
+* ``llama7b_lora_r16``  -- rank-16 LoRA adapters (README "Quick Start":
+  ``lora_rank=16`` with torch.optim.AdamW over the adapters) on all seven
+  linear projections of the 32 Llama-2-7B layers: per projection A
+  [16 x in] and B [out x 16]; 448 segments, 39,976,960 parameters; t = 10.
 
 Distributions: gradient bf16 = bf16(N(0, 1e-3)) (drawn in fp32, converted
 by torch), master ~ N(0, 0.02), m ~ N(0, 1e-4), v = N(0, 1e-3)^2 (square of
@@ -103,6 +107,18 @@ def _llama_attn_last4():
     return segs
 
 
+def _llama_lora_r16():
+    h, f, r = 4096, 11008, 16
+    shapes = {"q_proj": (h, h), "k_proj": (h, h), "v_proj": (h, h), "o_proj": (h, h),
+              "gate_proj": (f, h), "up_proj": (f, h), "down_proj": (h, f)}
+    segs = []
+    for layer in range(32):
+        for name, (out_f, in_f) in shapes.items():
+            segs.append((f"layers.{layer}.{name}.lora_A", (r, in_f)))
+            segs.append((f"layers.{layer}.{name}.lora_B", (out_f, r)))
+    return segs
+
+
 def _llama_full():
     segs = [("embed_tokens", (32000, 4096))]
     for layer in range(32):
@@ -129,6 +145,10 @@ WORKLOADS = {
         "llama7b_full", 4, _llama_full(), step=10,
         description="whole Llama-2-7B shape, 291 tensors resident, bf16 "
                     "grad, t=10"),
+    "llama7b_lora_r16": Workload(
+        "llama7b_lora_r16", 5, _llama_lora_r16(), step=10,
+        description="rank-16 LoRA adapters on all 7 linear projections of 32 "
+                    "Llama-2-7B layers: 448 tensors, bf16 grad, t=10"),
 }
 
 

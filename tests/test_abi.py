@@ -198,3 +198,38 @@ def test_valid_call_without_gpu_reports_hip_error(lib):
     s = fake_seg(1 << 32, 10)
     assert call(lib, [s]) == N.LEMA_ERR_HIP
     assert lib.lema_last_hip_error() != 0
+
+
+def test_step_accum_validation(lib):
+    a16 = args(grad_dtype=N.LEMA_GRAD_BF16)
+    a32 = args(grad_dtype=N.LEMA_GRAD_FP32)
+    s = fake_seg(1 << 32, 100)
+    arr = (N.AdamwSeg * 1)(s)
+    last = (ctypes.c_void_p * 1)(1 << 40)
+    assert lib.lema_adamw_step_accum(arr, last, 1, ctypes.byref(a16), None) == N.LEMA_ERR_DTYPE
+    assert lib.lema_adamw_step_accum(arr, None, 1, ctypes.byref(a32), None) == N.LEMA_ERR_NULL
+    nul = (ctypes.c_void_p * 1)(0)
+    assert lib.lema_adamw_step_accum(arr, nul, 1, ctypes.byref(a32), None) == N.LEMA_ERR_NULL
+    odd = (ctypes.c_void_p * 1)((1 << 40) + 1)
+    assert lib.lema_adamw_step_accum(arr, odd, 1, ctypes.byref(a32), None) == N.LEMA_ERR_ALIGN
+    over = (ctypes.c_void_p * 1)(s.weight_bf16 + 10)     # last overlaps a written array
+    assert lib.lema_adamw_step_accum(arr, over, 1, ctypes.byref(a32), None) == N.LEMA_ERR_OVERLAP
+    shared = (ctypes.c_void_p * 1)(s.grad)               # reading the accumulator twice is fine
+    assert lib.lema_adamw_step_accum(arr, shared, 1, ctypes.byref(a32), None) != N.LEMA_ERR_OVERLAP
+    assert lib.lema_adamw_step_accum(None, None, 0, ctypes.byref(a32), None) == N.LEMA_OK
+
+
+def test_merge_validation(lib):
+    assert lib.lema_merge_delta(None, 1, None) == N.LEMA_ERR_NULL
+    assert lib.lema_merge_delta(None, -1, None) == N.LEMA_ERR_SIZE
+    assert lib.lema_merge_delta(None, 0, None) == N.LEMA_OK
+    s = N.MergeSeg(1 << 32, 1 << 33, 0, 10)
+    assert lib.lema_merge_delta(ctypes.byref(s), 1, None) == N.LEMA_ERR_NULL
+    s = N.MergeSeg((1 << 32) + 1, 1 << 33, 1 << 34, 10)
+    assert lib.lema_merge_delta(ctypes.byref(s), 1, None) == N.LEMA_ERR_ALIGN
+    s = N.MergeSeg(1 << 32, (1 << 33) + 2, 1 << 34, 10)
+    assert lib.lema_merge_delta(ctypes.byref(s), 1, None) == N.LEMA_ERR_ALIGN
+    s = N.MergeSeg(1 << 32, 1 << 33, (1 << 32) + 4, 10)        # output over the base
+    assert lib.lema_merge_delta(ctypes.byref(s), 1, None) == N.LEMA_ERR_OVERLAP
+    s = N.MergeSeg(1 << 32, 1 << 33, 1 << 34, -3)
+    assert lib.lema_merge_delta(ctypes.byref(s), 1, None) == N.LEMA_ERR_SIZE

@@ -36,6 +36,7 @@ def test_state_layout_is_16_bytes():
     ("llama7b_attn_last4", 268_435_456, 16),
     ("llama7b_layer", 202_383_360, 9),
     ("llama7b_full", 6_738_415_616, 291),
+    ("llama7b_lora_r16", 39_976_960, 448),
 ])
 def test_workload_sizes(name, params, nseg):
     w = synth.WORKLOADS[name]

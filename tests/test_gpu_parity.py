@@ -236,6 +236,82 @@ def test_accumulation_eight_microbatches(L, offset):
         compare_f32(to_np(accs[i]), ref, f"acc{i}")
 
 
+@pytest.mark.parametrize("offset", [0, 1])
+def test_fused_last_microbatch(L, offset):
+    """Step on acc + f32(last) in one pass == accumulate(last) then step, bit for bit;
+    the accumulator itself is left untouched."""
+    sizes = [5, 256, 257, 4097, 100003, 0, 3 * 65536 + 17]
+    segs, _ = build_segments(L, sizes, 81, grad_f32=True, delta={0, 3, 4}, offset=offset)
+    lasts = [_bf16(n, 1e-3, 7000 + i, offset) for i, n in enumerate(sizes)]
+    twin = _clone_segs(L, segs)
+    acc_before = [to_np(s.grad).copy() for s in segs]
+    snaps = [{"master": to_np(s.master), "m": to_np(s.exp_avg), "v": to_np(s.exp_avg_sq),
+              "orig": None if s.orig is None else to_np(s.orig)} for s in segs]
+    L.adamw_step(segs, step=9, last_grads=lasts, **HP)
+    # the two-call path on the twin
+    L.grad_accum([L.AccumSegment(t.grad, g) for t, g in zip(twin, lasts)], overwrite=False)
+    L.adamw_step(twin, step=9, **HP)
+    torch.cuda.synchronize()
+    consts = oracle_consts(HP, 9)
+    for i, (s, t) in enumerate(zip(segs, twin)):
+        assert np.array_equal(to_np(s.grad).view(np.uint32), acc_before[i].view(np.uint32))
+        g = acc_before[i].copy()
+        oracle.grad_accum(g, to_np(lasts[i]), overwrite=False)
+        ref = oracle_segment(snaps[i]["master"], snaps[i]["m"], snaps[i]["v"], g, consts,
+                             snaps[i]["orig"])
+        tag = f"fused seg{i}"
+        compare_f32(to_np(s.master), ref["master"], tag + ".master")
+        compare_f32(to_np(s.exp_avg), ref["m"], tag + ".m")
+        compare_f32(to_np(s.exp_avg_sq), ref["v"], tag + ".v")
+        compare_bf16(to_np(s.weight), ref["weight"], tag + ".weight")
+        if s.delta is not None:
+            compare_f32(to_np(s.delta), ref["delta"], tag + ".delta")
+        for f in ("master", "exp_avg", "exp_avg_sq", "weight"):
+            assert _same(getattr(s, f), getattr(t, f)), (i, f)
+
+
+# ------------------------------------------------------------ merge delta
+
+@pytest.mark.parametrize("offset", [0, 1, 2])
+def test_merge_delta_ragged(L, offset):
+    sizes = [0, 1, 3, 255, 256, 257, 4097, 100003]
+    bases = [_bf16(n, 0.02, 8100 + i, offset) for i, n in enumerate(sizes)]
+    deltas = [_f32(n, 1e-4, 8200 + i, offset) for i, n in enumerate(sizes)]
+    deltas[7][:6] = torch.tensor([float("nan"), float("inf"), -float("inf"), 0.0, -0.0, 1e-42],
+                                 device=DEV)
+    outs = [_empty(n, torch.bfloat16, offset) for n in sizes]
+    L.merge_delta([L.MergeSegment(b, d, o) for b, d, o in zip(bases, deltas, outs)])
+    torch.cuda.synchronize()
+    for i, (b, d, o) in enumerate(zip(bases, deltas, outs)):
+        compare_bf16(to_np(o), oracle.merge_delta(to_np(b), to_np(d)), f"merge{i}")
+
+
+def test_merge_delta_reproduces_step_weight(L):
+    """A step's delta merged onto its base gives the step's bf16 weight back
+    wherever the subtraction was exact (README merge_delta), and equals the
+    oracle's merge everywhere."""
+    w = synth.WORKLOADS["llama7b_attn_last4"]
+    segs = _workload_segments(L, w, True)[:4]
+    L.adamw_step(segs, step=w.step, **HP)
+    merged = [torch.empty_like(s.weight) for s in segs]
+    L.merge_delta([L.MergeSegment(s.orig, s.delta, m) for s, m in zip(segs, merged)])
+    torch.cuda.synchronize()
+    for i, (s, m) in enumerate(zip(segs, merged)):
+        b = to_np(s.orig)
+        d = to_np(s.delta)
+        got = to_np(m)
+        compare_bf16(got, oracle.merge_delta(b, d), f"merge{i}")
+        wgt = to_np(s.weight)
+        base = oracle.bf16_to_f32(b).astype(np.float64)
+        new = to_np(s.master).astype(np.float64)
+        exact = (np.sign(new) == np.sign(base)) & (np.abs(new) <= 2 * np.abs(base)) & \
+                (np.abs(base) <= 2 * np.abs(new))
+        assert exact.mean() > 0.99
+        assert np.array_equal(got[exact], wgt[exact])
+    del segs
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------- invariances
 
 def _clone_segs(L, segs):
@@ -314,6 +390,30 @@ def test_split_permute_pack_invariance(L):
         assert _same(cat(getattr(ref[0], f), getattr(ref[1], f)), getattr(packed, f)), f
 
 
+def test_plans_match_direct_calls(L):
+    """AdamwPlan / AccumPlan (arguments marshalled once) == the direct calls."""
+    sizes = [4099, 256, 70001]
+    segs, _ = build_segments(L, sizes, 91, grad_f32=True, delta={1})
+    twin = _clone_segs(L, segs)
+    lasts = [_bf16(n, 1e-3, 9100 + i) for i, n in enumerate(sizes)]
+    plan = L.AdamwPlan(segs)
+    fused = L.AdamwPlan(segs, last_grads=lasts)
+    acc_plan = L.AccumPlan([L.AccumSegment(s.grad, g) for s, g in zip(segs, lasts)])
+    for t in (1, 2, 3):
+        plan.step(step=t, **HP)
+        L.adamw_step(twin, step=t, **HP)
+    fused.step(step=4, **HP)
+    L.adamw_step(twin, step=4, last_grads=lasts, **HP)
+    acc_plan.run(overwrite=False)
+    L.grad_accum([L.AccumSegment(s.grad, g) for s, g in zip(twin, lasts)], overwrite=False)
+    torch.cuda.synchronize()
+    for a, b in zip(segs, twin):
+        for f in ("master", "exp_avg", "exp_avg_sq", "grad", "weight"):
+            assert _same(getattr(a, f), getattr(b, f)), f
+        if a.delta is not None:
+            assert _same(a.delta, b.delta)
+
+
 def test_table_cache_many_lists_and_streams(L):
     """More distinct segment lists than cached tables, alternating two streams.
 
@@ -385,6 +485,17 @@ def test_gpt2_cattn_full(L, with_delta):
     L.adamw_step(segs, step=w.step, **HP)
     torch.cuda.synchronize()
     check_segments(segs, snaps, oracle_consts(HP, w.step), "gpt2 ")
+
+
+def test_llama7b_lora_r16_full(L):
+    """448 rank-16 LoRA adapter tensors in one call (t=10): every element."""
+    w = synth.WORKLOADS["llama7b_lora_r16"]
+    segs = _workload_segments(L, w, True)
+    snaps = [{"master": to_np(s.master), "m": to_np(s.exp_avg), "v": to_np(s.exp_avg_sq),
+              "grad": to_np(s.grad), "orig": to_np(s.orig)} for s in segs]
+    L.adamw_step(segs, step=w.step, **HP)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(HP, w.step), "lora ")
 
 
 def test_llama7b_attn_last4_full(L):
