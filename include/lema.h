@@ -252,6 +252,9 @@ typedef struct {
     double copy_busy_ms;          /* time at least one copy was running     */
     double wall_ms;               /* first copy start .. last copy end      */
     double last_kernel_ms;        /* duration of the last layer's kernel    */
+    double host_in_ms;            /* staged only: host copies into staging  */
+    double host_out_ms;           /* staged only: host copies out of staging */
+    double call_ms;               /* host clock over the whole call         */
 } lema_stream_stats;
 
 /*
@@ -265,6 +268,25 @@ typedef struct {
  */
 lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int32_t nlayers,
                              const lema_adamw_args *args, lema_stream_stats *stats);
+
+/*
+ * lema_slot_stream for host state that is not page-locked: ordinary memory or
+ * a memory-mapped file (the disk tier of the LEMA README's "Triple-Buffer
+ * Pipeline: Disk -> pinned RAM -> VRAM"; "Selective Full Fine-Tuning": fp32
+ * states in RAM with an mmap disk backend).  Layer i moves
+ *   caller memory -> page-locked staging[i mod 2] -> slot[i mod 2]
+ * and back the same way; `host_threads` host threads (0 = up to 16) do the
+ * copies between the caller's memory and the two staging buffers, which the
+ * pool allocates on first use (2 x slot_bytes of page-locked memory) and frees
+ * with the pool.  The host copies of one layer overlap the DMA and kernel
+ * work of the neighbouring layers.  Blocks until every layer is written back.
+ * Same arguments and errors as lema_slot_stream, except that host memory need
+ * not be page-locked (no LEMA_ERR_NOT_PINNED); LEMA_ERR_SIZE also for
+ * host_threads outside 0..256.
+ */
+lema_status lema_slot_stream_staged(lema_slot_pool *pool, const lema_layer *layers,
+                                    int32_t nlayers, const lema_adamw_args *args,
+                                    int32_t host_threads, lema_stream_stats *stats);
 
 /* Page-locked host allocation of exactly `bytes` bytes (hipHostMalloc). */
 lema_status lema_host_alloc(void **out, size_t bytes);

@@ -62,7 +62,8 @@ class Layer(ctypes.Structure):
 class StreamStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in (
         "h2d_bytes", "d2h_bytes", "h2d_ms", "d2h_ms", "kernel_ms",
-        "copy_busy_ms", "wall_ms", "last_kernel_ms")]
+        "copy_busy_ms", "wall_ms", "last_kernel_ms", "host_in_ms", "host_out_ms",
+        "call_ms")]
 
 
 # (name, restype, argtypes) of every exported function
@@ -81,6 +82,8 @@ SIGNATURES = [
     ("lema_slot_pool_set_writeback_stream", i32, [vp, vp]),
     ("lema_slot_stream", i32, [vp, ctypes.POINTER(Layer), i32, ctypes.POINTER(AdamwArgs),
                                ctypes.POINTER(StreamStats)]),
+    ("lema_slot_stream_staged", i32, [vp, ctypes.POINTER(Layer), i32, ctypes.POINTER(AdamwArgs),
+                                      i32, ctypes.POINTER(StreamStats)]),
     ("lema_host_alloc", i32, [ctypes.POINTER(vp), ctypes.c_size_t]),
     ("lema_host_free", i32, [vp]),
     ("lema_measure_copy", i32, [vp, vp, ctypes.c_size_t, vp]),

@@ -275,9 +275,12 @@ class SlotPool:
                     "lema_slot_pool_set_writeback_stream")
 
     def stream(self, layers: Sequence[Sequence[AdamwSegment]], *, lr, beta1=0.9, beta2=0.999,
-               eps=1e-8, weight_decay=0.01, step) -> dict:
+               eps=1e-8, weight_decay=0.01, step, staged: bool = False,
+               host_threads: int = 0) -> dict:
         """One AdamW step for every layer, streamed host -> slot -> host.
-        Blocks until done; returns the timing statistics."""
+        Blocks until done; returns the timing statistics.  With staged=True
+        the host state may be ordinary or memory-mapped memory, moved through
+        the pool's page-locked staging buffers (lema_slot_stream_staged)."""
         lib = N.load()
         keep = []
         c_layers = (N.Layer * max(1, len(layers)))()
@@ -287,8 +290,13 @@ class SlotPool:
             c_layers[i] = N.Layer(ctypes.cast(arr, ctypes.POINTER(N.AdamwSeg)), len(segs))
         args = _args(lr, beta1, beta2, eps, weight_decay, step, N.LEMA_GRAD_BF16)
         st = N.StreamStats()
-        N.check(lib.lema_slot_stream(self.handle, c_layers, len(layers), ctypes.byref(args),
-                                     ctypes.byref(st)), "lema_slot_stream")
+        if staged:
+            N.check(lib.lema_slot_stream_staged(self.handle, c_layers, len(layers),
+                                                ctypes.byref(args), int(host_threads),
+                                                ctypes.byref(st)), "lema_slot_stream_staged")
+        else:
+            N.check(lib.lema_slot_stream(self.handle, c_layers, len(layers), ctypes.byref(args),
+                                         ctypes.byref(st)), "lema_slot_stream")
         return {name: getattr(st, name) for name, _ in N.StreamStats._fields_}
 
     def close(self):

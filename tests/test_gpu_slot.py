@@ -172,3 +172,87 @@ def test_slot_stream_duplex_llama_layers(L):
           f"copy busy {stats['copy_busy_ms']:.1f} ms, last kernel {stats['last_kernel_ms']:.3f} ms")
     assert stats["wall_ms"] - stats["copy_busy_ms"] <= 1.05 * stats["last_kernel_ms"] + 1.0
     pool.close()
+
+
+# --------------------------------------------------- staged (pageable / mmap)
+
+def pageable_layer(sizes, seed, alloc=None):
+    """One layer in ordinary (pageable) host memory, or in tensors from alloc(n, dtype)."""
+    segs, snaps = [], []
+    for i, n in enumerate(sizes):
+        s = 100 * seed + 10 * i
+        dev = {"master": synth.normal(n, 0.02, s, DEV), "m": synth.normal(n, 1e-4, s + 1, DEV),
+               "v": synth.normal(n, 1e-3, s + 2, DEV).square_(),
+               "g": synth.bf16_normal(n, 1e-3, s + 3, DEV)}
+        make = alloc or (lambda k, dt: torch.empty(k, dtype=dt))
+        host = {k: make(n, t.dtype) for k, t in dev.items()}
+        for k in dev:
+            host[k].copy_(dev[k])
+        import optimizer_step_lema_amd as lema
+        segs.append(lema.AdamwSegment(host["master"], host["m"], host["v"], host["g"],
+                                      make(n, torch.bfloat16)))
+        snaps.append({"master": to_np(host["master"]).copy(), "m": to_np(host["m"]).copy(),
+                      "v": to_np(host["v"]).copy(), "grad": to_np(host["g"]).copy()})
+    return segs, snaps
+
+
+@pytest.mark.parametrize("duplex,threads", [(False, 0), (True, 3), (False, 1)])
+def test_slot_stream_staged_pageable(L, duplex, threads):
+    """Pageable host state through the page-locked staging buffers."""
+    shapes = [[100003, 4096, 2048 * 3 + 1], [777, 1 << 20], [1, 2, 3, 300000], [5000],
+              [1 << 20, 17]]
+    layers, snaps = zip(*[pageable_layer(s, 110 + i) for i, s in enumerate(shapes)])
+    pool = L.SlotPool(max(layer_bytes(s) for s in shapes), nslots=2, duplex=duplex)
+    stats = pool.stream(layers, step=6, staged=True, host_threads=threads, **HP)
+    check_layers(layers, snaps, 6)
+    P = sum(sum(s) for s in shapes)
+    assert stats["h2d_bytes"] == 14 * P and stats["d2h_bytes"] == 14 * P
+    assert stats["call_ms"] >= stats["wall_ms"] > 0
+    # a second step on the evolved state: the staging buffers are reused
+    snaps2 = [[{"master": to_np(s.master).copy(), "m": to_np(s.exp_avg).copy(),
+                "v": to_np(s.exp_avg_sq).copy(), "grad": to_np(s.grad).copy()} for s in segs]
+              for segs in layers]
+    pool.stream(layers, step=7, staged=True, host_threads=threads, **HP)
+    check_layers(layers, snaps2, 7)
+    pool.close()
+
+
+def test_slot_stream_staged_memory_mapped(L, tmp_path):
+    """Host state in memory-mapped files (the disk tier): results land in the files."""
+    files = []
+
+    def mapped(n, dtype):
+        np_dtype = {torch.float32: np.float32, torch.bfloat16: np.uint16}[dtype]
+        path = tmp_path / f"arr{len(files)}.bin"
+        mm = np.memmap(path, dtype=np_dtype, mode="w+", shape=(n,))
+        files.append((path, mm))
+        t = torch.from_numpy(mm)
+        return t.view(torch.bfloat16) if dtype == torch.bfloat16 else t
+
+    shapes = [[65536 * 3 + 5, 4096], [300001], [4096, 4096, 7]]
+    layers, snaps = zip(*[pageable_layer(s, 130 + i, alloc=mapped) for i, s in enumerate(shapes)])
+    pool = L.SlotPool(max(layer_bytes(s) for s in shapes), nslots=2)
+    pool.stream(layers, step=3, staged=True, **HP)
+    check_layers(layers, snaps, 3)
+    # re-read one array from its file: the update reached the mapped pages
+    for _, mm in files:
+        mm.flush()
+    path0 = files[0][0]
+    again = np.fromfile(path0, dtype=np.float32)
+    assert np.array_equal(again.view(np.uint32), to_np(layers[0][0].master).view(np.uint32))
+    pool.close()
+
+
+def test_slot_stream_staged_llama_layers(L):
+    """Four real Llama-2-7B layers from pageable memory, duplex write-back."""
+    w = synth.WORKLOADS["llama7b_layer"]
+    sizes = w.numels
+    layers, snaps = zip(*[pageable_layer(sizes, 150 + i) for i in range(4)])
+    pool = L.SlotPool(layer_bytes(sizes), nslots=2, duplex=True)
+    stats = pool.stream(layers, step=10, staged=True, **HP)
+    check_layers(layers, snaps, 10, sample=20000)
+    print(f"staged slot stream 4 Llama layers: call {stats['call_ms']:.1f} ms, GPU span "
+          f"{stats['wall_ms']:.1f} ms, host in {stats['host_in_ms']:.1f} ms, host out "
+          f"{stats['host_out_ms']:.1f} ms, H2D {stats['h2d_ms']:.1f} ms, D2H {stats['d2h_ms']:.1f} ms, "
+          f"kernel {stats['kernel_ms']:.2f} ms")
+    pool.close()
