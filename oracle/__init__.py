@@ -74,6 +74,10 @@ def _load():
     lib.oracle_accum.restype = None
     lib.oracle_merge_delta.argtypes = [i64, vp, vp, vp]
     lib.oracle_merge_delta.restype = None
+    lib.oracle_quantize_rows.argtypes = [i64, i64, vp, vp, vp]
+    lib.oracle_quantize_rows.restype = None
+    lib.oracle_dequantize_rows.argtypes = [i64, i64, vp, vp, vp]
+    lib.oracle_dequantize_rows.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     _lib = lib
@@ -178,3 +182,88 @@ def merge_delta(base_bf16: np.ndarray, delta: np.ndarray) -> np.ndarray:
     out = np.empty(n, dtype=np.uint16)
     _load().oracle_merge_delta(n, _ptr(base_bf16), _ptr(delta), _ptr(out))
     return out
+
+
+# ------------------------------------------------- int8 rows with scales
+
+def n_rows(n: int, row_len: int) -> int:
+    """Rows of a tensor of n elements cut into rows of row_len (last may be short)."""
+    if row_len < 1:
+        raise ValueError("row_len must be >= 1")
+    return (n + row_len - 1) // row_len
+
+
+def quantize_rows(x: np.ndarray, row_len: int):
+    """fp32 -> (int8 codes, fp32 per-row scales): symmetric absmax, 127 levels.
+
+    LEMA README "Quantization" (int8 + per-row scale for optimizer states and
+    accumulators); the exact reading is stated in ``lema_oracle.c``.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1)
+    n = x.shape[0]
+    q = np.empty(n, dtype=np.int8)
+    scale = np.empty(n_rows(n, row_len), dtype=np.float32)
+    _load().oracle_quantize_rows(n, row_len, _ptr(x), _ptr(q), _ptr(scale))
+    return q, scale
+
+
+def dequantize_rows(q: np.ndarray, scale: np.ndarray, row_len: int) -> np.ndarray:
+    """(int8 codes, per-row scales) -> fp32: x = f32(q) * scale[row]."""
+    n = q.shape[0]
+    _check(q, np.int8, n, "q")
+    _check(scale, np.float32, n_rows(n, row_len), "scale")
+    out = np.empty(n, dtype=np.float32)
+    _load().oracle_dequantize_rows(n, row_len, _ptr(q), _ptr(scale), _ptr(out))
+    return out
+
+
+def adamw_step_q8(master: np.ndarray, m, v, grad, consts: np.ndarray, row_len: int,
+                  orig: np.ndarray | None = None):
+    """One AdamW step with int8 moments and/or an int8 gradient accumulator.
+
+    The step of the README's "Quantization" section: quantized classes are
+    dequantized, the ordinary fp32 step (``adamw_step``) runs, and the new
+    moments are quantized again.
+      master     : fp32, updated in place
+      m, v       : each an fp32 array (updated in place) or a tuple
+                   (int8 codes, fp32 row scales) whose arrays are overwritten
+                   with the requantized moment
+      grad       : bf16 patterns (uint16), an fp32 accumulator, or a tuple
+                   (int8 codes, fp32 row scales) of a quantized accumulator
+    Returns ``(weight_bf16, delta)`` as ``adamw_step``.
+    """
+    n = master.shape[0]
+    moments = []
+    for arr in (m, v):
+        if isinstance(arr, tuple):
+            moments.append(dequantize_rows(arr[0], arr[1], row_len))
+        else:
+            moments.append(arr)
+    if isinstance(grad, tuple):
+        grad = dequantize_rows(grad[0], grad[1], row_len)
+    m32, v32 = moments
+    _check(m32, np.float32, n, "m")
+    weight, delta = adamw_step(master, m32, v32, grad, consts, orig=orig)
+    for arr, new in ((m, m32), (v, v32)):
+        if isinstance(arr, tuple):
+            q, s = quantize_rows(new, row_len)
+            arr[0][...] = q
+            arr[1][...] = s
+    return weight, delta
+
+
+def grad_accum_q8(acc_q: np.ndarray, acc_scale: np.ndarray, grad_bf16: np.ndarray,
+                  overwrite: bool, row_len: int) -> None:
+    """int8 accumulator += bf16 micro-batch, in place: dequantize, the fp32
+    accumulation of ``grad_accum``, quantize again (README "Quantization":
+    grad_acc_bits = 8)."""
+    n = acc_q.shape[0]
+    _check(acc_q, np.int8, n, "acc_q", True)
+    if overwrite:
+        acc = np.zeros(n, dtype=np.float32)
+    else:
+        acc = dequantize_rows(acc_q, acc_scale, row_len)
+    grad_accum(acc, grad_bf16, overwrite)
+    q, s = quantize_rows(acc, row_len)
+    acc_q[...] = q
+    acc_scale[...] = s

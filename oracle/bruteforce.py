@@ -112,3 +112,84 @@ def merge_delta(base_bf16, delta):
         for i in range(len(base_bf16)):
             out[i] = to_bf16_bits(F(from_bf16_bits(base_bf16[i]) + F(delta[i])))
     return out
+
+
+# ------------------------------------------------- int8 rows with scales
+#
+# Symmetric absmax int8 with one fp32 scale per row (README "Quantization",
+# the int8 + per-row-scale storage of moments and accumulators), restated
+# with Python integers and numpy float32 scalars: the absmax by comparing
+# magnitudes one at a time, the half-to-even rounding by Python's round() on
+# the exactly widened quotient.
+
+def quantize_row(xs):
+    """list of fp32 values -> (list of int codes, fp32 scale)."""
+    a = F(0.0)
+    nan = False
+    for x in xs:
+        mag = abs(F(x))
+        if mag != mag:
+            nan = True
+        elif mag > a:
+            a = mag
+    with np.errstate(all="ignore"):
+        s = F(np.nan) if nan else F(a / F(127.0))
+        usable = bool(np.isfinite(s)) and s > 0
+        codes = []
+        for x in xs:
+            if not usable:
+                codes.append(0)
+                continue
+            k = round(float(F(F(x) / s)))      # round() on a float: ties to even
+            codes.append(max(-127, min(127, k)))
+    return codes, s
+
+
+def quantize(x, row_len):
+    """1-D fp32 array -> (int8 array, fp32 scales), rows of row_len (last short)."""
+    n = len(x)
+    q = np.zeros(n, np.int8)
+    scales = []
+    for lo in range(0, n, row_len):
+        codes, s = quantize_row([x[i] for i in range(lo, min(n, lo + row_len))])
+        q[lo:lo + len(codes)] = codes
+        scales.append(s)
+    return q, np.array(scales, np.float32)
+
+
+def dequantize(q, scales, row_len):
+    out = np.empty(len(q), np.float32)
+    with np.errstate(all="ignore"):
+        for i in range(len(q)):
+            out[i] = F(F(int(q[i])) * scales[i // row_len])
+    return out
+
+
+def adamw_step_q8(master, m_q, m_s, v_q, v_s, grad, c, row_len, orig=None):
+    """Dequantize the moments, loop the fp32 step, quantize the new moments.
+
+    ``grad`` is uint16 (bf16), float32, or a tuple (int8 codes, scales).
+    Returns (master', (m_q', m_s'), (v_q', v_s'), weight_bf16, delta or None).
+    """
+    if isinstance(grad, tuple):
+        grad = dequantize(grad[0], grad[1], row_len)
+    m = dequantize(m_q, m_s, row_len)
+    v = dequantize(v_q, v_s, row_len)
+    w2, m2, v2, wb, d = adamw_step(master, m, v, grad, c, orig)
+    return w2, quantize(m2, row_len), quantize(v2, row_len), wb, d
+
+
+def accumulate_q8(grads_bf16, row_len):
+    """int8 accumulator after each bf16 micro-batch: the first is quantized on
+    its own, every later one is added to the dequantized accumulator."""
+    acc_q, acc_s = None, None
+    for k, g in enumerate(grads_bf16):
+        with np.errstate(all="ignore"):
+            if k == 0:
+                vals = np.array([from_bf16_bits(b) for b in g], np.float32)
+            else:
+                prev = dequantize(acc_q, acc_s, row_len)
+                vals = np.array([F(prev[i] + from_bf16_bits(g[i])) for i in range(len(g))],
+                                np.float32)
+        acc_q, acc_s = quantize(vals, row_len)
+    return acc_q, acc_s

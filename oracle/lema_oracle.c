@@ -220,6 +220,80 @@ void oracle_merge_delta(int64_t n, const uint16_t *base, const float *delta, uin
     }
 }
 
+/* ------------------------------------------------- int8 rows with scales */
+
+/*
+ * The int8 + per-row-scale storage of quantized optimizer moments and
+ * gradient accumulators (LEMA README, "Quantization": opt_state_bits = 8 and
+ * grad_acc_bits = 8 keep these classes as int8 codes with one scale per row,
+ * dequantized only inside the per-layer AdamW step).  The pages name the
+ * format but give no formula; the reading fixed here is symmetric absmax
+ * scaling:
+ *
+ *   A tensor of n elements is cut into rows of row_len consecutive elements
+ *   (the last row may be shorter), rows = ceil(n / row_len).  For a 2-D
+ *   [out x in] weight row_len = in gives the matrix rows.
+ *   Row r holds int8 codes q[i] in [-127, 127] and one fp32 scale s[r].
+ *   dequantize: x[i] = (float)q[i] * s[r]        one binary32 multiplication
+ *   quantize  : a    = max |x[i]| over the row   (NaN if the row has a NaN)
+ *               s[r] = a / 127                   binary32 division
+ *               if s[r] is finite and > 0:
+ *                   q[i] = round-half-even(x[i] / s[r]) clamped to [-127, 127]
+ *                   (x[i] / s[r] is a binary32 division)
+ *               otherwise q[i] = 0 (an all-zero row, an absmax whose division
+ *               underflows to 0, or a row holding an infinity or a NaN; the
+ *               last two dequantize to NaN everywhere since 0*inf and 0*NaN
+ *               are NaN)
+ */
+static float row_absmax(const float *x, int64_t len)
+{
+    float a = 0.0f;
+    int saw_nan = 0;
+    for (int64_t i = 0; i < len; ++i) {
+        float ax = fabsf(x[i]);
+        if (isnan(ax))
+            saw_nan = 1;
+        else if (ax > a)
+            a = ax;
+    }
+    return saw_nan ? NAN : a;
+}
+
+static int8_t quantize_one(float x, float scale)
+{
+    if (!(isfinite(scale) && scale > 0.0f))
+        return 0;
+    float r = x / scale;
+    float k = rintf(r);                /* default rounding mode: half to even */
+    if (k > 127.0f)
+        k = 127.0f;
+    if (k < -127.0f)
+        k = -127.0f;
+    return (int8_t)k;
+}
+
+void oracle_quantize_rows(int64_t n, int64_t row_len, const float *x, int8_t *q, float *scale)
+{
+    int64_t rows = (n + row_len - 1) / row_len;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t lo = r * row_len;
+        int64_t len = (n - lo < row_len) ? n - lo : row_len;
+        float s = row_absmax(x + lo, len) / 127.0f;
+        scale[r] = s;
+        for (int64_t i = 0; i < len; ++i)
+            q[lo + i] = quantize_one(x[lo + i], s);
+    }
+}
+
+void oracle_dequantize_rows(int64_t n, int64_t row_len, const int8_t *q, const float *scale,
+                            float *x)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        x[i] = (float)q[i] * scale[i / row_len];
+}
+
 /* Threads the OpenMP runtime will use for the loops above. */
 int oracle_num_threads(void)
 {

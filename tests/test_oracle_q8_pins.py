@@ -1,0 +1,348 @@
+"""Pins of the oracle's int8 + per-row-scale storage and the quantized step.
+
+LEMA README, "Quantization": with opt_state_bits = 8 and grad_acc_bits = 8
+the Adam moments and the gradient accumulators are kept as int8 with one
+scale per row and dequantized only inside the per-layer AdamW step.  The
+pages name the format but print no formula; the reading pinned here is
+symmetric absmax scaling with 127 levels per sign (stated in full in
+``oracle/lema_oracle.c``).  Every test names the mistake it would catch.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import bruteforce
+import synth
+
+H = synth.HPARAMS
+
+
+def consts(step):
+    return oracle.adamw_constants(H["lr"], H["beta1"], H["beta2"], H["eps"],
+                                  H["weight_decay"], step)
+
+
+def fp32_nearest(fr: Fraction) -> np.float32:
+    """The binary32 value nearest to an exact rational (ties to even), found
+    by bracketing with nextafter from a double estimate."""
+    f = np.float32(float(fr))
+    best = f
+    for cand in (np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))):
+        if abs(Fraction(float(cand)) - fr) < abs(Fraction(float(best)) - fr):
+            best = cand
+        elif abs(Fraction(float(cand)) - fr) == abs(Fraction(float(best)) - fr):
+            if int(np.array(cand).view(np.uint32)) % 2 == 0:
+                best = cand
+    return np.float32(best)
+
+
+# ---------------------------------------------------------------- quantizer
+
+def test_worked_example_power_of_two_scales():
+    """Rows whose absmax is 127 and 254 have scales 1 and 2 exactly, so every
+    quotient is exact and the codes can be written down by hand.  Ties go to
+    the even integer (-63.5 -> -64, 2.5 -> 2, 0.5 -> 0, -0.5 -> 0); rounding
+    half away from zero, 255 levels or a 128 divisor would all differ."""
+    x = np.array([127, -63.5, 0.5, 1.5, 2.5, -2.5, 0, 64,
+                  254, 3, 5, 1, -1, -7, 13, 0], np.float32)
+    q, s = oracle.quantize_rows(x, 8)
+    assert s.tolist() == [1.0, 2.0]
+    assert q.tolist() == [127, -64, 0, 2, 2, -2, 0, 64,
+                          127, 2, 2, 0, 0, -4, 6, 0]
+    back = oracle.dequantize_rows(q, s, 8)
+    assert back.tolist() == [127, -64, 0, 2, 2, -2, 0, 64,
+                             254, 4, 4, 0, 0, -8, 12, 0]
+
+
+def test_scale_is_absmax_over_127_exactly_rounded():
+    """s = a/127 correctly rounded (checked in rational arithmetic), where a is
+    the row's largest magnitude; a*(1/127) or a/128 would fail some rows."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(64 * 300) * np.exp(rng.uniform(-20, 20, 64 * 300))).astype(np.float32)
+    q, s = oracle.quantize_rows(x, 64)
+    rows = x.reshape(300, 64)
+    wrong_recip = 0
+    for r in range(300):
+        a = np.abs(rows[r]).max()
+        assert s[r] == fp32_nearest(Fraction(float(a)) / 127), r
+        wrong_recip += int(np.float32(a) * np.float32(1 / 127) != s[r])
+        # the largest magnitude always lands on the end code
+        assert abs(int(q[r * 64 + int(np.argmax(np.abs(rows[r])))])) == 127
+    assert wrong_recip > 0  # the multiply-by-reciprocal reading is distinguishable
+
+
+def test_codes_are_nearest_integers_of_the_exact_quotient():
+    """Away from half-integers the code is the integer nearest x/s in exact
+    arithmetic, and |x - q*s| <= s/2 up to the roundings; a truncating or
+    floor rounding, or a code off by one, breaks this."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal(4096) * 3e-3).astype(np.float32)
+    q, s = oracle.quantize_rows(x, 512)
+    back = oracle.dequantize_rows(q, s, 512)
+    for i in range(0, 4096, 7):
+        sc = Fraction(float(s[i // 512]))
+        exact = Fraction(float(x[i])) / sc
+        frac_part = exact - (exact.numerator // exact.denominator)
+        if abs(frac_part - Fraction(1, 2)) < Fraction(1, 2 ** 16):
+            continue  # a near-tie decided by the rounded quotient
+        nearest = round(exact)
+        assert int(q[i]) == max(-127, min(127, nearest)), i
+    err = np.abs(back.astype(np.float64) - x.astype(np.float64))
+    half = np.repeat(s.astype(np.float64), 512) / 2
+    assert (err <= half * (1 + 2 ** -16) + np.repeat(s.astype(np.float64), 512) * 2 ** -17).all()
+
+
+def test_rows_map_to_their_own_scales_with_ragged_tail():
+    """Row r holds (r+1)*127 somewhere and smaller values elsewhere, so its
+    scale is r+1 exactly; a row index taken modulo, an off-by-one row start or
+    a dropped short last row changes some scale."""
+    L, rows = 10, 7
+    n = L * (rows - 1) + 3                       # last row has 3 elements
+    rng = np.random.default_rng(13)
+    x = np.empty(n, np.float32)
+    for r in range(rows):
+        lo, hi = r * L, min(n, r * L + L)
+        x[lo:hi] = rng.uniform(-(r + 1) * 100, (r + 1) * 100, hi - lo).astype(np.float32)
+        x[lo + (r * 3) % (hi - lo)] = -(r + 1) * 127.0 if r % 2 else (r + 1) * 127.0
+    q, s = oracle.quantize_rows(x, L)
+    assert s.tolist() == [float(r + 1) for r in range(rows)]
+    back = oracle.dequantize_rows(q, s, L)
+    assert np.abs(back - x).max() <= rows / 2
+
+
+def test_row_len_one_and_longer_than_tensor():
+    """row_len 1 gives each element its own scale (codes 0 or +-127 only);
+    row_len beyond n gives a single short row."""
+    x = np.array([3.0, -0.0, 1e-30, -7.5, 0.0], np.float32)
+    q, s = oracle.quantize_rows(x, 1)
+    assert q.tolist() == [127, 0, 127, -127, 0]
+    assert s[0] == fp32_nearest(Fraction(3, 127)) and s[1] == 0 and s[4] == 0
+    q, s = oracle.quantize_rows(x, 100)
+    assert s.shape == (1,) and s[0] == fp32_nearest(Fraction(15, 2) / 127)
+    assert q[3] == -127
+
+
+def test_grid_values_round_trip_exactly():
+    """Values k * 2^e with |k| <= 127 in a row that contains +-127 * 2^e come
+    back bit-exactly: the scale is exactly 2^e and every code is k."""
+    rng = np.random.default_rng(14)
+    for e in (-30, -10, 0, 5):
+        k = rng.integers(-127, 128, 256)
+        k[rng.integers(0, 256)] = 127 * (1 if e % 2 else -1)
+        x = (k.astype(np.float64) * 2.0 ** e).astype(np.float32)
+        q, s = oracle.quantize_rows(x, 256)
+        assert s[0] == np.float32(2.0 ** e)
+        assert q.astype(np.int64).tolist() == k.tolist()
+        assert oracle.dequantize_rows(q, s, 256).tolist() == x.tolist()
+
+
+def test_special_rows():
+    """Zero row: scale 0, codes 0.  A row with NaN: scale NaN, dequantized all
+    NaN.  A row with an infinity: scale inf, codes 0, dequantized all NaN.
+    A row whose absmax/127 underflows: scale 0.  Neighbouring rows are
+    untouched by any of them."""
+    tiny = np.float32(1.4e-45)                   # smallest subnormal
+    x = np.array([0.0, -0.0, 0.0, 0.0,
+                  1.0, np.nan, -2.0, 0.5,
+                  np.inf, 1.0, -1.0, 0.0,
+                  tiny, -tiny, 0.0, tiny,
+                  127.0, 1.0, 2.0, 3.0], np.float32)
+    q, s = oracle.quantize_rows(x, 4)
+    assert s[0] == 0 and np.isnan(s[1]) and np.isinf(s[2]) and s[3] == 0 and s[4] == 1
+    assert q[:16].tolist() == [0] * 16 and q[16:].tolist() == [127, 1, 2, 3]
+    back = oracle.dequantize_rows(q, s, 4)
+    assert back[:4].tolist() == [0.0] * 4
+    assert np.isnan(back[4:12]).all()
+    assert back[12:16].tolist() == [0.0] * 4 and back[16:].tolist() == [127, 1, 2, 3]
+
+
+def test_subnormal_scale_keeps_codes_in_range():
+    """With a subnormal scale the quotient can pass 127.5; the clamp keeps the
+    code at 127 (both implementations agree bit for bit)."""
+    base = np.float32(2.0 ** -140)
+    x = np.array([base, base * np.float32(0.9), -base, base * np.float32(0.3)], np.float32)
+    q, s = oracle.quantize_rows(x, 4)
+    assert 0 < s[0] < np.float32(1.2e-38)
+    assert np.float32(x[0] / s[0]) > 127.5          # the clamp is really needed here
+    assert q[0] == 127 and q[2] == -127
+    bq, bs = bruteforce.quantize(x, 4)
+    assert bq.tolist() == q.tolist() and bs.view(np.uint32).tolist() == s.view(np.uint32).tolist()
+
+
+@pytest.mark.parametrize("row_len", [1, 3, 7, 64, 100, 1000])
+def test_bruteforce_agrees_bit_for_bit(row_len):
+    """Two implementations written apart (C loops; Python round() on exact
+    float quotients) agree on every code and scale, specials included."""
+    rng = np.random.default_rng(15 + row_len)
+    x = (rng.standard_normal(1000) * np.exp(rng.uniform(-30, 30, 1000))).astype(np.float32)
+    x[rng.integers(0, 1000, 5)] = 0.0
+    x[17], x[500] = np.float32(-0.0), np.float32(1e-44)
+    q, s = oracle.quantize_rows(x, row_len)
+    bq, bs = bruteforce.quantize(x, row_len)
+    assert q.tolist() == bq.tolist()
+    assert s.view(np.uint32).tolist() == bs.view(np.uint32).tolist()
+    assert oracle.dequantize_rows(q, s, row_len).view(np.uint32).tolist() == \
+        bruteforce.dequantize(q, s, row_len).view(np.uint32).tolist()
+
+
+# ------------------------------------------------------------ quantized step
+
+def grid_moments(rng, n, row_len, e_m, e_v):
+    """int8 m, v whose dequantized values are exact multiples of 2^e."""
+    rows = oracle.n_rows(n, row_len)
+    mq = rng.integers(-127, 128, n).astype(np.int8)
+    vq = rng.integers(0, 128, n).astype(np.int8)
+    ms = np.full(rows, 2.0 ** e_m, np.float32)
+    vs = np.full(rows, 2.0 ** e_v, np.float32)
+    return mq, ms, vq, vs
+
+
+@pytest.mark.parametrize("grad_kind", ["bf16", "fp32", "q8"])
+def test_q8_step_is_the_fp32_step_on_dequantized_state(grad_kind):
+    """On exactly representable moments the quantized step's master, bf16
+    weight and delta equal the fp32 step's on the dequantized values, and the
+    new codes are the quantization of the fp32 step's new moments.  A dropped
+    scale, a moment read from the wrong row or an unrequantized output fails."""
+    rng = np.random.default_rng(21)
+    n, L = 1000, 96
+    mq, ms, vq, vs = grid_moments(rng, n, L, -17, -30)
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    orig = oracle.rne16(master)
+    if grad_kind == "bf16":
+        grad = oracle.rne16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+        g32 = grad
+    elif grad_kind == "fp32":
+        grad = (rng.standard_normal(n) * 1e-3).astype(np.float32)
+        g32 = grad
+    else:
+        gq = rng.integers(-127, 128, n).astype(np.int8)
+        gs = np.full(oracle.n_rows(n, L), 2.0 ** -16, np.float32)
+        grad = (gq, gs)
+        g32 = (gq.astype(np.float64) * 2.0 ** -16).astype(np.float32)
+    c = consts(100)
+
+    m32 = (mq.astype(np.float64) * 2.0 ** -17).astype(np.float32)
+    v32 = (vq.astype(np.float64) * 2.0 ** -30).astype(np.float32)
+    master_ref = master.copy()
+    w_ref, d_ref = oracle.adamw_step(master_ref, m32, v32, g32, c, orig=orig)
+
+    m_t, v_t = (mq.copy(), ms.copy()), (vq.copy(), vs.copy())
+    master_q = master.copy()
+    w, d = oracle.adamw_step_q8(master_q, m_t, v_t, grad, c, L, orig=orig)
+    assert master_q.view(np.uint32).tolist() == master_ref.view(np.uint32).tolist()
+    assert w.tolist() == w_ref.tolist()
+    assert d.view(np.uint32).tolist() == d_ref.view(np.uint32).tolist()
+    for (q, s), ref in ((m_t, m32), (v_t, v32)):
+        rq, rs = oracle.quantize_rows(ref, L)
+        assert q.tolist() == rq.tolist() and s.tolist() == rs.tolist()
+        # the requantized moment is within half a step of the fp32 moment
+        back = oracle.dequantize_rows(q, s, L).astype(np.float64)
+        half = np.repeat(s.astype(np.float64), L)[:n] / 2
+        assert (np.abs(back - ref) <= half * (1 + 2 ** -15)).all()
+
+
+@pytest.mark.parametrize("L", [1, 5, 64, 333])
+def test_q8_step_bruteforce_agrees(L):
+    """The composed C step and the per-element Python loop agree bit for bit
+    on random (not grid) int8 state, three steps in a row."""
+    rng = np.random.default_rng(30 + L)
+    n = 700
+    m0 = (rng.standard_normal(n) * 1e-4).astype(np.float32)
+    v0 = ((rng.standard_normal(n) * 1e-3) ** 2).astype(np.float32)
+    mq, ms = oracle.quantize_rows(m0, L)
+    vq, vs = oracle.quantize_rows(v0, L)
+    master = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    bm, bmq, bms, bvq, bvs = master.copy(), mq.copy(), ms.copy(), vq.copy(), vs.copy()
+    for t in (5, 6, 7):
+        grad = oracle.rne16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+        c = consts(t)
+        m_t, v_t = (mq, ms), (vq, vs)
+        w, _ = oracle.adamw_step_q8(master, m_t, v_t, grad, c, L)
+        bc = bruteforce.constants(H["lr"], H["beta1"], H["beta2"], H["eps"],
+                                  H["weight_decay"], t)
+        bm, (bmq, bms), (bvq, bvs), bw, _ = bruteforce.adamw_step_q8(
+            bm, bmq, bms, bvq, bvs, grad, bc, L)
+        assert master.view(np.uint32).tolist() == bm.view(np.uint32).tolist()
+        assert w.tolist() == bw.tolist()
+        assert mq.tolist() == bmq.tolist() and vq.tolist() == bvq.tolist()
+        assert ms.view(np.uint32).tolist() == bms.view(np.uint32).tolist()
+        assert vs.view(np.uint32).tolist() == bvs.view(np.uint32).tolist()
+
+
+def test_q8_step_fresh_state_first_step_closed_form():
+    """From m = v = 0 (codes 0, scales 0) at t = 1 the fp32 step gives
+    m' = (1-b1) g and v' = (1-b2) g^2, so each requantized row's scale is
+    (1-b1)*max|g| / 127 and (1-b2)*max g^2 / 127 in binary32; a step that
+    skipped the requantization or quantized the old moments fails."""
+    rng = np.random.default_rng(40)
+    n, L = 512, 128
+    grad = oracle.rne16((rng.standard_normal(n) * 1e-3).astype(np.float32))
+    g = oracle.bf16_to_f32(grad)
+    c = consts(1)
+    m_t = (np.zeros(n, np.int8), np.zeros(4, np.float32))
+    v_t = (np.zeros(n, np.int8), np.zeros(4, np.float32))
+    master = np.zeros(n, np.float32)
+    oracle.adamw_step_q8(master, m_t, v_t, grad, c, L)
+    for r in range(4):
+        gr = g[r * L:(r + 1) * L]
+        am = np.abs(np.float32(c[1]) * gr).max()
+        av = (np.float32(c[3]) * (gr * gr)).max()
+        assert m_t[1][r] == np.float32(am / np.float32(127))
+        assert v_t[1][r] == np.float32(av / np.float32(127))
+        assert (v_t[0][r * L:(r + 1) * L] >= 0).all()
+    # at t = 1 a fresh state moves by lr*g/(|g| + eps): lr*sign(g) where
+    # |g| >> eps
+    big = np.abs(g) > 1e-4
+    assert np.allclose(master[big], -H["lr"] * np.sign(g[big]), rtol=2e-4)
+
+
+# ------------------------------------------------------- quantized accumulation
+
+def test_q8_accumulation_exact_on_grid():
+    """bf16 gradients that are small integers times 2^-10: every partial sum
+    is exact in fp32, and with a row absmax of 127 * 2^-10 the quantized
+    accumulator holds the exact sum; the first micro-batch overwrites."""
+    L, n = 16, 64
+    rng = np.random.default_rng(50)
+    ks = [rng.integers(-40, 41, n) for _ in range(3)]
+    for k in ks:
+        k[::L] = 0
+    ks[0][::L] = 127                        # each row's sum reaches 127 at column 0
+    grads = [oracle.rne16((k.astype(np.float64) * 2.0 ** -10).astype(np.float32)) for k in ks]
+    acc_q = np.full(n, 99, np.int8)          # garbage the overwrite must ignore
+    acc_s = np.full(n // L, 123.0, np.float32)
+    for i, g in enumerate(grads):
+        oracle.grad_accum_q8(acc_q, acc_s, g, i == 0, L)
+    total = ks[0] + ks[1] + ks[2]
+    if np.abs(total).max() <= 127:
+        assert acc_s.tolist() == [2.0 ** -10] * (n // L)
+        assert acc_q.astype(np.int64).tolist() == total.tolist()
+    bq, bs = bruteforce.accumulate_q8(grads, L)
+    assert bq.tolist() == acc_q.tolist()
+    assert bs.view(np.uint32).tolist() == acc_s.view(np.uint32).tolist()
+
+
+@pytest.mark.parametrize("L", [3, 100])
+def test_q8_accumulation_bruteforce_random(L):
+    """Four random micro-batches: the C composition and the Python loop agree,
+    and the accumulator tracks the fp32 sum within the quantization steps
+    taken (half a scale per requantization)."""
+    rng = np.random.default_rng(60 + L)
+    n = 500
+    grads = [oracle.rne16((rng.standard_normal(n) * 1e-3).astype(np.float32)) for _ in range(4)]
+    acc_q = np.zeros(n, np.int8)
+    acc_s = np.zeros(oracle.n_rows(n, L), np.float32)
+    bound = np.zeros(n)
+    for i, g in enumerate(grads):
+        oracle.grad_accum_q8(acc_q, acc_s, g, i == 0, L)
+        bound += np.repeat(acc_s.astype(np.float64), L)[:n] / 2 * (1 + 2 ** -15)
+    bq, bs = bruteforce.accumulate_q8(grads, L)
+    assert bq.tolist() == acc_q.tolist()
+    assert bs.view(np.uint32).tolist() == acc_s.view(np.uint32).tolist()
+    exact = sum(oracle.bf16_to_f32(g).astype(np.float64) for g in grads)
+    got = oracle.dequantize_rows(acc_q, acc_s, L).astype(np.float64)
+    assert (np.abs(got - exact) <= bound + 1e-12).all()
