@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--copy-gib", type=float, default=4.0, help="size of the copy-ceiling test")
     ap.add_argument("--merge", action="store_true",
                     help="time lema_merge_delta (base + delta -> servable bf16) on the workload")
+    ap.add_argument("--q8", action="store_true",
+                    help="int8 moments with per-row scales (and int8 accumulators for "
+                         "multi-micro-batch workloads), README 'Quantization'")
     ap.add_argument("--slot-stream", action="store_true",
                     help="stream the whole 7B shape from pinned host memory through 2 HBM slots")
     ap.add_argument("--layers", type=int, default=0,
@@ -150,6 +153,8 @@ def main():
         line = slot_stream_bench(torch, L, synth, a)
     elif a.merge:
         line = merge_bench(torch, L, synth, a)
+    elif a.q8:
+        line = q8_bench(torch, L, synth, a)
     else:
         line = resident_bench(torch, L, synth, a)
     print(json.dumps(line), flush=True)
@@ -329,6 +334,185 @@ def cpu_baseline(segs, w, hp, delta, seconds):
             "kind": "oracle",
             "sample": f"{w.segments[0][0]} ({n} params), {reps} oracle steps in {el:.1f} s, "
                       f"delta {'on' if delta else 'off'}; C oracle, OpenMP"}
+
+
+# ------------------------------------------------------------- int8
+
+def q8_step_bytes(numel, rows, grad, delta):
+    """Algorithmic bytes of one int8-moment step over one tensor: master
+    read+write, m and v codes read+write, their row scales read+write, the
+    gradient (bf16, or int8 codes plus row scales), bf16 weight, orig+delta."""
+    per = 8 + 2 + 2 + 2 + (6 if delta else 0) + (2 if grad == "bf16" else 1)
+    return numel * per + rows * (16 + (4 if grad == "q8" else 0))
+
+
+def q8_accum_bytes(numel, rows, overwrite):
+    """int8 accumulation of one bf16 micro-batch: read g, (read codes and
+    scales,) write codes and scales."""
+    return numel * (3 if overwrite else 4) + rows * (4 if overwrite else 8)
+
+
+def q8_bench(torch, L, synth, a):
+    """The step with int8 moments (README "Quantization", opt_state_bits = 8);
+    multi-micro-batch workloads also accumulate into int8 (grad_acc_bits = 8)."""
+    dev = "cuda"
+    w = synth.WORKLOADS[a.workload]
+    delta = not a.no_delta
+    hp = synth.HPARAMS
+    P = w.params
+    K = w.microbatches
+    grad = "q8" if K > 1 else "bf16"
+    row_lens = [shape[-1] for _, shape in w.segments]
+    rows = [-(-n // rl) for n, rl in zip(w.numels, row_lens)]
+    step_bytes = sum(q8_step_bytes(n, r, grad, delta) for n, r in zip(w.numels, rows))
+    accum_bytes = 0
+    if K > 1:
+        accum_bytes = sum(q8_accum_bytes(n, r, True) + (K - 1) * q8_accum_bytes(n, r, False)
+                          for n, r in zip(w.numels, rows))
+    per_step = step_bytes + accum_bytes
+
+    nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
+    sets = []
+    for _ in range(nsets):
+        segs, accs = [], []
+        for i in range(len(w.segments)):
+            st = synth.make_segment_state(w, i, dev, with_orig=delta)
+            n, rl = w.numels[i], row_lens[i]
+            m, v = L.Q8.empty(n, rl), L.Q8.empty(n, rl)
+            L.quantize_rows([(st["m"], m), (st["v"], v)])
+            if K > 1:
+                g = L.Q8.empty(n, rl)
+                accs.append((g, st["grads"]))
+            else:
+                g = st["grads"][0]
+            segs.append(L.AdamwQ8Segment(st["master"], m, v, g,
+                                         torch.empty(n, dtype=torch.bfloat16, device=dev),
+                                         st.get("orig"),
+                                         torch.empty(n, device=dev) if delta else None))
+            del st["m"], st["v"]
+        sets.append((segs, accs))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    copy_gbps = copy_ceiling(torch, L, a.copy_gib)
+
+    accum_plans = [[L.AccumQ8Plan([L.AccumQ8Segment(acc, g[j]) for acc, g in accs])
+                    for j in range(K)] for _, accs in sets] if K > 1 else []
+    plans = [L.AdamwQ8Plan(segs) for segs, _ in sets]
+
+    def accumulate(k):
+        for j, plan in enumerate(accum_plans[k % nsets]):
+            plan.run(overwrite=(j == 0))
+
+    def step(k):
+        plans[k % nsets].step(step=w.step, **hp)
+
+    def whole(k):
+        if K > 1:
+            accumulate(k)
+        step(k)
+
+    for k in range(a.warmup):
+        whole(k)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    step_ms = timed_events(torch, stream, whole, a.steps)
+    wall = time.perf_counter() - t_wall0
+    ms = sum(step_ms) / len(step_ms)
+    if K > 1:
+        adamw_ms_list = timed_events(torch, stream, step, a.steps)
+        accum_ms_list = timed_events(torch, stream, accumulate, a.steps)
+    else:
+        adamw_ms_list, accum_ms_list = step_ms, []
+    adamw_ms = sum(adamw_ms_list) / len(adamw_ms_list)
+    adamw_gbps = step_bytes / (adamw_ms * 1e-3) / 1e9
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(a.steps):
+        whole(k)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    pipelined_ms = start.elapsed_time(stop) / a.steps
+    gbps = per_step / (ms * 1e-3) / 1e9
+    key = f"{a.workload}:q8:{'delta' if delta else 'nodelta'}"
+    line = {
+        "metric": METRIC,
+        "value": P / (ms * 1e-3),
+        "unit": "params/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 arithmetic; int8 moments" + (" and accumulators" if K > 1 else ""),
+        "data": "synthetic",
+        "config": {
+            "workload": a.workload, "description": w.description, "params": P,
+            "segments": len(w.segments),
+            "moments": "int8 codes + fp32 scale per row (row = last dimension)",
+            "grad": ("int8 accumulator of 8 bf16 micro-batches" if K > 1 else "bf16"),
+            "delta": delta, "step_t": w.step,
+            "bytes_per_param": per_step / P, "bytes_per_step": per_step,
+            "rotated_state_sets": nsets,
+        },
+        "hbm_gbps": gbps,
+        "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
+        "copy_ceiling_gbps": copy_gbps,
+        "pct_copy_ceiling": 100.0 * gbps / copy_gbps,
+        "roofline": {"bound": "hbm", "achieved": adamw_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": adamw_gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic_for(key), "kernel": "adamw_q8_kernel",
+                     "algorithmic_bytes_per_launch": step_bytes,
+                     "avg_launch_ms": adamw_ms, "min_launch_ms": min(adamw_ms_list),
+                     "max_launch_ms": max(adamw_ms_list)},
+        "pipelined": {"ms_per_step": pipelined_ms,
+                      "hbm_gbps": per_step / (pipelined_ms * 1e-3) / 1e9,
+                      "params_per_s": P / (pipelined_ms * 1e-3)},
+        "host_wall_s_timed_region": wall,
+    }
+    if accum_ms_list:
+        acc_ms = sum(accum_ms_list) / len(accum_ms_list)
+        acc_gbps = accum_bytes / (acc_ms * 1e-3) / 1e9
+        line["accumulation"] = {"kernel": "code_rows_kernel", "launches_per_step": K,
+                                "ms_per_step": acc_ms, "hbm_gbps": acc_gbps,
+                                "frac": acc_gbps / HBM_PEAK_GBPS,
+                                "algorithmic_bytes_per_step": accum_bytes}
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = q8_cpu_baseline(sets[0][0][0], w, row_lens[0], hp, delta,
+                                               a.cpu_seconds)
+    return line
+
+
+def q8_cpu_baseline(seg, w, row_len, hp, delta, seconds):
+    """The oracle's int8 step (dequantize, fp32 step, quantize) on the first
+    tensor of the workload."""
+    import oracle
+    import torch
+
+    def host(t):
+        t = t.detach().cpu()
+        if t.dtype == torch.bfloat16:
+            return t.view(torch.int16).numpy().view("uint16").copy()
+        return t.numpy().copy()
+
+    master = host(seg.master)
+    m = (host(seg.exp_avg.codes), host(seg.exp_avg.scale))
+    v = (host(seg.exp_avg_sq.codes), host(seg.exp_avg_sq.scale))
+    grad = host(seg.grad)
+    orig = host(seg.orig) if delta else None
+    n = master.shape[0]
+    c = oracle.adamw_constants(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                               hp["weight_decay"], w.step)
+    oracle.adamw_step_q8(master, m, v, grad, c, row_len, orig=orig)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.adamw_step_q8(master, m, v, grad, c, row_len, orig=orig)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": n * reps / el, "unit": "params/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{w.segments[0][0]} ({n} params, rows of {row_len}), {reps} oracle "
+                      f"int8 steps in {el:.1f} s, delta {'on' if delta else 'off'}; C oracle, "
+                      "OpenMP, numpy glue"}
 
 
 # ------------------------------------------------------------ merge

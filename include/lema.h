@@ -82,7 +82,9 @@ int32_t lema_version(void);
 
 typedef enum {
     LEMA_GRAD_BF16 = 0,  /* grad is bf16 bit patterns (one micro-batch)   */
-    LEMA_GRAD_FP32 = 1   /* grad is an fp32 accumulator (lema_grad_accum) */
+    LEMA_GRAD_FP32 = 1,  /* grad is an fp32 accumulator (lema_grad_accum) */
+    LEMA_GRAD_Q8   = 2   /* grad is an int8 accumulator with row scales
+                            (lema_grad_accum_q8); lema_adamw_step_q8 only  */
 } lema_grad_dtype;
 
 /*
@@ -198,6 +200,121 @@ typedef struct {
  * LEMA_ERR_HIP.
  */
 lema_status lema_merge_delta(const lema_merge_seg *segs, int32_t nseg, void *stream);
+
+/* ------------------------------------------- int8 rows with row scales */
+
+/*
+ * Quantized optimizer moments and gradient accumulators (LEMA README,
+ * "Quantization": opt_state_bits = 8 stores Adam's moments and
+ * grad_acc_bits = 8 the gradient accumulators as int8 with one scale per
+ * row; both stay quantized and are dequantized only inside the per-layer
+ * AdamW step).  The pages give no formula; the format read here is
+ * symmetric absmax scaling:
+ *   - a tensor of numel elements is cut into rows of row_len consecutive
+ *     elements, the last row possibly shorter: rows = ceil(numel / row_len)
+ *     (row_len = in for a 2-D [out x in] weight gives its matrix rows);
+ *   - row r stores int8 codes q in [-127, 127] and one fp32 scale s[r];
+ *   - dequantize: x = f32(q) * s[r], one binary32 multiplication;
+ *   - quantize  : a = largest |x| of the row (NaN if the row has a NaN),
+ *                 s[r] = a / 127 (binary32 division); if s[r] is finite and
+ *                 > 0, q = round-half-even(x / s[r]) (binary32 division)
+ *                 clamped to [-127, 127], else every code of the row is 0.
+ *                 An all-zero row stores s = 0; a row holding an infinity or
+ *                 a NaN stores s = inf or NaN and dequantizes to NaN.
+ * Scales are fp32 arrays of `rows` entries; codes are int8 arrays of numel.
+ * row_len must lie in 1 .. LEMA_Q8_MAX_ROW (else LEMA_ERR_SIZE).  int8 arrays
+ * need no alignment; 4-byte aligned codes, 16-byte aligned fp32 and 8-byte
+ * aligned bf16 arrays with row_len a multiple of 4 take the vector path.
+ */
+#define LEMA_Q8_MAX_ROW 16384
+
+typedef enum {
+    LEMA_STATE_FP32 = 0,  /* exp_avg / exp_avg_sq are fp32 arrays         */
+    LEMA_STATE_Q8   = 1   /* exp_avg / exp_avg_sq are int8 codes + scales */
+} lema_state_dtype;
+
+/*
+ * One trainable tensor of lema_adamw_step_q8.  As lema_adamw_seg, plus the
+ * row scales of every int8 array and the row length.  master, the moments
+ * and their scales are updated in place; no two arrays may overlap where
+ * one is written (LEMA_ERR_OVERLAP).
+ */
+typedef struct {
+    float          *master;            /* fp32 master weight, in/out (required)     */
+    void           *exp_avg;           /* m: int8 codes or fp32, in/out (required)   */
+    float          *exp_avg_scale;     /* m's fp32 row scales, in/out (int8 m only)   */
+    void           *exp_avg_sq;        /* v: int8 codes or fp32, in/out (required)   */
+    float          *exp_avg_sq_scale;  /* v's row scales, in/out (int8 v only)       */
+    const void     *grad;              /* bf16 bits, fp32 or int8 codes (required)   */
+    const float    *grad_scale;        /* grad's row scales (LEMA_GRAD_Q8 only)      */
+    uint16_t       *weight_bf16;       /* out: bf16 of the new master (required)     */
+    const uint16_t *orig_bf16;         /* in: base weight; non-NULL iff delta is     */
+    float          *delta;             /* out: new master - f32(orig) (optional)     */
+    int64_t         numel;             /* >= 0; 0 makes the segment a no-op          */
+    int64_t         row_len;           /* 1 .. LEMA_Q8_MAX_ROW when any array is int8 */
+} lema_adamw_q8_seg;
+
+/*
+ * One AdamW step with quantized moments and/or a quantized gradient
+ * accumulator (LEMA README, "Quantization": the int8 classes are
+ * dequantized only inside the per-layer AdamW step).  Per row:
+ *   m, v  = dequantized moments (moment_dtype LEMA_STATE_Q8) or the fp32 ones
+ *   g     = bf16 widened, the fp32 accumulator, or the dequantized int8 one
+ *   the fp32 step of lema_adamw_step, element for element (same arithmetic,
+ *   same master, bf16 weight and delta outputs), then for int8 moments the
+ *   new m and v are quantized with fresh row scales.
+ *   segs        : host array of nseg descriptors (device pointers), read
+ *                 during the call only
+ *   args        : args->grad_dtype is LEMA_GRAD_BF16, LEMA_GRAD_FP32 or
+ *                 LEMA_GRAD_Q8
+ *   moment_dtype: lema_state_dtype, for every segment of the call
+ * With fp32 moments and a bf16 or fp32 gradient this is lema_adamw_step.
+ * Asynchronous on `stream`.  Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE,
+ * LEMA_ERR_HPARAM, LEMA_ERR_DTYPE, LEMA_ERR_ALIGN, LEMA_ERR_OVERLAP,
+ * LEMA_ERR_HIP.
+ */
+lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
+                               const lema_adamw_args *args, int32_t moment_dtype, void *stream);
+
+/* One int8 gradient accumulator and the bf16 micro-batch added into it. */
+typedef struct {
+    int8_t         *acc;        /* int8 codes, in/out (required)            */
+    float          *acc_scale;  /* row scales, in/out (required)            */
+    const uint16_t *grad_bf16;  /* bf16 bits, in (required)                 */
+    int64_t         numel;      /* >= 0                                     */
+    int64_t         row_len;    /* 1 .. LEMA_Q8_MAX_ROW                     */
+} lema_accum_q8_seg;
+
+/*
+ * int8 gradient accumulation of one bf16 micro-batch (LEMA README,
+ * "Quantization": grad_acc_bits = 8):
+ *   overwrite = 1 : acc = Q(f32(g))                (first micro-batch)
+ *   overwrite = 0 : acc = Q(D(acc) + f32(g))       (later ones, in order)
+ * with D and Q the dequantization and quantization above and one binary32
+ * addition per element.  Asynchronous on `stream`.  Errors: LEMA_ERR_NULL,
+ * LEMA_ERR_SIZE, LEMA_ERR_ALIGN, LEMA_ERR_OVERLAP, LEMA_ERR_HIP.
+ */
+lema_status lema_grad_accum_q8(const lema_accum_q8_seg *segs, int32_t nseg,
+                               int32_t overwrite, void *stream);
+
+/* One tensor converted between fp32 and int8 codes with row scales. */
+typedef struct {
+    float   *x;        /* fp32 values (required)             */
+    int8_t  *codes;    /* int8 codes (required)              */
+    float   *scale;    /* ceil(numel/row_len) scales (required) */
+    int64_t  numel;    /* >= 0                               */
+    int64_t  row_len;  /* 1 .. LEMA_Q8_MAX_ROW               */
+} lema_q8_tensor;
+
+/*
+ * Convert whole tensors: lema_quantize_rows reads x and writes codes and
+ * scales; lema_dequantize_rows reads codes and scales and writes x.  They
+ * set up and inspect quantized state (fp32 moments of a checkpoint into the
+ * int8 classes and back).  Asynchronous on `stream`.  Errors: LEMA_ERR_NULL,
+ * LEMA_ERR_SIZE, LEMA_ERR_ALIGN, LEMA_ERR_OVERLAP, LEMA_ERR_HIP.
+ */
+lema_status lema_quantize_rows(const lema_q8_tensor *t, int32_t n, void *stream);
+lema_status lema_dequantize_rows(const lema_q8_tensor *t, int32_t n, void *stream);
 
 /* --------------------------------------- slot-pool streaming (host RAM) */
 

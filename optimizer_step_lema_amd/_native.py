@@ -24,6 +24,11 @@ LEMA_ERR_ALIGN = -8
 
 LEMA_GRAD_BF16 = 0
 LEMA_GRAD_FP32 = 1
+LEMA_GRAD_Q8 = 2
+
+LEMA_STATE_FP32 = 0
+LEMA_STATE_Q8 = 1
+LEMA_Q8_MAX_ROW = 16384
 
 vp = ctypes.c_void_p
 i32 = ctypes.c_int32
@@ -55,6 +60,21 @@ class MergeSeg(ctypes.Structure):
     _fields_ = [("base_bf16", vp), ("delta", vp), ("merged_bf16", vp), ("numel", i64)]
 
 
+class AdamwQ8Seg(ctypes.Structure):
+    _fields_ = [("master", vp), ("exp_avg", vp), ("exp_avg_scale", vp), ("exp_avg_sq", vp),
+                ("exp_avg_sq_scale", vp), ("grad", vp), ("grad_scale", vp), ("weight_bf16", vp),
+                ("orig_bf16", vp), ("delta", vp), ("numel", i64), ("row_len", i64)]
+
+
+class AccumQ8Seg(ctypes.Structure):
+    _fields_ = [("acc", vp), ("acc_scale", vp), ("grad_bf16", vp), ("numel", i64),
+                ("row_len", i64)]
+
+
+class Q8Tensor(ctypes.Structure):
+    _fields_ = [("x", vp), ("codes", vp), ("scale", vp), ("numel", i64), ("row_len", i64)]
+
+
 class Layer(ctypes.Structure):
     _fields_ = [("host_segs", ctypes.POINTER(AdamwSeg)), ("nseg", i32)]
 
@@ -77,6 +97,11 @@ SIGNATURES = [
                                     ctypes.POINTER(AdamwArgs), vp]),
     ("lema_grad_accum", i32, [ctypes.POINTER(AccumSeg), i32, i32, vp]),
     ("lema_merge_delta", i32, [ctypes.POINTER(MergeSeg), i32, vp]),
+    ("lema_adamw_step_q8", i32, [ctypes.POINTER(AdamwQ8Seg), i32, ctypes.POINTER(AdamwArgs), i32,
+                                 vp]),
+    ("lema_grad_accum_q8", i32, [ctypes.POINTER(AccumQ8Seg), i32, i32, vp]),
+    ("lema_quantize_rows", i32, [ctypes.POINTER(Q8Tensor), i32, vp]),
+    ("lema_dequantize_rows", i32, [ctypes.POINTER(Q8Tensor), i32, vp]),
     ("lema_slot_pool_create", i32, [vp, ctypes.c_size_t, i32, vp, vp, ctypes.POINTER(vp)]),
     ("lema_slot_pool_destroy", i32, [vp]),
     ("lema_slot_pool_set_writeback_stream", i32, [vp, vp]),

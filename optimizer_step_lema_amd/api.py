@@ -9,7 +9,9 @@ Method (LEMA README "Quick Start" and "Selective Full Fine-Tuning"; LLMScale
 fine-tuning VRAM page): one per-layer AdamW step over fp32 master/m/v with a
 bf16 gradient (or an fp32 accumulator), bf16 weight write-back and an
 optional fp32 delta; fp32 accumulation of bf16 micro-batch gradients;
-streaming of host-resident state through a pool of HBM slots.
+streaming of host-resident state through a pool of HBM slots.  README
+"Quantization": the same step with int8 moments and int8 accumulators kept
+as codes with per-row scales.
 """
 from __future__ import annotations
 
@@ -215,6 +217,185 @@ class AccumPlan:
     def run(self, *, overwrite: bool, stream=None) -> None:
         N.check(self.lib.lema_grad_accum(self.c_segs, self.n, 1 if overwrite else 0,
                                          _stream_handle(stream)), "lema_grad_accum")
+
+
+# ------------------------------------------------- int8 rows with scales
+
+@dataclass
+class Q8:
+    """An int8 tensor with one fp32 scale per row of ``row_len`` elements
+    (README "Quantization": the int8 + per-row-scale storage of quantized
+    moments and accumulators; the format is stated in include/lema.h)."""
+    codes: torch.Tensor      # int8, numel elements
+    scale: torch.Tensor      # fp32, ceil(numel / row_len) row scales
+    row_len: int
+
+    @property
+    def numel(self) -> int:
+        return self.codes.numel()
+
+    @staticmethod
+    def rows_of(numel: int, row_len: int) -> int:
+        return -(-numel // row_len)
+
+    @classmethod
+    def empty(cls, numel: int, row_len: int, device="cuda") -> "Q8":
+        return cls(torch.empty(numel, dtype=torch.int8, device=device),
+                   torch.empty(cls.rows_of(numel, row_len), dtype=torch.float32, device=device),
+                   int(row_len))
+
+    @classmethod
+    def zeros(cls, numel: int, row_len: int, device="cuda") -> "Q8":
+        """A zero state: codes 0 and scales 0 dequantize to exact zeros."""
+        return cls(torch.zeros(numel, dtype=torch.int8, device=device),
+                   torch.zeros(cls.rows_of(numel, row_len), dtype=torch.float32, device=device),
+                   int(row_len))
+
+    def pointers(self, n: int, name: str):
+        if self.codes.numel() != n:
+            raise ValueError(f"{name}: expected {n} codes, got {self.codes.numel()}")
+        codes = _check(self.codes, torch.int8, n, f"{name}.codes")
+        scale = _check(self.scale, torch.float32, self.rows_of(n, self.row_len), f"{name}.scale")
+        return codes, scale
+
+
+def _q8_tensors(pairs) -> ctypes.Array:
+    cs = []
+    for i, (x, q) in enumerate(pairs):
+        n = x.numel()
+        codes, scale = q.pointers(n, f"q[{i}]")
+        cs.append(N.Q8Tensor(_check(x, torch.float32, n, f"x[{i}]"), codes, scale, n, q.row_len))
+    return (N.Q8Tensor * max(1, len(cs)))(*cs), len(cs)
+
+
+def quantize_rows(pairs: Sequence[tuple], stream=None) -> None:
+    """For each (x fp32, q Q8): q = quantization of x, on the GPU."""
+    arr, n = _q8_tensors(pairs)
+    N.check(N.load().lema_quantize_rows(arr, n, _stream_handle(stream)), "lema_quantize_rows")
+
+
+def dequantize_rows(pairs: Sequence[tuple], stream=None) -> None:
+    """For each (x fp32, q Q8): x = dequantization of q, on the GPU."""
+    arr, n = _q8_tensors(pairs)
+    N.check(N.load().lema_dequantize_rows(arr, n, _stream_handle(stream)),
+            "lema_dequantize_rows")
+
+
+@dataclass
+class AdamwQ8Segment:
+    """One trainable tensor of the quantized step: int8 moments (Q8) or fp32
+    ones, and a bf16 / fp32 gradient tensor or an int8 accumulator (Q8).
+    Every Q8 member of a segment shares one row length."""
+    master: torch.Tensor
+    exp_avg: object              # Q8 or fp32 tensor
+    exp_avg_sq: object           # Q8 or fp32 tensor
+    grad: object                 # bf16 / fp32 tensor or Q8
+    weight: torch.Tensor
+    orig: Optional[torch.Tensor] = None
+    delta: Optional[torch.Tensor] = None
+
+    def row_len(self) -> int:
+        lens = {q.row_len for q in (self.exp_avg, self.exp_avg_sq, self.grad) if isinstance(q, Q8)}
+        if len(lens) > 1:
+            raise ValueError("the int8 members of one segment must share a row length")
+        return lens.pop() if lens else 1
+
+    def kinds(self):
+        mom_q8 = isinstance(self.exp_avg, Q8)
+        if mom_q8 != isinstance(self.exp_avg_sq, Q8):
+            raise TypeError("exp_avg and exp_avg_sq must both be Q8 or both fp32")
+        if isinstance(self.grad, Q8):
+            gd = N.LEMA_GRAD_Q8
+        elif self.grad.dtype == torch.float32:
+            gd = N.LEMA_GRAD_FP32
+        elif self.grad.dtype == torch.bfloat16:
+            gd = N.LEMA_GRAD_BF16
+        else:
+            raise TypeError(f"grad: expected bfloat16, float32 or Q8, got {self.grad.dtype}")
+        return mom_q8, gd
+
+    def to_c(self) -> N.AdamwQ8Seg:
+        n = self.master.numel()
+        mom_q8, gd = self.kinds()
+        if mom_q8:
+            m, ms = self.exp_avg.pointers(n, "exp_avg")
+            v, vs = self.exp_avg_sq.pointers(n, "exp_avg_sq")
+        else:
+            m, ms = _check(self.exp_avg, torch.float32, n, "exp_avg"), 0
+            v, vs = _check(self.exp_avg_sq, torch.float32, n, "exp_avg_sq"), 0
+        if gd == N.LEMA_GRAD_Q8:
+            g, gs = self.grad.pointers(n, "grad")
+        else:
+            g, gs = _check(self.grad, self.grad.dtype, n, "grad"), 0
+        return N.AdamwQ8Seg(
+            _check(self.master, torch.float32, n, "master"), m, ms, v, vs, g, gs,
+            _check(self.weight, torch.bfloat16, n, "weight"),
+            _check(self.orig, torch.bfloat16, n, "orig"),
+            _check(self.delta, torch.float32, n, "delta"), n, self.row_len())
+
+
+def _q8_call_kinds(segments: Sequence[AdamwQ8Segment]):
+    kinds = {s.kinds() for s in segments}
+    if len(kinds) > 1:
+        raise TypeError("all segments of one call must share moment and gradient dtypes")
+    return kinds.pop() if kinds else (True, N.LEMA_GRAD_BF16)
+
+
+class AdamwQ8Plan:
+    """A quantized-step segment list marshalled once for repeated steps."""
+
+    def __init__(self, segments: Sequence[AdamwQ8Segment]):
+        self.lib = N.load()
+        self.segments = list(segments)
+        self.n = len(self.segments)
+        self.mom_q8, self.grad_dtype = _q8_call_kinds(self.segments)
+        self.c_segs = (N.AdamwQ8Seg * max(1, self.n))(*[s.to_c() for s in self.segments])
+
+    def step(self, *, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step,
+             stream=None) -> None:
+        args = _args(lr, beta1, beta2, eps, weight_decay, step, self.grad_dtype)
+        moments = N.LEMA_STATE_Q8 if self.mom_q8 else N.LEMA_STATE_FP32
+        N.check(self.lib.lema_adamw_step_q8(self.c_segs, self.n, ctypes.byref(args), moments,
+                                            _stream_handle(stream)), "lema_adamw_step_q8")
+
+
+def adamw_step_q8(segments: Sequence[AdamwQ8Segment], *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
+                  weight_decay=0.01, step, stream=None) -> None:
+    """One AdamW step with int8 moments and/or an int8 gradient accumulator
+    (README "Quantization": dequantized only inside the step)."""
+    AdamwQ8Plan(segments).step(lr=lr, beta1=beta1, beta2=beta2, eps=eps,
+                               weight_decay=weight_decay, step=step, stream=stream)
+
+
+@dataclass
+class AccumQ8Segment:
+    acc: Q8
+    grad: torch.Tensor           # bf16
+
+
+class AccumQ8Plan:
+    """int8 accumulation segments marshalled once for repeated calls."""
+
+    def __init__(self, segments: Sequence[AccumQ8Segment]):
+        self.lib = N.load()
+        self.segments = list(segments)
+        cs = []
+        for i, s in enumerate(self.segments):
+            n = s.grad.numel()
+            codes, scale = s.acc.pointers(n, f"acc[{i}]")
+            cs.append(N.AccumQ8Seg(codes, scale, _check(s.grad, torch.bfloat16, n, f"grad[{i}]"),
+                                   n, s.acc.row_len))
+        self.n = len(cs)
+        self.c_segs = (N.AccumQ8Seg * max(1, self.n))(*cs)
+
+    def run(self, *, overwrite: bool, stream=None) -> None:
+        N.check(self.lib.lema_grad_accum_q8(self.c_segs, self.n, 1 if overwrite else 0,
+                                            _stream_handle(stream)), "lema_grad_accum_q8")
+
+
+def grad_accum_q8(segments: Sequence[AccumQ8Segment], *, overwrite: bool, stream=None) -> None:
+    """acc = Q(f32(g)) (overwrite) or acc = Q(D(acc) + f32(g)), on the GPU."""
+    AccumQ8Plan(segments).run(overwrite=overwrite, stream=stream)
 
 
 # ------------------------------------------------------------ host memory

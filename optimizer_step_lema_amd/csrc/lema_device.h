@@ -1,0 +1,109 @@
+// lema_device.h -- device helpers shared by the gfx950 kernel files: vector
+// types, global-address-space access, bf16 conversion, the per-element AdamW
+// arithmetic and the tile -> segment lookup of the launch tables.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "lema_internal.h"
+
+namespace lema {
+namespace dev {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Pointers into global memory (address space 1).  The segment pointers come
+// out of LDS, so without this the compiler could not prove where they point
+// and would emit flat instructions instead of global loads and stores.
+#define LEMA_GLOBAL __attribute__((address_space(1)))
+typedef LEMA_GLOBAL float gfloat;
+typedef LEMA_GLOBAL uint16_t gu16;
+typedef LEMA_GLOBAL f32x4 gf32x4;
+typedef LEMA_GLOBAL u32x2 gu32x2;
+
+template <class T>
+__device__ __forceinline__ T *as_global(uint64_t addr) {
+    return reinterpret_cast<T *>(addr);
+}
+
+// ------------------------------------------------------------- helpers
+
+// bf16 is the upper half of an fp32: widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_one(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// Two fp32 -> a pair of bf16, nearest-even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t to_bf16_pair(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    bf16x2 b = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, b);
+}
+__device__ __forceinline__ uint16_t to_bf16_one(float x) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// One AdamW element (the arithmetic stated in include/lema.h).
+__device__ __forceinline__ void adamw_elem(float &w, float &m, float &v, float g,
+                                           const AdamwConsts &c) {
+#pragma clang fp contract(off)
+    const float w_decayed = w * c.decay;
+    const float m_new = c.b1 * m + c.omb1 * g;
+    const float v_new = c.b2 * v + c.omb2 * (g * g);
+    const float denom = __builtin_sqrtf(v_new) * c.inv_bc2_root + c.eps;
+    w = w_decayed - c.step_size * (m_new / denom);
+    m = m_new;
+    v = v_new;
+}
+
+__device__ __forceinline__ float accum_elem(float acc, float g, bool overwrite) {
+#pragma clang fp contract(off)
+    return overwrite ? g : acc + g;
+}
+
+// ---------------------------------------------------------- segment lookup
+
+// Nontemporal vector loads and stores through global-address-space pointers.
+template <class T>
+__device__ __forceinline__ T ld_nt(uint64_t base, int64_t i) {
+    return __builtin_nontemporal_load(reinterpret_cast<const LEMA_GLOBAL T *>(base) + i);
+}
+template <class T>
+__device__ __forceinline__ void st_nt(uint64_t base, int64_t i, T v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<LEMA_GLOBAL T *>(base) + i);
+}
+
+// The segment holding tile t: the last s with tile_begin[s] <= t.  The
+// table guarantees tile_begin[0] = 0 <= t < tile_begin[nseg].
+__device__ __forceinline__ int find_segment(const uint32_t *__restrict__ tile_begin, int nseg,
+                                            uint32_t t) {
+    int lo = 0, hi = nseg;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_begin[mid] <= t)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return lo;
+}
+
+// Run fn(record, block-within-segment) for the block of this workgroup.
+// Table layout: uint32_t begin[nseg + 1] (prefix sums of blocks per segment),
+// padded to 64 bytes, then Rec[nseg].
+template <class Rec, class Fn>
+__device__ __forceinline__ void block_of_table(const void *table, int nseg, uint32_t block0,
+                                               const Fn &fn) {
+    const uint32_t *begin = static_cast<const uint32_t *>(table);
+    const Rec *recs = reinterpret_cast<const Rec *>(static_cast<const char *>(table) +
+                                                    table_tiles_bytes(nseg));
+    const uint32_t t = block0 + blockIdx.x;
+    const int s = find_segment(begin, nseg, t);
+    fn(recs[s], t - begin[s]);
+}
+
+}  // namespace dev
+}  // namespace lema

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <vector>
 
@@ -43,7 +44,7 @@ static double beta_pow(double beta, int64_t t) {
     return acc;
 }
 
-lema_status check_hparams(const lema_adamw_args *a) {
+lema_status check_hparams(const lema_adamw_args *a, bool allow_q8_grad) {
     if (a == nullptr) return LEMA_ERR_NULL;
     const double vals[] = {a->lr, a->beta1, a->beta2, a->eps, a->weight_decay};
     for (double x : vals)
@@ -52,8 +53,9 @@ lema_status check_hparams(const lema_adamw_args *a) {
     if (a->beta1 < 0.0 || a->beta1 >= 1.0 || a->beta2 < 0.0 || a->beta2 >= 1.0) return LEMA_ERR_HPARAM;
     if (a->step < 1) return LEMA_ERR_HPARAM;
     if (a->reserved != 0) return LEMA_ERR_HPARAM;
-    if (a->grad_dtype != LEMA_GRAD_BF16 && a->grad_dtype != LEMA_GRAD_FP32) return LEMA_ERR_DTYPE;
-    return LEMA_OK;
+    if (a->grad_dtype == LEMA_GRAD_BF16 || a->grad_dtype == LEMA_GRAD_FP32) return LEMA_OK;
+    if (allow_q8_grad && a->grad_dtype == LEMA_GRAD_Q8) return LEMA_OK;
+    return LEMA_ERR_DTYPE;
 }
 
 AdamwConsts derive_consts(const lema_adamw_args *a) {
@@ -92,8 +94,8 @@ bool any_conflict(std::vector<Span> &spans) {
     return false;
 }
 
-static void add_span(std::vector<Span> &spans, const void *p, int64_t numel, size_t elem,
-                     bool written) {
+void add_span(std::vector<Span> &spans, const void *p, int64_t numel, size_t elem,
+              bool written) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
     spans.push_back(Span{lo, lo + static_cast<uintptr_t>(numel) * elem, written});
 }
@@ -286,65 +288,55 @@ uint64_t count_tiles(const std::vector<SegRec> &recs) {
 
 }  // namespace
 
+lema_status launch_on_table(const std::vector<unsigned char> &bytes, hipStream_t stream,
+                            const std::function<hipError_t(const void *)> &launch) {
+    DeviceState *d = nullptr;
+    lema_status st = device_state(&d, nullptr);
+    if (st != LEMA_OK) return st;
+    std::lock_guard<std::mutex> lock(d->mu);
+    TableEntry *t = nullptr;
+    st = acquire_table(*d, bytes, stream, &t);
+    if (st != LEMA_OK) return st;
+    hipError_t e = launch(t->dev);
+    lema_status rel = release_table(*d, t, stream);
+    if (e != hipSuccess) return hip_failed(e);
+    return rel;
+}
+
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
                               GradMode grad_mode, hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
-    DeviceState *d = nullptr;
-    lema_status st = device_state(&d, nullptr);
-    if (st != LEMA_OK) return st;
     bool with_delta = false;
     for (const SegRec &r : recs) with_delta |= r.p[6] != 0;
-
     TableBuild tb;
     build_table(recs, &tb);
-    std::lock_guard<std::mutex> lock(d->mu);
-    TableEntry *t = nullptr;
-    st = acquire_table(*d, tb.bytes, stream, &t);
-    if (st != LEMA_OK) return st;
-    hipError_t e = launch_adamw(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_mode,
-                                with_delta, c, stream);
-    lema_status rel = release_table(*d, t, stream);
-    if (e != hipSuccess) return hip_failed(e);
-    return rel;
+    return launch_on_table(tb.bytes, stream, [&](const void *table) {
+        return launch_adamw(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_mode,
+                            with_delta, c, stream);
+    });
 }
 
 lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
                               hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
-    DeviceState *d = nullptr;
-    lema_status st = device_state(&d, nullptr);
-    if (st != LEMA_OK) return st;
     TableBuild tb;
     build_table(recs, &tb);
-    std::lock_guard<std::mutex> lock(d->mu);
-    TableEntry *t = nullptr;
-    st = acquire_table(*d, tb.bytes, stream, &t);
-    if (st != LEMA_OK) return st;
-    hipError_t e = launch_accum(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), overwrite,
-                                stream);
-    lema_status rel = release_table(*d, t, stream);
-    if (e != hipSuccess) return hip_failed(e);
-    return rel;
+    return launch_on_table(tb.bytes, stream, [&](const void *table) {
+        return launch_accum(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), overwrite,
+                            stream);
+    });
 }
 
 lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
-    DeviceState *d = nullptr;
-    lema_status st = device_state(&d, nullptr);
-    if (st != LEMA_OK) return st;
     TableBuild tb;
     build_table(recs, &tb);
-    std::lock_guard<std::mutex> lock(d->mu);
-    TableEntry *t = nullptr;
-    st = acquire_table(*d, tb.bytes, stream, &t);
-    if (st != LEMA_OK) return st;
-    hipError_t e = launch_merge(t->dev, tb.nseg, static_cast<uint32_t>(tb.total_tiles), stream);
-    lema_status rel = release_table(*d, t, stream);
-    if (e != hipSuccess) return hip_failed(e);
-    return rel;
+    return launch_on_table(tb.bytes, stream, [&](const void *table) {
+        return launch_merge(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), stream);
+    });
 }
 
 void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out,

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <cstdint>
+#include <functional>
 #include <vector>
 
 #include "lema.h"
@@ -21,7 +22,8 @@ struct Span {
 // Records hipError_t `e` as this thread's last HIP error; returns LEMA_ERR_HIP.
 lema_status hip_failed(hipError_t e);
 
-lema_status check_hparams(const lema_adamw_args *a);
+// Hyperparameters and gradient dtype (LEMA_GRAD_Q8 only where allowed).
+lema_status check_hparams(const lema_adamw_args *a, bool allow_q8_grad = false);
 AdamwConsts derive_consts(const lema_adamw_args *a);
 
 // Validates segment descriptors (sizes, pairing, required pointers,
@@ -29,11 +31,18 @@ AdamwConsts derive_consts(const lema_adamw_args *a);
 lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_t grad_dtype,
                                 bool delta_allowed, std::vector<Span> *spans);
 bool any_conflict(std::vector<Span> &spans);
+void add_span(std::vector<Span> &spans, const void *p, int64_t numel, size_t elem, bool written);
 
 // Launch records of the non-empty segments; last_bf16 (may be NULL) gives
 // each segment's last micro-batch for the fused accumulate-and-step mode.
 void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out,
                    const uint16_t *const *last_bf16);
+
+// Run launch(device copy of `bytes`) on the per-device table cache: the
+// table is uploaded unless a byte-identical one is cached, and stays
+// reserved until the launched work on `stream` has finished.
+lema_status launch_on_table(const std::vector<unsigned char> &bytes, hipStream_t stream,
+                            const std::function<hipError_t(const void *)> &launch);
 
 // Launch through the per-device table cache on `stream`.
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,

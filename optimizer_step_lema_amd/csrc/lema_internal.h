@@ -51,6 +51,41 @@ constexpr size_t table_bytes(int nseg) {
     return table_tiles_bytes(nseg) + sizeof(SegRec) * size_t(nseg);
 }
 
+// ------------------------------------------------ int8 rows with scales
+//
+// The int8 kernels give each row to a team of 2^team_log2 lanes of one
+// workgroup; every lane holds up to kQChunks chunks of 4 consecutive row
+// elements in registers.  Workgroups have kQBlock lanes, or kQBlockWide for
+// rows longer than kQBlock * kQChunks * 4 elements.  The launch table has the
+// layout above with Q8Rec records, and its prefix sums count workgroups.
+constexpr int kQBlock = 256;
+constexpr int kQBlockWide = 1024;
+constexpr int kQChunks = 4;                      // per lane
+constexpr int64_t kQMaxRow = int64_t(kQBlockWide) * kQChunks * 4;   // 16384 elements
+
+struct Q8Rec {
+    // step        : {master, m, m_scale, v, v_scale, grad, grad_scale, weight, orig, delta}
+    // accumulation: {acc_codes, acc_scale, grad_bf16}
+    // quantize    : {x, codes, scale}
+    uint64_t p[10];
+    int64_t numel;
+    int64_t row_len;
+    int64_t rows;
+    int32_t team_log2;    // lanes per row = 1 << team_log2, at most the workgroup
+    int32_t chunks;       // 4-element chunks per lane, 1 .. kQChunks
+    int32_t flags;        // kQVector: full chunks take 16/8/4-byte vector accesses
+    int32_t reserved;
+};
+static_assert(sizeof(Q8Rec) == 120, "int8 segment record is 120 bytes");
+constexpr int32_t kQVector = 1;
+
+// How the int8 step reads the moments and the gradient.
+enum QGrad : int { kQGradBf16 = 0, kQGradF32 = 1, kQGradQ8 = 2 };
+
+constexpr size_t q8_table_bytes(int nseg) {
+    return table_tiles_bytes(nseg) + sizeof(Q8Rec) * size_t(nseg);
+}
+
 struct AdamwConsts {
     float b1, omb1, b2, omb2, eps, decay, step_size, inv_bc2_root;
 };
@@ -63,6 +98,16 @@ hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles,
 hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
                         bool overwrite, hipStream_t stream);
 hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream);
+
+// int8 kernels; `block` (kQBlock or kQBlockWide) is the workgroup size the
+// table's records were sized for.
+hipError_t launch_adamw_q8(const void *table, int nseg, uint32_t total_blocks, bool moments_q8,
+                           QGrad grad, bool with_delta, int block, const AdamwConsts &c,
+                           hipStream_t stream);
+hipError_t launch_accum_q8(const void *table, int nseg, uint32_t total_blocks, bool overwrite,
+                           int block, hipStream_t stream);
+hipError_t launch_quantize_q8(const void *table, int nseg, uint32_t total_blocks, bool dequantize,
+                              int block, hipStream_t stream);
 
 // Measurement aids (include/lema_measure.h).
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);

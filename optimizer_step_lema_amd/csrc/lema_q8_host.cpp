@@ -1,0 +1,258 @@
+// lema_q8_host.cpp -- host side of the int8 + per-row-scale entry points of
+// include/lema.h: validation, row-team sizing, launch tables and launches.
+//
+// Method: LEMA README, "Quantization" (opt_state_bits = 8 and grad_acc_bits
+// = 8: int8 moments and accumulators with per-row scales, dequantized only
+// inside the per-layer AdamW step).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "lema.h"
+#include "lema_host_internal.h"
+#include "lema_internal.h"
+
+namespace lema {
+namespace {
+
+static_assert(kQMaxRow == LEMA_Q8_MAX_ROW, "row limit of the header and the kernels agree");
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Team width (log2), chunks per lane and workgroup size for rows of row_len
+// elements: the narrowest team whose lanes hold at most kQChunks chunks, in a
+// kQBlock-lane workgroup when such a team fits there, else a wide one.
+void size_team(int64_t row_len, int32_t *log2w, int32_t *chunks, int *block) {
+    const int64_t need = ceil_div(row_len, 4);
+    int lg = 0;
+    while (ceil_div(need, int64_t(1) << lg) > kQChunks) ++lg;
+    *log2w = lg;
+    *chunks = static_cast<int32_t>(ceil_div(need, int64_t(1) << lg));
+    *block = (1 << lg) <= kQBlock ? kQBlock : kQBlockWide;
+}
+
+int block_of(const Q8Rec &r) {
+    int32_t lg, chunks;
+    int block;
+    size_team(r.row_len, &lg, &chunks, &block);
+    return block;
+}
+
+uint64_t blocks_of(const Q8Rec &r) {
+    const int64_t rows_per_block = block_of(r) >> r.team_log2;
+    return static_cast<uint64_t>(ceil_div(r.rows, rows_per_block));
+}
+
+bool row_len_ok(int64_t row_len) { return row_len >= 1 && row_len <= kQMaxRow; }
+
+Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok) {
+    Q8Rec r{};
+    r.numel = numel;
+    r.row_len = row_len;
+    r.rows = ceil_div(numel, row_len);
+    int block;
+    size_team(row_len, &r.team_log2, &r.chunks, &block);
+    r.flags = (vector_ok && row_len % 4 == 0) ? kQVector : 0;
+    return r;
+}
+
+uintptr_t bits(const void *p) { return reinterpret_cast<uintptr_t>(p); }
+
+// Launch `recs` in at most two groups, one per workgroup size.
+template <class LaunchFn>
+lema_status launch_groups(const std::vector<Q8Rec> &recs, hipStream_t stream,
+                          const LaunchFn &launch) {
+    for (int block : {kQBlock, kQBlockWide}) {
+        std::vector<Q8Rec> sel;
+        for (const Q8Rec &r : recs)
+            if (block_of(r) == block) sel.push_back(r);
+        if (sel.empty()) continue;
+        const int n = static_cast<int>(sel.size());
+        std::vector<unsigned char> bytes(q8_table_bytes(n), 0);
+        uint32_t *begin = reinterpret_cast<uint32_t *>(bytes.data());
+        uint64_t blocks = 0;
+        for (int i = 0; i < n; ++i) {
+            begin[i] = static_cast<uint32_t>(blocks);
+            blocks += blocks_of(sel[i]);
+            if (blocks > 0xFFF00000ull) return LEMA_ERR_SIZE;
+        }
+        begin[n] = static_cast<uint32_t>(blocks);
+        std::memcpy(bytes.data() + table_tiles_bytes(n), sel.data(), sizeof(Q8Rec) * n);
+        lema_status st = launch_on_table(bytes, stream, [&](const void *table) {
+            return launch(table, n, static_cast<uint32_t>(blocks), block);
+        });
+        if (st != LEMA_OK) return st;
+    }
+    return LEMA_OK;
+}
+
+// The fp32-moment step with a bf16 or fp32 gradient is the plain step.
+lema_status plain_step(const lema_adamw_q8_seg *segs, int32_t nseg, const lema_adamw_args *args,
+                       void *stream) {
+    std::vector<lema_adamw_seg> plain(static_cast<size_t>(nseg));
+    for (int32_t i = 0; i < nseg; ++i) {
+        const lema_adamw_q8_seg &s = segs[i];
+        plain[i] = lema_adamw_seg{s.master, static_cast<float *>(s.exp_avg),
+                                  static_cast<float *>(s.exp_avg_sq), s.grad, s.weight_bf16,
+                                  s.orig_bf16, s.delta, s.numel};
+    }
+    return lema_adamw_step(plain.data(), nseg, args, stream);
+}
+
+}  // namespace
+}  // namespace lema
+
+using namespace lema;
+
+extern "C" {
+
+lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
+                               const lema_adamw_args *args, int32_t moment_dtype, void *stream) {
+    lema_status st = check_hparams(args, true);
+    if (st != LEMA_OK) return st;
+    if (moment_dtype != LEMA_STATE_FP32 && moment_dtype != LEMA_STATE_Q8) return LEMA_ERR_DTYPE;
+    if (nseg < 0) return LEMA_ERR_SIZE;
+    if (nseg > 0 && segs == nullptr) return LEMA_ERR_NULL;
+    const bool mom_q8 = moment_dtype == LEMA_STATE_Q8;
+    const int32_t gd = args->grad_dtype;
+    if (!mom_q8 && gd != LEMA_GRAD_Q8) return plain_step(segs, nseg, args, stream);
+
+    const size_t mom_size = mom_q8 ? 1 : 4;
+    const size_t grad_size = gd == LEMA_GRAD_BF16 ? 2 : gd == LEMA_GRAD_FP32 ? 4 : 1;
+    std::vector<Span> spans;
+    std::vector<Q8Rec> recs;
+    bool with_delta = false;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const lema_adamw_q8_seg &s = segs[i];
+        if (s.numel < 0) return LEMA_ERR_SIZE;
+        if ((s.orig_bf16 == nullptr) != (s.delta == nullptr)) return LEMA_ERR_NULL;
+        if (s.numel == 0) continue;
+        if (!row_len_ok(s.row_len)) return LEMA_ERR_SIZE;
+        if (!s.master || !s.exp_avg || !s.exp_avg_sq || !s.grad || !s.weight_bf16)
+            return LEMA_ERR_NULL;
+        if (mom_q8 && (!s.exp_avg_scale || !s.exp_avg_sq_scale)) return LEMA_ERR_NULL;
+        if (gd == LEMA_GRAD_Q8 && !s.grad_scale) return LEMA_ERR_NULL;
+
+        // required alignment: each array to its element size
+        uintptr_t f32 = bits(s.master) | bits(s.delta) |
+                        (mom_q8 ? bits(s.exp_avg_scale) | bits(s.exp_avg_sq_scale)
+                                : bits(s.exp_avg) | bits(s.exp_avg_sq)) |
+                        (gd == LEMA_GRAD_FP32 ? bits(s.grad) : 0) |
+                        (gd == LEMA_GRAD_Q8 ? bits(s.grad_scale) : 0);
+        uintptr_t b16 = bits(s.weight_bf16) | bits(s.orig_bf16) |
+                        (gd == LEMA_GRAD_BF16 ? bits(s.grad) : 0);
+        if ((f32 & 3) || (b16 & 1)) return LEMA_ERR_ALIGN;
+        // vector path: 16-byte fp32 arrays, 8-byte bf16, 4-byte codes
+        const uintptr_t v16 = bits(s.master) | bits(s.delta) |
+                              (mom_q8 ? 0 : bits(s.exp_avg) | bits(s.exp_avg_sq)) |
+                              (gd == LEMA_GRAD_FP32 ? bits(s.grad) : 0);
+        const uintptr_t v4 = (mom_q8 ? bits(s.exp_avg) | bits(s.exp_avg_sq) : 0) |
+                             (gd == LEMA_GRAD_Q8 ? bits(s.grad) : 0);
+        const bool vec = (v16 & 15) == 0 && (b16 & 7) == 0 && (v4 & 3) == 0;
+
+        Q8Rec r = make_rec(s.numel, s.row_len, vec);
+        add_span(spans, s.master, s.numel, 4, true);
+        add_span(spans, s.exp_avg, s.numel, mom_size, true);
+        add_span(spans, s.exp_avg_sq, s.numel, mom_size, true);
+        if (mom_q8) {
+            add_span(spans, s.exp_avg_scale, r.rows, 4, true);
+            add_span(spans, s.exp_avg_sq_scale, r.rows, 4, true);
+        }
+        add_span(spans, s.grad, s.numel, grad_size, false);
+        if (gd == LEMA_GRAD_Q8) add_span(spans, s.grad_scale, r.rows, 4, false);
+        add_span(spans, s.weight_bf16, s.numel, 2, true);
+        if (s.delta) {
+            add_span(spans, s.orig_bf16, s.numel, 2, false);
+            add_span(spans, s.delta, s.numel, 4, true);
+            with_delta = true;
+        }
+        const void *ptrs[10] = {s.master, s.exp_avg, mom_q8 ? s.exp_avg_scale : nullptr,
+                                s.exp_avg_sq, mom_q8 ? s.exp_avg_sq_scale : nullptr, s.grad,
+                                gd == LEMA_GRAD_Q8 ? s.grad_scale : nullptr, s.weight_bf16,
+                                s.orig_bf16, s.delta};
+        for (int k = 0; k < 10; ++k) r.p[k] = reinterpret_cast<uint64_t>(ptrs[k]);
+        recs.push_back(r);
+    }
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    if (recs.empty()) return LEMA_OK;
+    const AdamwConsts c = derive_consts(args);
+    const QGrad qg = gd == LEMA_GRAD_BF16 ? kQGradBf16 : gd == LEMA_GRAD_FP32 ? kQGradF32 : kQGradQ8;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks, int block) {
+        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, c, hs);
+    });
+}
+
+lema_status lema_grad_accum_q8(const lema_accum_q8_seg *segs, int32_t nseg, int32_t overwrite,
+                               void *stream) {
+    if (nseg < 0) return LEMA_ERR_SIZE;
+    if (nseg > 0 && segs == nullptr) return LEMA_ERR_NULL;
+    std::vector<Span> spans;
+    std::vector<Q8Rec> recs;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const lema_accum_q8_seg &s = segs[i];
+        if (s.numel < 0) return LEMA_ERR_SIZE;
+        if (s.numel == 0) continue;
+        if (!row_len_ok(s.row_len)) return LEMA_ERR_SIZE;
+        if (!s.acc || !s.acc_scale || !s.grad_bf16) return LEMA_ERR_NULL;
+        if ((bits(s.acc_scale) & 3) || (bits(s.grad_bf16) & 1)) return LEMA_ERR_ALIGN;
+        const bool vec = (bits(s.acc) & 3) == 0 && (bits(s.grad_bf16) & 7) == 0;
+        Q8Rec r = make_rec(s.numel, s.row_len, vec);
+        add_span(spans, s.acc, s.numel, 1, true);
+        add_span(spans, s.acc_scale, r.rows, 4, true);
+        add_span(spans, s.grad_bf16, s.numel, 2, false);
+        r.p[0] = reinterpret_cast<uint64_t>(s.acc);
+        r.p[1] = reinterpret_cast<uint64_t>(s.acc_scale);
+        r.p[2] = reinterpret_cast<uint64_t>(s.grad_bf16);
+        recs.push_back(r);
+    }
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    if (recs.empty()) return LEMA_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks, int block) {
+        return launch_accum_q8(table, n, blocks, overwrite != 0, block, hs);
+    });
+}
+
+static lema_status convert_rows(const lema_q8_tensor *t, int32_t n, bool dequantize,
+                                void *stream) {
+    if (n < 0) return LEMA_ERR_SIZE;
+    if (n > 0 && t == nullptr) return LEMA_ERR_NULL;
+    std::vector<Span> spans;
+    std::vector<Q8Rec> recs;
+    for (int32_t i = 0; i < n; ++i) {
+        const lema_q8_tensor &s = t[i];
+        if (s.numel < 0) return LEMA_ERR_SIZE;
+        if (s.numel == 0) continue;
+        if (!row_len_ok(s.row_len)) return LEMA_ERR_SIZE;
+        if (!s.x || !s.codes || !s.scale) return LEMA_ERR_NULL;
+        if ((bits(s.x) | bits(s.scale)) & 3) return LEMA_ERR_ALIGN;
+        const bool vec = (bits(s.x) & 15) == 0 && (bits(s.codes) & 3) == 0;
+        Q8Rec r = make_rec(s.numel, s.row_len, vec);
+        add_span(spans, s.x, s.numel, 4, dequantize);
+        add_span(spans, s.codes, s.numel, 1, !dequantize);
+        add_span(spans, s.scale, r.rows, 4, !dequantize);
+        r.p[0] = reinterpret_cast<uint64_t>(s.x);
+        r.p[1] = reinterpret_cast<uint64_t>(s.codes);
+        r.p[2] = reinterpret_cast<uint64_t>(s.scale);
+        recs.push_back(r);
+    }
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    if (recs.empty()) return LEMA_OK;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    return launch_groups(recs, hs, [&](const void *table, int nrec, uint32_t blocks, int block) {
+        return launch_quantize_q8(table, nrec, blocks, dequantize, block, hs);
+    });
+}
+
+lema_status lema_quantize_rows(const lema_q8_tensor *t, int32_t n, void *stream) {
+    return convert_rows(t, n, false, stream);
+}
+
+lema_status lema_dequantize_rows(const lema_q8_tensor *t, int32_t n, void *stream) {
+    return convert_rows(t, n, true, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,335 @@
+"""GPU parity of the int8 + per-row-scale path against the CPU oracle.
+
+LEMA README, "Quantization": int8 moments (opt_state_bits = 8) and int8
+gradient accumulators (grad_acc_bits = 8) with one scale per row,
+dequantized only inside the per-layer AdamW step.  Initial int8 state is
+quantized by the oracle on the host and uploaded, so every comparison here
+checks the HIP path against oracle-made inputs and oracle-made outputs.  The
+bar is bit-exact for codes, scales (NaN compared as a class), the fp32
+master and delta and the bf16 weight.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from parity import compare_bf16, compare_f32, oracle_consts, to_np
+
+pytestmark = pytest.mark.gpu
+HP = synth.HPARAMS
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def L():
+    import optimizer_step_lema_amd as lema
+    lema.load()
+    return lema
+
+
+def up(a: np.ndarray, offset: int = 0) -> torch.Tensor:
+    """Host array -> device tensor starting `offset` elements into its buffer."""
+    dt = {np.float32: torch.float32, np.int8: torch.int8, np.uint16: torch.int16}[a.dtype.type]
+    buf = torch.empty(a.size + offset, dtype=dt, device=DEV)
+    t = buf[offset:]
+    src = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+    t.copy_(src)
+    return t.view(torch.bfloat16) if a.dtype == np.uint16 else t
+
+
+def host_f32(n, sigma, seed, square=False):
+    t = synth.normal(n, sigma, seed, DEV)
+    if square:
+        t.mul_(t)
+    return to_np(t)
+
+
+def host_bf16(n, sigma, seed):
+    return to_np(synth.normal(n, sigma, seed, DEV).to(torch.bfloat16))
+
+
+def compare_codes(got: torch.Tensor, ref: np.ndarray, name: str):
+    g = to_np(got)
+    bad = int((g != ref).sum())
+    assert bad == 0, f"{name}: {bad} int8 codes differ"
+
+
+class Case:
+    """One segment: host inputs, device tensors, and the oracle's outputs."""
+
+    def __init__(self, L, n, row_len, seed, *, grad="bf16", moments="q8", delta=False,
+                 offset=0, specials=False):
+        self.n, self.row_len = n, row_len
+        h = {"master": host_f32(n, 0.02, seed)}
+        m32 = host_f32(n, 1e-4, seed + 1)
+        v32 = host_f32(n, 1e-3, seed + 2, square=True)
+        if grad == "bf16":
+            g = host_bf16(n, 1e-3, seed + 3)
+        elif grad == "fp32":
+            g = host_f32(n, 3e-3, seed + 3)
+        else:
+            g = oracle.quantize_rows(host_f32(n, 3e-3, seed + 3), row_len)
+        if specials and n > 40:
+            gv = g[0] if isinstance(g, tuple) else g
+            if gv.dtype == np.uint16:
+                gv[3], gv[17] = 0x7FC0, 0x7F80          # NaN, +inf (bf16 patterns)
+            elif gv.dtype == np.float32:
+                gv[3], gv[17] = np.nan, np.inf
+            m32[5:5 + min(row_len, n - 5)] = 0.0        # a zero stretch of m
+        self.h = h
+        self.mom_q8 = moments == "q8"
+        if self.mom_q8:
+            self.mq = oracle.quantize_rows(m32, row_len)
+            self.vq = oracle.quantize_rows(v32, row_len)
+        else:
+            self.m32, self.v32 = m32, v32
+        self.g = g
+        self.orig = oracle.rne16(h["master"]) if delta else None
+
+        # device tensors
+        self.master = up(h["master"], offset)
+        if self.mom_q8:
+            self.m = L.Q8(up(self.mq[0], offset), up(self.mq[1]), row_len)
+            self.v = L.Q8(up(self.vq[0], offset), up(self.vq[1]), row_len)
+        else:
+            self.m, self.v = up(m32, offset), up(v32, offset)
+        self.grad = L.Q8(up(g[0], offset), up(g[1]), row_len) if isinstance(g, tuple) else up(g, offset)
+        self.weight = torch.empty(n + offset, dtype=torch.bfloat16, device=DEV)[offset:]
+        self.dev_orig = None if self.orig is None else up(self.orig, offset)
+        self.delta = None if self.orig is None else torch.empty(n + offset, device=DEV)[offset:]
+
+    def segment(self, L):
+        return L.AdamwQ8Segment(self.master, self.m, self.v, self.grad, self.weight,
+                                self.dev_orig, self.delta)
+
+    def run_oracle(self, consts):
+        master = self.h["master"].copy()
+        if self.mom_q8:
+            m = (self.mq[0].copy(), self.mq[1].copy())
+            v = (self.vq[0].copy(), self.vq[1].copy())
+        else:
+            m, v = self.m32.copy(), self.v32.copy()
+        w, d = oracle.adamw_step_q8(master, m, v, self.g, consts, self.row_len, orig=self.orig)
+        return master, m, v, w, d
+
+    def check(self, consts, tag):
+        master, m, v, w, d = self.run_oracle(consts)
+        compare_f32(to_np(self.master), master, tag + ".master")
+        compare_bf16(to_np(self.weight), w, tag + ".weight")
+        if d is not None:
+            compare_f32(to_np(self.delta), d, tag + ".delta")
+        if self.mom_q8:
+            for name, dev, ref in (("m", self.m, m), ("v", self.v, v)):
+                compare_codes(dev.codes, ref[0], f"{tag}.{name}.codes")
+                compare_f32(to_np(dev.scale), ref[1], f"{tag}.{name}.scale")
+        else:
+            compare_f32(to_np(self.m), m, tag + ".m")
+            compare_f32(to_np(self.v), v, tag + ".v")
+        return master, m, v
+
+
+def step(L, cases, t, stream=None):
+    L.adamw_step_q8([c.segment(L) for c in cases], step=t, stream=stream, **HP)
+
+
+# ------------------------------------------------------------ conversions
+
+@pytest.mark.parametrize("row_len", [1, 3, 4, 16, 100, 256, 4096, 4100, 11008, 16384])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_quantize_dequantize_rows(L, row_len, offset):
+    """Codes and scales of lema_quantize_rows and the values of
+    lema_dequantize_rows against the oracle, with a ragged last row, zero,
+    NaN, infinite and subnormal rows, on vector and element paths."""
+    rows = 5
+    n = row_len * rows + max(1, row_len // 3)
+    x = host_f32(n, 1e-3, 7000 + row_len)
+    x[:row_len] = 0.0                                   # an all-zero row
+    x[row_len] = np.nan                                 # a NaN row
+    x[2 * row_len] = np.inf                             # an infinite row
+    x[3 * row_len:4 * row_len] = np.float32(1e-42)      # a subnormal row
+    q = L.Q8(torch.empty(n + offset, dtype=torch.int8, device=DEV)[offset:],
+             torch.empty(L.Q8.rows_of(n, row_len), device=DEV), row_len)
+    xd = up(x, offset)
+    L.quantize_rows([(xd, q)])
+    rq, rs = oracle.quantize_rows(x, row_len)
+    compare_codes(q.codes, rq, "codes")
+    compare_f32(to_np(q.scale), rs, "scale")
+    back = torch.empty(n + offset, device=DEV)[offset:]
+    L.dequantize_rows([(back, q)])
+    compare_f32(to_np(back), oracle.dequantize_rows(rq, rs, row_len), "dequantized")
+
+
+# ------------------------------------------------------------------ step
+
+@pytest.mark.parametrize("grad", ["bf16", "fp32", "q8"])
+@pytest.mark.parametrize("delta", [False, True])
+@pytest.mark.parametrize("row_len", [1, 7, 64, 4096, 11008])
+def test_q8_step_matches_oracle(L, grad, delta, row_len):
+    """int8 moments with each gradient kind, ragged last rows, narrow teams
+    (row_len 1, 7: element path), one-workgroup rows (4096) and the wide
+    workgroup (11008)."""
+    n = row_len * 6 + (row_len // 2 or 1)
+    c = Case(L, n, row_len, 9000 + row_len, grad=grad, delta=delta)
+    step(L, [c], 100)
+    torch.cuda.synchronize()
+    c.check(oracle_consts(HP, 100), f"q8[{grad},{delta},{row_len}]")
+
+
+@pytest.mark.parametrize("offset", [1, 3])
+def test_q8_step_misaligned(L, offset):
+    """Arrays starting off their vector alignment take the element path."""
+    cases = [Case(L, 4096 * 3 + 5, 4096, 9100, delta=True, offset=offset),
+             Case(L, 333, 16, 9200, grad="q8", offset=offset)]
+    L.adamw_step_q8([cases[0].segment(L)], step=7, **HP)
+    L.adamw_step_q8([cases[1].segment(L)], step=7, **HP)
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        c.check(oracle_consts(HP, 7), f"misaligned{i}")
+
+
+def test_q8_step_mixed_segments_one_call(L):
+    """One call over segments of both workgroup sizes, different row lengths,
+    empty segments and delta on only some of them."""
+    spec = [(4096 * 4, 4096, True), (11008 * 2 + 9, 11008, False), (16 * 100, 16, True),
+            (2304, 2304, False), (5, 3, False), (16384 * 2, 16384, True), (777, 1, False)]
+    cases = [Case(L, n, rl, 9300 + 10 * i, delta=d) for i, (n, rl, d) in enumerate(spec)]
+    segs = [c.segment(L) for c in cases]
+    empty = L.AdamwQ8Segment(torch.empty(0, device=DEV), L.Q8.zeros(0, 4), L.Q8.zeros(0, 4),
+                             torch.empty(0, dtype=torch.bfloat16, device=DEV),
+                             torch.empty(0, dtype=torch.bfloat16, device=DEV))
+    L.adamw_step_q8(segs[:3] + [empty] + segs[3:], step=50, **HP)
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        c.check(oracle_consts(HP, 50), f"mixed{i}")
+
+
+def test_fp32_moments_with_q8_accumulator(L):
+    """fp32 moments with an int8 gradient accumulator (grad_acc_bits = 8 alone)."""
+    cases = [Case(L, 4096 * 3 + 100, 4096, 9400, grad="q8", moments="fp32", delta=True),
+             Case(L, 11008 * 2, 11008, 9410, grad="q8", moments="fp32")]
+    step(L, cases, 12)
+    torch.cuda.synchronize()
+    for i, c in enumerate(cases):
+        c.check(oracle_consts(HP, 12), f"fp32mom{i}")
+
+
+def test_q8_three_consecutive_steps(L):
+    """State carried over three steps (new bf16 gradients each time) stays
+    bit-identical to the oracle's."""
+    n, rl = 4096 * 5 + 300, 4096
+    c = Case(L, n, rl, 9500, delta=True)
+    master, m, v = c.h["master"].copy(), (c.mq[0].copy(), c.mq[1].copy()), (c.vq[0].copy(), c.vq[1].copy())
+    for t in (20, 21, 22):
+        g = host_bf16(n, 1e-3, 9600 + t)
+        c.grad = up(g)
+        step(L, [c], t)
+        w, d = oracle.adamw_step_q8(master, m, v, g, oracle_consts(HP, t), rl, orig=c.orig)
+        torch.cuda.synchronize()
+        compare_f32(to_np(c.master), master, f"t{t}.master")
+        compare_bf16(to_np(c.weight), w, f"t{t}.weight")
+        compare_f32(to_np(c.delta), d, f"t{t}.delta")
+        compare_codes(c.m.codes, m[0], f"t{t}.m")
+        compare_codes(c.v.codes, v[0], f"t{t}.v")
+        compare_f32(to_np(c.m.scale), m[1], f"t{t}.ms")
+        compare_f32(to_np(c.v.scale), v[1], f"t{t}.vs")
+
+
+def test_q8_step_special_values(L):
+    """NaN and infinite gradients: their rows get NaN or infinite scales and
+    zero codes, other rows are untouched; a zero stretch of m is exact."""
+    for grad in ("bf16", "fp32"):
+        c = Case(L, 64 * 10 + 3, 64, 9700, grad=grad, specials=True, delta=True)
+        step(L, [c], 3)
+        torch.cuda.synchronize()
+        _, m, _ = c.check(oracle_consts(HP, 3), f"specials[{grad}]")
+        assert np.isnan(m[1][0])                      # the NaN lands in row 0
+
+
+# ----------------------------------------------------------- accumulation
+
+@pytest.mark.parametrize("row_len", [3, 64, 4096, 11008])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_q8_accumulation(L, row_len, offset):
+    """Four bf16 micro-batches into an int8 accumulator: overwrite, then
+    dequantize-add-requantize, bit-exact after every micro-batch."""
+    n = row_len * 4 + row_len // 2 + 1
+    acc = L.Q8(torch.full((n + offset,), 77, dtype=torch.int8, device=DEV)[offset:],
+               torch.full((L.Q8.rows_of(n, row_len),), 5.0, device=DEV), row_len)
+    ref_q = np.zeros(n, np.int8)
+    ref_s = np.zeros(L.Q8.rows_of(n, row_len), np.float32)
+    for k in range(4):
+        g = host_bf16(n, 1e-3, 9800 + 10 * row_len + k)
+        L.grad_accum_q8([L.AccumQ8Segment(acc, up(g, offset))], overwrite=k == 0)
+        oracle.grad_accum_q8(ref_q, ref_s, g, k == 0, row_len)
+        torch.cuda.synchronize()
+        compare_codes(acc.codes, ref_q, f"acc{k}.codes")
+        compare_f32(to_np(acc.scale), ref_s, f"acc{k}.scale")
+
+
+def test_q8_plans_match_direct_calls(L):
+    """AdamwQ8Plan / AccumQ8Plan reuse one marshalled list; results equal a
+    direct call on cloned state."""
+    a = Case(L, 4096 * 2 + 10, 4096, 9900, delta=True)
+    b = Case(L, 4096 * 2 + 10, 4096, 9900, delta=True)
+    plan = L.AdamwQ8Plan([a.segment(L)])
+    plan.step(step=9, **HP)
+    step(L, [b], 9)
+    torch.cuda.synchronize()
+    for x, y in ((a.master, b.master), (a.m.codes, b.m.codes), (a.v.scale, b.v.scale),
+                 (a.weight, b.weight), (a.delta, b.delta)):
+        assert torch.equal(x, y)
+
+
+# -------------------------------------------------- workloads at full size
+
+def _workload_q8(L, w, row_len_of, *, delta, grad="bf16"):
+    cases = []
+    for i, (label, shape) in enumerate(w.segments):
+        n = w.numels[i]
+        cases.append(Case(L, n, row_len_of(shape), 100000 + 1000 * w.wid + i, grad=grad,
+                          delta=delta))
+    return cases
+
+
+def last_dim(shape):
+    return shape[-1]
+
+
+def test_llama7b_attn_last4_q8_full(L):
+    """Llama-2-7B q,k,v,o of the last 4 layers (268 M parameters, rows of
+    4096) with int8 moments, bf16 gradient and delta: every element checked."""
+    w = synth.WORKLOADS["llama7b_attn_last4"]
+    cases = _workload_q8(L, w, last_dim, delta=True)
+    step(L, cases, w.step)
+    torch.cuda.synchronize()
+    consts = oracle_consts(HP, w.step)
+    for i, c in enumerate(cases):
+        c.check(consts, f"attn{i}")
+        del c.master, c.m, c.v, c.grad, c.weight, c.dev_orig, c.delta
+
+
+def test_llama7b_layer_q8_accumulate_then_step(L):
+    """One Llama-2-7B layer (rows of 4096 and 11008, 1-D norms): 8 micro-
+    batches into int8 accumulators, then the step with int8 moments and the
+    int8 accumulator as its gradient; every element checked."""
+    w = synth.WORKLOADS["llama7b_layer"]
+    consts = oracle_consts(HP, w.step)
+    for i, (label, shape) in enumerate(w.segments):
+        n, rl = w.numels[i], shape[-1]
+        c = Case(L, n, rl, 200000 + i, grad="bf16", delta=True)
+        acc = L.Q8.empty(n, rl)
+        ref_q = np.zeros(n, np.int8)
+        ref_s = np.zeros(L.Q8.rows_of(n, rl), np.float32)
+        for k in range(w.microbatches):
+            g = host_bf16(n, 1e-3, synth.seed_of(w.wid, synth.ARRAY_GRAD0 + k, i))
+            L.grad_accum_q8([L.AccumQ8Segment(acc, up(g))], overwrite=k == 0)
+            oracle.grad_accum_q8(ref_q, ref_s, g, k == 0, rl)
+        c.grad, c.g = acc, (ref_q, ref_s)
+        step(L, [c], w.step)
+        torch.cuda.synchronize()
+        compare_codes(acc.codes, ref_q, f"{label}.acc")
+        compare_f32(to_np(acc.scale), ref_s, f"{label}.acc_scale")
+        c.check(consts, label)
