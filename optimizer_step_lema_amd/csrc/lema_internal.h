@@ -54,14 +54,24 @@ constexpr size_t table_bytes(int nseg) {
 // ------------------------------------------------ int8 rows with scales
 //
 // The int8 kernels give each row to a team of 2^team_log2 lanes of one
-// workgroup; every lane holds up to kQChunks chunks of 4 consecutive row
-// elements in registers.  Workgroups have kQBlock lanes, or kQBlockWide for
-// rows longer than kQBlock * kQChunks * 4 elements.  The launch table has the
-// layout above with Q8Rec records, and its prefix sums count workgroups.
+// workgroup; every lane holds up to `chunks` chunks of 4 consecutive row
+// elements in registers.  Workgroups have kQBlock lanes and hold up to
+// kQStepChunks (AdamW) or kQCodeChunks (accumulation, conversions) chunks per
+// lane; rows too long for that go to kQBlockWide-lane workgroups with
+// kQWideChunks per lane.  The launch table has the layout above with Q8Rec
+// records, and its prefix sums count workgroups.
 constexpr int kQBlock = 256;
 constexpr int kQBlockWide = 1024;
-constexpr int kQChunks = 4;                      // per lane
-constexpr int64_t kQMaxRow = int64_t(kQBlockWide) * kQChunks * 4;   // 16384 elements
+#ifndef LEMA_Q8_STEP_CHUNKS
+#define LEMA_Q8_STEP_CHUNKS 4
+#endif
+#ifndef LEMA_Q8_CODE_CHUNKS
+#define LEMA_Q8_CODE_CHUNKS 4
+#endif
+constexpr int kQStepChunks = LEMA_Q8_STEP_CHUNKS;
+constexpr int kQCodeChunks = LEMA_Q8_CODE_CHUNKS;
+constexpr int kQWideChunks = 4;
+constexpr int64_t kQMaxRow = int64_t(kQBlockWide) * kQWideChunks * 4;   // 16384 elements
 
 struct Q8Rec {
     // step        : {master, m, m_scale, v, v_scale, grad, grad_scale, weight, orig, delta}
@@ -72,7 +82,7 @@ struct Q8Rec {
     int64_t row_len;
     int64_t rows;
     int32_t team_log2;    // lanes per row = 1 << team_log2, at most the workgroup
-    int32_t chunks;       // 4-element chunks per lane, 1 .. kQChunks
+    int32_t chunks;       // 4-element chunks per lane
     int32_t flags;        // kQVector: full chunks take 16/8/4-byte vector accesses
     int32_t reserved;
 };

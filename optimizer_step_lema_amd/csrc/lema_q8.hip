@@ -8,9 +8,8 @@
 //
 // Row teams.  The new codes of a row depend on the absmax of the whole new
 // row, so each row belongs to one team of S lanes (S a power of two up to the
-// workgroup size: 256 lanes, or 1024 for rows beyond 4096 elements) that keeps
-// the row's new values in registers, at most 4 chunks per lane, until the
-// team has reduced the absmax.  Chunk c of team lane l holds row elements
+// workgroup size: 256 lanes, or 1024 for the longest rows) that keeps the
+// row's new values in registers until the team has reduced the absmax.  Chunk c of team lane l holds row elements
 // 4*(c*S + l) .. 4*(c*S + l) + 3, so one chunk step of a team covers a
 // contiguous run of 4*S elements: 16-byte fp32, 8-byte bf16 and 4-byte int8
 // accesses, contiguous across the team.  Teams of at most 64 lanes lie inside
@@ -21,12 +20,17 @@
 // Each lane issues all its loads before any arithmetic, since stores through
 // the table's pointers could alias later loads as far as the compiler knows.
 // The fp32 outputs of the step (master, bf16 weight, delta) are stored as
-// soon as they are computed; the codes and scales follow the reduction.
+// soon as they are computed; the codes and scales follow the reduction.  A
+// lane whose chunks are all full vector chunks (every lane of a row whose
+// length is a multiple of 4*S, on aligned arrays) takes a path without
+// per-chunk tests; other lanes take the element-guarded one.  The two paths
+// meet before the team reduction, so its barrier is never inside a
+// divergent branch.
 //
 // Arithmetic: the fp32 step of lema_kernels.hip element for element;
 // dequantization is one binary32 multiplication f32(code) * scale;
-// quantization divides by the scale with the IEEE division, rounds half to
-// even (v_rndne_f32) and clamps to [-127, 127].  Absmax is taken on the
+// quantization gives the code of the IEEE quotient x / scale rounded half to
+// even and clamped to [-127, 127], mostly without dividing (see QuantRow).  Absmax is taken on the
 // magnitude bits as unsigned integers, so a NaN anywhere in a row dominates
 // (giving a NaN scale) and the result does not depend on reduction order.
 #include <hip/hip_runtime.h>
@@ -66,21 +70,74 @@ __device__ __forceinline__ float scale_of(uint32_t absmax_bits) {
     return __uint_as_float(absmax_bits) / 127.0f;
 }
 
-// Codes are only formed from a finite positive scale; other rows get zeros.
-__device__ __forceinline__ bool usable(float scale) {
-    return scale > 0.0f && mag_bits(scale) < 0x7F800000u;
-}
+// The per-row part of quantization.  Codes are formed only from a finite
+// positive scale s (other rows get zeros).  When s is a normal number its
+// reciprocal r = 1/s (IEEE division, correctly rounded) is normal too, and
+// y = x*r serves in place of x/s:
+//   |x| <= absmax and s >= absmax/127 (1 - 2^-24) bound |x/s| by 127.00002;
+//   |y - x/s| <= |x/s| 2^-24 (r's rounding) + 2^-18 (half an ulp below 128)
+//   < 1.2e-5, and the IEEE quotient q = RN(x/s) is within 2^-18 of x/s.
+// So when y lies more than 2^-15 from the nearest half-integer, y and q lie
+// strictly between the same two half-integers and round to the same integer,
+// which is within [-127, 127].  The lane rounds y by adding 1.5 * 2^23: the
+// sum is rounded to an integer, half to even, and its low byte is that
+// integer's two's-complement byte.  A lane holding any value nearer to a
+// half-integer (about 6e-5 of all values), and every lane of a row with a
+// subnormal scale, takes the codes from the IEEE division instead.
+struct QuantRow {
+    float s;      // the row's new scale
+    float r;      // 1/s when `fast`
+    bool ok;      // codes are formed (else all zero)
+    bool fast;    // s is normal: x*r decides away from half-integers
+};
 
-__device__ __forceinline__ int32_t quant(float x, float scale) {
+__device__ __forceinline__ QuantRow quant_row(uint32_t absmax_bits) {
 #pragma clang fp contract(off)
-    float k = __builtin_rintf(x / scale);
-    k = __builtin_fminf(__builtin_fmaxf(k, -127.0f), 127.0f);
-    return static_cast<int32_t>(k);
+    QuantRow q;
+    q.s = scale_of(absmax_bits);
+    q.ok = q.s > 0.0f && mag_bits(q.s) < 0x7F800000u;
+    q.fast = q.ok && mag_bits(q.s) >= 0x00800000u;
+    q.r = q.fast ? 1.0f / q.s : 0.0f;
+    return q;
 }
 
-__device__ __forceinline__ uint32_t pack4(int32_t a, int32_t b, int32_t c, int32_t d) {
-    return (uint32_t(a) & 0xFFu) | ((uint32_t(b) & 0xFFu) << 8) | ((uint32_t(c) & 0xFFu) << 16) |
-           (uint32_t(d) << 24);
+constexpr float kRoundMagic = 12582912.0f;    // 1.5 * 2^23
+constexpr float kNearHalf = 0x1p-15f;
+
+// Packed codes of four values from y = x*r; `near` keeps the smallest
+// distance of any y from a half-integer.
+__device__ __forceinline__ uint32_t quant4_fast(f32x4 x, float r, float &near) {
+#pragma clang fp contract(off)
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float y = x[k] * r;
+        const float g = y + kRoundMagic;        // integer nearest y, ties to even
+        const float yk = g - kRoundMagic;       // that integer, exactly
+        near = __builtin_fminf(near, __builtin_fabsf(__builtin_fabsf(y - yk) - 0.5f));
+        w |= (__float_as_uint(g) & 0xFFu) << (8 * k);
+    }
+    return w;
+}
+
+// Packed codes of four values from the IEEE quotient x / s.
+__device__ __forceinline__ uint32_t quant4_exact(f32x4 x, float s) {
+#pragma clang fp contract(off)
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float q = __builtin_rintf(x[k] / s);
+        q = __builtin_fminf(__builtin_fmaxf(q, -127.0f), 127.0f);
+        w |= (uint32_t(static_cast<int32_t>(q)) & 0xFFu) << (8 * k);
+    }
+    return w;
+}
+
+__device__ __forceinline__ uint32_t absmax4(uint32_t acc, f32x4 x, int64_t valid) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        if (k < valid) acc = std::max(acc, mag_bits(x[k]));
+    return acc;
 }
 
 // ---------------------------------------------------------- row teams
@@ -94,7 +151,13 @@ struct Team {
     int log2w;
     int chunks;
     bool vec;        // full chunks take vector accesses
+    bool full;       // every chunk of this lane is a full vector chunk
 };
+
+// Offset within the row of chunk c's first element.
+__device__ __forceinline__ int64_t chunk_off(const Team &t, int c) {
+    return 4 * (int64_t(c) * t.width + t.lane);
+}
 
 template <int kThreads>
 __device__ __forceinline__ Team team_of(const Q8Rec &r, uint32_t local_block) {
@@ -107,12 +170,17 @@ __device__ __forceinline__ Team team_of(const Q8Rec &r, uint32_t local_block) {
     t.len = t.row < r.rows ? std::min<int64_t>(r.row_len, r.numel - t.first) : 0;
     t.chunks = r.chunks;
     t.vec = (r.flags & kQVector) != 0;
+    t.full = t.vec && t.len > 0 && chunk_off(t, t.chunks - 1) + 4 <= t.len;
     return t;
 }
 
-// Offset within the row of chunk c's first element.
-__device__ __forceinline__ int64_t chunk_off(const Team &t, int c) {
-    return 4 * (int64_t(c) * t.width + t.lane);
+// Elements of chunk c inside the row (0 .. 4).
+template <bool kFull>
+__device__ __forceinline__ int64_t valid_of(const Team &t, int c) {
+    if (c >= t.chunks) return 0;
+    if constexpr (kFull) return 4;
+    const int64_t rem = t.len - chunk_off(t, c);
+    return rem <= 0 ? 0 : (rem < 4 ? rem : 4);
 }
 
 // Max over the team of two unsigned values.  Every lane of the workgroup
@@ -143,44 +211,46 @@ __device__ __forceinline__ void team_max2(const Team &t, uint32_t &a, uint32_t &
     }
 }
 
-// -------------------------------------------------------------- loads
+// -------------------------------------------------------------- access
 
-// Four consecutive elements of one chunk.  Elements past the row's end read
-// as zero (they are never stored and never enter an absmax).
-__device__ __forceinline__ f32x4 load_f32(uint64_t base, int64_t e, bool full, bool vec,
-                                          int64_t valid) {
-    if (full && vec) return ld_nt<f32x4>(base, e >> 2);
+// Four consecutive elements of one chunk: a vector access, or `valid`
+// element accesses (elements past the row's end read as zero; they are never
+// stored and never enter an absmax).
+__device__ __forceinline__ f32x4 load_f32(uint64_t base, int64_t e, bool vector, int64_t valid) {
+    if (vector) return ld_nt<f32x4>(base, e >> 2);
     f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int k = 0; k < 4; ++k)
         if (k < valid) x[k] = as_global<gfloat>(base)[e + k];
     return x;
 }
 
-__device__ __forceinline__ f32x4 load_bf16(uint64_t base, int64_t e, bool full, bool vec,
-                                           int64_t valid) {
-    if (full && vec) {
-        const u32x2 p = ld_nt<u32x2>(base, e >> 2);
-        return f32x4{bf16_lo(p.x), bf16_hi(p.x), bf16_lo(p.y), bf16_hi(p.y)};
-    }
-    f32x4 x = {0.0f, 0.0f, 0.0f, 0.0f};
+// bf16 bits of four elements, packed two per word.
+__device__ __forceinline__ u32x2 load_bf16_bits(uint64_t base, int64_t e, bool vector,
+                                                int64_t valid) {
+    if (vector) return ld_nt<u32x2>(base, e >> 2);
+    uint32_t h[4] = {0, 0, 0, 0};
     for (int k = 0; k < 4; ++k)
-        if (k < valid) x[k] = bf16_one(as_global<gu16>(base)[e + k]);
-    return x;
+        if (k < valid) h[k] = as_global<gu16>(base)[e + k];
+    return u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+}
+
+__device__ __forceinline__ f32x4 widen_bf16(u32x2 p) {
+    return f32x4{bf16_lo(p.x), bf16_hi(p.x), bf16_lo(p.y), bf16_hi(p.y)};
 }
 
 // Four codes, packed as in memory (byte k = element k).
-__device__ __forceinline__ uint32_t load_codes(uint64_t base, int64_t e, bool full, bool vec,
+__device__ __forceinline__ uint32_t load_codes(uint64_t base, int64_t e, bool vector,
                                                int64_t valid) {
-    if (full && vec) return ld_nt<uint32_t>(base, e >> 2);
+    if (vector) return ld_nt<uint32_t>(base, e >> 2);
     uint32_t w = 0;
     for (int k = 0; k < 4; ++k)
         if (k < valid) w |= (uint32_t(uint8_t(as_global<gi8>(base)[e + k])) << (8 * k));
     return w;
 }
 
-__device__ __forceinline__ void store_f32(uint64_t base, int64_t e, bool full, bool vec,
-                                          int64_t valid, f32x4 x) {
-    if (full && vec) {
+__device__ __forceinline__ void store_f32(uint64_t base, int64_t e, bool vector, int64_t valid,
+                                          f32x4 x) {
+    if (vector) {
         st_nt<f32x4>(base, e >> 2, x);
         return;
     }
@@ -188,9 +258,9 @@ __device__ __forceinline__ void store_f32(uint64_t base, int64_t e, bool full, b
         if (k < valid) as_global<gfloat>(base)[e + k] = x[k];
 }
 
-__device__ __forceinline__ void store_bf16(uint64_t base, int64_t e, bool full, bool vec,
-                                           int64_t valid, f32x4 x) {
-    if (full && vec) {
+__device__ __forceinline__ void store_bf16(uint64_t base, int64_t e, bool vector, int64_t valid,
+                                           f32x4 x) {
+    if (vector) {
         st_nt<u32x2>(base, e >> 2, u32x2{to_bf16_pair(x.x, x.y), to_bf16_pair(x.z, x.w)});
         return;
     }
@@ -198,9 +268,9 @@ __device__ __forceinline__ void store_bf16(uint64_t base, int64_t e, bool full, 
         if (k < valid) as_global<gu16>(base)[e + k] = to_bf16_one(x[k]);
 }
 
-__device__ __forceinline__ void store_codes(uint64_t base, int64_t e, bool full, bool vec,
-                                            int64_t valid, uint32_t w) {
-    if (full && vec) {
+__device__ __forceinline__ void store_codes(uint64_t base, int64_t e, bool vector, int64_t valid,
+                                            uint32_t w) {
+    if (vector) {
         st_nt<uint32_t>(base, e >> 2, w);
         return;
     }
@@ -208,16 +278,33 @@ __device__ __forceinline__ void store_codes(uint64_t base, int64_t e, bool full,
         if (k < valid) as_global<gi8>(base)[e + k] = int8_t(w >> (8 * k));
 }
 
-// Codes of four values against a row scale (all zero if it is not usable).
-__device__ __forceinline__ uint32_t quant4(f32x4 x, float scale, bool ok) {
-    if (!ok) return 0u;
-    return pack4(quant(x.x, scale), quant(x.y, scale), quant(x.z, scale), quant(x.w, scale));
-}
-
-__device__ __forceinline__ uint32_t absmax4(uint32_t acc, f32x4 x, int64_t valid) {
-    for (int k = 0; k < 4; ++k)
-        if (k < valid) acc = std::max(acc, mag_bits(x[k]));
-    return acc;
+// Quantize this lane's chunks of one row and store the codes.
+template <int kC, bool kFull>
+__device__ __forceinline__ void quantize_store(const Team &t, uint64_t codes, const QuantRow &q,
+                                               const f32x4 (&x)[kC]) {
+    uint32_t w[kC];
+#pragma unroll
+    for (int ci = 0; ci < kC; ++ci) w[ci] = 0;
+    if (q.ok) {
+        float near = 1.0f;
+        if (q.fast) {
+#pragma unroll
+            for (int ci = 0; ci < kC; ++ci)
+                if (valid_of<kFull>(t, ci) > 0) w[ci] = quant4_fast(x[ci], q.r, near);
+        }
+        if (!q.fast || near < kNearHalf) {
+#pragma unroll
+            for (int ci = 0; ci < kC; ++ci)
+                if (valid_of<kFull>(t, ci) > 0) w[ci] = quant4_exact(x[ci], q.s);
+        }
+    }
+#pragma unroll
+    for (int ci = 0; ci < kC; ++ci) {
+        const int64_t valid = valid_of<kFull>(t, ci);
+        if (valid <= 0) continue;
+        store_codes(codes, t.first + chunk_off(t, ci), kFull || (t.vec && valid == 4), valid,
+                    w[ci]);
+    }
 }
 
 // ------------------------------------------------------------- AdamW
@@ -227,85 +314,64 @@ __device__ __forceinline__ uint32_t absmax4(uint32_t acc, f32x4 x, int64_t valid
 //   {master, m, m_scale, v, v_scale, grad, grad_scale, weight, orig, delta}
 template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads>
 struct AdamwRows {
-    static constexpr int kMaxC = kQChunks;
+    static constexpr int kC = kThreads == kQBlockWide ? kQWideChunks : kQStepChunks;
     AdamwConsts c;
 
-    __device__ __forceinline__ void operator()(const Q8Rec &r, uint32_t local_block) const {
-        const uint64_t master = r.p[0], m = r.p[1], m_scale = r.p[2], v = r.p[3],
-                       v_scale = r.p[4], grad = r.p[5], grad_scale = r.p[6], weight = r.p[7],
-                       orig = r.p[8], delta = r.p[9];
-        const Team t = team_of<kThreads>(r, local_block);
-        const bool has_row = t.len > 0;
-        const bool has_delta = kDelta && delta != 0;   // per segment within a delta launch
+    struct Row {
+        uint64_t master, m, m_scale, v, v_scale, grad, grad_scale, weight, orig, delta;
+        bool has_delta;
+        float ms, vs, gs;    // old row scales (int8 arrays only)
+    };
 
-        float ms_old = 0.0f, vs_old = 0.0f, gs = 0.0f;
-        if (has_row) {
-            if constexpr (kMomQ8) {
-                ms_old = as_global<gfloat>(m_scale)[t.row];
-                vs_old = as_global<gfloat>(v_scale)[t.row];
-            }
-            if constexpr (kGrad == kQGradQ8) gs = as_global<gfloat>(grad_scale)[t.row];
-        }
-
-        // ---- loads of every chunk
-        f32x4 w4[kMaxC], g4[kMaxC], mf[kMaxC], vf[kMaxC];
-        uint32_t mc[kMaxC], vc[kMaxC], gc[kMaxC];
-        u32x2 o2[kMaxC];
+    // Loads, the fp32 step and the stores of master, weight, delta (and of
+    // fp32 moments); int8 moments are left in mf/vf with their absmax bits.
+    template <bool kFull>
+    __device__ __forceinline__ void step_lane(const Team &t, const Row &R, f32x4 (&mf)[kC],
+                                              f32x4 (&vf)[kC], uint32_t &am,
+                                              uint32_t &av) const {
+        f32x4 w4[kC], g4[kC];
+        uint32_t mc[kC], vc[kC], gc[kC];
+        u32x2 gb[kC], o2[kC];
 #pragma unroll
-        for (int ci = 0; ci < kMaxC; ++ci) {
-            const int64_t off = chunk_off(t, ci);
-            const int64_t valid = (ci < t.chunks) ? std::min<int64_t>(4, t.len - off) : 0;
+        for (int ci = 0; ci < kC; ++ci) {
+            const int64_t valid = valid_of<kFull>(t, ci);
             if (valid <= 0) continue;
-            const int64_t e = t.first + off;
-            const bool full = valid == 4;
-            w4[ci] = load_f32(master, e, full, t.vec, valid);
+            const int64_t e = t.first + chunk_off(t, ci);
+            const bool vector = kFull || (t.vec && valid == 4);
+            w4[ci] = load_f32(R.master, e, vector, valid);
             if constexpr (kMomQ8) {
-                mc[ci] = load_codes(m, e, full, t.vec, valid);
-                vc[ci] = load_codes(v, e, full, t.vec, valid);
+                mc[ci] = load_codes(R.m, e, vector, valid);
+                vc[ci] = load_codes(R.v, e, vector, valid);
             } else {
-                mf[ci] = load_f32(m, e, full, t.vec, valid);
-                vf[ci] = load_f32(v, e, full, t.vec, valid);
+                mf[ci] = load_f32(R.m, e, vector, valid);
+                vf[ci] = load_f32(R.v, e, vector, valid);
             }
-            if constexpr (kGrad == kQGradBf16) g4[ci] = load_bf16(grad, e, full, t.vec, valid);
-            if constexpr (kGrad == kQGradF32) g4[ci] = load_f32(grad, e, full, t.vec, valid);
-            if constexpr (kGrad == kQGradQ8) gc[ci] = load_codes(grad, e, full, t.vec, valid);
-            if (has_delta) {
-                if (full && t.vec) {
-                    o2[ci] = ld_nt<u32x2>(orig, e >> 2);
-                } else {
-                    uint32_t lo = 0, hi = 0;
-                    for (int k = 0; k < 4; ++k) {
-                        if (k >= valid) continue;
-                        const uint32_t b = as_global<gu16>(orig)[e + k];
-                        if (k < 2) lo |= b << (16 * k);
-                        else hi |= b << (16 * (k - 2));
-                    }
-                    o2[ci] = u32x2{lo, hi};
-                }
-            }
+            if constexpr (kGrad == kQGradBf16) gb[ci] = load_bf16_bits(R.grad, e, vector, valid);
+            if constexpr (kGrad == kQGradF32) g4[ci] = load_f32(R.grad, e, vector, valid);
+            if constexpr (kGrad == kQGradQ8) gc[ci] = load_codes(R.grad, e, vector, valid);
+            if (R.has_delta) o2[ci] = load_bf16_bits(R.orig, e, vector, valid);
         }
 
-        // ---- the fp32 step; master, weight and delta go out at once
-        uint32_t am = 0, av = 0;
 #pragma unroll
-        for (int ci = 0; ci < kMaxC; ++ci) {
-            const int64_t off = chunk_off(t, ci);
-            const int64_t valid = (ci < t.chunks) ? std::min<int64_t>(4, t.len - off) : 0;
+        for (int ci = 0; ci < kC; ++ci) {
+            const int64_t valid = valid_of<kFull>(t, ci);
             if (valid <= 0) continue;
-            const int64_t e = t.first + off;
-            const bool full = valid == 4;
+            const int64_t e = t.first + chunk_off(t, ci);
+            const bool vector = kFull || (t.vec && valid == 4);
             f32x4 w = w4[ci], mm, vv, g;
             if constexpr (kMomQ8) {
                 for (int k = 0; k < 4; ++k) {
-                    mm[k] = dequant(code_at(mc[ci], k), ms_old);
-                    vv[k] = dequant(code_at(vc[ci], k), vs_old);
+                    mm[k] = dequant(code_at(mc[ci], k), R.ms);
+                    vv[k] = dequant(code_at(vc[ci], k), R.vs);
                 }
             } else {
                 mm = mf[ci];
                 vv = vf[ci];
             }
             if constexpr (kGrad == kQGradQ8) {
-                for (int k = 0; k < 4; ++k) g[k] = dequant(code_at(gc[ci], k), gs);
+                for (int k = 0; k < 4; ++k) g[k] = dequant(code_at(gc[ci], k), R.gs);
+            } else if constexpr (kGrad == kQGradBf16) {
+                g = widen_bf16(gb[ci]);
             } else {
                 g = g4[ci];
             }
@@ -317,14 +383,13 @@ struct AdamwRows {
                 mm[k] = mk;
                 vv[k] = vk;
             }
-            store_f32(master, e, full, t.vec, valid, w);
-            store_bf16(weight, e, full, t.vec, valid, w);
-            if (has_delta) {
+            store_f32(R.master, e, vector, valid, w);
+            store_bf16(R.weight, e, vector, valid, w);
+            if (R.has_delta) {
 #pragma clang fp contract(off)
-                const u32x2 o = o2[ci];
-                const f32x4 d = {w.x - bf16_lo(o.x), w.y - bf16_hi(o.x), w.z - bf16_lo(o.y),
-                                 w.w - bf16_hi(o.y)};
-                store_f32(delta, e, full, t.vec, valid, d);
+                const f32x4 o = widen_bf16(o2[ci]);
+                const f32x4 d = {w.x - o.x, w.y - o.y, w.z - o.z, w.w - o.w};
+                store_f32(R.delta, e, vector, valid, d);
             }
             if constexpr (kMomQ8) {
                 am = absmax4(am, mm, valid);
@@ -332,30 +397,47 @@ struct AdamwRows {
                 mf[ci] = mm;
                 vf[ci] = vv;
             } else {
-                store_f32(m, e, full, t.vec, valid, mm);
-                store_f32(v, e, full, t.vec, valid, vv);
+                store_f32(R.m, e, vector, valid, mm);
+                store_f32(R.v, e, vector, valid, vv);
             }
         }
+    }
+
+    __device__ __forceinline__ void operator()(const Q8Rec &r, uint32_t local_block) const {
+        Row R{r.p[0], r.p[1], r.p[2], r.p[3], r.p[4], r.p[5], r.p[6], r.p[7], r.p[8], r.p[9],
+              kDelta && r.p[9] != 0, 0.0f, 0.0f, 0.0f};
+        const Team t = team_of<kThreads>(r, local_block);
+        const bool has_row = t.len > 0;
+        if (has_row) {
+            if constexpr (kMomQ8) {
+                R.ms = as_global<gfloat>(R.m_scale)[t.row];
+                R.vs = as_global<gfloat>(R.v_scale)[t.row];
+            }
+            if constexpr (kGrad == kQGradQ8) R.gs = as_global<gfloat>(R.grad_scale)[t.row];
+        }
+
+        f32x4 mf[kC], vf[kC];
+        uint32_t am = 0, av = 0;
+        if (t.full)
+            step_lane<true>(t, R, mf, vf, am, av);
+        else
+            step_lane<false>(t, R, mf, vf, am, av);
         if constexpr (!kMomQ8) return;
 
-        // ---- requantize the moments against the new row scales
+        // requantize the moments against the new row scales
         team_max2<kThreads>(t, am, av);
         if (!has_row) return;
-        const float ms = scale_of(am), vs = scale_of(av);
-        const bool m_ok = usable(ms), v_ok = usable(vs);
-#pragma unroll
-        for (int ci = 0; ci < kMaxC; ++ci) {
-            const int64_t off = chunk_off(t, ci);
-            const int64_t valid = (ci < t.chunks) ? std::min<int64_t>(4, t.len - off) : 0;
-            if (valid <= 0) continue;
-            const int64_t e = t.first + off;
-            const bool full = valid == 4;
-            store_codes(m, e, full, t.vec, valid, quant4(mf[ci], ms, m_ok));
-            store_codes(v, e, full, t.vec, valid, quant4(vf[ci], vs, v_ok));
+        const QuantRow qm = quant_row(am), qv = quant_row(av);
+        if (t.full) {
+            quantize_store<kC, true>(t, R.m, qm, mf);
+            quantize_store<kC, true>(t, R.v, qv, vf);
+        } else {
+            quantize_store<kC, false>(t, R.m, qm, mf);
+            quantize_store<kC, false>(t, R.v, qv, vf);
         }
         if (t.lane == 0) {
-            as_global<gfloat>(m_scale)[t.row] = ms;
-            as_global<gfloat>(v_scale)[t.row] = vs;
+            as_global<gfloat>(R.m_scale)[t.row] = qm.s;
+            as_global<gfloat>(R.v_scale)[t.row] = qv.s;
         }
     }
 };
@@ -377,67 +459,77 @@ enum RowOp : int { kAccumAdd = 0, kAccumOverwrite = 1, kQuantize = 2, kDequantiz
 
 template <RowOp kOp, int kThreads>
 struct CodeRows {
-    static constexpr int kMaxC = kQChunks;
-    __device__ __forceinline__ void operator()(const Q8Rec &r, uint32_t local_block) const {
-        const Team t = team_of<kThreads>(r, local_block);
-        const bool has_row = t.len > 0;
-        // pointers: accumulation {codes, scale, grad}; conversions {x, codes, scale}
-        const uint64_t codes = (kOp == kAccumAdd || kOp == kAccumOverwrite) ? r.p[0] : r.p[1];
-        const uint64_t scale = (kOp == kAccumAdd || kOp == kAccumOverwrite) ? r.p[1] : r.p[2];
-        const uint64_t src = (kOp == kAccumAdd || kOp == kAccumOverwrite) ? r.p[2] : r.p[0];
+    static constexpr int kC = kThreads == kQBlockWide ? kQWideChunks : kQCodeChunks;
+    static constexpr bool kAccum = kOp == kAccumAdd || kOp == kAccumOverwrite;
+    static constexpr bool kReadsCodes = kOp == kAccumAdd || kOp == kDequantize;
 
-        float s_old = 0.0f;
-        if (has_row && (kOp == kAccumAdd || kOp == kDequantize))
-            s_old = as_global<gfloat>(scale)[t.row];
-
-        f32x4 x[kMaxC];
-        uint32_t cw[kMaxC];
+    // The lane's new values (and their absmax), or for kDequantize the stores.
+    template <bool kFull>
+    __device__ __forceinline__ void values_lane(const Team &t, uint64_t codes, uint64_t src,
+                                                float s_old, f32x4 (&x)[kC],
+                                                uint32_t &amax) const {
+        uint32_t cw[kC];
+        u32x2 gb[kC];
 #pragma unroll
-        for (int ci = 0; ci < kMaxC; ++ci) {
-            const int64_t off = chunk_off(t, ci);
-            const int64_t valid = (ci < t.chunks) ? std::min<int64_t>(4, t.len - off) : 0;
+        for (int ci = 0; ci < kC; ++ci) {
+            x[ci] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int64_t valid = valid_of<kFull>(t, ci);
             if (valid <= 0) continue;
-            const int64_t e = t.first + off;
-            const bool full = valid == 4;
-            if constexpr (kOp == kAccumAdd || kOp == kDequantize)
-                cw[ci] = load_codes(codes, e, full, t.vec, valid);
-            if constexpr (kOp == kAccumAdd || kOp == kAccumOverwrite)
-                x[ci] = load_bf16(src, e, full, t.vec, valid);
-            if constexpr (kOp == kQuantize) x[ci] = load_f32(src, e, full, t.vec, valid);
+            const int64_t e = t.first + chunk_off(t, ci);
+            const bool vector = kFull || (t.vec && valid == 4);
+            if constexpr (kReadsCodes) cw[ci] = load_codes(codes, e, vector, valid);
+            if constexpr (kAccum) gb[ci] = load_bf16_bits(src, e, vector, valid);
+            if constexpr (kOp == kQuantize) x[ci] = load_f32(src, e, vector, valid);
         }
-
-        uint32_t amax = 0, unused = 0;
 #pragma unroll
-        for (int ci = 0; ci < kMaxC; ++ci) {
-            const int64_t off = chunk_off(t, ci);
-            const int64_t valid = (ci < t.chunks) ? std::min<int64_t>(4, t.len - off) : 0;
+        for (int ci = 0; ci < kC; ++ci) {
+            const int64_t valid = valid_of<kFull>(t, ci);
             if (valid <= 0) continue;
-            if constexpr (kOp == kAccumAdd) {
+            if constexpr (kAccum) {
+                const f32x4 g = widen_bf16(gb[ci]);
                 for (int k = 0; k < 4; ++k)
-                    x[ci][k] = accum_elem(dequant(code_at(cw[ci], k), s_old), x[ci][k], false);
+                    x[ci][k] = kOp == kAccumAdd
+                                   ? accum_elem(dequant(code_at(cw[ci], k), s_old), g[k], false)
+                                   : g[k];
             }
             if constexpr (kOp == kDequantize) {
                 f32x4 d;
                 for (int k = 0; k < 4; ++k) d[k] = dequant(code_at(cw[ci], k), s_old);
-                store_f32(src, t.first + off, valid == 4, t.vec, valid, d);
+                const int64_t e = t.first + chunk_off(t, ci);
+                store_f32(src, e, kFull || (t.vec && valid == 4), valid, d);
             } else {
                 amax = absmax4(amax, x[ci], valid);
             }
         }
+    }
+
+    __device__ __forceinline__ void operator()(const Q8Rec &r, uint32_t local_block) const {
+        const Team t = team_of<kThreads>(r, local_block);
+        const bool has_row = t.len > 0;
+        // pointers: accumulation {codes, scale, grad}; conversions {x, codes, scale}
+        const uint64_t codes = kAccum ? r.p[0] : r.p[1];
+        const uint64_t scale = kAccum ? r.p[1] : r.p[2];
+        const uint64_t src = kAccum ? r.p[2] : r.p[0];
+
+        float s_old = 0.0f;
+        if (has_row && kReadsCodes) s_old = as_global<gfloat>(scale)[t.row];
+
+        f32x4 x[kC];
+        uint32_t amax = 0, unused = 0;
+        if (t.full)
+            values_lane<true>(t, codes, src, s_old, x, amax);
+        else
+            values_lane<false>(t, codes, src, s_old, x, amax);
         if constexpr (kOp == kDequantize) return;
 
         team_max2<kThreads>(t, amax, unused);
         if (!has_row) return;
-        const float s = scale_of(amax);
-        const bool ok = usable(s);
-#pragma unroll
-        for (int ci = 0; ci < kMaxC; ++ci) {
-            const int64_t off = chunk_off(t, ci);
-            const int64_t valid = (ci < t.chunks) ? std::min<int64_t>(4, t.len - off) : 0;
-            if (valid <= 0) continue;
-            store_codes(codes, t.first + off, valid == 4, t.vec, valid, quant4(x[ci], s, ok));
-        }
-        if (t.lane == 0) as_global<gfloat>(scale)[t.row] = s;
+        const QuantRow q = quant_row(amax);
+        if (t.full)
+            quantize_store<kC, true>(t, codes, q, x);
+        else
+            quantize_store<kC, false>(t, codes, q, x);
+        if (t.lane == 0) as_global<gfloat>(scale)[t.row] = q.s;
     }
 };
 

@@ -22,38 +22,42 @@ static_assert(kQMaxRow == LEMA_Q8_MAX_ROW, "row limit of the header and the kern
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Team width (log2), chunks per lane and workgroup size for rows of row_len
-// elements: the narrowest team whose lanes hold at most kQChunks chunks, in a
-// kQBlock-lane workgroup when such a team fits there, else a wide one.
-void size_team(int64_t row_len, int32_t *log2w, int32_t *chunks, int *block) {
+// elements: the narrowest team whose lanes hold at most `chunks_max` chunks
+// in a kQBlock-lane workgroup, else a team of a kQBlockWide-lane workgroup
+// with at most kQWideChunks per lane.
+struct Shape {
+    int32_t log2w, chunks;
+    int block;
+};
+
+Shape shape_for(int64_t row_len, int chunks_max) {
     const int64_t need = ceil_div(row_len, 4);
     int lg = 0;
-    while (ceil_div(need, int64_t(1) << lg) > kQChunks) ++lg;
-    *log2w = lg;
-    *chunks = static_cast<int32_t>(ceil_div(need, int64_t(1) << lg));
-    *block = (1 << lg) <= kQBlock ? kQBlock : kQBlockWide;
+    while ((1 << lg) < kQBlock && ceil_div(need, int64_t(1) << lg) > chunks_max) ++lg;
+    if (ceil_div(need, int64_t(1) << lg) <= chunks_max)
+        return {lg, static_cast<int32_t>(ceil_div(need, int64_t(1) << lg)), kQBlock};
+    lg = 0;
+    while (ceil_div(need, int64_t(1) << lg) > kQWideChunks) ++lg;
+    return {lg, static_cast<int32_t>(ceil_div(need, int64_t(1) << lg)), kQBlockWide};
 }
 
-int block_of(const Q8Rec &r) {
-    int32_t lg, chunks;
-    int block;
-    size_team(r.row_len, &lg, &chunks, &block);
-    return block;
-}
+int block_of(const Q8Rec &r, int chunks_max) { return shape_for(r.row_len, chunks_max).block; }
 
-uint64_t blocks_of(const Q8Rec &r) {
-    const int64_t rows_per_block = block_of(r) >> r.team_log2;
+uint64_t blocks_of(const Q8Rec &r, int chunks_max) {
+    const int64_t rows_per_block = block_of(r, chunks_max) >> r.team_log2;
     return static_cast<uint64_t>(ceil_div(r.rows, rows_per_block));
 }
 
 bool row_len_ok(int64_t row_len) { return row_len >= 1 && row_len <= kQMaxRow; }
 
-Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok) {
+Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok, int chunks_max) {
     Q8Rec r{};
     r.numel = numel;
     r.row_len = row_len;
     r.rows = ceil_div(numel, row_len);
-    int block;
-    size_team(row_len, &r.team_log2, &r.chunks, &block);
+    const Shape sh = shape_for(row_len, chunks_max);
+    r.team_log2 = sh.log2w;
+    r.chunks = sh.chunks;
     r.flags = (vector_ok && row_len % 4 == 0) ? kQVector : 0;
     return r;
 }
@@ -62,12 +66,12 @@ uintptr_t bits(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
 // Launch `recs` in at most two groups, one per workgroup size.
 template <class LaunchFn>
-lema_status launch_groups(const std::vector<Q8Rec> &recs, hipStream_t stream,
+lema_status launch_groups(const std::vector<Q8Rec> &recs, int chunks_max, hipStream_t stream,
                           const LaunchFn &launch) {
     for (int block : {kQBlock, kQBlockWide}) {
         std::vector<Q8Rec> sel;
         for (const Q8Rec &r : recs)
-            if (block_of(r) == block) sel.push_back(r);
+            if (block_of(r, chunks_max) == block) sel.push_back(r);
         if (sel.empty()) continue;
         const int n = static_cast<int>(sel.size());
         std::vector<unsigned char> bytes(q8_table_bytes(n), 0);
@@ -75,7 +79,7 @@ lema_status launch_groups(const std::vector<Q8Rec> &recs, hipStream_t stream,
         uint64_t blocks = 0;
         for (int i = 0; i < n; ++i) {
             begin[i] = static_cast<uint32_t>(blocks);
-            blocks += blocks_of(sel[i]);
+            blocks += blocks_of(sel[i], chunks_max);
             if (blocks > 0xFFF00000ull) return LEMA_ERR_SIZE;
         }
         begin[n] = static_cast<uint32_t>(blocks);
@@ -152,7 +156,7 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
                              (gd == LEMA_GRAD_Q8 ? bits(s.grad) : 0);
         const bool vec = (v16 & 15) == 0 && (b16 & 7) == 0 && (v4 & 3) == 0;
 
-        Q8Rec r = make_rec(s.numel, s.row_len, vec);
+        Q8Rec r = make_rec(s.numel, s.row_len, vec, kQStepChunks);
         add_span(spans, s.master, s.numel, 4, true);
         add_span(spans, s.exp_avg, s.numel, mom_size, true);
         add_span(spans, s.exp_avg_sq, s.numel, mom_size, true);
@@ -180,7 +184,8 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
     const AdamwConsts c = derive_consts(args);
     const QGrad qg = gd == LEMA_GRAD_BF16 ? kQGradBf16 : gd == LEMA_GRAD_FP32 ? kQGradF32 : kQGradQ8;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks, int block) {
+    return launch_groups(recs, kQStepChunks, hs, [&](const void *table, int n, uint32_t blocks,
+                                                     int block) {
         return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, c, hs);
     });
 }
@@ -199,7 +204,7 @@ lema_status lema_grad_accum_q8(const lema_accum_q8_seg *segs, int32_t nseg, int3
         if (!s.acc || !s.acc_scale || !s.grad_bf16) return LEMA_ERR_NULL;
         if ((bits(s.acc_scale) & 3) || (bits(s.grad_bf16) & 1)) return LEMA_ERR_ALIGN;
         const bool vec = (bits(s.acc) & 3) == 0 && (bits(s.grad_bf16) & 7) == 0;
-        Q8Rec r = make_rec(s.numel, s.row_len, vec);
+        Q8Rec r = make_rec(s.numel, s.row_len, vec, kQCodeChunks);
         add_span(spans, s.acc, s.numel, 1, true);
         add_span(spans, s.acc_scale, r.rows, 4, true);
         add_span(spans, s.grad_bf16, s.numel, 2, false);
@@ -211,7 +216,8 @@ lema_status lema_grad_accum_q8(const lema_accum_q8_seg *segs, int32_t nseg, int3
     if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
     if (recs.empty()) return LEMA_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks, int block) {
+    return launch_groups(recs, kQCodeChunks, hs, [&](const void *table, int n, uint32_t blocks,
+                                                     int block) {
         return launch_accum_q8(table, n, blocks, overwrite != 0, block, hs);
     });
 }
@@ -230,7 +236,7 @@ static lema_status convert_rows(const lema_q8_tensor *t, int32_t n, bool dequant
         if (!s.x || !s.codes || !s.scale) return LEMA_ERR_NULL;
         if ((bits(s.x) | bits(s.scale)) & 3) return LEMA_ERR_ALIGN;
         const bool vec = (bits(s.x) & 15) == 0 && (bits(s.codes) & 3) == 0;
-        Q8Rec r = make_rec(s.numel, s.row_len, vec);
+        Q8Rec r = make_rec(s.numel, s.row_len, vec, kQCodeChunks);
         add_span(spans, s.x, s.numel, 4, dequantize);
         add_span(spans, s.codes, s.numel, 1, !dequantize);
         add_span(spans, s.scale, r.rows, 4, !dequantize);
@@ -242,7 +248,8 @@ static lema_status convert_rows(const lema_q8_tensor *t, int32_t n, bool dequant
     if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
     if (recs.empty()) return LEMA_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    return launch_groups(recs, hs, [&](const void *table, int nrec, uint32_t blocks, int block) {
+    return launch_groups(recs, kQCodeChunks, hs, [&](const void *table, int nrec,
+                                                     uint32_t blocks, int block) {
         return launch_quantize_q8(table, nrec, blocks, dequantize, block, hs);
     });
 }

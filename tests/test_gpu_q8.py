@@ -162,6 +162,30 @@ def test_quantize_dequantize_rows(L, row_len, offset):
     compare_f32(to_np(back), oracle.dequantize_rows(rq, rs, row_len), "dequantized")
 
 
+def test_quantize_near_half_integers(L):
+    """Rows whose values divide by the row scale to half-integers or a few
+    ulps off them (where the kernels fall back from x*(1/s) to the IEEE
+    division), over scales from 2^-120 to 2^120."""
+    rng = np.random.default_rng(77)
+    rows = []
+    for e in range(-120, 121, 8):
+        a = np.float32(rng.uniform(1, 2) * 2.0 ** e)
+        s = np.float32(a / np.float32(127))
+        k = rng.integers(-127, 127, 256).astype(np.float64) + 0.5
+        j = rng.integers(-6, 7, 256) * 2.0 ** -19
+        x = ((k + j) * float(s)).astype(np.float32)
+        x = np.where(np.abs(x) <= a, x, np.float32(0))
+        x[0] = a
+        x[1:3] = np.nextafter(x[5:7], np.float32(np.inf))
+        rows.append(x)
+    x = np.concatenate(rows)
+    q = L.Q8.empty(x.size, 256)
+    L.quantize_rows([(up(x), q)])
+    rq, rs = oracle.quantize_rows(x, 256)
+    compare_codes(q.codes, rq, "codes")
+    compare_f32(to_np(q.scale), rs, "scale")
+
+
 # ------------------------------------------------------------------ step
 
 @pytest.mark.parametrize("grad", ["bf16", "fp32", "q8"])
