@@ -38,6 +38,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "AdamW params updated/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 COUNTERS = os.path.join(ROOT, "profiles", "adamw_counters.json")
 KERNEL_SOURCES = ["optimizer_step_lema_amd/csrc/lema_kernels.hip",
+                  "optimizer_step_lema_amd/csrc/lema_q8.hip",
+                  "optimizer_step_lema_amd/csrc/lema_device.h",
                   "optimizer_step_lema_amd/csrc/lema_internal.h",
                   "optimizer_step_lema_amd/build.py"]
 

@@ -40,6 +40,14 @@ lema_status lema_measure_copy(const void *src, void *dst, size_t bytes, void *st
 lema_status lema_probe_fp32(const float *a, const float *b, float *quot, float *root,
                             uint16_t *bf16, int64_t n, void *stream);
 
+/*
+ * Counters of the current device's launch-table cache since the library was
+ * loaded: out[0] calls that found their table cached, out[1] tables uploaded,
+ * out[2] uploads that had to wait for a pending launch, out[3] cached
+ * entries.  Errors: LEMA_ERR_NULL, LEMA_ERR_HIP.
+ */
+lema_status lema_table_cache_stats(int64_t out[4]);
+
 /* Compute units of the current device and the elements one workgroup takes
  * per tile in the AdamW and accumulation kernels. */
 lema_status lema_device_info(int32_t *compute_units, int32_t *tile_elements);

@@ -10,4 +10,4 @@ from .api import (AccumPlan, AccumQ8Plan, AccumQ8Segment, AccumSegment, AdamwPla
                   AdamwQ8Plan, AdamwQ8Segment, AdamwSegment, MergeSegment, Q8, SlotPool,
                   adamw_constants, adamw_step, adamw_step_q8, dequantize_rows, device_info,
                   grad_accum, grad_accum_q8, measure_copy, merge_delta, pinned_empty, probe_fp32,
-                  quantize_rows)
+                  quantize_rows, table_cache_stats)

@@ -512,6 +512,13 @@ def probe_fp32(a: torch.Tensor, b: torch.Tensor, stream=None):
     return q, r, h
 
 
+def table_cache_stats() -> dict:
+    """Launch-table cache counters of the current device (since load)."""
+    out = (ctypes.c_int64 * 4)()
+    N.check(N.load().lema_table_cache_stats(out), "lema_table_cache_stats")
+    return {"hits": out[0], "uploads": out[1], "waits": out[2], "entries": out[3]}
+
+
 def device_info() -> dict:
     cus, tile = ctypes.c_int32(), ctypes.c_int32()
     N.check(N.load().lema_device_info(ctypes.byref(cus), ctypes.byref(tile)), "lema_device_info")

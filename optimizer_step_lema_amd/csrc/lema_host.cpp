@@ -11,6 +11,7 @@
 #include <cmath>
 #include <cstring>
 #include <functional>
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -141,20 +142,25 @@ lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kCacheEntries = 16;
+// Tables kept per device.  A training loop that calls the library for every
+// layer and micro-batch cycles through a few hundred distinct tables, and a
+// cache smaller than that cycle misses on every call; entries cost 32 KiB
+// (device table plus page-locked staging), so all of them are kept.
+constexpr size_t kMaxCacheEntries = 512;
 
 // A launch table kept on the device.  Tables are immutable once uploaded;
 // a call whose table is byte-identical to a cached one launches on it
 // without any copy (the usual case: the same tensors every step).
 struct TableEntry {
     std::vector<unsigned char> bytes;
+    uint64_t hash = 0;
     void *dev = nullptr;
     size_t dev_cap = 0;
     void *staging = nullptr;      // page-locked source of the upload
     size_t staging_cap = 0;
     hipEvent_t last_use = nullptr;
     hipStream_t last_stream = nullptr;
-    bool in_use = false;          // last_use has been recorded
+    bool recorded = false;        // last_use marks the entry's latest launch
     uint64_t stamp = 0;
 };
 
@@ -163,10 +169,18 @@ struct DeviceState {
     bool ready = false;
     int cu_count = 0;
     uint64_t clock = 0;
-    TableEntry entries[kCacheEntries];
+    std::vector<std::unique_ptr<TableEntry>> entries;
+    int64_t hits = 0, uploads = 0, waits = 0;
 };
 
 DeviceState g_devices[kMaxDevices];
+
+// FNV-1a over the table bytes: a cheap first test before comparing bytes.
+uint64_t table_hash(const std::vector<unsigned char> &bytes) {
+    uint64_t h = 1469598103934665603ull;
+    for (unsigned char c : bytes) h = (h ^ c) * 1099511628211ull;
+    return h;
+}
 
 lema_status device_state(DeviceState **out, int *device) {
     int dev = 0;
@@ -187,32 +201,49 @@ lema_status device_state(DeviceState **out, int *device) {
     return LEMA_OK;
 }
 
+// True when no launch on the entry's table is still pending.
+bool entry_idle(const TableEntry &t) {
+    return !t.recorded || hipEventQuery(t.last_use) == hipSuccess;
+}
+
 // Pick the cache entry for `bytes` (must hold d.mu).  On a hit nothing is
-// copied; on a miss the least recently used entry is reloaded once every
-// launch still reading it has finished.
+// copied.  On a miss a new entry is added while there are fewer than
+// kMaxCacheEntries; beyond that the least recently used entry whose launches
+// have finished is reloaded, and only if all are pending does the call wait
+// for the least recently used one.
 lema_status acquire_table(DeviceState &d, const std::vector<unsigned char> &bytes,
                           hipStream_t stream, TableEntry **out) {
     hipError_t e;
-    for (TableEntry &t : d.entries) {
-        if (t.in_use && t.bytes == bytes) {
-            if (t.last_stream != stream) {
+    const uint64_t h = table_hash(bytes);
+    for (auto &p : d.entries) {
+        TableEntry &t = *p;
+        if (!t.bytes.empty() && t.hash == h && t.bytes == bytes) {
+            if (t.recorded && t.last_stream != stream) {
                 // a later reload must wait for both streams' launches
                 e = hipStreamWaitEvent(stream, t.last_use, 0);
                 if (e != hipSuccess) return hip_failed(e);
             }
             *out = &t;
+            ++d.hits;
             return LEMA_OK;
         }
     }
+    ++d.uploads;
     TableEntry *victim = nullptr;
-    for (TableEntry &t : d.entries) {
-        if (!t.in_use) { victim = &t; break; }
-        if (!victim || t.stamp < victim->stamp) victim = &t;
+    if (d.entries.size() < kMaxCacheEntries) {
+        d.entries.push_back(std::make_unique<TableEntry>());
+        victim = d.entries.back().get();
     }
-    if (victim->in_use) {
+    if (!victim) {
+        for (auto &p : d.entries)
+            if (entry_idle(*p) && (!victim || p->stamp < victim->stamp)) victim = p.get();
+    }
+    if (!victim) {
+        for (auto &p : d.entries)
+            if (!victim || p->stamp < victim->stamp) victim = p.get();
+        ++d.waits;
         e = hipEventSynchronize(victim->last_use);
         if (e != hipSuccess) return hip_failed(e);
-        victim->in_use = false;
     }
     victim->bytes.clear();
     const size_t n = bytes.size();
@@ -242,6 +273,7 @@ lema_status acquire_table(DeviceState &d, const std::vector<unsigned char> &byte
     e = hipMemcpyAsync(victim->dev, victim->staging, n, hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return hip_failed(e);
     victim->bytes = bytes;
+    victim->hash = h;
     *out = victim;
     return LEMA_OK;
 }
@@ -250,7 +282,7 @@ lema_status release_table(DeviceState &d, TableEntry *t, hipStream_t stream) {
     hipError_t e = hipEventRecord(t->last_use, stream);
     if (e != hipSuccess) return hip_failed(e);
     t->last_stream = stream;
-    t->in_use = true;
+    t->recorded = true;
     t->stamp = ++d.clock;
     return LEMA_OK;
 }
@@ -532,6 +564,19 @@ lema_status lema_probe_fp32(const float *a, const float *b, float *quot, float *
     if (!a || !b || !quot || !root || !bf16) return LEMA_ERR_NULL;
     hipError_t e = launch_fp32_probe(a, b, quot, root, bf16, n, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? LEMA_OK : hip_failed(e);
+}
+
+lema_status lema_table_cache_stats(int64_t out[4]) {
+    if (out == nullptr) return LEMA_ERR_NULL;
+    DeviceState *d = nullptr;
+    lema_status st = device_state(&d, nullptr);
+    if (st != LEMA_OK) return st;
+    std::lock_guard<std::mutex> lock(d->mu);
+    out[0] = d->hits;
+    out[1] = d->uploads;
+    out[2] = d->waits;
+    out[3] = static_cast<int64_t>(d->entries.size());
+    return LEMA_OK;
 }
 
 lema_status lema_device_info(int32_t *compute_units, int32_t *tile_elements) {

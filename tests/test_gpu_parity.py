@@ -460,6 +460,29 @@ def test_table_cache_many_lists_and_streams(L):
         compare_bf16(to_np(s.weight)[touched[i]], wout[i][touched[i]], f"cache seg{i} weight")
 
 
+def test_table_cache_beyond_capacity(L):
+    """More distinct tables than the cache may hold (512): 600 back-to-back
+    calls on prefixes of one tensor, each its own table, with no host wait in
+    between, so that the cache both grows and, at its cap, reuses entries whose
+    launches have finished.  Results follow the oracle's sequence of steps."""
+    base, snaps = build_segments(L, [4096], 62)
+    b = base[0]
+    lengths = [4096 - j for j in range(600)]
+    for j, n in enumerate(lengths):
+        seg = L.AdamwSegment(b.master[:n], b.exp_avg[:n], b.exp_avg_sq[:n], b.grad[:n],
+                             b.weight[:n])
+        L.adamw_step([seg], step=j + 1, **HP)
+    torch.cuda.synchronize()
+    st = {k: snaps[0][k].copy() for k in ("master", "m", "v", "grad")}
+    for j, n in enumerate(lengths):
+        out = oracle_segment(st["master"][:n], st["m"][:n], st["v"][:n], st["grad"][:n],
+                             oracle_consts(HP, j + 1))
+        st["master"][:n], st["m"][:n], st["v"][:n] = out["master"], out["m"], out["v"]
+    compare_f32(to_np(b.master), st["master"], "cache cap master")
+    compare_f32(to_np(b.exp_avg), st["m"], "cache cap m")
+    compare_f32(to_np(b.exp_avg_sq), st["v"], "cache cap v")
+
+
 # ------------------------------------------------------ full workloads
 
 def _workload_segments(L, w, with_orig, device_grads=1):

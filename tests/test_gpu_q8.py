@@ -307,6 +307,28 @@ def test_q8_plans_match_direct_calls(L):
         assert torch.equal(x, y)
 
 
+def test_repeated_calls_reuse_cached_tables(L):
+    """A plan stepped again and again uploads its launch tables once: calls
+    whose segments need both workgroup sizes (rows of 4096 and of 11,008)
+    launch two tables per call, and both stay cached."""
+    cases = [Case(L, 4096 * 2, 4096, 9950), Case(L, 11008 * 2, 11008, 9960)]
+    plan = L.AdamwQ8Plan([c.segment(L) for c in cases])
+    accs = [L.Q8.empty(c.n, c.row_len) for c in cases]
+    grads = [up(host_bf16(c.n, 1e-3, 9970 + i)) for i, c in enumerate(cases)]
+    acc_plan = L.AccumQ8Plan([L.AccumQ8Segment(a, g) for a, g in zip(accs, grads)])
+    acc_plan.run(overwrite=True)
+    plan.step(step=1, **HP)
+    torch.cuda.synchronize()
+    before = L.table_cache_stats()
+    for t in range(2, 12):
+        acc_plan.run(overwrite=False)
+        plan.step(step=t, **HP)
+    torch.cuda.synchronize()
+    after = L.table_cache_stats()
+    assert after["uploads"] == before["uploads"], (before, after)
+    assert after["hits"] - before["hits"] == 10 * 4, (before, after)
+
+
 # -------------------------------------------------- workloads at full size
 
 def _workload_q8(L, w, row_len_of, *, delta, grad="bf16"):
