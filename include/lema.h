@@ -405,6 +405,42 @@ lema_status lema_slot_stream_staged(lema_slot_pool *pool, const lema_layer *laye
                                     int32_t nlayers, const lema_adamw_args *args,
                                     int32_t host_threads, lema_stream_stats *stats);
 
+/*
+ * One layer of host-resident state for lema_slot_stream_q8: int8 moments
+ * with row scales and/or an int8 gradient accumulator, kept quantized in
+ * host memory.  Every array named by a segment is a host pointer; orig_bf16
+ * and delta must be NULL.
+ */
+typedef struct {
+    const lema_adamw_q8_seg *host_segs;
+    int32_t                  nseg;
+} lema_layer_q8;
+
+/*
+ * The slot-pool streaming of lema_slot_stream / lema_slot_stream_staged for
+ * quantized host state (LEMA README, "Quantization": optimizer states and
+ * accumulators stay quantized in RAM, including the mmap disk backend, and
+ * are dequantized only inside the per-layer AdamW step).  Per segment, the
+ * master, the moments (int8 codes and row scales, or fp32) and the gradient
+ * (bf16, fp32, or int8 codes and row scales) are copied in, the step of
+ * lema_adamw_step_q8 runs on the slot, and the master, the moments and
+ * their scales and the bf16 weight are copied back.  With int8 moments and
+ * a bf16 gradient that is 8 B per parameter each way instead of 14.
+ *   moment_dtype : lema_state_dtype of every segment
+ *   staged       : 0 = host arrays are page-locked and copied directly
+ *                  (LEMA_ERR_NOT_PINNED otherwise); 1 = any host memory,
+ *                  moved through the pool's page-locked staging buffers by
+ *                  `host_threads` threads (0 = up to 16)
+ * args->grad_dtype may be LEMA_GRAD_BF16, LEMA_GRAD_FP32 or LEMA_GRAD_Q8.
+ * Errors: as lema_slot_stream, plus LEMA_ERR_DTYPE for an unknown
+ * moment_dtype and LEMA_ERR_SIZE for a row length outside 1..LEMA_Q8_MAX_ROW
+ * or host_threads outside 0..256.
+ */
+lema_status lema_slot_stream_q8(lema_slot_pool *pool, const lema_layer_q8 *layers,
+                                int32_t nlayers, const lema_adamw_args *args,
+                                int32_t moment_dtype, int32_t staged, int32_t host_threads,
+                                lema_stream_stats *stats);
+
 /* Page-locked host allocation of exactly `bytes` bytes (hipHostMalloc). */
 lema_status lema_host_alloc(void **out, size_t bytes);
 lema_status lema_host_free(void *p);

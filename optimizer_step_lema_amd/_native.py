@@ -79,6 +79,10 @@ class Layer(ctypes.Structure):
     _fields_ = [("host_segs", ctypes.POINTER(AdamwSeg)), ("nseg", i32)]
 
 
+class LayerQ8(ctypes.Structure):
+    _fields_ = [("host_segs", ctypes.POINTER(AdamwQ8Seg)), ("nseg", i32)]
+
+
 class StreamStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in (
         "h2d_bytes", "d2h_bytes", "h2d_ms", "d2h_ms", "kernel_ms",
@@ -109,6 +113,8 @@ SIGNATURES = [
                                ctypes.POINTER(StreamStats)]),
     ("lema_slot_stream_staged", i32, [vp, ctypes.POINTER(Layer), i32, ctypes.POINTER(AdamwArgs),
                                       i32, ctypes.POINTER(StreamStats)]),
+    ("lema_slot_stream_q8", i32, [vp, ctypes.POINTER(LayerQ8), i32, ctypes.POINTER(AdamwArgs),
+                                  i32, i32, i32, ctypes.POINTER(StreamStats)]),
     ("lema_host_alloc", i32, [ctypes.POINTER(vp), ctypes.c_size_t]),
     ("lema_host_free", i32, [vp]),
     ("lema_measure_copy", i32, [vp, vp, ctypes.c_size_t, vp]),

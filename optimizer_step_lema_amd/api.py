@@ -251,11 +251,12 @@ class Q8:
                    torch.zeros(cls.rows_of(numel, row_len), dtype=torch.float32, device=device),
                    int(row_len))
 
-    def pointers(self, n: int, name: str):
+    def pointers(self, n: int, name: str, where: str = "cuda"):
         if self.codes.numel() != n:
             raise ValueError(f"{name}: expected {n} codes, got {self.codes.numel()}")
-        codes = _check(self.codes, torch.int8, n, f"{name}.codes")
-        scale = _check(self.scale, torch.float32, self.rows_of(n, self.row_len), f"{name}.scale")
+        codes = _check(self.codes, torch.int8, n, f"{name}.codes", where)
+        scale = _check(self.scale, torch.float32, self.rows_of(n, self.row_len), f"{name}.scale",
+                       where)
         return codes, scale
 
 
@@ -314,24 +315,24 @@ class AdamwQ8Segment:
             raise TypeError(f"grad: expected bfloat16, float32 or Q8, got {self.grad.dtype}")
         return mom_q8, gd
 
-    def to_c(self) -> N.AdamwQ8Seg:
+    def to_c(self, where: str = "cuda") -> N.AdamwQ8Seg:
         n = self.master.numel()
         mom_q8, gd = self.kinds()
         if mom_q8:
-            m, ms = self.exp_avg.pointers(n, "exp_avg")
-            v, vs = self.exp_avg_sq.pointers(n, "exp_avg_sq")
+            m, ms = self.exp_avg.pointers(n, "exp_avg", where)
+            v, vs = self.exp_avg_sq.pointers(n, "exp_avg_sq", where)
         else:
-            m, ms = _check(self.exp_avg, torch.float32, n, "exp_avg"), 0
-            v, vs = _check(self.exp_avg_sq, torch.float32, n, "exp_avg_sq"), 0
+            m, ms = _check(self.exp_avg, torch.float32, n, "exp_avg", where), 0
+            v, vs = _check(self.exp_avg_sq, torch.float32, n, "exp_avg_sq", where), 0
         if gd == N.LEMA_GRAD_Q8:
-            g, gs = self.grad.pointers(n, "grad")
+            g, gs = self.grad.pointers(n, "grad", where)
         else:
-            g, gs = _check(self.grad, self.grad.dtype, n, "grad"), 0
+            g, gs = _check(self.grad, self.grad.dtype, n, "grad", where), 0
         return N.AdamwQ8Seg(
-            _check(self.master, torch.float32, n, "master"), m, ms, v, vs, g, gs,
-            _check(self.weight, torch.bfloat16, n, "weight"),
-            _check(self.orig, torch.bfloat16, n, "orig"),
-            _check(self.delta, torch.float32, n, "delta"), n, self.row_len())
+            _check(self.master, torch.float32, n, "master", where), m, ms, v, vs, g, gs,
+            _check(self.weight, torch.bfloat16, n, "weight", where),
+            _check(self.orig, torch.bfloat16, n, "orig", where),
+            _check(self.delta, torch.float32, n, "delta", where), n, self.row_len())
 
 
 def _q8_call_kinds(segments: Sequence[AdamwQ8Segment]):
@@ -478,6 +479,32 @@ class SlotPool:
         else:
             N.check(lib.lema_slot_stream(self.handle, c_layers, len(layers), ctypes.byref(args),
                                          ctypes.byref(st)), "lema_slot_stream")
+        return {name: getattr(st, name) for name, _ in N.StreamStats._fields_}
+
+    def stream_q8(self, layers: Sequence[Sequence[AdamwQ8Segment]], *, lr, beta1=0.9,
+                  beta2=0.999, eps=1e-8, weight_decay=0.01, step, staged: bool = False,
+                  host_threads: int = 0) -> dict:
+        """The streamed step for quantized host state (lema_slot_stream_q8):
+        int8 moments with row scales and/or an int8 accumulator stay
+        quantized in host memory.  staged=False needs page-locked host
+        tensors; staged=True takes any host memory."""
+        lib = N.load()
+        keep = []
+        kinds = {s.kinds() for segs in layers for s in segs}
+        if len(kinds) > 1:
+            raise TypeError("all segments of one call must share moment and gradient dtypes")
+        mom_q8, gd = kinds.pop() if kinds else (True, N.LEMA_GRAD_BF16)
+        c_layers = (N.LayerQ8 * max(1, len(layers)))()
+        for i, segs in enumerate(layers):
+            arr = (N.AdamwQ8Seg * max(1, len(segs)))(*[s.to_c(where="cpu") for s in segs])
+            keep.append(arr)
+            c_layers[i] = N.LayerQ8(ctypes.cast(arr, ctypes.POINTER(N.AdamwQ8Seg)), len(segs))
+        args = _args(lr, beta1, beta2, eps, weight_decay, step, gd)
+        st = N.StreamStats()
+        N.check(lib.lema_slot_stream_q8(self.handle, c_layers, len(layers), ctypes.byref(args),
+                                        N.LEMA_STATE_Q8 if mom_q8 else N.LEMA_STATE_FP32,
+                                        1 if staged else 0, int(host_threads), ctypes.byref(st)),
+                "lema_slot_stream_q8")
         return {name: getattr(st, name) for name, _ in N.StreamStats._fields_}
 
     def close(self):

@@ -33,6 +33,18 @@ lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_
 bool any_conflict(std::vector<Span> &spans);
 void add_span(std::vector<Span> &spans, const void *p, int64_t numel, size_t elem, bool written);
 
+// Validates int8-path segment descriptors for a gradient dtype and moment
+// dtype: sizes, row lengths (when an array is int8), required pointers,
+// element alignment, and delta only where allowed.  Appends the arrays'
+// spans when `spans` is non-null and the launch records of the non-empty
+// segments when `recs` is non-null; sets *with_delta when a segment writes a
+// delta.
+lema_status validate_q8_segs(const lema_adamw_q8_seg *segs, int32_t nseg, int32_t grad_dtype,
+                             int32_t moment_dtype, bool delta_allowed, std::vector<Span> *spans,
+                             std::vector<Q8Rec> *recs, bool *with_delta);
+// Rows of a tensor of numel elements cut into rows of row_len.
+int64_t q8_rows(int64_t numel, int64_t row_len);
+
 // Launch records of the non-empty segments; last_bf16 (may be NULL) gives
 // each segment's last micro-batch for the fused accumulate-and-step mode.
 void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec> *out,

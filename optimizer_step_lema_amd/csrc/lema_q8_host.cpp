@@ -106,34 +106,25 @@ lema_status plain_step(const lema_adamw_q8_seg *segs, int32_t nseg, const lema_a
 }
 
 }  // namespace
-}  // namespace lema
 
-using namespace lema;
+int64_t q8_rows(int64_t numel, int64_t row_len) { return ceil_div(numel, row_len); }
 
-extern "C" {
-
-lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
-                               const lema_adamw_args *args, int32_t moment_dtype, void *stream) {
-    lema_status st = check_hparams(args, true);
-    if (st != LEMA_OK) return st;
-    if (moment_dtype != LEMA_STATE_FP32 && moment_dtype != LEMA_STATE_Q8) return LEMA_ERR_DTYPE;
+lema_status validate_q8_segs(const lema_adamw_q8_seg *segs, int32_t nseg, int32_t gd,
+                             int32_t moment_dtype, bool delta_allowed, std::vector<Span> *spans,
+                             std::vector<Q8Rec> *recs, bool *with_delta) {
     if (nseg < 0) return LEMA_ERR_SIZE;
     if (nseg > 0 && segs == nullptr) return LEMA_ERR_NULL;
     const bool mom_q8 = moment_dtype == LEMA_STATE_Q8;
-    const int32_t gd = args->grad_dtype;
-    if (!mom_q8 && gd != LEMA_GRAD_Q8) return plain_step(segs, nseg, args, stream);
-
+    const bool rows_used = mom_q8 || gd == LEMA_GRAD_Q8;
     const size_t mom_size = mom_q8 ? 1 : 4;
     const size_t grad_size = gd == LEMA_GRAD_BF16 ? 2 : gd == LEMA_GRAD_FP32 ? 4 : 1;
-    std::vector<Span> spans;
-    std::vector<Q8Rec> recs;
-    bool with_delta = false;
     for (int32_t i = 0; i < nseg; ++i) {
         const lema_adamw_q8_seg &s = segs[i];
         if (s.numel < 0) return LEMA_ERR_SIZE;
         if ((s.orig_bf16 == nullptr) != (s.delta == nullptr)) return LEMA_ERR_NULL;
+        if (!delta_allowed && s.delta != nullptr) return LEMA_ERR_NULL;
         if (s.numel == 0) continue;
-        if (!row_len_ok(s.row_len)) return LEMA_ERR_SIZE;
+        if (rows_used && !row_len_ok(s.row_len)) return LEMA_ERR_SIZE;
         if (!s.master || !s.exp_avg || !s.exp_avg_sq || !s.grad || !s.weight_bf16)
             return LEMA_ERR_NULL;
         if (mom_q8 && (!s.exp_avg_scale || !s.exp_avg_sq_scale)) return LEMA_ERR_NULL;
@@ -156,29 +147,59 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
                              (gd == LEMA_GRAD_Q8 ? bits(s.grad) : 0);
         const bool vec = (v16 & 15) == 0 && (b16 & 7) == 0 && (v4 & 3) == 0;
 
-        Q8Rec r = make_rec(s.numel, s.row_len, vec, kQStepChunks);
-        add_span(spans, s.master, s.numel, 4, true);
-        add_span(spans, s.exp_avg, s.numel, mom_size, true);
-        add_span(spans, s.exp_avg_sq, s.numel, mom_size, true);
-        if (mom_q8) {
-            add_span(spans, s.exp_avg_scale, r.rows, 4, true);
-            add_span(spans, s.exp_avg_sq_scale, r.rows, 4, true);
+        const int64_t rows = rows_used ? q8_rows(s.numel, s.row_len) : 0;
+        if (spans) {
+            add_span(*spans, s.master, s.numel, 4, true);
+            add_span(*spans, s.exp_avg, s.numel, mom_size, true);
+            add_span(*spans, s.exp_avg_sq, s.numel, mom_size, true);
+            if (mom_q8) {
+                add_span(*spans, s.exp_avg_scale, rows, 4, true);
+                add_span(*spans, s.exp_avg_sq_scale, rows, 4, true);
+            }
+            add_span(*spans, s.grad, s.numel, grad_size, false);
+            if (gd == LEMA_GRAD_Q8) add_span(*spans, s.grad_scale, rows, 4, false);
+            add_span(*spans, s.weight_bf16, s.numel, 2, true);
+            if (s.delta) {
+                add_span(*spans, s.orig_bf16, s.numel, 2, false);
+                add_span(*spans, s.delta, s.numel, 4, true);
+            }
         }
-        add_span(spans, s.grad, s.numel, grad_size, false);
-        if (gd == LEMA_GRAD_Q8) add_span(spans, s.grad_scale, r.rows, 4, false);
-        add_span(spans, s.weight_bf16, s.numel, 2, true);
-        if (s.delta) {
-            add_span(spans, s.orig_bf16, s.numel, 2, false);
-            add_span(spans, s.delta, s.numel, 4, true);
-            with_delta = true;
+        if (s.delta && with_delta) *with_delta = true;
+        if (recs) {
+            Q8Rec r = make_rec(s.numel, s.row_len, vec, kQStepChunks);
+            const void *ptrs[10] = {s.master, s.exp_avg, mom_q8 ? s.exp_avg_scale : nullptr,
+                                    s.exp_avg_sq, mom_q8 ? s.exp_avg_sq_scale : nullptr, s.grad,
+                                    gd == LEMA_GRAD_Q8 ? s.grad_scale : nullptr, s.weight_bf16,
+                                    s.orig_bf16, s.delta};
+            for (int k = 0; k < 10; ++k) r.p[k] = reinterpret_cast<uint64_t>(ptrs[k]);
+            recs->push_back(r);
         }
-        const void *ptrs[10] = {s.master, s.exp_avg, mom_q8 ? s.exp_avg_scale : nullptr,
-                                s.exp_avg_sq, mom_q8 ? s.exp_avg_sq_scale : nullptr, s.grad,
-                                gd == LEMA_GRAD_Q8 ? s.grad_scale : nullptr, s.weight_bf16,
-                                s.orig_bf16, s.delta};
-        for (int k = 0; k < 10; ++k) r.p[k] = reinterpret_cast<uint64_t>(ptrs[k]);
-        recs.push_back(r);
     }
+    return LEMA_OK;
+}
+
+}  // namespace lema
+
+using namespace lema;
+
+extern "C" {
+
+lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
+                               const lema_adamw_args *args, int32_t moment_dtype, void *stream) {
+    lema_status st = check_hparams(args, true);
+    if (st != LEMA_OK) return st;
+    if (moment_dtype != LEMA_STATE_FP32 && moment_dtype != LEMA_STATE_Q8) return LEMA_ERR_DTYPE;
+    if (nseg < 0) return LEMA_ERR_SIZE;
+    if (nseg > 0 && segs == nullptr) return LEMA_ERR_NULL;
+    const bool mom_q8 = moment_dtype == LEMA_STATE_Q8;
+    const int32_t gd = args->grad_dtype;
+    if (!mom_q8 && gd != LEMA_GRAD_Q8) return plain_step(segs, nseg, args, stream);
+
+    std::vector<Span> spans;
+    std::vector<Q8Rec> recs;
+    bool with_delta = false;
+    st = validate_q8_segs(segs, nseg, gd, moment_dtype, true, &spans, &recs, &with_delta);
+    if (st != LEMA_OK) return st;
     if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
     if (recs.empty()) return LEMA_OK;
     const AdamwConsts c = derive_consts(args);

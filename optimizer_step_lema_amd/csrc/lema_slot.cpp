@@ -19,11 +19,19 @@
 //
 //   copy stream     : H2D(0) H2D(1) H2D(2) ...      (H2D(i) waits for D2H(i - nslots))
 //   write-back      :        D2H(0) D2H(1) ...      (D2H(i) waits for K(i))
+//
+// Both pipelines work on a layer plan: the list of the layer's arrays, each
+// with its host address, its offset in the slot and whether it is copied in,
+// out or both, plus the launch of the layer's step on the slot.  fp32 state
+// (lema_slot_stream*) and int8 state with row scales (lema_slot_stream_q8,
+// README "Quantization": quantized states stay quantized in RAM) differ
+// only in their plans.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <chrono>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <thread>
 #include <utility>
@@ -54,39 +62,123 @@ constexpr size_t kSlotAlign = 256;
 
 size_t align_up(size_t x) { return (x + kSlotAlign - 1) & ~(kSlotAlign - 1); }
 
-// Bytes one layer needs in a slot: master, m, v, grad (bf16), weight (bf16)
-// per segment, each array starting on a 256-byte boundary.
-size_t layer_slot_bytes(const lema_layer &L) {
-    size_t off = 0;
-    for (int32_t i = 0; i < L.nseg; ++i) {
-        const size_t n = static_cast<size_t>(L.host_segs[i].numel);
-        if (n == 0) continue;
-        off = align_up(off) + 4 * n;
-        off = align_up(off) + 4 * n;
-        off = align_up(off) + 4 * n;
-        off = align_up(off) + 2 * n;
-        off = align_up(off) + 2 * n;
-    }
-    return off;
-}
+// One array of a layer: host memory, its place in the slot (and in a
+// staging buffer laid out like the slot), and the copies it takes part in.
+struct Xfer {
+    char *host;
+    size_t off;
+    size_t bytes;
+    bool in;     // host -> slot before the step
+    bool out;    // slot -> host after the step
+};
 
-// Device-side segment descriptors of layer L placed at `slot`.
-void slot_segments(const lema_layer &L, char *slot, std::vector<lema_adamw_seg> *out) {
-    out->clear();
-    size_t off = 0;
+// A layer's arrays and the launch of its step on a slot.
+struct LayerPlan {
+    std::vector<Xfer> xfers;
+    size_t bytes = 0;                                            // slot bytes used
+    std::function<lema_status(char *slot, hipStream_t)> launch;  // step on `slot`
+};
+
+struct PlanBuilder {
+    LayerPlan *plan;
+    // Places an array of `bytes` in the slot; returns its offset.
+    size_t add(const void *host, size_t bytes, bool in, bool out) {
+        const size_t off = align_up(plan->bytes);
+        plan->xfers.push_back({static_cast<char *>(const_cast<void *>(host)), off, bytes, in, out});
+        plan->bytes = off + bytes;
+        return off;
+    }
+};
+
+// fp32 state: master, m, v in and out (12 B), bf16 gradient in (2 B), bf16
+// weight out (2 B).
+LayerPlan plan_fp32(const lema_layer &L, const AdamwConsts &consts) {
+    LayerPlan plan;
+    PlanBuilder b{&plan};
+    struct Offs { size_t master, m, v, grad, weight; int64_t numel; };
+    std::vector<Offs> offs;
     for (int32_t i = 0; i < L.nseg; ++i) {
         const lema_adamw_seg &h = L.host_segs[i];
         const size_t n = static_cast<size_t>(h.numel);
         if (n == 0) continue;
-        lema_adamw_seg d{};
-        off = align_up(off); d.master = reinterpret_cast<float *>(slot + off); off += 4 * n;
-        off = align_up(off); d.exp_avg = reinterpret_cast<float *>(slot + off); off += 4 * n;
-        off = align_up(off); d.exp_avg_sq = reinterpret_cast<float *>(slot + off); off += 4 * n;
-        off = align_up(off); d.grad = slot + off; off += 2 * n;
-        off = align_up(off); d.weight_bf16 = reinterpret_cast<uint16_t *>(slot + off); off += 2 * n;
-        d.numel = h.numel;
-        out->push_back(d);
+        Offs o;
+        o.master = b.add(h.master, 4 * n, true, true);
+        o.m = b.add(h.exp_avg, 4 * n, true, true);
+        o.v = b.add(h.exp_avg_sq, 4 * n, true, true);
+        o.grad = b.add(h.grad, 2 * n, true, false);
+        o.weight = b.add(h.weight_bf16, 2 * n, false, true);
+        o.numel = h.numel;
+        offs.push_back(o);
     }
+    plan.launch = [offs, consts](char *slot, hipStream_t stream) -> lema_status {
+        std::vector<lema_adamw_seg> segs;
+        for (const Offs &o : offs) {
+            lema_adamw_seg d{};
+            d.master = reinterpret_cast<float *>(slot + o.master);
+            d.exp_avg = reinterpret_cast<float *>(slot + o.m);
+            d.exp_avg_sq = reinterpret_cast<float *>(slot + o.v);
+            d.grad = slot + o.grad;
+            d.weight_bf16 = reinterpret_cast<uint16_t *>(slot + o.weight);
+            d.numel = o.numel;
+            segs.push_back(d);
+        }
+        std::vector<SegRec> recs;
+        adamw_records(segs.data(), int32_t(segs.size()), &recs, nullptr);
+        return launch_adamw_recs(recs, consts, kGradBf16, stream);
+    };
+    return plan;
+}
+
+// int8 state: master in and out; m and v as codes plus row scales (or fp32)
+// in and out; the gradient (bf16, fp32, or int8 codes plus row scales) in;
+// the bf16 weight out.
+LayerPlan plan_q8(const lema_layer_q8 &L, const lema_adamw_args &args, int32_t moment_dtype) {
+    LayerPlan plan;
+    PlanBuilder b{&plan};
+    const bool mom_q8 = moment_dtype == LEMA_STATE_Q8;
+    const bool grad_q8 = args.grad_dtype == LEMA_GRAD_Q8;
+    const size_t msize = mom_q8 ? 1 : 4;
+    const size_t gsize = args.grad_dtype == LEMA_GRAD_BF16 ? 2 : args.grad_dtype == LEMA_GRAD_FP32 ? 4 : 1;
+    struct Offs { size_t master, m, ms, v, vs, grad, gs, weight; int64_t numel, row_len; };
+    std::vector<Offs> offs;
+    for (int32_t i = 0; i < L.nseg; ++i) {
+        const lema_adamw_q8_seg &h = L.host_segs[i];
+        const size_t n = static_cast<size_t>(h.numel);
+        if (n == 0) continue;
+        const size_t rows = (mom_q8 || grad_q8) ? size_t(q8_rows(h.numel, h.row_len)) : 0;
+        Offs o{};
+        o.master = b.add(h.master, 4 * n, true, true);
+        o.m = b.add(h.exp_avg, msize * n, true, true);
+        if (mom_q8) o.ms = b.add(h.exp_avg_scale, 4 * rows, true, true);
+        o.v = b.add(h.exp_avg_sq, msize * n, true, true);
+        if (mom_q8) o.vs = b.add(h.exp_avg_sq_scale, 4 * rows, true, true);
+        o.grad = b.add(h.grad, gsize * n, true, false);
+        if (grad_q8) o.gs = b.add(h.grad_scale, 4 * rows, true, false);
+        o.weight = b.add(h.weight_bf16, 2 * n, false, true);
+        o.numel = h.numel;
+        o.row_len = h.row_len;
+        offs.push_back(o);
+    }
+    plan.launch = [offs, args, moment_dtype, mom_q8, grad_q8](char *slot,
+                                                              hipStream_t stream) -> lema_status {
+        std::vector<lema_adamw_q8_seg> segs;
+        for (const Offs &o : offs) {
+            lema_adamw_q8_seg d{};
+            d.master = reinterpret_cast<float *>(slot + o.master);
+            d.exp_avg = slot + o.m;
+            d.exp_avg_scale = mom_q8 ? reinterpret_cast<float *>(slot + o.ms) : nullptr;
+            d.exp_avg_sq = slot + o.v;
+            d.exp_avg_sq_scale = mom_q8 ? reinterpret_cast<float *>(slot + o.vs) : nullptr;
+            d.grad = slot + o.grad;
+            d.grad_scale = grad_q8 ? reinterpret_cast<const float *>(slot + o.gs) : nullptr;
+            d.weight_bf16 = reinterpret_cast<uint16_t *>(slot + o.weight);
+            d.numel = o.numel;
+            d.row_len = o.row_len;
+            segs.push_back(d);
+        }
+        return lema_adamw_step_q8(segs.data(), int32_t(segs.size()), &args, moment_dtype, stream);
+    };
+    return plan;
 }
 
 // True if [p, p + bytes) lies in page-locked host memory known to HIP.
@@ -123,39 +215,32 @@ lema_status ensure_events(lema_slot_pool *pool, size_t n) {
 
 enum { EV_H2D_BEGIN = 0, EV_H2D_END, EV_K_BEGIN, EV_K_END, EV_D2H_BEGIN, EV_D2H_END, EV_PER_LAYER };
 
-// The non-empty segments of a layer, in order.
-void nonempty_segments(const lema_layer &L, std::vector<lema_adamw_seg> *out) {
-    out->clear();
-    for (int32_t i = 0; i < L.nseg; ++i)
-        if (L.host_segs[i].numel > 0) out->push_back(L.host_segs[i]);
-}
-
-// Host -> slot copies of master, m, v and the bf16 gradient (14 B/param).
-hipError_t enqueue_upload(const std::vector<lema_adamw_seg> &src,
-                          const std::vector<lema_adamw_seg> &dst, hipStream_t s, double *bytes) {
+// Copies of a plan's `in` arrays from `host_side` (host arrays, or a staging
+// buffer laid out like the slot when non-null) into the slot.
+hipError_t enqueue_upload(const LayerPlan &plan, char *slot, char *staging, hipStream_t s,
+                          double *bytes) {
     hipError_t e = hipSuccess;
-    for (size_t k = 0; k < src.size() && e == hipSuccess; ++k) {
-        const size_t n = size_t(src[k].numel);
-        e = hipMemcpyAsync(dst[k].master, src[k].master, 4 * n, hipMemcpyHostToDevice, s);
-        if (e == hipSuccess) e = hipMemcpyAsync(dst[k].exp_avg, src[k].exp_avg, 4 * n, hipMemcpyHostToDevice, s);
-        if (e == hipSuccess) e = hipMemcpyAsync(dst[k].exp_avg_sq, src[k].exp_avg_sq, 4 * n, hipMemcpyHostToDevice, s);
-        if (e == hipSuccess) e = hipMemcpyAsync(const_cast<void *>(dst[k].grad), src[k].grad, 2 * n, hipMemcpyHostToDevice, s);
-        *bytes += 14.0 * double(n);
+    for (const Xfer &x : plan.xfers) {
+        if (!x.in || x.bytes == 0) continue;
+        const char *src = staging ? staging + x.off : x.host;
+        e = hipMemcpyAsync(slot + x.off, src, x.bytes, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) return e;
+        *bytes += double(x.bytes);
     }
     return e;
 }
 
-// Slot -> host copies of master, m, v and the bf16 weight (14 B/param).
-hipError_t enqueue_writeback(const std::vector<lema_adamw_seg> &src,
-                             const std::vector<lema_adamw_seg> &dst, hipStream_t s, double *bytes) {
+// Copies of a plan's `out` arrays from the slot to the host arrays (or to a
+// staging buffer laid out like the slot when non-null).
+hipError_t enqueue_writeback(const LayerPlan &plan, char *slot, char *staging, hipStream_t s,
+                             double *bytes) {
     hipError_t e = hipSuccess;
-    for (size_t k = 0; k < src.size() && e == hipSuccess; ++k) {
-        const size_t n = size_t(src[k].numel);
-        e = hipMemcpyAsync(dst[k].master, src[k].master, 4 * n, hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipMemcpyAsync(dst[k].exp_avg, src[k].exp_avg, 4 * n, hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipMemcpyAsync(dst[k].exp_avg_sq, src[k].exp_avg_sq, 4 * n, hipMemcpyDeviceToHost, s);
-        if (e == hipSuccess) e = hipMemcpyAsync(dst[k].weight_bf16, src[k].weight_bf16, 2 * n, hipMemcpyDeviceToHost, s);
-        *bytes += 14.0 * double(n);
+    for (const Xfer &x : plan.xfers) {
+        if (!x.out || x.bytes == 0) continue;
+        char *dst = staging ? staging + x.off : x.host;
+        e = hipMemcpyAsync(dst, slot + x.off, x.bytes, hipMemcpyDeviceToHost, s);
+        if (e != hipSuccess) return e;
+        *bytes += double(x.bytes);
     }
     return e;
 }
@@ -241,43 +326,234 @@ void parallel_copy(const std::vector<CopyItem> &items, int threads) {
     for (std::thread &t : pool) t.join();
 }
 
-// Items moving a layer's inputs (master, m, v, grad) from the caller's memory
-// into staging laid out like the slot, or its outputs (master, m, v, weight)
-// back from staging.
-void staging_items(const std::vector<lema_adamw_seg> &host, const std::vector<lema_adamw_seg> &stage,
-                   bool inbound, std::vector<CopyItem> *out) {
+// Items moving a plan's `in` arrays from the caller's memory into staging
+// laid out like the slot, or its `out` arrays back from staging.
+void staging_items(const LayerPlan &plan, char *staging, bool inbound, std::vector<CopyItem> *out) {
     out->clear();
-    for (size_t k = 0; k < host.size(); ++k) {
-        const size_t n = size_t(host[k].numel);
-        if (inbound) {
-            out->push_back({stage[k].master, host[k].master, 4 * n});
-            out->push_back({stage[k].exp_avg, host[k].exp_avg, 4 * n});
-            out->push_back({stage[k].exp_avg_sq, host[k].exp_avg_sq, 4 * n});
-            out->push_back({const_cast<void *>(stage[k].grad), host[k].grad, 2 * n});
-        } else {
-            out->push_back({host[k].master, stage[k].master, 4 * n});
-            out->push_back({host[k].exp_avg, stage[k].exp_avg, 4 * n});
-            out->push_back({host[k].exp_avg_sq, stage[k].exp_avg_sq, 4 * n});
-            out->push_back({host[k].weight_bf16, stage[k].weight_bf16, 2 * n});
-        }
+    for (const Xfer &x : plan.xfers) {
+        if (x.bytes == 0) continue;
+        if (inbound && x.in) out->push_back({staging + x.off, x.host, x.bytes});
+        if (!inbound && x.out) out->push_back({x.host, staging + x.off, x.bytes});
     }
 }
 
 lema_status validate_layers(lema_slot_pool *pool, const lema_layer *layers, int32_t nlayers,
-                            const lema_adamw_args *args, std::vector<Span> *spans) {
+                            const lema_adamw_args *args, std::vector<Span> *spans,
+                            std::vector<LayerPlan> *plans) {
     if (pool == nullptr) return LEMA_ERR_NULL;
     lema_status st = check_hparams(args);
     if (st != LEMA_OK) return st;
     if (args->grad_dtype != LEMA_GRAD_BF16) return LEMA_ERR_DTYPE;
     if (nlayers < 0) return LEMA_ERR_SIZE;
     if (nlayers > 0 && layers == nullptr) return LEMA_ERR_NULL;
+    const AdamwConsts consts = derive_consts(args);
     for (int32_t i = 0; i < nlayers; ++i) {
         const lema_layer &L = layers[i];
         st = validate_adamw_segs(L.host_segs, L.nseg, LEMA_GRAD_BF16, false, spans);
         if (st != LEMA_OK) return st;
-        if (layer_slot_bytes(L) > pool->slot_bytes) return LEMA_ERR_SIZE;
+        plans->push_back(plan_fp32(L, consts));
+        if (plans->back().bytes > pool->slot_bytes) return LEMA_ERR_SIZE;
     }
     if (any_conflict(*spans)) return LEMA_ERR_OVERLAP;
+    return LEMA_OK;
+}
+
+lema_status validate_layers_q8(lema_slot_pool *pool, const lema_layer_q8 *layers,
+                               int32_t nlayers, const lema_adamw_args *args,
+                               int32_t moment_dtype, std::vector<Span> *spans,
+                               std::vector<LayerPlan> *plans) {
+    if (pool == nullptr) return LEMA_ERR_NULL;
+    lema_status st = check_hparams(args, true);
+    if (st != LEMA_OK) return st;
+    if (moment_dtype != LEMA_STATE_FP32 && moment_dtype != LEMA_STATE_Q8) return LEMA_ERR_DTYPE;
+    if (nlayers < 0) return LEMA_ERR_SIZE;
+    if (nlayers > 0 && layers == nullptr) return LEMA_ERR_NULL;
+    for (int32_t i = 0; i < nlayers; ++i) {
+        const lema_layer_q8 &L = layers[i];
+        st = validate_q8_segs(L.host_segs, L.nseg, args->grad_dtype, moment_dtype, false, spans,
+                              nullptr, nullptr);
+        if (st != LEMA_OK) return st;
+        plans->push_back(plan_q8(L, *args, moment_dtype));
+        if (plans->back().bytes > pool->slot_bytes) return LEMA_ERR_SIZE;
+    }
+    if (any_conflict(*spans)) return LEMA_ERR_OVERLAP;
+    return LEMA_OK;
+}
+
+// Host arrays used straight by the copy engines must be page-locked.
+lema_status check_pinned(const std::vector<Span> &spans) {
+    for (const Span &s : spans)
+        if (s.hi > s.lo && !is_pinned(reinterpret_cast<const void *>(s.lo), s.hi - s.lo))
+            return LEMA_ERR_NOT_PINNED;
+    return LEMA_OK;
+}
+
+// ------------------------------------------------------------- pipelines
+
+// Page-locked host arrays: copies go straight between host and slots.
+lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans,
+                       lema_stream_stats *stats) {
+    const int32_t nlayers = int32_t(plans.size());
+    if (nlayers == 0) {
+        if (stats) *stats = lema_stream_stats{};
+        return LEMA_OK;
+    }
+    const auto call_start = std::chrono::steady_clock::now();
+
+    std::lock_guard<std::mutex> lock(pool->mu);
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_failed(e);
+    if (cur != pool->device) return LEMA_ERR_HIP;
+    lema_status st = ensure_events(pool, size_t(nlayers) * EV_PER_LAYER);
+    if (st != LEMA_OK) return st;
+
+    auto ev = [&](int layer, int kind) { return pool->events[size_t(layer) * EV_PER_LAYER + kind]; };
+    auto slot_of = [&](int i) { return pool->base + size_t(i % pool->nslots) * pool->slot_bytes; };
+    double h2d_bytes = 0, d2h_bytes = 0;
+    hipStream_t d2h_stream = pool->writeback ? pool->writeback : pool->copy;
+
+    auto copy_back = [&](int j) -> lema_status {
+        hipError_t err = hipStreamWaitEvent(d2h_stream, ev(j, EV_K_END), 0);
+        if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_BEGIN), d2h_stream);
+        if (err == hipSuccess) err = enqueue_writeback(plans[j], slot_of(j), nullptr, d2h_stream, &d2h_bytes);
+        if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_END), d2h_stream);
+        return err == hipSuccess ? LEMA_OK : hip_failed(err);
+    };
+
+    for (int32_t i = 0; i < nlayers; ++i) {
+        // host -> slot; with a separate write-back stream the slot must first
+        // have been copied back from its previous occupant
+        e = hipSuccess;
+        if (pool->writeback && i >= pool->nslots)
+            e = hipStreamWaitEvent(pool->copy, ev(i - pool->nslots, EV_D2H_END), 0);
+        if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
+        if (e == hipSuccess) e = enqueue_upload(plans[i], slot_of(i), nullptr, pool->copy, &h2d_bytes);
+        if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
+        if (e != hipSuccess) return hip_failed(e);
+
+        // the step on the slot
+        e = hipStreamWaitEvent(pool->compute, ev(i, EV_H2D_END), 0);
+        if (e == hipSuccess) e = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
+        if (e != hipSuccess) return hip_failed(e);
+        st = plans[i].launch(slot_of(i), pool->compute);
+        if (st != LEMA_OK) return st;
+        e = hipEventRecord(ev(i, EV_K_END), pool->compute);
+        if (e != hipSuccess) return hip_failed(e);
+
+        // slot -> host for the previous layer, behind this layer's upload
+        if (i >= 1) {
+            st = copy_back(i - 1);
+            if (st != LEMA_OK) return st;
+        }
+    }
+    st = copy_back(nlayers - 1);
+    if (st != LEMA_OK) return st;
+    e = hipEventSynchronize(ev(nlayers - 1, EV_D2H_END));
+    if (e != hipSuccess) return hip_failed(e);
+
+    if (stats) {
+        fill_stats(pool, nlayers, h2d_bytes, d2h_bytes, stats);
+        stats->call_ms = std::chrono::duration<double, std::milli>(
+                             std::chrono::steady_clock::now() - call_start).count();
+    }
+    return LEMA_OK;
+}
+
+// Pageable or memory-mapped host arrays: each layer goes caller memory ->
+// staging[i % 2] -> slot[i % 2] -> staging[i % 2] -> caller memory.  Layer
+// i + 2 reuses both only after the host has copied layer i out of staging,
+// which itself waited for its write-back.
+lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans,
+                       int32_t host_threads, lema_stream_stats *stats) {
+    const int32_t nlayers = int32_t(plans.size());
+    if (nlayers == 0) {
+        if (stats) *stats = lema_stream_stats{};
+        return LEMA_OK;
+    }
+    int threads = host_threads;
+    if (threads == 0) {
+        const unsigned hc = std::thread::hardware_concurrency();
+        threads = int(std::min(16u, hc == 0 ? 4u : hc));
+    }
+    const auto call_start = std::chrono::steady_clock::now();
+
+    std::lock_guard<std::mutex> lock(pool->mu);
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_failed(e);
+    if (cur != pool->device) return LEMA_ERR_HIP;
+    for (int b = 0; b < 2; ++b) {
+        if (pool->staging[b] == nullptr) {
+            e = hipHostMalloc(reinterpret_cast<void **>(&pool->staging[b]), pool->slot_bytes,
+                              hipHostMallocDefault);
+            if (e != hipSuccess) {
+                pool->staging[b] = nullptr;
+                return hip_failed(e);
+            }
+        }
+    }
+    lema_status st = ensure_events(pool, size_t(nlayers) * EV_PER_LAYER);
+    if (st != LEMA_OK) return st;
+
+    auto ev = [&](int layer, int kind) { return pool->events[size_t(layer) * EV_PER_LAYER + kind]; };
+    double h2d_bytes = 0, d2h_bytes = 0, in_ms = 0, out_ms = 0;
+    hipStream_t d2h_stream = pool->writeback ? pool->writeback : pool->copy;
+    std::vector<CopyItem> items;
+    using clock = std::chrono::steady_clock;
+
+    auto stage_in_and_enqueue = [&](int i) -> lema_status {
+        const int b = i % 2;
+        char *slot = pool->base + size_t(b) * pool->slot_bytes;
+        staging_items(plans[i], pool->staging[b], true, &items);
+        const auto t0 = clock::now();
+        parallel_copy(items, threads);
+        in_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+
+        hipError_t err = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
+        if (err == hipSuccess) err = enqueue_upload(plans[i], slot, pool->staging[b], pool->copy, &h2d_bytes);
+        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
+        if (err == hipSuccess) err = hipStreamWaitEvent(pool->compute, ev(i, EV_H2D_END), 0);
+        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
+        if (err != hipSuccess) return hip_failed(err);
+        lema_status s2 = plans[i].launch(slot, pool->compute);
+        if (s2 != LEMA_OK) return s2;
+        err = hipEventRecord(ev(i, EV_K_END), pool->compute);
+        if (err == hipSuccess) err = hipStreamWaitEvent(d2h_stream, ev(i, EV_K_END), 0);
+        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_D2H_BEGIN), d2h_stream);
+        if (err == hipSuccess) err = enqueue_writeback(plans[i], slot, pool->staging[b], d2h_stream, &d2h_bytes);
+        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_D2H_END), d2h_stream);
+        return err == hipSuccess ? LEMA_OK : hip_failed(err);
+    };
+    auto wait_and_stage_out = [&](int i) -> lema_status {
+        hipError_t err = hipEventSynchronize(ev(i, EV_D2H_END));
+        if (err != hipSuccess) return hip_failed(err);
+        staging_items(plans[i], pool->staging[i % 2], false, &items);
+        const auto t0 = clock::now();
+        parallel_copy(items, threads);
+        out_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+        return LEMA_OK;
+    };
+
+    for (int i = 0; i < std::min(nlayers, 2); ++i) {
+        st = stage_in_and_enqueue(i);
+        if (st != LEMA_OK) return st;
+    }
+    for (int i = 0; i < nlayers; ++i) {
+        st = wait_and_stage_out(i);
+        if (st != LEMA_OK) return st;
+        if (i + 2 < nlayers) {
+            st = stage_in_and_enqueue(i + 2);
+            if (st != LEMA_OK) return st;
+        }
+    }
+
+    if (stats) {
+        fill_stats(pool, nlayers, h2d_bytes, d2h_bytes, stats);
+        stats->host_in_ms = in_ms;
+        stats->host_out_ms = out_ms;
+        stats->call_ms = std::chrono::duration<double, std::milli>(clock::now() - call_start).count();
+    }
     return LEMA_OK;
 }
 
@@ -338,193 +614,42 @@ lema_status lema_slot_pool_destroy(lema_slot_pool *pool) {
 
 lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int32_t nlayers,
                              const lema_adamw_args *args, lema_stream_stats *stats) {
-    // ---- validation of every layer before anything is enqueued
+    // validation of every layer before anything is enqueued
     std::vector<Span> spans;
-    lema_status st = validate_layers(pool, layers, nlayers, args, &spans);
+    std::vector<LayerPlan> plans;
+    lema_status st = validate_layers(pool, layers, nlayers, args, &spans, &plans);
     if (st != LEMA_OK) return st;
-    for (const Span &s : spans)
-        if (s.hi > s.lo && !is_pinned(reinterpret_cast<const void *>(s.lo), s.hi - s.lo))
-            return LEMA_ERR_NOT_PINNED;
-    if (nlayers == 0) {
-        if (stats) *stats = lema_stream_stats{};
-        return LEMA_OK;
-    }
-    const auto call_start = std::chrono::steady_clock::now();
-
-    std::lock_guard<std::mutex> lock(pool->mu);
-    int cur = 0;
-    hipError_t e = hipGetDevice(&cur);
-    if (e != hipSuccess) return hip_failed(e);
-    if (cur != pool->device) return LEMA_ERR_HIP;
-    st = ensure_events(pool, size_t(nlayers) * EV_PER_LAYER);
+    st = check_pinned(spans);
     if (st != LEMA_OK) return st;
-
-    const AdamwConsts consts = derive_consts(args);
-    auto ev = [&](int layer, int kind) { return pool->events[size_t(layer) * EV_PER_LAYER + kind]; };
-    std::vector<std::vector<lema_adamw_seg>> dev_segs(nlayers), host_segs(nlayers);
-    double h2d_bytes = 0, d2h_bytes = 0;
-    hipStream_t d2h_stream = pool->writeback ? pool->writeback : pool->copy;
-
-    auto copy_back = [&](int j) -> lema_status {
-        hipError_t err = hipStreamWaitEvent(d2h_stream, ev(j, EV_K_END), 0);
-        if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_BEGIN), d2h_stream);
-        if (err == hipSuccess) err = enqueue_writeback(dev_segs[j], host_segs[j], d2h_stream, &d2h_bytes);
-        if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_END), d2h_stream);
-        return err == hipSuccess ? LEMA_OK : hip_failed(err);
-    };
-
-    for (int32_t i = 0; i < nlayers; ++i) {
-        const lema_layer &L = layers[i];
-        char *slot = pool->base + size_t(i % pool->nslots) * pool->slot_bytes;
-        slot_segments(L, slot, &dev_segs[i]);
-        nonempty_segments(L, &host_segs[i]);
-
-        // host -> slot; with a separate write-back stream the slot must first
-        // have been copied back from its previous occupant
-        e = hipSuccess;
-        if (pool->writeback && i >= pool->nslots)
-            e = hipStreamWaitEvent(pool->copy, ev(i - pool->nslots, EV_D2H_END), 0);
-        if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
-        if (e == hipSuccess) e = enqueue_upload(host_segs[i], dev_segs[i], pool->copy, &h2d_bytes);
-        if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
-        if (e != hipSuccess) return hip_failed(e);
-
-        // the step on the slot
-        e = hipStreamWaitEvent(pool->compute, ev(i, EV_H2D_END), 0);
-        if (e == hipSuccess) e = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
-        if (e != hipSuccess) return hip_failed(e);
-        std::vector<SegRec> recs;
-        adamw_records(dev_segs[i].data(), int32_t(dev_segs[i].size()), &recs, nullptr);
-        st = launch_adamw_recs(recs, consts, kGradBf16, pool->compute);
-        if (st != LEMA_OK) return st;
-        e = hipEventRecord(ev(i, EV_K_END), pool->compute);
-        if (e != hipSuccess) return hip_failed(e);
-
-        // slot -> host for the previous layer, behind this layer's upload
-        if (i >= 1) {
-            st = copy_back(i - 1);
-            if (st != LEMA_OK) return st;
-        }
-    }
-    st = copy_back(nlayers - 1);
-    if (st != LEMA_OK) return st;
-    e = hipEventSynchronize(ev(nlayers - 1, EV_D2H_END));
-    if (e != hipSuccess) return hip_failed(e);
-
-    if (stats) {
-        fill_stats(pool, nlayers, h2d_bytes, d2h_bytes, stats);
-        stats->call_ms = std::chrono::duration<double, std::milli>(
-                             std::chrono::steady_clock::now() - call_start).count();
-    }
-    return LEMA_OK;
+    return run_direct(pool, plans, stats);
 }
 
 lema_status lema_slot_stream_staged(lema_slot_pool *pool, const lema_layer *layers,
                                     int32_t nlayers, const lema_adamw_args *args,
                                     int32_t host_threads, lema_stream_stats *stats) {
     std::vector<Span> spans;
-    lema_status st = validate_layers(pool, layers, nlayers, args, &spans);
+    std::vector<LayerPlan> plans;
+    lema_status st = validate_layers(pool, layers, nlayers, args, &spans, &plans);
     if (st != LEMA_OK) return st;
     if (host_threads < 0 || host_threads > 256) return LEMA_ERR_SIZE;
-    if (nlayers == 0) {
-        if (stats) *stats = lema_stream_stats{};
-        return LEMA_OK;
-    }
-    int threads = host_threads;
-    if (threads == 0) {
-        const unsigned hc = std::thread::hardware_concurrency();
-        threads = int(std::min(16u, hc == 0 ? 4u : hc));
-    }
-    const auto call_start = std::chrono::steady_clock::now();
+    return run_staged(pool, plans, host_threads, stats);
+}
 
-    std::lock_guard<std::mutex> lock(pool->mu);
-    int cur = 0;
-    hipError_t e = hipGetDevice(&cur);
-    if (e != hipSuccess) return hip_failed(e);
-    if (cur != pool->device) return LEMA_ERR_HIP;
-    for (int b = 0; b < 2; ++b) {
-        if (pool->staging[b] == nullptr) {
-            e = hipHostMalloc(reinterpret_cast<void **>(&pool->staging[b]), pool->slot_bytes,
-                              hipHostMallocDefault);
-            if (e != hipSuccess) {
-                pool->staging[b] = nullptr;
-                return hip_failed(e);
-            }
-        }
-    }
-    st = ensure_events(pool, size_t(nlayers) * EV_PER_LAYER);
+lema_status lema_slot_stream_q8(lema_slot_pool *pool, const lema_layer_q8 *layers,
+                                int32_t nlayers, const lema_adamw_args *args,
+                                int32_t moment_dtype, int32_t staged, int32_t host_threads,
+                                lema_stream_stats *stats) {
+    std::vector<Span> spans;
+    std::vector<LayerPlan> plans;
+    lema_status st = validate_layers_q8(pool, layers, nlayers, args, moment_dtype, &spans, &plans);
     if (st != LEMA_OK) return st;
-
-    const AdamwConsts consts = derive_consts(args);
-    auto ev = [&](int layer, int kind) { return pool->events[size_t(layer) * EV_PER_LAYER + kind]; };
-    std::vector<std::vector<lema_adamw_seg>> dev_segs(nlayers), stage_segs(nlayers),
-        host_segs(nlayers);
-    double h2d_bytes = 0, d2h_bytes = 0, in_ms = 0, out_ms = 0;
-    hipStream_t d2h_stream = pool->writeback ? pool->writeback : pool->copy;
-    std::vector<CopyItem> items;
-    using clock = std::chrono::steady_clock;
-
-    // Layer i goes caller memory -> staging[i % 2] -> slot[i % 2] -> staging[i % 2]
-    // -> caller memory.  Layer i + 2 reuses both only after the host has
-    // copied layer i out of staging, which itself waited for its write-back.
-    auto stage_in_and_enqueue = [&](int i) -> lema_status {
-        const lema_layer &L = layers[i];
-        const int b = i % 2;
-        slot_segments(L, pool->base + size_t(b) * pool->slot_bytes, &dev_segs[i]);
-        slot_segments(L, pool->staging[b], &stage_segs[i]);
-        nonempty_segments(L, &host_segs[i]);
-        staging_items(host_segs[i], stage_segs[i], true, &items);
-        const auto t0 = clock::now();
-        parallel_copy(items, threads);
-        in_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
-
-        hipError_t err = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
-        if (err == hipSuccess) err = enqueue_upload(stage_segs[i], dev_segs[i], pool->copy, &h2d_bytes);
-        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
-        if (err == hipSuccess) err = hipStreamWaitEvent(pool->compute, ev(i, EV_H2D_END), 0);
-        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
-        if (err != hipSuccess) return hip_failed(err);
-        std::vector<SegRec> recs;
-        adamw_records(dev_segs[i].data(), int32_t(dev_segs[i].size()), &recs, nullptr);
-        lema_status s2 = launch_adamw_recs(recs, consts, kGradBf16, pool->compute);
-        if (s2 != LEMA_OK) return s2;
-        err = hipEventRecord(ev(i, EV_K_END), pool->compute);
-        if (err == hipSuccess) err = hipStreamWaitEvent(d2h_stream, ev(i, EV_K_END), 0);
-        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_D2H_BEGIN), d2h_stream);
-        if (err == hipSuccess) err = enqueue_writeback(dev_segs[i], stage_segs[i], d2h_stream, &d2h_bytes);
-        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_D2H_END), d2h_stream);
-        return err == hipSuccess ? LEMA_OK : hip_failed(err);
-    };
-    auto wait_and_stage_out = [&](int i) -> lema_status {
-        hipError_t err = hipEventSynchronize(ev(i, EV_D2H_END));
-        if (err != hipSuccess) return hip_failed(err);
-        staging_items(host_segs[i], stage_segs[i], false, &items);
-        const auto t0 = clock::now();
-        parallel_copy(items, threads);
-        out_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
-        return LEMA_OK;
-    };
-
-    for (int i = 0; i < std::min(nlayers, 2); ++i) {
-        st = stage_in_and_enqueue(i);
-        if (st != LEMA_OK) return st;
+    if (staged) {
+        if (host_threads < 0 || host_threads > 256) return LEMA_ERR_SIZE;
+        return run_staged(pool, plans, host_threads, stats);
     }
-    for (int i = 0; i < nlayers; ++i) {
-        st = wait_and_stage_out(i);
-        if (st != LEMA_OK) return st;
-        if (i + 2 < nlayers) {
-            st = stage_in_and_enqueue(i + 2);
-            if (st != LEMA_OK) return st;
-        }
-    }
-
-    if (stats) {
-        fill_stats(pool, nlayers, h2d_bytes, d2h_bytes, stats);
-        stats->host_in_ms = in_ms;
-        stats->host_out_ms = out_ms;
-        stats->call_ms = std::chrono::duration<double, std::milli>(clock::now() - call_start).count();
-    }
-    return LEMA_OK;
+    st = check_pinned(spans);
+    if (st != LEMA_OK) return st;
+    return run_direct(pool, plans, stats);
 }
 
 }  // extern "C"

@@ -379,3 +379,35 @@ def test_llama7b_layer_q8_accumulate_then_step(L):
         compare_codes(acc.codes, ref_q, f"{label}.acc")
         compare_f32(to_np(acc.scale), ref_s, f"{label}.acc_scale")
         c.check(consts, label)
+
+
+def test_llama7b_lora_r16_q8_full(L):
+    """The 448 rank-16 LoRA adapters with int8 moments: A matrices have rows
+    of 4096 or 11,008, B matrices rows of 16 (256 rows per workgroup, one lane
+    per row); every element checked."""
+    w = synth.WORKLOADS["llama7b_lora_r16"]
+    cases = _workload_q8(L, w, last_dim, delta=True)
+    step(L, cases, w.step)
+    torch.cuda.synchronize()
+    consts = oracle_consts(HP, w.step)
+    for i, c in enumerate(cases):
+        c.check(consts, f"lora{i}")
+
+
+def test_gpt2_cattn_q8_full(L):
+    """GPT-2 c_attn of the first two layers with int8 moments from a fresh
+    state at t = 1 (all-zero rows to start); the 1-D biases are one row each."""
+    w = synth.WORKLOADS["gpt2_cattn_first2"]
+    cases = []
+    for i, (label, shape) in enumerate(w.segments):
+        c = Case(L, w.numels[i], shape[-1], 300000 + i, delta=True)
+        zq = (np.zeros(c.n, np.int8), np.zeros(-(-c.n // c.row_len), np.float32))
+        c.mq, c.vq = (zq[0].copy(), zq[1].copy()), (zq[0].copy(), zq[1].copy())
+        c.m = L.Q8(up(c.mq[0]), up(c.mq[1]), c.row_len)
+        c.v = L.Q8(up(c.vq[0]), up(c.vq[1]), c.row_len)
+        cases.append(c)
+    step(L, cases, 1)
+    torch.cuda.synchronize()
+    consts = oracle_consts(HP, 1)
+    for i, c in enumerate(cases):
+        c.check(consts, f"gpt2_{i}")
