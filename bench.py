@@ -559,17 +559,27 @@ def merge_bench(torch, L, synth, a):
 # ------------------------------------------------------------ streamed
 
 def slot_stream_bench(torch, L, synth, a):
-    """The whole 7B shape in page-locked host memory, streamed per layer."""
+    """The whole 7B shape in host memory, streamed per layer: fp32 master, m
+    and v, or with --q8 int8 moments with row scales (README "Quantization":
+    quantized states stay quantized in RAM)."""
     w = synth.WORKLOADS["llama7b_full"]
     hp = synth.HPARAMS
+    q8 = a.q8
+    row_len = lambda i: w.segments[i][1][-1]
+    rows = lambda i: -(-w.numels[i] // row_len(i))
     # the 34 loads: embedding, 32 decoder layers, final norm + LM head
     loads = [[0]] + [list(range(1 + 9 * l, 10 + 9 * l)) for l in range(32)] + [[289, 290]]
     requested = len(loads)
     if a.layers:
         loads = loads[:a.layers]
     align = lambda x: (x + 255) // 256 * 256
-    slot_bytes = max(sum(align(4 * w.numels[i]) * 3 + align(2 * w.numels[i]) * 2 for i in ld)
-                     for ld in loads)
+    if q8:
+        slot_bytes = max(sum(align(4 * w.numels[i]) + 2 * (align(w.numels[i]) + align(4 * rows(i)))
+                             + align(2 * w.numels[i]) * 2 for i in ld) for ld in loads)
+    else:
+        slot_bytes = max(sum(align(4 * w.numels[i]) * 3 + align(2 * w.numels[i]) * 2 for i in ld)
+                         for ld in loads)
+    host_bpp = 10 if q8 else 16
 
     # device side first: the pool's slots, then the standalone pinned copy
     # ceilings (half a slot each way); host staging comes last because the
@@ -590,7 +600,7 @@ def slot_stream_bench(torch, L, synth, a):
     budget = host_gib * (1 << 30)
     alloc = (lambda n, dt: torch.empty(n, dtype=dt)) if a.staged else L.pinned_empty
     for li, ld in enumerate(loads):
-        need = 16 * sum(w.numels[i] for i in ld)
+        need = host_bpp * sum(w.numels[i] for i in ld)
         if staged_bytes + need > budget:
             print(f"bench.py: host budget {host_gib} GiB reached after {len(layers)} loads",
                   file=sys.stderr, flush=True)
@@ -600,13 +610,26 @@ def slot_stream_bench(torch, L, synth, a):
             for i in ld:
                 st = synth.make_segment_state(w, i, "cuda")
                 n = w.numels[i]
+                if q8:
+                    dm, dv = L.Q8.empty(n, row_len(i)), L.Q8.empty(n, row_len(i))
+                    L.quantize_rows([(st["m"], dm), (st["v"], dv)])
+                    tensors = (("master", st["master"]), ("mc", dm.codes), ("ms", dm.scale),
+                               ("vc", dv.codes), ("vs", dv.scale), ("g", st["grads"][0]))
+                else:
+                    tensors = (("master", st["master"]), ("m", st["m"]), ("v", st["v"]),
+                               ("g", st["grads"][0]))
                 host = {}
-                for k, t in (("master", st["master"]), ("m", st["m"]), ("v", st["v"]),
-                             ("g", st["grads"][0])):
-                    host[k] = alloc(n, t.dtype)
+                for k, t in tensors:
+                    host[k] = alloc(t.numel(), t.dtype)
                     host[k].copy_(t)
-                segs.append(L.AdamwSegment(host["master"], host["m"], host["v"], host["g"],
-                                           alloc(n, torch.bfloat16)))
+                if q8:
+                    segs.append(L.AdamwQ8Segment(
+                        host["master"], L.Q8(host["mc"], host["ms"], row_len(i)),
+                        L.Q8(host["vc"], host["vs"], row_len(i)), host["g"],
+                        alloc(n, torch.bfloat16)))
+                else:
+                    segs.append(L.AdamwSegment(host["master"], host["m"], host["v"], host["g"],
+                                               alloc(n, torch.bfloat16)))
                 del st
         except (L.LemaError, RuntimeError) as e:
             del segs
@@ -622,13 +645,16 @@ def slot_stream_bench(torch, L, synth, a):
     setup_s = time.perf_counter() - t0
     P = sum(w.numels[i] for ld in loads for i in ld)
 
+    R = sum(rows(i) for ld in loads for i in ld)
+
     steps = max(1, min(a.steps, 3))
     stats = []
     kw = dict(staged=a.staged, host_threads=a.host_threads)
-    pool.stream(layers, step=w.step, **kw, **hp)            # warm-up step
+    run = pool.stream_q8 if q8 else pool.stream
+    run(layers, step=w.step, **kw, **hp)                     # warm-up step
     print("bench.py: warm-up streamed step done", file=sys.stderr, flush=True)
     for k in range(steps):
-        stats.append(pool.stream(layers, step=w.step + 1 + k, **kw, **hp))
+        stats.append(run(layers, step=w.step + 1 + k, **kw, **hp))
         print(f"bench.py: streamed step {k + 1}/{steps}: {stats[-1]['call_ms']:.0f} ms",
               file=sys.stderr, flush=True)
     pool.close()
@@ -648,14 +674,17 @@ def slot_stream_bench(torch, L, synth, a):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 arithmetic; int8 moments" if q8 else "f32",
         "data": "synthetic",
         "config": {"workload": "llama7b_full_streamed", "loads": len(loads),
                    "loads_requested": requested, "params": P, "slots": 2,
                    "slot_bytes": slot_bytes, "grad": "bf16", "delta": False,
                    "copy_streams": 2 if a.duplex else 1, "step_t": w.step,
                    "host_memory": "pageable, staged" if a.staged else "page-locked",
-                   "host_state_bytes": 16 * P, "setup_s": setup_s},
+                   "moments": "int8 codes + fp32 scale per row" if q8 else "fp32",
+                   "host_state_bytes": host_bpp * P + (8 * R if q8 else 0),
+                   "pcie_bytes_per_param_each_way": (8 + 8 * R / P) if q8 else 14,
+                   "setup_s": setup_s},
         "stream": {"h2d_gbps": s0["h2d_bytes"] / (s0["h2d_ms"] * 1e-3) / 1e9,
                    "d2h_gbps": s0["d2h_bytes"] / (s0["d2h_ms"] * 1e-3) / 1e9,
                    "standalone_h2d_gbps": h2d_gbps, "standalone_d2h_gbps": d2h_gbps,
@@ -664,7 +693,8 @@ def slot_stream_bench(torch, L, synth, a):
                    "host_in_ms": s0["host_in_ms"], "host_out_ms": s0["host_out_ms"],
                    "last_kernel_ms": s0["last_kernel_ms"],
                    "exposed_ms": s0["wall_ms"] - s0["copy_busy_ms"],
-                   "kernel_hbm_gbps": 28 * P / (s0["kernel_ms"] * 1e-3) / 1e9,
+                   "kernel_hbm_gbps": ((16 * P + 16 * R) if q8 else 28 * P)
+                   / (s0["kernel_ms"] * 1e-3) / 1e9,
                    "ms_per_param_billion": wall / (P / 1e9),
                    "projected_full_7b_ms": wall * full_params / P},
     }
