@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--fused-last", action="store_true",
                     help="multi-micro-batch workloads: fold the last micro-batch into the step "
                          "(lema_adamw_step_accum) instead of a separate accumulation pass")
+    ap.add_argument("--resident-microbatches", action="store_true",
+                    help="multi-micro-batch workloads: all K bf16 gradients stay resident and the "
+                         "step sums them in fp32 (lema_adamw_step_microbatches), no accumulator")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-gib", type=float, default=4.0, help="size of the copy-ceiling test")
@@ -171,11 +174,15 @@ def resident_bench(torch, L, synth, a):
     hp = synth.HPARAMS
     P = w.params
     K = w.microbatches
-    grad_f32 = K > 1
-    fused = a.fused_last and K > 1
+    resident_mb = a.resident_microbatches and K > 1
+    grad_f32 = K > 1 and not resident_mb
+    fused = a.fused_last and K > 1 and not resident_mb
     step_bytes = adamw_bytes_per_param(grad_f32, delta) + (2 if fused else 0)
+    if resident_mb:
+        step_bytes += 2 * (K - 1)          # K bf16 gradients instead of one
     accum_launches = K - 1 if fused else K
-    accum_bytes = (ACCUM_BYTES_OVERWRITE + (accum_launches - 1) * ACCUM_BYTES) if K > 1 else 0
+    accum_bytes = (ACCUM_BYTES_OVERWRITE + (accum_launches - 1) * ACCUM_BYTES) \
+        if K > 1 and not resident_mb else 0
     per_step = P * (step_bytes + accum_bytes)
 
     # state resident in HBM; small workloads get rotated copies so that the
@@ -188,8 +195,10 @@ def resident_bench(torch, L, synth, a):
             st = synth.make_segment_state(w, i, dev, with_orig=delta)
             n = w.numels[i]
             grad = torch.empty(n, device=dev) if grad_f32 else st["grads"][0]
-            if grad_f32:
+            if grad_f32 or resident_mb:
                 accs.append((grad, st["grads"]))
+            if resident_mb:
+                grad = None
             segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], grad,
                                        torch.empty(n, dtype=torch.bfloat16, device=dev),
                                        st.get("orig"),
@@ -200,7 +209,7 @@ def resident_bench(torch, L, synth, a):
     copy_gbps = copy_ceiling(torch, L, a.copy_gib)
 
     accum_plans = [[L.AccumPlan([L.AccumSegment(acc, g[j]) for acc, g in accs])
-                    for j in range(accum_launches)] for _, accs in sets]
+                    for j in range(accum_launches)] for _, accs in sets] if grad_f32 else []
 
     def accumulate(k):
         for j, plan in enumerate(accum_plans[k % nsets]):
@@ -208,14 +217,15 @@ def resident_bench(torch, L, synth, a):
 
     # the step's arguments are marshalled once (a training loop's usage), so
     # the timed region holds the library call, not Python argument packing
-    plans = [L.AdamwPlan(segs, last_grads=[g[K - 1] for _, g in accs] if fused else None)
+    plans = [L.AdamwPlan(segs, last_grads=[g[K - 1] for _, g in accs] if fused else None,
+                         microbatch_grads=[g for _, g in accs] if resident_mb else None)
              for segs, accs in sets]
 
     def step(k):
         plans[k % nsets].step(step=w.step, **hp)
 
     def whole(k):
-        if K > 1:
+        if grad_f32:
             accumulate(k)
         step(k)
 
@@ -232,7 +242,7 @@ def resident_bench(torch, L, synth, a):
     ms = sum(step_ms) / len(step_ms)
 
     # the AdamW kernel alone, one launch per event pair
-    if K > 1:
+    if grad_f32:
         adamw_ms_list = timed_events(torch, stream, step, a.steps)
         accum_ms_list = timed_events(torch, stream, accumulate, a.steps)
     else:
@@ -249,7 +259,8 @@ def resident_bench(torch, L, synth, a):
     pipelined_ms = start.elapsed_time(stop) / a.steps
 
     gbps = per_step / (ms * 1e-3) / 1e9
-    key = f"{a.workload}:{'delta' if delta else 'nodelta'}" + (":fused" if fused else "")
+    key = f"{a.workload}:{'delta' if delta else 'nodelta'}" + (":fused" if fused else "") + \
+        (":resident_mb" if resident_mb else "")
     info = L.device_info()
     line = {
         "metric": METRIC,
@@ -269,8 +280,10 @@ def resident_bench(torch, L, synth, a):
             "description": w.description,
             "params": P,
             "segments": len(w.segments),
-            "grad": ("fp32 accumulator of 8 bf16 micro-batches" + (", last one folded into "
-                     "the step" if fused else "")) if K > 1 else "bf16",
+            "grad": (f"{K} resident bf16 micro-batches summed in fp32 inside the step"
+                     if resident_mb else ("fp32 accumulator of 8 bf16 micro-batches" +
+                                          (", last one folded into the step" if fused else "")))
+            if K > 1 else "bf16",
             "delta": delta,
             "step_t": w.step,
             "bytes_per_param": step_bytes + accum_bytes,
@@ -302,12 +315,16 @@ def resident_bench(torch, L, synth, a):
                                 "frac": acc_gbps / HBM_PEAK_GBPS,
                                 "algorithmic_bytes_per_step": P * accum_bytes}
     if not a.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(sets[0][0], w, hp, delta, a.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(sets[0][0], w, hp, delta, a.cpu_seconds,
+                                            sets[0][1][0][1] if resident_mb else None)
     return line
 
 
-def cpu_baseline(segs, w, hp, delta, seconds):
-    """Time the oracle (as it stands) on the first tensor of the workload."""
+def cpu_baseline(segs, w, hp, delta, seconds, microbatches=None):
+    """Time the oracle (as it stands) on the first tensor of the workload;
+    with `microbatches` (its resident bf16 gradients) each timed step is the
+    oracle's accumulation of them followed by the step."""
+    import numpy as np
     import oracle
     import torch
 
@@ -319,15 +336,25 @@ def cpu_baseline(segs, w, hp, delta, seconds):
 
     s = segs[0]
     master, m, v = host_copy(s.master), host_copy(s.exp_avg), host_copy(s.exp_avg_sq)
-    grad = host_copy(s.grad)
     orig = host_copy(s.orig) if delta else None
     n = master.shape[0]
     c = oracle.adamw_constants(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
                                hp["weight_decay"], w.step)
-    oracle.adamw_step(master, m, v, grad, c, orig=orig)        # warm-up pass
+    if microbatches is None:
+        grad = host_copy(s.grad)
+        one_step = lambda: oracle.adamw_step(master, m, v, grad, c, orig=orig)
+    else:
+        gs = [host_copy(g) for g in microbatches]
+        acc = np.empty(n, np.float32)
+
+        def one_step():
+            for k, g in enumerate(gs):
+                oracle.grad_accum(acc, g, overwrite=(k == 0))
+            oracle.adamw_step(master, m, v, acc, c, orig=orig)
+    one_step()                                                 # warm-up pass
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.adamw_step(master, m, v, grad, c, orig=orig)
+        one_step()
         reps += 1
         el = time.perf_counter() - t0
         if el >= seconds:
@@ -335,7 +362,9 @@ def cpu_baseline(segs, w, hp, delta, seconds):
     return {"value": n * reps / el, "unit": "params/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{w.segments[0][0]} ({n} params), {reps} oracle steps in {el:.1f} s, "
-                      f"delta {'on' if delta else 'off'}; C oracle, OpenMP"}
+                      f"delta {'on' if delta else 'off'}"
+                      + (f", each with {len(microbatches)} accumulations" if microbatches else "")
+                      + "; C oracle, OpenMP"}
 
 
 # ------------------------------------------------------------- int8

@@ -158,6 +158,31 @@ lema_status lema_adamw_step(const lema_adamw_seg *segs, int32_t nseg,
 lema_status lema_adamw_step_accum(const lema_adamw_seg *segs, const uint16_t *const *last_bf16,
                                   int32_t nseg, const lema_adamw_args *args, void *stream);
 
+/*
+ * The step on the fp32 sum of K bf16 micro-batch gradients that are all
+ * resident at once: per element g = f32(g_1), then g = g + f32(g_k) for
+ * k = 2..K in order, the additions lema_grad_accum performs, so the results
+ * are bit-identical to K lema_grad_accum calls (the first overwriting)
+ * followed by lema_adamw_step on the accumulator (LEMA README, "Selective
+ * Full Fine-Tuning": fp32 gradient accumulation feeding the per-layer AdamW
+ * step).  The sum stays in registers: no accumulator array is read or
+ * written, so one call moves 2K + 26 B per parameter (2K + 32 with delta)
+ * instead of the 10 B per micro-batch and extra accumulator read of the
+ * separate calls.  For callers that keep the micro-batch gradients.
+ *   segs  : as for lema_adamw_step, with segs[i].grad NULL (LEMA_ERR_NULL
+ *           otherwise)
+ *   grads : host array of nseg * nmb device pointers; grads[i * nmb + k] is
+ *           the bf16 gradient of micro-batch k + 1 for segment i
+ *   nmb   : K, 1 .. LEMA_MAX_MICROBATCHES (else LEMA_ERR_SIZE)
+ *   args  : args->grad_dtype must be LEMA_GRAD_BF16 (else LEMA_ERR_DTYPE)
+ * Errors: as lema_adamw_step.
+ */
+#define LEMA_MAX_MICROBATCHES 16
+lema_status lema_adamw_step_microbatches(const lema_adamw_seg *segs,
+                                         const uint16_t *const *grads, int32_t nseg,
+                                         int32_t nmb, const lema_adamw_args *args,
+                                         void *stream);
+
 /* ------------------------------------------------ gradient accumulation */
 
 /* One accumulator and the bf16 micro-batch gradient added into it. */

@@ -29,6 +29,7 @@ LEMA_GRAD_Q8 = 2
 LEMA_STATE_FP32 = 0
 LEMA_STATE_Q8 = 1
 LEMA_Q8_MAX_ROW = 16384
+LEMA_MAX_MICROBATCHES = 16
 
 vp = ctypes.c_void_p
 i32 = ctypes.c_int32
@@ -99,6 +100,8 @@ SIGNATURES = [
     ("lema_adamw_step", i32, [ctypes.POINTER(AdamwSeg), i32, ctypes.POINTER(AdamwArgs), vp]),
     ("lema_adamw_step_accum", i32, [ctypes.POINTER(AdamwSeg), ctypes.POINTER(vp), i32,
                                     ctypes.POINTER(AdamwArgs), vp]),
+    ("lema_adamw_step_microbatches", i32, [ctypes.POINTER(AdamwSeg), ctypes.POINTER(vp), i32, i32,
+                                           ctypes.POINTER(AdamwArgs), vp]),
     ("lema_grad_accum", i32, [ctypes.POINTER(AccumSeg), i32, i32, vp]),
     ("lema_merge_delta", i32, [ctypes.POINTER(MergeSeg), i32, vp]),
     ("lema_adamw_step_q8", i32, [ctypes.POINTER(AdamwQ8Seg), i32, ctypes.POINTER(AdamwArgs), i32,

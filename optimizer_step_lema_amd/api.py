@@ -51,18 +51,19 @@ def _check(t: Optional[torch.Tensor], dtype, n: int, name: str, where: str = "cu
 
 @dataclass
 class AdamwSegment:
-    """One trainable tensor: fp32 master/m/v, bf16 or fp32 grad, bf16 weight out."""
+    """One trainable tensor: fp32 master/m/v, bf16 or fp32 grad, bf16 weight out.
+    `grad` is None when the step takes resident micro-batch gradients."""
     master: torch.Tensor
     exp_avg: torch.Tensor
     exp_avg_sq: torch.Tensor
-    grad: torch.Tensor
+    grad: Optional[torch.Tensor]
     weight: torch.Tensor
     orig: Optional[torch.Tensor] = None
     delta: Optional[torch.Tensor] = None
 
     def to_c(self, where: str = "cuda") -> N.AdamwSeg:
         n = self.master.numel()
-        gdt = self.grad.dtype
+        gdt = torch.bfloat16 if self.grad is None else self.grad.dtype
         if gdt not in (torch.bfloat16, torch.float32):
             raise TypeError(f"grad: expected bfloat16 or float32, got {gdt}")
         return N.AdamwSeg(
@@ -82,7 +83,7 @@ def _args(lr, beta1, beta2, eps, weight_decay, step, grad_dtype) -> N.AdamwArgs:
 
 
 def _grad_dtype(segments: Sequence[AdamwSegment]) -> int:
-    kinds = {s.grad.dtype for s in segments}
+    kinds = {torch.bfloat16 if s.grad is None else s.grad.dtype for s in segments}
     if len(kinds) > 1:
         raise TypeError("all segments of one call must share the gradient dtype")
     return N.LEMA_GRAD_FP32 if kinds == {torch.float32} else N.LEMA_GRAD_BF16
@@ -99,15 +100,41 @@ def adamw_constants(*, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, 
     return {name: np.float32(getattr(out, name)) for name, _ in N.AdamwConsts._fields_}
 
 
+def _microbatch_pointers(segments, microbatch_grads):
+    """Flat nseg * K pointer array of resident micro-batch gradients."""
+    if len(microbatch_grads) != len(segments):
+        raise ValueError("one list of micro-batch gradients per segment is required")
+    ks = {len(g) for g in microbatch_grads}
+    if len(ks) != 1:
+        raise ValueError("every segment needs the same number of micro-batches")
+    k = ks.pop()
+    ptrs = []
+    for i, (gs, s) in enumerate(zip(microbatch_grads, segments)):
+        if s.grad is not None:
+            raise ValueError(f"segment {i}: grad must be None with micro-batch gradients")
+        ptrs += [_check(g, torch.bfloat16, s.master.numel(), f"microbatch_grads[{i}][{j}]")
+                 for j, g in enumerate(gs)]
+    return (ctypes.c_void_p * max(1, len(ptrs)))(*ptrs), k
+
+
 def adamw_step(segments: Sequence[AdamwSegment], *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
                weight_decay=0.01, step, stream=None,
-               last_grads: Optional[Sequence[torch.Tensor]] = None) -> None:
+               last_grads: Optional[Sequence[torch.Tensor]] = None,
+               microbatch_grads: Optional[Sequence[Sequence[torch.Tensor]]] = None) -> None:
     """One AdamW step over `segments` on the GPU (asynchronous on `stream`).
 
     With `last_grads` (one bf16 tensor per segment) each segment's grad is an
     fp32 accumulator and the step adds the last micro-batch to it on the fly
-    (lema_adamw_step_accum); the accumulator is not updated.
+    (lema_adamw_step_accum); the accumulator is not updated.  With
+    `microbatch_grads` (per segment, the K bf16 micro-batch gradients; the
+    segments' grad None) the step sums them in fp32 in order
+    (lema_adamw_step_microbatches).
     """
+    if microbatch_grads is not None:
+        AdamwPlan(segments, microbatch_grads=microbatch_grads).step(
+            lr=lr, beta1=beta1, beta2=beta2, eps=eps, weight_decay=weight_decay, step=step,
+            stream=stream)
+        return
     lib = N.load()
     segs = (N.AdamwSeg * max(1, len(segments)))(*[s.to_c() for s in segments])
     args = _args(lr, beta1, beta2, eps, weight_decay, step, _grad_dtype(segments))
@@ -134,12 +161,18 @@ class AdamwPlan:
     """
 
     def __init__(self, segments: Sequence[AdamwSegment],
-                 last_grads: Optional[Sequence[torch.Tensor]] = None):
+                 last_grads: Optional[Sequence[torch.Tensor]] = None,
+                 microbatch_grads: Optional[Sequence[Sequence[torch.Tensor]]] = None):
         self.lib = N.load()
         self.segments = list(segments)
         self.n = len(self.segments)
         self.c_segs = (N.AdamwSeg * max(1, self.n))(*[s.to_c() for s in self.segments])
         self.grad_dtype = _grad_dtype(self.segments)
+        self.microbatch_grads = None if microbatch_grads is None else [list(g) for g in
+                                                                       microbatch_grads]
+        self.c_mb, self.nmb = (None, 0)
+        if self.microbatch_grads is not None:
+            self.c_mb, self.nmb = _microbatch_pointers(self.segments, self.microbatch_grads)
         self.last_grads = None if last_grads is None else list(last_grads)
         self.c_last = None
         if self.last_grads is not None:
@@ -152,7 +185,12 @@ class AdamwPlan:
     def step(self, *, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step,
              stream=None) -> None:
         args = _args(lr, beta1, beta2, eps, weight_decay, step, self.grad_dtype)
-        if self.c_last is None:
+        if self.c_mb is not None:
+            N.check(self.lib.lema_adamw_step_microbatches(self.c_segs, self.c_mb, self.n,
+                                                          self.nmb, ctypes.byref(args),
+                                                          _stream_handle(stream)),
+                    "lema_adamw_step_microbatches")
+        elif self.c_last is None:
             N.check(self.lib.lema_adamw_step(self.c_segs, self.n, ctypes.byref(args),
                                              _stream_handle(stream)), "lema_adamw_step")
         else:

@@ -22,6 +22,8 @@
 
 namespace lema {
 
+static_assert(kMaxMicrobatches == LEMA_MAX_MICROBATCHES, "micro-batch limit of header and kernel");
+
 // ------------------------------------------------------------ errors
 
 static thread_local int32_t t_last_hip_error = 0;
@@ -349,6 +351,26 @@ lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts
     });
 }
 
+lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<uint64_t> &lists,
+                                  int nmb, const AdamwConsts &c, hipStream_t stream) {
+    if (recs.empty()) return LEMA_OK;
+    if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
+    bool with_delta = false;
+    const int n = static_cast<int>(recs.size());
+    for (int i = 0; i < n; ++i) {
+        with_delta |= recs[i].p[6] != 0;
+        recs[i].p[3] = table_bytes(n) + sizeof(uint64_t) * size_t(nmb) * size_t(i);
+    }
+    TableBuild tb;
+    build_table(recs, &tb);
+    tb.bytes.resize(table_bytes(n) + sizeof(uint64_t) * lists.size());
+    std::memcpy(tb.bytes.data() + table_bytes(n), lists.data(), sizeof(uint64_t) * lists.size());
+    return launch_on_table(tb.bytes, stream, [&](const void *table) {
+        return launch_adamw(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), kGradBf16Sum,
+                            with_delta, c, stream, nmb);
+    });
+}
+
 lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
                               hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
@@ -469,6 +491,57 @@ lema_status lema_adamw_step_accum(const lema_adamw_seg *segs, const uint16_t *co
     adamw_records(segs, nseg, &recs, last_bf16);
     return launch_adamw_recs(recs, derive_consts(args), kGradF32PlusBf16,
                              static_cast<hipStream_t>(stream));
+}
+
+lema_status lema_adamw_step_microbatches(const lema_adamw_seg *segs,
+                                         const uint16_t *const *grads, int32_t nseg,
+                                         int32_t nmb, const lema_adamw_args *args,
+                                         void *stream) {
+    lema_status st = check_hparams(args);
+    if (st != LEMA_OK) return st;
+    if (args->grad_dtype != LEMA_GRAD_BF16) return LEMA_ERR_DTYPE;
+    if (nmb < 1 || nmb > kMaxMicrobatches) return LEMA_ERR_SIZE;
+    if (nseg < 0) return LEMA_ERR_SIZE;
+    if (nseg > 0 && (segs == nullptr || grads == nullptr)) return LEMA_ERR_NULL;
+    // validate as one-micro-batch segments on the first micro-batch, then
+    // add the other micro-batches' spans
+    std::vector<lema_adamw_seg> first(segs, segs + nseg);
+    for (int32_t i = 0; i < nseg; ++i) {
+        if (first[i].grad != nullptr) return LEMA_ERR_NULL;   // gradients come from `grads`
+        first[i].grad = grads[size_t(i) * nmb];
+    }
+    std::vector<Span> spans;
+    st = validate_adamw_segs(first.data(), nseg, LEMA_GRAD_BF16, true, &spans);
+    if (st != LEMA_OK) return st;
+    std::vector<SegRec> recs;
+    std::vector<uint64_t> lists;
+    for (int32_t i = 0; i < nseg; ++i) {
+        const lema_adamw_seg &s = first[i];
+        if (s.numel == 0) continue;
+        uint64_t any = 0;
+        for (int32_t j = 0; j < nmb; ++j) {
+            const uint16_t *g = grads[size_t(i) * nmb + j];
+            if (g == nullptr) return LEMA_ERR_NULL;
+            if (reinterpret_cast<uintptr_t>(g) & 1) return LEMA_ERR_ALIGN;
+            if (j > 0) add_span(spans, g, s.numel, 2, false);
+            any |= reinterpret_cast<uint64_t>(g);
+            lists.push_back(reinterpret_cast<uint64_t>(g));
+        }
+        SegRec r{};
+        r.p[0] = reinterpret_cast<uint64_t>(s.master);
+        r.p[1] = reinterpret_cast<uint64_t>(s.exp_avg);
+        r.p[2] = reinterpret_cast<uint64_t>(s.exp_avg_sq);
+        r.p[4] = reinterpret_cast<uint64_t>(s.weight_bf16);
+        r.p[5] = reinterpret_cast<uint64_t>(s.orig_bf16);
+        r.p[6] = reinterpret_cast<uint64_t>(s.delta);
+        r.p[7] = any;
+        r.numel = s.numel;
+        r.reserved = nmb;
+        recs.push_back(r);
+    }
+    if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
+    return launch_adamw_sum_recs(recs, lists, nmb, derive_consts(args),
+                                 static_cast<hipStream_t>(stream));
 }
 
 lema_status lema_grad_accum(const lema_accum_seg *segs, int32_t nseg, int32_t overwrite,

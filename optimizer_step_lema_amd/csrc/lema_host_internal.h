@@ -61,6 +61,10 @@ lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts
                               GradMode grad_mode, hipStream_t stream);
 lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
                               hipStream_t stream);
+// kGradBf16Sum: `lists` holds each record's `nmb` micro-batch pointers in
+// record order; they are appended to the table and the records point there.
+lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<uint64_t> &lists,
+                                  int nmb, const AdamwConsts &c, hipStream_t stream);
 lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t stream);
 
 }  // namespace lema

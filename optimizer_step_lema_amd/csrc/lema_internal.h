@@ -38,7 +38,14 @@ enum GradMode : int {
     kGradBf16 = 0,         // grad: bf16 bits of one micro-batch
     kGradF32 = 1,          // grad: the fp32 accumulator
     kGradF32PlusBf16 = 2,  // grad: fp32 accumulator + f32(last bf16 micro-batch)
+    kGradBf16Sum = 3,      // grad: fp32 sum, in order, of K bf16 micro-batches
 };
+
+// kGradBf16Sum records: p[3] is the byte offset, from the start of the launch
+// table, of the segment's K micro-batch pointers (uint64 each, appended after
+// the records); p[7] is the OR of those pointers (for the alignment test);
+// `reserved` is K.
+constexpr int kMaxMicrobatches = 16;
 
 // The launch table in device memory is
 //   uint32_t tile_begin[nseg + 1]   (prefix sum of tiles per segment)
@@ -100,9 +107,10 @@ struct AdamwConsts {
 
 // Kernel launches (asynchronous on `stream`).  `table` is the device copy of
 // the launch table; one workgroup runs per tile 0 .. total_tiles-1.
+// `nmb` is the micro-batch count of kGradBf16Sum (ignored otherwise).
 hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles,
                         GradMode grad_mode, bool with_delta, const AdamwConsts &c,
-                        hipStream_t stream);
+                        hipStream_t stream, int nmb = 0);
 hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
                         bool overwrite, hipStream_t stream);
 hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream);

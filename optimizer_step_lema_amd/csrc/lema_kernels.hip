@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <utility>
 
 #include "lema_device.h"
 #include "lema_internal.h"
@@ -42,9 +43,12 @@ using namespace dev;
 
 // ------------------------------------------------------------- AdamW
 
-template <GradMode kMode, bool kDelta>
+// kNmb: the number of micro-batches of kGradBf16Sum (a compile-time count,
+// so that all their loads issue back to back); 0 for the other modes.
+template <GradMode kMode, bool kDelta, int kNmb>
 struct AdamwTile {
     AdamwConsts c;
+    const char *table;   // the launch table (micro-batch pointer lists live there)
 
     __device__ __forceinline__ void operator()(const SegRec &r, uint32_t local_tile) const {
         const uint64_t master = r.p[0], m = r.p[1], v = r.p[2], grad = r.p[3];
@@ -52,11 +56,11 @@ struct AdamwTile {
         const int64_t numel = r.numel;
         const int64_t base = int64_t(local_tile) * kTile;
 
-        constexpr bool kGradIsF32 = kMode != kGradBf16;
+        constexpr bool kGradIsF32 = kMode == kGradF32 || kMode == kGradF32PlusBf16;
         const bool has_delta = kDelta && delta != 0;
         const uint64_t fp32_bits = master | m | v | (kGradIsF32 ? grad : 0) | (has_delta ? delta : 0);
-        const uint64_t bf16_bits = (kGradIsF32 ? 0 : grad) | weight | (has_delta ? orig : 0) |
-                                   (kMode == kGradF32PlusBf16 ? last : 0);
+        const uint64_t bf16_bits = (kMode == kGradBf16 ? grad : 0) | weight | (has_delta ? orig : 0) |
+                                   (kMode == kGradF32PlusBf16 || kMode == kGradBf16Sum ? last : 0);
         const bool vector_ok = base + kTile <= numel && (fp32_bits & 15) == 0 && (bf16_bits & 7) == 0;
 
         if (vector_ok) {
@@ -70,6 +74,11 @@ struct AdamwTile {
         }
     }
 
+    // The K micro-batch pointers of a kGradBf16Sum segment.
+    __device__ __forceinline__ const uint64_t *microbatches(uint64_t list_offset) const {
+        return reinterpret_cast<const uint64_t *>(table + list_offset);
+    }
+
     // The gradient of 4 consecutive elements starting at vector index q.
     __device__ __forceinline__ f32x4 load_grad4(uint64_t grad, uint64_t last, int64_t q) const {
 #pragma clang fp contract(off)
@@ -78,6 +87,22 @@ struct AdamwTile {
             return f32x4{bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
         } else if constexpr (kMode == kGradF32) {
             return ld_nt<f32x4>(grad, q);
+        } else if constexpr (kMode == kGradBf16Sum) {
+            // every micro-batch's loads first, then the fp32 sum in micro-batch
+            // order, the first one widened exactly (lema_grad_accum's overwrite)
+            const uint64_t *mb = microbatches(grad);
+            u32x2 gb[kNmb];
+#pragma unroll
+            for (int k = 0; k < kNmb; ++k) gb[k] = ld_nt<u32x2>(mb[k], q);
+            f32x4 acc = {bf16_lo(gb[0].x), bf16_hi(gb[0].x), bf16_lo(gb[0].y), bf16_hi(gb[0].y)};
+#pragma unroll
+            for (int k = 1; k < kNmb; ++k) {
+                acc = f32x4{accum_elem(acc.x, bf16_lo(gb[k].x), false),
+                            accum_elem(acc.y, bf16_hi(gb[k].x), false),
+                            accum_elem(acc.z, bf16_lo(gb[k].y), false),
+                            accum_elem(acc.w, bf16_hi(gb[k].y), false)};
+            }
+            return acc;
         } else {
             // the last micro-batch's fp32 addition, as lema_grad_accum does it
             const f32x4 acc = ld_nt<f32x4>(grad, q);
@@ -150,7 +175,12 @@ struct AdamwTile {
                     g = bf16_one(as_global<gu16>(grad)[e]);
                 else if constexpr (kMode == kGradF32)
                     g = as_global<gfloat>(grad)[e];
-                else
+                else if constexpr (kMode == kGradBf16Sum) {
+                    const uint64_t *mb = microbatches(grad);
+                    g = bf16_one(as_global<gu16>(mb[0])[e]);
+                    for (int j = 1; j < kNmb; ++j)
+                        g = accum_elem(g, bf16_one(as_global<gu16>(mb[j])[e]), false);
+                } else
                     g = accum_elem(as_global<gfloat>(grad)[e], bf16_one(as_global<gu16>(last)[e]), false);
                 float w = as_global<gfloat>(master)[e];
                 float mm = as_global<gfloat>(m)[e];
@@ -166,10 +196,24 @@ struct AdamwTile {
     }
 };
 
-template <GradMode kMode, bool kDelta>
+template <GradMode kMode, bool kDelta, int kNmb = 0>
 __global__ __launch_bounds__(kBlock) void adamw_tile_kernel(const void *table, int nseg,
                                                             uint32_t tile0, AdamwConsts c) {
-    block_of_table<SegRec>(table, nseg, tile0, AdamwTile<kMode, kDelta>{c});
+    block_of_table<SegRec>(table, nseg, tile0,
+                           AdamwTile<kMode, kDelta, kNmb>{c, static_cast<const char *>(table)});
+}
+
+template <int kNmb>
+const void *sum_kernel(bool with_delta) {
+    return with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<kGradBf16Sum, true, kNmb>)
+                      : reinterpret_cast<const void *>(&adamw_tile_kernel<kGradBf16Sum, false, kNmb>);
+}
+
+// The kGradBf16Sum kernel for nmb micro-batches (1 .. kMaxMicrobatches).
+template <std::size_t... I>
+const void *pick_sum_kernel(int nmb, bool with_delta, std::index_sequence<I...>) {
+    const void *fns[] = {sum_kernel<int(I) + 1>(with_delta)...};
+    return fns[nmb - 1];
 }
 
 // ------------------------------------------------------ accumulation
@@ -310,7 +354,7 @@ __global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restr
 // directly instead of through the thread's sticky last-error slot.  Grids
 // larger than kMaxBlocksPerLaunch are split into consecutive launches.
 hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradMode grad_mode,
-                        bool with_delta, const AdamwConsts &c, hipStream_t stream) {
+                        bool with_delta, const AdamwConsts &c, hipStream_t stream, int nmb) {
     const void *fn;
 #define LEMA_PICK(M) with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<M, true>) \
                                 : reinterpret_cast<const void *>(&adamw_tile_kernel<M, false>)
@@ -318,6 +362,10 @@ hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradM
     case kGradBf16: fn = LEMA_PICK(kGradBf16); break;
     case kGradF32: fn = LEMA_PICK(kGradF32); break;
     case kGradF32PlusBf16: fn = LEMA_PICK(kGradF32PlusBf16); break;
+    case kGradBf16Sum:
+        if (nmb < 1 || nmb > kMaxMicrobatches) return hipErrorInvalidValue;
+        fn = pick_sum_kernel(nmb, with_delta, std::make_index_sequence<kMaxMicrobatches>{});
+        break;
     default: return hipErrorInvalidValue;
     }
 #undef LEMA_PICK

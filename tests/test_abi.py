@@ -233,3 +233,38 @@ def test_merge_validation(lib):
     assert lib.lema_merge_delta(ctypes.byref(s), 1, None) == N.LEMA_ERR_OVERLAP
     s = N.MergeSeg(1 << 32, 1 << 33, 1 << 34, -3)
     assert lib.lema_merge_delta(ctypes.byref(s), 1, None) == N.LEMA_ERR_SIZE
+
+
+def microbatch_call(lib, segs, grads, nmb, a=None):
+    arr = (N.AdamwSeg * max(1, len(segs)))(*segs)
+    ptrs = (ctypes.c_void_p * max(1, len(grads)))(*grads)
+    return lib.lema_adamw_step_microbatches(arr, ptrs, len(segs), nmb, ctypes.byref(a or args()),
+                                            None)
+
+
+def test_microbatch_step_validation(lib):
+    """lema_adamw_step_microbatches: K range, grad field NULL, every micro-batch
+    pointer present, aligned and not overlapping a written array."""
+    def seg():
+        s = fake_seg(1 << 32, 1000)
+        s.grad = 0
+        return s
+    grads = [(1 << 40) + k * (1 << 24) for k in range(3)]
+    assert microbatch_call(lib, [seg()], grads, 0) == N.LEMA_ERR_SIZE
+    assert microbatch_call(lib, [seg()], grads * 6, 17) == N.LEMA_ERR_SIZE
+    s = fake_seg(1 << 32, 1000)                           # grad must be NULL
+    assert microbatch_call(lib, [s], grads, 3) == N.LEMA_ERR_NULL
+    assert microbatch_call(lib, [seg()], grads, 3, args(grad_dtype=N.LEMA_GRAD_FP32)) == \
+        N.LEMA_ERR_DTYPE
+    assert microbatch_call(lib, [seg()], [grads[0], 0, grads[2]], 3) == N.LEMA_ERR_NULL
+    assert microbatch_call(lib, [seg()], [grads[0], grads[1] + 1, grads[2]], 3) == N.LEMA_ERR_ALIGN
+    s = seg()
+    assert microbatch_call(lib, [s], [grads[0], s.master + 8, grads[2]], 3) == N.LEMA_ERR_OVERLAP
+    arr = (N.AdamwSeg * 1)(seg())
+    assert lib.lema_adamw_step_microbatches(arr, None, 1, 3, ctypes.byref(args()), None) == \
+        N.LEMA_ERR_NULL
+    assert lib.lema_adamw_step_microbatches(None, None, 0, 3, ctypes.byref(args()), None) == \
+        N.LEMA_OK
+    z = seg()
+    z.numel = 0
+    assert microbatch_call(lib, [z], [0, 0, 0], 3) == N.LEMA_OK   # empty segment: no pointers needed

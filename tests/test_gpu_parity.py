@@ -483,6 +483,74 @@ def test_table_cache_beyond_capacity(L):
     compare_f32(to_np(b.exp_avg_sq), st["v"], "cache cap v")
 
 
+def _accumulate_then_step(snap, grads_np, consts, orig=None):
+    """The oracle's separate calls: K accumulations (the first overwriting),
+    then the step on the fp32 accumulator."""
+    acc = np.empty(len(snap["master"]), np.float32)
+    for k, g in enumerate(grads_np):
+        oracle.grad_accum(acc, g, overwrite=(k == 0))
+    return oracle_segment(snap["master"], snap["m"], snap["v"], acc, consts, orig)
+
+
+@pytest.mark.parametrize("nmb", [1, 2, 3, 8, 16])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_microbatch_sum_step(L, nmb, offset):
+    """lema_adamw_step_microbatches equals K accumulations then the step on
+    the accumulator, bit for bit: ragged sizes, misaligned arrays, delta on
+    some segments only, planted -0 / inf / NaN gradients."""
+    sizes = [4096 * 3 + 17, 255, 1, 70001]
+    segs, snaps = build_segments(L, sizes, 70 + nmb, delta=(0, 3), offset=offset)
+    mbs = []
+    for i, (seg, n) in enumerate(zip(segs, sizes)):
+        gs = [_bf16(n, 1e-3, 7000 + 100 * nmb + 10 * i + k, offset) for k in range(nmb)]
+        if n > 40:
+            gs[0][5] = -0.0
+            gs[-1][9] = float("inf")
+            gs[nmb // 2][13] = float("nan")
+        mbs.append(gs)
+        seg.grad = None
+    L.adamw_step(segs, step=11, microbatch_grads=mbs, **HP)
+    torch.cuda.synchronize()
+    c = oracle_consts(HP, 11)
+    for i, (seg, h, gs) in enumerate(zip(segs, snaps, mbs)):
+        ref = _accumulate_then_step(h, [to_np(g) for g in gs], c, h["orig"])
+        tag = f"mb{nmb}.seg{i}"
+        compare_f32(to_np(seg.master), ref["master"], tag + ".master")
+        compare_f32(to_np(seg.exp_avg), ref["m"], tag + ".m")
+        compare_f32(to_np(seg.exp_avg_sq), ref["v"], tag + ".v")
+        compare_bf16(to_np(seg.weight), ref["weight"], tag + ".weight")
+        if seg.delta is not None:
+            compare_f32(to_np(seg.delta), ref["delta"], tag + ".delta")
+
+
+def test_microbatch_sum_llama7b_layer_full(L):
+    """One Llama-2-7B layer with its 8 micro-batch gradients resident, summed
+    inside the step: every element equals accumulate-then-step."""
+    w = synth.WORKLOADS["llama7b_layer"]
+    c = oracle_consts(HP, w.step)
+    segs, mbs, hosts = [], [], []
+    for i in range(len(w.segments)):
+        st = synth.make_segment_state(w, i, DEV, with_orig=True)
+        n = w.numels[i]
+        seg = L.AdamwSegment(st["master"], st["m"], st["v"], None,
+                             torch.empty(n, dtype=torch.bfloat16, device=DEV), st["orig"],
+                             torch.empty(n, device=DEV))
+        hosts.append({"master": to_np(st["master"]), "m": to_np(st["m"]), "v": to_np(st["v"]),
+                      "orig": to_np(st["orig"])})
+        segs.append(seg)
+        mbs.append(st["grads"])
+    plan = L.AdamwPlan(segs, microbatch_grads=mbs)
+    plan.step(step=w.step, **HP)
+    torch.cuda.synchronize()
+    for i, (seg, h, gs) in enumerate(zip(segs, hosts, mbs)):
+        ref = _accumulate_then_step(h, [to_np(g) for g in gs], c, h["orig"])
+        compare_f32(to_np(seg.master), ref["master"], f"layer.seg{i}.master")
+        compare_f32(to_np(seg.exp_avg), ref["m"], f"layer.seg{i}.m")
+        compare_f32(to_np(seg.exp_avg_sq), ref["v"], f"layer.seg{i}.v")
+        compare_bf16(to_np(seg.weight), ref["weight"], f"layer.seg{i}.weight")
+        compare_f32(to_np(seg.delta), ref["delta"], f"layer.seg{i}.delta")
+
+
 # ------------------------------------------------------ full workloads
 
 def _workload_segments(L, w, with_orig, device_grads=1):
