@@ -405,8 +405,13 @@ typedef struct {
  * i mod nslots.  Blocks until the last copy back has completed.  `stats`
  * may be NULL.  Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE (a layer does not fit a
  * slot), LEMA_ERR_HPARAM, LEMA_ERR_DTYPE, LEMA_ERR_ALIGN,
- * LEMA_ERR_NOT_PINNED, LEMA_ERR_HIP; errors found before the first copy
- * enqueue nothing.
+ * LEMA_ERR_NOT_PINNED, LEMA_ERR_HIP.  Every argument error is found before
+ * the first copy, and then nothing is enqueued.  A HIP failure after copies
+ * began returns only once the pool's streams have finished what was already
+ * enqueued; the host state then holds some layers stepped, some not, and
+ * possibly one layer partly written back.  (Test hook: with the environment
+ * variable LEMA_FAULT_INJECT=copy:<n>, the n-th copy a streaming call would
+ * enqueue fails with hipErrorUnknown instead, from the host.)
  */
 lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int32_t nlayers,
                              const lema_adamw_args *args, lema_stream_stats *stats);

@@ -30,6 +30,7 @@
 
 #include <algorithm>
 #include <chrono>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
 #include <mutex>
@@ -215,15 +216,35 @@ lema_status ensure_events(lema_slot_pool *pool, size_t n) {
 
 enum { EV_H2D_BEGIN = 0, EV_H2D_END, EV_K_BEGIN, EV_K_END, EV_D2H_BEGIN, EV_D2H_END, EV_PER_LAYER };
 
+// Test hook for the failure path: with LEMA_FAULT_INJECT=copy:<n> in the
+// environment, the n-th copy (1-based) that one streaming call would enqueue
+// is not issued and reports hipErrorUnknown instead.  Nothing reaches the
+// GPU; the call then takes its ordinary HIP-failure exit.
+struct FaultInjector {
+    long fail_at = 0;    // 0: off
+    long count = 0;
+    FaultInjector() {
+        const char *v = std::getenv("LEMA_FAULT_INJECT");
+        if (v != nullptr && std::strncmp(v, "copy:", 5) == 0) fail_at = std::atol(v + 5);
+    }
+    bool fire() { return fail_at > 0 && ++count == fail_at; }
+};
+
+hipError_t copy_async(void *dst, const void *src, size_t bytes, hipMemcpyKind kind,
+                      hipStream_t s, FaultInjector *fi) {
+    if (fi != nullptr && fi->fire()) return hipErrorUnknown;
+    return hipMemcpyAsync(dst, src, bytes, kind, s);
+}
+
 // Copies of a plan's `in` arrays from `host_side` (host arrays, or a staging
 // buffer laid out like the slot when non-null) into the slot.
 hipError_t enqueue_upload(const LayerPlan &plan, char *slot, char *staging, hipStream_t s,
-                          double *bytes) {
+                          double *bytes, FaultInjector *fi) {
     hipError_t e = hipSuccess;
     for (const Xfer &x : plan.xfers) {
         if (!x.in || x.bytes == 0) continue;
         const char *src = staging ? staging + x.off : x.host;
-        e = hipMemcpyAsync(slot + x.off, src, x.bytes, hipMemcpyHostToDevice, s);
+        e = copy_async(slot + x.off, src, x.bytes, hipMemcpyHostToDevice, s, fi);
         if (e != hipSuccess) return e;
         *bytes += double(x.bytes);
     }
@@ -233,12 +254,12 @@ hipError_t enqueue_upload(const LayerPlan &plan, char *slot, char *staging, hipS
 // Copies of a plan's `out` arrays from the slot to the host arrays (or to a
 // staging buffer laid out like the slot when non-null).
 hipError_t enqueue_writeback(const LayerPlan &plan, char *slot, char *staging, hipStream_t s,
-                             double *bytes) {
+                             double *bytes, FaultInjector *fi) {
     hipError_t e = hipSuccess;
     for (const Xfer &x : plan.xfers) {
         if (!x.out || x.bytes == 0) continue;
         char *dst = staging ? staging + x.off : x.host;
-        e = hipMemcpyAsync(dst, slot + x.off, x.bytes, hipMemcpyDeviceToHost, s);
+        e = copy_async(dst, slot + x.off, x.bytes, hipMemcpyDeviceToHost, s, fi);
         if (e != hipSuccess) return e;
         *bytes += double(x.bytes);
     }
@@ -390,6 +411,15 @@ lema_status check_pinned(const std::vector<Span> &spans) {
 
 // ------------------------------------------------------------- pipelines
 
+// After a failure in the middle of a pipeline: wait for whatever was already
+// enqueued on the pool's streams, so that no copy still reads or writes the
+// caller's memory once the call has returned.  Returns `st`.
+lema_status drain(lema_slot_pool *pool, lema_status st) {
+    for (hipStream_t s : {pool->copy, pool->compute, pool->writeback})
+        if (s != nullptr) (void)hipStreamSynchronize(s);
+    return st;
+}
+
 // Page-locked host arrays: copies go straight between host and slots.
 lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans,
                        lema_stream_stats *stats) {
@@ -411,12 +441,13 @@ lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     auto ev = [&](int layer, int kind) { return pool->events[size_t(layer) * EV_PER_LAYER + kind]; };
     auto slot_of = [&](int i) { return pool->base + size_t(i % pool->nslots) * pool->slot_bytes; };
     double h2d_bytes = 0, d2h_bytes = 0;
+    FaultInjector fi;
     hipStream_t d2h_stream = pool->writeback ? pool->writeback : pool->copy;
 
     auto copy_back = [&](int j) -> lema_status {
         hipError_t err = hipStreamWaitEvent(d2h_stream, ev(j, EV_K_END), 0);
         if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_BEGIN), d2h_stream);
-        if (err == hipSuccess) err = enqueue_writeback(plans[j], slot_of(j), nullptr, d2h_stream, &d2h_bytes);
+        if (err == hipSuccess) err = enqueue_writeback(plans[j], slot_of(j), nullptr, d2h_stream, &d2h_bytes, &fi);
         if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_END), d2h_stream);
         return err == hipSuccess ? LEMA_OK : hip_failed(err);
     };
@@ -428,29 +459,29 @@ lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         if (pool->writeback && i >= pool->nslots)
             e = hipStreamWaitEvent(pool->copy, ev(i - pool->nslots, EV_D2H_END), 0);
         if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
-        if (e == hipSuccess) e = enqueue_upload(plans[i], slot_of(i), nullptr, pool->copy, &h2d_bytes);
+        if (e == hipSuccess) e = enqueue_upload(plans[i], slot_of(i), nullptr, pool->copy, &h2d_bytes, &fi);
         if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
-        if (e != hipSuccess) return hip_failed(e);
+        if (e != hipSuccess) return drain(pool, hip_failed(e));
 
         // the step on the slot
         e = hipStreamWaitEvent(pool->compute, ev(i, EV_H2D_END), 0);
         if (e == hipSuccess) e = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
-        if (e != hipSuccess) return hip_failed(e);
+        if (e != hipSuccess) return drain(pool, hip_failed(e));
         st = plans[i].launch(slot_of(i), pool->compute);
-        if (st != LEMA_OK) return st;
+        if (st != LEMA_OK) return drain(pool, st);
         e = hipEventRecord(ev(i, EV_K_END), pool->compute);
-        if (e != hipSuccess) return hip_failed(e);
+        if (e != hipSuccess) return drain(pool, hip_failed(e));
 
         // slot -> host for the previous layer, behind this layer's upload
         if (i >= 1) {
             st = copy_back(i - 1);
-            if (st != LEMA_OK) return st;
+            if (st != LEMA_OK) return drain(pool, st);
         }
     }
     st = copy_back(nlayers - 1);
-    if (st != LEMA_OK) return st;
+    if (st != LEMA_OK) return drain(pool, st);
     e = hipEventSynchronize(ev(nlayers - 1, EV_D2H_END));
-    if (e != hipSuccess) return hip_failed(e);
+    if (e != hipSuccess) return drain(pool, hip_failed(e));
 
     if (stats) {
         fill_stats(pool, nlayers, h2d_bytes, d2h_bytes, stats);
@@ -498,6 +529,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
 
     auto ev = [&](int layer, int kind) { return pool->events[size_t(layer) * EV_PER_LAYER + kind]; };
     double h2d_bytes = 0, d2h_bytes = 0, in_ms = 0, out_ms = 0;
+    FaultInjector fi;
     hipStream_t d2h_stream = pool->writeback ? pool->writeback : pool->copy;
     std::vector<CopyItem> items;
     using clock = std::chrono::steady_clock;
@@ -511,7 +543,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         in_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
 
         hipError_t err = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
-        if (err == hipSuccess) err = enqueue_upload(plans[i], slot, pool->staging[b], pool->copy, &h2d_bytes);
+        if (err == hipSuccess) err = enqueue_upload(plans[i], slot, pool->staging[b], pool->copy, &h2d_bytes, &fi);
         if (err == hipSuccess) err = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
         if (err == hipSuccess) err = hipStreamWaitEvent(pool->compute, ev(i, EV_H2D_END), 0);
         if (err == hipSuccess) err = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
@@ -521,7 +553,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         err = hipEventRecord(ev(i, EV_K_END), pool->compute);
         if (err == hipSuccess) err = hipStreamWaitEvent(d2h_stream, ev(i, EV_K_END), 0);
         if (err == hipSuccess) err = hipEventRecord(ev(i, EV_D2H_BEGIN), d2h_stream);
-        if (err == hipSuccess) err = enqueue_writeback(plans[i], slot, pool->staging[b], d2h_stream, &d2h_bytes);
+        if (err == hipSuccess) err = enqueue_writeback(plans[i], slot, pool->staging[b], d2h_stream, &d2h_bytes, &fi);
         if (err == hipSuccess) err = hipEventRecord(ev(i, EV_D2H_END), d2h_stream);
         return err == hipSuccess ? LEMA_OK : hip_failed(err);
     };
@@ -537,14 +569,14 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
 
     for (int i = 0; i < std::min(nlayers, 2); ++i) {
         st = stage_in_and_enqueue(i);
-        if (st != LEMA_OK) return st;
+        if (st != LEMA_OK) return drain(pool, st);
     }
     for (int i = 0; i < nlayers; ++i) {
         st = wait_and_stage_out(i);
-        if (st != LEMA_OK) return st;
+        if (st != LEMA_OK) return drain(pool, st);
         if (i + 2 < nlayers) {
             st = stage_in_and_enqueue(i + 2);
-            if (st != LEMA_OK) return st;
+            if (st != LEMA_OK) return drain(pool, st);
         }
     }
 

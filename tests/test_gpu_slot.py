@@ -256,3 +256,24 @@ def test_slot_stream_staged_llama_layers(L):
           f"{stats['host_out_ms']:.1f} ms, H2D {stats['h2d_ms']:.1f} ms, D2H {stats['d2h_ms']:.1f} ms, "
           f"kernel {stats['kernel_ms']:.2f} ms")
     pool.close()
+
+
+@pytest.mark.parametrize("staged,fail_at", [(False, 6), (False, 13), (True, 2), (True, 9)])
+def test_injected_copy_failure_then_recovery(L, monkeypatch, staged, fail_at):
+    """A copy that fails in the middle of a streamed call (forced from the
+    host with LEMA_FAULT_INJECT) returns LEMA_ERR_HIP after the pool's streams
+    have drained; the same pool then streams fresh layers correctly and can
+    be destroyed."""
+    from optimizer_step_lema_amd import _native as N
+    shapes = [[5000, 777], [4096], [300, 20000]]
+    layers, _ = zip(*[host_layer(L, s, 80 + i) for i, s in enumerate(shapes)])
+    pool = L.SlotPool(max(layer_bytes(s) for s in shapes), nslots=2)
+    monkeypatch.setenv("LEMA_FAULT_INJECT", f"copy:{fail_at}")
+    with pytest.raises(N.LemaError) as e:
+        pool.stream(layers, step=3, staged=staged, **HP)
+    assert e.value.status == N.LEMA_ERR_HIP and e.value.hip_error != 0
+    monkeypatch.delenv("LEMA_FAULT_INJECT")
+    layers2, snaps2 = zip(*[host_layer(L, s, 90 + i) for i, s in enumerate(shapes)])
+    pool.stream(layers2, step=3, staged=staged, **HP)
+    check_layers(layers2, snaps2, 3)
+    pool.close()

@@ -158,3 +158,19 @@ def test_stream_q8_llama_layers_staged(L):
     check_layers(layers, snaps, w.step)
     assert stats["kernel_ms"] > 0
     pool.close()
+
+
+def test_stream_q8_injected_copy_failure(L, monkeypatch):
+    """The int8 pipeline's failure exit: LEMA_ERR_HIP, then the pool works."""
+    from optimizer_step_lema_amd import _native as N
+    layers, _ = zip(*[q8_layer(L, s, 80 + i, pinned=True) for i, s in enumerate(SHAPES)])
+    pool = L.SlotPool(max(slot_bytes(s) for s in SHAPES), nslots=2)
+    monkeypatch.setenv("LEMA_FAULT_INJECT", "copy:9")
+    with pytest.raises(N.LemaError) as e:
+        pool.stream_q8(layers, step=2, **HP)
+    assert e.value.status == N.LEMA_ERR_HIP
+    monkeypatch.delenv("LEMA_FAULT_INJECT")
+    layers2, snaps2 = zip(*[q8_layer(L, s, 90 + i, pinned=True) for i, s in enumerate(SHAPES)])
+    pool.stream_q8(layers2, step=2, **HP)
+    check_layers(layers2, snaps2, 2)
+    pool.close()
