@@ -12,7 +12,8 @@
 // Both are elementwise and bound by HBM bandwidth, so there is no MFMA and
 // no LDS tiling of data: each lane streams 4 contiguous elements per access
 // (16-byte fp32 / 8-byte bf16 vector loads and stores, contiguous across the
-// wavefront), with the nontemporal hint since no byte is touched twice.
+// wavefront).  The accesses go through per-tile buffer resources with the
+// nontemporal hint, since no byte is touched twice (lema_device.h).
 //
 // One workgroup per tile, not a persistent grid: on gfx9 the vector-memory
 // counter also counts stores, so a persistent loop would wait for a tile's
@@ -79,21 +80,23 @@ struct AdamwTile {
         return reinterpret_cast<const uint64_t *>(table + list_offset);
     }
 
-    // The gradient of 4 consecutive elements starting at vector index q.
-    __device__ __forceinline__ f32x4 load_grad4(uint64_t grad, uint64_t last, int64_t q) const {
+    // The gradient of this lane's 4 elements of the tile whose first vector
+    // index is q0.
+    __device__ __forceinline__ f32x4 load_grad4(uint64_t grad, uint64_t last, int64_t q0,
+                                                int lane) const {
 #pragma clang fp contract(off)
         if constexpr (kMode == kGradBf16) {
-            const u32x2 gb = ld_nt<u32x2>(grad, q);
+            const u32x2 gb = tile_ld<u32x2>(tile_rsrc<u32x2>(grad, q0, kBlock), lane);
             return f32x4{bf16_lo(gb.x), bf16_hi(gb.x), bf16_lo(gb.y), bf16_hi(gb.y)};
         } else if constexpr (kMode == kGradF32) {
-            return ld_nt<f32x4>(grad, q);
+            return tile_ld<f32x4>(tile_rsrc<f32x4>(grad, q0, kBlock), lane);
         } else if constexpr (kMode == kGradBf16Sum) {
             // every micro-batch's loads first, then the fp32 sum in micro-batch
             // order, the first one widened exactly (lema_grad_accum's overwrite)
             const uint64_t *mb = microbatches(grad);
             u32x2 gb[kNmb];
 #pragma unroll
-            for (int k = 0; k < kNmb; ++k) gb[k] = ld_nt<u32x2>(mb[k], q);
+            for (int k = 0; k < kNmb; ++k) gb[k] = tile_ld<u32x2>(tile_rsrc<u32x2>(mb[k], q0, kBlock), lane);
             f32x4 acc = {bf16_lo(gb[0].x), bf16_hi(gb[0].x), bf16_lo(gb[0].y), bf16_hi(gb[0].y)};
 #pragma unroll
             for (int k = 1; k < kNmb; ++k) {
@@ -105,8 +108,8 @@ struct AdamwTile {
             return acc;
         } else {
             // the last micro-batch's fp32 addition, as lema_grad_accum does it
-            const f32x4 acc = ld_nt<f32x4>(grad, q);
-            const u32x2 lb = ld_nt<u32x2>(last, q);
+            const f32x4 acc = tile_ld<f32x4>(tile_rsrc<f32x4>(grad, q0, kBlock), lane);
+            const u32x2 lb = tile_ld<u32x2>(tile_rsrc<u32x2>(last, q0, kBlock), lane);
             return f32x4{accum_elem(acc.x, bf16_lo(lb.x), false), accum_elem(acc.y, bf16_hi(lb.x), false),
                          accum_elem(acc.z, bf16_lo(lb.y), false), accum_elem(acc.w, bf16_hi(lb.y), false)};
         }
@@ -118,22 +121,22 @@ struct AdamwTile {
                                                 uint64_t orig, uint64_t delta, int64_t base) const {
         f32x4 w4[kUnroll], m4[kUnroll], v4[kUnroll], g4[kUnroll];
         u32x2 o2[kUnroll];
-        const int64_t lane = int64_t(threadIdx.x) * kVec;
+        const int lane = int(threadIdx.x);
 
         // all loads of the tile first, so each lane has them in flight together
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;   // vector index
-            w4[u] = ld_nt<f32x4>(master, q);
-            m4[u] = ld_nt<f32x4>(m, q);
-            v4[u] = ld_nt<f32x4>(v, q);
-            g4[u] = load_grad4(grad, last, q);
-            if constexpr (kHasDelta) o2[u] = ld_nt<u32x2>(orig, q);
+            const int64_t q0 = (base + u * (kBlock * kVec)) / kVec;   // first vector of the access
+            w4[u] = tile_ld<f32x4>(tile_rsrc<f32x4>(master, q0, kBlock), lane);
+            m4[u] = tile_ld<f32x4>(tile_rsrc<f32x4>(m, q0, kBlock), lane);
+            v4[u] = tile_ld<f32x4>(tile_rsrc<f32x4>(v, q0, kBlock), lane);
+            g4[u] = load_grad4(grad, last, q0, lane);
+            if constexpr (kHasDelta) o2[u] = tile_ld<u32x2>(tile_rsrc<u32x2>(orig, q0, kBlock), lane);
         }
 
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
-            const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
+            const int64_t q0 = (base + u * (kBlock * kVec)) / kVec;
             f32x4 w = w4[u], mm = m4[u], vv = v4[u];
             const f32x4 g = g4[u];
 #pragma unroll
@@ -144,16 +147,17 @@ struct AdamwTile {
                 mm[k] = mk;
                 vv[k] = vk;
             }
-            st_nt<f32x4>(master, q, w);
-            st_nt<f32x4>(m, q, mm);
-            st_nt<f32x4>(v, q, vv);
-            st_nt<u32x2>(weight, q, u32x2{to_bf16_pair(w.x, w.y), to_bf16_pair(w.z, w.w)});
+            tile_st<f32x4>(tile_rsrc<f32x4>(master, q0, kBlock), lane, w);
+            tile_st<f32x4>(tile_rsrc<f32x4>(m, q0, kBlock), lane, mm);
+            tile_st<f32x4>(tile_rsrc<f32x4>(v, q0, kBlock), lane, vv);
+            tile_st<u32x2>(tile_rsrc<u32x2>(weight, q0, kBlock), lane,
+                           u32x2{to_bf16_pair(w.x, w.y), to_bf16_pair(w.z, w.w)});
             if constexpr (kHasDelta) {
 #pragma clang fp contract(off)
                 const u32x2 o = o2[u];
                 const f32x4 d = {w.x - bf16_lo(o.x), w.y - bf16_hi(o.x),
                                  w.z - bf16_lo(o.y), w.w - bf16_hi(o.y)};
-                st_nt<f32x4>(delta, q, d);
+                tile_st<f32x4>(tile_rsrc<f32x4>(delta, q0, kBlock), lane, d);
             }
         }
     }
@@ -230,15 +234,16 @@ struct AccumTile {
         if (vector_ok) {
             f32x4 a4[kUnroll];
             u32x2 g2[kUnroll];
+            const int vl = int(threadIdx.x);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
-                if constexpr (!kOverwrite) a4[u] = ld_nt<f32x4>(acc, q);
-                g2[u] = ld_nt<u32x2>(g, q);
+                const int64_t q0 = (base + u * (kBlock * kVec)) / kVec;
+                if constexpr (!kOverwrite) a4[u] = tile_ld<f32x4>(tile_rsrc<f32x4>(acc, q0, kBlock), vl);
+                g2[u] = tile_ld<u32x2>(tile_rsrc<u32x2>(g, q0, kBlock), vl);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
+                const int64_t q0 = (base + u * (kBlock * kVec)) / kVec;
                 const f32x4 gf = {bf16_lo(g2[u].x), bf16_hi(g2[u].x), bf16_lo(g2[u].y),
                                   bf16_hi(g2[u].y)};
                 f32x4 out;
@@ -248,7 +253,7 @@ struct AccumTile {
 #pragma unroll
                     for (int k = 0; k < kVec; ++k) out[k] = accum_elem(a4[u][k], gf[k], false);
                 }
-                st_nt<f32x4>(acc, q, out);
+                tile_st<f32x4>(tile_rsrc<f32x4>(acc, q0, kBlock), vl, out);
             }
         } else {
             for (int u = 0; u < kUnroll; ++u) {
@@ -285,18 +290,20 @@ struct MergeTile {
         if (vector_ok) {
             u32x2 b2[kUnroll];
             f32x4 d4[kUnroll];
+            const int vl = int(threadIdx.x);
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
-                b2[u] = ld_nt<u32x2>(base_w, q);
-                d4[u] = ld_nt<f32x4>(delta, q);
+                const int64_t q0 = (base + u * (kBlock * kVec)) / kVec;
+                b2[u] = tile_ld<u32x2>(tile_rsrc<u32x2>(base_w, q0, kBlock), vl);
+                d4[u] = tile_ld<f32x4>(tile_rsrc<f32x4>(delta, q0, kBlock), vl);
             }
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) {
-                const int64_t q = (base + u * (kBlock * kVec) + lane) / kVec;
+                const int64_t q0 = (base + u * (kBlock * kVec)) / kVec;
                 const float s0 = bf16_lo(b2[u].x) + d4[u].x, s1 = bf16_hi(b2[u].x) + d4[u].y;
                 const float s2 = bf16_lo(b2[u].y) + d4[u].z, s3 = bf16_hi(b2[u].y) + d4[u].w;
-                st_nt<u32x2>(merged, q, u32x2{to_bf16_pair(s0, s1), to_bf16_pair(s2, s3)});
+                tile_st<u32x2>(tile_rsrc<u32x2>(merged, q0, kBlock), vl,
+                               u32x2{to_bf16_pair(s0, s1), to_bf16_pair(s2, s3)});
             }
         } else {
             for (int u = 0; u < kUnroll; ++u) {
