@@ -76,6 +76,9 @@ def parse():
     ap.add_argument("--resident-microbatches", action="store_true",
                     help="multi-micro-batch workloads: all K bf16 gradients stay resident and the "
                          "step sums them in fp32 (lema_adamw_step_microbatches), no accumulator")
+    ap.add_argument("--layout", choices=("flat", "per-tensor"), default="flat",
+                    help="flat: one buffer per array kind, tensors as views (flat optimizer "
+                         "state); per-tensor: every array of every tensor allocated on its own")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-gib", type=float, default=4.0, help="size of the copy-ceiling test")
@@ -129,13 +132,15 @@ def copy_ceiling(torch, L, gib):
     return 2 * nbytes / (sum(ms) / len(ms) * 1e-3) / 1e9
 
 
-def traffic_for(key):
-    """Counter-measured HBM bytes per launch, if recorded for this kernel source."""
+def traffic_for(key, layout):
+    """Counter-measured HBM bytes per launch, if recorded for this kernel
+    source and state layout."""
     if not os.path.exists(COUNTERS):
         return None
     rec = json.load(open(COUNTERS))
     entry = rec.get("workloads", {}).get(key)
-    if entry and rec.get("kernel_digest") == kernel_digest():
+    if entry and rec.get("kernel_digest") == kernel_digest() and \
+            entry.get("layout", "per-tensor") == layout:
         return entry["traffic_bytes_per_launch"]
     return None
 
@@ -188,28 +193,14 @@ def resident_bench(torch, L, synth, a):
     # state resident in HBM; small workloads get rotated copies so that the
     # working set exceeds the 256 MB last-level cache between launches
     nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
-    sets = []
-    for _ in range(nsets):
-        segs, accs = [], []
-        for i in range(len(w.segments)):
-            st = synth.make_segment_state(w, i, dev, with_orig=delta)
-            n = w.numels[i]
-            grad = torch.empty(n, device=dev) if grad_f32 else st["grads"][0]
-            if grad_f32 or resident_mb:
-                accs.append((grad, st["grads"]))
-            if resident_mb:
-                grad = None
-            segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], grad,
-                                       torch.empty(n, dtype=torch.bfloat16, device=dev),
-                                       st.get("orig"),
-                                       torch.empty(n, device=dev) if delta else None))
-        sets.append((segs, accs))
+    sets = [resident_state(torch, L, synth, w, a.layout, delta, grad_f32, resident_mb)
+            for _ in range(nsets)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     copy_gbps = copy_ceiling(torch, L, a.copy_gib)
 
     accum_plans = [[L.AccumPlan([L.AccumSegment(acc, g[j]) for acc, g in accs])
-                    for j in range(accum_launches)] for _, accs in sets] if grad_f32 else []
+                    for j in range(accum_launches)] for _, accs, _ in sets] if grad_f32 else []
 
     def accumulate(k):
         for j, plan in enumerate(accum_plans[k % nsets]):
@@ -219,7 +210,7 @@ def resident_bench(torch, L, synth, a):
     # the timed region holds the library call, not Python argument packing
     plans = [L.AdamwPlan(segs, last_grads=[g[K - 1] for _, g in accs] if fused else None,
                          microbatch_grads=[g for _, g in accs] if resident_mb else None)
-             for segs, accs in sets]
+             for segs, accs, _ in sets]
 
     def step(k):
         plans[k % nsets].step(step=w.step, **hp)
@@ -289,6 +280,7 @@ def resident_bench(torch, L, synth, a):
             "bytes_per_param": step_bytes + accum_bytes,
             "bytes_per_step": per_step,
             "rotated_state_sets": nsets,
+            "layout": a.layout,
         },
         "hbm_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
@@ -296,7 +288,7 @@ def resident_bench(torch, L, synth, a):
         "pct_copy_ceiling": 100.0 * gbps / copy_gbps,
         "roofline": {"bound": "hbm", "achieved": adamw_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": adamw_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic_for(key), "kernel": "adamw_tile_kernel",
+                     "traffic": traffic_for(key, a.layout), "kernel": "adamw_tile_kernel",
                      "algorithmic_bytes_per_launch": P * step_bytes,
                      "avg_launch_ms": adamw_ms, "min_launch_ms": min(adamw_ms_list),
                      "max_launch_ms": max(adamw_ms_list)},
@@ -318,6 +310,54 @@ def resident_bench(torch, L, synth, a):
         line["cpu_baseline"] = cpu_baseline(sets[0][0], w, hp, delta, a.cpu_seconds,
                                             sets[0][1][0][1] if resident_mb else None)
     return line
+
+
+def resident_state(torch, L, synth, w, layout, delta, grad_f32, resident_mb):
+    """One state set of the workload on the GPU: (segments, [(accumulator or
+    None, [bf16 micro-batch gradients])]) plus the buffers that back them.
+
+    The values are the seeded synthetic draws either way; `layout` only
+    decides where they live: "flat" puts each array kind of all tensors in
+    one buffer, "per-tensor" allocates every array of every tensor alone."""
+    dev = "cuda"
+    K = w.microbatches
+    accs = []
+    if layout == "flat":
+        nmb = K if (grad_f32 or resident_mb) else 0
+        fs, segs = L.flat_adamw_state(
+            w.numels, grad=None if resident_mb else (torch.float32 if grad_f32 else torch.bfloat16),
+            delta=delta, microbatches=nmb, device=dev)
+        for i in range(len(w.segments)):
+            st = synth.make_segment_state(w, i, dev, with_orig=delta)
+            s = segs[i]
+            s.master.copy_(st["master"])
+            s.exp_avg.copy_(st["m"])
+            s.exp_avg_sq.copy_(st["v"])
+            if delta:
+                s.orig.copy_(st["orig"])
+            if nmb:
+                mbs = [fs.view(f"mb{k}", i) for k in range(K)]
+                for dst, src in zip(mbs, st["grads"]):
+                    dst.copy_(src)
+                accs.append((s.grad if grad_f32 else None, mbs))
+            else:
+                s.grad.copy_(st["grads"][0])
+            del st
+        return segs, accs, fs
+    segs = []
+    for i in range(len(w.segments)):
+        st = synth.make_segment_state(w, i, dev, with_orig=delta)
+        n = w.numels[i]
+        grad = torch.empty(n, device=dev) if grad_f32 else st["grads"][0]
+        if grad_f32 or resident_mb:
+            accs.append((grad, st["grads"]))
+        if resident_mb:
+            grad = None
+        segs.append(L.AdamwSegment(st["master"], st["m"], st["v"], grad,
+                                   torch.empty(n, dtype=torch.bfloat16, device=dev),
+                                   st.get("orig"),
+                                   torch.empty(n, device=dev) if delta else None))
+    return segs, accs, None
 
 
 def cpu_baseline(segs, w, hp, delta, seconds, microbatches=None):
@@ -352,19 +392,32 @@ def cpu_baseline(segs, w, hp, delta, seconds, microbatches=None):
                 oracle.grad_accum(acc, g, overwrite=(k == 0))
             oracle.adamw_step(master, m, v, acc, c, orig=orig)
     one_step()                                                 # warm-up pass
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        one_step()
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": n * reps / el, "unit": "params/s", "cores": oracle.num_threads(),
+    reps, el = timed_loop(one_step, seconds)
+    cores = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        reps1, el1 = timed_loop(one_step, seconds / 4)
+    finally:
+        oracle.set_num_threads(cores)
+    return {"value": n * reps / el, "unit": "params/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{w.segments[0][0]} ({n} params), {reps} oracle steps in {el:.1f} s, "
                       f"delta {'on' if delta else 'off'}"
                       + (f", each with {len(microbatches)} accumulations" if microbatches else "")
-                      + "; C oracle, OpenMP"}
+                      + "; C oracle, OpenMP",
+            "single_thread": {"value": n * reps1 / el1, "unit": "params/s", "cores": 1,
+                              "sample": f"the same step, {reps1} times in {el1:.1f} s"}}
+
+
+def timed_loop(fn, seconds):
+    """Runs fn until `seconds` have passed; returns (calls, elapsed s)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return reps, el
 
 
 # ------------------------------------------------------------- int8
@@ -403,32 +456,14 @@ def q8_bench(torch, L, synth, a):
     per_step = step_bytes + accum_bytes
 
     nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
-    sets = []
-    for _ in range(nsets):
-        segs, accs = [], []
-        for i in range(len(w.segments)):
-            st = synth.make_segment_state(w, i, dev, with_orig=delta)
-            n, rl = w.numels[i], row_lens[i]
-            m, v = L.Q8.empty(n, rl), L.Q8.empty(n, rl)
-            L.quantize_rows([(st["m"], m), (st["v"], v)])
-            if K > 1:
-                g = L.Q8.empty(n, rl)
-                accs.append((g, st["grads"]))
-            else:
-                g = st["grads"][0]
-            segs.append(L.AdamwQ8Segment(st["master"], m, v, g,
-                                         torch.empty(n, dtype=torch.bfloat16, device=dev),
-                                         st.get("orig"),
-                                         torch.empty(n, device=dev) if delta else None))
-            del st["m"], st["v"]
-        sets.append((segs, accs))
+    sets = [q8_state(torch, L, synth, w, row_lens, a.layout, delta) for _ in range(nsets)]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     copy_gbps = copy_ceiling(torch, L, a.copy_gib)
 
     accum_plans = [[L.AccumQ8Plan([L.AccumQ8Segment(acc, g[j]) for acc, g in accs])
-                    for j in range(K)] for _, accs in sets] if K > 1 else []
-    plans = [L.AdamwQ8Plan(segs) for segs, _ in sets]
+                    for j in range(K)] for _, accs, _ in sets] if K > 1 else []
+    plans = [L.AdamwQ8Plan(segs) for segs, _, _ in sets]
 
     def accumulate(k):
         for j, plan in enumerate(accum_plans[k % nsets]):
@@ -482,6 +517,7 @@ def q8_bench(torch, L, synth, a):
             "delta": delta, "step_t": w.step,
             "bytes_per_param": per_step / P, "bytes_per_step": per_step,
             "rotated_state_sets": nsets,
+            "layout": a.layout,
         },
         "hbm_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
@@ -489,7 +525,7 @@ def q8_bench(torch, L, synth, a):
         "pct_copy_ceiling": 100.0 * gbps / copy_gbps,
         "roofline": {"bound": "hbm", "achieved": adamw_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": adamw_gbps / HBM_PEAK_GBPS,
-                     "traffic": traffic_for(key), "kernel": "adamw_q8_kernel",
+                     "traffic": traffic_for(key, a.layout), "kernel": "adamw_q8_kernel",
                      "algorithmic_bytes_per_launch": step_bytes,
                      "avg_launch_ms": adamw_ms, "min_launch_ms": min(adamw_ms_list),
                      "max_launch_ms": max(adamw_ms_list)},
@@ -509,6 +545,53 @@ def q8_bench(torch, L, synth, a):
         line["cpu_baseline"] = q8_cpu_baseline(sets[0][0][0], w, row_lens[0], hp, delta,
                                                a.cpu_seconds)
     return line
+
+
+def q8_state(torch, L, synth, w, row_lens, layout, delta):
+    """One int8-moment state set on the GPU: (segments, [(int8 accumulator,
+    [bf16 micro-batch gradients])], buffers).  The moments are the seeded fp32
+    draws quantized by lema_quantize_rows; `layout` as for resident_state."""
+    dev = "cuda"
+    K = w.microbatches
+    accs = []
+    if layout == "flat":
+        el, rw, segs = L.flat_q8_state(w.numels, row_lens, grad="q8" if K > 1 else "bf16",
+                                       delta=delta, device=dev)
+        mbs = [L.FlatState(w.numels, {"g": torch.bfloat16}, device=dev) for _ in range(K)] \
+            if K > 1 else []
+        for i in range(len(w.segments)):
+            st = synth.make_segment_state(w, i, dev, with_orig=delta)
+            s = segs[i]
+            s.master.copy_(st["master"])
+            L.quantize_rows([(st["m"], s.exp_avg), (st["v"], s.exp_avg_sq)])
+            if delta:
+                s.orig.copy_(st["orig"])
+            if K > 1:
+                gs = [fs.view("g", i) for fs in mbs]
+                for dst, src in zip(gs, st["grads"]):
+                    dst.copy_(src)
+                accs.append((s.grad, gs))
+            else:
+                s.grad.copy_(st["grads"][0])
+            del st
+        return segs, accs, (el, rw, mbs)
+    segs = []
+    for i in range(len(w.segments)):
+        st = synth.make_segment_state(w, i, dev, with_orig=delta)
+        n, rl = w.numels[i], row_lens[i]
+        m, v = L.Q8.empty(n, rl), L.Q8.empty(n, rl)
+        L.quantize_rows([(st["m"], m), (st["v"], v)])
+        if K > 1:
+            g = L.Q8.empty(n, rl)
+            accs.append((g, st["grads"]))
+        else:
+            g = st["grads"][0]
+        segs.append(L.AdamwQ8Segment(st["master"], m, v, g,
+                                     torch.empty(n, dtype=torch.bfloat16, device=dev),
+                                     st.get("orig"),
+                                     torch.empty(n, device=dev) if delta else None))
+        del st["m"], st["v"]
+    return segs, accs, None
 
 
 def q8_cpu_baseline(seg, w, row_len, hp, delta, seconds):
@@ -532,13 +615,8 @@ def q8_cpu_baseline(seg, w, row_len, hp, delta, seconds):
     c = oracle.adamw_constants(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
                                hp["weight_decay"], w.step)
     oracle.adamw_step_q8(master, m, v, grad, c, row_len, orig=orig)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.adamw_step_q8(master, m, v, grad, c, row_len, orig=orig)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    reps, el = timed_loop(lambda: oracle.adamw_step_q8(master, m, v, grad, c, row_len, orig=orig),
+                          seconds)
     return {"value": n * reps / el, "unit": "params/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"{w.segments[0][0]} ({n} params, rows of {row_len}), {reps} oracle "
@@ -554,11 +632,19 @@ def merge_bench(torch, L, synth, a):
     w = synth.WORKLOADS[a.workload]
     P = w.params
     segs = []
+    fs = L.FlatState(w.numels, {"base": torch.bfloat16, "delta": torch.float32,
+                                "merged": torch.bfloat16}) if a.layout == "flat" else None
     for i in range(len(w.segments)):
         n = w.numels[i]
         base = synth.bf16_normal(n, 0.02, synth.seed_of(w.wid, 0, i), "cuda")
         delta = synth.normal(n, 1e-4, synth.seed_of(w.wid, 5, i), "cuda")
-        segs.append(L.MergeSegment(base, delta, torch.empty_like(base)))
+        if fs is not None:
+            fs.view("base", i).copy_(base)
+            fs.view("delta", i).copy_(delta)
+            base, delta = fs.view("base", i), fs.view("delta", i)
+            segs.append(L.MergeSegment(base, delta, fs.view("merged", i)))
+        else:
+            segs.append(L.MergeSegment(base, delta, torch.empty_like(base)))
     per = 8 * P
     nsets = 1
     torch.cuda.synchronize()
@@ -576,7 +662,7 @@ def merge_bench(torch, L, synth, a):
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": a.workload, "params": P, "segments": len(w.segments),
-                   "bytes_per_param": 8, "rotated_state_sets": nsets},
+                   "bytes_per_param": 8, "rotated_state_sets": nsets, "layout": a.layout},
         "hbm_gbps": gbps, "pct_hbm_peak": 100 * gbps / HBM_PEAK_GBPS,
         "copy_ceiling_gbps": copy_gbps,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -199,6 +199,78 @@ class AdamwPlan:
                     "lema_adamw_step_accum")
 
 
+class FlatState:
+    """Flat device buffers, one per array kind, holding that array of every
+    tensor of a segment list.
+
+    Tensor i's array of kind k is the view of buffer k at the same element
+    offset for every kind; offsets are rounded up to `align` elements (256 B
+    of fp32), so every view is vector-aligned for the kernels.  This is the
+    layout of flat parameter and optimizer-state buffers in ZeRO/FSDP-style
+    training.  It also places the arrays that one AdamW launch streams side by
+    side a whole buffer apart in HBM; allocating them tensor by tensor instead
+    puts one tensor's arrays next to each other, which measured 10-15% slower
+    on MI355X for the same launch.
+    """
+
+    def __init__(self, numels: Sequence[int], kinds: dict, device="cuda", align: int = 64):
+        if align < 1:
+            raise ValueError("align must be >= 1")
+        self.numels = [int(n) for n in numels]
+        if any(n < 0 for n in self.numels):
+            raise ValueError("numels must be >= 0")
+        self.offsets = []
+        total = 0
+        for n in self.numels:
+            self.offsets.append(total)
+            total += -(-n // align) * align
+        self.total = total
+        self.buffers = {k: torch.empty(total, dtype=dt, device=device) for k, dt in kinds.items()}
+
+    def __len__(self) -> int:
+        return len(self.numels)
+
+    def view(self, kind: str, i: int) -> torch.Tensor:
+        o = self.offsets[i]
+        return self.buffers[kind][o:o + self.numels[i]]
+
+    def views(self, kind: str) -> list:
+        return [self.view(kind, i) for i in range(len(self.numels))]
+
+
+def flat_adamw_state(numels: Sequence[int], *, grad: Optional[torch.dtype] = torch.bfloat16,
+                     delta: bool = False, microbatches: int = 0,
+                     device="cuda") -> tuple[FlatState, list]:
+    """AdamW state for tensors of the given sizes in flat buffers.
+
+    Kinds: master, exp_avg, exp_avg_sq (fp32), weight (bf16 output), grad
+    (bf16, or the fp32 accumulator; None for no gradient buffer), orig and
+    delta when `delta`, and mb0 .. mb{K-1} (bf16) for K resident micro-batch
+    gradients.  Returns the buffers and the AdamwSegment list over their
+    views; the contents are uninitialised except m and v, which start at 0.
+    """
+    kinds = {"master": torch.float32, "exp_avg": torch.float32, "exp_avg_sq": torch.float32,
+             "weight": torch.bfloat16}
+    if grad is not None:
+        if grad not in (torch.bfloat16, torch.float32):
+            raise TypeError("grad must be torch.bfloat16, torch.float32 or None")
+        kinds["grad"] = grad
+    if delta:
+        kinds["orig"] = torch.bfloat16
+        kinds["delta"] = torch.float32
+    for k in range(microbatches):
+        kinds[f"mb{k}"] = torch.bfloat16
+    fs = FlatState(numels, kinds, device=device)
+    fs.buffers["exp_avg"].zero_()
+    fs.buffers["exp_avg_sq"].zero_()
+    segs = [AdamwSegment(fs.view("master", i), fs.view("exp_avg", i), fs.view("exp_avg_sq", i),
+                         fs.view("grad", i) if grad is not None else None, fs.view("weight", i),
+                         fs.view("orig", i) if delta else None,
+                         fs.view("delta", i) if delta else None)
+            for i in range(len(fs))]
+    return fs, segs
+
+
 @dataclass
 class AccumSegment:
     acc: torch.Tensor
@@ -371,6 +443,45 @@ class AdamwQ8Segment:
             _check(self.weight, torch.bfloat16, n, "weight", where),
             _check(self.orig, torch.bfloat16, n, "orig", where),
             _check(self.delta, torch.float32, n, "delta", where), n, self.row_len())
+
+
+def flat_q8_state(numels: Sequence[int], row_lens: Sequence[int], *, grad: str = "bf16",
+                  delta: bool = False, device="cuda") -> tuple[FlatState, FlatState, list]:
+    """int8-moment AdamW state for tensors of the given sizes in flat buffers.
+
+    Element kinds: master (fp32), weight (bf16 output), m and v codes (int8),
+    the gradient (bf16, or int8 accumulator codes when grad == "q8"), orig and
+    delta when `delta`.  Row kinds, in a second FlatState over each tensor's
+    row count: the m, v (and accumulator) scales.  Returns both and the
+    AdamwQ8Segment list over their views; codes and scales start at zero.
+    """
+    if grad not in ("bf16", "q8"):
+        raise ValueError('grad must be "bf16" or "q8"')
+    if len(row_lens) != len(numels):
+        raise ValueError("one row length per tensor is required")
+    kinds = {"master": torch.float32, "weight": torch.bfloat16, "m": torch.int8,
+             "v": torch.int8, "grad": torch.int8 if grad == "q8" else torch.bfloat16}
+    if delta:
+        kinds["orig"] = torch.bfloat16
+        kinds["delta"] = torch.float32
+    el = FlatState(numels, kinds, device=device)
+    rows = [Q8.rows_of(int(n), int(rl)) for n, rl in zip(numels, row_lens)]
+    rk = {"m": torch.float32, "v": torch.float32}
+    if grad == "q8":
+        rk["grad"] = torch.float32
+    rw = FlatState(rows, rk, device=device)
+    for fs in (el, rw):
+        for k in rk:
+            fs.buffers[k].zero_()
+    segs = []
+    for i, rl in enumerate(row_lens):
+        q = lambda k: Q8(el.view(k, i), rw.view(k, i), int(rl))
+        segs.append(AdamwQ8Segment(el.view("master", i), q("m"), q("v"),
+                                   q("grad") if grad == "q8" else el.view("grad", i),
+                                   el.view("weight", i),
+                                   el.view("orig", i) if delta else None,
+                                   el.view("delta", i) if delta else None))
+    return el, rw, segs
 
 
 def _q8_call_kinds(segments: Sequence[AdamwQ8Segment]):

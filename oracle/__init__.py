@@ -80,6 +80,8 @@ def _load():
     lib.oracle_dequantize_rows.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
+    lib.oracle_set_num_threads.argtypes = [i32]
+    lib.oracle_set_num_threads.restype = None
     _lib = lib
     return lib
 
@@ -104,6 +106,11 @@ def _check(a: np.ndarray, dtype, n: int, name: str, writable: bool = False):
 def num_threads() -> int:
     """OpenMP threads the C oracle's loops use (OMP_NUM_THREADS governs it)."""
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads for later oracle calls (results do not depend on it)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def rne16(x: np.ndarray) -> np.ndarray:

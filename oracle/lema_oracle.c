@@ -304,3 +304,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* Sets the threads of later loops (n >= 1); results do not depend on it,
+ * every element being computed alone. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}

@@ -24,6 +24,10 @@ Workloads (tensor shapes from the models the LEMA README trains):
   ``lora_rank=16`` with torch.optim.AdamW over the adapters) on all seven
   linear projections of the 32 Llama-2-7B layers: per projection A
   [16 x in] and B [out x 16]; 448 segments, 39,976,960 parameters; t = 10.
+* ``llama7b_full_shard8``  -- one data-parallel rank's share of the whole
+  7B shape when each tensor's flat element range is split 8 ways (ZeRO-1/2
+  style ownership): the first eighth of each of the 291 tensors, as 1-D
+  segments; 842,301,952 parameters; t = 10.
 
 Distributions: gradient bf16 = bf16(N(0, 1e-3)) (drawn in fp32, converted
 by torch), master ~ N(0, 0.02), m ~ N(0, 1e-4), v = N(0, 1e-3)^2 (square of
@@ -128,6 +132,26 @@ def _llama_full():
     return segs
 
 
+def shard_range(numel: int, ranks: int, rank: int) -> tuple[int, int]:
+    """[begin, end) of the elements rank owns when a tensor's flat range is
+    split into `ranks` contiguous pieces (the first numel % ranks get one
+    extra element)."""
+    q, r = divmod(numel, ranks)
+    begin = rank * q + min(rank, r)
+    return begin, begin + q + (1 if rank < r else 0)
+
+
+def _llama_full_shard(ranks: int, rank: int):
+    segs = []
+    for label, shape in _llama_full():
+        n = 1
+        for d in shape:
+            n *= d
+        b, e = shard_range(n, ranks, rank)
+        segs.append((f"{label}[{b}:{e}]", (e - b,)))
+    return segs
+
+
 WORKLOADS = {
     "gpt2_cattn_first2": Workload(
         "gpt2_cattn_first2", 1, _gpt2_first2(), step=1, fresh_state=True,
@@ -149,6 +173,11 @@ WORKLOADS = {
         "llama7b_lora_r16", 5, _llama_lora_r16(), step=10,
         description="rank-16 LoRA adapters on all 7 linear projections of 32 "
                     "Llama-2-7B layers: 448 tensors, bf16 grad, t=10"),
+    "llama7b_full_shard8": Workload(
+        "llama7b_full_shard8", 6, _llama_full_shard(8, 0), step=10,
+        description="one of 8 data-parallel ranks' share of the whole "
+                    "Llama-2-7B shape: the first eighth of each of the 291 "
+                    "tensors, bf16 grad, t=10"),
 }
 
 

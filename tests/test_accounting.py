@@ -37,6 +37,7 @@ def test_state_layout_is_16_bytes():
     ("llama7b_layer", 202_383_360, 9),
     ("llama7b_full", 6_738_415_616, 291),
     ("llama7b_lora_r16", 39_976_960, 448),
+    ("llama7b_full_shard8", 842_301_952, 291),
 ])
 def test_workload_sizes(name, params, nseg):
     w = synth.WORKLOADS[name]
@@ -49,3 +50,21 @@ def test_resident_and_slot_footprints():
     slot = synth.WORKLOADS["llama7b_layer"].params * 16
     assert abs(slot / 1e9 - 3.238) < 0.001                 # one layer slot
     assert full < 288e9 / 1.3                              # room for orig + delta on one GPU
+
+
+@pytest.mark.parametrize("numel", [0, 1, 7, 8, 9, 4096 * 3 + 5, 32000 * 4096])
+@pytest.mark.parametrize("ranks", [1, 2, 3, 8])
+def test_shard_ranges_partition(numel, ranks):
+    """Rank ranges are contiguous, in order, cover every element once and
+    differ in length by at most one."""
+    ranges = [synth.shard_range(numel, ranks, k) for k in range(ranks)]
+    assert ranges[0][0] == 0 and ranges[-1][1] == numel
+    assert all(a[1] == b[0] for a, b in zip(ranges, ranges[1:]))
+    lens = [e - b for b, e in ranges]
+    assert min(lens) >= 0 and max(lens) - min(lens) <= 1 and sum(lens) == numel
+
+
+def test_shard_workload_is_the_first_eighth():
+    full, shard = synth.WORKLOADS["llama7b_full"], synth.WORKLOADS["llama7b_full_shard8"]
+    assert shard.numels == [synth.shard_range(n, 8, 0)[1] for n in full.numels]
+    assert shard.params * 8 == full.params

@@ -390,6 +390,87 @@ def test_split_permute_pack_invariance(L):
         assert _same(cat(getattr(ref[0], f), getattr(ref[1], f)), getattr(packed, f)), f
 
 
+def test_rank_shards_equal_whole_call(L):
+    """Data-parallel ownership: eight calls, call k over rank k's contiguous
+    eighth of every tensor (views; where numel % 8 != 0 the ranks after the
+    first start unaligned), give the same bytes as one call over the whole
+    tensors, which itself matches the oracle."""
+    sizes = [4096 * 4096, 11008 * 512, 4096, 4096 * 3 + 5, 13, 7]
+    segs, snaps = build_segments(L, sizes, 61, delta="all")
+    sharded = _clone_segs(L, segs)
+    L.adamw_step(segs, step=10, **HP)
+    for k in range(8):
+        views = []
+        for s in sharded:
+            b, e = synth.shard_range(s.master.numel(), 8, k)
+            if e > b:
+                sl = slice(b, e)
+                views.append(L.AdamwSegment(s.master[sl], s.exp_avg[sl], s.exp_avg_sq[sl],
+                                            s.grad[sl], s.weight[sl], s.orig[sl], s.delta[sl]))
+        L.adamw_step(views, step=10, **HP)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(segs, sharded)):
+        for f in ("master", "exp_avg", "exp_avg_sq", "weight", "delta"):
+            assert _same(getattr(a, f), getattr(b, f)), (i, f)
+    check_segments(segs[2:], snaps[2:], oracle_consts(HP, 10), "whole ")
+
+
+def _fill_flat(segs, sizes, seed):
+    snaps = []
+    for i, (s, n) in enumerate(zip(segs, sizes)):
+        k = seed + 10 * i
+        s.master.copy_(_f32(n, 0.02, k))
+        s.exp_avg.copy_(_f32(n, 1e-4, k + 1))
+        s.exp_avg_sq.copy_(_f32(n, 1e-3, k + 2, square=True))
+        if s.grad is not None:
+            s.grad.copy_(_bf16(n, 1e-3, k + 3))
+        if s.orig is not None:
+            s.orig.copy_(s.master.to(torch.bfloat16))
+        snaps.append({"master": to_np(s.master), "m": to_np(s.exp_avg), "v": to_np(s.exp_avg_sq),
+                      "grad": None if s.grad is None else to_np(s.grad),
+                      "orig": None if s.orig is None else to_np(s.orig)})
+    return snaps
+
+
+FLAT_SIZES = [70001, 4096, 5, 1, 0, 3 * 4096 + 5, 256]
+
+
+def test_flat_state_step_matches_oracle(L):
+    """Segments that are views of flat per-kind buffers (flat_adamw_state):
+    ragged sizes including an empty tensor, delta on, every element."""
+    fs, segs = L.flat_adamw_state(FLAT_SIZES, delta=True, device=DEV)
+    snaps = _fill_flat(segs, FLAT_SIZES, 71000)
+    L.adamw_step(segs, step=7, **HP)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(HP, 7), "flat ")
+
+
+def test_flat_state_resident_microbatches(L):
+    """Flat state with three resident micro-batch gradient buffers, stepped
+    through an AdamwPlan: K accumulations then the step, bit for bit."""
+    K = 3
+    fs, segs = L.flat_adamw_state(FLAT_SIZES, grad=None, delta=True, microbatches=K, device=DEV)
+    snaps = _fill_flat(segs, FLAT_SIZES, 72000)
+    mbs = []
+    for i, n in enumerate(FLAT_SIZES):
+        views = [fs.view(f"mb{k}", i) for k in range(K)]
+        for k, v in enumerate(views):
+            v.copy_(_bf16(n, 1e-3, 72500 + 10 * i + k))
+        mbs.append(views)
+    L.AdamwPlan(segs, microbatch_grads=mbs).step(step=12, **HP)
+    torch.cuda.synchronize()
+    c = oracle_consts(HP, 12)
+    for i, (seg, h, gs) in enumerate(zip(segs, snaps, mbs)):
+        if FLAT_SIZES[i] == 0:
+            continue
+        ref = _accumulate_then_step(h, [to_np(g) for g in gs], c, h["orig"])
+        compare_f32(to_np(seg.master), ref["master"], f"flat mb seg{i}.master")
+        compare_f32(to_np(seg.exp_avg), ref["m"], f"flat mb seg{i}.m")
+        compare_f32(to_np(seg.exp_avg_sq), ref["v"], f"flat mb seg{i}.v")
+        compare_bf16(to_np(seg.weight), ref["weight"], f"flat mb seg{i}.weight")
+        compare_f32(to_np(seg.delta), ref["delta"], f"flat mb seg{i}.delta")
+
+
 def test_plans_match_direct_calls(L):
     """AdamwPlan / AccumPlan (arguments marshalled once) == the direct calls."""
     sizes = [4099, 256, 70001]
@@ -634,11 +715,13 @@ def test_llama7b_layer_accumulate_then_step(L):
     torch.cuda.empty_cache()
 
 
-def test_llama7b_full_resident_sampled(L):
-    """Whole 7B shape resident (291 tensors, ~148 GB with delta): two steps
-    (t=10 with delta, t=11 without), checked on sampled elements of every
-    tensor, including each tensor's first and last 2048."""
-    w = synth.WORKLOADS["llama7b_full"]
+@pytest.mark.parametrize("workload", ["llama7b_full", "llama7b_full_shard8"])
+def test_llama7b_full_resident_sampled(L, workload):
+    """Whole 7B shape resident (291 tensors, ~148 GB with delta), and one of 8
+    data-parallel ranks' share of it: two steps (t=10 with delta, t=11
+    without), checked on sampled elements of every tensor, including each
+    tensor's first and last 2048."""
+    w = synth.WORKLOADS[workload]
     segs = _workload_segments(L, w, True)
     rng = np.random.default_rng(4)
     idx = []

@@ -344,6 +344,43 @@ def last_dim(shape):
     return shape[-1]
 
 
+def test_flat_q8_state_step_matches_oracle(L):
+    """int8-moment segments that are views of flat buffers (flat_q8_state):
+    codes at 64-element offsets of shared buffers, scales at row offsets of
+    another; bf16 gradient, delta on; every element against the oracle."""
+    numels, row_lens = [4096 * 3, 11008 * 2 + 5, 100, 16 * 30, 0, 4099], [4096, 11008, 7, 16, 5, 4099]
+    el, rw, segs = L.flat_q8_state(numels, row_lens, grad="bf16", delta=True, device=DEV)
+    refs = []
+    for i, (s, n, rl) in enumerate(zip(segs, numels, row_lens)):
+        k = 73000 + 10 * i
+        master = host_f32(n, 0.02, k)
+        mq = oracle.quantize_rows(host_f32(n, 1e-4, k + 1), rl)
+        vq = oracle.quantize_rows(host_f32(n, 1e-3, k + 2, square=True), rl)
+        g = host_bf16(n, 1e-3, k + 3)
+        orig = oracle.rne16(master)
+        s.master.copy_(torch.from_numpy(master))
+        s.exp_avg.codes.copy_(torch.from_numpy(mq[0]))
+        s.exp_avg.scale.copy_(torch.from_numpy(mq[1]))
+        s.exp_avg_sq.codes.copy_(torch.from_numpy(vq[0]))
+        s.exp_avg_sq.scale.copy_(torch.from_numpy(vq[1]))
+        s.grad.copy_(torch.from_numpy(g.view(np.int16)).view(torch.bfloat16))
+        s.orig.copy_(torch.from_numpy(orig.view(np.int16)).view(torch.bfloat16))
+        refs.append((master, mq, vq, g, orig))
+    L.adamw_step_q8(segs, step=9, **HP)
+    torch.cuda.synchronize()
+    consts = oracle_consts(HP, 9)
+    for i, (s, (master, mq, vq, g, orig)) in enumerate(zip(segs, refs)):
+        m, v = (mq[0].copy(), mq[1].copy()), (vq[0].copy(), vq[1].copy())
+        w, d = oracle.adamw_step_q8(master, m, v, g, consts, row_lens[i], orig=orig)
+        tag = f"flat q8 seg{i}"
+        compare_f32(to_np(s.master), master, tag + ".master")
+        compare_bf16(to_np(s.weight), w, tag + ".weight")
+        compare_f32(to_np(s.delta), d, tag + ".delta")
+        for name, dq, ref in (("m", s.exp_avg, m), ("v", s.exp_avg_sq, v)):
+            compare_codes(dq.codes, ref[0], f"{tag}.{name}.codes")
+            compare_f32(to_np(dq.scale), ref[1], f"{tag}.{name}.scale")
+
+
 def test_llama7b_attn_last4_q8_full(L):
     """Llama-2-7B q,k,v,o of the last 4 layers (268 M parameters, rows of
     4096) with int8 moments, bf16 gradient and delta: every element checked."""

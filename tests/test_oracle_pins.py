@@ -516,3 +516,23 @@ def test_merge_delta_zero_delta_and_bruteforce():
     mval = oracle.bf16_to_f32(got[4:]).astype(np.float64)
     ulp16 = np.spacing(np.abs(mval).astype(np.float32)).astype(np.float64) * 65536
     assert np.all(np.abs(mval - exact) <= 0.5 * ulp16 + np.spacing(np.abs(exact).astype(np.float32)))
+
+
+def test_thread_count_does_not_change_results():
+    """The oracle's loops run element by element, so one thread and all
+    threads must give identical bytes."""
+    n = 200_003
+    cores = oracle.num_threads()
+    outs = []
+    try:
+        for t in (1, max(2, cores)):
+            oracle.set_num_threads(t)
+            assert oracle.num_threads() == t
+            master, m, v, grad = rng_state(n, 77)
+            wb, delta = oracle.adamw_step(master, m, v, grad, consts(10), orig=oracle.rne16(master))
+            outs.append([a.view(np.uint32) if a.dtype == np.float32 else a
+                         for a in (master, m, v, wb, delta)])
+    finally:
+        oracle.set_num_threads(cores)
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
