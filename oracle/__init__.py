@@ -57,7 +57,13 @@ def _load():
         return _lib
     if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         build()
-    lib = ctypes.CDLL(_LIB)
+    _lib = bind(ctypes.CDLL(_LIB))
+    return _lib
+
+
+def bind(lib):
+    """Declare the C signatures on a loaded copy of the oracle library (the
+    tests also bind copies built from deliberately altered sources)."""
     i64, f64, i32 = ctypes.c_int64, ctypes.c_double, ctypes.c_int
     vp = ctypes.c_void_p
     lib.oracle_rne16.argtypes = [ctypes.c_float]
@@ -82,7 +88,6 @@ def _load():
     lib.oracle_num_threads.restype = i32
     lib.oracle_set_num_threads.argtypes = [i32]
     lib.oracle_set_num_threads.restype = None
-    _lib = lib
     return lib
 
 
