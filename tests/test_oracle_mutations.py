@@ -52,6 +52,7 @@ MATH_PINS = [
     ("q8 special rows", Q.test_special_rows),
     ("q8 subnormal scale", Q.test_subnormal_scale_keeps_codes_in_range),
     ("q8 step on grid moments", lambda: Q.test_q8_step_is_the_fp32_step_on_dequantized_state("bf16")),
+    ("q8 step, int8 gradient", lambda: Q.test_q8_step_is_the_fp32_step_on_dequantized_state("q8")),
     ("q8 fresh step", Q.test_q8_step_fresh_state_first_step_closed_form),
     ("q8 accumulation on grid", Q.test_q8_accumulation_exact_on_grid),
 ]
@@ -162,6 +163,59 @@ def test_unaltered_copy_passes_every_pin(source, tmp_path):
 @pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_planted_mistake_fails_a_pin(source, tmp_path, name, edits):
     with bound(build_copy(source, edits, tmp_path, name)):
+        caught = first_failure(MATH_PINS)
+    assert caught is not None, f"{name}: no pin grounded outside the oracle fails"
+    print(f"{name}: caught by {caught}")
+
+
+# Mistakes in the Python composition of the int8 functions (oracle/__init__.py):
+# (name, [(text, replacement)])
+PY_MUTANTS = [
+    ("int8_step_skips_requantization",
+     [("            arr[0][...] = q\n            arr[1][...] = s", "            pass")]),
+    ("int8_overwrite_adds_to_old_accumulator",
+     [("        acc = np.zeros(n, dtype=np.float32)",
+       "        acc = dequantize_rows(acc_q, acc_scale, row_len)"),
+      ("    grad_accum(acc, grad_bf16, overwrite)", "    grad_accum(acc, grad_bf16, False)")]),
+    ("int8_gradient_not_dequantized",
+     [("        grad = dequantize_rows(grad[0], grad[1], row_len)",
+       "        grad = grad[0].astype(np.float32)")]),
+]
+
+
+@contextlib.contextmanager
+def python_copy(edits, directory, name):
+    """A copy of the oracle package's module with `edits`, bound to the real
+    library, put in place of `oracle` inside the pin modules."""
+    import importlib.util
+    with open(oracle.__file__) as f:
+        text = f.read()
+    for old, new in edits:
+        assert text.count(old) == 1, f"{name}: edit target not found once: {old!r}"
+        text = text.replace(old, new)
+    path = directory / f"oracle_{name}.py"
+    path.write_text(text)
+    spec = importlib.util.spec_from_file_location(f"oracle_{name}", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    mod._lib = oracle._load()
+    saved = P.oracle, Q.oracle
+    P.oracle = Q.oracle = mod
+    try:
+        yield
+    finally:
+        P.oracle, Q.oracle = saved
+
+
+def test_unaltered_python_copy_passes_every_pin(tmp_path):
+    with python_copy([], tmp_path, "unaltered"):
+        for label, fn in MATH_PINS:
+            fn()
+
+
+@pytest.mark.parametrize("name,edits", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_planted_composition_mistake_fails_a_pin(tmp_path, name, edits):
+    with python_copy(edits, tmp_path, name):
         caught = first_failure(MATH_PINS)
     assert caught is not None, f"{name}: no pin grounded outside the oracle fails"
     print(f"{name}: caught by {caught}")
