@@ -25,6 +25,7 @@ and the CPU oracle timed on a bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import statistics
 import hashlib
 import json
 import os
@@ -291,6 +292,7 @@ def resident_bench(torch, L, synth, a):
                      "traffic": traffic_for(key, a.layout), "kernel": "adamw_tile_kernel",
                      "algorithmic_bytes_per_launch": P * step_bytes,
                      "avg_launch_ms": adamw_ms, "min_launch_ms": min(adamw_ms_list),
+                     "median_launch_ms": statistics.median(adamw_ms_list),
                      "max_launch_ms": max(adamw_ms_list)},
         "pipelined": {"ms_per_step": pipelined_ms,
                       "hbm_gbps": per_step / (pipelined_ms * 1e-3) / 1e9,
@@ -400,13 +402,32 @@ def cpu_baseline(segs, w, hp, delta, seconds, microbatches=None):
     finally:
         oracle.set_num_threads(cores)
     return {"value": n * reps / el, "unit": "params/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "host": host_info(),
             "sample": f"{w.segments[0][0]} ({n} params), {reps} oracle steps in {el:.1f} s, "
                       f"delta {'on' if delta else 'off'}"
                       + (f", each with {len(microbatches)} accumulations" if microbatches else "")
                       + "; C oracle, OpenMP",
             "single_thread": {"value": n * reps1 / el1, "unit": "params/s", "cores": 1,
                               "sample": f"the same step, {reps1} times in {el1:.1f} s"}}
+
+
+def host_info():
+    """CPU model, logical CPUs and RAM of the host the oracle ran on."""
+    info = {"logical_cpus": os.cpu_count()}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu"] = line.split(":", 1)[1].strip()
+                    break
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal"):
+                    info["ram_gib"] = round(int(line.split()[1]) / 2 ** 20, 1)
+                    break
+    except OSError:
+        pass
+    return info
 
 
 def timed_loop(fn, seconds):
@@ -528,6 +549,7 @@ def q8_bench(torch, L, synth, a):
                      "traffic": traffic_for(key, a.layout), "kernel": "adamw_q8_kernel",
                      "algorithmic_bytes_per_launch": step_bytes,
                      "avg_launch_ms": adamw_ms, "min_launch_ms": min(adamw_ms_list),
+                     "median_launch_ms": statistics.median(adamw_ms_list),
                      "max_launch_ms": max(adamw_ms_list)},
         "pipelined": {"ms_per_step": pipelined_ms,
                       "hbm_gbps": per_step / (pipelined_ms * 1e-3) / 1e9,
@@ -812,6 +834,15 @@ def slot_stream_bench(torch, L, synth, a):
                    / (s0["kernel_ms"] * 1e-3) / 1e9,
                    "ms_per_param_billion": wall / (P / 1e9),
                    "projected_full_7b_ms": wall * full_params / P},
+    }
+    st = line["stream"]
+    # "fully hidden": only the pipeline's tail is exposed, and the copies
+    # run at (nearly) their standalone rate while overlapped
+    st["hidden"] = {
+        "exposed_over_last_kernel": st["exposed_ms"] / st["last_kernel_ms"]
+        if st["last_kernel_ms"] > 0 else None,
+        "h2d_over_standalone": st["h2d_gbps"] / h2d_gbps if h2d_gbps else None,
+        "d2h_over_standalone": st["d2h_gbps"] / d2h_gbps if d2h_gbps else None,
     }
     return line
 
