@@ -149,8 +149,9 @@ def traffic_for(key, layout):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: --gpus {a.gpus}: this build runs on one GPU only; the multi-GPU "
-              "(sharded) layout is described but not built", file=sys.stderr)
+        print(f"bench.py: --gpus {a.gpus}: only one GPU is supported; the data-parallel "
+              "(sharded) layout is measured on one rank's share instead "
+              "(--workload llama7b_full_shard8)", file=sys.stderr)
         sys.exit(2)
 
     import torch
