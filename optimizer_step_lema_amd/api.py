@@ -42,8 +42,12 @@ def _check(t: Optional[torch.Tensor], dtype, n: int, name: str, where: str = "cu
         raise ValueError(f"{name}: expected {n} elements, got {t.numel()}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
-    if where == "cuda" and not t.is_cuda:
-        raise ValueError(f"{name}: must be a GPU tensor")
+    if where == "cuda":
+        if not t.is_cuda:
+            raise ValueError(f"{name}: must be a GPU tensor")
+        if t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{name}: on {t.device}, but the current device is "
+                             f"cuda:{torch.cuda.current_device()} (the library launches there)")
     if where == "cpu" and t.is_cuda:
         raise ValueError(f"{name}: must be a host tensor")
     return t.data_ptr() if n > 0 else 0
