@@ -715,6 +715,47 @@ def test_llama7b_layer_accumulate_then_step(L):
     torch.cuda.empty_cache()
 
 
+def _boundary_samples(n, rng):
+    """Element indices around every power of two from 2^20 up to n, where a
+    32-bit element or byte offset would wrap, plus both ends and random ones."""
+    idx = [np.arange(2048), np.arange(n - 2048, n), rng.integers(0, n, 16384)]
+    e = 20
+    while (1 << e) < n:
+        b = 1 << e
+        idx.append(np.arange(max(0, b - 600), min(n, b + 600)))
+        e += 1
+    return np.unique(np.concatenate(idx))
+
+
+def test_single_segment_beyond_2_31_elements(L):
+    """One tensor of 2^31 + 4099 elements (73 GB of state with delta): every
+    offset computation past 2, 4 and 8 GiB inside one segment, checked against
+    the oracle on the elements around each power of two and at both ends."""
+    n = (1 << 31) + 4099
+    k = 90000
+    master = synth.normal(n, 0.02, k, DEV)
+    m = synth.normal(n, 1e-4, k + 1, DEV)
+    v = synth.normal(n, 1e-3, k + 2, DEV).square_()
+    grad = synth.bf16_normal(n, 1e-3, k + 3, DEV)
+    orig = master.to(torch.bfloat16)
+    weight = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    delta = torch.empty(n, device=DEV)
+    idx = torch.from_numpy(_boundary_samples(n, np.random.default_rng(7))).to(DEV)
+    before = {name: to_np(t[idx]) for name, t in
+              (("master", master), ("m", m), ("v", v), ("grad", grad), ("orig", orig))}
+    L.adamw_step([L.AdamwSegment(master, m, v, grad, weight, orig, delta)], step=10, **HP)
+    torch.cuda.synchronize()
+    ref = oracle_segment(before["master"], before["m"], before["v"], before["grad"],
+                         oracle_consts(HP, 10), before["orig"])
+    compare_f32(to_np(master[idx]), ref["master"], "2^31+ master")
+    compare_f32(to_np(m[idx]), ref["m"], "2^31+ m")
+    compare_f32(to_np(v[idx]), ref["v"], "2^31+ v")
+    compare_bf16(to_np(weight[idx]), ref["weight"], "2^31+ weight")
+    compare_f32(to_np(delta[idx]), ref["delta"], "2^31+ delta")
+    del master, m, v, grad, orig, weight, delta
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("workload", ["llama7b_full", "llama7b_full_shard8"])
 def test_llama7b_full_resident_sampled(L, workload):
     """Whole 7B shape resident (291 tensors, ~148 GB with delta), and one of 8

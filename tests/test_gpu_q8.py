@@ -381,6 +381,48 @@ def test_flat_q8_state_step_matches_oracle(L):
             compare_f32(to_np(dq.scale), ref[1], f"{tag}.{name}.scale")
 
 
+def test_q8_single_segment_beyond_2_31_elements(L):
+    """int8 moments on one tensor of 2^31 + 4096 elements in rows of 4096
+    (524,289 rows): row and element offsets past 2^31, checked against the
+    oracle on whole rows around every power-of-two element index and at both
+    ends (a row is the unit the oracle quantizes)."""
+    rl = 4096
+    n = (1 << 31) + rl
+    rows = n // rl
+    k = 91000
+    master = synth.normal(n, 0.02, k, DEV)
+    m32 = synth.normal(n, 1e-4, k + 1, DEV)
+    v32 = synth.normal(n, 1e-3, k + 2, DEV).square_()
+    mq, vq = L.Q8.empty(n, rl), L.Q8.empty(n, rl)
+    L.quantize_rows([(m32, mq), (v32, vq)])
+    del m32, v32
+    grad = synth.bf16_normal(n, 1e-3, k + 3, DEV)
+    weight = torch.empty(n, dtype=torch.bfloat16, device=DEV)
+    pick = {0, 1, rows - 2, rows - 1}
+    e = 20
+    while (1 << e) < n:
+        pick |= {max(0, (1 << e) // rl - 1), min(rows - 1, (1 << e) // rl)}
+        e += 1
+    pick = sorted(pick)
+    elems = torch.from_numpy(np.concatenate([np.arange(r * rl, (r + 1) * rl) for r in pick])).to(DEV)
+    ridx = torch.tensor(pick, device=DEV)
+    before = {"master": to_np(master[elems]), "mq": to_np(mq.codes[elems]), "ms": to_np(mq.scale[ridx]),
+              "vq": to_np(vq.codes[elems]), "vs": to_np(vq.scale[ridx]), "g": to_np(grad[elems])}
+    L.adamw_step_q8([L.AdamwQ8Segment(master, mq, vq, grad, weight)], step=10, **HP)
+    torch.cuda.synchronize()
+    mref, vref = (before["mq"].copy(), before["ms"].copy()), (before["vq"].copy(), before["vs"].copy())
+    mref_master = before["master"].copy()
+    w, _ = oracle.adamw_step_q8(mref_master, mref, vref, before["g"], oracle_consts(HP, 10), rl)
+    compare_f32(to_np(master[elems]), mref_master, "2^31+ q8 master")
+    compare_bf16(to_np(weight[elems]), w, "2^31+ q8 weight")
+    compare_codes(mq.codes[elems], mref[0], "2^31+ q8 m codes")
+    compare_codes(vq.codes[elems], vref[0], "2^31+ q8 v codes")
+    compare_f32(to_np(mq.scale[ridx]), mref[1], "2^31+ q8 m scales")
+    compare_f32(to_np(vq.scale[ridx]), vref[1], "2^31+ q8 v scales")
+    del master, mq, vq, grad, weight
+    torch.cuda.empty_cache()
+
+
 def test_llama7b_attn_last4_q8_full(L):
     """Llama-2-7B q,k,v,o of the last 4 layers (268 M parameters, rows of
     4096) with int8 moments, bf16 gradient and delta: every element checked."""
