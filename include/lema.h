@@ -41,6 +41,10 @@
  *   - Every argument is validated before any HIP call: on any error nothing
  *     is enqueued and nothing is modified.  HIP failures return LEMA_ERR_HIP
  *     and lema_last_hip_error() gives the raw hipError_t of this thread.
+ *   - Calls that launch kernels refuse a stream that is capturing a HIP
+ *     graph (LEMA_ERR_CAPTURE, nothing enqueued): their launch tables live
+ *     in a cache whose entries may be reused after the call, which a
+ *     captured graph would outlive.
  *   - Nothing aborts, throws or prints across this ABI.
  *   - The caller owns all tensors, streams and the step counter t; the
  *     library is stateless apart from caches of small launch tables.
@@ -68,6 +72,7 @@ typedef int32_t lema_status;
 #define LEMA_ERR_NOT_PINNED (-6)  /* host memory is not page-locked                    */
 #define LEMA_ERR_HIP        (-7)  /* the HIP runtime reported an error                 */
 #define LEMA_ERR_ALIGN      (-8)  /* pointer not aligned to its element size           */
+#define LEMA_ERR_CAPTURE    (-9)  /* the stream is capturing a HIP graph               */
 
 /* Static string naming a status (never NULL). */
 const char *lema_status_string(lema_status s);

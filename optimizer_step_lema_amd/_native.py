@@ -21,6 +21,7 @@ LEMA_ERR_OVERLAP = -5
 LEMA_ERR_NOT_PINNED = -6
 LEMA_ERR_HIP = -7
 LEMA_ERR_ALIGN = -8
+LEMA_ERR_CAPTURE = -9
 
 LEMA_GRAD_BF16 = 0
 LEMA_GRAD_FP32 = 1

@@ -327,6 +327,11 @@ lema_status launch_on_table(const std::vector<unsigned char> &bytes, hipStream_t
     DeviceState *d = nullptr;
     lema_status st = device_state(&d, nullptr);
     if (st != LEMA_OK) return st;
+    // a captured graph would keep using a table the cache may later reuse
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    hipError_t ce = hipStreamIsCapturing(stream, &capture);
+    if (ce != hipSuccess) return hip_failed(ce);
+    if (capture != hipStreamCaptureStatusNone) return LEMA_ERR_CAPTURE;
     std::lock_guard<std::mutex> lock(d->mu);
     TableEntry *t = nullptr;
     st = acquire_table(*d, bytes, stream, &t);
@@ -432,6 +437,7 @@ const char *lema_status_string(lema_status s) {
     case LEMA_ERR_NOT_PINNED: return "LEMA_ERR_NOT_PINNED: host memory is not page-locked";
     case LEMA_ERR_HIP: return "LEMA_ERR_HIP: HIP runtime error (see lema_last_hip_error)";
     case LEMA_ERR_ALIGN: return "LEMA_ERR_ALIGN: pointer not aligned to its element size";
+    case LEMA_ERR_CAPTURE: return "LEMA_ERR_CAPTURE: the stream is capturing a HIP graph";
     default: return "unknown lema_status";
     }
 }

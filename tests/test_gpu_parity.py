@@ -471,6 +471,25 @@ def test_flat_state_resident_microbatches(L):
         compare_f32(to_np(seg.delta), ref["delta"], f"flat mb seg{i}.delta")
 
 
+def test_rejects_graph_capture(L):
+    """A stream capturing a HIP graph is refused before anything is enqueued:
+    the launch tables live in a cache a captured graph would outlive."""
+    from optimizer_step_lema_amd import _native as N
+    segs, snaps = build_segments(L, [4099], 96)
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with pytest.raises(N.LemaError) as e:
+        with torch.cuda.graph(graph, stream=side):
+            L.adamw_step(segs, step=3, **HP)
+    assert e.value.status == N.LEMA_ERR_CAPTURE
+    torch.cuda.synchronize()
+    # nothing ran: the state is still the input, and an ordinary call works
+    assert np.array_equal(to_np(segs[0].master).view(np.uint32), snaps[0]["master"].view(np.uint32))
+    L.adamw_step(segs, step=3, **HP)
+    torch.cuda.synchronize()
+    check_segments(segs, snaps, oracle_consts(HP, 3), "after capture ")
+
+
 def test_plans_match_direct_calls(L):
     """AdamwPlan / AccumPlan (arguments marshalled once) == the direct calls."""
     sizes = [4099, 256, 70001]
