@@ -490,6 +490,46 @@ def test_rejects_graph_capture(L):
     check_segments(segs, snaps, oracle_consts(HP, 3), "after capture ")
 
 
+def test_concurrent_host_threads(L):
+    """Eight host threads, each with its own stream and segment list, call the
+    library at once (ctypes releases the GIL, so the calls really overlap in
+    the launch-table cache); every thread's five steps must match the oracle."""
+    import threading
+    groups = [build_segments(L, [4099 + 64 * i, 300, 70001], 200 + i, delta="all")
+              for i in range(8)]
+    streams = [torch.cuda.Stream() for _ in groups]
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(i):
+        try:
+            segs, _ = groups[i]
+            for t in range(1, 6):
+                L.adamw_step(segs, step=t, stream=streams[i], **HP)
+        except Exception as e:  # reported below
+            errors.append((i, e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(groups))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i, (segs, snaps) in enumerate(groups):
+        for s, h in zip(segs, snaps):
+            master, m, v = h["master"].copy(), h["m"].copy(), h["v"].copy()
+            for t in range(1, 6):
+                ref = oracle_segment(master, m, v, h["grad"], oracle_consts(HP, t), h["orig"])
+                master, m, v = ref["master"], ref["m"], ref["v"]
+            tag = f"thread{i} n={s.master.numel()}"
+            compare_f32(to_np(s.master), ref["master"], tag + ".master")
+            compare_f32(to_np(s.exp_avg), ref["m"], tag + ".m")
+            compare_f32(to_np(s.exp_avg_sq), ref["v"], tag + ".v")
+            compare_bf16(to_np(s.weight), ref["weight"], tag + ".weight")
+            compare_f32(to_np(s.delta), ref["delta"], tag + ".delta")
+
+
 def test_plans_match_direct_calls(L):
     """AdamwPlan / AccumPlan (arguments marshalled once) == the direct calls."""
     sizes = [4099, 256, 70001]
