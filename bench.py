@@ -641,7 +641,7 @@ def q8_cpu_baseline(seg, w, row_len, hp, delta, seconds):
     reps, el = timed_loop(lambda: oracle.adamw_step_q8(master, m, v, grad, c, row_len, orig=orig),
                           seconds)
     return {"value": n * reps / el, "unit": "params/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "host": host_info(),
             "sample": f"{w.segments[0][0]} ({n} params, rows of {row_len}), {reps} oracle "
                       f"int8 steps in {el:.1f} s, delta {'on' if delta else 'off'}; C oracle, "
                       "OpenMP, numpy glue"}
