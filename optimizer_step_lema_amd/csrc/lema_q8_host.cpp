@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <cstring>
+#include <utility>
 #include <vector>
 
 #include "lema.h"
@@ -64,28 +65,39 @@ Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok, int chunks_max) {
 
 uintptr_t bits(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
-// Launch `recs` in at most two groups, one per workgroup size.
+// Launch `recs` in at most two groups, one per workgroup size.  Both groups'
+// tables are built and checked before the first launch, so a size error
+// enqueues nothing.
 template <class LaunchFn>
 lema_status launch_groups(const std::vector<Q8Rec> &recs, int chunks_max, hipStream_t stream,
                           const LaunchFn &launch) {
+    struct Group {
+        int block;
+        int n;
+        uint64_t blocks;
+        std::vector<unsigned char> bytes;
+    };
+    std::vector<Group> groups;
     for (int block : {kQBlock, kQBlockWide}) {
         std::vector<Q8Rec> sel;
         for (const Q8Rec &r : recs)
             if (block_of(r, chunks_max) == block) sel.push_back(r);
         if (sel.empty()) continue;
-        const int n = static_cast<int>(sel.size());
-        std::vector<unsigned char> bytes(q8_table_bytes(n), 0);
-        uint32_t *begin = reinterpret_cast<uint32_t *>(bytes.data());
-        uint64_t blocks = 0;
-        for (int i = 0; i < n; ++i) {
-            begin[i] = static_cast<uint32_t>(blocks);
-            blocks += blocks_of(sel[i], chunks_max);
-            if (blocks > 0xFFF00000ull) return LEMA_ERR_SIZE;
+        Group g{block, static_cast<int>(sel.size()), 0, {}};
+        g.bytes.assign(q8_table_bytes(g.n), 0);
+        uint32_t *begin = reinterpret_cast<uint32_t *>(g.bytes.data());
+        for (int i = 0; i < g.n; ++i) {
+            begin[i] = static_cast<uint32_t>(g.blocks);
+            g.blocks += blocks_of(sel[i], chunks_max);
+            if (g.blocks > 0xFFF00000ull) return LEMA_ERR_SIZE;
         }
-        begin[n] = static_cast<uint32_t>(blocks);
-        std::memcpy(bytes.data() + table_tiles_bytes(n), sel.data(), sizeof(Q8Rec) * n);
-        lema_status st = launch_on_table(bytes, stream, [&](const void *table) {
-            return launch(table, n, static_cast<uint32_t>(blocks), block);
+        begin[g.n] = static_cast<uint32_t>(g.blocks);
+        std::memcpy(g.bytes.data() + table_tiles_bytes(g.n), sel.data(), sizeof(Q8Rec) * g.n);
+        groups.push_back(std::move(g));
+    }
+    for (const Group &g : groups) {
+        lema_status st = launch_on_table(g.bytes, stream, [&](const void *table) {
+            return launch(table, g.n, static_cast<uint32_t>(g.blocks), g.block);
         });
         if (st != LEMA_OK) return st;
     }
