@@ -177,10 +177,17 @@ struct DeviceState {
 
 DeviceState g_devices[kMaxDevices];
 
-// FNV-1a over the table bytes: a cheap first test before comparing bytes.
+// FNV-1a over the table's 8-byte words (then any tail bytes): a cheap first
+// test before comparing bytes.
 uint64_t table_hash(const std::vector<unsigned char> &bytes) {
     uint64_t h = 1469598103934665603ull;
-    for (unsigned char c : bytes) h = (h ^ c) * 1099511628211ull;
+    const size_t words = bytes.size() / 8;
+    for (size_t i = 0; i < words; ++i) {
+        uint64_t w;
+        std::memcpy(&w, bytes.data() + 8 * i, 8);
+        h = (h ^ w) * 1099511628211ull;
+    }
+    for (size_t i = 8 * words; i < bytes.size(); ++i) h = (h ^ bytes[i]) * 1099511628211ull;
     return h;
 }
 
