@@ -298,8 +298,7 @@ def resident_bench(torch, L, synth, a):
         "pipelined": {"ms_per_step": pipelined_ms,
                       "hbm_gbps": per_step / (pipelined_ms * 1e-3) / 1e9,
                       "params_per_s": P / (pipelined_ms * 1e-3)},
-        "device": {"compute_units": info["compute_units"],
-                   "tile_elements": info["tile_elements"]},
+        "device": info,
         "host_wall_s_timed_region": wall,
     }
     if accum_ms_list:

@@ -48,6 +48,14 @@ lema_status lema_probe_fp32(const float *a, const float *b, float *quot, float *
  */
 lema_status lema_table_cache_stats(int64_t out[4]);
 
+/* The LDS size per compute unit the current device reports, and the LDS the
+ * AdamW step reserves per workgroup (the kernel uses none) to cap how many of
+ * its workgroups share a CU: about 13, or 10 when the step reads
+ * `microbatches` >= 4 resident micro-batch gradients (0 = an ordinary step).
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE (microbatches < 0), LEMA_ERR_HIP. */
+lema_status lema_step_lds_reservation(int32_t microbatches, int32_t *lds_per_cu,
+                                      int32_t *reserved_bytes);
+
 /* Compute units of the current device and the elements one workgroup takes
  * per tile in the AdamW and accumulation kernels. */
 lema_status lema_device_info(int32_t *compute_units, int32_t *tile_elements);

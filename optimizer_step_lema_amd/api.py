@@ -700,6 +700,14 @@ def table_cache_stats() -> dict:
 
 
 def device_info() -> dict:
+    lib = N.load()
     cus, tile = ctypes.c_int32(), ctypes.c_int32()
-    N.check(N.load().lema_device_info(ctypes.byref(cus), ctypes.byref(tile)), "lema_device_info")
-    return {"compute_units": cus.value, "tile_elements": tile.value}
+    N.check(lib.lema_device_info(ctypes.byref(cus), ctypes.byref(tile)), "lema_device_info")
+    lds, res, res_mb = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    N.check(lib.lema_step_lds_reservation(0, ctypes.byref(lds), ctypes.byref(res)),
+            "lema_step_lds_reservation")
+    N.check(lib.lema_step_lds_reservation(8, ctypes.byref(lds), ctypes.byref(res_mb)),
+            "lema_step_lds_reservation")
+    return {"compute_units": cus.value, "tile_elements": tile.value,
+            "lds_per_cu": lds.value, "step_lds_reserved": res.value,
+            "step_lds_reserved_8_microbatches": res_mb.value}

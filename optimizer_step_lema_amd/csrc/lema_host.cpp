@@ -170,6 +170,7 @@ struct DeviceState {
     std::mutex mu;
     bool ready = false;
     int cu_count = 0;
+    int lds_per_cu = 0;           // bytes of LDS per compute unit
     uint64_t clock = 0;
     std::vector<std::unique_ptr<TableEntry>> entries;
     int64_t hits = 0, uploads = 0, waits = 0;
@@ -203,6 +204,10 @@ lema_status device_state(DeviceState **out, int *device) {
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return hip_failed(e);
         d.cu_count = cus > 0 ? cus : 1;
+        int lds = 0;
+        e = hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev);
+        if (e != hipSuccess) return hip_failed(e);
+        d.lds_per_cu = lds;
         d.ready = true;
     }
     *out = &d;
@@ -349,17 +354,43 @@ lema_status launch_on_table(const std::vector<unsigned char> &bytes, hipStream_t
     return rel;
 }
 
+// Workgroups of the AdamW step kernel allowed on one CU.  Each streams
+// 7-12 KB of HBM traffic for its tile, from 5-12 arrays at once.  With every
+// CU full of them (32 per CU) the HBM stacks see so many concurrent streams
+// that they deliver 6-10% less than with about 13 (measured on MI355X over
+// 8-18 per CU, for 28-38 B per parameter); the step that reads 8 resident
+// micro-batches (48 B per parameter) does best at about 10.
+constexpr int kStepWorkgroupsPerCu = 13;
+constexpr int kStepWorkgroupsPerCuManyMb = 10;
+constexpr int kManyMicrobatches = 4;
+
+// The LDS to reserve per workgroup so that at most `per_cu` of them fit on
+// one CU (0 when the device reports no LDS size).
+uint32_t step_lds_bytes(int lds_per_cu, int per_cu) {
+    if (lds_per_cu <= 0 || per_cu <= 0) return 0;
+    const uint32_t b = static_cast<uint32_t>(lds_per_cu / per_cu) & ~255u;
+    return std::min<uint32_t>(b, 65536u);
+}
+
+uint32_t step_lds_bytes_for(int nmb) {
+    DeviceState *d = nullptr;
+    if (device_state(&d, nullptr) != LEMA_OK) return 0;   // the launch reports the error
+    return step_lds_bytes(d->lds_per_cu, nmb >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb
+                                                                  : kStepWorkgroupsPerCu);
+}
+
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
                               GradMode grad_mode, hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
+    const uint32_t lds = step_lds_bytes_for(0);
     bool with_delta = false;
     for (const SegRec &r : recs) with_delta |= r.p[6] != 0;
     TableBuild tb;
     build_table(recs, &tb);
     return launch_on_table(tb.bytes, stream, [&](const void *table) {
         return launch_adamw(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_mode,
-                            with_delta, c, stream);
+                            with_delta, c, stream, 0, lds);
     });
 }
 
@@ -367,6 +398,7 @@ lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<ui
                                   int nmb, const AdamwConsts &c, hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
+    const uint32_t lds = step_lds_bytes_for(nmb);
     bool with_delta = false;
     const int n = static_cast<int>(recs.size());
     for (int i = 0; i < n; ++i) {
@@ -379,7 +411,7 @@ lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<ui
     std::memcpy(tb.bytes.data() + table_bytes(n), lists.data(), sizeof(uint64_t) * lists.size());
     return launch_on_table(tb.bytes, stream, [&](const void *table) {
         return launch_adamw(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), kGradBf16Sum,
-                            with_delta, c, stream, nmb);
+                            with_delta, c, stream, nmb, lds);
     });
 }
 
@@ -662,6 +694,20 @@ lema_status lema_table_cache_stats(int64_t out[4]) {
     out[1] = d->uploads;
     out[2] = d->waits;
     out[3] = static_cast<int64_t>(d->entries.size());
+    return LEMA_OK;
+}
+
+lema_status lema_step_lds_reservation(int32_t microbatches, int32_t *lds_per_cu,
+                                      int32_t *reserved_bytes) {
+    if (lds_per_cu == nullptr || reserved_bytes == nullptr) return LEMA_ERR_NULL;
+    if (microbatches < 0) return LEMA_ERR_SIZE;
+    DeviceState *d = nullptr;
+    lema_status st = device_state(&d, nullptr);
+    if (st != LEMA_OK) return st;
+    *lds_per_cu = d->lds_per_cu;
+    *reserved_bytes = static_cast<int32_t>(step_lds_bytes(
+        d->lds_per_cu, microbatches >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb
+                                                         : kStepWorkgroupsPerCu));
     return LEMA_OK;
 }
 

@@ -108,9 +108,12 @@ struct AdamwConsts {
 // Kernel launches (asynchronous on `stream`).  `table` is the device copy of
 // the launch table; one workgroup runs per tile 0 .. total_tiles-1.
 // `nmb` is the micro-batch count of kGradBf16Sum (ignored otherwise).
+// `lds_bytes` of LDS are reserved per workgroup of the AdamW kernel, which
+// itself uses none: the reservation caps how many of its workgroups share a
+// CU.
 hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles,
                         GradMode grad_mode, bool with_delta, const AdamwConsts &c,
-                        hipStream_t stream, int nmb = 0);
+                        hipStream_t stream, int nmb, uint32_t lds_bytes);
 hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
                         bool overwrite, hipStream_t stream);
 hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream);

@@ -361,7 +361,8 @@ __global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restr
 // directly instead of through the thread's sticky last-error slot.  Grids
 // larger than kMaxBlocksPerLaunch are split into consecutive launches.
 hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradMode grad_mode,
-                        bool with_delta, const AdamwConsts &c, hipStream_t stream, int nmb) {
+                        bool with_delta, const AdamwConsts &c, hipStream_t stream, int nmb,
+                        uint32_t lds_bytes) {
     const void *fn;
 #define LEMA_PICK(M) with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<M, true>) \
                                 : reinterpret_cast<const void *>(&adamw_tile_kernel<M, false>)
@@ -380,7 +381,7 @@ hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradM
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
         const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
         void *args[] = {&table, &nseg, &tile0, &consts};
-        hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, 0, stream);
+        hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, lds_bytes, stream);
         if (e != hipSuccess) return e;
         tile0 += n;
     }

@@ -530,6 +530,17 @@ def test_concurrent_host_threads(L):
             compare_f32(to_np(s.delta), ref["delta"], tag + ".delta")
 
 
+def test_step_lds_reservation(L):
+    """The step reserves LDS it does not use so that about 13 of its
+    workgroups (10 with >= 4 resident micro-batches) share a CU."""
+    info = L.device_info()
+    lds, res, res_mb = info["lds_per_cu"], info["step_lds_reserved"], \
+        info["step_lds_reserved_8_microbatches"]
+    assert lds >= 64 * 1024, info
+    assert lds // res == 13 and lds // res_mb == 10, info
+    assert res % 256 == 0 and res_mb % 256 == 0 and res_mb <= 65536
+
+
 def test_plans_match_direct_calls(L):
     """AdamwPlan / AccumPlan (arguments marshalled once) == the direct calls."""
     sizes = [4099, 256, 70001]
