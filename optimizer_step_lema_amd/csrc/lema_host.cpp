@@ -366,17 +366,21 @@ constexpr int kManyMicrobatches = 4;
 
 // The LDS to reserve per workgroup so that at most `per_cu` of them fit on
 // one CU (0 when the device reports no LDS size).
-uint32_t step_lds_bytes(int lds_per_cu, int per_cu) {
+static uint32_t step_lds_bytes(int lds_per_cu, int per_cu) {
     if (lds_per_cu <= 0 || per_cu <= 0) return 0;
     const uint32_t b = static_cast<uint32_t>(lds_per_cu / per_cu) & ~255u;
     return std::min<uint32_t>(b, 65536u);
 }
 
-uint32_t step_lds_bytes_for(int nmb) {
+uint32_t occupancy_lds_bytes(int workgroups_per_cu) {
     DeviceState *d = nullptr;
     if (device_state(&d, nullptr) != LEMA_OK) return 0;   // the launch reports the error
-    return step_lds_bytes(d->lds_per_cu, nmb >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb
-                                                                  : kStepWorkgroupsPerCu);
+    return step_lds_bytes(d->lds_per_cu, workgroups_per_cu);
+}
+
+static uint32_t step_lds_bytes_for(int nmb) {
+    return occupancy_lds_bytes(nmb >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb
+                                                        : kStepWorkgroupsPerCu);
 }
 
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,

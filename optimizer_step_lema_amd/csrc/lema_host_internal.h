@@ -67,4 +67,8 @@ lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<ui
                                   int nmb, const AdamwConsts &c, hipStream_t stream);
 lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t stream);
 
+// LDS to reserve per workgroup so that at most `workgroups_per_cu` of them
+// share a CU of the current device (0 if the device cannot be queried).
+uint32_t occupancy_lds_bytes(int workgroups_per_cu);
+
 }  // namespace lema

@@ -74,6 +74,7 @@ constexpr int kQBlockWide = 1024;
 // (int8 step 5.50 TB/s at 4, 4.97 at 8, 2.47 at 16 with 256 VGPRs;
 // accumulation 4.0 TB/s at 4, 1.7 at 8, 2.5 at 16).
 constexpr int kQStepChunks = 4;
+constexpr int kQ8StepWorkgroupsPerCu = 3;     // occupancy cap of the 256-lane step
 constexpr int kQCodeChunks = 4;
 constexpr int kQWideChunks = 4;
 constexpr int64_t kQMaxRow = int64_t(kQBlockWide) * kQWideChunks * 4;   // 16384 elements
@@ -88,11 +89,16 @@ struct Q8Rec {
     int64_t rows;
     int32_t team_log2;    // lanes per row = 1 << team_log2, at most the workgroup
     int32_t chunks;       // 4-element chunks per lane
-    int32_t flags;        // kQVector: full chunks take 16/8/4-byte vector accesses
+    int32_t flags;        // kQVector: full chunks take 16/8/4-byte vector accesses;
+                          // kQPacked: packed rows
     int32_t reserved;
 };
 static_assert(sizeof(Q8Rec) == 120, "int8 segment record is 120 bytes");
 constexpr int32_t kQVector = 1;
+// Rows of 4*2^team_log2 elements (4 .. 256) on vector-aligned arrays: every
+// chunk of a lane belongs to its own row, `chunks` rows per lane, so that a
+// wavefront's chunk steps stay contiguous (lema_q8.hip, packed rows).
+constexpr int32_t kQPacked = 2;
 
 // How the int8 step reads the moments and the gradient.
 enum QGrad : int { kQGradBf16 = 0, kQGradF32 = 1, kQGradQ8 = 2 };
@@ -119,14 +125,16 @@ hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
 hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream);
 
 // int8 kernels; `block` (kQBlock or kQBlockWide) is the workgroup size the
-// table's records were sized for.
+// table's records were sized for, `packed` whether they are packed rows
+// (kQPacked, kQBlock only).  The step reserves `lds_bytes` of unused LDS per
+// workgroup, a cap on its workgroups per CU.
 hipError_t launch_adamw_q8(const void *table, int nseg, uint32_t total_blocks, bool moments_q8,
-                           QGrad grad, bool with_delta, int block, const AdamwConsts &c,
-                           hipStream_t stream);
+                           QGrad grad, bool with_delta, int block, bool packed,
+                           const AdamwConsts &c, hipStream_t stream, uint32_t lds_bytes);
 hipError_t launch_accum_q8(const void *table, int nseg, uint32_t total_blocks, bool overwrite,
-                           int block, hipStream_t stream);
+                           int block, bool packed, hipStream_t stream);
 hipError_t launch_quantize_q8(const void *table, int nseg, uint32_t total_blocks, bool dequantize,
-                              int block, hipStream_t stream);
+                              int block, bool packed, hipStream_t stream);
 
 // Measurement aids (include/lema_measure.h).
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);

@@ -307,12 +307,78 @@ __device__ __forceinline__ void quantize_store(const Team &t, uint64_t codes, co
     }
 }
 
+// ------------------------------------------------------- packed rows
+//
+// Rows of 4*S elements, S a power of two of at most 64 lanes, are packed
+// (kQPacked): a team of S lanes covers a whole row in one chunk step, so lane
+// t's chunk c holds elements 4*(t mod S) .. +3 of row  row0 + c*G + t/S
+// (G = kThreads/S teams per chunk step), and each chunk step of a wavefront
+// is one contiguous run of 256 elements.  With the mapping above such rows
+// would give a lane whole rows, and a wavefront's accesses would be strided
+// by the row length.  Teams lie inside one wavefront, so the absmax
+// reductions are shuffles only; each chunk belongs to its own row and scale.
+struct Packed {
+    int64_t row0;    // row of chunk 0
+    int G;           // rows per chunk step
+    int lane;        // lane within the team
+    int width;       // S
+};
+
+template <int kThreads, int kC>
+__device__ __forceinline__ Packed packed_of(const Q8Rec &r, uint32_t local_block) {
+    Packed p;
+    p.width = 1 << r.team_log2;
+    p.G = kThreads >> r.team_log2;
+    p.lane = int(threadIdx.x) & (p.width - 1);
+    p.row0 = int64_t(local_block) * (int64_t(kC) * p.G) + (int(threadIdx.x) >> r.team_log2);
+    return p;
+}
+
+// Chunk c of a packed lane: its row, first element and valid elements.
+struct PackedChunk {
+    int64_t row;
+    int64_t e;
+    int64_t valid;   // 0 .. 4
+    bool has_row;
+};
+
+__device__ __forceinline__ PackedChunk packed_chunk(const Packed &p, const Q8Rec &r, int c) {
+    PackedChunk k;
+    k.row = p.row0 + int64_t(c) * p.G;
+    const int64_t first = k.row * r.row_len;
+    const int64_t len = k.row < r.rows ? std::min<int64_t>(r.row_len, r.numel - first) : 0;
+    k.has_row = len > 0;
+    k.e = first + 4 * int64_t(p.lane);
+    const int64_t rem = len - 4 * int64_t(p.lane);
+    k.valid = rem <= 0 ? 0 : (rem < 4 ? rem : 4);
+    return k;
+}
+
+// Max over the lanes of a packed team; every lane of the wavefront calls it.
+__device__ __forceinline__ uint32_t packed_max(uint32_t a, int width) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1)
+        if (o < width) a = std::max(a, uint32_t(__shfl_xor(int(a), o)));
+    return a;
+}
+
+// Codes of one chunk against its row's quantization.
+__device__ __forceinline__ uint32_t quant_chunk(const QuantRow &q, f32x4 x) {
+    uint32_t w = 0;
+    if (q.ok) {
+        float near = 1.0f;
+        if (q.fast) w = quant4_fast(x, q.r, near);
+        if (!q.fast || near < kNearHalf) w = quant4_exact(x, q.s);
+    }
+    return w;
+}
+
 // ------------------------------------------------------------- AdamW
 
 // One AdamW step with int8 moments (kMomQ8) and/or an int8 gradient
 // accumulator (kGrad == kQGradQ8).  Record pointers:
 //   {master, m, m_scale, v, v_scale, grad, grad_scale, weight, orig, delta}
-template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads>
+template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads, bool kPacked>
 struct AdamwRows {
     static constexpr int kC = kThreads == kQBlockWide ? kQWideChunks : kQStepChunks;
     AdamwConsts c;
@@ -323,87 +389,164 @@ struct AdamwRows {
         float ms, vs, gs;    // old row scales (int8 arrays only)
     };
 
+    // One chunk's inputs, as loaded.
+    struct ChunkIn {
+        f32x4 w, mf, vf, g4;
+        uint32_t mc, vc, gc;
+        u32x2 gb, o2;
+    };
+
+    __device__ __forceinline__ void load_chunk(const Row &R, int64_t e, bool vector,
+                                               int64_t valid, ChunkIn &in) const {
+        in.w = load_f32(R.master, e, vector, valid);
+        if constexpr (kMomQ8) {
+            in.mc = load_codes(R.m, e, vector, valid);
+            in.vc = load_codes(R.v, e, vector, valid);
+        } else {
+            in.mf = load_f32(R.m, e, vector, valid);
+            in.vf = load_f32(R.v, e, vector, valid);
+        }
+        if constexpr (kGrad == kQGradBf16) in.gb = load_bf16_bits(R.grad, e, vector, valid);
+        if constexpr (kGrad == kQGradF32) in.g4 = load_f32(R.grad, e, vector, valid);
+        if constexpr (kGrad == kQGradQ8) in.gc = load_codes(R.grad, e, vector, valid);
+        if (R.has_delta) in.o2 = load_bf16_bits(R.orig, e, vector, valid);
+    }
+
+    // The fp32 step of one chunk with its row's old scales: stores master,
+    // weight and delta (and fp32 moments); int8 moments come back in mm, vv.
+    __device__ __forceinline__ void step_chunk(const Row &R, int64_t e, bool vector,
+                                               int64_t valid, const ChunkIn &in, float ms,
+                                               float vs, float gs, f32x4 &mm,
+                                               f32x4 &vv) const {
+        f32x4 w = in.w, g;
+        if constexpr (kMomQ8) {
+            for (int k = 0; k < 4; ++k) {
+                mm[k] = dequant(code_at(in.mc, k), ms);
+                vv[k] = dequant(code_at(in.vc, k), vs);
+            }
+        } else {
+            mm = in.mf;
+            vv = in.vf;
+        }
+        if constexpr (kGrad == kQGradQ8) {
+            for (int k = 0; k < 4; ++k) g[k] = dequant(code_at(in.gc, k), gs);
+        } else if constexpr (kGrad == kQGradBf16) {
+            g = widen_bf16(in.gb);
+        } else {
+            g = in.g4;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            float wk = w[k], mk = mm[k], vk = vv[k];
+            adamw_elem(wk, mk, vk, g[k], c);
+            w[k] = wk;
+            mm[k] = mk;
+            vv[k] = vk;
+        }
+        store_f32(R.master, e, vector, valid, w);
+        store_bf16(R.weight, e, vector, valid, w);
+        if (R.has_delta) {
+#pragma clang fp contract(off)
+            const f32x4 o = widen_bf16(in.o2);
+            const f32x4 d = {w.x - o.x, w.y - o.y, w.z - o.z, w.w - o.w};
+            store_f32(R.delta, e, vector, valid, d);
+        }
+        if constexpr (!kMomQ8) {
+            store_f32(R.m, e, vector, valid, mm);
+            store_f32(R.v, e, vector, valid, vv);
+        }
+    }
+
     // Loads, the fp32 step and the stores of master, weight, delta (and of
     // fp32 moments); int8 moments are left in mf/vf with their absmax bits.
     template <bool kFull>
     __device__ __forceinline__ void step_lane(const Team &t, const Row &R, f32x4 (&mf)[kC],
                                               f32x4 (&vf)[kC], uint32_t &am,
                                               uint32_t &av) const {
-        f32x4 w4[kC], g4[kC];
-        uint32_t mc[kC], vc[kC], gc[kC];
-        u32x2 gb[kC], o2[kC];
+        ChunkIn in[kC];
 #pragma unroll
         for (int ci = 0; ci < kC; ++ci) {
             const int64_t valid = valid_of<kFull>(t, ci);
             if (valid <= 0) continue;
-            const int64_t e = t.first + chunk_off(t, ci);
-            const bool vector = kFull || (t.vec && valid == 4);
-            w4[ci] = load_f32(R.master, e, vector, valid);
-            if constexpr (kMomQ8) {
-                mc[ci] = load_codes(R.m, e, vector, valid);
-                vc[ci] = load_codes(R.v, e, vector, valid);
-            } else {
-                mf[ci] = load_f32(R.m, e, vector, valid);
-                vf[ci] = load_f32(R.v, e, vector, valid);
-            }
-            if constexpr (kGrad == kQGradBf16) gb[ci] = load_bf16_bits(R.grad, e, vector, valid);
-            if constexpr (kGrad == kQGradF32) g4[ci] = load_f32(R.grad, e, vector, valid);
-            if constexpr (kGrad == kQGradQ8) gc[ci] = load_codes(R.grad, e, vector, valid);
-            if (R.has_delta) o2[ci] = load_bf16_bits(R.orig, e, vector, valid);
+            load_chunk(R, t.first + chunk_off(t, ci), kFull || (t.vec && valid == 4), valid, in[ci]);
         }
 
 #pragma unroll
         for (int ci = 0; ci < kC; ++ci) {
             const int64_t valid = valid_of<kFull>(t, ci);
             if (valid <= 0) continue;
-            const int64_t e = t.first + chunk_off(t, ci);
-            const bool vector = kFull || (t.vec && valid == 4);
-            f32x4 w = w4[ci], mm, vv, g;
-            if constexpr (kMomQ8) {
-                for (int k = 0; k < 4; ++k) {
-                    mm[k] = dequant(code_at(mc[ci], k), R.ms);
-                    vv[k] = dequant(code_at(vc[ci], k), R.vs);
-                }
-            } else {
-                mm = mf[ci];
-                vv = vf[ci];
-            }
-            if constexpr (kGrad == kQGradQ8) {
-                for (int k = 0; k < 4; ++k) g[k] = dequant(code_at(gc[ci], k), R.gs);
-            } else if constexpr (kGrad == kQGradBf16) {
-                g = widen_bf16(gb[ci]);
-            } else {
-                g = g4[ci];
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                float wk = w[k], mk = mm[k], vk = vv[k];
-                adamw_elem(wk, mk, vk, g[k], c);
-                w[k] = wk;
-                mm[k] = mk;
-                vv[k] = vk;
-            }
-            store_f32(R.master, e, vector, valid, w);
-            store_bf16(R.weight, e, vector, valid, w);
-            if (R.has_delta) {
-#pragma clang fp contract(off)
-                const f32x4 o = widen_bf16(o2[ci]);
-                const f32x4 d = {w.x - o.x, w.y - o.y, w.z - o.z, w.w - o.w};
-                store_f32(R.delta, e, vector, valid, d);
-            }
+            f32x4 mm, vv;
+            step_chunk(R, t.first + chunk_off(t, ci), kFull || (t.vec && valid == 4), valid, in[ci],
+                       R.ms, R.vs, R.gs, mm, vv);
             if constexpr (kMomQ8) {
                 am = absmax4(am, mm, valid);
                 av = absmax4(av, vv, valid);
                 mf[ci] = mm;
                 vf[ci] = vv;
-            } else {
-                store_f32(R.m, e, vector, valid, mm);
-                store_f32(R.v, e, vector, valid, vv);
+            }
+        }
+    }
+
+    // Packed rows: each chunk is a row of its own (see Packed).
+    __device__ __forceinline__ void packed_rows(const Q8Rec &r, uint32_t local_block) const {
+        const Row R{r.p[0], r.p[1], r.p[2], r.p[3], r.p[4], r.p[5], r.p[6], r.p[7], r.p[8],
+                    r.p[9], kDelta && r.p[9] != 0, 0.0f, 0.0f, 0.0f};
+        const Packed p = packed_of<kThreads, kC>(r, local_block);
+        PackedChunk k[kC];
+        ChunkIn in[kC];
+        float ms[kC], vs[kC], gs[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            k[c] = packed_chunk(p, r, c);
+            ms[c] = vs[c] = gs[c] = 0.0f;
+            if (k[c].has_row) {
+                if constexpr (kMomQ8) {
+                    ms[c] = as_global<gfloat>(R.m_scale)[k[c].row];
+                    vs[c] = as_global<gfloat>(R.v_scale)[k[c].row];
+                }
+                if constexpr (kGrad == kQGradQ8) gs[c] = as_global<gfloat>(R.grad_scale)[k[c].row];
+            }
+            if (k[c].valid > 0) load_chunk(R, k[c].e, k[c].valid == 4, k[c].valid, in[c]);
+        }
+        f32x4 mf[kC], vf[kC];
+        uint32_t am[kC], av[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            am[c] = av[c] = 0;
+            if (k[c].valid <= 0) continue;
+            step_chunk(R, k[c].e, k[c].valid == 4, k[c].valid, in[c], ms[c], vs[c], gs[c],
+                       mf[c], vf[c]);
+            if constexpr (kMomQ8) {
+                am[c] = absmax4(0u, mf[c], k[c].valid);
+                av[c] = absmax4(0u, vf[c], k[c].valid);
+            }
+        }
+        if constexpr (!kMomQ8) return;
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            am[c] = packed_max(am[c], p.width);
+            av[c] = packed_max(av[c], p.width);
+        }
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            if (!k[c].has_row) continue;
+            const QuantRow qm = quant_row(am[c]), qv = quant_row(av[c]);
+            if (k[c].valid > 0) {
+                store_codes(R.m, k[c].e, k[c].valid == 4, k[c].valid, quant_chunk(qm, mf[c]));
+                store_codes(R.v, k[c].e, k[c].valid == 4, k[c].valid, quant_chunk(qv, vf[c]));
+            }
+            if (p.lane == 0) {
+                as_global<gfloat>(R.m_scale)[k[c].row] = qm.s;
+                as_global<gfloat>(R.v_scale)[k[c].row] = qv.s;
             }
         }
     }
 
     __device__ __forceinline__ void operator()(const Q8Rec &r, uint32_t local_block) const {
+        if constexpr (kPacked) {      // a kernel of its own: the two paths differ in registers
+            packed_rows(r, local_block);
+            return;
+        }
         Row R{r.p[0], r.p[1], r.p[2], r.p[3], r.p[4], r.p[5], r.p[6], r.p[7], r.p[8], r.p[9],
               kDelta && r.p[9] != 0, 0.0f, 0.0f, 0.0f};
         const Team t = team_of<kThreads>(r, local_block);
@@ -442,10 +585,11 @@ struct AdamwRows {
     }
 };
 
-template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads>
+template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads, bool kPacked>
 __global__ __launch_bounds__(kThreads) void adamw_q8_kernel(const void *table, int nseg,
                                                             uint32_t block0, AdamwConsts c) {
-    block_of_table<Q8Rec>(table, nseg, block0, AdamwRows<kMomQ8, kGrad, kDelta, kThreads>{c});
+    block_of_table<Q8Rec>(table, nseg, block0,
+                          AdamwRows<kMomQ8, kGrad, kDelta, kThreads, kPacked>{c});
 }
 
 // ------------------------------------------------------ accumulation
@@ -457,7 +601,7 @@ __global__ __launch_bounds__(kThreads) void adamw_q8_kernel(const void *table, i
 // quantize {x, codes, scale} and dequantize (codes, scale -> x).
 enum RowOp : int { kAccumAdd = 0, kAccumOverwrite = 1, kQuantize = 2, kDequantize = 3 };
 
-template <RowOp kOp, int kThreads>
+template <RowOp kOp, int kThreads, bool kPacked>
 struct CodeRows {
     static constexpr int kC = kThreads == kQBlockWide ? kQWideChunks : kQCodeChunks;
     static constexpr bool kAccum = kOp == kAccumAdd || kOp == kAccumOverwrite;
@@ -503,7 +647,69 @@ struct CodeRows {
         }
     }
 
+    // Packed rows: each chunk is a row of its own (see Packed).
+    __device__ __forceinline__ void packed_rows(const Q8Rec &r, uint32_t local_block) const {
+        const uint64_t codes = kAccum ? r.p[0] : r.p[1];
+        const uint64_t scale = kAccum ? r.p[1] : r.p[2];
+        const uint64_t src = kAccum ? r.p[2] : r.p[0];
+        const Packed p = packed_of<kThreads, kC>(r, local_block);
+        PackedChunk k[kC];
+        float s_old[kC];
+        uint32_t cw[kC];
+        u32x2 gb[kC];
+        f32x4 x[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            k[c] = packed_chunk(p, r, c);
+            s_old[c] = 0.0f;
+            if (kReadsCodes && k[c].has_row) s_old[c] = as_global<gfloat>(scale)[k[c].row];
+            x[c] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const int64_t valid = k[c].valid;
+            if (valid <= 0) continue;
+            const bool vector = valid == 4;
+            if constexpr (kReadsCodes) cw[c] = load_codes(codes, k[c].e, vector, valid);
+            if constexpr (kAccum) gb[c] = load_bf16_bits(src, k[c].e, vector, valid);
+            if constexpr (kOp == kQuantize) x[c] = load_f32(src, k[c].e, vector, valid);
+        }
+        uint32_t amax[kC];
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            amax[c] = 0;
+            const int64_t valid = k[c].valid;
+            if (valid <= 0) continue;
+            if constexpr (kAccum) {
+                const f32x4 g = widen_bf16(gb[c]);
+                for (int i = 0; i < 4; ++i)
+                    x[c][i] = kOp == kAccumAdd
+                                  ? accum_elem(dequant(code_at(cw[c], i), s_old[c]), g[i], false)
+                                  : g[i];
+            }
+            if constexpr (kOp == kDequantize) {
+                f32x4 d;
+                for (int i = 0; i < 4; ++i) d[i] = dequant(code_at(cw[c], i), s_old[c]);
+                store_f32(src, k[c].e, valid == 4, valid, d);
+            } else {
+                amax[c] = absmax4(0u, x[c], valid);
+            }
+        }
+        if constexpr (kOp == kDequantize) return;
+#pragma unroll
+        for (int c = 0; c < kC; ++c) amax[c] = packed_max(amax[c], p.width);
+#pragma unroll
+        for (int c = 0; c < kC; ++c) {
+            if (!k[c].has_row) continue;
+            const QuantRow q = quant_row(amax[c]);
+            if (k[c].valid > 0)
+                store_codes(codes, k[c].e, k[c].valid == 4, k[c].valid, quant_chunk(q, x[c]));
+            if (p.lane == 0) as_global<gfloat>(scale)[k[c].row] = q.s;
+        }
+    }
+
     __device__ __forceinline__ void operator()(const Q8Rec &r, uint32_t local_block) const {
+        if constexpr (kPacked) {      // a kernel of its own: the two paths differ in registers
+            packed_rows(r, local_block);
+            return;
+        }
         const Team t = team_of<kThreads>(r, local_block);
         const bool has_row = t.len > 0;
         // pointers: accumulation {codes, scale, grad}; conversions {x, codes, scale}
@@ -533,81 +739,93 @@ struct CodeRows {
     }
 };
 
-template <RowOp kOp, int kThreads>
+template <RowOp kOp, int kThreads, bool kPacked>
 __global__ __launch_bounds__(kThreads) void code_rows_kernel(const void *table, int nseg,
                                                              uint32_t block0) {
-    block_of_table<Q8Rec>(table, nseg, block0, CodeRows<kOp, kThreads>{});
+    block_of_table<Q8Rec>(table, nseg, block0, CodeRows<kOp, kThreads, kPacked>{});
 }
 
+// `lds` bytes of dynamic LDS are reserved per workgroup (none of these
+// kernels reads them): a cap on how many workgroups share a CU.
 template <class... Args>
-hipError_t launch_split(const void *fn, int block, uint32_t total_blocks, hipStream_t stream,
-                        const void *table, int nseg, Args... extra) {
+hipError_t launch_split(const void *fn, int block, uint32_t total_blocks, uint32_t lds,
+                        hipStream_t stream, const void *table, int nseg, Args... extra) {
     for (uint32_t block0 = 0; block0 < total_blocks;) {
         const uint32_t n = std::min<uint32_t>(total_blocks - block0, kMaxBlocksPerLaunch);
         void *args[] = {&table, &nseg, &block0, &extra...};
-        hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(block), args, 0, stream);
+        hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(block), args, lds, stream);
         if (e != hipSuccess) return e;
         block0 += n;
     }
     return hipSuccess;
 }
 
+// Kernels per launch group: row teams in kQBlock- or kQBlockWide-lane
+// workgroups, or packed rows (kQBlock lanes only).
 template <bool kMomQ8, QGrad kGrad, bool kDelta>
-const void *pick_adamw(int block) {
+const void *pick_adamw(int block, bool packed) {
+    if (packed)
+        return reinterpret_cast<const void *>(&adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock, true>);
     return block == kQBlock
-               ? reinterpret_cast<const void *>(&adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock>)
-               : reinterpret_cast<const void *>(&adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlockWide>);
+               ? reinterpret_cast<const void *>(&adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock, false>)
+               : reinterpret_cast<const void *>(
+                     &adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlockWide, false>);
 }
 
 template <bool kMomQ8, QGrad kGrad>
-const void *pick_adamw_delta(bool with_delta, int block) {
-    return with_delta ? pick_adamw<kMomQ8, kGrad, true>(block)
-                      : pick_adamw<kMomQ8, kGrad, false>(block);
+const void *pick_adamw_delta(bool with_delta, int block, bool packed) {
+    return with_delta ? pick_adamw<kMomQ8, kGrad, true>(block, packed)
+                      : pick_adamw<kMomQ8, kGrad, false>(block, packed);
 }
 
 template <RowOp kOp>
-const void *pick_rows(int block) {
-    return block == kQBlock ? reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock>)
-                            : reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlockWide>);
+const void *pick_rows(int block, bool packed) {
+    if (packed) return reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, true>);
+    return block == kQBlock ? reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, false>)
+                            : reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlockWide, false>);
 }
 
-bool block_ok(int block) { return block == kQBlock || block == kQBlockWide; }
+bool block_ok(int block, bool packed) {
+    return block == kQBlock || (block == kQBlockWide && !packed);
+}
 
 }  // namespace
 
 hipError_t launch_adamw_q8(const void *table, int nseg, uint32_t total_blocks, bool moments_q8,
-                           QGrad grad, bool with_delta, int block, const AdamwConsts &c,
-                           hipStream_t stream) {
-    if (!block_ok(block)) return hipErrorInvalidValue;
+                           QGrad grad, bool with_delta, int block, bool packed,
+                           const AdamwConsts &c, hipStream_t stream, uint32_t lds_bytes) {
+    if (!block_ok(block, packed)) return hipErrorInvalidValue;
     const void *fn = nullptr;
     if (moments_q8) {
         switch (grad) {
-        case kQGradBf16: fn = pick_adamw_delta<true, kQGradBf16>(with_delta, block); break;
-        case kQGradF32: fn = pick_adamw_delta<true, kQGradF32>(with_delta, block); break;
-        case kQGradQ8: fn = pick_adamw_delta<true, kQGradQ8>(with_delta, block); break;
+        case kQGradBf16: fn = pick_adamw_delta<true, kQGradBf16>(with_delta, block, packed); break;
+        case kQGradF32: fn = pick_adamw_delta<true, kQGradF32>(with_delta, block, packed); break;
+        case kQGradQ8: fn = pick_adamw_delta<true, kQGradQ8>(with_delta, block, packed); break;
         default: return hipErrorInvalidValue;
         }
     } else {
         // fp32 moments only pair with an int8 gradient here; the other
         // combinations run on the tile kernels of lema_kernels.hip
         if (grad != kQGradQ8) return hipErrorInvalidValue;
-        fn = pick_adamw_delta<false, kQGradQ8>(with_delta, block);
+        fn = pick_adamw_delta<false, kQGradQ8>(with_delta, block, packed);
     }
-    return launch_split(fn, block, total_blocks, stream, table, nseg, c);
+    return launch_split(fn, block, total_blocks, lds_bytes, stream, table, nseg, c);
 }
 
 hipError_t launch_accum_q8(const void *table, int nseg, uint32_t total_blocks, bool overwrite,
-                           int block, hipStream_t stream) {
-    if (!block_ok(block)) return hipErrorInvalidValue;
-    const void *fn = overwrite ? pick_rows<kAccumOverwrite>(block) : pick_rows<kAccumAdd>(block);
-    return launch_split(fn, block, total_blocks, stream, table, nseg);
+                           int block, bool packed, hipStream_t stream) {
+    if (!block_ok(block, packed)) return hipErrorInvalidValue;
+    const void *fn = overwrite ? pick_rows<kAccumOverwrite>(block, packed)
+                               : pick_rows<kAccumAdd>(block, packed);
+    return launch_split(fn, block, total_blocks, 0, stream, table, nseg);
 }
 
 hipError_t launch_quantize_q8(const void *table, int nseg, uint32_t total_blocks, bool dequantize,
-                              int block, hipStream_t stream) {
-    if (!block_ok(block)) return hipErrorInvalidValue;
-    const void *fn = dequantize ? pick_rows<kDequantize>(block) : pick_rows<kQuantize>(block);
-    return launch_split(fn, block, total_blocks, stream, table, nseg);
+                              int block, bool packed, hipStream_t stream) {
+    if (!block_ok(block, packed)) return hipErrorInvalidValue;
+    const void *fn = dequantize ? pick_rows<kDequantize>(block, packed)
+                                : pick_rows<kQuantize>(block, packed);
+    return launch_split(fn, block, total_blocks, 0, stream, table, nseg);
 }
 
 }  // namespace lema

@@ -42,10 +42,22 @@ Shape shape_for(int64_t row_len, int chunks_max) {
     return {lg, static_cast<int32_t>(ceil_div(need, int64_t(1) << lg)), kQBlockWide};
 }
 
-int block_of(const Q8Rec &r, int chunks_max) { return shape_for(r.row_len, chunks_max).block; }
+// Rows of 4*S elements, S a power of two up to 64 lanes, go packed: a team
+// of S lanes covers the row in one chunk step and each lane's chunks hold
+// `chunks_max` different rows (contiguous accesses across the wavefront).
+bool packed_row_len(int64_t row_len) {
+    if (row_len < 4 || row_len > 256 || row_len % 4 != 0) return false;
+    const int64_t s = row_len / 4;
+    return (s & (s - 1)) == 0;
+}
+
+int block_of(const Q8Rec &r, int chunks_max) {
+    return (r.flags & kQPacked) ? kQBlock : shape_for(r.row_len, chunks_max).block;
+}
 
 uint64_t blocks_of(const Q8Rec &r, int chunks_max) {
-    const int64_t rows_per_block = block_of(r, chunks_max) >> r.team_log2;
+    int64_t rows_per_block = block_of(r, chunks_max) >> r.team_log2;
+    if (r.flags & kQPacked) rows_per_block *= r.chunks;
     return static_cast<uint64_t>(ceil_div(r.rows, rows_per_block));
 }
 
@@ -60,30 +72,42 @@ Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok, int chunks_max) {
     r.team_log2 = sh.log2w;
     r.chunks = sh.chunks;
     r.flags = (vector_ok && row_len % 4 == 0) ? kQVector : 0;
+    if (r.flags && packed_row_len(row_len)) {
+        int lg = 0;
+        while ((int64_t(4) << lg) < row_len) ++lg;
+        r.team_log2 = lg;
+        r.chunks = chunks_max;
+        r.flags |= kQPacked;
+    }
     return r;
 }
 
 uintptr_t bits(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
-// Launch `recs` in at most two groups, one per workgroup size.  Both groups'
-// tables are built and checked before the first launch, so a size error
+// Launch `recs` in at most three groups, one per kernel shape: row teams in
+// kQBlock- or kQBlockWide-lane workgroups, and packed rows.  Every group's
+// table is built and checked before the first launch, so a size error
 // enqueues nothing.
 template <class LaunchFn>
 lema_status launch_groups(const std::vector<Q8Rec> &recs, int chunks_max, hipStream_t stream,
                           const LaunchFn &launch) {
     struct Group {
         int block;
+        bool packed;
         int n;
         uint64_t blocks;
         std::vector<unsigned char> bytes;
     };
     std::vector<Group> groups;
-    for (int block : {kQBlock, kQBlockWide}) {
+    const struct { int block; bool packed; } kinds[] = {
+        {kQBlock, false}, {kQBlock, true}, {kQBlockWide, false}};
+    for (const auto &kind : kinds) {
         std::vector<Q8Rec> sel;
         for (const Q8Rec &r : recs)
-            if (block_of(r, chunks_max) == block) sel.push_back(r);
+            if (block_of(r, chunks_max) == kind.block && ((r.flags & kQPacked) != 0) == kind.packed)
+                sel.push_back(r);
         if (sel.empty()) continue;
-        Group g{block, static_cast<int>(sel.size()), 0, {}};
+        Group g{kind.block, kind.packed, static_cast<int>(sel.size()), 0, {}};
         g.bytes.assign(q8_table_bytes(g.n), 0);
         uint32_t *begin = reinterpret_cast<uint32_t *>(g.bytes.data());
         for (int i = 0; i < g.n; ++i) {
@@ -97,7 +121,7 @@ lema_status launch_groups(const std::vector<Q8Rec> &recs, int chunks_max, hipStr
     }
     for (const Group &g : groups) {
         lema_status st = launch_on_table(g.bytes, stream, [&](const void *table) {
-            return launch(table, g.n, static_cast<uint32_t>(g.blocks), g.block);
+            return launch(table, g.n, static_cast<uint32_t>(g.blocks), g.block, g.packed);
         });
         if (st != LEMA_OK) return st;
     }
@@ -217,9 +241,16 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
     const AdamwConsts c = derive_consts(args);
     const QGrad qg = gd == LEMA_GRAD_BF16 ? kQGradBf16 : gd == LEMA_GRAD_FP32 ? kQGradF32 : kQGradQ8;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    // 256-lane workgroups of the step each stream ~90 KB of state for their
+    // row; beyond 3 of them per CU (5 fit by registers) HBM delivers less
+    // (measured on MI355X: +3% at 3 per CU).  The 1024-lane ones fit once
+    // per CU anyway.  Accumulation and conversions move less per workgroup
+    // and keep full occupancy.
+    const uint32_t lds = occupancy_lds_bytes(kQ8StepWorkgroupsPerCu);
     return launch_groups(recs, kQStepChunks, hs, [&](const void *table, int n, uint32_t blocks,
-                                                     int block) {
-        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, c, hs);
+                                                     int block, bool packed) {
+        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, packed, c, hs,
+                               block == kQBlock ? lds : 0);
     });
 }
 
@@ -250,8 +281,8 @@ lema_status lema_grad_accum_q8(const lema_accum_q8_seg *segs, int32_t nseg, int3
     if (recs.empty()) return LEMA_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     return launch_groups(recs, kQCodeChunks, hs, [&](const void *table, int n, uint32_t blocks,
-                                                     int block) {
-        return launch_accum_q8(table, n, blocks, overwrite != 0, block, hs);
+                                                     int block, bool packed) {
+        return launch_accum_q8(table, n, blocks, overwrite != 0, block, packed, hs);
     });
 }
 
@@ -282,8 +313,8 @@ static lema_status convert_rows(const lema_q8_tensor *t, int32_t n, bool dequant
     if (recs.empty()) return LEMA_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     return launch_groups(recs, kQCodeChunks, hs, [&](const void *table, int nrec,
-                                                     uint32_t blocks, int block) {
-        return launch_quantize_q8(table, nrec, blocks, dequantize, block, hs);
+                                                     uint32_t blocks, int block, bool packed) {
+        return launch_quantize_q8(table, nrec, blocks, dequantize, block, packed, hs);
     });
 }
 

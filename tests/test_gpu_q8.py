@@ -143,7 +143,8 @@ def test_quantize_dequantize_rows(L, row_len, offset):
     """Codes and scales of lema_quantize_rows and the values of
     lema_dequantize_rows against the oracle, with a ragged last row, zero,
     NaN, infinite and subnormal rows, on vector and element paths."""
-    rows = 5
+    # short rows: several workgroups' worth (packed rows for 4, 16, 256)
+    rows = 5 if row_len > 256 else 2 * (4 * 256 * 4 // max(row_len, 4)) + 5
     n = row_len * rows + max(1, row_len // 3)
     x = host_f32(n, 1e-3, 7000 + row_len)
     x[:row_len] = 0.0                                   # an all-zero row
@@ -200,6 +201,21 @@ def test_q8_step_matches_oracle(L, grad, delta, row_len):
     step(L, [c], 100)
     torch.cuda.synchronize()
     c.check(oracle_consts(HP, 100), f"q8[{grad},{delta},{row_len}]")
+
+
+@pytest.mark.parametrize("row_len", [4, 8, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("kinds", [("q8", "bf16"), ("q8", "q8"), ("fp32", "q8")])
+def test_q8_step_packed_rows(L, row_len, kinds):
+    """Rows of 4*S elements (S a power of two up to 64) run packed: each
+    lane's chunks belong to different rows, so a wavefront's accesses stay
+    contiguous.  Two and a bit workgroups of rows, a ragged last row, delta on."""
+    moments, grad = kinds
+    rows_per_block = 4 * 256 * 4 // row_len
+    n = row_len * (2 * rows_per_block + 37) + row_len // 2 + 1
+    c = Case(L, n, row_len, 9500 + row_len, grad=grad, moments=moments, delta=True)
+    step(L, [c], 100)
+    torch.cuda.synchronize()
+    c.check(oracle_consts(HP, 100), f"packed[{moments},{grad},{row_len}]")
 
 
 @pytest.mark.parametrize("offset", [1, 3])
@@ -274,12 +290,13 @@ def test_q8_step_special_values(L):
 
 # ----------------------------------------------------------- accumulation
 
-@pytest.mark.parametrize("row_len", [3, 64, 4096, 11008])
+@pytest.mark.parametrize("row_len", [3, 16, 64, 256, 4096, 11008])
 @pytest.mark.parametrize("offset", [0, 1])
 def test_q8_accumulation(L, row_len, offset):
     """Four bf16 micro-batches into an int8 accumulator: overwrite, then
     dequantize-add-requantize, bit-exact after every micro-batch."""
-    n = row_len * 4 + row_len // 2 + 1
+    rows = 4 if row_len > 256 else 2 * (4 * 256 * 4 // row_len) + 5   # packed: several workgroups
+    n = row_len * rows + row_len // 2 + 1
     acc = L.Q8(torch.full((n + offset,), 77, dtype=torch.int8, device=DEV)[offset:],
                torch.full((L.Q8.rows_of(n, row_len),), 5.0, device=DEV), row_len)
     ref_q = np.zeros(n, np.int8)
