@@ -74,7 +74,7 @@ constexpr int kQBlockWide = 1024;
 // (int8 step 5.50 TB/s at 4, 4.97 at 8, 2.47 at 16 with 256 VGPRs;
 // accumulation 4.0 TB/s at 4, 1.7 at 8, 2.5 at 16).
 constexpr int kQStepChunks = 4;
-constexpr int kQ8StepWorkgroupsPerCu = 3;     // occupancy cap of the 256-lane step
+constexpr int kQ8StepWorkgroupsPerCu = 4;     // occupancy cap of the 256-lane step
 constexpr int kQCodeChunks = 4;
 constexpr int kQWideChunks = 4;
 constexpr int64_t kQMaxRow = int64_t(kQBlockWide) * kQWideChunks * 4;   // 16384 elements
