@@ -213,8 +213,9 @@ class FlatState:
     layout of flat parameter and optimizer-state buffers in ZeRO/FSDP-style
     training.  It also places the arrays that one AdamW launch streams side by
     side a whole buffer apart in HBM; allocating them tensor by tensor instead
-    puts one tensor's arrays next to each other, which measured 10-15% slower
-    on MI355X for the same launch.
+    puts one tensor's arrays next to each other, which measured slower on
+    MI355X for the same launch (about 1.5% with the step's occupancy cap,
+    10-15% at full occupancy).
     """
 
     def __init__(self, numels: Sequence[int], kinds: dict, device="cuda", align: int = 64):
