@@ -90,7 +90,7 @@ struct Q8Rec {
     int32_t team_log2;    // lanes per row = 1 << team_log2, at most the workgroup
     int32_t chunks;       // 4-element chunks per lane
     int32_t flags;        // kQVector: full chunks take 16/8/4-byte vector accesses;
-                          // kQPacked: packed rows
+                          // kQPacked: packed rows; kQWave: wave rows
     int32_t reserved;
 };
 static_assert(sizeof(Q8Rec) == 120, "int8 segment record is 120 bytes");
@@ -99,6 +99,13 @@ constexpr int32_t kQVector = 1;
 // chunk of a lane belongs to its own row, `chunks` rows per lane, so that a
 // wavefront's chunk steps stay contiguous (lema_q8.hip, packed rows).
 constexpr int32_t kQPacked = 2;
+// Rows whose team spans whole wavefronts (team_log2 >= 6) on vector-aligned
+// arrays with a multiple-of-4 element count: every wavefront works on one
+// row, reached through row-sized buffer resources (lema_q8.hip, wave rows).
+constexpr int32_t kQWave = 4;
+
+// Kernel family of a launch group: row teams, packed rows or wave rows.
+enum QRows : int { kQRowsTeam = 0, kQRowsPacked = 1, kQRowsWave = 2 };
 
 // How the int8 step reads the moments and the gradient.
 enum QGrad : int { kQGradBf16 = 0, kQGradF32 = 1, kQGradQ8 = 2 };
@@ -125,16 +132,16 @@ hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
 hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream);
 
 // int8 kernels; `block` (kQBlock or kQBlockWide) is the workgroup size the
-// table's records were sized for, `packed` whether they are packed rows
-// (kQPacked, kQBlock only).  The step reserves `lds_bytes` of unused LDS per
-// workgroup, a cap on its workgroups per CU.
+// table's records were sized for, `rows` the kernel family of all its records
+// (packed rows: kQBlock only).  The step reserves `lds_bytes` of unused LDS
+// per workgroup, a cap on its workgroups per CU.
 hipError_t launch_adamw_q8(const void *table, int nseg, uint32_t total_blocks, bool moments_q8,
-                           QGrad grad, bool with_delta, int block, bool packed,
+                           QGrad grad, bool with_delta, int block, QRows rows,
                            const AdamwConsts &c, hipStream_t stream, uint32_t lds_bytes);
 hipError_t launch_accum_q8(const void *table, int nseg, uint32_t total_blocks, bool overwrite,
-                           int block, bool packed, hipStream_t stream);
+                           int block, QRows rows, hipStream_t stream);
 hipError_t launch_quantize_q8(const void *table, int nseg, uint32_t total_blocks, bool dequantize,
-                              int block, bool packed, hipStream_t stream);
+                              int block, QRows rows, hipStream_t stream);
 
 // Measurement aids (include/lema_measure.h).
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);

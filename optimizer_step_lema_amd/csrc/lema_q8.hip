@@ -9,30 +9,38 @@
 // Row teams.  The new codes of a row depend on the absmax of the whole new
 // row, so each row belongs to one team of S lanes (S a power of two up to the
 // workgroup size: 256 lanes, or 1024 for the longest rows) that keeps the
-// row's new values in registers until the team has reduced the absmax.  Chunk c of team lane l holds row elements
-// 4*(c*S + l) .. 4*(c*S + l) + 3, so one chunk step of a team covers a
-// contiguous run of 4*S elements: 16-byte fp32, 8-byte bf16 and 4-byte int8
-// accesses, contiguous across the team.  Teams of at most 64 lanes lie inside
-// one wavefront and reduce with cross-lane shuffles; wider teams add one LDS
-// exchange behind a workgroup barrier (every lane reaches it: the team width
-// is uniform across the workgroup, whose rows all come from one segment).
+// row's new values in registers until the team has reduced the absmax.
+// Chunk c of team lane l holds row elements 4*(c*S + l) .. 4*(c*S + l) + 3,
+// so one chunk step of a team covers a contiguous run of 4*S elements:
+// 16-byte fp32, 8-byte bf16 and 4-byte int8 accesses, contiguous across the
+// team.  Teams of at most 64 lanes lie inside one wavefront and reduce with
+// DPP and row-swap instructions; wider teams add one LDS exchange behind a
+// workgroup barrier (every lane reaches it: the team width is uniform across
+// the workgroup, whose rows all come from one segment).
+//
+// Three kernel families share this mapping: wave rows (teams of whole
+// wavefronts on aligned arrays, the common case: rows of about 500 to 16,384
+// elements, every access through row-sized buffer resources), packed rows
+// (rows of 4..256 elements, several rows per lane) and general row teams
+// (everything else: misaligned arrays, short or odd rows, element-guarded
+// accesses).
 //
 // Each lane issues all its loads before any arithmetic, since stores through
 // the table's pointers could alias later loads as far as the compiler knows.
 // The fp32 outputs of the step (master, bf16 weight, delta) are stored as
-// soon as they are computed; the codes and scales follow the reduction.  A
-// lane whose chunks are all full vector chunks (every lane of a row whose
-// length is a multiple of 4*S, on aligned arrays) takes a path without
-// per-chunk tests; other lanes take the element-guarded one.  The two paths
-// meet before the team reduction, so its barrier is never inside a
-// divergent branch.
+// soon as they are computed; the codes and scales follow the reduction.  In
+// the general row teams, a lane whose chunks are all full vector chunks
+// takes a path without per-chunk tests and other lanes the element-guarded
+// one; the two paths meet before the team reduction, so its barrier is never
+// inside a divergent branch.
 //
 // Arithmetic: the fp32 step of lema_kernels.hip element for element;
 // dequantization is one binary32 multiplication f32(code) * scale;
 // quantization gives the code of the IEEE quotient x / scale rounded half to
-// even and clamped to [-127, 127], mostly without dividing (see QuantRow).  Absmax is taken on the
-// magnitude bits as unsigned integers, so a NaN anywhere in a row dominates
-// (giving a NaN scale) and the result does not depend on reduction order.
+// even and clamped to [-127, 127], mostly without dividing (see QuantRow).
+// Absmax is taken on the magnitude bits as unsigned integers, so a NaN
+// anywhere in a row dominates (giving a NaN scale) and the result does not
+// depend on reduction order.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -71,12 +79,13 @@ __device__ __forceinline__ float scale_of(uint32_t absmax_bits) {
 }
 
 // The per-row part of quantization.  Codes are formed only from a finite
-// positive scale s (other rows get zeros).  When s is a normal number its
-// reciprocal r = 1/s (IEEE division, correctly rounded) is normal too, and
-// y = x*r serves in place of x/s:
+// positive scale s (other rows get zeros).  When s is a normal number
+// (s <= FLT_MAX/127, so 1/s is normal too), a reciprocal r with
+// |r*s - 1| <= 2^-23 lets y = x*r serve in place of x/s:
 //   |x| <= absmax and s >= absmax/127 (1 - 2^-24) bound |x/s| by 127.00002;
-//   |y - x/s| <= |x/s| 2^-24 (r's rounding) + 2^-18 (half an ulp below 128)
-//   < 1.2e-5, and the IEEE quotient q = RN(x/s) is within 2^-18 of x/s.
+//   |y - x/s| <= |x/s| 2^-23 (r) + |x*r| 2^-24 (the product's rounding)
+//   < 2.3e-5, and the IEEE quotient q = RN(x/s) is within 2^-18 of x/s;
+//   so |y - q| < 2.7e-5 < 2^-15.
 // So when y lies more than 2^-15 from the nearest half-integer, y and q lie
 // strictly between the same two half-integers and round to the same integer,
 // which is within [-127, 127].  The lane rounds y by adding 1.5 * 2^23: the
@@ -84,9 +93,14 @@ __device__ __forceinline__ float scale_of(uint32_t absmax_bits) {
 // integer's two's-complement byte.  A lane holding any value nearer to a
 // half-integer (about 6e-5 of all values), and every lane of a row with a
 // subnormal scale, takes the codes from the IEEE division instead.
+//
+// r is one Newton step from the hardware reciprocal r0 = 1/s (1 + d):
+// e = fma(-s, r0, 1) = -d exactly rounded, r = fma(e, r0, r0) =
+// RN(1/s (1 - d^2 - d e')), so |r*s - 1| <= 2^-24 + d^2 + 2^-24 |d|, inside
+// 2^-23 for any |d| <= 2^-21, far more than v_rcp_f32's documented 1 ulp.
 struct QuantRow {
     float s;      // the row's new scale
-    float r;      // 1/s when `fast`
+    float r;      // about 1/s (see above) when `fast`
     bool ok;      // codes are formed (else all zero)
     bool fast;    // s is normal: x*r decides away from half-integers
 };
@@ -97,27 +111,35 @@ __device__ __forceinline__ QuantRow quant_row(uint32_t absmax_bits) {
     q.s = scale_of(absmax_bits);
     q.ok = q.s > 0.0f && mag_bits(q.s) < 0x7F800000u;
     q.fast = q.ok && mag_bits(q.s) >= 0x00800000u;
-    q.r = q.fast ? 1.0f / q.s : 0.0f;
+    const float r0 = __builtin_amdgcn_rcpf(q.s);
+    const float e = __builtin_fmaf(-q.s, r0, 1.0f);
+    q.r = q.fast ? __builtin_fmaf(e, r0, r0) : 0.0f;
     return q;
 }
 
 constexpr float kRoundMagic = 12582912.0f;    // 1.5 * 2^23
-constexpr float kNearHalf = 0x1p-15f;
+// y is decided by x*r when |y - round(y)| <= 1/2 - 2^-15 (see QuantRow)
+constexpr float kFarFromHalf = 0.5f - 0x1p-15f;
 
-// Packed codes of four values from y = x*r; `near` keeps the smallest
-// distance of any y from a half-integer.
-__device__ __forceinline__ uint32_t quant4_fast(f32x4 x, float r, float &near) {
+// Packed codes of four values from y = x*r; `dmax` keeps the largest
+// distance |y - round(y)| seen.  The codes are the low bytes of the rounded
+// sums, gathered by byte permutes.
+__device__ __forceinline__ uint32_t quant4_fast(f32x4 x, float r, float &dmax) {
 #pragma clang fp contract(off)
-    uint32_t w = 0;
+    uint32_t g[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const float y = x[k] * r;
-        const float g = y + kRoundMagic;        // integer nearest y, ties to even
-        const float yk = g - kRoundMagic;       // that integer, exactly
-        near = __builtin_fminf(near, __builtin_fabsf(__builtin_fabsf(y - yk) - 0.5f));
-        w |= (__float_as_uint(g) & 0xFFu) << (8 * k);
+        const float sum = y + kRoundMagic;      // integer nearest y, ties to even
+        const float yk = sum - kRoundMagic;     // that integer, exactly
+        dmax = __builtin_fmaxf(dmax, __builtin_fabsf(y - yk));
+        g[k] = __float_as_uint(sum);
     }
-    return w;
+    // v_perm_b32: selector bytes 0-3 pick bytes of the second operand, 4-7
+    // of the first, 12 gives zero
+    const uint32_t lo = __builtin_amdgcn_perm(g[1], g[0], 0x0C0C0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(g[3], g[2], 0x0C0C0400u);
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
 }
 
 // Packed codes of four values from the IEEE quotient x / s.
@@ -183,18 +205,43 @@ __device__ __forceinline__ int64_t valid_of(const Team &t, int c) {
     return rem <= 0 ? 0 : (rem < 4 ? rem : 4);
 }
 
+// Max over aligned groups of `width` lanes (a power of two; 64 and more
+// mean the whole wavefront): every lane ends with its group's max.  Each
+// level combines two neighbouring groups of the level before: quad
+// permutations [1,0,3,2] and [2,3,0,1] for pairs and quads, the half-row and
+// row mirrors (lane i reads lane 7-i, or 15-i, within 8 or 16) for 8 and 16,
+// and the gfx950 row swaps (v_permlane16_swap, v_permlane32_swap: the two
+// results hold a lane's own value and its partner's 16 or 32 lanes away)
+// for 32 and 64.  `width` is the same on every lane, and every lane of the
+// wavefront must be active.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t a) {
+    return std::max(a, uint32_t(__builtin_amdgcn_update_dpp(0, int(a), kCtrl, 0xF, 0xF, false)));
+}
+
+__device__ __forceinline__ uint32_t group_max(uint32_t a, int width) {
+    if (width > 1) a = dpp_max<0xB1>(a);      // quad_perm [1,0,3,2]
+    if (width > 2) a = dpp_max<0x4E>(a);      // quad_perm [2,3,0,1]
+    if (width > 4) a = dpp_max<0x141>(a);     // row_half_mirror
+    if (width > 8) a = dpp_max<0x140>(a);     // row_mirror
+    if (width > 16) {
+        const auto p = __builtin_amdgcn_permlane16_swap(a, a, false, false);
+        a = std::max(uint32_t(p[0]), uint32_t(p[1]));
+    }
+    if (width > 32) {
+        const auto p = __builtin_amdgcn_permlane32_swap(a, a, false, false);
+        a = std::max(uint32_t(p[0]), uint32_t(p[1]));
+    }
+    return a;
+}
+
 // Max over the team of two unsigned values.  Every lane of the workgroup
 // must call it (it may contain a barrier).
 template <int kThreads>
 __device__ __forceinline__ void team_max2(const Team &t, uint32_t &a, uint32_t &b) {
     __shared__ uint32_t part[2][kThreads / 64];
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        if (o < t.width) {
-            a = std::max(a, uint32_t(__shfl_xor(int(a), o)));
-            b = std::max(b, uint32_t(__shfl_xor(int(b), o)));
-        }
-    }
+    a = group_max(a, t.width);
+    b = group_max(b, t.width);
     if (t.width > 64) {
         const int wave = int(threadIdx.x) >> 6;
         if ((threadIdx.x & 63) == 0) {
@@ -286,13 +333,13 @@ __device__ __forceinline__ void quantize_store(const Team &t, uint64_t codes, co
 #pragma unroll
     for (int ci = 0; ci < kC; ++ci) w[ci] = 0;
     if (q.ok) {
-        float near = 1.0f;
+        float dmax = 0.0f;
         if (q.fast) {
 #pragma unroll
             for (int ci = 0; ci < kC; ++ci)
-                if (valid_of<kFull>(t, ci) > 0) w[ci] = quant4_fast(x[ci], q.r, near);
+                if (valid_of<kFull>(t, ci) > 0) w[ci] = quant4_fast(x[ci], q.r, dmax);
         }
-        if (!q.fast || near < kNearHalf) {
+        if (!q.fast || dmax > kFarFromHalf) {
 #pragma unroll
             for (int ci = 0; ci < kC; ++ci)
                 if (valid_of<kFull>(t, ci) > 0) w[ci] = quant4_exact(x[ci], q.s);
@@ -354,23 +401,135 @@ __device__ __forceinline__ PackedChunk packed_chunk(const Packed &p, const Q8Rec
     return k;
 }
 
-// Max over the lanes of a packed team; every lane of the wavefront calls it.
-__device__ __forceinline__ uint32_t packed_max(uint32_t a, int width) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1)
-        if (o < width) a = std::max(a, uint32_t(__shfl_xor(int(a), o)));
-    return a;
-}
 
 // Codes of one chunk against its row's quantization.
 __device__ __forceinline__ uint32_t quant_chunk(const QuantRow &q, f32x4 x) {
     uint32_t w = 0;
     if (q.ok) {
-        float near = 1.0f;
-        if (q.fast) w = quant4_fast(x, q.r, near);
-        if (!q.fast || near < kNearHalf) w = quant4_exact(x, q.s);
+        float dmax = 0.0f;
+        if (q.fast) w = quant4_fast(x, q.r, dmax);
+        if (!q.fast || dmax > kFarFromHalf) w = quant4_exact(x, q.s);
     }
     return w;
+}
+
+// --------------------------------------------------------- wave rows
+//
+// Rows whose team spans whole wavefronts (S >= 64 lanes), on vector-aligned
+// arrays whose element count is a multiple of 4 (kQWave), run in kernels of
+// their own.  Every lane of a wavefront works on the same row, so the row,
+// its first element and its length are wave-uniform and sit in scalar
+// registers; each array is reached through a buffer resource based at the
+// row's first element and sized to the row, and chunk c of team lane l is
+// vector c*S + l of that resource.  No per-chunk 64-bit address arithmetic
+// is left.  A chunk lies wholly inside the row or wholly past its end (the
+// length is a multiple of 4): the resource's range check reads the latter
+// as zeros and drops its stores, and the lane leaves it out of the absmax.
+// A team without a row (past the segment's last row) has a zero-sized
+// resource and only takes part in the team reduction.
+struct WaveRow {
+    int64_t row;     // row index within the segment (wave-uniform)
+    int64_t first;   // element index of the row's first element
+    int32_t len;     // elements of the row; 0 when the team has no row
+    int32_t nvec;    // len / 4
+    int32_t lane;    // lane within the team
+    int32_t width;   // S
+    int32_t chunks;  // chunks per lane of the segment's rows
+};
+
+template <int kThreads>
+__device__ __forceinline__ WaveRow wave_row_of(const Q8Rec &r, uint32_t local_block) {
+    WaveRow w;
+    const int log2w = r.team_log2;    // at least 6
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    w.width = 1 << log2w;
+    w.lane = int(threadIdx.x) & (w.width - 1);
+    w.row = int64_t(local_block) * (kThreads >> log2w) + (wave >> (log2w - 6));
+    w.first = w.row * r.row_len;
+    w.len = w.row < r.rows ? int32_t(std::min<int64_t>(r.row_len, r.numel - w.first)) : 0;
+    w.nvec = w.len >> 2;
+    w.chunks = r.chunks;
+    return w;
+}
+
+// The buffer resource of one array (kBytes per element) over the row.
+template <int kBytes>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(uint64_t array, const WaveRow &w) {
+    return __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void *>(array + uint64_t(w.first) * kBytes), 0, w.len * kBytes,
+        kRawBufferWord3);
+}
+
+// Vector v (elements 4v .. 4v+3) of a row's array; nontemporal (gfx950 NT
+// bit), like the global accesses of the other int8 paths.
+constexpr int kRowPolicy = 2;
+
+__device__ __forceinline__ uint32_t row_ld_codes(__amdgpu_buffer_rsrc_t r, uint32_t v) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, int(v * 4), 0, kRowPolicy);
+}
+__device__ __forceinline__ u32x2 row_ld_bf16(__amdgpu_buffer_rsrc_t r, uint32_t v) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, int(v * 8), 0, kRowPolicy));
+}
+__device__ __forceinline__ f32x4 row_ld_f32(__amdgpu_buffer_rsrc_t r, uint32_t v) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(v * 16), 0, kRowPolicy));
+}
+__device__ __forceinline__ void row_st_codes(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t w) {
+    __builtin_amdgcn_raw_buffer_store_b32(w, r, int(v * 4), 0, kRowPolicy);
+}
+__device__ __forceinline__ void row_st_bf16(__amdgpu_buffer_rsrc_t r, uint32_t v, f32x4 x) {
+    const u32x2_t b = {to_bf16_pair(x.x, x.y), to_bf16_pair(x.z, x.w)};
+    __builtin_amdgcn_raw_buffer_store_b64(b, r, int(v * 8), 0, kRowPolicy);
+}
+__device__ __forceinline__ void row_st_f32(__amdgpu_buffer_rsrc_t r, uint32_t v, f32x4 x) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), r, int(v * 16), 0,
+                                           kRowPolicy);
+}
+
+// Max over a wave-rows team of kN values: the wavefront's reduction, then,
+// for teams of several wavefronts, one LDS exchange behind a workgroup
+// barrier that every lane reaches (the team width is the same across the
+// workgroup).
+template <int kThreads, int kN>
+__device__ __forceinline__ void wave_team_max(uint32_t (&a)[kN], int width) {
+#pragma unroll
+    for (int i = 0; i < kN; ++i) a[i] = group_max(a[i], 64);
+    if constexpr (kThreads > 64) {
+        __shared__ uint32_t part[kN][kThreads / 64];
+        if (width > 64) {
+            const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+            if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+                for (int i = 0; i < kN; ++i) part[i][wave] = a[i];
+            }
+            __syncthreads();
+            const int per_team = width >> 6;
+            const int w0 = wave & ~(per_team - 1);
+            for (int k = 0; k < per_team; ++k) {
+#pragma unroll
+                for (int i = 0; i < kN; ++i) a[i] = std::max(a[i], part[i][w0 + k]);
+            }
+        }
+    }
+}
+
+// Codes of a lane's first `chunks` chunks against its row's quantization.
+template <int kC>
+__device__ __forceinline__ void quant_lane(const QuantRow &q, const f32x4 (&x)[kC], int chunks,
+                                           uint32_t (&w)[kC]) {
+#pragma unroll
+    for (int c = 0; c < kC; ++c) w[c] = 0;
+    if (!q.ok) return;
+    float dmax = 0.0f;
+    if (q.fast) {
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+            if (c < chunks) w[c] = quant4_fast(x[c], q.r, dmax);
+    }
+    if (!q.fast || dmax > kFarFromHalf) {
+#pragma unroll
+        for (int c = 0; c < kC; ++c)
+            if (c < chunks) w[c] = quant4_exact(x[c], q.s);
+    }
 }
 
 // ------------------------------------------------------------- AdamW
@@ -378,7 +537,7 @@ __device__ __forceinline__ uint32_t quant_chunk(const QuantRow &q, f32x4 x) {
 // One AdamW step with int8 moments (kMomQ8) and/or an int8 gradient
 // accumulator (kGrad == kQGradQ8).  Record pointers:
 //   {master, m, m_scale, v, v_scale, grad, grad_scale, weight, orig, delta}
-template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads, bool kPacked>
+template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads, int kRows>
 struct AdamwRows {
     static constexpr int kC = kThreads == kQBlockWide ? kQWideChunks : kQStepChunks;
     AdamwConsts c;
@@ -412,13 +571,13 @@ struct AdamwRows {
         if (R.has_delta) in.o2 = load_bf16_bits(R.orig, e, vector, valid);
     }
 
-    // The fp32 step of one chunk with its row's old scales: stores master,
-    // weight and delta (and fp32 moments); int8 moments come back in mm, vv.
-    __device__ __forceinline__ void step_chunk(const Row &R, int64_t e, bool vector,
-                                               int64_t valid, const ChunkIn &in, float ms,
-                                               float vs, float gs, f32x4 &mm,
-                                               f32x4 &vv) const {
-        f32x4 w = in.w, g;
+    // The fp32 step of one chunk with its row's old scales: the new master
+    // weight w, moments mm, vv and (with delta) the delta d.
+    __device__ __forceinline__ void step_math(const ChunkIn &in, bool has_delta, float ms,
+                                              float vs, float gs, f32x4 &w, f32x4 &mm,
+                                              f32x4 &vv, f32x4 &d) const {
+        f32x4 g;
+        w = in.w;
         if constexpr (kMomQ8) {
             for (int k = 0; k < 4; ++k) {
                 mm[k] = dequant(code_at(in.mc, k), ms);
@@ -443,14 +602,24 @@ struct AdamwRows {
             mm[k] = mk;
             vv[k] = vk;
         }
-        store_f32(R.master, e, vector, valid, w);
-        store_bf16(R.weight, e, vector, valid, w);
-        if (R.has_delta) {
+        if (has_delta) {
 #pragma clang fp contract(off)
             const f32x4 o = widen_bf16(in.o2);
-            const f32x4 d = {w.x - o.x, w.y - o.y, w.z - o.z, w.w - o.w};
-            store_f32(R.delta, e, vector, valid, d);
+            d = f32x4{w.x - o.x, w.y - o.y, w.z - o.z, w.w - o.w};
         }
+    }
+
+    // step_math, then the stores of master, weight, delta (and of fp32
+    // moments); int8 moments come back in mm, vv.
+    __device__ __forceinline__ void step_chunk(const Row &R, int64_t e, bool vector,
+                                               int64_t valid, const ChunkIn &in, float ms,
+                                               float vs, float gs, f32x4 &mm,
+                                               f32x4 &vv) const {
+        f32x4 w, d;
+        step_math(in, R.has_delta, ms, vs, gs, w, mm, vv, d);
+        store_f32(R.master, e, vector, valid, w);
+        store_bf16(R.weight, e, vector, valid, w);
+        if (R.has_delta) store_f32(R.delta, e, vector, valid, d);
         if constexpr (!kMomQ8) {
             store_f32(R.m, e, vector, valid, mm);
             store_f32(R.v, e, vector, valid, vv);
@@ -524,8 +693,8 @@ struct AdamwRows {
         if constexpr (!kMomQ8) return;
 #pragma unroll
         for (int c = 0; c < kC; ++c) {
-            am[c] = packed_max(am[c], p.width);
-            av[c] = packed_max(av[c], p.width);
+            am[c] = group_max(am[c], p.width);
+            av[c] = group_max(av[c], p.width);
         }
 #pragma unroll
         for (int c = 0; c < kC; ++c) {
@@ -542,9 +711,96 @@ struct AdamwRows {
         }
     }
 
+    // Wave rows (see WaveRow).
+    __device__ __forceinline__ void wave_rows(const Q8Rec &r, uint32_t local_block) const {
+        constexpr int kMomBytes = kMomQ8 ? 1 : 4;
+        constexpr int kGradBytes = kGrad == kQGradBf16 ? 2 : kGrad == kQGradF32 ? 4 : 1;
+        const WaveRow wr = wave_row_of<kThreads>(r, local_block);
+        const bool has_delta = kDelta && r.p[9] != 0;
+        const auto r_master = row_rsrc<4>(r.p[0], wr);
+        const auto r_m = row_rsrc<kMomBytes>(r.p[1], wr);
+        const auto r_v = row_rsrc<kMomBytes>(r.p[3], wr);
+        const auto r_g = row_rsrc<kGradBytes>(r.p[5], wr);
+        const auto r_w = row_rsrc<2>(r.p[7], wr);
+        const auto r_o = row_rsrc<2>(r.p[8], wr);
+        const auto r_d = row_rsrc<4>(r.p[9], wr);
+        float ms = 0.0f, vs = 0.0f, gs = 0.0f;
+        if (wr.len > 0) {
+            if constexpr (kMomQ8) {
+                ms = as_global<gfloat>(r.p[2])[wr.row];
+                vs = as_global<gfloat>(r.p[4])[wr.row];
+            }
+            if constexpr (kGrad == kQGradQ8) gs = as_global<gfloat>(r.p[6])[wr.row];
+        }
+
+        ChunkIn in[kC];
+#pragma unroll
+        for (int ci = 0; ci < kC; ++ci) {
+            if (ci >= wr.chunks) continue;
+            const uint32_t v = uint32_t(ci * wr.width + wr.lane);
+            in[ci].w = row_ld_f32(r_master, v);
+            if constexpr (kMomQ8) {
+                in[ci].mc = row_ld_codes(r_m, v);
+                in[ci].vc = row_ld_codes(r_v, v);
+            } else {
+                in[ci].mf = row_ld_f32(r_m, v);
+                in[ci].vf = row_ld_f32(r_v, v);
+            }
+            if constexpr (kGrad == kQGradBf16) in[ci].gb = row_ld_bf16(r_g, v);
+            if constexpr (kGrad == kQGradF32) in[ci].g4 = row_ld_f32(r_g, v);
+            if constexpr (kGrad == kQGradQ8) in[ci].gc = row_ld_codes(r_g, v);
+            if (has_delta) in[ci].o2 = row_ld_bf16(r_o, v);
+        }
+
+        f32x4 mf[kC], vf[kC];
+        uint32_t amax[2] = {0, 0};
+#pragma unroll
+        for (int ci = 0; ci < kC; ++ci) {
+            if (ci >= wr.chunks) continue;
+            const uint32_t v = uint32_t(ci * wr.width + wr.lane);
+            f32x4 w, d;
+            step_math(in[ci], has_delta, ms, vs, gs, w, mf[ci], vf[ci], d);
+            row_st_f32(r_master, v, w);
+            row_st_bf16(r_w, v, w);
+            if (has_delta) row_st_f32(r_d, v, d);
+            if constexpr (!kMomQ8) {
+                row_st_f32(r_m, v, mf[ci]);
+                row_st_f32(r_v, v, vf[ci]);
+            }
+            if (kMomQ8 && int32_t(v) < wr.nvec) {
+                amax[0] = absmax4(amax[0], mf[ci], 4);
+                amax[1] = absmax4(amax[1], vf[ci], 4);
+            }
+        }
+        if constexpr (!kMomQ8) return;
+
+        // requantize the moments against the new row scales
+        wave_team_max<kThreads, 2>(amax, wr.width);
+        if (wr.len == 0) return;
+        const QuantRow qm = quant_row(amax[0]), qv = quant_row(amax[1]);
+        uint32_t cm[kC], cv[kC];
+        quant_lane<kC>(qm, mf, wr.chunks, cm);
+        quant_lane<kC>(qv, vf, wr.chunks, cv);
+#pragma unroll
+        for (int ci = 0; ci < kC; ++ci) {
+            if (ci >= wr.chunks) continue;
+            const uint32_t v = uint32_t(ci * wr.width + wr.lane);
+            row_st_codes(r_m, v, cm[ci]);
+            row_st_codes(r_v, v, cv[ci]);
+        }
+        if (wr.lane == 0) {
+            as_global<gfloat>(r.p[2])[wr.row] = qm.s;
+            as_global<gfloat>(r.p[4])[wr.row] = qv.s;
+        }
+    }
+
     __device__ __forceinline__ void operator()(const Q8Rec &r, uint32_t local_block) const {
-        if constexpr (kPacked) {      // a kernel of its own: the two paths differ in registers
-            packed_rows(r, local_block);
+        if constexpr (kRows == kQRowsPacked) {   // kernels of their own: the paths differ
+            packed_rows(r, local_block);         // in registers
+            return;
+        }
+        if constexpr (kRows == kQRowsWave) {
+            wave_rows(r, local_block);
             return;
         }
         Row R{r.p[0], r.p[1], r.p[2], r.p[3], r.p[4], r.p[5], r.p[6], r.p[7], r.p[8], r.p[9],
@@ -585,11 +841,11 @@ struct AdamwRows {
     }
 };
 
-template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads, bool kPacked>
+template <bool kMomQ8, QGrad kGrad, bool kDelta, int kThreads, int kRows>
 __global__ __launch_bounds__(kThreads) void adamw_q8_kernel(const void *table, int nseg,
                                                             uint32_t block0, AdamwConsts c) {
     block_of_table<Q8Rec>(table, nseg, block0,
-                          AdamwRows<kMomQ8, kGrad, kDelta, kThreads, kPacked>{c});
+                          AdamwRows<kMomQ8, kGrad, kDelta, kThreads, kRows>{c});
 }
 
 // ------------------------------------------------------ accumulation
@@ -601,7 +857,7 @@ __global__ __launch_bounds__(kThreads) void adamw_q8_kernel(const void *table, i
 // quantize {x, codes, scale} and dequantize (codes, scale -> x).
 enum RowOp : int { kAccumAdd = 0, kAccumOverwrite = 1, kQuantize = 2, kDequantize = 3 };
 
-template <RowOp kOp, int kThreads, bool kPacked>
+template <RowOp kOp, int kThreads, int kRows>
 struct CodeRows {
     static constexpr int kC = kThreads == kQBlockWide ? kQWideChunks : kQCodeChunks;
     static constexpr bool kAccum = kOp == kAccumAdd || kOp == kAccumOverwrite;
@@ -694,7 +950,7 @@ struct CodeRows {
         }
         if constexpr (kOp == kDequantize) return;
 #pragma unroll
-        for (int c = 0; c < kC; ++c) amax[c] = packed_max(amax[c], p.width);
+        for (int c = 0; c < kC; ++c) amax[c] = group_max(amax[c], p.width);
 #pragma unroll
         for (int c = 0; c < kC; ++c) {
             if (!k[c].has_row) continue;
@@ -705,9 +961,71 @@ struct CodeRows {
         }
     }
 
+    // Wave rows (see WaveRow).
+    __device__ __forceinline__ void wave_rows(const Q8Rec &r, uint32_t local_block) const {
+        const uint64_t codes = kAccum ? r.p[0] : r.p[1];
+        const uint64_t scale = kAccum ? r.p[1] : r.p[2];
+        const uint64_t src = kAccum ? r.p[2] : r.p[0];
+        const WaveRow wr = wave_row_of<kThreads>(r, local_block);
+        const auto rc = row_rsrc<1>(codes, wr);
+        const auto rs = row_rsrc<kAccum ? 2 : 4>(src, wr);
+        float s_old = 0.0f;
+        if (kReadsCodes && wr.len > 0) s_old = as_global<gfloat>(scale)[wr.row];
+
+        uint32_t cw[kC];
+        u32x2 gb[kC];
+        f32x4 x[kC];
+#pragma unroll
+        for (int ci = 0; ci < kC; ++ci) {
+            x[ci] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (ci >= wr.chunks) continue;
+            const uint32_t v = uint32_t(ci * wr.width + wr.lane);
+            if constexpr (kReadsCodes) cw[ci] = row_ld_codes(rc, v);
+            if constexpr (kAccum) gb[ci] = row_ld_bf16(rs, v);
+            if constexpr (kOp == kQuantize) x[ci] = row_ld_f32(rs, v);
+        }
+        uint32_t amax[1] = {0};
+#pragma unroll
+        for (int ci = 0; ci < kC; ++ci) {
+            if (ci >= wr.chunks) continue;
+            const uint32_t v = uint32_t(ci * wr.width + wr.lane);
+            if constexpr (kAccum) {
+                const f32x4 g = widen_bf16(gb[ci]);
+                for (int k = 0; k < 4; ++k)
+                    x[ci][k] = kOp == kAccumAdd
+                                   ? accum_elem(dequant(code_at(cw[ci], k), s_old), g[k], false)
+                                   : g[k];
+            }
+            if constexpr (kOp == kDequantize) {
+                f32x4 d;
+                for (int k = 0; k < 4; ++k) d[k] = dequant(code_at(cw[ci], k), s_old);
+                row_st_f32(rs, v, d);
+            } else if (int32_t(v) < wr.nvec) {
+                amax[0] = absmax4(amax[0], x[ci], 4);
+            }
+        }
+        if constexpr (kOp == kDequantize) return;
+
+        wave_team_max<kThreads, 1>(amax, wr.width);
+        if (wr.len == 0) return;
+        const QuantRow q = quant_row(amax[0]);
+        uint32_t w[kC];
+        quant_lane<kC>(q, x, wr.chunks, w);
+#pragma unroll
+        for (int ci = 0; ci < kC; ++ci) {
+            if (ci >= wr.chunks) continue;
+            row_st_codes(rc, uint32_t(ci * wr.width + wr.lane), w[ci]);
+        }
+        if (wr.lane == 0) as_global<gfloat>(scale)[wr.row] = q.s;
+    }
+
     __device__ __forceinline__ void operator()(const Q8Rec &r, uint32_t local_block) const {
-        if constexpr (kPacked) {      // a kernel of its own: the two paths differ in registers
-            packed_rows(r, local_block);
+        if constexpr (kRows == kQRowsPacked) {   // kernels of their own: the paths differ
+            packed_rows(r, local_block);         // in registers
+            return;
+        }
+        if constexpr (kRows == kQRowsWave) {
+            wave_rows(r, local_block);
             return;
         }
         const Team t = team_of<kThreads>(r, local_block);
@@ -739,10 +1057,10 @@ struct CodeRows {
     }
 };
 
-template <RowOp kOp, int kThreads, bool kPacked>
+template <RowOp kOp, int kThreads, int kRows>
 __global__ __launch_bounds__(kThreads) void code_rows_kernel(const void *table, int nseg,
                                                              uint32_t block0) {
-    block_of_table<Q8Rec>(table, nseg, block0, CodeRows<kOp, kThreads, kPacked>{});
+    block_of_table<Q8Rec>(table, nseg, block0, CodeRows<kOp, kThreads, kRows>{});
 }
 
 // `lds` bytes of dynamic LDS are reserved per workgroup (none of these
@@ -760,71 +1078,90 @@ hipError_t launch_split(const void *fn, int block, uint32_t total_blocks, uint32
     return hipSuccess;
 }
 
-// Kernels per launch group: row teams in kQBlock- or kQBlockWide-lane
-// workgroups, or packed rows (kQBlock lanes only).
-template <bool kMomQ8, QGrad kGrad, bool kDelta>
-const void *pick_adamw(int block, bool packed) {
-    if (packed)
-        return reinterpret_cast<const void *>(&adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock, true>);
+// Kernels per launch group: row teams, wave rows (kQBlock- or kQBlockWide-
+// lane workgroups) or packed rows (kQBlock lanes only).
+template <bool kMomQ8, QGrad kGrad, bool kDelta, int kRows>
+const void *pick_adamw_rows(int block) {
     return block == kQBlock
-               ? reinterpret_cast<const void *>(&adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock, false>)
+               ? reinterpret_cast<const void *>(&adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock, kRows>)
                : reinterpret_cast<const void *>(
-                     &adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlockWide, false>);
+                     &adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlockWide, kRows>);
+}
+
+template <bool kMomQ8, QGrad kGrad, bool kDelta>
+const void *pick_adamw(int block, QRows rows) {
+    switch (rows) {
+    case kQRowsPacked:
+        return reinterpret_cast<const void *>(
+            &adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock, kQRowsPacked>);
+    case kQRowsWave: return pick_adamw_rows<kMomQ8, kGrad, kDelta, kQRowsWave>(block);
+    default: return pick_adamw_rows<kMomQ8, kGrad, kDelta, kQRowsTeam>(block);
+    }
 }
 
 template <bool kMomQ8, QGrad kGrad>
-const void *pick_adamw_delta(bool with_delta, int block, bool packed) {
-    return with_delta ? pick_adamw<kMomQ8, kGrad, true>(block, packed)
-                      : pick_adamw<kMomQ8, kGrad, false>(block, packed);
+const void *pick_adamw_delta(bool with_delta, int block, QRows rows) {
+    return with_delta ? pick_adamw<kMomQ8, kGrad, true>(block, rows)
+                      : pick_adamw<kMomQ8, kGrad, false>(block, rows);
+}
+
+template <RowOp kOp, int kRows>
+const void *pick_code_rows(int block) {
+    return block == kQBlock ? reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, kRows>)
+                            : reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlockWide, kRows>);
 }
 
 template <RowOp kOp>
-const void *pick_rows(int block, bool packed) {
-    if (packed) return reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, true>);
-    return block == kQBlock ? reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, false>)
-                            : reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlockWide, false>);
+const void *pick_rows(int block, QRows rows) {
+    switch (rows) {
+    case kQRowsPacked:
+        return reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, kQRowsPacked>);
+    case kQRowsWave: return pick_code_rows<kOp, kQRowsWave>(block);
+    default: return pick_code_rows<kOp, kQRowsTeam>(block);
+    }
 }
 
-bool block_ok(int block, bool packed) {
-    return block == kQBlock || (block == kQBlockWide && !packed);
+bool block_ok(int block, QRows rows) {
+    if (rows != kQRowsTeam && rows != kQRowsPacked && rows != kQRowsWave) return false;
+    return block == kQBlock || (block == kQBlockWide && rows != kQRowsPacked);
 }
 
 }  // namespace
 
 hipError_t launch_adamw_q8(const void *table, int nseg, uint32_t total_blocks, bool moments_q8,
-                           QGrad grad, bool with_delta, int block, bool packed,
+                           QGrad grad, bool with_delta, int block, QRows rows,
                            const AdamwConsts &c, hipStream_t stream, uint32_t lds_bytes) {
-    if (!block_ok(block, packed)) return hipErrorInvalidValue;
+    if (!block_ok(block, rows)) return hipErrorInvalidValue;
     const void *fn = nullptr;
     if (moments_q8) {
         switch (grad) {
-        case kQGradBf16: fn = pick_adamw_delta<true, kQGradBf16>(with_delta, block, packed); break;
-        case kQGradF32: fn = pick_adamw_delta<true, kQGradF32>(with_delta, block, packed); break;
-        case kQGradQ8: fn = pick_adamw_delta<true, kQGradQ8>(with_delta, block, packed); break;
+        case kQGradBf16: fn = pick_adamw_delta<true, kQGradBf16>(with_delta, block, rows); break;
+        case kQGradF32: fn = pick_adamw_delta<true, kQGradF32>(with_delta, block, rows); break;
+        case kQGradQ8: fn = pick_adamw_delta<true, kQGradQ8>(with_delta, block, rows); break;
         default: return hipErrorInvalidValue;
         }
     } else {
         // fp32 moments only pair with an int8 gradient here; the other
         // combinations run on the tile kernels of lema_kernels.hip
         if (grad != kQGradQ8) return hipErrorInvalidValue;
-        fn = pick_adamw_delta<false, kQGradQ8>(with_delta, block, packed);
+        fn = pick_adamw_delta<false, kQGradQ8>(with_delta, block, rows);
     }
     return launch_split(fn, block, total_blocks, lds_bytes, stream, table, nseg, c);
 }
 
 hipError_t launch_accum_q8(const void *table, int nseg, uint32_t total_blocks, bool overwrite,
-                           int block, bool packed, hipStream_t stream) {
-    if (!block_ok(block, packed)) return hipErrorInvalidValue;
-    const void *fn = overwrite ? pick_rows<kAccumOverwrite>(block, packed)
-                               : pick_rows<kAccumAdd>(block, packed);
+                           int block, QRows rows, hipStream_t stream) {
+    if (!block_ok(block, rows)) return hipErrorInvalidValue;
+    const void *fn = overwrite ? pick_rows<kAccumOverwrite>(block, rows)
+                               : pick_rows<kAccumAdd>(block, rows);
     return launch_split(fn, block, total_blocks, 0, stream, table, nseg);
 }
 
 hipError_t launch_quantize_q8(const void *table, int nseg, uint32_t total_blocks, bool dequantize,
-                              int block, bool packed, hipStream_t stream) {
-    if (!block_ok(block, packed)) return hipErrorInvalidValue;
-    const void *fn = dequantize ? pick_rows<kDequantize>(block, packed)
-                                : pick_rows<kQuantize>(block, packed);
+                              int block, QRows rows, hipStream_t stream) {
+    if (!block_ok(block, rows)) return hipErrorInvalidValue;
+    const void *fn = dequantize ? pick_rows<kDequantize>(block, rows)
+                                : pick_rows<kQuantize>(block, rows);
     return launch_split(fn, block, total_blocks, 0, stream, table, nseg);
 }
 

@@ -78,36 +78,42 @@ Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok, int chunks_max) {
         r.team_log2 = lg;
         r.chunks = chunks_max;
         r.flags |= kQPacked;
+    } else if (r.flags && r.team_log2 >= 6 && numel % 4 == 0) {
+        r.flags |= kQWave;    // teams of whole wavefronts, every row a multiple of 4 long
     }
     return r;
 }
 
+QRows rows_of(const Q8Rec &r) {
+    return (r.flags & kQPacked) ? kQRowsPacked : (r.flags & kQWave) ? kQRowsWave : kQRowsTeam;
+}
+
 uintptr_t bits(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
-// Launch `recs` in at most three groups, one per kernel shape: row teams in
-// kQBlock- or kQBlockWide-lane workgroups, and packed rows.  Every group's
-// table is built and checked before the first launch, so a size error
-// enqueues nothing.
+// Launch `recs` in at most five groups, one per kernel: row teams and wave
+// rows in kQBlock- or kQBlockWide-lane workgroups, and packed rows.  Every
+// group's table is built and checked before the first launch, so a size
+// error enqueues nothing.
 template <class LaunchFn>
 lema_status launch_groups(const std::vector<Q8Rec> &recs, int chunks_max, hipStream_t stream,
                           const LaunchFn &launch) {
     struct Group {
         int block;
-        bool packed;
+        QRows rows;
         int n;
         uint64_t blocks;
         std::vector<unsigned char> bytes;
     };
     std::vector<Group> groups;
-    const struct { int block; bool packed; } kinds[] = {
-        {kQBlock, false}, {kQBlock, true}, {kQBlockWide, false}};
+    const struct { int block; QRows rows; } kinds[] = {
+        {kQBlock, kQRowsTeam}, {kQBlock, kQRowsPacked}, {kQBlock, kQRowsWave},
+        {kQBlockWide, kQRowsTeam}, {kQBlockWide, kQRowsWave}};
     for (const auto &kind : kinds) {
         std::vector<Q8Rec> sel;
         for (const Q8Rec &r : recs)
-            if (block_of(r, chunks_max) == kind.block && ((r.flags & kQPacked) != 0) == kind.packed)
-                sel.push_back(r);
+            if (block_of(r, chunks_max) == kind.block && rows_of(r) == kind.rows) sel.push_back(r);
         if (sel.empty()) continue;
-        Group g{kind.block, kind.packed, static_cast<int>(sel.size()), 0, {}};
+        Group g{kind.block, kind.rows, static_cast<int>(sel.size()), 0, {}};
         g.bytes.assign(q8_table_bytes(g.n), 0);
         uint32_t *begin = reinterpret_cast<uint32_t *>(g.bytes.data());
         for (int i = 0; i < g.n; ++i) {
@@ -121,7 +127,7 @@ lema_status launch_groups(const std::vector<Q8Rec> &recs, int chunks_max, hipStr
     }
     for (const Group &g : groups) {
         lema_status st = launch_on_table(g.bytes, stream, [&](const void *table) {
-            return launch(table, g.n, static_cast<uint32_t>(g.blocks), g.block, g.packed);
+            return launch(table, g.n, static_cast<uint32_t>(g.blocks), g.block, g.rows);
         });
         if (st != LEMA_OK) return st;
     }
@@ -249,8 +255,8 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
     // and conversions move less per workgroup and keep full occupancy.
     const uint32_t lds = occupancy_lds_bytes(kQ8StepWorkgroupsPerCu);
     return launch_groups(recs, kQStepChunks, hs, [&](const void *table, int n, uint32_t blocks,
-                                                     int block, bool packed) {
-        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, packed, c, hs,
+                                                     int block, QRows rows) {
+        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, rows, c, hs,
                                block == kQBlock ? lds : 0);
     });
 }
@@ -282,8 +288,8 @@ lema_status lema_grad_accum_q8(const lema_accum_q8_seg *segs, int32_t nseg, int3
     if (recs.empty()) return LEMA_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     return launch_groups(recs, kQCodeChunks, hs, [&](const void *table, int n, uint32_t blocks,
-                                                     int block, bool packed) {
-        return launch_accum_q8(table, n, blocks, overwrite != 0, block, packed, hs);
+                                                     int block, QRows rows) {
+        return launch_accum_q8(table, n, blocks, overwrite != 0, block, rows, hs);
     });
 }
 
@@ -314,8 +320,8 @@ static lema_status convert_rows(const lema_q8_tensor *t, int32_t n, bool dequant
     if (recs.empty()) return LEMA_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     return launch_groups(recs, kQCodeChunks, hs, [&](const void *table, int nrec,
-                                                     uint32_t blocks, int block, bool packed) {
-        return launch_quantize_q8(table, nrec, blocks, dequantize, block, packed, hs);
+                                                     uint32_t blocks, int block, QRows rows) {
+        return launch_quantize_q8(table, nrec, blocks, dequantize, block, rows, hs);
     });
 }
 

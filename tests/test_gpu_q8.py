@@ -346,6 +346,106 @@ def test_repeated_calls_reuse_cached_tables(L):
     assert after["hits"] - before["hits"] == 10 * 4, (before, after)
 
 
+# ------------------------------------------------------------ wave rows
+#
+# Rows whose team is one or more whole wavefronts (64 lanes and up: rows of
+# about 500 to 16,384 elements) on vector-aligned arrays whose element count
+# is a multiple of 4 run in kernels of their own, through row-sized buffer
+# resources.  Team widths covered: 64 (1000: four rows per workgroup), 128
+# (2000), 256 (3000 with three chunks per lane, 4096 with four), 512 (5000,
+# wide workgroups) and 1024 (11,008 and 16,384).  Every case has a ragged
+# last row and, for the narrower teams, workgroups with teams past the last
+# row.
+
+WAVE_ROWS = [1000, 2000, 3000, 4096, 5000, 11008, 16384]
+
+
+def wave_numel(row_len: int) -> int:
+    rows = 9 if row_len <= 2000 else 3          # 9 rows of 1000: the third workgroup holds one
+    return row_len * rows + (row_len // 3) // 4 * 4 + 4
+
+
+@pytest.mark.parametrize("row_len", WAVE_ROWS)
+def test_wave_rows_quantize_dequantize(L, row_len):
+    """Zero, NaN, infinite and subnormal rows, a ragged last row."""
+    n = wave_numel(row_len)
+    assert n % 4 == 0
+    x = host_f32(n, 1e-3, 7100 + row_len)
+    x[:row_len] = 0.0
+    x[row_len + 5] = np.nan
+    x[2 * row_len - 1] = -np.inf
+    if n >= 4 * row_len:
+        x[3 * row_len:4 * row_len] = np.float32(-3e-42)
+    q = L.Q8.empty(n, row_len)
+    L.quantize_rows([(up(x), q)])
+    rq, rs = oracle.quantize_rows(x, row_len)
+    compare_codes(q.codes, rq, "codes")
+    compare_f32(to_np(q.scale), rs, "scale")
+    back = torch.empty(n, device=DEV)
+    L.dequantize_rows([(back, q)])
+    compare_f32(to_np(back), oracle.dequantize_rows(rq, rs, row_len), "dequantized")
+
+
+@pytest.mark.parametrize("row_len", WAVE_ROWS)
+@pytest.mark.parametrize("kinds", [("q8", "bf16", True), ("q8", "q8", True), ("q8", "fp32", False),
+                                   ("fp32", "q8", True)])
+def test_wave_rows_step(L, row_len, kinds):
+    moments, grad, delta = kinds
+    c = Case(L, wave_numel(row_len), row_len, 9050 + row_len, grad=grad, moments=moments,
+             delta=delta)
+    step(L, [c], 30)
+    torch.cuda.synchronize()
+    c.check(oracle_consts(HP, 30), f"wave[{moments},{grad},{delta},{row_len}]")
+
+
+def nonzero_codes(n, seed):
+    rng = np.random.default_rng(seed)
+    k = rng.integers(1, 128, n) * rng.choice([-1, 1], n)
+    return k.astype(np.int8)
+
+
+@pytest.mark.parametrize("row_len", WAVE_ROWS)
+def test_wave_rows_step_special_scales(L, row_len):
+    """Old row scales of +inf (over codes that are all nonzero, so every
+    element of the row dequantizes to an infinity) and NaN: lanes whose
+    chunks lie past the row's end must stay out of the new absmax."""
+    c = Case(L, wave_numel(row_len), row_len, 9150 + row_len, delta=True)
+    rows = L.Q8.rows_of(c.n, row_len)
+    last = slice((rows - 1) * row_len, c.n)
+    c.mq[0][last] = nonzero_codes(c.n - (rows - 1) * row_len, 1)
+    c.mq[1][rows - 1] = np.inf
+    c.vq[1][1] = np.nan
+    c.m = L.Q8(up(c.mq[0]), up(c.mq[1]), row_len)
+    c.v = L.Q8(up(c.vq[0]), up(c.vq[1]), row_len)
+    step(L, [c], 4)
+    torch.cuda.synchronize()
+    _, m, v = c.check(oracle_consts(HP, 4), f"wave_specials[{row_len}]")
+    assert np.isinf(m[1][rows - 1]) and np.isnan(v[1][1])
+
+
+@pytest.mark.parametrize("row_len", WAVE_ROWS)
+def test_wave_rows_accumulation(L, row_len):
+    """Overwrite, then three dequantize-add-requantize micro-batches; then
+    one more onto old scales of +inf (all codes nonzero) and NaN."""
+    n = wave_numel(row_len)
+    rows = L.Q8.rows_of(n, row_len)
+    acc = L.Q8.empty(n, row_len)
+    ref_q = np.zeros(n, np.int8)
+    ref_s = np.zeros(rows, np.float32)
+    for k in range(5):
+        if k == 4:
+            ref_q[(rows - 1) * row_len:] = nonzero_codes(n - (rows - 1) * row_len, 2)
+            ref_s[rows - 1], ref_s[0] = np.inf, np.nan
+            acc = L.Q8(up(ref_q), up(ref_s), row_len)
+        g = host_bf16(n, 1e-3, 9850 + 10 * row_len + k)
+        L.grad_accum_q8([L.AccumQ8Segment(acc, up(g))], overwrite=k == 0)
+        oracle.grad_accum_q8(ref_q, ref_s, g, k == 0, row_len)
+        torch.cuda.synchronize()
+        compare_codes(acc.codes, ref_q, f"acc{k}.codes")
+        compare_f32(to_np(acc.scale), ref_s, f"acc{k}.scale")
+    assert np.isinf(ref_s[rows - 1]) and np.isnan(ref_s[0])
+
+
 # -------------------------------------------------- workloads at full size
 
 def _workload_q8(L, w, row_len_of, *, delta, grad="bf16"):
