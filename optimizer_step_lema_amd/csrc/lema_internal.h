@@ -77,6 +77,13 @@ constexpr int kQStepChunks = 4;
 constexpr int kQ8StepWorkgroupsPerCu = 4;     // occupancy cap of the 256-lane step
 constexpr int kQCodeChunks = 4;
 constexpr int kQWideChunks = 4;
+// Wave-row accumulation and conversions hold up to 16 chunks per lane in
+// kQBlock-lane workgroups, which covers every row up to kQMaxRow there: on
+// MI355X rows of 11,008 ran 26% faster as 256-lane teams with 11 chunks than
+// as 1024-lane teams with 3 (four or five rows per CU instead of two), and
+// rows of 4096 as well as one wavefront with 16 chunks as four with 4.  The
+// step keeps 4 (its lanes hold more state per chunk).
+constexpr int kQWaveCodeChunks = 16;
 constexpr int64_t kQMaxRow = int64_t(kQBlockWide) * kQWideChunks * 4;   // 16384 elements
 
 struct Q8Rec {
@@ -91,7 +98,7 @@ struct Q8Rec {
     int32_t chunks;       // 4-element chunks per lane
     int32_t flags;        // kQVector: full chunks take 16/8/4-byte vector accesses;
                           // kQPacked: packed rows; kQWave: wave rows
-    int32_t reserved;
+    int32_t block;        // lanes of the workgroups the record is sized for
 };
 static_assert(sizeof(Q8Rec) == 120, "int8 segment record is 120 bytes");
 constexpr int32_t kQVector = 1;

@@ -859,7 +859,9 @@ enum RowOp : int { kAccumAdd = 0, kAccumOverwrite = 1, kQuantize = 2, kDequantiz
 
 template <RowOp kOp, int kThreads, int kRows>
 struct CodeRows {
-    static constexpr int kC = kThreads == kQBlockWide ? kQWideChunks : kQCodeChunks;
+    static constexpr int kC = kRows == kQRowsWave     ? kQWaveCodeChunks
+                              : kThreads == kQBlockWide ? kQWideChunks
+                                                        : kQCodeChunks;
     static constexpr bool kAccum = kOp == kAccumAdd || kOp == kAccumOverwrite;
     static constexpr bool kReadsCodes = kOp == kAccumAdd || kOp == kDequantize;
 
@@ -1105,25 +1107,29 @@ const void *pick_adamw_delta(bool with_delta, int block, QRows rows) {
                       : pick_adamw<kMomQ8, kGrad, false>(block, rows);
 }
 
-template <RowOp kOp, int kRows>
-const void *pick_code_rows(int block) {
-    return block == kQBlock ? reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, kRows>)
-                            : reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlockWide, kRows>);
-}
-
+// Accumulation and conversions: wave rows and packed rows run in kQBlock-lane
+// workgroups only (wave rows hold up to kQWaveCodeChunks chunks per lane).
 template <RowOp kOp>
 const void *pick_rows(int block, QRows rows) {
     switch (rows) {
     case kQRowsPacked:
         return reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, kQRowsPacked>);
-    case kQRowsWave: return pick_code_rows<kOp, kQRowsWave>(block);
-    default: return pick_code_rows<kOp, kQRowsTeam>(block);
+    case kQRowsWave:
+        return reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, kQRowsWave>);
+    default:
+        return block == kQBlock
+                   ? reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlock, kQRowsTeam>)
+                   : reinterpret_cast<const void *>(&code_rows_kernel<kOp, kQBlockWide, kQRowsTeam>);
     }
 }
 
 bool block_ok(int block, QRows rows) {
     if (rows != kQRowsTeam && rows != kQRowsPacked && rows != kQRowsWave) return false;
     return block == kQBlock || (block == kQBlockWide && rows != kQRowsPacked);
+}
+
+bool rows_block_ok(int block, QRows rows) {
+    return block_ok(block, rows) && (block == kQBlock || rows == kQRowsTeam);
 }
 
 }  // namespace
@@ -1151,7 +1157,7 @@ hipError_t launch_adamw_q8(const void *table, int nseg, uint32_t total_blocks, b
 
 hipError_t launch_accum_q8(const void *table, int nseg, uint32_t total_blocks, bool overwrite,
                            int block, QRows rows, hipStream_t stream) {
-    if (!block_ok(block, rows)) return hipErrorInvalidValue;
+    if (!rows_block_ok(block, rows)) return hipErrorInvalidValue;
     const void *fn = overwrite ? pick_rows<kAccumOverwrite>(block, rows)
                                : pick_rows<kAccumAdd>(block, rows);
     return launch_split(fn, block, total_blocks, 0, stream, table, nseg);
@@ -1159,7 +1165,7 @@ hipError_t launch_accum_q8(const void *table, int nseg, uint32_t total_blocks, b
 
 hipError_t launch_quantize_q8(const void *table, int nseg, uint32_t total_blocks, bool dequantize,
                               int block, QRows rows, hipStream_t stream) {
-    if (!block_ok(block, rows)) return hipErrorInvalidValue;
+    if (!rows_block_ok(block, rows)) return hipErrorInvalidValue;
     const void *fn = dequantize ? pick_rows<kDequantize>(block, rows)
                                 : pick_rows<kQuantize>(block, rows);
     return launch_split(fn, block, total_blocks, 0, stream, table, nseg);

@@ -19,25 +19,28 @@ namespace lema {
 namespace {
 
 static_assert(kQMaxRow == LEMA_Q8_MAX_ROW, "row limit of the header and the kernels agree");
+static_assert(int64_t(kQBlock) * kQWaveCodeChunks * 4 >= kQMaxRow,
+              "wave-row accumulation and conversions need only kQBlock-lane workgroups");
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Team width (log2), chunks per lane and workgroup size for rows of row_len
 // elements: the narrowest team whose lanes hold at most `chunks_max` chunks
 // in a kQBlock-lane workgroup, else a team of a kQBlockWide-lane workgroup
-// with at most kQWideChunks per lane.
+// with at most kQWideChunks per lane.  Wave rows use teams of at least one
+// wavefront (min_log2w = 6).
 struct Shape {
     int32_t log2w, chunks;
     int block;
 };
 
-Shape shape_for(int64_t row_len, int chunks_max) {
+Shape shape_for(int64_t row_len, int chunks_max, int min_log2w = 0) {
     const int64_t need = ceil_div(row_len, 4);
-    int lg = 0;
+    int lg = min_log2w;
     while ((1 << lg) < kQBlock && ceil_div(need, int64_t(1) << lg) > chunks_max) ++lg;
     if (ceil_div(need, int64_t(1) << lg) <= chunks_max)
         return {lg, static_cast<int32_t>(ceil_div(need, int64_t(1) << lg)), kQBlock};
-    lg = 0;
+    lg = min_log2w;
     while (ceil_div(need, int64_t(1) << lg) > kQWideChunks) ++lg;
     return {lg, static_cast<int32_t>(ceil_div(need, int64_t(1) << lg)), kQBlockWide};
 }
@@ -51,19 +54,20 @@ bool packed_row_len(int64_t row_len) {
     return (s & (s - 1)) == 0;
 }
 
-int block_of(const Q8Rec &r, int chunks_max) {
-    return (r.flags & kQPacked) ? kQBlock : shape_for(r.row_len, chunks_max).block;
-}
-
-uint64_t blocks_of(const Q8Rec &r, int chunks_max) {
-    int64_t rows_per_block = block_of(r, chunks_max) >> r.team_log2;
+uint64_t blocks_of(const Q8Rec &r) {
+    int64_t rows_per_block = r.block >> r.team_log2;
     if (r.flags & kQPacked) rows_per_block *= r.chunks;
     return static_cast<uint64_t>(ceil_div(r.rows, rows_per_block));
 }
 
 bool row_len_ok(int64_t row_len) { return row_len >= 1 && row_len <= kQMaxRow; }
 
-Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok, int chunks_max) {
+// The record of one segment.  Vector-aligned rows go packed (4 .. 256
+// elements, S a power of two), or as wave rows when the segment's element
+// count is a multiple of 4 and a row spans at least 64 vectors (teams of
+// whole wavefronts holding up to `wave_chunks` chunks per lane); everything
+// else goes to row teams of at most `chunks_max` chunks per lane.
+Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok, int chunks_max, int wave_chunks) {
     Q8Rec r{};
     r.numel = numel;
     r.row_len = row_len;
@@ -71,15 +75,21 @@ Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok, int chunks_max) {
     const Shape sh = shape_for(row_len, chunks_max);
     r.team_log2 = sh.log2w;
     r.chunks = sh.chunks;
+    r.block = sh.block;
     r.flags = (vector_ok && row_len % 4 == 0) ? kQVector : 0;
     if (r.flags && packed_row_len(row_len)) {
         int lg = 0;
         while ((int64_t(4) << lg) < row_len) ++lg;
         r.team_log2 = lg;
         r.chunks = chunks_max;
+        r.block = kQBlock;
         r.flags |= kQPacked;
-    } else if (r.flags && r.team_log2 >= 6 && numel % 4 == 0) {
-        r.flags |= kQWave;    // teams of whole wavefronts, every row a multiple of 4 long
+    } else if (r.flags && row_len >= 256 && numel % 4 == 0) {
+        const Shape w = shape_for(row_len, wave_chunks, 6);
+        r.team_log2 = w.log2w;
+        r.chunks = w.chunks;
+        r.block = w.block;
+        r.flags |= kQWave;
     }
     return r;
 }
@@ -95,7 +105,7 @@ uintptr_t bits(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 // group's table is built and checked before the first launch, so a size
 // error enqueues nothing.
 template <class LaunchFn>
-lema_status launch_groups(const std::vector<Q8Rec> &recs, int chunks_max, hipStream_t stream,
+lema_status launch_groups(const std::vector<Q8Rec> &recs, hipStream_t stream,
                           const LaunchFn &launch) {
     struct Group {
         int block;
@@ -111,14 +121,14 @@ lema_status launch_groups(const std::vector<Q8Rec> &recs, int chunks_max, hipStr
     for (const auto &kind : kinds) {
         std::vector<Q8Rec> sel;
         for (const Q8Rec &r : recs)
-            if (block_of(r, chunks_max) == kind.block && rows_of(r) == kind.rows) sel.push_back(r);
+            if (r.block == kind.block && rows_of(r) == kind.rows) sel.push_back(r);
         if (sel.empty()) continue;
         Group g{kind.block, kind.rows, static_cast<int>(sel.size()), 0, {}};
         g.bytes.assign(q8_table_bytes(g.n), 0);
         uint32_t *begin = reinterpret_cast<uint32_t *>(g.bytes.data());
         for (int i = 0; i < g.n; ++i) {
             begin[i] = static_cast<uint32_t>(g.blocks);
-            g.blocks += blocks_of(sel[i], chunks_max);
+            g.blocks += blocks_of(sel[i]);
             if (g.blocks > 0xFFF00000ull) return LEMA_ERR_SIZE;
         }
         begin[g.n] = static_cast<uint32_t>(g.blocks);
@@ -208,7 +218,7 @@ lema_status validate_q8_segs(const lema_adamw_q8_seg *segs, int32_t nseg, int32_
         }
         if (s.delta && with_delta) *with_delta = true;
         if (recs) {
-            Q8Rec r = make_rec(s.numel, s.row_len, vec, kQStepChunks);
+            Q8Rec r = make_rec(s.numel, s.row_len, vec, kQStepChunks, kQStepChunks);
             const void *ptrs[10] = {s.master, s.exp_avg, mom_q8 ? s.exp_avg_scale : nullptr,
                                     s.exp_avg_sq, mom_q8 ? s.exp_avg_sq_scale : nullptr, s.grad,
                                     gd == LEMA_GRAD_Q8 ? s.grad_scale : nullptr, s.weight_bf16,
@@ -254,7 +264,7 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
     // adapters).  The 1024-lane ones fit once per CU anyway.  Accumulation
     // and conversions move less per workgroup and keep full occupancy.
     const uint32_t lds = occupancy_lds_bytes(kQ8StepWorkgroupsPerCu);
-    return launch_groups(recs, kQStepChunks, hs, [&](const void *table, int n, uint32_t blocks,
+    return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks,
                                                      int block, QRows rows) {
         return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, rows, c, hs,
                                block == kQBlock ? lds : 0);
@@ -275,7 +285,7 @@ lema_status lema_grad_accum_q8(const lema_accum_q8_seg *segs, int32_t nseg, int3
         if (!s.acc || !s.acc_scale || !s.grad_bf16) return LEMA_ERR_NULL;
         if ((bits(s.acc_scale) & 3) || (bits(s.grad_bf16) & 1)) return LEMA_ERR_ALIGN;
         const bool vec = (bits(s.acc) & 3) == 0 && (bits(s.grad_bf16) & 7) == 0;
-        Q8Rec r = make_rec(s.numel, s.row_len, vec, kQCodeChunks);
+        Q8Rec r = make_rec(s.numel, s.row_len, vec, kQCodeChunks, kQWaveCodeChunks);
         add_span(spans, s.acc, s.numel, 1, true);
         add_span(spans, s.acc_scale, r.rows, 4, true);
         add_span(spans, s.grad_bf16, s.numel, 2, false);
@@ -287,7 +297,7 @@ lema_status lema_grad_accum_q8(const lema_accum_q8_seg *segs, int32_t nseg, int3
     if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
     if (recs.empty()) return LEMA_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    return launch_groups(recs, kQCodeChunks, hs, [&](const void *table, int n, uint32_t blocks,
+    return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks,
                                                      int block, QRows rows) {
         return launch_accum_q8(table, n, blocks, overwrite != 0, block, rows, hs);
     });
@@ -307,7 +317,7 @@ static lema_status convert_rows(const lema_q8_tensor *t, int32_t n, bool dequant
         if (!s.x || !s.codes || !s.scale) return LEMA_ERR_NULL;
         if ((bits(s.x) | bits(s.scale)) & 3) return LEMA_ERR_ALIGN;
         const bool vec = (bits(s.x) & 15) == 0 && (bits(s.codes) & 3) == 0;
-        Q8Rec r = make_rec(s.numel, s.row_len, vec, kQCodeChunks);
+        Q8Rec r = make_rec(s.numel, s.row_len, vec, kQCodeChunks, kQWaveCodeChunks);
         add_span(spans, s.x, s.numel, 4, dequantize);
         add_span(spans, s.codes, s.numel, 1, !dequantize);
         add_span(spans, s.scale, r.rows, 4, !dequantize);
@@ -319,7 +329,7 @@ static lema_status convert_rows(const lema_q8_tensor *t, int32_t n, bool dequant
     if (any_conflict(spans)) return LEMA_ERR_OVERLAP;
     if (recs.empty()) return LEMA_OK;
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    return launch_groups(recs, kQCodeChunks, hs, [&](const void *table, int nrec,
+    return launch_groups(recs, hs, [&](const void *table, int nrec,
                                                      uint32_t blocks, int block, QRows rows) {
         return launch_quantize_q8(table, nrec, blocks, dequantize, block, rows, hs);
     });

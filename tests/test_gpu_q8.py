@@ -325,9 +325,10 @@ def test_q8_plans_match_direct_calls(L):
 
 
 def test_repeated_calls_reuse_cached_tables(L):
-    """A plan stepped again and again uploads its launch tables once: calls
-    whose segments need both workgroup sizes (rows of 4096 and of 11,008)
-    launch two tables per call, and both stay cached."""
+    """A plan stepped again and again uploads its launch tables once: step
+    calls whose segments need both workgroup sizes (rows of 4096 and of
+    11,008) launch two tables per call, accumulation calls (both row lengths
+    in 256-lane wave rows) one, and all stay cached."""
     cases = [Case(L, 4096 * 2, 4096, 9950), Case(L, 11008 * 2, 11008, 9960)]
     plan = L.AdamwQ8Plan([c.segment(L) for c in cases])
     accs = [L.Q8.empty(c.n, c.row_len) for c in cases]
@@ -343,21 +344,23 @@ def test_repeated_calls_reuse_cached_tables(L):
     torch.cuda.synchronize()
     after = L.table_cache_stats()
     assert after["uploads"] == before["uploads"], (before, after)
-    assert after["hits"] - before["hits"] == 10 * 4, (before, after)
+    assert after["hits"] - before["hits"] == 10 * (2 + 1), (before, after)
 
 
 # ------------------------------------------------------------ wave rows
 #
-# Rows whose team is one or more whole wavefronts (64 lanes and up: rows of
-# about 500 to 16,384 elements) on vector-aligned arrays whose element count
-# is a multiple of 4 run in kernels of their own, through row-sized buffer
-# resources.  Team widths covered: 64 (1000: four rows per workgroup), 128
-# (2000), 256 (3000 with three chunks per lane, 4096 with four), 512 (5000,
-# wide workgroups) and 1024 (11,008 and 16,384).  Every case has a ragged
-# last row and, for the narrower teams, workgroups with teams past the last
-# row.
+# Rows of 256 elements and more (other than the packed ones) on
+# vector-aligned arrays whose element count is a multiple of 4 run as wave
+# rows: teams of whole wavefronts, through row-sized buffer resources.  The
+# step's teams (4 chunks per lane) covered here: 64 lanes (300 with two
+# chunks, 1000 with four: four rows per workgroup), 128 (2000), 256 (3000,
+# 4096), 512 and 1024 in wide workgroups (5000; 11,008 and 16,384).
+# Accumulation and conversions hold up to 16 chunks per lane in 256-lane
+# workgroups: 64 lanes for rows up to 4096, 128 for 5000, 256 for 11,008 and
+# 16,384.  Every case has a ragged last row and, for the narrower teams,
+# workgroups with teams past the last row.
 
-WAVE_ROWS = [1000, 2000, 3000, 4096, 5000, 11008, 16384]
+WAVE_ROWS = [300, 1000, 2000, 3000, 4096, 5000, 11008, 16384]
 
 
 def wave_numel(row_len: int) -> int:
