@@ -468,6 +468,15 @@ def q8_bench(torch, L, synth, a):
     K = w.microbatches
     grad = "q8" if K > 1 else "bf16"
     row_lens = [shape[-1] for _, shape in w.segments]
+    from optimizer_step_lema_amd._native import LEMA_Q8_MAX_ROW
+    if max(row_lens) > LEMA_Q8_MAX_ROW:
+        # e.g. the rank-share workload: its segments are element ranges of the
+        # flattened tensors, while int8 state is sharded on whole rows (a rank
+        # owns complete rows and their scales)
+        print(f"bench.py: --q8 --workload {a.workload}: its segments are 1-D element "
+              f"ranges (rows of up to {max(row_lens)} elements, the limit is "
+              f"{LEMA_Q8_MAX_ROW}); int8 state shards on whole rows", file=sys.stderr)
+        sys.exit(2)
     rows = [-(-n // rl) for n, rl in zip(w.numels, row_lens)]
     step_bytes = sum(q8_step_bytes(n, r, grad, delta) for n, r in zip(w.numels, rows))
     accum_bytes = 0
