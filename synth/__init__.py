@@ -152,6 +152,23 @@ def _llama_full_shard(ranks: int, rank: int):
     return segs
 
 
+def _llama_full_row_shard(ranks: int, rank: int):
+    """Rank `rank`'s share when every tensor is split on whole rows (its last
+    dimension is the row): int8 state keeps each row's codes with that row's
+    scale, so a rank owns complete rows.  The row index range is split like
+    shard_range splits elements; a 1-D tensor is one row and goes whole to
+    rank 0."""
+    segs = []
+    for label, shape in _llama_full():
+        rows = 1
+        for d in shape[:-1]:
+            rows *= d
+        b, e = shard_range(rows, ranks, rank)
+        if e > b:
+            segs.append((f"{label}[rows {b}:{e}]", (e - b, shape[-1])))
+    return segs
+
+
 WORKLOADS = {
     "gpt2_cattn_first2": Workload(
         "gpt2_cattn_first2", 1, _gpt2_first2(), step=1, fresh_state=True,
@@ -178,6 +195,12 @@ WORKLOADS = {
         description="one of 8 data-parallel ranks' share of the whole "
                     "Llama-2-7B shape: the first eighth of each of the 291 "
                     "tensors, bf16 grad, t=10"),
+    "llama7b_full_rows_shard8": Workload(
+        "llama7b_full_rows_shard8", 7, _llama_full_row_shard(8, 0), step=10,
+        description="rank 0 of 8 data-parallel ranks' share of the whole "
+                    "Llama-2-7B shape split on whole rows (the layout int8 "
+                    "state shards in): the first eighth of each tensor's "
+                    "rows, the 1-D norm weights whole, bf16 grad, t=10"),
 }
 
 

@@ -38,6 +38,7 @@ def test_state_layout_is_16_bytes():
     ("llama7b_full", 6_738_415_616, 291),
     ("llama7b_lora_r16", 39_976_960, 448),
     ("llama7b_full_shard8", 842_301_952, 291),
+    ("llama7b_full_rows_shard8", 842_534_912, 291),
 ])
 def test_workload_sizes(name, params, nseg):
     w = synth.WORKLOADS[name]
@@ -68,3 +69,24 @@ def test_shard_workload_is_the_first_eighth():
     full, shard = synth.WORKLOADS["llama7b_full"], synth.WORKLOADS["llama7b_full_shard8"]
     assert shard.numels == [synth.shard_range(n, 8, 0)[1] for n in full.numels]
     assert shard.params * 8 == full.params
+
+
+def test_row_shards_are_whole_rows_and_partition_the_model():
+    """Splitting on whole rows: every rank's segments are complete rows of
+    their tensor, the 8 ranks together hold every parameter once, and rank 0
+    holds an eighth of every 2-D tensor (all of them split evenly) plus the
+    65 norm weights whole: 6,738,415,616 / 8 + 7/8 * 65 * 4096."""
+    full = synth.WORKLOADS["llama7b_full"]
+    shapes = dict(full.segments)
+    total = 0
+    for rank in range(8):
+        segs = synth._llama_full_row_shard(8, rank)
+        for label, (rows, row_len) in segs:
+            assert row_len == shapes[label.split("[")[0]][-1]
+        total += sum(rows * row_len for _, (rows, row_len) in segs)
+        if rank:
+            assert len(segs) == 291 - 65           # the norm rows stay on rank 0
+    assert total == full.params
+    w = synth.WORKLOADS["llama7b_full_rows_shard8"]
+    assert w.segments == synth._llama_full_row_shard(8, 0)
+    assert w.params == full.params // 8 + 7 * 65 * 4096 // 8

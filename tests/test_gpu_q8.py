@@ -543,6 +543,58 @@ def test_q8_single_segment_beyond_2_31_elements(L):
     torch.cuda.empty_cache()
 
 
+def test_llama7b_full_rows_shard8_q8_sampled(L):
+    """One of 8 data-parallel ranks' share of the whole 7B shape split on
+    whole rows (842.5 M params in 291 tensors), with int8 moments, in the flat
+    state bench.py times: one step with delta, checked against the oracle on
+    whole sampled rows of every tensor (the first, the last and 14 random
+    ones; a row is the unit the oracle quantizes)."""
+    w = synth.WORKLOADS["llama7b_full_rows_shard8"]
+    row_lens = [shape[-1] for _, shape in w.segments]
+    el, rw, segs = L.flat_q8_state(w.numels, row_lens, grad="bf16", delta=True, device=DEV)
+    for i, s in enumerate(segs):
+        st = synth.make_segment_state(w, i, DEV, with_orig=True)
+        s.master.copy_(st["master"])
+        L.quantize_rows([(st["m"], s.exp_avg), (st["v"], s.exp_avg_sq)])
+        s.orig.copy_(st["orig"])
+        s.grad.copy_(st["grads"][0])
+        del st
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(21)
+    picks = []
+    for n, rl in zip(w.numels, row_lens):
+        rows = n // rl
+        r = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 14)]))
+        el_idx = (r[:, None] * rl + np.arange(rl)[None, :]).reshape(-1)
+        picks.append((torch.from_numpy(r).to(DEV), torch.from_numpy(el_idx).to(DEV)))
+
+    def take(t, i):
+        return to_np(t[i])
+
+    before = []
+    for s, (ri, ei) in zip(segs, picks):
+        before.append({
+            "master": take(s.master, ei), "grad": take(s.grad, ei), "orig": take(s.orig, ei),
+            "m": (take(s.exp_avg.codes, ei), take(s.exp_avg.scale, ri)),
+            "v": (take(s.exp_avg_sq.codes, ei), take(s.exp_avg_sq.scale, ri))})
+    L.adamw_step_q8(segs, step=w.step, **HP)
+    torch.cuda.synchronize()
+    consts = oracle_consts(HP, w.step)
+    for k, (s, (ri, ei), b, rl) in enumerate(zip(segs, picks, before, row_lens)):
+        master, m, v = b["master"].copy(), b["m"], b["v"]
+        wref, dref = oracle.adamw_step_q8(master, m, v, b["grad"], consts, rl, orig=b["orig"])
+        tag = f"rows shard seg{k}"
+        compare_f32(take(s.master, ei), master, tag + ".master")
+        compare_bf16(take(s.weight, ei), wref, tag + ".weight")
+        compare_f32(take(s.delta, ei), dref, tag + ".delta")
+        for name, q, ref in (("m", s.exp_avg, m), ("v", s.exp_avg_sq, v)):
+            bad = int((take(q.codes, ei) != ref[0]).sum())
+            assert bad == 0, f"{tag}.{name}: {bad} int8 codes differ"
+            compare_f32(take(q.scale, ri), ref[1], f"{tag}.{name}.scale")
+    del segs, el, rw
+    torch.cuda.empty_cache()
+
+
 def test_llama7b_attn_last4_q8_full(L):
     """Llama-2-7B q,k,v,o of the last 4 layers (268 M parameters, rows of
     4096) with int8 moments, bf16 gradient and delta: every element checked."""
