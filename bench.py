@@ -85,6 +85,9 @@ def parse():
     ap.add_argument("--copy-gib", type=float, default=4.0, help="size of the copy-ceiling test")
     ap.add_argument("--merge", action="store_true",
                     help="time lema_merge_delta (base + delta -> servable bf16) on the workload")
+    ap.add_argument("--checkpoint", metavar="DIR", default=None,
+                    help="time lema_checkpoint_save and lema_checkpoint_load of the "
+                         "workload's master, m, v and delta to a file in DIR")
     ap.add_argument("--q8", action="store_true",
                     help="int8 moments with per-row scales (and int8 accumulators for "
                          "multi-micro-batch workloads), README 'Quantization'")
@@ -163,6 +166,8 @@ def main():
         sys.exit(2)
     if a.slot_stream:
         line = slot_stream_bench(torch, L, synth, a)
+    elif a.checkpoint:
+        line = checkpoint_bench(torch, L, synth, a)
     elif a.merge:
         line = merge_bench(torch, L, synth, a)
     elif a.q8:
@@ -699,6 +704,54 @@ def merge_bench(torch, L, synth, a):
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "merge_tile_kernel",
                      "algorithmic_bytes_per_launch": per, "avg_launch_ms": ms},
+    }
+
+
+# ------------------------------------------------------------ checkpoint
+
+def checkpoint_bench(torch, L, synth, a):
+    """lema_checkpoint_save and lema_checkpoint_load of the workload's fp32
+    master, m, v and delta (README "Features": checkpoints of the delta with
+    the optimizer states) to a safetensors file in --checkpoint DIR: the
+    rate of each whole call, device to file and back, through the page cache
+    of the file system DIR is on."""
+    w = synth.WORKLOADS[a.workload]
+    fs, segs = L.flat_adamw_state(w.numels, delta=True)
+    for i, s in enumerate(segs):
+        st = synth.make_segment_state(w, i, "cuda")
+        s.master.copy_(st["master"])
+        s.exp_avg.copy_(st["m"])
+        s.exp_avg_sq.copy_(st["v"])
+        s.delta.copy_(st["master"])
+        del st
+    tensors = L.checkpoint_tensors(segs, delta=True)
+    nbytes = sum(t.numel() * t.element_size() for t in tensors.values())
+    path = os.path.join(a.checkpoint, f"bench_{w.name}.safetensors")
+    torch.cuda.synchronize()
+    save_s, load_s = [], []
+    file_bytes = None
+    try:
+        for _ in range(max(1, a.steps)):
+            t0 = time.perf_counter()
+            L.save_checkpoint(path, tensors, step=w.step)
+            save_s.append(time.perf_counter() - t0)
+            file_bytes = os.path.getsize(path)
+            t0 = time.perf_counter()
+            L.load_checkpoint(path, tensors)
+            load_s.append(time.perf_counter() - t0)
+    finally:
+        if os.path.exists(path):
+            os.remove(path)
+    sv, ld = sorted(save_s)[len(save_s) // 2], sorted(load_s)[len(load_s) // 2]
+    return {
+        "metric": "checkpoint save GB/s (load GB/s beside it), 1 GPU",
+        "value": nbytes / sv / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": len(save_s),
+        "warmup": 0, "ms_per_step": 1e3 * sv, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": a.workload, "params": w.params, "segments": len(w.segments),
+                   "tensors": len(tensors), "file_bytes": file_bytes, "data_bytes": nbytes,
+                   "contents": "fp32 master, m, v and delta of every tensor"},
+        "save_s": save_s, "load_s": load_s, "load_gbps": nbytes / ld / 1e9,
     }
 
 

@@ -73,6 +73,9 @@ typedef int32_t lema_status;
 #define LEMA_ERR_HIP        (-7)  /* the HIP runtime reported an error                 */
 #define LEMA_ERR_ALIGN      (-8)  /* pointer not aligned to its element size           */
 #define LEMA_ERR_CAPTURE    (-9)  /* the stream is capturing a HIP graph               */
+#define LEMA_ERR_IO         (-10) /* a checkpoint file could not be read or written,   */
+                                  /* or is not a well-formed safetensors file          */
+#define LEMA_ERR_NOT_FOUND  (-11) /* a requested tensor is not in the checkpoint file  */
 
 /* Static string naming a status (never NULL). */
 const char *lema_status_string(lema_status s);
@@ -479,6 +482,68 @@ lema_status lema_slot_stream_q8(lema_slot_pool *pool, const lema_layer_q8 *layer
 /* Page-locked host allocation of exactly `bytes` bytes (hipHostMalloc). */
 lema_status lema_host_alloc(void **out, size_t bytes);
 lema_status lema_host_free(void *p);
+
+/* ----------------------------------------------------------- checkpoints
+ *
+ * LEMA README, "Features" (interval-based automatic checkpointing of the
+ * full fine-tuning delta with the optimizer states) and "Selective Full
+ * Fine-Tuning" (a checkpoint holds the small fp32 delta, updated minus
+ * original, plus the optimizer state; training resumes from it, and
+ * merge_delta turns a base model and a delta file into a servable one).
+ *
+ * A checkpoint file is a safetensors file, the format of the pages'
+ * checkpoints and of merge_delta: an 8-byte little-endian header length N,
+ * N bytes of JSON naming every tensor with its dtype ("F32", "BF16" or
+ * "I8"), its 1-D shape [numel] and its byte range [begin, end) in the data
+ * that follows, padded with spaces to a multiple of 8; then the tensors'
+ * bytes back to back, in the order given.  The JSON's "__metadata__" object
+ * holds {"format": "lema-checkpoint", "step": "<t>"}, t being the last step
+ * taken.  Which tensors to store is the caller's choice: the fp32 master, m
+ * and v (or their int8 codes and row scales) for a bit-exact resume, the
+ * delta for merge_delta.
+ *
+ * Both calls are synchronous: they copy between device memory and the file
+ * through page-locked staging buffers on `stream` (device copies overlap the
+ * file reads and writes) and return once the data has arrived, having
+ * synchronized `stream`.  They refuse a capturing stream (LEMA_ERR_CAPTURE).
+ */
+typedef enum { LEMA_DT_F32 = 0, LEMA_DT_BF16 = 1, LEMA_DT_I8 = 2 } lema_dtype;
+
+typedef struct {
+    const char *name;     /* 1 .. 255 bytes of printable ASCII other than the  */
+                          /* double quote and the backslash; unique in a call  */
+    int32_t     dtype;    /* lema_dtype                                         */
+    int32_t     reserved; /* 0                                                  */
+    void       *data;     /* device memory: read by save, written by load;     */
+                          /* NULL only when numel == 0                          */
+    int64_t     numel;    /* >= 0                                               */
+} lema_ckpt_tensor;
+
+/* Writes the n tensors and the step t to `path`.  The file is written under
+ * `path` + ".tmp", flushed to storage and then renamed over `path`, so a save
+ * that fails (or is interrupted) leaves an earlier file at `path` intact and
+ * removes its temporary file.
+ * Errors: LEMA_ERR_NULL (path, t with n > 0, a name, or data with numel > 0),
+ * LEMA_ERR_SIZE (n < 0, numel < 0, a bad or repeated name, reserved != 0),
+ * LEMA_ERR_DTYPE, LEMA_ERR_CAPTURE, LEMA_ERR_IO, LEMA_ERR_HIP. */
+lema_status lema_checkpoint_save(const char *path, const lema_ckpt_tensor *t, int32_t n,
+                                 int64_t step, void *stream);
+
+/* Reads the n named tensors of the safetensors file `path` into their device
+ * buffers and its step into *step (-1 when the metadata holds no integer
+ * step; step may be NULL).  Every requested tensor must be in the file with the same dtype
+ * and element count; other tensors of the file are ignored, so files from
+ * other writers load as long as they hold the requested names.  The whole
+ * header is parsed and checked, and every request matched, before any
+ * device memory is written.
+ * Errors: as for lema_checkpoint_save, and LEMA_ERR_NOT_FOUND (a requested
+ * name is not in the file), LEMA_ERR_DTYPE or LEMA_ERR_SIZE (it is, with
+ * another dtype or element count), LEMA_ERR_IO (the file cannot be read, is
+ * shorter than its header says, or its header is not valid safetensors
+ * JSON).  Only a read or HIP error after all checks have passed can leave
+ * the device buffers partly written. */
+lema_status lema_checkpoint_load(const char *path, const lema_ckpt_tensor *t, int32_t n,
+                                 int64_t *step, void *stream);
 
 #ifdef __cplusplus
 }

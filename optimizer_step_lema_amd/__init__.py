@@ -8,7 +8,7 @@ raises ImportError if it has not been built: no step has a non-HIP fallback.
 from ._native import LemaError, load  # noqa: F401
 from .api import (AccumPlan, AccumQ8Plan, AccumQ8Segment, AccumSegment, AdamwPlan,  # noqa: F401
                   AdamwQ8Plan, AdamwQ8Segment, AdamwSegment, FlatState, MergeSegment, Q8,
-                  SlotPool, adamw_constants, adamw_step, adamw_step_q8, dequantize_rows,
-                  device_info, flat_adamw_state, flat_q8_state,
-                  grad_accum, grad_accum_q8, measure_copy, merge_delta, pinned_empty, probe_fp32,
-                  quantize_rows, table_cache_stats)
+                  SlotPool, adamw_constants, adamw_step, adamw_step_q8, checkpoint_tensors,
+                  dequantize_rows, device_info, flat_adamw_state, flat_q8_state,
+                  grad_accum, grad_accum_q8, load_checkpoint, measure_copy, merge_delta,
+                  pinned_empty, probe_fp32, quantize_rows, save_checkpoint, table_cache_stats)

@@ -22,6 +22,12 @@ LEMA_ERR_NOT_PINNED = -6
 LEMA_ERR_HIP = -7
 LEMA_ERR_ALIGN = -8
 LEMA_ERR_CAPTURE = -9
+LEMA_ERR_IO = -10
+LEMA_ERR_NOT_FOUND = -11
+
+LEMA_DT_F32 = 0
+LEMA_DT_BF16 = 1
+LEMA_DT_I8 = 2
 
 LEMA_GRAD_BF16 = 0
 LEMA_GRAD_FP32 = 1
@@ -85,6 +91,11 @@ class LayerQ8(ctypes.Structure):
     _fields_ = [("host_segs", ctypes.POINTER(AdamwQ8Seg)), ("nseg", i32)]
 
 
+class CkptTensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("dtype", i32), ("reserved", i32), ("data", vp),
+                ("numel", i64)]
+
+
 class StreamStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_double) for n in (
         "h2d_bytes", "d2h_bytes", "h2d_ms", "d2h_ms", "kernel_ms",
@@ -121,6 +132,9 @@ SIGNATURES = [
                                   i32, i32, i32, ctypes.POINTER(StreamStats)]),
     ("lema_host_alloc", i32, [ctypes.POINTER(vp), ctypes.c_size_t]),
     ("lema_host_free", i32, [vp]),
+    ("lema_checkpoint_save", i32, [ctypes.c_char_p, ctypes.POINTER(CkptTensor), i32, i64, vp]),
+    ("lema_checkpoint_load", i32, [ctypes.c_char_p, ctypes.POINTER(CkptTensor), i32,
+                                   ctypes.POINTER(i64), vp]),
     ("lema_measure_copy", i32, [vp, vp, ctypes.c_size_t, vp]),
     ("lema_probe_fp32", i32, [vp, vp, vp, vp, vp, i64, vp]),
     ("lema_device_info", i32, [ctypes.POINTER(i32), ctypes.POINTER(i32)]),

@@ -11,13 +11,16 @@ bf16 gradient (or an fp32 accumulator), bf16 weight write-back and an
 optional fp32 delta; fp32 accumulation of bf16 micro-batch gradients;
 streaming of host-resident state through a pool of HBM slots.  README
 "Quantization": the same step with int8 moments and int8 accumulators kept
-as codes with per-row scales.
+as codes with per-row scales.  README "Features" and "Selective Full
+Fine-Tuning": checkpoints of the delta and the optimizer state as
+safetensors files.
 """
 from __future__ import annotations
 
 import ctypes
+import os
 from dataclasses import dataclass
-from typing import Optional, Sequence
+from typing import Mapping, Optional, Sequence
 
 import numpy as np
 import torch
@@ -712,3 +715,67 @@ def device_info() -> dict:
     return {"compute_units": cus.value, "tile_elements": tile.value,
             "lds_per_cu": lds.value, "step_lds_reserved": res.value,
             "step_lds_reserved_8_microbatches": res_mb.value}
+
+
+# ------------------------------------------------------------ checkpoints
+
+_CKPT_DTYPES = {torch.float32: N.LEMA_DT_F32, torch.bfloat16: N.LEMA_DT_BF16,
+                torch.int8: N.LEMA_DT_I8}
+
+
+def _ckpt_array(tensors: Mapping[str, torch.Tensor]):
+    arr = (N.CkptTensor * len(tensors))()
+    names = []
+    for k, (name, t) in enumerate(tensors.items()):
+        if t.dtype not in _CKPT_DTYPES:
+            raise TypeError(f"{name}: checkpoints hold float32, bfloat16 or int8, not {t.dtype}")
+        ptr = _check(t, t.dtype, t.numel(), name)
+        b = name.encode("ascii")
+        names.append(b)
+        arr[k] = N.CkptTensor(b, _CKPT_DTYPES[t.dtype], 0, ptr, t.numel())
+    return arr, names
+
+
+def save_checkpoint(path, tensors: Mapping[str, torch.Tensor], *, step: int, stream=None) -> None:
+    """Write the named device tensors and the step to a safetensors file
+    (lema_checkpoint_save: written under path + ".tmp", then renamed).
+    Returns once the file is complete."""
+    arr, _names = _ckpt_array(tensors)
+    N.check(N.load().lema_checkpoint_save(os.fsencode(path), arr, len(arr), int(step),
+                                          _stream_handle(stream)), "lema_checkpoint_save")
+
+
+def load_checkpoint(path, tensors: Mapping[str, torch.Tensor], *, stream=None) -> int:
+    """Fill the named device tensors from a safetensors file (each must be
+    there with the same dtype and element count) and return its step (-1 if
+    it records none).  Returns once the data is in device memory."""
+    arr, _names = _ckpt_array(tensors)
+    step = ctypes.c_int64(-1)
+    N.check(N.load().lema_checkpoint_load(os.fsencode(path), arr, len(arr), ctypes.byref(step),
+                                          _stream_handle(stream)), "lema_checkpoint_load")
+    return step.value
+
+
+def checkpoint_tensors(segments, *, prefix: str = "", state: bool = True,
+                       delta: bool = False) -> dict:
+    """Name -> tensor map of a segment list's checkpoint: with `state`, each
+    segment's fp32 master and its moments (fp32 tensors, or int8 codes and
+    row scales: "exp_avg.codes", "exp_avg.scale"), with `delta` its delta.
+    Segment i's names start with f"{prefix}{i}."."""
+    out = {}
+    for i, s in enumerate(segments):
+        p = f"{prefix}{i}."
+        if state:
+            out[p + "master"] = s.master
+            for name in ("exp_avg", "exp_avg_sq"):
+                m = getattr(s, name)
+                if isinstance(m, Q8):
+                    out[p + name + ".codes"] = m.codes
+                    out[p + name + ".scale"] = m.scale
+                else:
+                    out[p + name] = m
+        if delta:
+            if s.delta is None:
+                raise ValueError(f"segment {i} has no delta")
+            out[p + "delta"] = s.delta
+    return out

@@ -481,6 +481,8 @@ const char *lema_status_string(lema_status s) {
     case LEMA_ERR_HIP: return "LEMA_ERR_HIP: HIP runtime error (see lema_last_hip_error)";
     case LEMA_ERR_ALIGN: return "LEMA_ERR_ALIGN: pointer not aligned to its element size";
     case LEMA_ERR_CAPTURE: return "LEMA_ERR_CAPTURE: the stream is capturing a HIP graph";
+    case LEMA_ERR_IO: return "LEMA_ERR_IO: checkpoint file unreadable, unwritable or malformed";
+    case LEMA_ERR_NOT_FOUND: return "LEMA_ERR_NOT_FOUND: tensor not in the checkpoint file";
     default: return "unknown lema_status";
     }
 }

@@ -44,7 +44,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for code in range(-9, 1):
+    for code in range(-11, 1):
         assert lib.lema_status_string(code).startswith(b"LEMA_")
     assert b"unknown" in lib.lema_status_string(-99)
     assert lib.lema_version() >= 100
