@@ -38,18 +38,21 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "AdamW params updated/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 COUNTERS = os.path.join(ROOT, "profiles", "adamw_counters.json")
+# the traffic counters stand for the kernels built from these sources with
+# the build's compiler flags (optimizer_step_lema_amd.build.COMMON)
 KERNEL_SOURCES = ["optimizer_step_lema_amd/csrc/lema_kernels.hip",
                   "optimizer_step_lema_amd/csrc/lema_q8.hip",
                   "optimizer_step_lema_amd/csrc/lema_device.h",
-                  "optimizer_step_lema_amd/csrc/lema_internal.h",
-                  "optimizer_step_lema_amd/build.py"]
+                  "optimizer_step_lema_amd/csrc/lema_internal.h"]
 
 
 def kernel_digest() -> str:
+    from optimizer_step_lema_amd import build
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(build.COMMON).encode())
     return h.hexdigest()
 
 
