@@ -39,7 +39,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "AdamW params updated/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 COUNTERS = os.path.join(ROOT, "profiles", "adamw_counters.json")
 # the traffic counters stand for the kernels built from these sources with
-# the build's compiler flags (optimizer_step_lema_amd.build.COMMON)
+# the build's compiler flags (optimizer_step_lema_amd.build.FLAGS)
 KERNEL_SOURCES = ["optimizer_step_lema_amd/csrc/lema_kernels.hip",
                   "optimizer_step_lema_amd/csrc/lema_q8.hip",
                   "optimizer_step_lema_amd/csrc/lema_device.h",
@@ -52,7 +52,7 @@ def kernel_digest() -> str:
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    h.update(" ".join(build.COMMON).encode())
+    h.update(" ".join(build.FLAGS).encode())
     return h.hexdigest()
 
 

@@ -32,13 +32,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build liblema.so)")
 
 
-COMMON = [
+# compiler flags of every source (the include directories are added below)
+FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
-    "-I" + INCLUDE, "-I" + CSRC,
 ]
+COMMON = FLAGS + ["-I" + INCLUDE, "-I" + CSRC]
 
 
 def _compile(src: str, verbose: bool) -> str:
