@@ -520,9 +520,11 @@ typedef struct {
 } lema_ckpt_tensor;
 
 /* Writes the n tensors and the step t to `path`.  The file is written under
- * `path` + ".tmp", flushed to storage and then renamed over `path`, so a save
- * that fails (or is interrupted) leaves an earlier file at `path` intact and
- * removes its temporary file.
+ * a temporary name of its own in the same directory (`path` + ".tmp." and a
+ * unique suffix), flushed to storage and then renamed over `path`, so a save
+ * that fails leaves an earlier file at `path` intact and removes its
+ * temporary file, and concurrent saves to one path each leave a whole file
+ * (the last rename wins).
  * Errors: LEMA_ERR_NULL (path, t with n > 0, a name, or data with numel > 0),
  * LEMA_ERR_SIZE (n < 0, numel < 0, a bad or repeated name, reserved != 0),
  * LEMA_ERR_DTYPE, LEMA_ERR_CAPTURE, LEMA_ERR_IO, LEMA_ERR_HIP. */

@@ -738,8 +738,8 @@ def _ckpt_array(tensors: Mapping[str, torch.Tensor]):
 
 def save_checkpoint(path, tensors: Mapping[str, torch.Tensor], *, step: int, stream=None) -> None:
     """Write the named device tensors and the step to a safetensors file
-    (lema_checkpoint_save: written under path + ".tmp", then renamed).
-    Returns once the file is complete."""
+    (lema_checkpoint_save: written under a temporary name next to `path`,
+    flushed, then renamed over it).  Returns once the file is complete."""
     arr, _names = _ckpt_array(tensors)
     N.check(N.load().lema_checkpoint_save(os.fsencode(path), arr, len(arr), int(step),
                                           _stream_handle(stream)), "lema_checkpoint_save")

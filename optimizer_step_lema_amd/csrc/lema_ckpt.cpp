@@ -470,13 +470,14 @@ lema_status lema_checkpoint_save(const char *path, const lema_ckpt_tensor *t, in
         if ((e = stg.init(size_t(off))) != hipSuccess) return hip_failed(e);
     }
 
+    // a temporary file of its own next to `path` (concurrent saves to one
+    // path do not share it), renamed over `path` once complete
     TmpFile tmp;
-    tmp.path = std::string(path) + ".tmp";
-    tmp.fd = ::open(tmp.path.c_str(), O_WRONLY | O_CREAT | O_TRUNC | O_CLOEXEC, 0644);
-    if (tmp.fd < 0) {
-        tmp.path.clear();      // not ours to remove
-        return LEMA_ERR_IO;
-    }
+    std::string name = std::string(path) + ".tmp.XXXXXX";
+    tmp.fd = ::mkostemp(&name[0], O_CLOEXEC);
+    if (tmp.fd < 0) return LEMA_ERR_IO;
+    tmp.path = name;
+    if (::fchmod(tmp.fd, 0644) != 0) return LEMA_ERR_IO;
     unsigned char len[8];
     for (int k = 0; k < 8; ++k) len[k] = static_cast<unsigned char>(uint64_t(h.size()) >> (8 * k));
     if (!write_all(tmp.fd, reinterpret_cast<const char *>(len), 8) ||

@@ -214,3 +214,31 @@ def test_delta_checkpoint_feeds_merge_delta(L, tmp_path):
         assert same(m1, m2)
         ref = oracle.merge_delta(to_np(s.orig), to_np(d))
         assert np.array_equal(to_np(m1), ref)
+
+
+def test_concurrent_saves_to_one_path(L, tmp_path):
+    """Four threads save different contents to one path at once: each writes
+    its own temporary file, the last rename wins, the file is whole (its
+    data matches its own step) and no temporary file is left."""
+    import threading
+    p = str(tmp_path / "c.safetensors")
+    xs = [torch.full((1 << 22,), float(k), device=DEV) for k in range(4)]
+    torch.cuda.synchronize()
+    errs = []
+
+    def run(k):
+        try:
+            L.save_checkpoint(p, {"x": xs[k]}, step=k)
+        except Exception as e:          # reported below
+            errs.append(e)
+
+    threads = [threading.Thread(target=run, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errs
+    assert sorted(os.listdir(tmp_path)) == ["c.safetensors"]
+    y = torch.empty(1 << 22, device=DEV)
+    step = L.load_checkpoint(p, {"x": y})
+    assert 0 <= step < 4 and bool(torch.all(y == float(step)))
