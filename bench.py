@@ -318,7 +318,8 @@ def resident_bench(torch, L, synth, a):
                                 "algorithmic_bytes_per_step": P * accum_bytes}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(sets[0][0], w, hp, delta, a.cpu_seconds,
-                                            sets[0][1][0][1] if resident_mb else None)
+                                            sets[0][1][0][1] if resident_mb else None,
+                                            bytes_per_param=step_bytes + accum_bytes)
     return line
 
 
@@ -370,10 +371,11 @@ def resident_state(torch, L, synth, w, layout, delta, grad_f32, resident_mb):
     return segs, accs, None
 
 
-def cpu_baseline(segs, w, hp, delta, seconds, microbatches=None):
+def cpu_baseline(segs, w, hp, delta, seconds, microbatches=None, bytes_per_param=None):
     """Time the oracle (as it stands) on the first tensor of the workload;
     with `microbatches` (its resident bf16 gradients) each timed step is the
-    oracle's accumulation of them followed by the step."""
+    oracle's accumulation of them followed by the step.  `bytes_per_param`,
+    the GPU line's algorithmic bytes, turns params/s into GB/s."""
     import numpy as np
     import oracle
     import torch
@@ -409,13 +411,16 @@ def cpu_baseline(segs, w, hp, delta, seconds, microbatches=None):
         reps1, el1 = timed_loop(one_step, seconds / 4)
     finally:
         oracle.set_num_threads(cores)
-    return {"value": n * reps / el, "unit": "params/s", "cores": cores,
+    rate, rate1 = n * reps / el, n * reps1 / el1
+    gbps = (lambda r: r * bytes_per_param / 1e9) if bytes_per_param else (lambda r: None)
+    return {"value": rate, "unit": "params/s", "cores": cores, "gbps": gbps(rate),
             "kind": "oracle", "host": host_info(),
             "sample": f"{w.segments[0][0]} ({n} params), {reps} oracle steps in {el:.1f} s, "
                       f"delta {'on' if delta else 'off'}"
                       + (f", each with {len(microbatches)} accumulations" if microbatches else "")
                       + "; C oracle, OpenMP",
-            "single_thread": {"value": n * reps1 / el1, "unit": "params/s", "cores": 1,
+            "single_thread": {"value": rate1, "unit": "params/s", "cores": 1,
+                              "gbps": gbps(rate1),
                               "sample": f"the same step, {reps1} times in {el1:.1f} s"}}
 
 
@@ -582,7 +587,7 @@ def q8_bench(torch, L, synth, a):
                                 "algorithmic_bytes_per_step": accum_bytes}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = q8_cpu_baseline(sets[0][0][0], w, row_lens[0], hp, delta,
-                                               a.cpu_seconds)
+                                               a.cpu_seconds, step_bytes / P)
     return line
 
 
@@ -633,9 +638,9 @@ def q8_state(torch, L, synth, w, row_lens, layout, delta):
     return segs, accs, None
 
 
-def q8_cpu_baseline(seg, w, row_len, hp, delta, seconds):
+def q8_cpu_baseline(seg, w, row_len, hp, delta, seconds, bytes_per_param):
     """The oracle's int8 step (dequantize, fp32 step, quantize) on the first
-    tensor of the workload."""
+    tensor of the workload; GB/s with the GPU line's algorithmic bytes."""
     import oracle
     import torch
 
@@ -657,6 +662,7 @@ def q8_cpu_baseline(seg, w, row_len, hp, delta, seconds):
     reps, el = timed_loop(lambda: oracle.adamw_step_q8(master, m, v, grad, c, row_len, orig=orig),
                           seconds)
     return {"value": n * reps / el, "unit": "params/s", "cores": oracle.num_threads(),
+            "gbps": n * reps / el * bytes_per_param / 1e9,
             "kind": "oracle", "host": host_info(),
             "sample": f"{w.segments[0][0]} ({n} params, rows of {row_len}), {reps} oracle "
                       f"int8 steps in {el:.1f} s, delta {'on' if delta else 'off'}; C oracle, "
