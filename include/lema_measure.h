@@ -41,6 +41,16 @@ lema_status lema_probe_fp32(const float *a, const float *b, float *quot, float *
                             uint16_t *bf16, int64_t n, void *stream);
 
 /*
+ * r[i] = the reciprocal the int8 kernels take of a row scale s[i] (one Newton
+ * step from v_rcp_f32, compiled exactly as in the kernels), for n elements.
+ * Their division-free quantization (lema_q8.hip, QuantRow) is exact as long
+ * as |r*s - 1| <= 2^-23 for every normal scale, which a test checks over
+ * all of them.  Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_ALIGN,
+ * LEMA_ERR_HIP.
+ */
+lema_status lema_probe_q8_reciprocal(const float *s, float *r, int64_t n, void *stream);
+
+/*
  * Counters of the current device's launch-table cache since the library was
  * loaded: out[0] calls that found their table cached, out[1] tables uploaded,
  * out[2] uploads that had to wait for a pending launch, out[3] cached

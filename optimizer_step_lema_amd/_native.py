@@ -137,6 +137,7 @@ SIGNATURES = [
                                    ctypes.POINTER(i64), vp]),
     ("lema_measure_copy", i32, [vp, vp, ctypes.c_size_t, vp]),
     ("lema_probe_fp32", i32, [vp, vp, vp, vp, vp, i64, vp]),
+    ("lema_probe_q8_reciprocal", i32, [vp, vp, i64, vp]),
     ("lema_device_info", i32, [ctypes.POINTER(i32), ctypes.POINTER(i32)]),
     ("lema_step_lds_reservation", i32, [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
     ("lema_table_cache_stats", i32, [ctypes.POINTER(i64)]),

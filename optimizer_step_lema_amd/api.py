@@ -696,6 +696,16 @@ def probe_fp32(a: torch.Tensor, b: torch.Tensor, stream=None):
     return q, r, h
 
 
+def probe_q8_reciprocal(s: torch.Tensor, stream=None) -> torch.Tensor:
+    """The reciprocal the int8 kernels take of each row scale in `s`."""
+    n = s.numel()
+    _check(s, torch.float32, n, "s")
+    r = torch.empty_like(s)
+    N.check(N.load().lema_probe_q8_reciprocal(s.data_ptr(), r.data_ptr(), n,
+                                              _stream_handle(stream)), "lema_probe_q8_reciprocal")
+    return r
+
+
 def table_cache_stats() -> dict:
     """Launch-table cache counters of the current device (since load)."""
     out = (ctypes.c_int64 * 4)()

@@ -155,5 +155,6 @@ hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t str
 hipError_t launch_fp32_probe(const float *a, const float *b, float *quot,
                              float *root, uint16_t *bf16, int64_t n,
                              hipStream_t stream);
+hipError_t launch_q8_recip_probe(const float *s, float *r, int64_t n, hipStream_t stream);
 
 }  // namespace lema

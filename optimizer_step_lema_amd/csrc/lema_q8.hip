@@ -105,15 +105,21 @@ struct QuantRow {
     bool fast;    // s is normal: x*r decides away from half-integers
 };
 
+// The reciprocal of a normal scale s (see above).
+__device__ __forceinline__ float row_reciprocal(float s) {
+    const float r0 = __builtin_amdgcn_rcpf(s);
+    const float e = __builtin_fmaf(-s, r0, 1.0f);
+    return __builtin_fmaf(e, r0, r0);
+}
+
 __device__ __forceinline__ QuantRow quant_row(uint32_t absmax_bits) {
 #pragma clang fp contract(off)
     QuantRow q;
     q.s = scale_of(absmax_bits);
     q.ok = q.s > 0.0f && mag_bits(q.s) < 0x7F800000u;
     q.fast = q.ok && mag_bits(q.s) >= 0x00800000u;
-    const float r0 = __builtin_amdgcn_rcpf(q.s);
-    const float e = __builtin_fmaf(-q.s, r0, 1.0f);
-    q.r = q.fast ? __builtin_fmaf(e, r0, r0) : 0.0f;
+    const float r = row_reciprocal(q.s);
+    q.r = q.fast ? r : 0.0f;
     return q;
 }
 
@@ -1065,6 +1071,15 @@ __global__ __launch_bounds__(kThreads) void code_rows_kernel(const void *table, 
     block_of_table<Q8Rec>(table, nseg, block0, CodeRows<kOp, kThreads, kRows>{});
 }
 
+// row_reciprocal over n scales (a measurement aid: its error bound is what
+// the division-free quantization relies on).  Grid-stride over n.
+__global__ __launch_bounds__(256) void q8_recip_probe_kernel(const float *__restrict__ s,
+                                                             float *__restrict__ r, int64_t n) {
+    for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n;
+         i += int64_t(gridDim.x) * 256)
+        r[i] = row_reciprocal(s[i]);
+}
+
 // `lds` bytes of dynamic LDS are reserved per workgroup (none of these
 // kernels reads them): a cap on how many workgroups share a CU.
 template <class... Args>
@@ -1169,6 +1184,13 @@ hipError_t launch_quantize_q8(const void *table, int nseg, uint32_t total_blocks
     const void *fn = dequantize ? pick_rows<kDequantize>(block, rows)
                                 : pick_rows<kQuantize>(block, rows);
     return launch_split(fn, block, total_blocks, 0, stream, table, nseg);
+}
+
+hipError_t launch_q8_recip_probe(const float *s, float *r, int64_t n, hipStream_t stream) {
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536));
+    void *args[] = {&s, &r, &n};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&q8_recip_probe_kernel),
+                           dim3(unsigned(blocks)), dim3(256), args, 0, stream);
 }
 
 }  // namespace lema

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "lema.h"
+#include "lema_measure.h"
 #include "lema_host_internal.h"
 #include "lema_internal.h"
 
@@ -333,6 +334,15 @@ static lema_status convert_rows(const lema_q8_tensor *t, int32_t n, bool dequant
                                                      uint32_t blocks, int block, QRows rows) {
         return launch_quantize_q8(table, nrec, blocks, dequantize, block, rows, hs);
     });
+}
+
+lema_status lema_probe_q8_reciprocal(const float *s, float *r, int64_t n, void *stream) {
+    if (n < 0) return LEMA_ERR_SIZE;
+    if (n == 0) return LEMA_OK;
+    if (s == nullptr || r == nullptr) return LEMA_ERR_NULL;
+    if ((bits(s) | bits(r)) & 3) return LEMA_ERR_ALIGN;
+    const hipError_t e = launch_q8_recip_probe(s, r, n, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LEMA_OK : hip_failed(e);
 }
 
 lema_status lema_quantize_rows(const lema_q8_tensor *t, int32_t n, void *stream) {
