@@ -871,6 +871,22 @@ struct CodeRows {
     static constexpr bool kAccum = kOp == kAccumAdd || kOp == kAccumOverwrite;
     static constexpr bool kReadsCodes = kOp == kAccumAdd || kOp == kDequantize;
 
+    // The new accumulator values of one chunk: f32(g) on overwrite, else the
+    // dequantized old value plus f32(g) (one binary32 addition each).
+    __device__ __forceinline__ static f32x4 accumulated(uint32_t codes, u32x2 grad, float s_old) {
+        const f32x4 g = widen_bf16(grad);
+        if constexpr (kOp == kAccumOverwrite) return g;
+        f32x4 x;
+        for (int k = 0; k < 4; ++k) x[k] = accum_elem(dequant(code_at(codes, k), s_old), g[k], false);
+        return x;
+    }
+
+    __device__ __forceinline__ static f32x4 dequantized(uint32_t codes, float s) {
+        f32x4 d;
+        for (int k = 0; k < 4; ++k) d[k] = dequant(code_at(codes, k), s);
+        return d;
+    }
+
     // The lane's new values (and their absmax), or for kDequantize the stores.
     template <bool kFull>
     __device__ __forceinline__ void values_lane(const Team &t, uint64_t codes, uint64_t src,
@@ -893,18 +909,10 @@ struct CodeRows {
         for (int ci = 0; ci < kC; ++ci) {
             const int64_t valid = valid_of<kFull>(t, ci);
             if (valid <= 0) continue;
-            if constexpr (kAccum) {
-                const f32x4 g = widen_bf16(gb[ci]);
-                for (int k = 0; k < 4; ++k)
-                    x[ci][k] = kOp == kAccumAdd
-                                   ? accum_elem(dequant(code_at(cw[ci], k), s_old), g[k], false)
-                                   : g[k];
-            }
+            if constexpr (kAccum) x[ci] = accumulated(cw[ci], gb[ci], s_old);
             if constexpr (kOp == kDequantize) {
-                f32x4 d;
-                for (int k = 0; k < 4; ++k) d[k] = dequant(code_at(cw[ci], k), s_old);
                 const int64_t e = t.first + chunk_off(t, ci);
-                store_f32(src, e, kFull || (t.vec && valid == 4), valid, d);
+                store_f32(src, e, kFull || (t.vec && valid == 4), valid, dequantized(cw[ci], s_old));
             } else {
                 amax = absmax4(amax, x[ci], valid);
             }
@@ -941,17 +949,9 @@ struct CodeRows {
             amax[c] = 0;
             const int64_t valid = k[c].valid;
             if (valid <= 0) continue;
-            if constexpr (kAccum) {
-                const f32x4 g = widen_bf16(gb[c]);
-                for (int i = 0; i < 4; ++i)
-                    x[c][i] = kOp == kAccumAdd
-                                  ? accum_elem(dequant(code_at(cw[c], i), s_old[c]), g[i], false)
-                                  : g[i];
-            }
+            if constexpr (kAccum) x[c] = accumulated(cw[c], gb[c], s_old[c]);
             if constexpr (kOp == kDequantize) {
-                f32x4 d;
-                for (int i = 0; i < 4; ++i) d[i] = dequant(code_at(cw[c], i), s_old[c]);
-                store_f32(src, k[c].e, valid == 4, valid, d);
+                store_f32(src, k[c].e, valid == 4, valid, dequantized(cw[c], s_old[c]));
             } else {
                 amax[c] = absmax4(0u, x[c], valid);
             }
@@ -997,17 +997,9 @@ struct CodeRows {
         for (int ci = 0; ci < kC; ++ci) {
             if (ci >= wr.chunks) continue;
             const uint32_t v = uint32_t(ci * wr.width + wr.lane);
-            if constexpr (kAccum) {
-                const f32x4 g = widen_bf16(gb[ci]);
-                for (int k = 0; k < 4; ++k)
-                    x[ci][k] = kOp == kAccumAdd
-                                   ? accum_elem(dequant(code_at(cw[ci], k), s_old), g[k], false)
-                                   : g[k];
-            }
+            if constexpr (kAccum) x[ci] = accumulated(cw[ci], gb[ci], s_old);
             if constexpr (kOp == kDequantize) {
-                f32x4 d;
-                for (int k = 0; k < 4; ++k) d[k] = dequant(code_at(cw[ci], k), s_old);
-                row_st_f32(rs, v, d);
+                row_st_f32(rs, v, dequantized(cw[ci], s_old));
             } else if (int32_t(v) < wr.nvec) {
                 amax[0] = absmax4(amax[0], x[ci], 4);
             }
