@@ -518,13 +518,17 @@ __device__ __forceinline__ void wave_team_max(uint32_t (&a)[kN], int width) {
     }
 }
 
-// Codes of a lane's first `chunks` chunks against its row's quantization.
+// Codes of a lane's first `chunks` chunks against its row's quantization
+// (the words past `chunks` are left unset: no caller reads them).
 template <int kC>
 __device__ __forceinline__ void quant_lane(const QuantRow &q, const f32x4 (&x)[kC], int chunks,
                                            uint32_t (&w)[kC]) {
+    if (!q.ok) {
 #pragma unroll
-    for (int c = 0; c < kC; ++c) w[c] = 0;
-    if (!q.ok) return;
+        for (int c = 0; c < kC; ++c)
+            if (c < chunks) w[c] = 0;
+        return;
+    }
     float dmax = 0.0f;
     if (q.fast) {
 #pragma unroll
@@ -980,12 +984,12 @@ struct CodeRows {
         float s_old = 0.0f;
         if (kReadsCodes && wr.len > 0) s_old = as_global<gfloat>(scale)[wr.row];
 
+        // chunks past wr.chunks are never read: no initialization for them
         uint32_t cw[kC];
         u32x2 gb[kC];
         f32x4 x[kC];
 #pragma unroll
         for (int ci = 0; ci < kC; ++ci) {
-            x[ci] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             if (ci >= wr.chunks) continue;
             const uint32_t v = uint32_t(ci * wr.width + wr.lane);
             if constexpr (kReadsCodes) cw[ci] = row_ld_codes(rc, v);
