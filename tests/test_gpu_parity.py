@@ -471,6 +471,7 @@ def test_flat_state_resident_microbatches(L):
         compare_f32(to_np(seg.delta), ref["delta"], f"flat mb seg{i}.delta")
 
 
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")   # the refusal leaves it empty
 def test_rejects_graph_capture(L):
     """A stream capturing a HIP graph is refused before anything is enqueued:
     the launch tables live in a cache a captured graph would outlive."""
