@@ -489,7 +489,7 @@ const char *lema_status_string(lema_status s) {
 
 int32_t lema_last_hip_error(void) { return t_last_hip_error; }
 
-int32_t lema_version(void) { return 100; }
+int32_t lema_version(void) { return 200; }   // 0.2.0: checkpoint files, reciprocal probe
 
 lema_status lema_adamw_constants(const lema_adamw_args *args, lema_adamw_consts *out) {
     if (args == nullptr || out == nullptr) return LEMA_ERR_NULL;
