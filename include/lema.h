@@ -502,10 +502,12 @@ lema_status lema_host_free(void *p);
  * and v (or their int8 codes and row scales) for a bit-exact resume, the
  * delta for merge_delta.
  *
- * Both calls are synchronous: they copy between device memory and the file
- * through page-locked staging buffers on `stream` (device copies overlap the
+ * Both calls are synchronous: they copy between the tensors and the file
+ * through page-locked staging buffers on `stream` (the copies overlap the
  * file reads and writes) and return once the data has arrived, having
- * synchronized `stream`.  They refuse a capturing stream (LEMA_ERR_CAPTURE).
+ * synchronized `stream`.  Tensors may be in device memory or in host memory,
+ * so the host-resident state of a streamed run is checkpointed in place.
+ * They refuse a capturing stream (LEMA_ERR_CAPTURE).
  */
 typedef enum { LEMA_DT_F32 = 0, LEMA_DT_BF16 = 1, LEMA_DT_I8 = 2 } lema_dtype;
 
@@ -514,8 +516,9 @@ typedef struct {
                           /* double quote and the backslash; unique in a call  */
     int32_t     dtype;    /* lema_dtype                                         */
     int32_t     reserved; /* 0                                                  */
-    void       *data;     /* device memory: read by save, written by load;     */
-                          /* NULL only when numel == 0                          */
+    void       *data;     /* read by save, written by load: device memory, or  */
+                          /* host memory (page-locked or not: the state of a   */
+                          /* streamed run lives there); NULL only if numel == 0 */
     int64_t     numel;    /* >= 0                                               */
 } lema_ckpt_tensor;
 

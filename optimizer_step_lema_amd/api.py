@@ -739,7 +739,7 @@ def _ckpt_array(tensors: Mapping[str, torch.Tensor]):
     for k, (name, t) in enumerate(tensors.items()):
         if t.dtype not in _CKPT_DTYPES:
             raise TypeError(f"{name}: checkpoints hold float32, bfloat16 or int8, not {t.dtype}")
-        ptr = _check(t, t.dtype, t.numel(), name)
+        ptr = _check(t, t.dtype, t.numel(), name, "cuda" if t.is_cuda else "cpu")
         b = name.encode("ascii")
         names.append(b)
         arr[k] = N.CkptTensor(b, _CKPT_DTYPES[t.dtype], 0, ptr, t.numel())
@@ -747,7 +747,7 @@ def _ckpt_array(tensors: Mapping[str, torch.Tensor]):
 
 
 def save_checkpoint(path, tensors: Mapping[str, torch.Tensor], *, step: int, stream=None) -> None:
-    """Write the named device tensors and the step to a safetensors file
+    """Write the named tensors (GPU, or host-resident state) and the step to a safetensors file
     (lema_checkpoint_save: written under a temporary name next to `path`,
     flushed, then renamed over it).  Returns once the file is complete."""
     arr, _names = _ckpt_array(tensors)
@@ -756,7 +756,7 @@ def save_checkpoint(path, tensors: Mapping[str, torch.Tensor], *, step: int, str
 
 
 def load_checkpoint(path, tensors: Mapping[str, torch.Tensor], *, stream=None) -> int:
-    """Fill the named device tensors from a safetensors file (each must be
+    """Fill the named tensors (GPU or host) from a safetensors file (each must be
     there with the same dtype and element count) and return its step (-1 if
     it records none).  Returns once the data is in device memory."""
     arr, _names = _ckpt_array(tensors)

@@ -242,3 +242,25 @@ def test_concurrent_saves_to_one_path(L, tmp_path):
     y = torch.empty(1 << 22, device=DEV)
     step = L.load_checkpoint(p, {"x": y})
     assert 0 <= step < 4 and bool(torch.all(y == float(step)))
+
+
+def test_host_resident_state(L, tmp_path):
+    """The host-resident state of a streamed run (page-locked and ordinary
+    host tensors) is saved and loaded in place, mixed with device tensors in
+    one file."""
+    n = 3_000_017
+    pinned = L.pinned_empty(n, torch.float32)
+    pinned.copy_(torch.randn(n))
+    pageable = torch.randn(n // 3).to(torch.bfloat16)
+    codes = torch.randint(-127, 128, (12_345,), dtype=torch.int8)
+    dev = synth.normal(777, 1.0, 9, DEV)
+    p = str(tmp_path / "host.safetensors")
+    L.save_checkpoint(p, {"m": pinned, "g": pageable, "c": codes, "d": dev}, step=11)
+    back = load_file(p)
+    for k, v in (("m", pinned), ("g", pageable), ("c", codes), ("d", dev.cpu())):
+        assert same(back[k], v), k
+    out = {"m": L.pinned_empty(n, torch.float32), "g": torch.empty(n // 3, dtype=torch.bfloat16),
+           "c": torch.empty(12_345, dtype=torch.int8), "d": torch.empty(777, device=DEV)}
+    assert L.load_checkpoint(p, out) == 11
+    assert same(out["m"], pinned) and same(out["g"], pageable) and same(out["c"], codes)
+    assert same(out["d"], dev)
