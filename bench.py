@@ -711,7 +711,9 @@ def merge_bench(torch, L, synth, a):
         "hbm_gbps": gbps, "pct_hbm_peak": 100 * gbps / HBM_PEAK_GBPS,
         "copy_ceiling_gbps": copy_gbps,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": gbps / HBM_PEAK_GBPS, "traffic": None, "kernel": "merge_tile_kernel",
+                     "frac": gbps / HBM_PEAK_GBPS,
+                     "traffic": traffic_for(f"{a.workload}:merge", a.layout),
+                     "kernel": "merge_tile_kernel",
                      "algorithmic_bytes_per_launch": per, "avg_launch_ms": ms},
     }
 
