@@ -8,10 +8,16 @@ A step is one pass of the hot path over the whole workload on inputs already
 resident in HBM: for one micro-batch, one lema_adamw_step call (constants,
 segment walk, AdamW, bf16 write-back and, by default, the fp32 delta); for
 the one-layer workload, 8 lema_grad_accum calls then the step on the fp32
-accumulator.  The default workload is the Llama-2-7B q, k, v, o projections
-of the last 4 decoder layers (16 x [4096 x 4096], 268,435,456 parameters,
-bf16 gradient, t = 100), the selection the LEMA README's "Selective Full
-Fine-Tuning" section uses as its example.
+accumulator.  The default workload is the whole Llama-2-7B shape resident in
+HBM (291 tensors, 6,738,415,616 parameters, bf16 gradient, t = 10, delta on:
+229 GB of HBM traffic per step), the largest selection of the LEMA README's
+"Selective Full Fine-Tuning" section ("the entire model") that fits one GPU.
+`--workload llama7b_attn_last4` is its example selection (q, k, v, o of the
+last 4 layers, 268,435,456 parameters, t = 100).
+
+--fold-counters KEY FETCH_CSV WRITE_CSV folds two rocprofv3 --pmc passes
+(FETCH_SIZE, then WRITE_SIZE, of the same bench command) into the counter
+record bench.py reads for roofline.traffic; it needs no GPU.
 
 --slot-stream streams the whole Llama-2-7B shape from page-locked host
 memory through two HBM slots (README "TensorStore", "Features") and reports
@@ -38,18 +44,23 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, published
 METRIC = "AdamW params updated/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 COUNTERS = os.path.join(ROOT, "profiles", "adamw_counters.json")
-# the traffic counters stand for the kernels built from these sources with
-# the build's compiler flags (optimizer_step_lema_amd.build.FLAGS)
-KERNEL_SOURCES = ["optimizer_step_lema_amd/csrc/lema_kernels.hip",
-                  "optimizer_step_lema_amd/csrc/lema_q8.hip",
-                  "optimizer_step_lema_amd/csrc/lema_device.h",
-                  "optimizer_step_lema_amd/csrc/lema_internal.h"]
+# the traffic counters of a kernel stand for it as built from these sources
+# with the build's compiler flags (optimizer_step_lema_amd.build.FLAGS)
+_CSRC = "optimizer_step_lema_amd/csrc/"
+KERNEL_SOURCES = {
+    "adamw_tile_kernel": [_CSRC + "lema_kernels.hip", _CSRC + "lema_device.h",
+                          _CSRC + "lema_internal.h"],
+    "merge_tile_kernel": [_CSRC + "lema_kernels.hip", _CSRC + "lema_device.h",
+                          _CSRC + "lema_internal.h"],
+    "adamw_q8_kernel": [_CSRC + "lema_q8.hip", _CSRC + "lema_device.h",
+                        _CSRC + "lema_internal.h"],
+}
 
 
-def kernel_digest() -> str:
+def kernel_digest(kernel: str) -> str:
     from optimizer_step_lema_amd import build
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     h.update(" ".join(build.FLAGS).encode())
@@ -72,7 +83,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="llama7b_attn_last4")
+    ap.add_argument("--workload", default="llama7b_full")
     ap.add_argument("--no-delta", action="store_true", help="time the step without the delta")
     ap.add_argument("--fused-last", action="store_true",
                     help="multi-micro-batch workloads: fold the last micro-batch into the step "
@@ -108,7 +119,16 @@ def parse():
                          "through the pool's page-locked staging buffers")
     ap.add_argument("--host-threads", type=int, default=0,
                     help="with --staged: host copy threads (0 = library default)")
+    ap.add_argument("--fold-counters", nargs=3, metavar=("KEY", "FETCH_CSV", "WRITE_CSV"),
+                    default=None,
+                    help="fold rocprofv3 FETCH_SIZE and WRITE_SIZE passes (counter_collection "
+                         "CSVs) into the counter record under KEY, e.g. llama7b_full:delta, "
+                         "llama7b_attn_last4:q8:delta or gpt2_cattn_first2:merge")
     return ap.parse_args()
+
+
+def progress(msg):
+    print(f"bench.py: {msg}", file=sys.stderr, flush=True)
 
 
 def timed_events(torch, stream, fn, n):
@@ -146,14 +166,98 @@ def traffic_for(key, layout):
         return None
     rec = json.load(open(COUNTERS))
     entry = rec.get("workloads", {}).get(key)
-    if entry and rec.get("kernel_digest") == kernel_digest() and \
+    if entry and entry.get("kernel_digest") == kernel_digest(entry["kernel"]) and \
             entry.get("layout", "per-tensor") == layout:
         return entry["traffic_bytes_per_launch"]
     return None
 
 
+def counter_key_bytes(key):
+    """(kernel name, algorithmic bytes per launch) of a counter-record key
+    "<workload>:delta", ":nodelta", ":q8:delta", ":q8:nodelta" or ":merge"."""
+    import synth
+    wl, *mode = key.split(":")
+    w = synth.WORKLOADS[wl]
+    if mode == ["merge"]:
+        return "merge_tile_kernel", 8 * w.params
+    if mode and mode[0] == "q8" and len(mode) == 2 and mode[1] in ("delta", "nodelta"):
+        return "adamw_q8_kernel", sum(
+            q8_step_bytes(n, -(-n // sh[-1]), "bf16", mode[1] == "delta")
+            for n, (_, sh) in zip(w.numels, w.segments))
+    if mode in (["delta"], ["nodelta"]) and w.microbatches == 1:
+        return "adamw_tile_kernel", w.params * adamw_bytes_per_param(False, mode[0] == "delta")
+    raise SystemExit(f"bench.py: --fold-counters: unknown key {key!r}")
+
+
+COPY_KIB = 2 * (1 << 30) / 1024          # lema_measure_copy in copy_ceiling: 2 GiB each way
+
+
+def fold_counters(key, fetch_csv, write_csv):
+    """Per-dispatch FETCH_SIZE and WRITE_SIZE (KiB, summed over the counter's
+    instances) of the key's kernel, each scaled by what the same counter read
+    for the copy kernel's known 2 GiB read + 2 GiB write in the same run, into
+    the record's entry for `key`, stamped with the digest of the kernel's
+    current sources (entries whose kernel has changed since are dropped)."""
+    import csv
+
+    def per_dispatch(path, kernel, counter):
+        vals = {}
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Kernel_Name"].strip('"') != kernel or row["Counter_Name"] != counter:
+                    continue
+                vals[row["Dispatch_Id"]] = vals.get(row["Dispatch_Id"], 0.0) + \
+                    float(row["Counter_Value"])
+        if not vals:
+            raise SystemExit(f"bench.py: no {counter} rows for {kernel} in {path}")
+        return sum(vals.values()) / len(vals), len(vals)
+
+    kernel, alg = counter_key_bytes(key)
+    layout = "flat"
+    fk, nd = per_dispatch(fetch_csv, kernel, "FETCH_SIZE")
+    wk, _ = per_dispatch(write_csv, kernel, "WRITE_SIZE")
+    cf, _ = per_dispatch(fetch_csv, "copy_kernel", "FETCH_SIZE")
+    cw, _ = per_dispatch(write_csv, "copy_kernel", "WRITE_SIZE")
+    ff, wf = cf / COPY_KIB, cw / COPY_KIB
+    read, written = fk * 1024 / ff, wk * 1024 / wf
+    rec = json.load(open(COUNTERS)) if os.path.exists(COUNTERS) else {}
+    # entries measured on kernels built from other sources no longer count
+    rec["workloads"] = {k: e for k, e in rec.get("workloads", {}).items()
+                        if e.get("kernel_digest") == kernel_digest(e["kernel"])}
+    rec.pop("kernel_digest", None)
+    rec["note"] = ("HBM bytes per dispatch from two rocprofv3 --pmc passes (FETCH_SIZE, then "
+                   "WRITE_SIZE, KiB per dispatch), each scaled by what the same counter reads "
+                   "for lema_measure_copy of 2 GiB read + 2 GiB write in the same run")
+    rec["commands"] = [
+        "rocprofv3 --pmc FETCH_SIZE -T -f csv -d <out>/pmc_fetch -o fetch -- python3 "
+        "<repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline --copy-gib 4 "
+        "[--workload W] [--no-delta | --q8 | --merge]",
+        "rocprofv3 --pmc WRITE_SIZE -T -f csv -d <out>/pmc_write -o write -- python3 "
+        "<repo>/bench.py --steps 5 --warmup 1 --no-cpu-baseline --copy-gib 4 "
+        "[--workload W] [--no-delta | --q8 | --merge]",
+        "python3 <repo>/bench.py --fold-counters KEY <out>/pmc_fetch/fetch_counter_collection.csv "
+        "<out>/pmc_write/write_counter_collection.csv"]
+    rec["kernel_sources"] = {k: v + ["compiler flags: optimizer_step_lema_amd.build.FLAGS"]
+                             for k, v in KERNEL_SOURCES.items()}
+    rec["workloads"][key] = {
+        "kernel": kernel, "kernel_digest": kernel_digest(kernel), "layout": layout, "dispatches": nd, "fetch_kib": fk, "write_kib": wk,
+        "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_factor": ff, "write_factor": wf,
+        "read_bytes": read, "written_bytes": written,
+        "traffic_bytes_per_launch": read + written,
+        "algorithmic_bytes_per_launch": alg,
+        "traffic_over_algorithmic": (read + written) / alg}
+    rec["workloads"] = dict(sorted(rec["workloads"].items()))
+    with open(COUNTERS, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps({key: rec["workloads"][key]}))
+
+
 def main():
     a = parse()
+    if a.fold_counters:
+        fold_counters(*a.fold_counters)
+        return
     if a.gpus != 1:
         print(f"bench.py: --gpus {a.gpus}: only one GPU is supported; the data-parallel "
               "(sharded) layout is measured on one rank's share instead "
@@ -203,11 +307,15 @@ def resident_bench(torch, L, synth, a):
     # state resident in HBM; small workloads get rotated copies so that the
     # working set exceeds the 256 MB last-level cache between launches
     nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
+    t_setup = time.perf_counter()
     sets = [resident_state(torch, L, synth, w, a.layout, delta, grad_f32, resident_mb)
             for _ in range(nsets)]
     torch.cuda.synchronize()
+    progress(f"{a.workload}: {nsets} state set(s) of {P} params resident "
+             f"({time.perf_counter() - t_setup:.1f} s)")
     stream = torch.cuda.current_stream()
     copy_gbps = copy_ceiling(torch, L, a.copy_gib)
+    progress(f"copy ceiling {copy_gbps:.0f} GB/s")
 
     accum_plans = [[L.AccumPlan([L.AccumSegment(acc, g[j]) for acc, g in accs])
                     for j in range(accum_launches)] for _, accs, _ in sets] if grad_f32 else []
@@ -258,6 +366,7 @@ def resident_bench(torch, L, synth, a):
     stop.record(stream)
     torch.cuda.synchronize()
     pipelined_ms = start.elapsed_time(stop) / a.steps
+    progress(f"timed {a.steps} steps: {ms:.4f} ms per step")
 
     gbps = per_step / (ms * 1e-3) / 1e9
     key = f"{a.workload}:{'delta' if delta else 'nodelta'}" + (":fused" if fused else "") + \
@@ -317,6 +426,7 @@ def resident_bench(torch, L, synth, a):
                                 "frac": acc_gbps / HBM_PEAK_GBPS,
                                 "algorithmic_bytes_per_step": P * accum_bytes}
     if not a.no_cpu_baseline:
+        progress("timing the oracle on the host")
         line["cpu_baseline"] = cpu_baseline(sets[0][0], w, hp, delta, a.cpu_seconds,
                                             sets[0][1][0][1] if resident_mb else None,
                                             bytes_per_param=step_bytes + accum_bytes)

@@ -18,9 +18,14 @@ constexpr int kBlock = 64;
 constexpr int kVec = 4;
 constexpr int kUnroll = 1;
 constexpr int64_t kTile = int64_t(kBlock) * kVec * kUnroll;   // 256 elements
-// One workgroup per tile; at most this many workgroups per launch (keeps the
-// grid's work-item count well inside 32 bits).
-constexpr uint32_t kMaxBlocksPerLaunch = 1u << 24;
+// A launch's grid holds at most 2^31 work-items (the dispatch packet counts
+// work-items in 32 bits); larger grids are split into consecutive launches.
+// For the 64-lane tile kernels that is 2^25 tiles (8.6 G elements), so a
+// step over a whole 7B-parameter model is one launch.
+constexpr uint32_t kMaxWorkItemsPerLaunch = 1u << 31;
+constexpr uint32_t max_blocks_per_launch(int lanes) {
+    return kMaxWorkItemsPerLaunch / uint32_t(lanes);
+}
 
 // One segment of the launch table: up to eight array pointers and the length.
 //   AdamW : p = {master, m, v, grad, weight_bf16, orig_bf16, delta, last_bf16}

@@ -359,7 +359,7 @@ __global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restr
 
 // Launches go through hipLaunchKernel, which returns the launch status
 // directly instead of through the thread's sticky last-error slot.  Grids
-// larger than kMaxBlocksPerLaunch are split into consecutive launches.
+// larger than max_blocks_per_launch are split into consecutive launches.
 hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradMode grad_mode,
                         bool with_delta, const AdamwConsts &c, hipStream_t stream, int nmb,
                         uint32_t lds_bytes) {
@@ -379,7 +379,7 @@ hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradM
 #undef LEMA_PICK
     AdamwConsts consts = c;
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
-        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
+        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, max_blocks_per_launch(kBlock));
         void *args[] = {&table, &nseg, &tile0, &consts};
         hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, lds_bytes, stream);
         if (e != hipSuccess) return e;
@@ -393,7 +393,7 @@ hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles, bool 
     const void *fn = overwrite ? reinterpret_cast<const void *>(&accum_tile_kernel<true>)
                                : reinterpret_cast<const void *>(&accum_tile_kernel<false>);
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
-        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
+        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, max_blocks_per_launch(kBlock));
         void *args[] = {&table, &nseg, &tile0};
         hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, 0, stream);
         if (e != hipSuccess) return e;
@@ -404,7 +404,7 @@ hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles, bool 
 
 hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream) {
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
-        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, kMaxBlocksPerLaunch);
+        const uint32_t n = std::min<uint32_t>(total_tiles - tile0, max_blocks_per_launch(kBlock));
         void *args[] = {&table, &nseg, &tile0};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&merge_tile_kernel), dim3(n),
                                        dim3(kBlock), args, 0, stream);
@@ -420,7 +420,7 @@ hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t str
     size_t n16 = bytes / 16;
     const size_t blocks = (n16 + kCopyBlock - 1) / kCopyBlock;
     for (size_t block0 = 0; block0 < blocks;) {
-        const size_t n = std::min<size_t>(blocks - block0, kMaxBlocksPerLaunch / 4);
+        const size_t n = std::min<size_t>(blocks - block0, max_blocks_per_launch(kCopyBlock));
         void *args[] = {&s, &d, &n16, &block0};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&copy_kernel),
                                        dim3(unsigned(n)), dim3(kCopyBlock), args, 0, stream);

@@ -1082,7 +1082,7 @@ template <class... Args>
 hipError_t launch_split(const void *fn, int block, uint32_t total_blocks, uint32_t lds,
                         hipStream_t stream, const void *table, int nseg, Args... extra) {
     for (uint32_t block0 = 0; block0 < total_blocks;) {
-        const uint32_t n = std::min<uint32_t>(total_blocks - block0, kMaxBlocksPerLaunch);
+        const uint32_t n = std::min<uint32_t>(total_blocks - block0, max_blocks_per_launch(block));
         void *args[] = {&table, &nseg, &block0, &extra...};
         hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(block), args, lds, stream);
         if (e != hipSuccess) return e;
