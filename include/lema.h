@@ -150,6 +150,27 @@ lema_status lema_adamw_step(const lema_adamw_seg *segs, int32_t nseg,
                             const lema_adamw_args *args, void *stream);
 
 /*
+ * lema_adamw_step for callers that cannot allocate memory: code that must
+ * not call hipMalloc (tight serving or training loops, harnesses that
+ * forbid allocation).  Same arguments, kernels and results as
+ * lema_adamw_step, but nothing is allocated on the device or the host: the
+ * launch table goes into a fixed array of device memory that each GPU holds
+ * from the library's first use there until the process ends (table bytes of
+ * LEMA_NOALLOC_MAX_SEGMENTS segments, about 84 KiB), written through kernel
+ * arguments on `stream` ahead of the step.
+ *   nseg : at most LEMA_NOALLOC_MAX_SEGMENTS (else LEMA_ERR_SIZE, nothing
+ *          enqueued)
+ * Every call on one GPU overwrites that GPU's array.  Calls on one stream
+ * are ordered; calls that overlap on one GPU from different streams race
+ * for the array (undefined results), so such callers serialize them.  A
+ * capturing stream is refused (LEMA_ERR_CAPTURE), as for the other calls.
+ * Errors: as lema_adamw_step.
+ */
+#define LEMA_NOALLOC_MAX_SEGMENTS 1024
+lema_status lema_adamw_step_noalloc(const lema_adamw_seg *segs, int32_t nseg,
+                                    const lema_adamw_args *args, void *stream);
+
+/*
  * The step on an fp32 accumulator with the last micro-batch folded in:
  * per element g = acc + f32(last), the same fp32 addition lema_grad_accum
  * performs, so the results are bit-identical to lema_grad_accum(last) followed

@@ -8,8 +8,8 @@ raises ImportError if it has not been built: no step has a non-HIP fallback.
 from ._native import LemaError, load  # noqa: F401
 from .api import (AccumPlan, AccumQ8Plan, AccumQ8Segment, AccumSegment, AdamwPlan,  # noqa: F401
                   AdamwQ8Plan, AdamwQ8Segment, AdamwSegment, FlatState, MergeSegment, Q8,
-                  SlotPool, adamw_constants, adamw_step, adamw_step_q8, checkpoint_tensors,
-                  dequantize_rows, device_info, flat_adamw_state, flat_q8_state,
+                  SlotPool, adamw_constants, adamw_step, adamw_step_noalloc, adamw_step_q8,
+                  checkpoint_tensors, dequantize_rows, device_info, flat_adamw_state, flat_q8_state,
                   grad_accum, grad_accum_q8, load_checkpoint, measure_copy, merge_delta,
                   pinned_empty, probe_fp32, probe_q8_reciprocal, quantize_rows, save_checkpoint,
                   table_cache_stats)

@@ -37,6 +37,7 @@ LEMA_STATE_FP32 = 0
 LEMA_STATE_Q8 = 1
 LEMA_Q8_MAX_ROW = 16384
 LEMA_MAX_MICROBATCHES = 16
+LEMA_NOALLOC_MAX_SEGMENTS = 1024
 
 vp = ctypes.c_void_p
 i32 = ctypes.c_int32
@@ -110,6 +111,8 @@ SIGNATURES = [
     ("lema_version", i32, []),
     ("lema_adamw_constants", i32, [ctypes.POINTER(AdamwArgs), ctypes.POINTER(AdamwConsts)]),
     ("lema_adamw_step", i32, [ctypes.POINTER(AdamwSeg), i32, ctypes.POINTER(AdamwArgs), vp]),
+    ("lema_adamw_step_noalloc", i32, [ctypes.POINTER(AdamwSeg), i32, ctypes.POINTER(AdamwArgs),
+                                      vp]),
     ("lema_adamw_step_accum", i32, [ctypes.POINTER(AdamwSeg), ctypes.POINTER(vp), i32,
                                     ctypes.POINTER(AdamwArgs), vp]),
     ("lema_adamw_step_microbatches", i32, [ctypes.POINTER(AdamwSeg), ctypes.POINTER(vp), i32, i32,

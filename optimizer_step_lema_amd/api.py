@@ -158,6 +158,19 @@ def adamw_step(segments: Sequence[AdamwSegment], *, lr, beta1=0.9, beta2=0.999, 
                                       _stream_handle(stream)), "lema_adamw_step_accum")
 
 
+def adamw_step_noalloc(segments: Sequence[AdamwSegment], *, lr, beta1=0.9, beta2=0.999,
+                       eps=1e-8, weight_decay=0.01, step, stream=None) -> None:
+    """adamw_step for callers that cannot allocate device memory
+    (lema_adamw_step_noalloc): the launch table goes into the library's fixed
+    per-GPU array; at most LEMA_NOALLOC_MAX_SEGMENTS segments, and calls that
+    overlap on one GPU from different streams race for that array."""
+    lib = N.load()
+    segs = (N.AdamwSeg * max(1, len(segments)))(*[s.to_c() for s in segments])
+    args = _args(lr, beta1, beta2, eps, weight_decay, step, _grad_dtype(segments))
+    N.check(lib.lema_adamw_step_noalloc(segs, len(segments), ctypes.byref(args),
+                                        _stream_handle(stream)), "lema_adamw_step_noalloc")
+
+
 class AdamwPlan:
     """A segment list marshalled once for repeated steps.
 

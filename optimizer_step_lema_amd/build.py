@@ -21,8 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblema.so")
-SOURCES = ["lema_kernels.hip", "lema_q8.hip", "lema_host.cpp", "lema_q8_host.cpp", "lema_slot.cpp",
-           "lema_ckpt.cpp"]
+SOURCES = ["lema_kernels.hip", "lema_q8.hip", "lema_noalloc.hip", "lema_host.cpp",
+           "lema_q8_host.cpp", "lema_slot.cpp", "lema_ckpt.cpp"]
 
 
 def hipcc() -> str:

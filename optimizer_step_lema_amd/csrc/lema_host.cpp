@@ -80,12 +80,12 @@ AdamwConsts derive_consts(const lema_adamw_args *a) {
 // ------------------------------------------------------- validation
 
 // True if two spans intersect and at least one of them is written.
-bool any_conflict(std::vector<Span> &spans) {
-    std::sort(spans.begin(), spans.end(),
-              [](const Span &x, const Span &y) { return x.lo < y.lo; });
+bool any_conflict(Span *begin, Span *end) {
+    std::sort(begin, end, [](const Span &x, const Span &y) { return x.lo < y.lo; });
     uintptr_t reach_any = 0, reach_written = 0;   // max end of spans seen so far
     bool seen = false;
-    for (const Span &s : spans) {
+    for (const Span *p = begin; p != end; ++p) {
+        const Span &s = *p;
         if (seen) {
             if (reach_written > s.lo) return true;
             if (s.written && reach_any > s.lo) return true;
@@ -97,14 +97,25 @@ bool any_conflict(std::vector<Span> &spans) {
     return false;
 }
 
-void add_span(std::vector<Span> &spans, const void *p, int64_t numel, size_t elem,
-              bool written) {
+bool any_conflict(std::vector<Span> &spans) {
+    return any_conflict(spans.data(), spans.data() + spans.size());
+}
+
+template <class Spans>
+static void push_span(Spans &spans, const void *p, int64_t numel, size_t elem, bool written) {
     const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
     spans.push_back(Span{lo, lo + static_cast<uintptr_t>(numel) * elem, written});
 }
 
-lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_t grad_dtype,
-                                bool delta_allowed, std::vector<Span> *spans) {
+void add_span(std::vector<Span> &spans, const void *p, int64_t numel, size_t elem,
+              bool written) {
+    push_span(spans, p, numel, elem, written);
+}
+
+template <class Spans>
+static lema_status validate_adamw_segs_into(const lema_adamw_seg *segs, int32_t nseg,
+                                            int32_t grad_dtype, bool delta_allowed,
+                                            Spans *spans) {
     if (nseg < 0) return LEMA_ERR_SIZE;
     if (nseg > 0 && segs == nullptr) return LEMA_ERR_NULL;
     const size_t gsize = grad_dtype == LEMA_GRAD_FP32 ? 4 : 2;
@@ -125,18 +136,28 @@ lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_
                               (gsize == 2 ? reinterpret_cast<uintptr_t>(s.grad) : 0);
         if ((f32 & 3) || (b16 & 1)) return LEMA_ERR_ALIGN;
         if (spans) {
-            add_span(*spans, s.master, s.numel, 4, true);
-            add_span(*spans, s.exp_avg, s.numel, 4, true);
-            add_span(*spans, s.exp_avg_sq, s.numel, 4, true);
-            add_span(*spans, s.grad, s.numel, gsize, false);
-            add_span(*spans, s.weight_bf16, s.numel, 2, true);
+            push_span(*spans, s.master, s.numel, 4, true);
+            push_span(*spans, s.exp_avg, s.numel, 4, true);
+            push_span(*spans, s.exp_avg_sq, s.numel, 4, true);
+            push_span(*spans, s.grad, s.numel, gsize, false);
+            push_span(*spans, s.weight_bf16, s.numel, 2, true);
             if (s.delta) {
-                add_span(*spans, s.orig_bf16, s.numel, 2, false);
-                add_span(*spans, s.delta, s.numel, 4, true);
+                push_span(*spans, s.orig_bf16, s.numel, 2, false);
+                push_span(*spans, s.delta, s.numel, 4, true);
             }
         }
     }
     return LEMA_OK;
+}
+
+lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_t grad_dtype,
+                                bool delta_allowed, std::vector<Span> *spans) {
+    return validate_adamw_segs_into(segs, nseg, grad_dtype, delta_allowed, spans);
+}
+
+lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_t grad_dtype,
+                                bool delta_allowed, FixedSpans *spans) {
+    return validate_adamw_segs_into(segs, nseg, grad_dtype, delta_allowed, spans);
 }
 
 // ----------------------------------------------- per-device state
@@ -323,9 +344,6 @@ void build_table(const std::vector<SegRec> &recs, TableBuild *tb) {
     tb->total_tiles = tiles;
 }
 
-// Tile counts must leave room for the grid stride in 32-bit tile indices.
-constexpr uint64_t kMaxTiles = (uint64_t(1) << 32) - (uint64_t(1) << 20);
-
 uint64_t count_tiles(const std::vector<SegRec> &recs) {
     uint64_t tiles = 0;
     for (const SegRec &r : recs) tiles += static_cast<uint64_t>((r.numel + kTile - 1) / kTile);
@@ -378,7 +396,7 @@ uint32_t occupancy_lds_bytes(int workgroups_per_cu) {
     return step_lds_bytes(d->lds_per_cu, workgroups_per_cu);
 }
 
-static uint32_t step_lds_bytes_for(int nmb) {
+uint32_t step_lds_bytes_for(int nmb) {
     return occupancy_lds_bytes(nmb >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb
                                                         : kStepWorkgroupsPerCu);
 }

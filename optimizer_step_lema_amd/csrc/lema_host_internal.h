@@ -12,6 +12,10 @@
 
 namespace lema {
 
+// Tile counts of one call stay below this, so that 32-bit tile indices plus
+// a launch's grid never wrap.
+constexpr uint64_t kMaxTiles = (uint64_t(1) << 32) - (uint64_t(1) << 20);
+
 // Address range [lo, hi) of one array in one call; `written` if the call
 // stores into it.
 struct Span {
@@ -26,10 +30,30 @@ lema_status hip_failed(hipError_t e);
 lema_status check_hparams(const lema_adamw_args *a, bool allow_q8_grad = false);
 AdamwConsts derive_consts(const lema_adamw_args *a);
 
+// Spans kept in storage the caller provides, for a call that allocates
+// nothing: a span beyond `cap` sets `overflow` instead of being stored.
+struct FixedSpans {
+    Span *data;
+    size_t cap;
+    size_t n = 0;
+    bool overflow = false;
+    void push_back(const Span &s) {
+        if (n < cap)
+            data[n++] = s;
+        else
+            overflow = true;
+    }
+};
+
 // Validates segment descriptors (sizes, pairing, required pointers,
 // element alignment) and appends their spans when `spans` is non-null.
 lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_t grad_dtype,
                                 bool delta_allowed, std::vector<Span> *spans);
+lema_status validate_adamw_segs(const lema_adamw_seg *segs, int32_t nseg, int32_t grad_dtype,
+                                bool delta_allowed, FixedSpans *spans);
+// True if two spans intersect and at least one of them is written (sorts
+// the spans in place; allocates nothing).
+bool any_conflict(Span *begin, Span *end);
 bool any_conflict(std::vector<Span> &spans);
 void add_span(std::vector<Span> &spans, const void *p, int64_t numel, size_t elem, bool written);
 
@@ -70,5 +94,8 @@ lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t strea
 // LDS to reserve per workgroup so that at most `workgroups_per_cu` of them
 // share a CU of the current device (0 if the device cannot be queried).
 uint32_t occupancy_lds_bytes(int workgroups_per_cu);
+// The reservation of the AdamW step kernel reading `nmb` resident
+// micro-batches (0 for the other gradient modes).
+uint32_t step_lds_bytes_for(int nmb);
 
 }  // namespace lema

@@ -268,3 +268,32 @@ def test_microbatch_step_validation(lib):
     z = seg()
     z.numel = 0
     assert microbatch_call(lib, [z], [0, 0, 0], 3) == N.LEMA_OK   # empty segment: no pointers needed
+
+
+def test_noalloc_validation(lib):
+    """lema_adamw_step_noalloc validates as lema_adamw_step does, and refuses
+    more than LEMA_NOALLOC_MAX_SEGMENTS segments, all before any HIP call."""
+    a = args()
+
+    def na(segs, a=a):
+        arr = (N.AdamwSeg * max(1, len(segs)))(*segs)
+        return lib.lema_adamw_step_noalloc(arr, len(segs), ctypes.byref(a), None)
+
+    assert lib.lema_adamw_step_noalloc(None, 0, ctypes.byref(a), None) == N.LEMA_OK
+    assert lib.lema_adamw_step_noalloc(None, -1, ctypes.byref(a), None) == N.LEMA_ERR_SIZE
+    assert lib.lema_adamw_step_noalloc(None, 1, ctypes.byref(a), None) == N.LEMA_ERR_NULL
+    assert na([fake_seg(1 << 32, 10)], args(step=0)) == N.LEMA_ERR_HPARAM
+    lim = N.LEMA_NOALLOC_MAX_SEGMENTS
+    many = [fake_seg((1 << 36) + (k << 28), 8) for k in range(lim + 1)]
+    assert na(many) == N.LEMA_ERR_SIZE
+    s = fake_seg(1 << 32, 1000)
+    s.exp_avg = s.master + 400
+    assert na([s]) == N.LEMA_ERR_OVERLAP
+    s = fake_seg(1 << 32, 10)
+    s.master += 2
+    assert na([s]) == N.LEMA_ERR_ALIGN
+    z = fake_seg(1 << 32, 0)
+    z.master = 0
+    assert na([z] * 3) == N.LEMA_OK                      # only empty segments: a no-op
+    # a valid call at the limit gets past validation (no GPU here: HIP error)
+    assert na(many[:lim]) == N.LEMA_ERR_HIP

@@ -1,0 +1,130 @@
+"""lema_adamw_step_noalloc, the AdamW step for callers that cannot allocate
+device memory, against lema_adamw_step on the same inputs: every output bit
+for bit, on two calls in a row (the second with a smaller input, so it
+reuses the fixed table array the first call filled), at the segment limit,
+and beyond it (refused, nothing written)."""
+from __future__ import annotations
+
+import ctypes
+
+import pytest
+import torch
+
+import optimizer_step_lema_amd as L
+from optimizer_step_lema_amd import _native as N
+import synth
+
+pytestmark = pytest.mark.gpu
+
+HP = synth.HPARAMS
+
+
+def _state(sizes, seed, delta=True, offset=0):
+    """Two identical copies of a segment list's state (fresh draws per
+    segment; `offset` > 0 starts every array that many elements into its
+    buffer, so that the arrays are not 16-byte aligned)."""
+    copies = ([], [])
+    for i, n in enumerate(sizes):
+        s = seed + 10 * i
+        base = {"master": synth.normal(n + offset, 0.02, s, "cuda"),
+                "m": synth.normal(n + offset, 1e-4, s + 1, "cuda"),
+                "v": synth.normal(n + offset, 1e-3, s + 2, "cuda").square_(),
+                "g": synth.bf16_normal(n + offset, 1e-3, s + 3, "cuda")}
+        for segs in copies:
+            t = {k: v.clone()[offset:] for k, v in base.items()}
+            orig = t["master"].to(torch.bfloat16) if delta else None
+            segs.append(L.AdamwSegment(
+                t["master"], t["m"], t["v"], t["g"],
+                torch.full((n,), 0x7FC1, dtype=torch.int16, device="cuda").view(torch.bfloat16),
+                orig, torch.full((n,), float("nan"), device="cuda") if delta else None))
+    return copies
+
+
+def _bits(t):
+    return t.view(torch.int32) if t.dtype == torch.float32 else t.view(torch.int16)
+
+
+def _assert_same(ref, got):
+    for a, b in zip(ref, got):
+        for name in ("master", "exp_avg", "exp_avg_sq", "weight", "delta"):
+            x, y = getattr(a, name), getattr(b, name)
+            if x is None:
+                assert y is None
+                continue
+            assert torch.equal(_bits(x), _bits(y)), name
+
+
+def test_two_calls_match_lema_adamw_step():
+    torch.cuda.synchronize()
+    # GPT-2 c_attn-like tensors with a ragged tail, then a smaller list
+    for sizes, seed, step, offset in (([768 * 2304, 2304, 768 * 2304 + 77, 2304], 500, 1, 0),
+                                      ([4096 + 5, 300], 900, 7, 1)):
+        ref, got = _state(sizes, seed, offset=offset)
+        print(f"noalloc: {len(sizes)} segments, {sum(sizes)} params, t={step}", flush=True)
+        L.adamw_step(ref, step=step, **HP)
+        L.adamw_step_noalloc(got, step=step, **HP)
+        torch.cuda.synchronize()
+        _assert_same(ref, got)
+
+
+def test_repeated_steps_and_no_delta_match():
+    sizes = [4096 * 4096, 11008, 1]
+    ref, got = _state(sizes, 1300, delta=False)
+    for t in (1, 2, 3):
+        L.adamw_step(ref, step=t, **HP)
+        L.adamw_step_noalloc(got, step=t, **HP)
+    torch.cuda.synchronize()
+    _assert_same(ref, got)
+
+
+def test_segment_limit():
+    lim = N.LEMA_NOALLOC_MAX_SEGMENTS
+    sizes = [257 + (i % 7) for i in range(lim)]
+    # lim segments as views of one buffer per array kind, twice
+    _, segs_ref = L.flat_adamw_state(sizes, delta=True)
+    _, segs_got = L.flat_adamw_state(sizes, delta=True)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1700)
+    for a, b in zip(segs_ref, segs_got):
+        a.master.normal_(0, 0.02, generator=gen)
+        a.exp_avg.normal_(0, 1e-4, generator=gen)
+        a.exp_avg_sq.normal_(0, 1e-3, generator=gen).square_()
+        a.grad.copy_((torch.randn(a.master.shape, device="cuda", generator=gen) * 1e-3)
+                     .to(torch.bfloat16))
+        a.orig.copy_(a.master.to(torch.bfloat16))
+        for name in ("master", "exp_avg", "exp_avg_sq", "grad", "orig"):
+            getattr(b, name).copy_(getattr(a, name))
+    L.adamw_step(segs_ref, step=4, **HP)
+    L.adamw_step_noalloc(segs_got, step=4, **HP)
+    torch.cuda.synchronize()
+    _assert_same(segs_ref, segs_got)
+
+    # one segment more is refused before anything is enqueued
+    _, extra = _state([1000], 1800)
+    big = list(segs_got) + extra
+    before = [t.clone() for t in (segs_got[0].master, extra[0].master)]
+    lib = N.load()
+    c = (N.AdamwSeg * len(big))(*[s.to_c() for s in big])
+    args = N.AdamwArgs(HP["lr"], HP["beta1"], HP["beta2"], HP["eps"], HP["weight_decay"], 5,
+                       N.LEMA_GRAD_BF16, 0)
+    st = lib.lema_adamw_step_noalloc(c, len(big), ctypes.byref(args),
+                                     torch.cuda.current_stream().cuda_stream)
+    assert st == N.LEMA_ERR_SIZE
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(before[0]), _bits(segs_got[0].master))
+    assert torch.equal(_bits(before[1]), _bits(extra[0].master))
+
+
+def test_interleaved_with_cached_calls():
+    # the two entry points' tables live in different places: alternating them
+    # on one stream, each sees its own
+    a_ref, a_got = _state([65536, 999], 2100)
+    b_ref, b_got = _state([1 << 20], 2200)
+    for t in (1, 2):
+        L.adamw_step(a_ref, step=t, **HP)
+        L.adamw_step_noalloc(a_got, step=t, **HP)
+        L.adamw_step(b_ref, step=t, **HP)
+        L.adamw_step_noalloc(b_got, step=t, **HP)
+    torch.cuda.synchronize()
+    _assert_same(a_ref, a_got)
+    _assert_same(b_ref, b_got)
