@@ -59,12 +59,43 @@ lema_status lema_probe_q8_reciprocal(const float *s, float *r, int64_t n, void *
 lema_status lema_table_cache_stats(int64_t out[4]);
 
 /* The LDS size per compute unit the current device reports, and the LDS the
- * AdamW step reserves per workgroup (the kernel uses none) to cap how many of
- * its workgroups share a CU: about 13, or 10 when the step reads
+ * AdamW step (delta on) reserves per workgroup (the kernel uses none) to cap
+ * how many of its workgroups share a CU: 13, or 10 when the step reads
  * `microbatches` >= 4 resident micro-batch gradients (0 = an ordinary step).
  * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE (microbatches < 0), LEMA_ERR_HIP. */
 lema_status lema_step_lds_reservation(int32_t microbatches, int32_t *lds_per_cu,
                                       int32_t *reserved_bytes);
+
+/*
+ * Residency probe: launches `workgroups` workgroups of `lanes` lanes (a
+ * multiple of 64, at most 1024), each with `lds_bytes` of LDS reserved (at
+ * most 65536).  The first wavefront of workgroup i stays resident for about
+ * `spin_us` microseconds (1 .. 1000) and writes three words to
+ * records[3*i .. 3*i+2]: (XCC id << 32) | the HW_ID register (compute unit,
+ * shader array and engine bits), then the device wall clock at its start and
+ * at its end (hipDeviceAttributeWallClockRate kHz).  The most workgroups
+ * that overlapped in time on one compute unit is how many of that size fit
+ * there at once.  `records` is device memory of 3 * workgroups words.
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE, LEMA_ERR_ALIGN, LEMA_ERR_HIP.
+ */
+lema_status lema_probe_residency(uint64_t *records, int32_t workgroups, int32_t lanes,
+                                 int32_t lds_bytes, int32_t spin_us, void *stream);
+
+/*
+ * The occupancy plan of a step kernel on the current device, for checking
+ * with lema_probe_residency.  `kernel`:
+ *   0  the fp32 AdamW step (bf16 gradient, delta on)
+ *   1  the fp32 step on 8 resident bf16 micro-batches (delta on)
+ *   2  the int8-moment step, 256-lane wave-row workgroups (bf16 gradient,
+ *      delta on)
+ * out[0] lanes per workgroup, out[1] the kernel's static LDS bytes, out[2]
+ * the dynamic LDS bytes a launch reserves, out[3] the workgroups per CU the
+ * reservation is meant to allow, out[4] the workgroups per CU its registers
+ * and static LDS alone allow (hipOccupancyMaxActiveBlocksPerMultiprocessor),
+ * out[5] the LDS allocation granule the reservation assumes.
+ * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE (unknown kernel), LEMA_ERR_HIP.
+ */
+lema_status lema_step_occupancy(int32_t kernel, int32_t out[6]);
 
 /* Compute units of the current device and the elements one workgroup takes
  * per tile in the AdamW and accumulation kernels. */

@@ -11,5 +11,5 @@ from .api import (AccumPlan, AccumQ8Plan, AccumQ8Segment, AccumSegment, AdamwPla
                   SlotPool, adamw_constants, adamw_step, adamw_step_noalloc, adamw_step_q8,
                   checkpoint_tensors, dequantize_rows, device_info, flat_adamw_state, flat_q8_state,
                   grad_accum, grad_accum_q8, load_checkpoint, measure_copy, merge_delta,
-                  pinned_empty, probe_fp32, probe_q8_reciprocal, quantize_rows, save_checkpoint,
-                  table_cache_stats)
+                  pinned_empty, probe_fp32, probe_q8_reciprocal, probe_residency, quantize_rows,
+                  save_checkpoint, step_occupancy, table_cache_stats)

@@ -143,6 +143,8 @@ SIGNATURES = [
     ("lema_probe_q8_reciprocal", i32, [vp, vp, i64, vp]),
     ("lema_device_info", i32, [ctypes.POINTER(i32), ctypes.POINTER(i32)]),
     ("lema_step_lds_reservation", i32, [i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]),
+    ("lema_probe_residency", i32, [vp, i32, i32, i32, i32, vp]),
+    ("lema_step_occupancy", i32, [i32, ctypes.POINTER(i32)]),
     ("lema_table_cache_stats", i32, [ctypes.POINTER(i64)]),
 ]
 

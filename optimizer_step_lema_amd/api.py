@@ -719,6 +719,47 @@ def probe_q8_reciprocal(s: torch.Tensor, stream=None) -> torch.Tensor:
     return r
 
 
+def probe_residency(lanes: int, lds_bytes: int, *, per_cu: int = 40, spin_us: int = 20,
+                    stream=None) -> dict:
+    """How many workgroups of `lanes` lanes with `lds_bytes` of LDS each are
+    resident on one compute unit at once (lema_probe_residency): the most
+    whose resident intervals overlap on one CU, over a grid of `per_cu`
+    workgroups per CU.  Returns that maximum, the minimum over CUs, and the
+    number of distinct CUs seen."""
+    cus = device_info()["compute_units"]
+    n = per_cu * cus
+    rec = torch.zeros(3 * n, dtype=torch.int64, device="cuda")
+    N.check(N.load().lema_probe_residency(rec.data_ptr(), n, lanes, lds_bytes, spin_us,
+                                          _stream_handle(stream)), "lema_probe_residency")
+    torch.cuda.synchronize()
+    r = rec.view(n, 3).cpu().tolist()
+    # a compute unit: its XCC and the HW_ID bits 8..15 (CU, shader array, engine)
+    events = {}
+    for key, t0, t1 in r:
+        cu = (key >> 32, (key >> 8) & 0xFF)
+        events.setdefault(cu, []).extend(((t0, 1), (t1, -1)))
+    most = []
+    for ev in events.values():
+        ev.sort(key=lambda e: (e[0], e[1]))      # an end before a start at the same tick
+        cur = best = 0
+        for _, d in ev:
+            cur += d
+            best = max(best, cur)
+        most.append(best)
+    return {"max_per_cu": max(most), "min_per_cu": min(most), "cus_seen": len(events),
+            "workgroups": n}
+
+
+def step_occupancy(kernel: int) -> dict:
+    """The occupancy plan of step kernel `kernel` (lema_step_occupancy):
+    0 fp32 step, 1 fp32 step on 8 resident micro-batches, 2 int8 step."""
+    out = (ctypes.c_int32 * 6)()
+    N.check(N.load().lema_step_occupancy(kernel, out), "lema_step_occupancy")
+    keys = ("lanes", "static_lds", "reserved_lds", "intended_per_cu", "per_cu_by_registers",
+            "lds_granule")
+    return dict(zip(keys, list(out)))
+
+
 def table_cache_stats() -> dict:
     """Launch-table cache counters of the current device (since load)."""
     out = (ctypes.c_int64 * 4)()

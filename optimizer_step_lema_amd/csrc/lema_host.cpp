@@ -375,39 +375,75 @@ lema_status launch_on_table(const std::vector<unsigned char> &bytes, hipStream_t
 // Workgroups of the AdamW step kernel allowed on one CU.  Each streams
 // 7-12 KB of HBM traffic for its tile, from 5-12 arrays at once.  With every
 // CU full of them (32 per CU) the HBM stacks see so many concurrent streams
-// that they deliver 6-10% less than with about 13 (measured on MI355X over
-// 8-18 per CU, for 28-38 B per parameter); the step that reads 8 resident
-// micro-batches (48 B per parameter) does best at about 10.
-constexpr int kStepWorkgroupsPerCu = 13;
-constexpr int kStepWorkgroupsPerCuManyMb = 10;
+// that they deliver 6-10% less than with 12 (measured on MI355X over 8-18
+// per CU, for 28-38 B per parameter); the step that reads 8 resident
+// micro-batches (48 B per parameter) does best at 9.
+constexpr int kStepWorkgroupsPerCu = 12;
+constexpr int kStepWorkgroupsPerCuManyMb = 9;
 constexpr int kManyMicrobatches = 4;
 
-// The LDS to reserve per workgroup so that at most `per_cu` of them fit on
-// one CU (0 when the device reports no LDS size).
-static uint32_t step_lds_bytes(int lds_per_cu, int per_cu) {
+// LDS goes to a workgroup in whole granules: its static and dynamic LDS
+// together, rounded up to a multiple of the granule.  On gfx950 the granule
+// is 1280 bytes, 128 of them per CU (lema_probe_residency: 12,288 bytes per
+// 64-lane workgroup let 12 share a CU, not 13; 16,384 let 9, 32,768 bytes
+// per 256-lane workgroup 4), so only counts of the form floor(128 / k) are
+// reachable through LDS: 12 or 14 per CU, never 13.
+constexpr uint32_t kLdsGranule = 1280;
+
+namespace {
+
+// Static LDS of the kernels occupancy planning has asked about.
+std::mutex g_static_lds_mu;
+std::vector<std::pair<const void *, uint32_t>> g_static_lds;
+
+uint32_t static_lds_bytes(const void *fn) {
+    std::lock_guard<std::mutex> lock(g_static_lds_mu);
+    for (const auto &e : g_static_lds)
+        if (e.first == fn) return e.second;
+    hipFuncAttributes attr{};
+    const uint32_t b = hipFuncGetAttributes(&attr, fn) == hipSuccess
+                           ? static_cast<uint32_t>(attr.sharedSizeBytes) : 0;
+    g_static_lds.emplace_back(fn, b);
+    return b;
+}
+
+// LDS of one workgroup (static plus dynamic) such that at most `per_cu`
+// of them fit on one CU, as close to per_cu as the granule allows: the
+// fewest granules k with floor(granules per CU / k) <= per_cu, at most
+// 64 KiB.
+uint32_t lds_per_workgroup(int lds_per_cu, int per_cu) {
     if (lds_per_cu <= 0 || per_cu <= 0) return 0;
-    const uint32_t b = static_cast<uint32_t>(lds_per_cu / per_cu) & ~255u;
-    return std::min<uint32_t>(b, 65536u);
+    const uint32_t granules = static_cast<uint32_t>(lds_per_cu) / kLdsGranule;
+    const uint32_t k = granules / static_cast<uint32_t>(per_cu + 1) + 1;
+    return std::min<uint32_t>(k * kLdsGranule, 65536u);
 }
 
-uint32_t occupancy_lds_bytes(int workgroups_per_cu) {
+}  // namespace
+
+uint32_t occupancy_lds_bytes(const void *fn, int workgroups_per_cu) {
     DeviceState *d = nullptr;
-    if (device_state(&d, nullptr) != LEMA_OK) return 0;   // the launch reports the error
-    return step_lds_bytes(d->lds_per_cu, workgroups_per_cu);
+    if (fn == nullptr || device_state(&d, nullptr) != LEMA_OK) return 0;  // the launch reports it
+    const uint32_t total = lds_per_workgroup(d->lds_per_cu, workgroups_per_cu);
+    const uint32_t fixed = static_lds_bytes(fn);
+    return total > fixed ? total - fixed : 0;
 }
 
-uint32_t step_lds_bytes_for(int nmb) {
-    return occupancy_lds_bytes(nmb >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb
-                                                        : kStepWorkgroupsPerCu);
+int step_workgroups_per_cu(int nmb) {
+    return nmb >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb : kStepWorkgroupsPerCu;
+}
+
+uint32_t step_lds_bytes_for(GradMode grad_mode, bool with_delta, int nmb) {
+    return occupancy_lds_bytes(adamw_kernel_fn(grad_mode, with_delta, nmb),
+                               step_workgroups_per_cu(nmb));
 }
 
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
                               GradMode grad_mode, hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
-    const uint32_t lds = step_lds_bytes_for(0);
     bool with_delta = false;
     for (const SegRec &r : recs) with_delta |= r.p[6] != 0;
+    const uint32_t lds = step_lds_bytes_for(grad_mode, with_delta, 0);
     TableBuild tb;
     build_table(recs, &tb);
     return launch_on_table(tb.bytes, stream, [&](const void *table) {
@@ -420,13 +456,13 @@ lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<ui
                                   int nmb, const AdamwConsts &c, hipStream_t stream) {
     if (recs.empty()) return LEMA_OK;
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
-    const uint32_t lds = step_lds_bytes_for(nmb);
     bool with_delta = false;
     const int n = static_cast<int>(recs.size());
     for (int i = 0; i < n; ++i) {
         with_delta |= recs[i].p[6] != 0;
         recs[i].p[3] = table_bytes(n) + sizeof(uint64_t) * size_t(nmb) * size_t(i);
     }
+    const uint32_t lds = step_lds_bytes_for(kGradBf16Sum, with_delta, nmb);
     TableBuild tb;
     build_table(recs, &tb);
     tb.bytes.resize(table_bytes(n) + sizeof(uint64_t) * lists.size());
@@ -729,9 +765,62 @@ lema_status lema_step_lds_reservation(int32_t microbatches, int32_t *lds_per_cu,
     lema_status st = device_state(&d, nullptr);
     if (st != LEMA_OK) return st;
     *lds_per_cu = d->lds_per_cu;
-    *reserved_bytes = static_cast<int32_t>(step_lds_bytes(
-        d->lds_per_cu, microbatches >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb
-                                                         : kStepWorkgroupsPerCu));
+    *reserved_bytes = static_cast<int32_t>(
+        microbatches >= 1 && microbatches <= kMaxMicrobatches
+            ? step_lds_bytes_for(kGradBf16Sum, true, microbatches)
+            : step_lds_bytes_for(kGradBf16, true, 0));
+    return LEMA_OK;
+}
+
+lema_status lema_probe_residency(uint64_t *records, int32_t workgroups, int32_t lanes,
+                                 int32_t lds_bytes, int32_t spin_us, void *stream) {
+    if (records == nullptr) return LEMA_ERR_NULL;
+    if (workgroups < 1 || workgroups > (1 << 20) || lanes < 64 || lanes > 1024 || lanes % 64 ||
+        lds_bytes < 0 || lds_bytes > 65536 || spin_us < 1 || spin_us > 1000)
+        return LEMA_ERR_SIZE;
+    if (reinterpret_cast<uintptr_t>(records) & 7) return LEMA_ERR_ALIGN;
+    int dev = 0, khz = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+    if (e != hipSuccess) return hip_failed(e);
+    const uint64_t ticks = std::max<uint64_t>(1, uint64_t(khz) * uint64_t(spin_us) / 1000);
+    e = launch_residency_probe(records, workgroups, lanes, static_cast<uint32_t>(lds_bytes), ticks,
+                               static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? LEMA_OK : hip_failed(e);
+}
+
+lema_status lema_step_occupancy(int32_t kernel, int32_t out[6]) {
+    if (out == nullptr) return LEMA_ERR_NULL;
+    const void *fn = nullptr;
+    int lanes = kBlock, per_cu = 0;
+    switch (kernel) {
+    case 0:
+        fn = adamw_kernel_fn(kGradBf16, true, 0);
+        per_cu = step_workgroups_per_cu(0);
+        break;
+    case 1:
+        fn = adamw_kernel_fn(kGradBf16Sum, true, 8);
+        per_cu = step_workgroups_per_cu(8);
+        break;
+    case 2:
+        fn = adamw_q8_kernel_fn(true, kQGradBf16, true, kQBlock, kQRowsWave);
+        lanes = kQBlock;
+        per_cu = kQ8StepWorkgroupsPerCu;
+        break;
+    default: return LEMA_ERR_SIZE;
+    }
+    hipFuncAttributes attr{};
+    hipError_t e = hipFuncGetAttributes(&attr, fn);
+    if (e != hipSuccess) return hip_failed(e);
+    int by_regs = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&by_regs, fn, lanes, 0);
+    if (e != hipSuccess) return hip_failed(e);
+    out[0] = lanes;
+    out[1] = static_cast<int32_t>(attr.sharedSizeBytes);
+    out[2] = static_cast<int32_t>(occupancy_lds_bytes(fn, per_cu));
+    out[3] = per_cu;
+    out[4] = by_regs;
+    out[5] = static_cast<int32_t>(kLdsGranule);
     return LEMA_OK;
 }
 

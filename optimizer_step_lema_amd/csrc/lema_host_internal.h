@@ -91,11 +91,15 @@ lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<ui
                                   int nmb, const AdamwConsts &c, hipStream_t stream);
 lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t stream);
 
-// LDS to reserve per workgroup so that at most `workgroups_per_cu` of them
-// share a CU of the current device (0 if the device cannot be queried).
-uint32_t occupancy_lds_bytes(int workgroups_per_cu);
-// The reservation of the AdamW step kernel reading `nmb` resident
-// micro-batches (0 for the other gradient modes).
-uint32_t step_lds_bytes_for(int nmb);
+// Dynamic LDS to reserve per workgroup of kernel `fn` so that at most
+// `workgroups_per_cu` of them share a CU of the current device: the
+// kernel's static LDS is subtracted and the total kept to whole allocation
+// granules (0 if the device or the kernel cannot be queried).
+uint32_t occupancy_lds_bytes(const void *fn, int workgroups_per_cu);
+// Workgroups of the fp32 AdamW step allowed per CU when it reads `nmb`
+// resident micro-batches (0 for the other gradient modes), and the dynamic
+// LDS its kernel reserves for that.
+int step_workgroups_per_cu(int nmb);
+uint32_t step_lds_bytes_for(GradMode grad_mode, bool with_delta, int nmb);
 
 }  // namespace lema

@@ -79,7 +79,7 @@ constexpr int kQBlockWide = 1024;
 // (int8 step 5.50 TB/s at 4, 4.97 at 8, 2.47 at 16 with 256 VGPRs;
 // accumulation 4.0 TB/s at 4, 1.7 at 8, 2.5 at 16).
 constexpr int kQStepChunks = 4;
-constexpr int kQ8StepWorkgroupsPerCu = 4;     // occupancy cap of the 256-lane step
+constexpr int kQ8StepWorkgroupsPerCu = 3;     // occupancy cap of the 256-lane step
 constexpr int kQCodeChunks = 4;
 constexpr int kQWideChunks = 4;
 // Wave-row accumulation and conversions hold up to 16 chunks per lane in
@@ -155,7 +155,16 @@ hipError_t launch_accum_q8(const void *table, int nseg, uint32_t total_blocks, b
 hipError_t launch_quantize_q8(const void *table, int nseg, uint32_t total_blocks, bool dequantize,
                               int block, QRows rows, hipStream_t stream);
 
+// The kernel functions launch_adamw and launch_adamw_q8 run for these
+// arguments (nullptr where they would refuse them): occupancy planning
+// queries their static LDS and registers.
+const void *adamw_kernel_fn(GradMode grad_mode, bool with_delta, int nmb);
+const void *adamw_q8_kernel_fn(bool moments_q8, QGrad grad, bool with_delta, int block,
+                               QRows rows);
+
 // Measurement aids (include/lema_measure.h).
+hipError_t launch_residency_probe(uint64_t *rec, int workgroups, int lanes, uint32_t lds_bytes,
+                                  uint64_t ticks, hipStream_t stream);
 hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 hipError_t launch_fp32_probe(const float *a, const float *b, float *quot,
                              float *root, uint16_t *bf16, int64_t n,

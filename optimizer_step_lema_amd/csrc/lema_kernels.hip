@@ -338,6 +338,30 @@ __global__ __launch_bounds__(kCopyBlock) void copy_kernel(const f32x4 *__restric
     if (i < n16) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Residency probe: the first wavefront of each workgroup notes its compute
+// unit (XCC_ID and the HW_ID register) and the device wall clock, stays
+// resident for `ticks` of that clock (a bounded wait), and notes the clock
+// again.  The workgroup's LDS is whatever the launch reserves; the most
+// workgroups that overlap in time on one compute unit is how many of them
+// fit there.  rec holds 3 words per workgroup of the grid.
+__global__ void residency_probe_kernel(uint64_t *__restrict__ rec, uint64_t ticks) {
+    if (threadIdx.x != 0) return;
+    constexpr int kHwIdReg = 4 | (31 << 11);      // hwreg(HW_REG_HW_ID, 0, 32)
+    constexpr int kXccIdReg = 20 | (3 << 11);     // hwreg(HW_REG_XCC_ID, 0, 4)
+    const uint32_t hw = __builtin_amdgcn_s_getreg(kHwIdReg);
+    const uint32_t xcc = __builtin_amdgcn_s_getreg(kXccIdReg);
+    const uint64_t t0 = wall_clock64();
+    uint64_t t1 = t0;
+    for (int i = 0; i < (1 << 22) && t1 - t0 < ticks; ++i) {
+        __builtin_amdgcn_s_sleep(2);
+        t1 = wall_clock64();
+    }
+    uint64_t *r = rec + 3 * uint64_t(blockIdx.x);
+    r[0] = (uint64_t(xcc) << 32) | hw;
+    r[1] = t0;
+    r[2] = t1;
+}
+
 // The division, square root and bf16 rounding exactly as the AdamW kernel
 // compiles them, for checking against IEEE results on the host.
 __global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restrict__ a,
@@ -360,23 +384,26 @@ __global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restr
 // Launches go through hipLaunchKernel, which returns the launch status
 // directly instead of through the thread's sticky last-error slot.  Grids
 // larger than max_blocks_per_launch are split into consecutive launches.
-hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradMode grad_mode,
-                        bool with_delta, const AdamwConsts &c, hipStream_t stream, int nmb,
-                        uint32_t lds_bytes) {
-    const void *fn;
+const void *adamw_kernel_fn(GradMode grad_mode, bool with_delta, int nmb) {
 #define LEMA_PICK(M) with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<M, true>) \
                                 : reinterpret_cast<const void *>(&adamw_tile_kernel<M, false>)
     switch (grad_mode) {
-    case kGradBf16: fn = LEMA_PICK(kGradBf16); break;
-    case kGradF32: fn = LEMA_PICK(kGradF32); break;
-    case kGradF32PlusBf16: fn = LEMA_PICK(kGradF32PlusBf16); break;
+    case kGradBf16: return LEMA_PICK(kGradBf16);
+    case kGradF32: return LEMA_PICK(kGradF32);
+    case kGradF32PlusBf16: return LEMA_PICK(kGradF32PlusBf16);
     case kGradBf16Sum:
-        if (nmb < 1 || nmb > kMaxMicrobatches) return hipErrorInvalidValue;
-        fn = pick_sum_kernel(nmb, with_delta, std::make_index_sequence<kMaxMicrobatches>{});
-        break;
-    default: return hipErrorInvalidValue;
+        if (nmb < 1 || nmb > kMaxMicrobatches) return nullptr;
+        return pick_sum_kernel(nmb, with_delta, std::make_index_sequence<kMaxMicrobatches>{});
+    default: return nullptr;
     }
 #undef LEMA_PICK
+}
+
+hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradMode grad_mode,
+                        bool with_delta, const AdamwConsts &c, hipStream_t stream, int nmb,
+                        uint32_t lds_bytes) {
+    const void *fn = adamw_kernel_fn(grad_mode, with_delta, nmb);
+    if (fn == nullptr) return hipErrorInvalidValue;
     AdamwConsts consts = c;
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
         const uint32_t n = std::min<uint32_t>(total_tiles - tile0, max_blocks_per_launch(kBlock));
@@ -428,6 +455,14 @@ hipError_t launch_copy(const void *src, void *dst, size_t bytes, hipStream_t str
         block0 += n;
     }
     return hipSuccess;
+}
+
+hipError_t launch_residency_probe(uint64_t *rec, int workgroups, int lanes, uint32_t lds_bytes,
+                                  uint64_t ticks, hipStream_t stream) {
+    void *args[] = {&rec, &ticks};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&residency_probe_kernel),
+                           dim3(unsigned(workgroups)), dim3(unsigned(lanes)), args, lds_bytes,
+                           stream);
 }
 
 hipError_t launch_fp32_probe(const float *a, const float *b, float *quot, float *root,

@@ -1145,24 +1145,28 @@ bool rows_block_ok(int block, QRows rows) {
 
 }  // namespace
 
+const void *adamw_q8_kernel_fn(bool moments_q8, QGrad grad, bool with_delta, int block,
+                               QRows rows) {
+    if (!block_ok(block, rows)) return nullptr;
+    if (moments_q8) {
+        switch (grad) {
+        case kQGradBf16: return pick_adamw_delta<true, kQGradBf16>(with_delta, block, rows);
+        case kQGradF32: return pick_adamw_delta<true, kQGradF32>(with_delta, block, rows);
+        case kQGradQ8: return pick_adamw_delta<true, kQGradQ8>(with_delta, block, rows);
+        default: return nullptr;
+        }
+    }
+    // fp32 moments only pair with an int8 gradient here; the other
+    // combinations run on the tile kernels of lema_kernels.hip
+    if (grad != kQGradQ8) return nullptr;
+    return pick_adamw_delta<false, kQGradQ8>(with_delta, block, rows);
+}
+
 hipError_t launch_adamw_q8(const void *table, int nseg, uint32_t total_blocks, bool moments_q8,
                            QGrad grad, bool with_delta, int block, QRows rows,
                            const AdamwConsts &c, hipStream_t stream, uint32_t lds_bytes) {
-    if (!block_ok(block, rows)) return hipErrorInvalidValue;
-    const void *fn = nullptr;
-    if (moments_q8) {
-        switch (grad) {
-        case kQGradBf16: fn = pick_adamw_delta<true, kQGradBf16>(with_delta, block, rows); break;
-        case kQGradF32: fn = pick_adamw_delta<true, kQGradF32>(with_delta, block, rows); break;
-        case kQGradQ8: fn = pick_adamw_delta<true, kQGradQ8>(with_delta, block, rows); break;
-        default: return hipErrorInvalidValue;
-        }
-    } else {
-        // fp32 moments only pair with an int8 gradient here; the other
-        // combinations run on the tile kernels of lema_kernels.hip
-        if (grad != kQGradQ8) return hipErrorInvalidValue;
-        fn = pick_adamw_delta<false, kQGradQ8>(with_delta, block, rows);
-    }
+    const void *fn = adamw_q8_kernel_fn(moments_q8, grad, with_delta, block, rows);
+    if (fn == nullptr) return hipErrorInvalidValue;
     return launch_split(fn, block, total_blocks, lds_bytes, stream, table, nseg, c);
 }
 

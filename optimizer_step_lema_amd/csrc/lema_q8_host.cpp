@@ -259,16 +259,20 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
     const QGrad qg = gd == LEMA_GRAD_BF16 ? kQGradBf16 : gd == LEMA_GRAD_FP32 ? kQGradF32 : kQGradQ8;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     // 256-lane workgroups of the step each stream ~90 KB of state for their
-    // row; beyond 4 of them per CU (5 fit by registers) HBM delivers less
-    // (measured on MI355X: 3-4% faster at 4 per CU on the attention and
-    // layer workloads; 3 per CU starves small launches such as the LoRA
-    // adapters).  The 1024-lane ones fit once per CU anyway.  Accumulation
-    // and conversions move less per workgroup and keep full occupancy.
-    const uint32_t lds = occupancy_lds_bytes(kQ8StepWorkgroupsPerCu);
+    // row; beyond 3 of them per CU (7 fit by registers) HBM delivers less
+    // (measured on MI355X: 2-3% faster at 3 per CU than uncapped on the
+    // attention and layer workloads, 1-2% faster than at 4 or 5; 2 per CU
+    // starves small launches such as the LoRA adapters).  The 1024-lane
+    // ones fit once per CU anyway.  Accumulation and conversions move less
+    // per workgroup and keep full occupancy.
     return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks,
                                                      int block, QRows rows) {
-        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, rows, c, hs,
-                               block == kQBlock ? lds : 0);
+        const uint32_t lds = block == kQBlock
+                                 ? occupancy_lds_bytes(adamw_q8_kernel_fn(mom_q8, qg, with_delta,
+                                                                          block, rows),
+                                                       kQ8StepWorkgroupsPerCu)
+                                 : 0;
+        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, rows, c, hs, lds);
     });
 }
 

@@ -297,3 +297,17 @@ def test_noalloc_validation(lib):
     assert na([z] * 3) == N.LEMA_OK                      # only empty segments: a no-op
     # a valid call at the limit gets past validation (no GPU here: HIP error)
     assert na(many[:lim]) == N.LEMA_ERR_HIP
+
+
+def test_residency_probe_validation(lib):
+    rec = 1 << 32
+    assert lib.lema_probe_residency(None, 10, 64, 0, 20, None) == N.LEMA_ERR_NULL
+    for wg, lanes, lds, spin in ((0, 64, 0, 20), (10, 32, 0, 20), (10, 96, 0, 20),
+                                 (10, 2048, 0, 20), (10, 64, -1, 20), (10, 64, 65537, 20),
+                                 (10, 64, 0, 0), (10, 64, 0, 1001)):
+        assert lib.lema_probe_residency(rec, wg, lanes, lds, spin, None) == N.LEMA_ERR_SIZE
+    assert lib.lema_probe_residency(rec + 4, 10, 64, 0, 20, None) == N.LEMA_ERR_ALIGN
+    out = (ctypes.c_int32 * 6)()
+    assert lib.lema_step_occupancy(0, None) == N.LEMA_ERR_NULL
+    assert lib.lema_step_occupancy(3, out) == N.LEMA_ERR_SIZE
+    assert lib.lema_step_occupancy(-1, out) == N.LEMA_ERR_SIZE

@@ -346,3 +346,51 @@ def test_q8_accumulation_bruteforce_random(L):
     exact = sum(oracle.bf16_to_f32(g).astype(np.float64) for g in grads)
     got = oracle.dequantize_rows(acc_q, acc_s, L).astype(np.float64)
     assert (np.abs(got - exact) <= bound + 1e-12).all()
+
+
+# ------------------------------------------------- a hazard of the reading
+
+def test_q8_v_collapse_with_zero_gradient_steps_by_m_over_eps():
+    """A consequence of the int8 reading (symmetric absmax/127 rows), pinned
+    so that it is stated and not discovered: in a row of v = N(0, 1e-3)^2
+    about a fifth of the elements lie below half the row's scale and
+    quantize to code 0.  When such an element's m code is not 0 and its
+    gradient is 0 (a frozen slice, an embedding row no token touched), the
+    step sees v' = 0, its denominator is eps alone, and the weight moves by
+    step * (b1*m) / eps: 3.24 for the element below (m = 2.3e-4, t = 10),
+    against weights of about 0.02, and 754 of the row's 4096 elements move
+    by more than 0.1.  With fp32 v the same element moves by 5.2e-5.  The
+    pages leave the format open; this is what the chosen one does.  A
+    dropped or misplaced eps, or a step that floored v, would change the
+    numbers below."""
+    L = 4096
+    rng = np.random.default_rng(11)
+    root = (rng.standard_normal(L) * 1e-3).astype(np.float32)
+    v = root * root
+    m = (rng.standard_normal(L) * 1e-4).astype(np.float32)
+    vq, vs = oracle.quantize_rows(v, L)
+    mq, ms = oracle.quantize_rows(m, L)
+    zero_v = vq == 0
+    assert 0.15 < zero_v.mean() < 0.25                     # about a fifth of the row
+    pick = int(np.flatnonzero(zero_v & (np.abs(mq) >= 80))[0])
+    master = (rng.standard_normal(L) * 0.02).astype(np.float32)
+    w0 = master.copy()
+    grad = np.zeros(L, np.uint16)                          # bf16 +0 everywhere
+    c = consts(10)
+    b1, eps, decay, step = (np.float32(c[i]) for i in (0, 4, 5, 6))
+    oracle.adamw_step_q8(master, (mq.copy(), ms.copy()), (vq.copy(), vs.copy()), grad, c, L)
+
+    m_deq = np.float32(mq[pick]) * ms[0]
+    m_new = b1 * m_deq                                     # + (1-b1)*0
+    upd = step * (m_new / eps)                             # sqrt(0)*ibc2 + eps = eps
+    assert master[pick] == np.float32(w0[pick] * decay) - upd
+    assert abs(upd) > 1.0 and abs(upd) > 50 * abs(w0[pick])
+    moved = np.abs(master - w0 * decay) > 0.1
+    assert 0.1 < moved.mean() < 0.25 and not moved[~zero_v].any()
+
+    # the same element with fp32 moments: v' = b2*v > 0 keeps the step small
+    m32, v32 = m.copy(), v.copy()
+    m32[pick], v32[pick] = m_deq, v[pick]
+    w32 = w0.copy()
+    oracle.adamw_step(w32, m32, v32, grad, c)
+    assert abs(np.float64(w32[pick]) - np.float64(w0[pick]) * np.float64(decay)) < 1e-4
