@@ -418,6 +418,8 @@ def resident_bench(torch, L, synth, a):
         "device": info,
         "host_wall_s_timed_region": wall,
     }
+    if nsets > 1:
+        line["same_bytes_copy"] = same_bytes_copy(torch, L, stream, P * step_bytes, nsets, a.steps)
     if accum_ms_list:
         acc_ms = sum(accum_ms_list) / len(accum_ms_list)
         acc_gbps = P * accum_bytes / (acc_ms * 1e-3) / 1e9
@@ -431,6 +433,27 @@ def resident_bench(torch, L, synth, a):
                                             sets[0][1][0][1] if resident_mb else None,
                                             bytes_per_param=step_bytes + accum_bytes)
     return line
+
+
+def same_bytes_copy(torch, L, stream, nbytes, nsets, steps):
+    """The plain copy kernel moving the step's bytes (half read, half
+    written) per launch, rotated over `nsets` buffer pairs like the step's
+    state sets: the floor a launch of this size has, ramp and drain
+    included, when every byte moves once."""
+    half = nbytes // 2 // 4096 * 4096
+    pairs = [(torch.empty(half, dtype=torch.uint8, device="cuda"),
+              torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(nsets)]
+    for src, _ in pairs:
+        src.fill_(1)
+    run = lambda k: L.measure_copy(pairs[k % nsets][0], pairs[k % nsets][1], half)
+    for k in range(5):
+        run(k)
+    torch.cuda.synchronize()
+    ms = timed_events(torch, stream, run, steps)
+    avg = sum(ms) / len(ms)
+    return {"kernel": "copy_kernel", "bytes_per_launch": 2 * half, "rotated_buffer_pairs": nsets,
+            "avg_launch_ms": avg, "median_launch_ms": statistics.median(ms),
+            "min_launch_ms": min(ms), "gbps": 2 * half / (avg * 1e-3) / 1e9}
 
 
 def resident_state(torch, L, synth, w, layout, delta, grad_f32, resident_mb):
@@ -880,8 +903,8 @@ def checkpoint_bench(torch, L, synth, a):
 
 def slot_stream_bench(torch, L, synth, a):
     """The whole 7B shape in host memory, streamed per layer: fp32 master, m
-    and v, or with --q8 int8 moments with row scales (README "Quantization":
-    quantized states stay quantized in RAM)."""
+    and v, or with --q8 int8 moments with row scales, kept as codes in host
+    memory (README "Quantization")."""
     w = synth.WORKLOADS["llama7b_full"]
     hp = synth.HPARAMS
     q8 = a.q8

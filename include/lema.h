@@ -259,10 +259,10 @@ lema_status lema_merge_delta(const lema_merge_seg *segs, int32_t nseg, void *str
 
 /*
  * Quantized optimizer moments and gradient accumulators (LEMA README,
- * "Quantization": opt_state_bits = 8 stores Adam's moments and
- * grad_acc_bits = 8 the gradient accumulators as int8 with one scale per
- * row; both stay quantized and are dequantized only inside the per-layer
- * AdamW step).  The pages give no formula; the format read here is
+ * "Quantization": the opt_state_bits and grad_acc_bits settings of 8 keep
+ * Adam's moments and the gradient accumulators as int8 codes with a scale
+ * per row, widened to fp32 only within the step).  The pages give no
+ * formula; the format read here is
  * symmetric absmax scaling:
  *   - a tensor of numel elements is cut into rows of row_len consecutive
  *     elements, the last row possibly shorter: rows = ceil(numel / row_len)
@@ -310,8 +310,8 @@ typedef struct {
 
 /*
  * One AdamW step with quantized moments and/or a quantized gradient
- * accumulator (LEMA README, "Quantization": the int8 classes are
- * dequantized only inside the per-layer AdamW step).  Per row:
+ * accumulator (LEMA README, "Quantization": int8 state is widened to fp32
+ * within the step and nowhere else).  Per row:
  *   m, v  = dequantized moments (moment_dtype LEMA_STATE_Q8) or the fp32 ones
  *   g     = bf16 widened, the fp32 accumulator, or the dequantized int8 one
  *   the fp32 step of lema_adamw_step, element for element (same arithmetic,
@@ -423,8 +423,8 @@ typedef struct {
     double copy_busy_ms;          /* time at least one copy was running     */
     double wall_ms;               /* first copy start .. last copy end      */
     double last_kernel_ms;        /* duration of the last layer's kernel    */
-    double host_in_ms;            /* staged only: host copies into staging  */
-    double host_out_ms;           /* staged only: host copies out of staging */
+    double host_in_ms;            /* staged only: host copies into the upload ring   */
+    double host_out_ms;           /* staged only: host copies out of the write-back ring */
     double call_ms;               /* host clock over the whole call         */
 } lema_stream_stats;
 
@@ -449,13 +449,19 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
  * lema_slot_stream for host state that is not page-locked: ordinary memory or
  * a memory-mapped file (the disk tier of the LEMA README's "Triple-Buffer
  * Pipeline: Disk -> pinned RAM -> VRAM"; "Selective Full Fine-Tuning": fp32
- * states in RAM with an mmap disk backend).  Layer i moves
- *   caller memory -> page-locked staging[i mod 2] -> slot[i mod 2]
- * and back the same way; `host_threads` host threads (0 = up to 16) do the
- * copies between the caller's memory and the two staging buffers, which the
- * pool allocates on first use (2 x slot_bytes of page-locked memory) and frees
- * with the pool.  The host copies of one layer overlap the DMA and kernel
- * work of the neighbouring layers.  Blocks until every layer is written back.
+ * states in RAM with an mmap disk backend).  Every array moves in pieces of
+ * at most 32 MiB:
+ *   caller memory -> page-locked upload ring -> slot[i mod nslots]
+ *   slot[i mod nslots] -> page-locked write-back ring -> caller memory
+ * The two rings (16 chunks of 32 MiB each, 1 GiB in all) are allocated by
+ * the pool on first use and freed with it.  `host_threads` host threads
+ * (0 = up to 16), split between the two directions, do the copies between
+ * the caller's memory and the rings, piece by piece, so that a layer's first
+ * upload starts after one piece's host copy and a write-back's host copies
+ * follow its DMA.  The calling thread enqueues the uploads and steps; a
+ * second thread of the library enqueues the write-backs and copies them out.
+ * On a single copy stream each layer's write-back is enqueued after the next
+ * layer's uploads.  Blocks until every layer is written back.
  * Same arguments and errors as lema_slot_stream, except that host memory need
  * not be page-locked (no LEMA_ERR_NOT_PINNED); LEMA_ERR_SIZE also for
  * host_threads outside 0..256.
@@ -477,9 +483,9 @@ typedef struct {
 
 /*
  * The slot-pool streaming of lema_slot_stream / lema_slot_stream_staged for
- * quantized host state (LEMA README, "Quantization": optimizer states and
- * accumulators stay quantized in RAM, including the mmap disk backend, and
- * are dequantized only inside the per-layer AdamW step).  Per segment, the
+ * quantized host state (LEMA README, "Quantization": host memory, and the
+ * memory-mapped disk tier, hold int8 codes and row scales, which are widened
+ * to fp32 only on the GPU within the step).  Per segment, the
  * master, the moments (int8 codes and row scales, or fp32) and the gradient
  * (bf16, fp32, or int8 codes and row scales) are copied in, the step of
  * lema_adamw_step_q8 runs on the slot, and the master, the moments and
@@ -488,7 +494,7 @@ typedef struct {
  *   moment_dtype : lema_state_dtype of every segment
  *   staged       : 0 = host arrays are page-locked and copied directly
  *                  (LEMA_ERR_NOT_PINNED otherwise); 1 = any host memory,
- *                  moved through the pool's page-locked staging buffers by
+ *                  moved through the pool's page-locked rings by
  *                  `host_threads` threads (0 = up to 16)
  * args->grad_dtype may be LEMA_GRAD_BF16, LEMA_GRAD_FP32 or LEMA_GRAD_Q8.
  * Errors: as lema_slot_stream, plus LEMA_ERR_DTYPE for an unknown

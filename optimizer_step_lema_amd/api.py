@@ -533,7 +533,7 @@ class AdamwQ8Plan:
 def adamw_step_q8(segments: Sequence[AdamwQ8Segment], *, lr, beta1=0.9, beta2=0.999, eps=1e-8,
                   weight_decay=0.01, step, stream=None) -> None:
     """One AdamW step with int8 moments and/or an int8 gradient accumulator
-    (README "Quantization": dequantized only inside the step)."""
+    (README "Quantization"): the int8 arrays are widened within the step."""
     AdamwQ8Plan(segments).step(lr=lr, beta1=beta1, beta2=beta2, eps=eps,
                                weight_decay=weight_decay, step=step, stream=stream)
 

@@ -76,7 +76,9 @@ void adamw_records(const lema_adamw_seg *segs, int32_t nseg, std::vector<SegRec>
 
 // Run launch(device copy of `bytes`) on the per-device table cache: the
 // table is uploaded unless a byte-identical one is cached, and stays
-// reserved until the launched work on `stream` has finished.
+// reserved until the launched work on `stream` has finished.  `launch` runs
+// with the device's cache locked: it must not call anything that takes that
+// lock again (device state, occupancy_lds_bytes, another launch_on_table).
 lema_status launch_on_table(const std::vector<unsigned char> &bytes, hipStream_t stream,
                             const std::function<hipError_t(const void *)> &launch);
 

@@ -1,8 +1,8 @@
 // lema_q8.hip -- gfx950 kernels of the int8 + per-row-scale path.
 //
-// LEMA README, "Quantization": with opt_state_bits = 8 and grad_acc_bits = 8
-// Adam's moments and the gradient accumulators stay int8 with one scale per
-// row and are dequantized only inside the per-layer AdamW step.  The storage
+// LEMA README, "Quantization": 8-bit settings for the optimizer state and
+// the gradient accumulator keep Adam's moments and the accumulators as int8
+// codes with a scale per row, widened to fp32 only within the step.  The storage
 // (symmetric absmax scaling, 127 levels per sign) is stated in
 // include/lema.h.
 //

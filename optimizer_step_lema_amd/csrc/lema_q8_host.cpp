@@ -1,9 +1,9 @@
 // lema_q8_host.cpp -- host side of the int8 + per-row-scale entry points of
 // include/lema.h: validation, row-team sizing, launch tables and launches.
 //
-// Method: LEMA README, "Quantization" (opt_state_bits = 8 and grad_acc_bits
-// = 8: int8 moments and accumulators with per-row scales, dequantized only
-// inside the per-layer AdamW step).
+// Method: LEMA README, "Quantization" (8-bit optimizer state and gradient
+// accumulators: int8 codes with a scale per row, widened to fp32 within the
+// step).
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -265,14 +265,16 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
     // starves small launches such as the LoRA adapters).  The 1024-lane
     // ones fit once per CU anyway.  Accumulation and conversions move less
     // per workgroup and keep full occupancy.
+    // (the reservations are looked up here: the launch callback below runs
+    // with the device's table cache locked)
+    uint32_t lds[3];
+    for (QRows rows : {kQRowsTeam, kQRowsPacked, kQRowsWave})
+        lds[rows] = occupancy_lds_bytes(adamw_q8_kernel_fn(mom_q8, qg, with_delta, kQBlock, rows),
+                                        kQ8StepWorkgroupsPerCu);
     return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks,
                                                      int block, QRows rows) {
-        const uint32_t lds = block == kQBlock
-                                 ? occupancy_lds_bytes(adamw_q8_kernel_fn(mom_q8, qg, with_delta,
-                                                                          block, rows),
-                                                       kQ8StepWorkgroupsPerCu)
-                                 : 0;
-        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, rows, c, hs, lds);
+        return launch_adamw_q8(table, n, blocks, mom_q8, qg, with_delta, block, rows, c, hs,
+                               block == kQBlock ? lds[rows] : 0);
     });
 }
 

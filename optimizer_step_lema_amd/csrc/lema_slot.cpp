@@ -24,14 +24,17 @@
 // with its host address, its offset in the slot and whether it is copied in,
 // out or both, plus the launch of the layer's step on the slot.  fp32 state
 // (lema_slot_stream*) and int8 state with row scales (lema_slot_stream_q8,
-// README "Quantization": quantized states stay quantized in RAM) differ
+// README "Quantization": host memory holds the codes and scales) differ
 // only in their plans.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <atomic>
 #include <chrono>
+#include <condition_variable>
 #include <cstdlib>
 #include <cstring>
+#include <deque>
 #include <functional>
 #include <mutex>
 #include <thread>
@@ -52,8 +55,8 @@ struct lema_slot_pool {
     hipStream_t copy = nullptr;
     hipStream_t compute = nullptr;
     hipStream_t writeback = nullptr;  // NULL: D2H copies share the copy stream
-    std::vector<hipEvent_t> events;   // 6 per layer, grown on demand, reused
-    char *staging[2] = {nullptr, nullptr};   // page-locked, slot_bytes each (staged path)
+    std::vector<hipEvent_t> events;   // grown on demand, reused by later calls
+    char *ring[2] = {nullptr, nullptr};   // staged path: page-locked upload and write-back rings
     std::mutex mu;
 };
 
@@ -222,7 +225,7 @@ enum { EV_H2D_BEGIN = 0, EV_H2D_END, EV_K_BEGIN, EV_K_END, EV_D2H_BEGIN, EV_D2H_
 // GPU; the call then takes its ordinary HIP-failure exit.
 struct FaultInjector {
     long fail_at = 0;    // 0: off
-    long count = 0;
+    std::atomic<long> count{0};
     FaultInjector() {
         const char *v = std::getenv("LEMA_FAULT_INJECT");
         if (v != nullptr && std::strncmp(v, "copy:", 5) == 0) fail_at = std::atol(v + 5);
@@ -236,30 +239,26 @@ hipError_t copy_async(void *dst, const void *src, size_t bytes, hipMemcpyKind ki
     return hipMemcpyAsync(dst, src, bytes, kind, s);
 }
 
-// Copies of a plan's `in` arrays from `host_side` (host arrays, or a staging
-// buffer laid out like the slot when non-null) into the slot.
-hipError_t enqueue_upload(const LayerPlan &plan, char *slot, char *staging, hipStream_t s,
-                          double *bytes, FaultInjector *fi) {
+// Copies of a plan's `in` arrays from the host arrays into the slot.
+hipError_t enqueue_upload(const LayerPlan &plan, char *slot, hipStream_t s, double *bytes,
+                          FaultInjector *fi) {
     hipError_t e = hipSuccess;
     for (const Xfer &x : plan.xfers) {
         if (!x.in || x.bytes == 0) continue;
-        const char *src = staging ? staging + x.off : x.host;
-        e = copy_async(slot + x.off, src, x.bytes, hipMemcpyHostToDevice, s, fi);
+        e = copy_async(slot + x.off, x.host, x.bytes, hipMemcpyHostToDevice, s, fi);
         if (e != hipSuccess) return e;
         *bytes += double(x.bytes);
     }
     return e;
 }
 
-// Copies of a plan's `out` arrays from the slot to the host arrays (or to a
-// staging buffer laid out like the slot when non-null).
-hipError_t enqueue_writeback(const LayerPlan &plan, char *slot, char *staging, hipStream_t s,
-                             double *bytes, FaultInjector *fi) {
+// Copies of a plan's `out` arrays from the slot back to the host arrays.
+hipError_t enqueue_writeback(const LayerPlan &plan, char *slot, hipStream_t s, double *bytes,
+                             FaultInjector *fi) {
     hipError_t e = hipSuccess;
     for (const Xfer &x : plan.xfers) {
         if (!x.out || x.bytes == 0) continue;
-        char *dst = staging ? staging + x.off : x.host;
-        e = copy_async(dst, slot + x.off, x.bytes, hipMemcpyDeviceToHost, s, fi);
+        e = copy_async(x.host, slot + x.off, x.bytes, hipMemcpyDeviceToHost, s, fi);
         if (e != hipSuccess) return e;
         *bytes += double(x.bytes);
     }
@@ -317,44 +316,104 @@ struct CopyItem {
     size_t bytes;
 };
 
-// memcpy of a list of ranges split evenly over `threads` host threads.
-void parallel_copy(const std::vector<CopyItem> &items, int threads) {
-    size_t total = 0;
-    for (const CopyItem &c : items) total += c.bytes;
-    if (threads <= 1 || total < (size_t(8) << 20)) {
-        for (const CopyItem &c : items) std::memcpy(c.dst, c.src, c.bytes);
-        return;
+// A fixed set of host threads for memcpy.  copy(items) splits the items'
+// bytes evenly over the threads, the caller's included, and returns when all
+// are copied.  One caller at a time.
+class CopyWorkers {
+public:
+    explicit CopyWorkers(int threads) : n_(std::max(1, threads)) {
+        for (int t = 1; t < n_; ++t) threads_.emplace_back([this, t] { loop(t); });
     }
-    const size_t share = ((total + threads - 1) / threads + 63) & ~size_t(63);
-    auto run = [&](size_t begin, size_t end) {
+    ~CopyWorkers() {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            stop_ = true;
+            ++gen_;
+        }
+        cv_.notify_all();
+        for (std::thread &t : threads_) t.join();
+    }
+    void copy(const CopyItem *items, size_t nitems) {
+        size_t total = 0;
+        for (size_t i = 0; i < nitems; ++i) total += items[i].bytes;
+        if (n_ == 1 || total < (size_t(4) << 20)) {
+            for (size_t i = 0; i < nitems; ++i) std::memcpy(items[i].dst, items[i].src, items[i].bytes);
+            return;
+        }
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            items_ = items;
+            nitems_ = nitems;
+            total_ = total;
+            share_ = ((total + n_ - 1) / n_ + 63) & ~size_t(63);
+            pending_ = n_ - 1;
+            ++gen_;
+        }
+        cv_.notify_all();
+        run(0);
+        std::unique_lock<std::mutex> lk(mu_);
+        done_.wait(lk, [this] { return pending_ == 0; });
+    }
+
+private:
+    // thread t's share: bytes [t*share, (t+1)*share) of the items laid end to end
+    void run(int t) {
+        const size_t begin = size_t(t) * share_, end = std::min(total_, begin + share_);
         size_t pos = 0;
-        for (const CopyItem &c : items) {
+        for (size_t i = 0; i < nitems_ && pos < end; ++i) {
+            const CopyItem &c = items_[i];
             const size_t lo = std::max(begin, pos), hi = std::min(end, pos + c.bytes);
             if (lo < hi)
                 std::memcpy(static_cast<char *>(c.dst) + (lo - pos),
                             static_cast<const char *>(c.src) + (lo - pos), hi - lo);
             pos += c.bytes;
-            if (pos >= end) break;
         }
-    };
-    std::vector<std::thread> pool;
-    for (int t = 1; t < threads; ++t) {
-        const size_t b = size_t(t) * share;
-        if (b >= total) break;
-        pool.emplace_back(run, b, std::min(total, b + share));
     }
-    run(0, std::min(total, share));
-    for (std::thread &t : pool) t.join();
-}
+    void loop(int t) {
+        uint64_t seen = 0;
+        std::unique_lock<std::mutex> lk(mu_);
+        for (;;) {
+            cv_.wait(lk, [&] { return gen_ != seen; });
+            seen = gen_;
+            if (stop_) return;
+            lk.unlock();
+            run(t);
+            lk.lock();
+            if (--pending_ == 0) done_.notify_one();
+        }
+    }
 
-// Items moving a plan's `in` arrays from the caller's memory into staging
-// laid out like the slot, or its `out` arrays back from staging.
-void staging_items(const LayerPlan &plan, char *staging, bool inbound, std::vector<CopyItem> *out) {
+    const int n_;
+    std::vector<std::thread> threads_;
+    std::mutex mu_;
+    std::condition_variable cv_, done_;
+    uint64_t gen_ = 0;
+    bool stop_ = false;
+    const CopyItem *items_ = nullptr;
+    size_t nitems_ = 0, total_ = 0, share_ = 0;
+    int pending_ = 0;
+};
+
+// The staged path moves every array in pieces of at most one ring chunk
+// through two page-locked rings, one per direction, so that a layer's first
+// upload starts after one chunk's host copy and a write-back's host copies
+// follow its DMA chunk by chunk.
+constexpr size_t kStageChunk = size_t(32) << 20;
+constexpr int kStageRing = 16;              // chunks per ring (512 MiB)
+
+// One piece of a layer's transfer: part of one array, at most one chunk.
+struct Piece {
+    char *host;
+    size_t slot_off;
+    size_t bytes;
+};
+
+void plan_pieces(const LayerPlan &plan, bool inbound, std::vector<Piece> *out) {
     out->clear();
     for (const Xfer &x : plan.xfers) {
-        if (x.bytes == 0) continue;
-        if (inbound && x.in) out->push_back({staging + x.off, x.host, x.bytes});
-        if (!inbound && x.out) out->push_back({x.host, staging + x.off, x.bytes});
+        if (x.bytes == 0 || (inbound ? !x.in : !x.out)) continue;
+        for (size_t o = 0; o < x.bytes; o += kStageChunk)
+            out->push_back({x.host + o, x.off + o, std::min(kStageChunk, x.bytes - o)});
     }
 }
 
@@ -447,7 +506,7 @@ lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     auto copy_back = [&](int j) -> lema_status {
         hipError_t err = hipStreamWaitEvent(d2h_stream, ev(j, EV_K_END), 0);
         if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_BEGIN), d2h_stream);
-        if (err == hipSuccess) err = enqueue_writeback(plans[j], slot_of(j), nullptr, d2h_stream, &d2h_bytes, &fi);
+        if (err == hipSuccess) err = enqueue_writeback(plans[j], slot_of(j), d2h_stream, &d2h_bytes, &fi);
         if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_END), d2h_stream);
         return err == hipSuccess ? LEMA_OK : hip_failed(err);
     };
@@ -459,7 +518,7 @@ lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         if (pool->writeback && i >= pool->nslots)
             e = hipStreamWaitEvent(pool->copy, ev(i - pool->nslots, EV_D2H_END), 0);
         if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
-        if (e == hipSuccess) e = enqueue_upload(plans[i], slot_of(i), nullptr, pool->copy, &h2d_bytes, &fi);
+        if (e == hipSuccess) e = enqueue_upload(plans[i], slot_of(i), pool->copy, &h2d_bytes, &fi);
         if (e == hipSuccess) e = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
         if (e != hipSuccess) return drain(pool, hip_failed(e));
 
@@ -491,10 +550,64 @@ lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     return LEMA_OK;
 }
 
-// Pageable or memory-mapped host arrays: each layer goes caller memory ->
-// staging[i % 2] -> slot[i % 2] -> staging[i % 2] -> caller memory.  Layer
-// i + 2 reuses both only after the host has copied layer i out of staging,
-// which itself waited for its write-back.
+// Copy intervals and kernel times of a staged call from its events: every
+// piece has a begin and an end event, so gaps between pieces count as idle.
+void fill_stats_pieces(lema_slot_pool *pool, int32_t nlayers, size_t ev_layer, size_t ev_in,
+                       size_t n_in, size_t ev_out, size_t n_out, double h2d_bytes,
+                       double d2h_bytes, lema_stream_stats *out) {
+    auto ev = [&](size_t i) { return pool->events[i]; };
+    lema_stream_stats s{};
+    s.h2d_bytes = h2d_bytes;
+    s.d2h_bytes = d2h_bytes;
+    const hipEvent_t t0 = ev(ev_in);            // begin of the first upload piece
+    std::vector<std::pair<float, float>> busy;
+    float b = 0.f, en = 0.f, ms = 0.f;
+    auto piece = [&](size_t base, size_t k, double *sum) {
+        if (hipEventElapsedTime(&b, t0, ev(base + 2 * k)) == hipSuccess &&
+            hipEventElapsedTime(&en, t0, ev(base + 2 * k + 1)) == hipSuccess) {
+            *sum += en - b;
+            busy.emplace_back(b, en);
+        }
+    };
+    for (size_t k = 0; k < n_in; ++k) piece(ev_in, k, &s.h2d_ms);
+    for (size_t k = 0; k < n_out; ++k) piece(ev_out, k, &s.d2h_ms);
+    for (int32_t i = 0; i < nlayers; ++i) {
+        if (hipEventElapsedTime(&ms, ev(ev_layer + 4 * size_t(i) + 1),
+                                ev(ev_layer + 4 * size_t(i) + 2)) == hipSuccess) {
+            s.kernel_ms += ms;
+            if (i == nlayers - 1) s.last_kernel_ms = ms;
+        }
+    }
+    std::sort(busy.begin(), busy.end());
+    float lo = 0.f, hi = -1.f;
+    for (const auto &iv : busy) {
+        if (iv.first > hi) {
+            if (hi > lo) s.copy_busy_ms += hi - lo;
+            lo = iv.first;
+            hi = iv.second;
+        } else if (iv.second > hi) {
+            hi = iv.second;
+        }
+    }
+    if (hi > lo) s.copy_busy_ms += hi - lo;
+    if (hipEventElapsedTime(&ms, t0, ev(ev_layer + 4 * size_t(nlayers - 1) + 3)) == hipSuccess)
+        s.wall_ms = ms;
+    *out = s;
+}
+
+// Pageable or memory-mapped host arrays.  Every array moves in pieces of at
+// most one chunk: caller memory -> upload ring -> slot, and slot -> write-
+// back ring -> caller memory.  The calling thread copies pieces into the
+// upload ring and enqueues their uploads and each layer's step; a second
+// thread enqueues the write-backs and copies their pieces out as they land.
+//
+//   - A ring chunk is reused only after its previous piece is done: its
+//     upload finished, or its write-back finished and was copied out.
+//   - Layer i's uploads into slot i mod nslots wait for the write-back of
+//     layer i - nslots out of that slot.
+//   - On a single copy stream a layer's write-back is enqueued after the
+//     next layer's uploads, so the copy engine never waits for the step in
+//     between (the step of layer i runs while layer i+1 uploads).
 lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans,
                        int32_t host_threads, lema_stream_stats *stats) {
     const int32_t nlayers = int32_t(plans.size());
@@ -507,81 +620,210 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         const unsigned hc = std::thread::hardware_concurrency();
         threads = int(std::min(16u, hc == 0 ? 4u : hc));
     }
-    const auto call_start = std::chrono::steady_clock::now();
+    const int threads_in = std::max(1, threads / 2), threads_out = std::max(1, threads - threads_in);
+    using clock = std::chrono::steady_clock;
+    const auto call_start = clock::now();
 
     std::lock_guard<std::mutex> lock(pool->mu);
     int cur = 0;
     hipError_t e = hipGetDevice(&cur);
     if (e != hipSuccess) return hip_failed(e);
     if (cur != pool->device) return LEMA_ERR_HIP;
-    for (int b = 0; b < 2; ++b) {
-        if (pool->staging[b] == nullptr) {
-            e = hipHostMalloc(reinterpret_cast<void **>(&pool->staging[b]), pool->slot_bytes,
+    for (char *&r : pool->ring) {
+        if (r == nullptr) {
+            e = hipHostMalloc(reinterpret_cast<void **>(&r), kStageChunk * kStageRing,
                               hipHostMallocDefault);
             if (e != hipSuccess) {
-                pool->staging[b] = nullptr;
+                r = nullptr;
                 return hip_failed(e);
             }
         }
     }
-    lema_status st = ensure_events(pool, size_t(nlayers) * EV_PER_LAYER);
-    if (st != LEMA_OK) return st;
-
-    auto ev = [&](int layer, int kind) { return pool->events[size_t(layer) * EV_PER_LAYER + kind]; };
-    double h2d_bytes = 0, d2h_bytes = 0, in_ms = 0, out_ms = 0;
-    FaultInjector fi;
-    hipStream_t d2h_stream = pool->writeback ? pool->writeback : pool->copy;
-    std::vector<CopyItem> items;
-    using clock = std::chrono::steady_clock;
-
-    auto stage_in_and_enqueue = [&](int i) -> lema_status {
-        const int b = i % 2;
-        char *slot = pool->base + size_t(b) * pool->slot_bytes;
-        staging_items(plans[i], pool->staging[b], true, &items);
-        const auto t0 = clock::now();
-        parallel_copy(items, threads);
-        in_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
-
-        hipError_t err = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
-        if (err == hipSuccess) err = enqueue_upload(plans[i], slot, pool->staging[b], pool->copy, &h2d_bytes, &fi);
-        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
-        if (err == hipSuccess) err = hipStreamWaitEvent(pool->compute, ev(i, EV_H2D_END), 0);
-        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
-        if (err != hipSuccess) return hip_failed(err);
-        lema_status s2 = plans[i].launch(slot, pool->compute);
-        if (s2 != LEMA_OK) return s2;
-        err = hipEventRecord(ev(i, EV_K_END), pool->compute);
-        if (err == hipSuccess) err = hipStreamWaitEvent(d2h_stream, ev(i, EV_K_END), 0);
-        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_D2H_BEGIN), d2h_stream);
-        if (err == hipSuccess) err = enqueue_writeback(plans[i], slot, pool->staging[b], d2h_stream, &d2h_bytes, &fi);
-        if (err == hipSuccess) err = hipEventRecord(ev(i, EV_D2H_END), d2h_stream);
-        return err == hipSuccess ? LEMA_OK : hip_failed(err);
-    };
-    auto wait_and_stage_out = [&](int i) -> lema_status {
-        hipError_t err = hipEventSynchronize(ev(i, EV_D2H_END));
-        if (err != hipSuccess) return hip_failed(err);
-        staging_items(plans[i], pool->staging[i % 2], false, &items);
-        const auto t0 = clock::now();
-        parallel_copy(items, threads);
-        out_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+    std::vector<std::vector<Piece>> in_p(nlayers), out_p(nlayers);
+    std::vector<size_t> first_in(nlayers), first_out(nlayers);
+    size_t n_in = 0, n_out = 0;
+    for (int32_t i = 0; i < nlayers; ++i) {
+        plan_pieces(plans[i], true, &in_p[i]);
+        plan_pieces(plans[i], false, &out_p[i]);
+        first_in[i] = n_in;
+        first_out[i] = n_out;
+        n_in += in_p[i].size();
+        n_out += out_p[i].size();
+    }
+    if (n_in == 0 || n_out == 0) {                 // only empty segments: nothing moves
+        if (stats) *stats = lema_stream_stats{};
         return LEMA_OK;
+    }
+    // events: per layer {uploads done, step begin, step end, write-back done},
+    // then a begin/end pair per upload piece and per write-back piece
+    const size_t ev_layer = 0, ev_in = 4 * size_t(nlayers), ev_out = ev_in + 2 * n_in;
+    lema_status st = ensure_events(pool, ev_out + 2 * n_out);
+    if (st != LEMA_OK) return st;
+    auto lev = [&](int32_t i, int k) { return pool->events[ev_layer + 4 * size_t(i) + k]; };
+    auto iev = [&](size_t g, int k) { return pool->events[ev_in + 2 * g + k]; };
+    auto oev = [&](size_t g, int k) { return pool->events[ev_out + 2 * g + k]; };
+    auto slot_of = [&](int32_t i) { return pool->base + size_t(i % pool->nslots) * pool->slot_bytes; };
+
+    const bool duplex = pool->writeback != nullptr;
+    hipStream_t d2h_stream = duplex ? pool->writeback : pool->copy;
+    FaultInjector fi;
+
+    // progress shared by the two threads
+    std::mutex m;
+    std::condition_variable cv;
+    int32_t steps_enqueued = 0;     // layers whose uploads and step are enqueued
+    int32_t backs_enqueued = 0;     // layers whose write-backs are enqueued
+    bool abort = false;
+    lema_status out_status = LEMA_OK;
+    double h2d_bytes = 0, d2h_bytes = 0, in_ms = 0, out_ms = 0;
+
+    auto fail = [&](lema_status s2) {
+        std::lock_guard<std::mutex> lk(m);
+        abort = true;
+        return s2;
     };
 
-    for (int i = 0; i < std::min(nlayers, 2); ++i) {
-        st = stage_in_and_enqueue(i);
-        if (st != LEMA_OK) return drain(pool, st);
-    }
-    for (int i = 0; i < nlayers; ++i) {
-        st = wait_and_stage_out(i);
-        if (st != LEMA_OK) return drain(pool, st);
-        if (i + 2 < nlayers) {
-            st = stage_in_and_enqueue(i + 2);
-            if (st != LEMA_OK) return drain(pool, st);
+    std::thread outbound([&] {
+        CopyWorkers workers(threads_out);
+        struct Pending { size_t g; char *host; char *chunk; size_t bytes; };
+        std::deque<Pending> fifo;
+        size_t next = 0;
+        auto complete_oldest = [&]() -> lema_status {
+            const Pending p = fifo.front();
+            fifo.pop_front();
+            hipError_t err = hipEventSynchronize(oev(p.g, 1));
+            if (err != hipSuccess) return hip_failed(err);
+            const CopyItem item{p.host, p.chunk, p.bytes};
+            const auto t0 = clock::now();
+            workers.copy(&item, 1);
+            out_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+            return LEMA_OK;
+        };
+        lema_status s2 = LEMA_OK;
+        for (int32_t j = 0; j < nlayers && s2 == LEMA_OK; ++j) {
+            {
+                // the step of layer j enqueued, and on a single copy stream also
+                // the uploads of layer j + 1
+                std::unique_lock<std::mutex> lk(m);
+                const int32_t need = (duplex || j == nlayers - 1) ? j + 1 : j + 2;
+                cv.wait(lk, [&] { return abort || steps_enqueued >= need; });
+                if (abort) break;
+            }
+            hipError_t err = hipStreamWaitEvent(d2h_stream, lev(j, 2), 0);
+            if (err != hipSuccess) { s2 = hip_failed(err); break; }
+            char *slot = slot_of(j);
+            for (size_t k = 0; k < out_p[j].size(); ++k) {
+                if (fifo.size() == size_t(kStageRing)) {
+                    s2 = complete_oldest();
+                    if (s2 != LEMA_OK) break;
+                }
+                const Piece &p = out_p[j][k];
+                const size_t g = first_out[j] + k;
+                char *chunk = pool->ring[1] + (next++ % kStageRing) * kStageChunk;
+                err = hipEventRecord(oev(g, 0), d2h_stream);
+                if (err == hipSuccess)
+                    err = copy_async(chunk, slot + p.slot_off, p.bytes, hipMemcpyDeviceToHost,
+                                     d2h_stream, &fi);
+                if (err == hipSuccess) err = hipEventRecord(oev(g, 1), d2h_stream);
+                if (err != hipSuccess) { s2 = hip_failed(err); break; }
+                d2h_bytes += double(p.bytes);
+                fifo.push_back({g, p.host, chunk, p.bytes});
+            }
+            if (s2 != LEMA_OK) break;
+            err = hipEventRecord(lev(j, 3), d2h_stream);
+            if (err != hipSuccess) { s2 = hip_failed(err); break; }
+            {
+                std::lock_guard<std::mutex> lk(m);
+                backs_enqueued = j + 1;
+            }
+            cv.notify_all();
         }
+        while (s2 == LEMA_OK && !fifo.empty()) {
+            bool stop;
+            {
+                std::lock_guard<std::mutex> lk(m);
+                stop = abort;
+            }
+            if (stop) break;
+            s2 = complete_oldest();
+        }
+        if (s2 != LEMA_OK) {
+            std::lock_guard<std::mutex> lk(m);
+            abort = true;
+            out_status = s2;
+        }
+        cv.notify_all();
+    });
+
+    // this thread: uploads and steps
+    st = LEMA_OK;
+    {
+        CopyWorkers workers(threads_in);
+        std::vector<long> chunk_piece(kStageRing, -1);     // last upload piece in each chunk
+        size_t next = 0;
+        for (int32_t i = 0; i < nlayers && st == LEMA_OK; ++i) {
+            {
+                std::lock_guard<std::mutex> lk(m);
+                if (abort) break;
+            }
+            if (i >= pool->nslots) {
+                // the slot's previous occupant is written back first
+                std::unique_lock<std::mutex> lk(m);
+                cv.wait(lk, [&] { return abort || backs_enqueued >= i - pool->nslots + 1; });
+                if (abort) break;
+                lk.unlock();
+                e = hipStreamWaitEvent(pool->copy, lev(i - pool->nslots, 3), 0);
+                if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+            }
+            char *slot = slot_of(i);
+            for (size_t k = 0; k < in_p[i].size(); ++k) {
+                const Piece &p = in_p[i][k];
+                const size_t g = first_in[i] + k;
+                const size_t c = next++ % kStageRing;
+                if (chunk_piece[c] >= 0) {
+                    e = hipEventSynchronize(iev(size_t(chunk_piece[c]), 1));
+                    if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+                }
+                char *chunk = pool->ring[0] + c * kStageChunk;
+                const CopyItem item{chunk, p.host, p.bytes};
+                const auto t0 = clock::now();
+                workers.copy(&item, 1);
+                in_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
+                e = hipEventRecord(iev(g, 0), pool->copy);
+                if (e == hipSuccess)
+                    e = copy_async(slot + p.slot_off, chunk, p.bytes, hipMemcpyHostToDevice,
+                                   pool->copy, &fi);
+                if (e == hipSuccess) e = hipEventRecord(iev(g, 1), pool->copy);
+                if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+                chunk_piece[c] = long(g);
+                h2d_bytes += double(p.bytes);
+            }
+            if (st != LEMA_OK) break;
+            e = hipEventRecord(lev(i, 0), pool->copy);
+            if (e == hipSuccess) e = hipStreamWaitEvent(pool->compute, lev(i, 0), 0);
+            if (e == hipSuccess) e = hipEventRecord(lev(i, 1), pool->compute);
+            if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+            st = plans[i].launch(slot, pool->compute);
+            if (st != LEMA_OK) { fail(st); break; }
+            e = hipEventRecord(lev(i, 2), pool->compute);
+            if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+            {
+                std::lock_guard<std::mutex> lk(m);
+                steps_enqueued = i + 1;
+            }
+            cv.notify_all();
+        }
+        cv.notify_all();
     }
+    outbound.join();
+    if (st == LEMA_OK) st = out_status;
+    if (st != LEMA_OK) return drain(pool, st);
+    e = hipEventSynchronize(lev(nlayers - 1, 3));
+    if (e != hipSuccess) return drain(pool, hip_failed(e));
 
     if (stats) {
-        fill_stats(pool, nlayers, h2d_bytes, d2h_bytes, stats);
+        fill_stats_pieces(pool, nlayers, ev_layer, ev_in, n_in, ev_out, n_out, h2d_bytes,
+                          d2h_bytes, stats);
         stats->host_in_ms = in_ms;
         stats->host_out_ms = out_ms;
         stats->call_ms = std::chrono::duration<double, std::milli>(clock::now() - call_start).count();
@@ -635,7 +877,7 @@ lema_status lema_slot_pool_destroy(lema_slot_pool *pool) {
             (void)hipEventDestroy(ev);
         }
         pool->events.clear();
-        for (char *&p : pool->staging) {
+        for (char *&p : pool->ring) {
             if (p) (void)hipHostFree(p);
             p = nullptr;
         }

@@ -124,8 +124,9 @@ def test_ragged_segments(L, offset, grad_f32):
     check_segments(segs, snaps, oracle_consts(HP, 37))
 
 
-def test_many_segments_cross_lds_windows(L):
-    """More segments than one LDS window, with empty ones in between."""
+def test_many_segments_with_empty_ones(L):
+    """300 segments of mixed sizes in one call, empty ones in between: the
+    binary search over the launch table's tile prefix sums finds each."""
     rng = np.random.default_rng(3)
     sizes = [int(x) for x in rng.choice([0, 1, 17, 2048, 5000, 40000], size=300)]
     segs, snaps = build_segments(L, sizes, 11, delta=set(range(0, 300, 3)))
@@ -532,14 +533,16 @@ def test_concurrent_host_threads(L):
 
 
 def test_step_lds_reservation(L):
-    """The step reserves LDS it does not use so that about 13 of its
-    workgroups (10 with >= 4 resident micro-batches) share a CU."""
+    """The step reserves LDS it does not use, in whole allocation granules,
+    so that 12 of its workgroups (9 with >= 4 resident micro-batches) share
+    a CU (test_gpu_occupancy.py measures the counts)."""
     info = L.device_info()
     lds, res, res_mb = info["lds_per_cu"], info["step_lds_reserved"], \
         info["step_lds_reserved_8_microbatches"]
+    g = L.step_occupancy(0)["lds_granule"]
     assert lds >= 64 * 1024, info
-    assert lds // res == 13 and lds // res_mb == 10, info
-    assert res % 256 == 0 and res_mb % 256 == 0 and res_mb <= 65536
+    assert res % g == 0 and res_mb % g == 0 and res_mb <= 65536, info
+    assert lds // res == 12 and lds // res_mb == 9, info
 
 
 def test_plans_match_direct_calls(L):

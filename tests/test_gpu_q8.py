@@ -1,8 +1,8 @@
 """GPU parity of the int8 + per-row-scale path against the CPU oracle.
 
-LEMA README, "Quantization": int8 moments (opt_state_bits = 8) and int8
-gradient accumulators (grad_acc_bits = 8) with one scale per row,
-dequantized only inside the per-layer AdamW step.  Initial int8 state is
+int8 moments and int8 gradient accumulators with a scale per row, widened
+to fp32 within the step alone (LEMA README, "Quantization": the 8-bit
+optimizer-state and accumulator settings).  Initial int8 state is
 quantized by the oracle on the host and uploaded, so every comparison here
 checks the HIP path against oracle-made inputs and oracle-made outputs.  The
 bar is bit-exact for codes, scales (NaN compared as a class), the fp32

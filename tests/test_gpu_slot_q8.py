@@ -1,9 +1,9 @@
 """GPU tests of slot-pool streaming with quantized host state
 (lema_slot_stream_q8).
 
-LEMA README, "Quantization": optimizer states and gradient accumulators stay
-quantized in RAM (including the mmap disk backend) and are dequantized only
-inside the per-layer AdamW step.  Host-resident fp32 master weights, int8
+int8 moments and accumulators are kept as codes plus row scales in host
+memory (and the memory-mapped tier) and widened only inside the step (LEMA
+README, "Quantization").  Host-resident fp32 master weights, int8
 moments with row scales and bf16 gradients (or int8 accumulators) stream
 through two HBM slots; every layer's results, copied back to the host, must
 equal the oracle's on the same bytes.

@@ -1,8 +1,8 @@
 """Pins of the oracle's int8 + per-row-scale storage and the quantized step.
 
-LEMA README, "Quantization": with opt_state_bits = 8 and grad_acc_bits = 8
-the Adam moments and the gradient accumulators are kept as int8 with one
-scale per row and dequantized only inside the per-layer AdamW step.  The
+LEMA README, "Quantization": the 8-bit optimizer-state and accumulator
+settings hold Adam's moments and the gradient accumulators as int8 codes
+with a scale per row, widened to fp32 within the step alone.  The
 pages name the format but print no formula; the reading pinned here is
 symmetric absmax scaling with 127 levels per sign (stated in full in
 ``oracle/lema_oracle.c``).  Every test names the mistake it would catch.
