@@ -450,10 +450,10 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
  * a memory-mapped file (the disk tier of the LEMA README's "Triple-Buffer
  * Pipeline: Disk -> pinned RAM -> VRAM"; "Selective Full Fine-Tuning": fp32
  * states in RAM with an mmap disk backend).  Every array moves in pieces of
- * at most 32 MiB:
+ * at most 128 MiB:
  *   caller memory -> page-locked upload ring -> slot[i mod nslots]
  *   slot[i mod nslots] -> page-locked write-back ring -> caller memory
- * The two rings (16 chunks of 32 MiB each, 1 GiB in all) are allocated by
+ * The two rings (16 chunks of 128 MiB each, 4 GiB in all) are allocated by
  * the pool on first use and freed with it.  `host_threads` host threads
  * (0 = up to 16), split between the two directions, do the copies between
  * the caller's memory and the rings, piece by piece, so that a layer's first

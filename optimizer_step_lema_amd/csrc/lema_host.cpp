@@ -418,7 +418,27 @@ uint32_t lds_per_workgroup(int lds_per_cu, int per_cu) {
     return std::min<uint32_t>(k * kLdsGranule, 65536u);
 }
 
+// Workgroups of `lanes` lanes of kernel `fn` that fit one CU by registers
+// and static LDS alone.
+std::mutex g_occupancy_mu;
+std::vector<std::pair<const void *, int>> g_occupancy;
+
 }  // namespace
+
+int compute_units() {
+    DeviceState *d = nullptr;
+    return device_state(&d, nullptr) == LEMA_OK ? d->cu_count : 0;
+}
+
+int register_occupancy(const void *fn, int lanes) {
+    std::lock_guard<std::mutex> lock(g_occupancy_mu);
+    for (const auto &e : g_occupancy)
+        if (e.first == fn) return e.second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, lanes, 0) != hipSuccess) n = 0;
+    g_occupancy.emplace_back(fn, n);
+    return n;
+}
 
 uint32_t occupancy_lds_bytes(const void *fn, int workgroups_per_cu) {
     DeviceState *d = nullptr;

@@ -98,6 +98,11 @@ lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t strea
 // kernel's static LDS is subtracted and the total kept to whole allocation
 // granules (0 if the device or the kernel cannot be queried).
 uint32_t occupancy_lds_bytes(const void *fn, int workgroups_per_cu);
+// Workgroups of `lanes` lanes of kernel `fn` that its registers and static
+// LDS alone let share a CU (0 if the runtime cannot tell); cached per kernel.
+int register_occupancy(const void *fn, int lanes);
+// Compute units of the current device (0 if it cannot be queried).
+int compute_units();
 // Workgroups of the fp32 AdamW step allowed per CU when it reads `nmb`
 // resident micro-batches (0 for the other gradient modes), and the dynamic
 // LDS its kernel reserves for that.

@@ -116,8 +116,19 @@ constexpr int32_t kQPacked = 2;
 // row, reached through row-sized buffer resources (lema_q8.hip, wave rows).
 constexpr int32_t kQWave = 4;
 
-// Kernel family of a launch group: row teams, packed rows or wave rows.
-enum QRows : int { kQRowsTeam = 0, kQRowsPacked = 1, kQRowsWave = 2 };
+// Kernel family of a launch group: row teams, packed rows or wave rows; or,
+// for the step, mixed: packed-row and wave-row records in one launch of
+// kQBlock-lane workgroups, each workgroup taking its record's path, with
+// wave rows of up to kQMixedWaveChunks chunks per lane (rows of up to
+// 11,264 elements, which other launches put in kQBlockWide-lane
+// workgroups).  11 chunks keep the mixed kernel at 167 VGPRs or fewer for
+// the common gradient kinds, within the 3 workgroups per CU of the step's
+// occupancy cap; 12 took it to 178.  One launch lets the families' workgroups fill each other's
+// tails instead of running one group after another.
+enum QRows : int { kQRowsTeam = 0, kQRowsPacked = 1, kQRowsWave = 2, kQRowsMixed = 3 };
+constexpr int kQMixedWaveChunks = 11;
+// Records of a mixed launch carry this flag (with kQPacked or kQWave).
+constexpr int32_t kQMixed = 8;
 
 // How the int8 step reads the moments and the gradient.
 enum QGrad : int { kQGradBf16 = 0, kQGradF32 = 1, kQGradQ8 = 2 };

@@ -721,7 +721,8 @@ struct AdamwRows {
         }
     }
 
-    // Wave rows (see WaveRow).
+    // Wave rows (see WaveRow), with up to kCW chunks per lane.
+    template <int kCW>
     __device__ __forceinline__ void wave_rows(const Q8Rec &r, uint32_t local_block) const {
         constexpr int kMomBytes = kMomQ8 ? 1 : 4;
         constexpr int kGradBytes = kGrad == kQGradBf16 ? 2 : kGrad == kQGradF32 ? 4 : 1;
@@ -743,9 +744,9 @@ struct AdamwRows {
             if constexpr (kGrad == kQGradQ8) gs = as_global<gfloat>(r.p[6])[wr.row];
         }
 
-        ChunkIn in[kC];
+        ChunkIn in[kCW];
 #pragma unroll
-        for (int ci = 0; ci < kC; ++ci) {
+        for (int ci = 0; ci < kCW; ++ci) {
             if (ci >= wr.chunks) continue;
             const uint32_t v = uint32_t(ci * wr.width + wr.lane);
             in[ci].w = row_ld_f32(r_master, v);
@@ -762,10 +763,10 @@ struct AdamwRows {
             if (has_delta) in[ci].o2 = row_ld_bf16(r_o, v);
         }
 
-        f32x4 mf[kC], vf[kC];
+        f32x4 mf[kCW], vf[kCW];
         uint32_t amax[2] = {0, 0};
 #pragma unroll
-        for (int ci = 0; ci < kC; ++ci) {
+        for (int ci = 0; ci < kCW; ++ci) {
             if (ci >= wr.chunks) continue;
             const uint32_t v = uint32_t(ci * wr.width + wr.lane);
             f32x4 w, d;
@@ -788,11 +789,11 @@ struct AdamwRows {
         wave_team_max<kThreads, 2>(amax, wr.width);
         if (wr.len == 0) return;
         const QuantRow qm = quant_row(amax[0]), qv = quant_row(amax[1]);
-        uint32_t cm[kC], cv[kC];
-        quant_lane<kC>(qm, mf, wr.chunks, cm);
-        quant_lane<kC>(qv, vf, wr.chunks, cv);
+        uint32_t cm[kCW], cv[kCW];
+        quant_lane<kCW>(qm, mf, wr.chunks, cm);
+        quant_lane<kCW>(qv, vf, wr.chunks, cv);
 #pragma unroll
-        for (int ci = 0; ci < kC; ++ci) {
+        for (int ci = 0; ci < kCW; ++ci) {
             if (ci >= wr.chunks) continue;
             const uint32_t v = uint32_t(ci * wr.width + wr.lane);
             row_st_codes(r_m, v, cm[ci]);
@@ -810,7 +811,19 @@ struct AdamwRows {
             return;
         }
         if constexpr (kRows == kQRowsWave) {
-            wave_rows(r, local_block);
+            wave_rows<kC>(r, local_block);
+            return;
+        }
+        if constexpr (kRows == kQRowsMixed) {
+            // the record decides, for the whole workgroup (so a team's
+            // barrier is reached by every lane or none); rows that fit the
+            // separate launches' chunk count keep that loop's code
+            if (r.flags & kQPacked)
+                packed_rows(r, local_block);
+            else if (r.chunks <= kC)
+                wave_rows<kC>(r, local_block);
+            else
+                wave_rows<kQMixedWaveChunks>(r, local_block);
             return;
         }
         Row R{r.p[0], r.p[1], r.p[2], r.p[3], r.p[4], r.p[5], r.p[6], r.p[7], r.p[8], r.p[9],
@@ -1107,6 +1120,9 @@ const void *pick_adamw(int block, QRows rows) {
     case kQRowsPacked:
         return reinterpret_cast<const void *>(
             &adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock, kQRowsPacked>);
+    case kQRowsMixed:
+        return reinterpret_cast<const void *>(
+            &adamw_q8_kernel<kMomQ8, kGrad, kDelta, kQBlock, kQRowsMixed>);
     case kQRowsWave: return pick_adamw_rows<kMomQ8, kGrad, kDelta, kQRowsWave>(block);
     default: return pick_adamw_rows<kMomQ8, kGrad, kDelta, kQRowsTeam>(block);
     }
@@ -1134,13 +1150,16 @@ const void *pick_rows(int block, QRows rows) {
     }
 }
 
+// Families of the step kernels and the workgroup sizes they come in.
 bool block_ok(int block, QRows rows) {
+    if (rows == kQRowsMixed) return block == kQBlock;
     if (rows != kQRowsTeam && rows != kQRowsPacked && rows != kQRowsWave) return false;
     return block == kQBlock || (block == kQBlockWide && rows != kQRowsPacked);
 }
 
+// ... and of the accumulation and conversion kernels (no mixed launches).
 bool rows_block_ok(int block, QRows rows) {
-    return block_ok(block, rows) && (block == kQBlock || rows == kQRowsTeam);
+    return rows != kQRowsMixed && block_ok(block, rows) && (block == kQBlock || rows == kQRowsTeam);
 }
 
 }  // namespace

@@ -96,13 +96,63 @@ Q8Rec make_rec(int64_t numel, int64_t row_len, bool vector_ok, int chunks_max, i
 }
 
 QRows rows_of(const Q8Rec &r) {
+    if (r.flags & kQMixed) return kQRowsMixed;
     return (r.flags & kQPacked) ? kQRowsPacked : (r.flags & kQWave) ? kQRowsWave : kQRowsTeam;
+}
+
+// The step's packed-row and wave-row records go into one mixed launch when
+// they would otherwise take more than one launch group, every such group is
+// small enough that its ramp and drain weigh (at most kMixRounds rounds of
+// workgroups over the GPU at the step's occupancy), and every wave row fits
+// a kQBlock-lane team of at most kQMixedWaveChunks chunks per lane (rows of
+// up to 11,264 elements).  Measured on MI355X: the rank-16 LoRA step (three
+// groups of 0.7 to 21 rounds) ran 4-5% faster in one launch, while the
+// whole 7B shape (groups of hundreds of rounds) ran 4-9% slower, and one
+// Llama-2-7B layer (40 rounds) the same.  Rows that the separate launches
+// give 1024-lane workgroups get one 256-lane team each; the others keep
+// their shape.  The records are ordered by the work of one of their
+// workgroups, the largest first, so that the long rows start early and the
+// short ones fill the end of the launch.
+constexpr int64_t kMixRounds = 16;
+
+void mix_step_records(std::vector<Q8Rec> *recs, int cus) {
+    uint64_t packed = 0, wave = 0, wide = 0;    // workgroups of each separate group
+    for (const Q8Rec &r : *recs) {
+        if (r.flags & kQPacked) {
+            packed += blocks_of(r);
+        } else if (r.flags & kQWave) {
+            if (r.block == kQBlock) {
+                wave += blocks_of(r);
+            } else {
+                wide += blocks_of(r);
+                if (ceil_div(r.row_len, 4) > int64_t(kQBlock) * kQMixedWaveChunks) return;
+            }
+        }
+    }
+    if (int(packed > 0) + int(wave > 0) + int(wide > 0) < 2) return;
+    const uint64_t round = uint64_t(std::max(cus, 1)) * kQ8StepWorkgroupsPerCu;
+    if (std::max({packed, wave, wide}) > uint64_t(kMixRounds) * round) return;
+    for (Q8Rec &r : *recs) {
+        if (!(r.flags & (kQPacked | kQWave))) continue;
+        if ((r.flags & kQWave) && r.block != kQBlock) {
+            r.team_log2 = 8;                                  // kQBlock lanes
+            r.chunks = static_cast<int32_t>(ceil_div(ceil_div(r.row_len, 4), kQBlock));
+            r.block = kQBlock;
+        }
+        r.flags |= kQMixed;
+    }
+    // every lane of a kQBlock-lane workgroup steps 4 elements per chunk, so
+    // a workgroup's work is its record's chunk count
+    auto work = [](const Q8Rec &r) { return (r.flags & kQMixed) ? r.chunks : 0; };
+    std::stable_sort(recs->begin(), recs->end(),
+                     [&](const Q8Rec &a, const Q8Rec &b) { return work(a) > work(b); });
 }
 
 uintptr_t bits(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
-// Launch `recs` in at most five groups, one per kernel: row teams and wave
-// rows in kQBlock- or kQBlockWide-lane workgroups, and packed rows.  Every
+// Launch `recs` in at most six groups, one per kernel: the step's mixed
+// records, row teams and wave rows in kQBlock- or kQBlockWide-lane
+// workgroups, and packed rows.  Every
 // group's table is built and checked before the first launch, so a size
 // error enqueues nothing.
 template <class LaunchFn>
@@ -117,8 +167,8 @@ lema_status launch_groups(const std::vector<Q8Rec> &recs, hipStream_t stream,
     };
     std::vector<Group> groups;
     const struct { int block; QRows rows; } kinds[] = {
-        {kQBlock, kQRowsTeam}, {kQBlock, kQRowsPacked}, {kQBlock, kQRowsWave},
-        {kQBlockWide, kQRowsTeam}, {kQBlockWide, kQRowsWave}};
+        {kQBlock, kQRowsMixed}, {kQBlock, kQRowsTeam}, {kQBlock, kQRowsPacked},
+        {kQBlock, kQRowsWave}, {kQBlockWide, kQRowsTeam}, {kQBlockWide, kQRowsWave}};
     for (const auto &kind : kinds) {
         std::vector<Q8Rec> sel;
         for (const Q8Rec &r : recs)
@@ -265,10 +315,15 @@ lema_status lema_adamw_step_q8(const lema_adamw_q8_seg *segs, int32_t nseg,
     // starves small launches such as the LoRA adapters).  The 1024-lane
     // ones fit once per CU anyway.  Accumulation and conversions move less
     // per workgroup and keep full occupancy.
+    // one mixed launch where its kernel's registers still allow the step's
+    // workgroups per CU (some gradient and moment combinations need more)
+    if (register_occupancy(adamw_q8_kernel_fn(mom_q8, qg, with_delta, kQBlock, kQRowsMixed),
+                           kQBlock) >= kQ8StepWorkgroupsPerCu)
+        mix_step_records(&recs, compute_units());
     // (the reservations are looked up here: the launch callback below runs
     // with the device's table cache locked)
-    uint32_t lds[3];
-    for (QRows rows : {kQRowsTeam, kQRowsPacked, kQRowsWave})
+    uint32_t lds[4];
+    for (QRows rows : {kQRowsTeam, kQRowsPacked, kQRowsWave, kQRowsMixed})
         lds[rows] = occupancy_lds_bytes(adamw_q8_kernel_fn(mom_q8, qg, with_delta, kQBlock, rows),
                                         kQ8StepWorkgroupsPerCu);
     return launch_groups(recs, hs, [&](const void *table, int n, uint32_t blocks,
