@@ -632,10 +632,14 @@ def q8_bench(torch, L, synth, a):
     per_step = step_bytes + accum_bytes
 
     nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
+    t_setup = time.perf_counter()
     sets = [q8_state(torch, L, synth, w, row_lens, a.layout, delta) for _ in range(nsets)]
     torch.cuda.synchronize()
+    progress(f"{a.workload}: {nsets} int8 state set(s) of {P} params resident "
+             f"({time.perf_counter() - t_setup:.1f} s)")
     stream = torch.cuda.current_stream()
     copy_gbps = copy_ceiling(torch, L, a.copy_gib)
+    progress(f"copy ceiling {copy_gbps:.0f} GB/s")
 
     accum_plans = [[L.AccumQ8Plan([L.AccumQ8Segment(acc, g[j]) for acc, g in accs])
                     for j in range(K)] for _, accs, _ in sets] if K > 1 else []
@@ -675,6 +679,7 @@ def q8_bench(torch, L, synth, a):
     stop.record(stream)
     torch.cuda.synchronize()
     pipelined_ms = start.elapsed_time(stop) / a.steps
+    progress(f"timed {a.steps} int8 steps: {ms:.4f} ms per step")
     gbps = per_step / (ms * 1e-3) / 1e9
     key = f"{a.workload}:q8:{'delta' if delta else 'nodelta'}"
     line = {
@@ -826,8 +831,10 @@ def merge_bench(torch, L, synth, a):
     per = 8 * P
     nsets = 1
     torch.cuda.synchronize()
+    progress(f"{a.workload}: base and delta of {P} params resident")
     stream = torch.cuda.current_stream()
     copy_gbps = copy_ceiling(torch, L, a.copy_gib)
+    progress(f"copy ceiling {copy_gbps:.0f} GB/s")
     for _ in range(a.warmup):
         L.merge_delta(segs)
     torch.cuda.synchronize()

@@ -318,11 +318,20 @@ struct CopyItem {
 
 // A fixed set of host threads for memcpy.  copy(items) splits the items'
 // bytes evenly over the threads, the caller's included, and returns when all
-// are copied.  One caller at a time.
+// are copied.  One caller at a time.  If the system refuses a thread, the
+// set works with the threads it got (at least the caller's).
 class CopyWorkers {
 public:
-    explicit CopyWorkers(int threads) : n_(std::max(1, threads)) {
-        for (int t = 1; t < n_; ++t) threads_.emplace_back([this, t] { loop(t); });
+    explicit CopyWorkers(int threads) {
+        const int want = std::max(1, threads);
+        for (int t = 1; t < want; ++t) {
+            try {
+                threads_.emplace_back([this, t] { loop(t); });
+            } catch (...) {
+                break;
+            }
+        }
+        n_ = 1 + int(threads_.size());
     }
     ~CopyWorkers() {
         {
@@ -383,7 +392,7 @@ private:
         }
     }
 
-    const int n_;
+    int n_ = 1;
     std::vector<std::thread> threads_;
     std::mutex mu_;
     std::condition_variable cv_, done_;
@@ -686,7 +695,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         return s2;
     };
 
-    std::thread outbound([&] {
+    auto outbound_work = [&] {
         CopyWorkers workers(threads_out);
         struct Pending { size_t g; char *host; char *chunk; size_t bytes; };
         std::deque<Pending> fifo;
@@ -756,7 +765,13 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
             out_status = s2;
         }
         cv.notify_all();
-    });
+    };
+    std::thread outbound;
+    try {
+        outbound = std::thread(outbound_work);
+    } catch (...) {                        // nothing is enqueued yet
+        return hip_failed(hipErrorOutOfMemory);
+    }
 
     // this thread: uploads and steps
     st = LEMA_OK;
