@@ -200,11 +200,13 @@ def fold_counters(key, fetch_csv, write_csv):
     current sources (entries whose kernel has changed since are dropped)."""
     import csv
 
-    def per_dispatch(path, kernel, counter):
+    def per_dispatch(path, kernel, counter, grid=None):
         vals = {}
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row["Kernel_Name"].strip('"') != kernel or row["Counter_Name"] != counter:
+                    continue
+                if grid is not None and int(row["Grid_Size"]) != grid:
                     continue
                 vals[row["Dispatch_Id"]] = vals.get(row["Dispatch_Id"], 0.0) + \
                     float(row["Counter_Value"])
@@ -216,8 +218,11 @@ def fold_counters(key, fetch_csv, write_csv):
     layout = "flat"
     fk, nd = per_dispatch(fetch_csv, kernel, "FETCH_SIZE")
     wk, _ = per_dispatch(write_csv, kernel, "WRITE_SIZE")
-    cf, _ = per_dispatch(fetch_csv, "copy_kernel", "FETCH_SIZE")
-    cw, _ = per_dispatch(write_csv, "copy_kernel", "WRITE_SIZE")
+    # the reference is copy_ceiling's copy of 2 GiB each way (one 16-byte
+    # vector per work-item); small workloads also run same_bytes_copy
+    ref_grid = int(COPY_KIB * 1024) // 16
+    cf, _ = per_dispatch(fetch_csv, "copy_kernel", "FETCH_SIZE", ref_grid)
+    cw, _ = per_dispatch(write_csv, "copy_kernel", "WRITE_SIZE", ref_grid)
     ff, wf = cf / COPY_KIB, cw / COPY_KIB
     read, written = fk * 1024 / ff, wk * 1024 / wf
     rec = json.load(open(COUNTERS)) if os.path.exists(COUNTERS) else {}

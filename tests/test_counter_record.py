@@ -66,14 +66,19 @@ def test_lookup_checks_layout_and_sources(monkeypatch, key):
     assert bench.traffic_for(key, e["layout"]) is None
 
 
+COPY_GRID = 2 * (1 << 30) // 16        # work-items of the 2 GiB reference copy
+
+
 def _counter_csv(path, counter, rows):
-    """A rocprofv3 counter_collection CSV with the columns fold_counters reads."""
+    """A rocprofv3 counter_collection CSV with the columns fold_counters
+    reads; rows are (dispatch, kernel, value[, grid])."""
     with open(path, "w", newline="") as f:
-        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
-                                           "Counter_Value"])
+        wr = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Grid_Size",
+                                           "Counter_Name", "Counter_Value"])
         wr.writeheader()
-        for d, k, v in rows:
-            wr.writerow({"Dispatch_Id": d, "Kernel_Name": k, "Counter_Name": counter,
+        for d, k, v, *g in rows:
+            wr.writerow({"Dispatch_Id": d, "Kernel_Name": k,
+                         "Grid_Size": g[0] if g else COPY_GRID, "Counter_Name": counter,
                          "Counter_Value": v})
 
 
@@ -89,6 +94,10 @@ def test_fold_counters(tmp_path, monkeypatch):
     read, written = 16 * alg // 34, 18 * alg // 34
     fetch = [(1, "copy_kernel", COPY_KIB / 2 / 2), (1, "copy_kernel", COPY_KIB / 2 / 2)]
     write = [(1, "copy_kernel", COPY_KIB)]
+    # a smaller copy of the same kernel (bench.py's same_bytes_copy) is not
+    # the reference
+    fetch += [(9, "copy_kernel", 1000.0, 4096)]
+    write += [(9, "copy_kernel", 2000.0, 4096)]
     for d in (2, 3):
         fetch += [(d, "adamw_tile_kernel", read / 1024 / 2 / 2)] * 2
         write += [(d, "adamw_tile_kernel", written / 1024)]
