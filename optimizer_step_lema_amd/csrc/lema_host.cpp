@@ -392,19 +392,36 @@ constexpr uint32_t kLdsGranule = 1280;
 
 namespace {
 
+// A small fixed cache of one number per kernel function (no allocation,
+// so that lema_adamw_step_noalloc may use it); when full, values are
+// computed again each time.
+struct KernelCache {
+    std::mutex mu;
+    const void *fn[128] = {};
+    int value[128] = {};
+    int n = 0;
+    template <class F>
+    int get(const void *f, F compute) {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < n; ++i)
+            if (fn[i] == f) return value[i];
+        const int v = compute();
+        if (n < 128) {
+            fn[n] = f;
+            value[n++] = v;
+        }
+        return v;
+    }
+};
+
 // Static LDS of the kernels occupancy planning has asked about.
-std::mutex g_static_lds_mu;
-std::vector<std::pair<const void *, uint32_t>> g_static_lds;
+KernelCache g_static_lds;
 
 uint32_t static_lds_bytes(const void *fn) {
-    std::lock_guard<std::mutex> lock(g_static_lds_mu);
-    for (const auto &e : g_static_lds)
-        if (e.first == fn) return e.second;
-    hipFuncAttributes attr{};
-    const uint32_t b = hipFuncGetAttributes(&attr, fn) == hipSuccess
-                           ? static_cast<uint32_t>(attr.sharedSizeBytes) : 0;
-    g_static_lds.emplace_back(fn, b);
-    return b;
+    return static_cast<uint32_t>(g_static_lds.get(fn, [&] {
+        hipFuncAttributes attr{};
+        return hipFuncGetAttributes(&attr, fn) == hipSuccess ? int(attr.sharedSizeBytes) : 0;
+    }));
 }
 
 // LDS of one workgroup (static plus dynamic) such that at most `per_cu`
@@ -418,10 +435,9 @@ uint32_t lds_per_workgroup(int lds_per_cu, int per_cu) {
     return std::min<uint32_t>(k * kLdsGranule, 65536u);
 }
 
-// Workgroups of `lanes` lanes of kernel `fn` that fit one CU by registers
-// and static LDS alone.
-std::mutex g_occupancy_mu;
-std::vector<std::pair<const void *, int>> g_occupancy;
+// Workgroups of kernel `fn` that fit one CU by registers and static LDS
+// alone (each kernel is always launched with the same workgroup size).
+KernelCache g_occupancy;
 
 }  // namespace
 
@@ -431,13 +447,10 @@ int compute_units() {
 }
 
 int register_occupancy(const void *fn, int lanes) {
-    std::lock_guard<std::mutex> lock(g_occupancy_mu);
-    for (const auto &e : g_occupancy)
-        if (e.first == fn) return e.second;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, lanes, 0) != hipSuccess) n = 0;
-    g_occupancy.emplace_back(fn, n);
-    return n;
+    return g_occupancy.get(fn, [&] {
+        int n = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, lanes, 0) == hipSuccess ? n : 0;
+    });
 }
 
 uint32_t occupancy_lds_bytes(const void *fn, int workgroups_per_cu) {
