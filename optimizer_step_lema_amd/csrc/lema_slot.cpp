@@ -56,6 +56,7 @@ struct lema_slot_pool {
     hipStream_t compute = nullptr;
     hipStream_t writeback = nullptr;  // NULL: D2H copies share the copy stream
     std::vector<hipEvent_t> events;   // grown on demand, reused by later calls
+    std::vector<hipEvent_t> marks;    // staged path: completion events without timing, likewise
     char *ring[2] = {nullptr, nullptr};   // staged path: page-locked upload and write-back rings
     std::mutex mu;
 };
@@ -406,10 +407,9 @@ private:
 // The staged path moves every array in pieces of at most one ring chunk
 // through two page-locked rings, one per direction, so that a layer's first
 // upload starts after one chunk's host copy and a write-back's host copies
-// follow its DMA chunk by chunk.
-// 128 MiB pieces: on one copy stream the gaps between pieces added 31 ms to
-// the whole 7B step with 32 MiB, 18 ms with 64 MiB and 14 ms with 128 MiB
-// (MI355X, 16-chunk rings; an 8-chunk ring of 128 MiB starved the engine).
+// follow its DMA chunk by chunk.  Back-to-back 128 MiB copies run at the
+// rate of one 2 GiB copy on MI355X; a ring of 8 chunks of 128 MiB starved
+// the copy engine on the whole 7B shape, 16 kept it busy.
 constexpr size_t kStageChunk = size_t(128) << 20;
 constexpr int kStageRing = 16;              // chunks per ring (2 GiB)
 
@@ -562,64 +562,40 @@ lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     return LEMA_OK;
 }
 
-// Copy intervals and kernel times of a staged call from its events: every
-// piece has a begin and an end event, so gaps between pieces count as idle.
-void fill_stats_pieces(lema_slot_pool *pool, int32_t nlayers, size_t ev_layer, size_t ev_in,
-                       size_t n_in, size_t ev_out, size_t n_out, double h2d_bytes,
-                       double d2h_bytes, lema_stream_stats *out) {
-    auto ev = [&](size_t i) { return pool->events[i]; };
-    lema_stream_stats s{};
-    s.h2d_bytes = h2d_bytes;
-    s.d2h_bytes = d2h_bytes;
-    const hipEvent_t t0 = ev(ev_in);            // begin of the first upload piece
-    std::vector<std::pair<float, float>> busy;
-    float b = 0.f, en = 0.f, ms = 0.f;
-    auto piece = [&](size_t base, size_t k, double *sum) {
-        if (hipEventElapsedTime(&b, t0, ev(base + 2 * k)) == hipSuccess &&
-            hipEventElapsedTime(&en, t0, ev(base + 2 * k + 1)) == hipSuccess) {
-            *sum += en - b;
-            busy.emplace_back(b, en);
-        }
-    };
-    for (size_t k = 0; k < n_in; ++k) piece(ev_in, k, &s.h2d_ms);
-    for (size_t k = 0; k < n_out; ++k) piece(ev_out, k, &s.d2h_ms);
-    for (int32_t i = 0; i < nlayers; ++i) {
-        if (hipEventElapsedTime(&ms, ev(ev_layer + 4 * size_t(i) + 1),
-                                ev(ev_layer + 4 * size_t(i) + 2)) == hipSuccess) {
-            s.kernel_ms += ms;
-            if (i == nlayers - 1) s.last_kernel_ms = ms;
-        }
-    }
-    std::sort(busy.begin(), busy.end());
-    float lo = 0.f, hi = -1.f;
-    for (const auto &iv : busy) {
-        if (iv.first > hi) {
-            if (hi > lo) s.copy_busy_ms += hi - lo;
-            lo = iv.first;
-            hi = iv.second;
-        } else if (iv.second > hi) {
-            hi = iv.second;
-        }
-    }
-    if (hi > lo) s.copy_busy_ms += hi - lo;
-    if (hipEventElapsedTime(&ms, t0, ev(ev_layer + 4 * size_t(nlayers - 1) + 3)) == hipSuccess)
-        s.wall_ms = ms;
-    *out = s;
-}
-
 // Pageable or memory-mapped host arrays.  Every array moves in pieces of at
 // most one chunk: caller memory -> upload ring -> slot, and slot -> write-
 // back ring -> caller memory.  The calling thread copies pieces into the
 // upload ring and enqueues their uploads and each layer's step; a second
 // thread enqueues the write-backs and copies their pieces out as they land.
 //
-//   - A ring chunk is reused only after its previous piece is done: its
-//     upload finished, or its write-back finished and was copied out.
-//   - Layer i's uploads into slot i mod nslots wait for the write-back of
+//   - Completion is tracked per group of kStageGroup pieces: one event
+//     without timing after each group.  An event recorded between two copies
+//     costs the copy engine about 5 us (MI355X, timing or not), so an event
+//     per piece would add milliseconds to a step of ~1,500 pieces.
+//   - A ring chunk is reused only after the group of its previous piece is
+//     done: uploaded, or written back and copied out.
+//   - Layer i's uploads into slot i mod nslots follow the write-back of
 //     layer i - nslots out of that slot.
 //   - On a single copy stream a layer's write-back is enqueued after the
 //     next layer's uploads, so the copy engine never waits for the step in
 //     between (the step of layer i runs while layer i+1 uploads).
+//   - Timing events are per layer and direction, as in run_direct: the copy
+//     intervals run from the first piece's start to the last piece's end.
+constexpr int kStageGroup = 4;
+
+lema_status ensure_marks(lema_slot_pool *pool, size_t n) {
+    while (pool->marks.size() < n) {
+        hipEvent_t ev;
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_failed(e);
+        pool->marks.push_back(ev);
+    }
+    return LEMA_OK;
+}
+
+// groups of a transfer of n pieces that end before its last piece
+size_t inner_groups(size_t n) { return n == 0 ? 0 : (n - 1) / kStageGroup; }
+
 lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans,
                        int32_t host_threads, lema_stream_stats *stats) {
     const int32_t nlayers = int32_t(plans.size());
@@ -652,29 +628,34 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         }
     }
     std::vector<std::vector<Piece>> in_p(nlayers), out_p(nlayers);
-    std::vector<size_t> first_in(nlayers), first_out(nlayers);
-    size_t n_in = 0, n_out = 0;
+    std::vector<size_t> in_mark(nlayers), out_mark(nlayers);   // first inner-group mark per layer
+    size_t n_in = 0, n_out = 0, n_marks = 0;
     for (int32_t i = 0; i < nlayers; ++i) {
         plan_pieces(plans[i], true, &in_p[i]);
         plan_pieces(plans[i], false, &out_p[i]);
-        first_in[i] = n_in;
-        first_out[i] = n_out;
         n_in += in_p[i].size();
         n_out += out_p[i].size();
+        in_mark[i] = n_marks;
+        n_marks += inner_groups(in_p[i].size());
+        out_mark[i] = n_marks;
+        n_marks += inner_groups(out_p[i].size());
     }
     if (n_in == 0 || n_out == 0) {                 // only empty segments: nothing moves
         if (stats) *stats = lema_stream_stats{};
         return LEMA_OK;
     }
-    // events: per layer {uploads done, step begin, step end, write-back done},
-    // then a begin/end pair per upload piece and per write-back piece
-    const size_t ev_layer = 0, ev_in = 4 * size_t(nlayers), ev_out = ev_in + 2 * n_in;
-    lema_status st = ensure_events(pool, ev_out + 2 * n_out);
+    lema_status st = ensure_events(pool, size_t(nlayers) * EV_PER_LAYER);
+    if (st == LEMA_OK) st = ensure_marks(pool, n_marks);
     if (st != LEMA_OK) return st;
-    auto lev = [&](int32_t i, int k) { return pool->events[ev_layer + 4 * size_t(i) + k]; };
-    auto iev = [&](size_t g, int k) { return pool->events[ev_in + 2 * g + k]; };
-    auto oev = [&](size_t g, int k) { return pool->events[ev_out + 2 * g + k]; };
+    auto ev = [&](int32_t layer, int kind) { return pool->events[size_t(layer) * EV_PER_LAYER + kind]; };
     auto slot_of = [&](int32_t i) { return pool->base + size_t(i % pool->nslots) * pool->slot_bytes; };
+    // The event that completes piece k of a transfer of n pieces: the mark
+    // of its group, or for the last group the transfer's own end event.
+    auto group_event = [&](size_t first_mark, size_t k, size_t n, hipEvent_t end) {
+        const size_t g = k / kStageGroup;
+        return g < inner_groups(n) ? pool->marks[first_mark + g] : end;
+    };
+    auto closes_group = [](size_t k, size_t n) { return k + 1 == n || (k + 1) % kStageGroup == 0; };
 
     const bool duplex = pool->writeback != nullptr;
     hipStream_t d2h_stream = duplex ? pool->writeback : pool->copy;
@@ -697,17 +678,22 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
 
     auto outbound_work = [&] {
         CopyWorkers workers(threads_out);
-        struct Pending { size_t g; char *host; char *chunk; size_t bytes; };
-        std::deque<Pending> fifo;
+        struct Pending { hipEvent_t done; CopyItem item; };
+        std::deque<Pending> fifo;          // enqueued pieces not yet copied out, oldest first
+        std::vector<CopyItem> batch;
         size_t next = 0;
+        // copy out the oldest group: every pending piece that its event completes
         auto complete_oldest = [&]() -> lema_status {
-            const Pending p = fifo.front();
-            fifo.pop_front();
-            hipError_t err = hipEventSynchronize(oev(p.g, 1));
+            const hipEvent_t done = fifo.front().done;
+            hipError_t err = hipEventSynchronize(done);
             if (err != hipSuccess) return hip_failed(err);
-            const CopyItem item{p.host, p.chunk, p.bytes};
+            batch.clear();
+            while (!fifo.empty() && fifo.front().done == done) {
+                batch.push_back(fifo.front().item);
+                fifo.pop_front();
+            }
             const auto t0 = clock::now();
-            workers.copy(&item, 1);
+            workers.copy(batch.data(), batch.size());
             out_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
             return LEMA_OK;
         };
@@ -721,29 +707,31 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
                 cv.wait(lk, [&] { return abort || steps_enqueued >= need; });
                 if (abort) break;
             }
-            hipError_t err = hipStreamWaitEvent(d2h_stream, lev(j, 2), 0);
+            hipError_t err = hipStreamWaitEvent(d2h_stream, ev(j, EV_K_END), 0);
+            if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_BEGIN), d2h_stream);
             if (err != hipSuccess) { s2 = hip_failed(err); break; }
             char *slot = slot_of(j);
-            for (size_t k = 0; k < out_p[j].size(); ++k) {
+            const size_t n = out_p[j].size();
+            for (size_t k = 0; k < n; ++k) {
                 if (fifo.size() == size_t(kStageRing)) {
                     s2 = complete_oldest();
                     if (s2 != LEMA_OK) break;
                 }
                 const Piece &p = out_p[j][k];
-                const size_t g = first_out[j] + k;
                 char *chunk = pool->ring[1] + (next++ % kStageRing) * kStageChunk;
-                err = hipEventRecord(oev(g, 0), d2h_stream);
-                if (err == hipSuccess)
-                    err = copy_async(chunk, slot + p.slot_off, p.bytes, hipMemcpyDeviceToHost,
-                                     d2h_stream, &fi);
-                if (err == hipSuccess) err = hipEventRecord(oev(g, 1), d2h_stream);
+                err = copy_async(chunk, slot + p.slot_off, p.bytes, hipMemcpyDeviceToHost,
+                                 d2h_stream, &fi);
+                const hipEvent_t done = group_event(out_mark[j], k, n, ev(j, EV_D2H_END));
+                if (err == hipSuccess && closes_group(k, n)) err = hipEventRecord(done, d2h_stream);
                 if (err != hipSuccess) { s2 = hip_failed(err); break; }
                 d2h_bytes += double(p.bytes);
-                fifo.push_back({g, p.host, chunk, p.bytes});
+                fifo.push_back({done, {p.host, chunk, p.bytes}});
             }
             if (s2 != LEMA_OK) break;
-            err = hipEventRecord(lev(j, 3), d2h_stream);
-            if (err != hipSuccess) { s2 = hip_failed(err); break; }
+            if (n == 0) {
+                err = hipEventRecord(ev(j, EV_D2H_END), d2h_stream);
+                if (err != hipSuccess) { s2 = hip_failed(err); break; }
+            }
             {
                 std::lock_guard<std::mutex> lk(m);
                 backs_enqueued = j + 1;
@@ -777,7 +765,8 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     st = LEMA_OK;
     {
         CopyWorkers workers(threads_in);
-        std::vector<long> chunk_piece(kStageRing, -1);     // last upload piece in each chunk
+        std::vector<hipEvent_t> chunk_done(kStageRing, nullptr);   // completes a chunk's last upload
+        std::vector<size_t> open;                                  // chunks of the group being enqueued
         size_t next = 0;
         for (int32_t i = 0; i < nlayers && st == LEMA_OK; ++i) {
             {
@@ -785,21 +774,26 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
                 if (abort) break;
             }
             if (i >= pool->nslots) {
-                // the slot's previous occupant is written back first
+                // the slot's previous occupant is written back first: on one
+                // copy stream by the order of enqueueing, else by its event
                 std::unique_lock<std::mutex> lk(m);
                 cv.wait(lk, [&] { return abort || backs_enqueued >= i - pool->nslots + 1; });
                 if (abort) break;
                 lk.unlock();
-                e = hipStreamWaitEvent(pool->copy, lev(i - pool->nslots, 3), 0);
-                if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+                if (duplex) {
+                    e = hipStreamWaitEvent(pool->copy, ev(i - pool->nslots, EV_D2H_END), 0);
+                    if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+                }
             }
+            e = hipEventRecord(ev(i, EV_H2D_BEGIN), pool->copy);
+            if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
             char *slot = slot_of(i);
-            for (size_t k = 0; k < in_p[i].size(); ++k) {
+            const size_t n = in_p[i].size();
+            for (size_t k = 0; k < n; ++k) {
                 const Piece &p = in_p[i][k];
-                const size_t g = first_in[i] + k;
                 const size_t c = next++ % kStageRing;
-                if (chunk_piece[c] >= 0) {
-                    e = hipEventSynchronize(iev(size_t(chunk_piece[c]), 1));
+                if (chunk_done[c] != nullptr) {
+                    e = hipEventSynchronize(chunk_done[c]);
                     if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
                 }
                 char *chunk = pool->ring[0] + c * kStageChunk;
@@ -807,23 +801,30 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
                 const auto t0 = clock::now();
                 workers.copy(&item, 1);
                 in_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
-                e = hipEventRecord(iev(g, 0), pool->copy);
-                if (e == hipSuccess)
-                    e = copy_async(slot + p.slot_off, chunk, p.bytes, hipMemcpyHostToDevice,
-                                   pool->copy, &fi);
-                if (e == hipSuccess) e = hipEventRecord(iev(g, 1), pool->copy);
+                e = copy_async(slot + p.slot_off, chunk, p.bytes, hipMemcpyHostToDevice,
+                               pool->copy, &fi);
                 if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
-                chunk_piece[c] = long(g);
                 h2d_bytes += double(p.bytes);
+                open.push_back(c);
+                if (closes_group(k, n)) {
+                    const hipEvent_t done = group_event(in_mark[i], k, n, ev(i, EV_H2D_END));
+                    e = hipEventRecord(done, pool->copy);
+                    if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+                    for (size_t oc : open) chunk_done[oc] = done;
+                    open.clear();
+                }
             }
             if (st != LEMA_OK) break;
-            e = hipEventRecord(lev(i, 0), pool->copy);
-            if (e == hipSuccess) e = hipStreamWaitEvent(pool->compute, lev(i, 0), 0);
-            if (e == hipSuccess) e = hipEventRecord(lev(i, 1), pool->compute);
+            if (n == 0) {
+                e = hipEventRecord(ev(i, EV_H2D_END), pool->copy);
+                if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
+            }
+            e = hipStreamWaitEvent(pool->compute, ev(i, EV_H2D_END), 0);
+            if (e == hipSuccess) e = hipEventRecord(ev(i, EV_K_BEGIN), pool->compute);
             if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
             st = plans[i].launch(slot, pool->compute);
             if (st != LEMA_OK) { fail(st); break; }
-            e = hipEventRecord(lev(i, 2), pool->compute);
+            e = hipEventRecord(ev(i, EV_K_END), pool->compute);
             if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
             {
                 std::lock_guard<std::mutex> lk(m);
@@ -836,12 +837,11 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     outbound.join();
     if (st == LEMA_OK) st = out_status;
     if (st != LEMA_OK) return drain(pool, st);
-    e = hipEventSynchronize(lev(nlayers - 1, 3));
+    e = hipEventSynchronize(ev(nlayers - 1, EV_D2H_END));
     if (e != hipSuccess) return drain(pool, hip_failed(e));
 
     if (stats) {
-        fill_stats_pieces(pool, nlayers, ev_layer, ev_in, n_in, ev_out, n_out, h2d_bytes,
-                          d2h_bytes, stats);
+        fill_stats(pool, nlayers, h2d_bytes, d2h_bytes, stats);
         stats->host_in_ms = in_ms;
         stats->host_out_ms = out_ms;
         stats->call_ms = std::chrono::duration<double, std::milli>(clock::now() - call_start).count();
@@ -895,6 +895,12 @@ lema_status lema_slot_pool_destroy(lema_slot_pool *pool) {
             (void)hipEventDestroy(ev);
         }
         pool->events.clear();
+        for (hipEvent_t ev : pool->marks) {
+            hipError_t e = hipEventSynchronize(ev);
+            if (e != hipSuccess && e != hipErrorInvalidResourceHandle && st == LEMA_OK) st = hip_failed(e);
+            (void)hipEventDestroy(ev);
+        }
+        pool->marks.clear();
         for (char *&p : pool->ring) {
             if (p) (void)hipHostFree(p);
             p = nullptr;

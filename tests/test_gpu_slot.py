@@ -243,12 +243,15 @@ def test_slot_stream_staged_memory_mapped(L, tmp_path):
     pool.close()
 
 
-def test_slot_stream_staged_llama_layers(L):
-    """Four real Llama-2-7B layers from pageable memory, duplex write-back."""
+@pytest.mark.parametrize("duplex", [True, False])
+def test_slot_stream_staged_llama_layers(L, duplex):
+    """Four real Llama-2-7B layers from pageable memory: each direction of a
+    layer moves in 45 pieces, more than a ring holds, in groups of 4
+    with a ragged last group."""
     w = synth.WORKLOADS["llama7b_layer"]
     sizes = w.numels
     layers, snaps = zip(*[pageable_layer(sizes, 150 + i) for i in range(4)])
-    pool = L.SlotPool(layer_bytes(sizes), nslots=2, duplex=True)
+    pool = L.SlotPool(layer_bytes(sizes), nslots=2, duplex=duplex)
     stats = pool.stream(layers, step=10, staged=True, **HP)
     check_layers(layers, snaps, 10, sample=20000)
     print(f"staged slot stream 4 Llama layers: call {stats['call_ms']:.1f} ms, GPU span "
