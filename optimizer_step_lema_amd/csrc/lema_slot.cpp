@@ -404,7 +404,7 @@ private:
     int pending_ = 0;
 };
 
-// The staged path moves every array in pieces of at most one ring chunk
+// The staged path moves a layer's arrays in pieces of at most one ring chunk
 // through two page-locked rings, one per direction, so that a layer's first
 // upload starts after one chunk's host copy and a write-back's host copies
 // follow its DMA chunk by chunk.  Back-to-back 128 MiB copies run at the
@@ -413,19 +413,49 @@ private:
 constexpr size_t kStageChunk = size_t(128) << 20;
 constexpr int kStageRing = 16;              // chunks per ring (2 GiB)
 
-// One piece of a layer's transfer: part of one array, at most one chunk.
-struct Piece {
+// One piece of a layer's transfer in one direction: a span of the slot of
+// at most one chunk, holding whole or partial arrays that follow each other
+// in the slot with only alignment padding between them.  A piece moves as
+// one copy between the slot and a ring chunk laid out like the span, and as
+// one host copy per part between the chunk and the caller's arrays.  (The
+// upload carries the padding's stale ring bytes into slot padding, which no
+// array uses.)
+struct PiecePart {
     char *host;
-    size_t slot_off;
+    size_t at;        // offset in the span and in the chunk
     size_t bytes;
+};
+struct Piece {
+    size_t slot_off;
+    size_t span;
+    std::vector<PiecePart> parts;
+    size_t bytes() const {
+        size_t b = 0;
+        for (const PiecePart &q : parts) b += q.bytes;
+        return b;
+    }
 };
 
 void plan_pieces(const LayerPlan &plan, bool inbound, std::vector<Piece> *out) {
     out->clear();
+    bool open = false;
     for (const Xfer &x : plan.xfers) {
         if (x.bytes == 0 || (inbound ? !x.in : !x.out)) continue;
-        for (size_t o = 0; o < x.bytes; o += kStageChunk)
-            out->push_back({x.host + o, x.off + o, std::min(kStageChunk, x.bytes - o)});
+        for (size_t done = 0; done < x.bytes;) {
+            const size_t off = x.off + done;
+            const bool extend = open && off == align_up(out->back().slot_off + out->back().span) &&
+                                off - out->back().slot_off < kStageChunk;
+            if (!extend) {
+                out->push_back({off, 0, {}});
+                open = true;
+            }
+            Piece &p = out->back();
+            const size_t at = off - p.slot_off;
+            const size_t take = std::min(x.bytes - done, kStageChunk - at);
+            p.parts.push_back({x.host + done, at, take});
+            p.span = at + take;
+            done += take;
+        }
     }
 }
 
@@ -562,8 +592,8 @@ lema_status run_direct(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     return LEMA_OK;
 }
 
-// Pageable or memory-mapped host arrays.  Every array moves in pieces of at
-// most one chunk: caller memory -> upload ring -> slot, and slot -> write-
+// Pageable or memory-mapped host arrays.  Arrays move in pieces of at most
+// one chunk: caller memory -> upload ring -> slot, and slot -> write-
 // back ring -> caller memory.  The calling thread copies pieces into the
 // upload ring and enqueues their uploads and each layer's step; a second
 // thread enqueues the write-backs and copies their pieces out as they land.
@@ -678,7 +708,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
 
     auto outbound_work = [&] {
         CopyWorkers workers(threads_out);
-        struct Pending { hipEvent_t done; CopyItem item; };
+        struct Pending { hipEvent_t done; char *chunk; const Piece *piece; };
         std::deque<Pending> fifo;          // enqueued pieces not yet copied out, oldest first
         std::vector<CopyItem> batch;
         size_t next = 0;
@@ -689,7 +719,8 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
             if (err != hipSuccess) return hip_failed(err);
             batch.clear();
             while (!fifo.empty() && fifo.front().done == done) {
-                batch.push_back(fifo.front().item);
+                for (const PiecePart &q : fifo.front().piece->parts)
+                    batch.push_back({q.host, fifo.front().chunk + q.at, q.bytes});
                 fifo.pop_front();
             }
             const auto t0 = clock::now();
@@ -719,13 +750,13 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
                 }
                 const Piece &p = out_p[j][k];
                 char *chunk = pool->ring[1] + (next++ % kStageRing) * kStageChunk;
-                err = copy_async(chunk, slot + p.slot_off, p.bytes, hipMemcpyDeviceToHost,
+                err = copy_async(chunk, slot + p.slot_off, p.span, hipMemcpyDeviceToHost,
                                  d2h_stream, &fi);
                 const hipEvent_t done = group_event(out_mark[j], k, n, ev(j, EV_D2H_END));
                 if (err == hipSuccess && closes_group(k, n)) err = hipEventRecord(done, d2h_stream);
                 if (err != hipSuccess) { s2 = hip_failed(err); break; }
-                d2h_bytes += double(p.bytes);
-                fifo.push_back({done, {p.host, chunk, p.bytes}});
+                d2h_bytes += double(p.bytes());
+                fifo.push_back({done, chunk, &p});
             }
             if (s2 != LEMA_OK) break;
             if (n == 0) {
@@ -767,6 +798,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         CopyWorkers workers(threads_in);
         std::vector<hipEvent_t> chunk_done(kStageRing, nullptr);   // completes a chunk's last upload
         std::vector<size_t> open;                                  // chunks of the group being enqueued
+        std::vector<CopyItem> items;
         size_t next = 0;
         for (int32_t i = 0; i < nlayers && st == LEMA_OK; ++i) {
             {
@@ -797,14 +829,15 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
                     if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
                 }
                 char *chunk = pool->ring[0] + c * kStageChunk;
-                const CopyItem item{chunk, p.host, p.bytes};
+                items.clear();
+                for (const PiecePart &q : p.parts) items.push_back({chunk + q.at, q.host, q.bytes});
                 const auto t0 = clock::now();
-                workers.copy(&item, 1);
+                workers.copy(items.data(), items.size());
                 in_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
-                e = copy_async(slot + p.slot_off, chunk, p.bytes, hipMemcpyHostToDevice,
+                e = copy_async(slot + p.slot_off, chunk, p.span, hipMemcpyHostToDevice,
                                pool->copy, &fi);
                 if (e != hipSuccess) { st = fail(hip_failed(e)); break; }
-                h2d_bytes += double(p.bytes);
+                h2d_bytes += double(p.bytes());
                 open.push_back(c);
                 if (closes_group(k, n)) {
                     const hipEvent_t done = group_event(in_mark[i], k, n, ev(i, EV_H2D_END));
