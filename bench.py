@@ -721,6 +721,8 @@ def q8_bench(torch, L, synth, a):
                       "params_per_s": P / (pipelined_ms * 1e-3)},
         "host_wall_s_timed_region": wall,
     }
+    if nsets > 1:
+        line["same_bytes_copy"] = same_bytes_copy(torch, L, stream, step_bytes, nsets, a.steps)
     if accum_ms_list:
         acc_ms = sum(accum_ms_list) / len(accum_ms_list)
         acc_gbps = accum_bytes / (acc_ms * 1e-3) / 1e9

@@ -418,7 +418,7 @@ typedef struct {
 
 typedef struct {
     double h2d_bytes, d2h_bytes;  /* bytes copied in each direction         */
-    double h2d_ms, d2h_ms;        /* summed copy durations                  */
+    double h2d_ms, d2h_ms;        /* summed copy durations, per layer and direction */
     double kernel_ms;             /* summed AdamW kernel durations          */
     double copy_busy_ms;          /* time at least one copy was running     */
     double wall_ms;               /* first copy start .. last copy end      */
@@ -449,8 +449,9 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
  * lema_slot_stream for host state that is not page-locked: ordinary memory or
  * a memory-mapped file (the disk tier of the LEMA README's "Triple-Buffer
  * Pipeline: Disk -> pinned RAM -> VRAM"; "Selective Full Fine-Tuning": fp32
- * states in RAM with an mmap disk backend).  Every array moves in pieces of
- * at most 128 MiB:
+ * states in RAM with an mmap disk backend).  A layer's arrays move in pieces
+ * of at most 128 MiB, each a span of the slot that holds arrays adjacent
+ * there (one copy between slot and ring, one host copy per array part):
  *   caller memory -> page-locked upload ring -> slot[i mod nslots]
  *   slot[i mod nslots] -> page-locked write-back ring -> caller memory
  * The two rings (16 chunks of 128 MiB each, 4 GiB in all) are allocated by
@@ -461,7 +462,10 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
  * follow its DMA.  The calling thread enqueues the uploads and steps; a
  * second thread of the library enqueues the write-backs and copies them out.
  * On a single copy stream each layer's write-back is enqueued after the next
- * layer's uploads.  Blocks until every layer is written back.
+ * layer's uploads.  Blocks until every layer is written back.  In `stats`,
+ * as for lema_slot_stream, copy times are per layer and direction (first
+ * piece's start to last piece's end); a wait for the host inside a layer's
+ * transfer shows as a lower h2d/d2h rate, not as uncovered time.
  * Same arguments and errors as lema_slot_stream, except that host memory need
  * not be page-locked (no LEMA_ERR_NOT_PINNED); LEMA_ERR_SIZE also for
  * host_threads outside 0..256.
