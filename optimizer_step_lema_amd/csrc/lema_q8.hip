@@ -542,6 +542,23 @@ __device__ __forceinline__ void quant_lane(const QuantRow &q, const f32x4 (&x)[k
     }
 }
 
+// int8 codes of a wave-rows team through LDS: each wavefront moves the codes
+// of 4 chunks (4 spans of 256 elements, one per chunk) as one 16-byte access
+// per lane instead of four 4-byte ones, and LDS turns the spans around between
+// that layout (lane j holds 16 codes of span j/16) and the chunk layout of the
+// fp32 arrays (lane t holds 4 codes of every span).  A wavefront's code
+// accesses are then 1 KB each, like its fp32 accesses; with 4-byte code
+// accesses the step issued as many vector memory instructions per element as
+// the fp32 step while moving two thirds of the bytes, and the address FIFO
+// in front of the texture unit was full about a quarter of the time.
+// One buffer per workgroup: kGroups groups of 4 chunks, for m and for v, per
+// wavefront (1 KB each).
+template <int kThreads, int kGroups>
+__device__ __forceinline__ uint32_t *code_stage() {
+    __shared__ __attribute__((aligned(16))) uint32_t buf[kThreads / 64][2][kGroups][256];
+    return &buf[0][0][0][0];
+}
+
 // ------------------------------------------------------------- AdamW
 
 // One AdamW step with int8 moments (kMomQ8) and/or an int8 gradient
@@ -744,15 +761,52 @@ struct AdamwRows {
             if constexpr (kGrad == kQGradQ8) gs = as_global<gfloat>(r.p[6])[wr.row];
         }
 
+        // 16-byte code accesses: rows (all of the segment's, and this one) of
+        // a multiple of 16 elements in code arrays aligned to 16 bytes (the
+        // test is uniform over the team)
+        constexpr int kG = (kCW + 3) / 4;
+        constexpr int kStageGroups =
+            kRows == kQRowsMixed ? (kQMixedWaveChunks + 3) / 4 : (kC + 3) / 4;
+        static_assert(kG <= kStageGroups, "code staging groups");
+        const bool wide = kMomQ8 && (wr.len & 15) == 0 && (r.row_len & 15) == 0 &&
+                          ((r.p[1] | r.p[3]) & 15) == 0;
+        const int j = int(threadIdx.x) & 63;           // lane in the wavefront
+        const int wt = wr.lane >> 6;                    // wavefront in the team
+        uint32_t *stage = code_stage<kThreads, kStageGroups>() +
+                          (int(threadIdx.x) >> 6) * (2 * kStageGroups * 256);
+        // byte offset of lane j's 16 codes of group g: span 4g + j/16, part j % 16
+        auto wide_off = [&](int g) {
+            return ((4 * g + (j >> 4)) * wr.width + 64 * wt + (j & 15) * 4) * 4;
+        };
+
         ChunkIn in[kCW];
+        if (wide) {
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                if (4 * g + (j >> 4) >= wr.chunks) continue;
+                const u32x4_t qm = __builtin_amdgcn_raw_buffer_load_b128(r_m, wide_off(g), 0, kRowPolicy);
+                const u32x4_t qv = __builtin_amdgcn_raw_buffer_load_b128(r_v, wide_off(g), 0, kRowPolicy);
+                *reinterpret_cast<u32x4_t *>(stage + g * 256 + 4 * j) = qm;
+                *reinterpret_cast<u32x4_t *>(stage + (kStageGroups + g) * 256 + 4 * j) = qv;
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int ci = 0; ci < kCW; ++ci) {
+                if (ci >= wr.chunks) continue;
+                in[ci].mc = stage[(ci >> 2) * 256 + (ci & 3) * 64 + j];
+                in[ci].vc = stage[(kStageGroups + (ci >> 2)) * 256 + (ci & 3) * 64 + j];
+            }
+        }
 #pragma unroll
         for (int ci = 0; ci < kCW; ++ci) {
             if (ci >= wr.chunks) continue;
             const uint32_t v = uint32_t(ci * wr.width + wr.lane);
             in[ci].w = row_ld_f32(r_master, v);
             if constexpr (kMomQ8) {
-                in[ci].mc = row_ld_codes(r_m, v);
-                in[ci].vc = row_ld_codes(r_v, v);
+                if (!wide) {
+                    in[ci].mc = row_ld_codes(r_m, v);
+                    in[ci].vc = row_ld_codes(r_v, v);
+                }
             } else {
                 in[ci].mf = row_ld_f32(r_m, v);
                 in[ci].vf = row_ld_f32(r_v, v);
@@ -792,12 +846,31 @@ struct AdamwRows {
         uint32_t cm[kCW], cv[kCW];
         quant_lane<kCW>(qm, mf, wr.chunks, cm);
         quant_lane<kCW>(qv, vf, wr.chunks, cv);
+        if (wide) {
 #pragma unroll
-        for (int ci = 0; ci < kCW; ++ci) {
-            if (ci >= wr.chunks) continue;
-            const uint32_t v = uint32_t(ci * wr.width + wr.lane);
-            row_st_codes(r_m, v, cm[ci]);
-            row_st_codes(r_v, v, cv[ci]);
+            for (int ci = 0; ci < kCW; ++ci) {
+                if (ci >= wr.chunks) continue;
+                stage[(ci >> 2) * 256 + (ci & 3) * 64 + j] = cm[ci];
+                stage[(kStageGroups + (ci >> 2)) * 256 + (ci & 3) * 64 + j] = cv[ci];
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int g = 0; g < kG; ++g) {
+                if (4 * g + (j >> 4) >= wr.chunks) continue;
+                const u32x4_t qm4 = *reinterpret_cast<const u32x4_t *>(stage + g * 256 + 4 * j);
+                const u32x4_t qv4 =
+                    *reinterpret_cast<const u32x4_t *>(stage + (kStageGroups + g) * 256 + 4 * j);
+                __builtin_amdgcn_raw_buffer_store_b128(qm4, r_m, wide_off(g), 0, kRowPolicy);
+                __builtin_amdgcn_raw_buffer_store_b128(qv4, r_v, wide_off(g), 0, kRowPolicy);
+            }
+        } else {
+#pragma unroll
+            for (int ci = 0; ci < kCW; ++ci) {
+                if (ci >= wr.chunks) continue;
+                const uint32_t v = uint32_t(ci * wr.width + wr.lane);
+                row_st_codes(r_m, v, cm[ci]);
+                row_st_codes(r_v, v, cv[ci]);
+            }
         }
         if (wr.lane == 0) {
             as_global<gfloat>(r.p[2])[wr.row] = qm.s;
