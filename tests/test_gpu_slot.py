@@ -196,13 +196,14 @@ def pageable_layer(sizes, seed, alloc=None):
     return segs, snaps
 
 
-@pytest.mark.parametrize("duplex,threads", [(False, 0), (True, 3), (False, 1)])
-def test_slot_stream_staged_pageable(L, duplex, threads):
+@pytest.mark.parametrize("duplex,threads,nslots", [(False, 0, 2), (True, 3, 2), (False, 1, 2),
+                                                   (False, 0, 3), (True, 2, 3)])
+def test_slot_stream_staged_pageable(L, duplex, threads, nslots):
     """Pageable host state through the page-locked staging buffers."""
     shapes = [[100003, 4096, 2048 * 3 + 1], [777, 1 << 20], [1, 2, 3, 300000], [5000],
               [1 << 20, 17]]
     layers, snaps = zip(*[pageable_layer(s, 110 + i) for i, s in enumerate(shapes)])
-    pool = L.SlotPool(max(layer_bytes(s) for s in shapes), nslots=2, duplex=duplex)
+    pool = L.SlotPool(max(layer_bytes(s) for s in shapes), nslots=nslots, duplex=duplex)
     stats = pool.stream(layers, step=6, staged=True, host_threads=threads, **HP)
     check_layers(layers, snaps, 6)
     P = sum(sum(s) for s in shapes)

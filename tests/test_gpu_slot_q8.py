@@ -147,13 +147,16 @@ def test_stream_q8_rejects(L):
     small.close()
 
 
-def test_stream_q8_llama_layers_staged(L):
+@pytest.mark.parametrize("duplex", [True, False])
+def test_stream_q8_llama_layers_staged(L, duplex):
     """Two Llama-2-7B decoder layers (404.8 M params) of int8 host state,
-    staged, every element checked."""
+    staged, every element checked.  A piece spans adjacent arrays of the
+    slot (master, codes, row scales and gradient of a segment going in), so
+    pieces mix 4-byte, 1-byte and row-scale arrays."""
     w = synth.WORKLOADS["llama7b_layer"]
     shapes = [(n, sh[-1]) for n, (_, sh) in zip(w.numels, w.segments)]
     layers, snaps = zip(*[q8_layer(L, shapes, 70 + i, pinned=False) for i in range(2)])
-    pool = L.SlotPool(slot_bytes(shapes), nslots=2, duplex=True)
+    pool = L.SlotPool(slot_bytes(shapes), nslots=2, duplex=duplex)
     stats = pool.stream_q8(layers, step=w.step, staged=True, **HP)
     check_layers(layers, snaps, w.step)
     assert stats["kernel_ms"] > 0
