@@ -423,7 +423,7 @@ def resident_bench(torch, L, synth, a):
         "device": info,
         "host_wall_s_timed_region": wall,
     }
-    if nsets > 1:
+    if nsets > 1 or P * step_bytes < SMALL_STEP_BYTES:
         line["same_bytes_copy"] = same_bytes_copy(torch, L, stream, P * step_bytes, nsets, a.steps)
     if accum_ms_list:
         acc_ms = sum(accum_ms_list) / len(accum_ms_list)
@@ -438,6 +438,11 @@ def resident_bench(torch, L, synth, a):
                                             sets[0][1][0][1] if resident_mb else None,
                                             bytes_per_param=step_bytes + accum_bytes)
     return line
+
+
+# steps that move less than this also time a plain copy of their bytes: the
+# ramp and drain of such a launch are a visible part of it
+SMALL_STEP_BYTES = 2 << 30
 
 
 def same_bytes_copy(torch, L, stream, nbytes, nsets, steps):
@@ -721,7 +726,7 @@ def q8_bench(torch, L, synth, a):
                       "params_per_s": P / (pipelined_ms * 1e-3)},
         "host_wall_s_timed_region": wall,
     }
-    if nsets > 1:
+    if nsets > 1 or step_bytes < SMALL_STEP_BYTES:
         line["same_bytes_copy"] = same_bytes_copy(torch, L, stream, step_bytes, nsets, a.steps)
     if accum_ms_list:
         acc_ms = sum(accum_ms_list) / len(accum_ms_list)
