@@ -281,3 +281,26 @@ def test_injected_copy_failure_then_recovery(L, monkeypatch, staged, fail_at):
     pool.stream(layers2, step=3, staged=staged, **HP)
     check_layers(layers2, snaps2, 3)
     pool.close()
+
+
+@pytest.mark.parametrize("duplex,fail_at", [(False, 40), (False, 125), (True, 60), (True, 130)])
+def test_staged_failure_mid_stream_then_recovery(L, monkeypatch, duplex, fail_at):
+    """A copy that fails while a staged call over real Llama-2-7B layers is
+    well under way (each direction of a layer moves in 45 pieces, so both
+    rings are full and completion groups are pending in both threads):
+    LEMA_ERR_HIP once the streams have drained, then the same pool streams
+    the layers again and every element matches the oracle."""
+    from optimizer_step_lema_amd import _native as N
+    w = synth.WORKLOADS["llama7b_layer"]
+    sizes = w.numels
+    layers, snaps = zip(*[pageable_layer(sizes, 170 + i) for i in range(3)])
+    pool = L.SlotPool(layer_bytes(sizes), nslots=2, duplex=duplex)
+    monkeypatch.setenv("LEMA_FAULT_INJECT", f"copy:{fail_at}")
+    with pytest.raises(N.LemaError) as e:
+        pool.stream(layers, step=10, staged=True, **HP)
+    assert e.value.status == N.LEMA_ERR_HIP and e.value.hip_error != 0
+    monkeypatch.delenv("LEMA_FAULT_INJECT")
+    layers2, snaps2 = zip(*[pageable_layer(sizes, 180 + i) for i in range(3)])
+    pool.stream(layers2, step=10, staged=True, **HP)
+    check_layers(layers2, snaps2, 10, sample=20000)
+    pool.close()
