@@ -232,11 +232,24 @@ class FlatState:
     puts one tensor's arrays next to each other, which measured slower on
     MI355X for the same launch (about 1.5% with the step's occupancy cap,
     10-15% at full occupancy).
+
+    The buffer of the k-th kind starts `stagger` * k bytes into an allocation
+    that much larger (a multiple of 256 B, so views stay vector-aligned).
+    Without it every kind starts at the allocator's large alignment, and one
+    tile's accesses to all arrays share their low address bits.  Measured on
+    one MI355X (three interleaved runs each), 4 KiB per kind against none:
+    the Llama-2-7B attention step 1.386 against 1.409 ms, one rank's share
+    of the 7B shape 4.37 against 4.49 ms, 8 resident micro-batches 1.515
+    against 1.535 ms; the whole 7B shape the same within the runs' spread;
+    the rank-16 LoRA step 0.233 against 0.229 ms.
     """
 
-    def __init__(self, numels: Sequence[int], kinds: dict, device="cuda", align: int = 64):
+    def __init__(self, numels: Sequence[int], kinds: dict, device="cuda", align: int = 64,
+                 stagger: int = 4096):
         if align < 1:
             raise ValueError("align must be >= 1")
+        if stagger < 0 or stagger % 256:
+            raise ValueError("stagger must be a non-negative multiple of 256 bytes")
         self.numels = [int(n) for n in numels]
         if any(n < 0 for n in self.numels):
             raise ValueError("numels must be >= 0")
@@ -246,7 +259,10 @@ class FlatState:
             self.offsets.append(total)
             total += -(-n // align) * align
         self.total = total
-        self.buffers = {k: torch.empty(total, dtype=dt, device=device) for k, dt in kinds.items()}
+        self.buffers = {}
+        for k, (name, dt) in enumerate(kinds.items()):
+            shift = k * stagger // torch.empty(0, dtype=dt).element_size()
+            self.buffers[name] = torch.empty(total + shift, dtype=dt, device=device)[shift:]
 
     def __len__(self) -> int:
         return len(self.numels)

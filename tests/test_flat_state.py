@@ -25,6 +25,22 @@ def test_offsets_aligned_and_disjoint():
             assert (v.data_ptr() - base) % (64 * esz) == 0
 
 
+def test_kinds_are_staggered():
+    kinds = {"a": torch.float32, "b": torch.bfloat16, "c": torch.int8, "d": torch.float32}
+    fs = L.FlatState([100, 7], kinds, device="cpu")
+    for k, (name, dt) in enumerate(kinds.items()):
+        b = fs.buffers[name]
+        assert b.numel() == fs.total and b.is_contiguous()
+        assert b.storage_offset() * b.element_size() == 4096 * k
+    fs0 = L.FlatState([100], kinds, device="cpu", stagger=0)
+    assert all(b.storage_offset() == 0 for b in fs0.buffers.values())
+    fs1 = L.FlatState([100], kinds, device="cpu", stagger=768)
+    assert fs1.buffers["d"].storage_offset() * 4 == 3 * 768
+    for bad in (-256, 100, 4097):
+        with pytest.raises(ValueError):
+            L.FlatState([1], kinds, device="cpu", stagger=bad)
+
+
 def test_views_share_the_buffer():
     fs = L.FlatState([3, 7], {"x": torch.float32}, device="cpu")
     fs.buffers["x"].zero_()
