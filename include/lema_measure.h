@@ -60,8 +60,10 @@ lema_status lema_table_cache_stats(int64_t out[4]);
 
 /* The LDS size per compute unit the current device reports, and the LDS the
  * AdamW step (delta on) reserves per workgroup (the kernel uses none) to cap
- * how many of its workgroups share a CU: 13, or 10 when the step reads
+ * how many of its workgroups share a CU: 12, or 9 when the step reads
  * `microbatches` >= 4 resident micro-batch gradients (0 = an ordinary step).
+ * LDS goes to a workgroup in 1280-byte granules on gfx950, so the
+ * reservation is a whole number of granules.
  * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE (microbatches < 0), LEMA_ERR_HIP. */
 lema_status lema_step_lds_reservation(int32_t microbatches, int32_t *lds_per_cu,
                                       int32_t *reserved_bytes);
