@@ -61,9 +61,10 @@ lema_status lema_table_cache_stats(int64_t out[4]);
 /* The LDS size per compute unit the current device reports, and the LDS the
  * AdamW step (delta on) reserves per workgroup (the kernel uses none) to cap
  * how many of its workgroups share a CU: 12, or 9 when the step reads
- * `microbatches` >= 4 resident micro-batch gradients (0 = an ordinary step).
- * LDS goes to a workgroup in 1280-byte granules on gfx950, so the
- * reservation is a whole number of granules.
+ * `microbatches` >= 4 resident micro-batch gradients (0 = an ordinary step),
+ * for launches of 2^18 tiles or more (smaller launches: 16, see
+ * lema_step_occupancy kernel 3).  LDS goes to a workgroup in 1280-byte
+ * granules on gfx950, so the reservation is a whole number of granules.
  * Errors: LEMA_ERR_NULL, LEMA_ERR_SIZE (microbatches < 0), LEMA_ERR_HIP. */
 lema_status lema_step_lds_reservation(int32_t microbatches, int32_t *lds_per_cu,
                                       int32_t *reserved_bytes);
@@ -86,10 +87,12 @@ lema_status lema_probe_residency(uint64_t *records, int32_t workgroups, int32_t 
 /*
  * The occupancy plan of a step kernel on the current device, for checking
  * with lema_probe_residency.  `kernel`:
- *   0  the fp32 AdamW step (bf16 gradient, delta on)
+ *   0  the fp32 AdamW step (bf16 gradient, delta on), launches of 2^18
+ *      tiles or more
  *   1  the fp32 step on 8 resident bf16 micro-batches (delta on)
  *   2  the int8-moment step, 256-lane wave-row workgroups (bf16 gradient,
  *      delta on)
+ *   3  the fp32 AdamW step in launches of fewer than 2^18 tiles
  * out[0] lanes per workgroup, out[1] the kernel's static LDS bytes, out[2]
  * the dynamic LDS bytes a launch reserves, out[3] the workgroups per CU the
  * reservation is meant to allow, out[4] the workgroups per CU its registers

@@ -768,7 +768,8 @@ def probe_residency(lanes: int, lds_bytes: int, *, per_cu: int = 40, spin_us: in
 
 def step_occupancy(kernel: int) -> dict:
     """The occupancy plan of step kernel `kernel` (lema_step_occupancy):
-    0 fp32 step, 1 fp32 step on 8 resident micro-batches, 2 int8 step."""
+    0 fp32 step, 1 fp32 step on 8 resident micro-batches, 2 int8 step, 3 fp32
+    step in launches of fewer than 2^18 tiles."""
     out = (ctypes.c_int32 * 6)()
     N.check(N.load().lema_step_occupancy(kernel, out), "lema_step_occupancy")
     keys = ("lanes", "static_lds", "reserved_lds", "intended_per_cu", "per_cu_by_registers",

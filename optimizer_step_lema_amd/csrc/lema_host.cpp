@@ -381,6 +381,14 @@ lema_status launch_on_table(const std::vector<unsigned char> &bytes, hipStream_t
 constexpr int kStepWorkgroupsPerCu = 12;
 constexpr int kStepWorkgroupsPerCuManyMb = 9;
 constexpr int kManyMicrobatches = 4;
+// Launches of fewer tiles than this (under 64 rounds of 16 per CU over 256
+// CUs) ramp up and drain for a larger share of their time and do better
+// with 16 per CU: the rank-16 LoRA step (156 K tiles) 0.2214 against
+// 0.2270 ms at 12, GPT-2 c_attn (13.8 K tiles) 21.84 against 22.20 us under
+// the tracer (MI355X, interleaved runs on one box); the attention workload
+// (1 M tiles) runs 2% slower at 16 than at 12.
+constexpr int kStepWorkgroupsPerCuSmall = 16;
+constexpr uint64_t kSmallLaunchTiles = uint64_t(1) << 18;
 
 // LDS goes to a workgroup in whole granules: its static and dynamic LDS
 // together, rounded up to a multiple of the granule.  On gfx950 the granule
@@ -461,13 +469,14 @@ uint32_t occupancy_lds_bytes(const void *fn, int workgroups_per_cu) {
     return total > fixed ? total - fixed : 0;
 }
 
-int step_workgroups_per_cu(int nmb) {
-    return nmb >= kManyMicrobatches ? kStepWorkgroupsPerCuManyMb : kStepWorkgroupsPerCu;
+int step_workgroups_per_cu(int nmb, uint64_t tiles) {
+    if (nmb >= kManyMicrobatches) return kStepWorkgroupsPerCuManyMb;
+    return tiles < kSmallLaunchTiles ? kStepWorkgroupsPerCuSmall : kStepWorkgroupsPerCu;
 }
 
-uint32_t step_lds_bytes_for(GradMode grad_mode, bool with_delta, int nmb) {
+uint32_t step_lds_bytes_for(GradMode grad_mode, bool with_delta, int nmb, uint64_t tiles) {
     return occupancy_lds_bytes(adamw_kernel_fn(grad_mode, with_delta, nmb),
-                               step_workgroups_per_cu(nmb));
+                               step_workgroups_per_cu(nmb, tiles));
 }
 
 lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts &c,
@@ -476,9 +485,9 @@ lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
     bool with_delta = false;
     for (const SegRec &r : recs) with_delta |= r.p[6] != 0;
-    const uint32_t lds = step_lds_bytes_for(grad_mode, with_delta, 0);
     TableBuild tb;
     build_table(recs, &tb);
+    const uint32_t lds = step_lds_bytes_for(grad_mode, with_delta, 0, tb.total_tiles);
     return launch_on_table(tb.bytes, stream, [&](const void *table) {
         return launch_adamw(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_mode,
                             with_delta, c, stream, 0, lds);
@@ -495,9 +504,9 @@ lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<ui
         with_delta |= recs[i].p[6] != 0;
         recs[i].p[3] = table_bytes(n) + sizeof(uint64_t) * size_t(nmb) * size_t(i);
     }
-    const uint32_t lds = step_lds_bytes_for(kGradBf16Sum, with_delta, nmb);
     TableBuild tb;
     build_table(recs, &tb);
+    const uint32_t lds = step_lds_bytes_for(kGradBf16Sum, with_delta, nmb, tb.total_tiles);
     tb.bytes.resize(table_bytes(n) + sizeof(uint64_t) * lists.size());
     std::memcpy(tb.bytes.data() + table_bytes(n), lists.data(), sizeof(uint64_t) * lists.size());
     return launch_on_table(tb.bytes, stream, [&](const void *table) {
@@ -800,8 +809,8 @@ lema_status lema_step_lds_reservation(int32_t microbatches, int32_t *lds_per_cu,
     *lds_per_cu = d->lds_per_cu;
     *reserved_bytes = static_cast<int32_t>(
         microbatches >= 1 && microbatches <= kMaxMicrobatches
-            ? step_lds_bytes_for(kGradBf16Sum, true, microbatches)
-            : step_lds_bytes_for(kGradBf16, true, 0));
+            ? step_lds_bytes_for(kGradBf16Sum, true, microbatches, kSmallLaunchTiles)
+            : step_lds_bytes_for(kGradBf16, true, 0, kSmallLaunchTiles));
     return LEMA_OK;
 }
 
@@ -829,11 +838,15 @@ lema_status lema_step_occupancy(int32_t kernel, int32_t out[6]) {
     switch (kernel) {
     case 0:
         fn = adamw_kernel_fn(kGradBf16, true, 0);
-        per_cu = step_workgroups_per_cu(0);
+        per_cu = step_workgroups_per_cu(0, kSmallLaunchTiles);
         break;
     case 1:
         fn = adamw_kernel_fn(kGradBf16Sum, true, 8);
-        per_cu = step_workgroups_per_cu(8);
+        per_cu = step_workgroups_per_cu(8, kSmallLaunchTiles);
+        break;
+    case 3:
+        fn = adamw_kernel_fn(kGradBf16, true, 0);
+        per_cu = step_workgroups_per_cu(0, 0);
         break;
     case 2:
         fn = adamw_q8_kernel_fn(true, kQGradBf16, true, kQBlock, kQRowsWave);

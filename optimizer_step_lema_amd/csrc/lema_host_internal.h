@@ -104,9 +104,9 @@ int register_occupancy(const void *fn, int lanes);
 // Compute units of the current device (0 if it cannot be queried).
 int compute_units();
 // Workgroups of the fp32 AdamW step allowed per CU when it reads `nmb`
-// resident micro-batches (0 for the other gradient modes), and the dynamic
-// LDS its kernel reserves for that.
-int step_workgroups_per_cu(int nmb);
-uint32_t step_lds_bytes_for(GradMode grad_mode, bool with_delta, int nmb);
+// resident micro-batches (0 for the other gradient modes) in a launch of
+// `tiles` tiles, and the dynamic LDS its kernel reserves for that.
+int step_workgroups_per_cu(int nmb, uint64_t tiles);
+uint32_t step_lds_bytes_for(GradMode grad_mode, bool with_delta, int nmb, uint64_t tiles);
 
 }  // namespace lema

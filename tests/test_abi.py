@@ -309,5 +309,5 @@ def test_residency_probe_validation(lib):
     assert lib.lema_probe_residency(rec + 4, 10, 64, 0, 20, None) == N.LEMA_ERR_ALIGN
     out = (ctypes.c_int32 * 6)()
     assert lib.lema_step_occupancy(0, None) == N.LEMA_ERR_NULL
-    assert lib.lema_step_occupancy(3, out) == N.LEMA_ERR_SIZE
+    assert lib.lema_step_occupancy(4, out) == N.LEMA_ERR_SIZE
     assert lib.lema_step_occupancy(-1, out) == N.LEMA_ERR_SIZE

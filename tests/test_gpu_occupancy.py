@@ -12,7 +12,9 @@ import optimizer_step_lema_amd as L
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = {0: "fp32 step", 1: "fp32 step, 8 resident micro-batches", 2: "int8 step"}
+KERNELS = {0: "fp32 step", 1: "fp32 step, 8 resident micro-batches", 2: "int8 step",
+           3: "fp32 step, launches under 2^18 tiles"}
+INTENDED = {0: 12, 1: 9, 2: 3, 3: 16}
 
 
 @pytest.mark.parametrize("kernel", sorted(KERNELS))
@@ -23,6 +25,7 @@ def test_reservation_gives_intended_count(kernel):
     assert lds % plan["lds_granule"] == 0          # whole granules: nothing rounds up
     got = L.probe_residency(plan["lanes"], lds)
     assert got["cus_seen"] == L.device_info()["compute_units"]
+    assert plan["intended_per_cu"] == INTENDED[kernel]
     assert got["max_per_cu"] == got["min_per_cu"] == plan["intended_per_cu"]
     # registers alone would allow at least as many
     assert plan["per_cu_by_registers"] >= plan["intended_per_cu"]
