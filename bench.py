@@ -94,6 +94,9 @@ def parse():
     ap.add_argument("--layout", choices=("flat", "per-tensor"), default="flat",
                     help="flat: one buffer per array kind, tensors as views (flat optimizer "
                          "state); per-tensor: every array of every tensor allocated on its own")
+    ap.add_argument("--stagger", type=int, default=4096,
+                    help="flat layout: the k-th array kind's buffer starts k * STAGGER bytes "
+                         "into its allocation (a multiple of 256; 0 = no offsets)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-gib", type=float, default=4.0, help="size of the copy-ceiling test")
@@ -313,7 +316,8 @@ def resident_bench(torch, L, synth, a):
     # working set exceeds the 256 MB last-level cache between launches
     nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
     t_setup = time.perf_counter()
-    sets = [resident_state(torch, L, synth, w, a.layout, delta, grad_f32, resident_mb)
+    sets = [resident_state(torch, L, synth, w, a.layout, delta, grad_f32, resident_mb,
+                           a.stagger)
             for _ in range(nsets)]
     torch.cuda.synchronize()
     progress(f"{a.workload}: {nsets} state set(s) of {P} params resident "
@@ -405,6 +409,7 @@ def resident_bench(torch, L, synth, a):
             "bytes_per_step": per_step,
             "rotated_state_sets": nsets,
             "layout": a.layout,
+            "kind_offset_bytes": a.stagger if a.layout == "flat" else None,
         },
         "hbm_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
@@ -466,7 +471,7 @@ def same_bytes_copy(torch, L, stream, nbytes, nsets, steps):
             "min_launch_ms": min(ms), "gbps": 2 * half / (avg * 1e-3) / 1e9}
 
 
-def resident_state(torch, L, synth, w, layout, delta, grad_f32, resident_mb):
+def resident_state(torch, L, synth, w, layout, delta, grad_f32, resident_mb, stagger=4096):
     """One state set of the workload on the GPU: (segments, [(accumulator or
     None, [bf16 micro-batch gradients])]) plus the buffers that back them.
 
@@ -480,7 +485,7 @@ def resident_state(torch, L, synth, w, layout, delta, grad_f32, resident_mb):
         nmb = K if (grad_f32 or resident_mb) else 0
         fs, segs = L.flat_adamw_state(
             w.numels, grad=None if resident_mb else (torch.float32 if grad_f32 else torch.bfloat16),
-            delta=delta, microbatches=nmb, device=dev)
+            delta=delta, microbatches=nmb, device=dev, stagger=stagger)
         for i in range(len(w.segments)):
             st = synth.make_segment_state(w, i, dev, with_orig=delta)
             s = segs[i]
@@ -643,7 +648,8 @@ def q8_bench(torch, L, synth, a):
 
     nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
     t_setup = time.perf_counter()
-    sets = [q8_state(torch, L, synth, w, row_lens, a.layout, delta) for _ in range(nsets)]
+    sets = [q8_state(torch, L, synth, w, row_lens, a.layout, delta, a.stagger)
+            for _ in range(nsets)]
     torch.cuda.synchronize()
     progress(f"{a.workload}: {nsets} int8 state set(s) of {P} params resident "
              f"({time.perf_counter() - t_setup:.1f} s)")
@@ -709,6 +715,7 @@ def q8_bench(torch, L, synth, a):
             "bytes_per_param": per_step / P, "bytes_per_step": per_step,
             "rotated_state_sets": nsets,
             "layout": a.layout,
+            "kind_offset_bytes": a.stagger if a.layout == "flat" else None,
         },
         "hbm_gbps": gbps,
         "pct_hbm_peak": 100.0 * gbps / HBM_PEAK_GBPS,
@@ -741,7 +748,7 @@ def q8_bench(torch, L, synth, a):
     return line
 
 
-def q8_state(torch, L, synth, w, row_lens, layout, delta):
+def q8_state(torch, L, synth, w, row_lens, layout, delta, stagger=4096):
     """One int8-moment state set on the GPU: (segments, [(int8 accumulator,
     [bf16 micro-batch gradients])], buffers).  The moments are the seeded fp32
     draws quantized by lema_quantize_rows; `layout` as for resident_state."""
@@ -750,7 +757,7 @@ def q8_state(torch, L, synth, w, row_lens, layout, delta):
     accs = []
     if layout == "flat":
         el, rw, segs = L.flat_q8_state(w.numels, row_lens, grad="q8" if K > 1 else "bf16",
-                                       delta=delta, device=dev)
+                                       delta=delta, device=dev, stagger=stagger)
         mbs = [L.FlatState(w.numels, {"g": torch.bfloat16}, device=dev) for _ in range(K)] \
             if K > 1 else []
         for i in range(len(w.segments)):
@@ -828,7 +835,8 @@ def merge_bench(torch, L, synth, a):
     P = w.params
     segs = []
     fs = L.FlatState(w.numels, {"base": torch.bfloat16, "delta": torch.float32,
-                                "merged": torch.bfloat16}) if a.layout == "flat" else None
+                                "merged": torch.bfloat16},
+                     stagger=a.stagger) if a.layout == "flat" else None
     for i in range(len(w.segments)):
         n = w.numels[i]
         base = synth.bf16_normal(n, 0.02, synth.seed_of(w.wid, 0, i), "cuda")
@@ -859,7 +867,8 @@ def merge_bench(torch, L, synth, a):
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": a.workload, "params": P, "segments": len(w.segments),
-                   "bytes_per_param": 8, "rotated_state_sets": nsets, "layout": a.layout},
+                   "bytes_per_param": 8, "rotated_state_sets": nsets, "layout": a.layout,
+                   "kind_offset_bytes": a.stagger if a.layout == "flat" else None},
         "hbm_gbps": gbps, "pct_hbm_peak": 100 * gbps / HBM_PEAK_GBPS,
         "copy_ceiling_gbps": copy_gbps,
         "roofline": {"bound": "hbm", "achieved": gbps, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

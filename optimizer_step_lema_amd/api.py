@@ -277,7 +277,7 @@ class FlatState:
 
 def flat_adamw_state(numels: Sequence[int], *, grad: Optional[torch.dtype] = torch.bfloat16,
                      delta: bool = False, microbatches: int = 0,
-                     device="cuda") -> tuple[FlatState, list]:
+                     device="cuda", stagger: int = 4096) -> tuple[FlatState, list]:
     """AdamW state for tensors of the given sizes in flat buffers.
 
     Kinds: master, exp_avg, exp_avg_sq (fp32), weight (bf16 output), grad
@@ -297,7 +297,7 @@ def flat_adamw_state(numels: Sequence[int], *, grad: Optional[torch.dtype] = tor
         kinds["delta"] = torch.float32
     for k in range(microbatches):
         kinds[f"mb{k}"] = torch.bfloat16
-    fs = FlatState(numels, kinds, device=device)
+    fs = FlatState(numels, kinds, device=device, stagger=stagger)
     fs.buffers["exp_avg"].zero_()
     fs.buffers["exp_avg_sq"].zero_()
     segs = [AdamwSegment(fs.view("master", i), fs.view("exp_avg", i), fs.view("exp_avg_sq", i),
@@ -483,7 +483,8 @@ class AdamwQ8Segment:
 
 
 def flat_q8_state(numels: Sequence[int], row_lens: Sequence[int], *, grad: str = "bf16",
-                  delta: bool = False, device="cuda") -> tuple[FlatState, FlatState, list]:
+                  delta: bool = False, device="cuda",
+                  stagger: int = 4096) -> tuple[FlatState, FlatState, list]:
     """int8-moment AdamW state for tensors of the given sizes in flat buffers.
 
     Element kinds: master (fp32), weight (bf16 output), m and v codes (int8),
@@ -501,12 +502,12 @@ def flat_q8_state(numels: Sequence[int], row_lens: Sequence[int], *, grad: str =
     if delta:
         kinds["orig"] = torch.bfloat16
         kinds["delta"] = torch.float32
-    el = FlatState(numels, kinds, device=device)
+    el = FlatState(numels, kinds, device=device, stagger=stagger)
     rows = [Q8.rows_of(int(n), int(rl)) for n, rl in zip(numels, row_lens)]
     rk = {"m": torch.float32, "v": torch.float32}
     if grad == "q8":
         rk["grad"] = torch.float32
-    rw = FlatState(rows, rk, device=device)
+    rw = FlatState(rows, rk, device=device, stagger=stagger)
     for fs in (el, rw):
         for k in rk:
             fs.buffers[k].zero_()
