@@ -79,3 +79,70 @@ def test_llama7b_full_every_element():
     assert checked == 5 * w.params
     print(f"full 7B: {checked} output elements bit-exact ({time.perf_counter() - t0:.0f} s)",
           flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_llama7b_full_q8_every_element():
+    """The whole 7B shape with int8 moments (rows = the weights' last
+    dimension, one fp32 scale per row), bf16 gradient and delta, in the flat
+    int8 state bench.py --q8 times, one lema_adamw_step_q8 call: every
+    output element compared with the oracle, segment by segment (master,
+    weight and delta bit for bit, every int8 code as an integer, every row
+    scale bit for bit).  Host snapshots: 10 B per parameter, 67 GB."""
+    import oracle
+    import optimizer_step_lema_amd as L
+
+    w = synth.WORKLOADS["llama7b_full"]
+    row_lens = [shape[-1] for _, shape in w.segments]
+    t0 = time.perf_counter()
+    _, _, segs = L.flat_q8_state(w.numels, row_lens, grad="bf16", delta=True, device="cuda")
+    snaps = []
+    for i, s in enumerate(segs):
+        st = synth.make_segment_state(w, i, "cuda", with_orig=True)
+        s.master.copy_(st["master"])
+        L.quantize_rows([(st["m"], s.exp_avg), (st["v"], s.exp_avg_sq)])
+        s.grad.copy_(st["grads"][0])
+        s.orig.copy_(st["orig"])
+        del st
+        snaps.append({"master": to_np(s.master), "grad": to_np(s.grad), "orig": to_np(s.orig),
+                      "m": (to_np(s.exp_avg.codes), to_np(s.exp_avg.scale)),
+                      "v": (to_np(s.exp_avg_sq.codes), to_np(s.exp_avg_sq.scale))})
+        if i % 64 == 0:
+            print(f"full 7B q8: snapshot of segment {i}/{len(segs)} "
+                  f"({time.perf_counter() - t0:.0f} s)", flush=True)
+    L.AdamwQ8Plan(segs).step(step=w.step, **HP)
+    torch.cuda.synchronize()
+    print(f"full 7B q8: stepped ({time.perf_counter() - t0:.0f} s)", flush=True)
+
+    consts = oracle_consts(HP, w.step)
+    checked = 0
+    for i, (s, rl) in enumerate(zip(segs, row_lens)):
+        b = snaps[i]
+        master = b["master"].copy()
+        wref, dref = oracle.adamw_step_q8(master, b["m"], b["v"], b["grad"], consts, rl,
+                                          orig=b["orig"])
+        tag = f"7b q8 seg{i} {w.segments[i][0]}"
+        for got, ref, name, kind in ((s.master, master, "master", "f"),
+                                     (s.weight, wref, "weight", "b"),
+                                     (s.delta, dref, "delta", "f"),
+                                     (s.exp_avg.scale, b["m"][1], "m.scale", "f"),
+                                     (s.exp_avg_sq.scale, b["v"][1], "v.scale", "f")):
+            g = to_np(got)
+            if not _same_bits(g, ref):
+                if kind == "f":
+                    compare_f32(g, ref, f"{tag}.{name}")
+                else:
+                    compare_bf16(g, ref, f"{tag}.{name}")
+            checked += g.size if name in ("master", "weight", "delta") else 0
+        for got, ref, name in ((s.exp_avg.codes, b["m"][0], "m.codes"),
+                               (s.exp_avg_sq.codes, b["v"][0], "v.codes")):
+            bad = int(np.count_nonzero(to_np(got) != ref))
+            assert bad == 0, f"{tag}.{name}: {bad} int8 codes differ"
+            checked += ref.size
+        snaps[i] = None
+        if i % 64 == 0:
+            print(f"full 7B q8: segment {i}/{len(segs)} equal ({time.perf_counter() - t0:.0f} s)",
+                  flush=True)
+    assert checked == 5 * w.params
+    print(f"full 7B q8: {checked} output elements and every row scale bit-exact "
+          f"({time.perf_counter() - t0:.0f} s)", flush=True)
