@@ -196,36 +196,45 @@ COPY_KIB = 2 * (1 << 30) / 1024          # lema_measure_copy in copy_ceiling: 2 
 
 
 def fold_counters(key, fetch_csv, write_csv):
-    """Per-dispatch FETCH_SIZE and WRITE_SIZE (KiB, summed over the counter's
-    instances) of the key's kernel, each scaled by what the same counter read
-    for the copy kernel's known 2 GiB read + 2 GiB write in the same run, into
-    the record's entry for `key`, stamped with the digest of the kernel's
-    current sources (entries whose kernel has changed since are dropped)."""
+    """FETCH_SIZE and WRITE_SIZE per step (KiB, summed over the counter's
+    instances and over the step's launches of the key's kernel), each scaled
+    by what the same counter read for the copy kernel's known 2 GiB read +
+    2 GiB write in the same run, into the record's entry for `key`, stamped
+    with the digest of the kernel's current sources (entries whose kernel
+    has changed since are dropped).  A step's launches are told apart by
+    their grid sizes: each appears once per step, so the number of steps is
+    the smallest count of dispatches of one grid size (steps whose launches
+    share a grid size are counted as one launch per step)."""
     import csv
 
-    def per_dispatch(path, kernel, counter, grid=None):
-        vals = {}
+    def per_step(path, kernel, counter, grid=None):
+        vals, grids = {}, {}
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row["Kernel_Name"].strip('"') != kernel or row["Counter_Name"] != counter:
                     continue
                 if grid is not None and int(row["Grid_Size"]) != grid:
                     continue
-                vals[row["Dispatch_Id"]] = vals.get(row["Dispatch_Id"], 0.0) + \
-                    float(row["Counter_Value"])
+                d = row["Dispatch_Id"]
+                vals[d] = vals.get(d, 0.0) + float(row["Counter_Value"])
+                grids[d] = int(row["Grid_Size"])
         if not vals:
             raise SystemExit(f"bench.py: no {counter} rows for {kernel} in {path}")
-        return sum(vals.values()) / len(vals), len(vals)
+        per_grid = {}
+        for d, g in grids.items():
+            per_grid[g] = per_grid.get(g, 0) + 1
+        steps = min(per_grid.values())
+        return sum(vals.values()) / steps, steps, len(vals) / steps
 
     kernel, alg = counter_key_bytes(key)
     layout = "flat"
-    fk, nd = per_dispatch(fetch_csv, kernel, "FETCH_SIZE")
-    wk, _ = per_dispatch(write_csv, kernel, "WRITE_SIZE")
+    fk, nd, launches = per_step(fetch_csv, kernel, "FETCH_SIZE")
+    wk, _, _ = per_step(write_csv, kernel, "WRITE_SIZE")
     # the reference is copy_ceiling's copy of 2 GiB each way (one 16-byte
     # vector per work-item); small workloads also run same_bytes_copy
     ref_grid = int(COPY_KIB * 1024) // 16
-    cf, _ = per_dispatch(fetch_csv, "copy_kernel", "FETCH_SIZE", ref_grid)
-    cw, _ = per_dispatch(write_csv, "copy_kernel", "WRITE_SIZE", ref_grid)
+    cf, _, _ = per_step(fetch_csv, "copy_kernel", "FETCH_SIZE", ref_grid)
+    cw, _, _ = per_step(write_csv, "copy_kernel", "WRITE_SIZE", ref_grid)
     ff, wf = cf / COPY_KIB, cw / COPY_KIB
     read, written = fk * 1024 / ff, wk * 1024 / wf
     rec = json.load(open(COUNTERS)) if os.path.exists(COUNTERS) else {}
@@ -248,7 +257,9 @@ def fold_counters(key, fetch_csv, write_csv):
     rec["kernel_sources"] = {k: v + ["compiler flags: optimizer_step_lema_amd.build.FLAGS"]
                              for k, v in KERNEL_SOURCES.items()}
     rec["workloads"][key] = {
-        "kernel": kernel, "kernel_digest": kernel_digest(kernel), "layout": layout, "dispatches": nd, "fetch_kib": fk, "write_kib": wk,
+        "kernel": kernel, "kernel_digest": kernel_digest(kernel), "layout": layout,
+        "dispatches": round(nd * launches), "steps": nd, "launches_per_step": launches,
+        "fetch_kib": fk, "write_kib": wk,
         "copy_fetch_kib": cf, "copy_write_kib": cw, "fetch_factor": ff, "write_factor": wf,
         "read_bytes": read, "written_bytes": written,
         "traffic_bytes_per_launch": read + written,

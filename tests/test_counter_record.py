@@ -117,3 +117,28 @@ def test_fold_counters(tmp_path, monkeypatch):
     assert bench.traffic_for(key, "flat") == pytest.approx(alg)
     with pytest.raises(SystemExit):
         bench.counter_key_bytes("llama7b_layer:delta")   # a multi-launch step has no entry
+
+
+def test_fold_counters_two_launches_per_step(tmp_path, monkeypatch):
+    """A step of two launches of different grid sizes (the int8 step over
+    rows of 4096 and rows of 11,008): the entry holds the bytes of a whole
+    step, the sum over its launches, not the mean of one dispatch."""
+    rec_path = tmp_path / "counters.json"
+    monkeypatch.setattr(bench, "COUNTERS", str(rec_path))
+    key = "llama7b_full:q8:delta"
+    alg = algorithmic(key)
+    parts = [(0.7, 1000), (0.3, 4000)]                 # share of the bytes, grid size
+    fetch = [(1, "copy_kernel", COPY_KIB / 2)]
+    write = [(1, "copy_kernel", COPY_KIB)]
+    d = 2
+    for _ in range(3):                                 # three steps
+        for share, grid in parts:
+            fetch.append((d, "adamw_q8_kernel", share * alg * 10 / 22 / 1024 / 2, grid))
+            write.append((d, "adamw_q8_kernel", share * alg * 12 / 22 / 1024, grid))
+            d += 1
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", fetch)
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", write)
+    bench.fold_counters(key, str(tmp_path / "f.csv"), str(tmp_path / "w.csv"))
+    e = json.loads(rec_path.read_text())["workloads"][key]
+    assert e["dispatches"] == 6 and e["steps"] == 3 and e["launches_per_step"] == 2
+    assert e["traffic_over_algorithmic"] == pytest.approx(1.0)
