@@ -114,6 +114,8 @@ def parse():
                     help="with --slot-stream: stream only the first L loads (0 = all 34)")
     ap.add_argument("--duplex", action="store_true",
                     help="with --slot-stream: slot -> host copies on a stream of their own")
+    ap.add_argument("--slots", type=int, default=2,
+                    help="with --slot-stream: HBM slots in the pool (default 2)")
     ap.add_argument("--host-gib", type=float, default=0.0,
                     help="with --slot-stream: host state to stage at most (default: 56 GiB "
                          "page-locked, 120 GiB with --staged)")
@@ -966,7 +968,7 @@ def slot_stream_bench(torch, L, synth, a):
     # device side first: the pool's slots, then the standalone pinned copy
     # ceilings (half a slot each way); host staging comes last because the
     # GPU-mappable page-locked memory of a host is bounded
-    pool = L.SlotPool(slot_bytes, nslots=2, duplex=a.duplex)
+    pool = L.SlotPool(slot_bytes, nslots=a.slots, duplex=a.duplex)
     stream = torch.cuda.current_stream()
     hbuf = L.pinned_empty(slot_bytes // 2, torch.uint8)
     dbuf = torch.empty(slot_bytes // 2, dtype=torch.uint8, device="cuda")
@@ -1059,7 +1061,7 @@ def slot_stream_bench(torch, L, synth, a):
         "dtype": "f32 arithmetic; int8 moments" if q8 else "f32",
         "data": "synthetic",
         "config": {"workload": "llama7b_full_streamed", "loads": len(loads),
-                   "loads_requested": requested, "params": P, "slots": 2,
+                   "loads_requested": requested, "params": P, "slots": a.slots,
                    "slot_bytes": slot_bytes, "grad": "bf16", "delta": False,
                    "copy_streams": 2 if a.duplex else 1, "step_t": w.step,
                    "host_memory": "pageable, staged" if a.staged else "page-locked",
