@@ -619,7 +619,11 @@ def pinned_empty(numel: int, dtype: torch.dtype) -> torch.Tensor:
 class SlotPool:
     """A pool of `nslots` HBM slots of `slot_bytes` each, with its own copy and
     compute streams (default priority), for lema_slot_stream.  With
-    duplex=True the slot -> host copies get a third stream of their own."""
+    duplex=True the slot -> host copies get a third stream of their own.
+    In duplex, layer i's upload into slot i mod nslots waits for the
+    write-back of the layer that used the slot before; with 3 slots that
+    write-back is long done, and on MI355X the whole 7B shape's staged
+    duplex step was 2-4% faster than with 2 and its kernels fully hidden."""
 
     def __init__(self, slot_bytes: int, nslots: int = 2, duplex: bool = False):
         lib = N.load()
