@@ -284,6 +284,13 @@ def main():
               "(sharded) layout is measured on one rank's share instead "
               "(--workload llama7b_full_shard8)", file=sys.stderr)
         sys.exit(2)
+    if a.stagger < 0 or a.stagger % 256:
+        print(f"bench.py: --stagger {a.stagger}: a non-negative multiple of 256 bytes is needed",
+              file=sys.stderr)
+        sys.exit(2)
+    if a.slots < 2:
+        print(f"bench.py: --slots {a.slots}: a slot pool needs at least 2 slots", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import optimizer_step_lema_amd as L
