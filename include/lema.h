@@ -44,7 +44,10 @@
  *   - Calls that launch kernels refuse a stream that is capturing a HIP
  *     graph (LEMA_ERR_CAPTURE, nothing enqueued): their launch tables live
  *     in a cache whose entries may be reused after the call, which a
- *     captured graph would outlive.
+ *     captured graph would outlive.  (A table of at most 2048 bytes of the
+ *     fp32 step, accumulation and merge travels in the kernel arguments
+ *     instead; those calls are refused as well, so that whether a call may
+ *     be captured does not depend on its segment count.)
  *   - Nothing aborts, throws or prints across this ABI.
  *   - The caller owns all tensors, streams and the step counter t; the
  *     library is stateless apart from caches of small launch tables.

@@ -54,7 +54,9 @@ lema_status lema_probe_q8_reciprocal(const float *s, float *r, int64_t n, void *
  * Counters of the current device's launch-table cache since the library was
  * loaded: out[0] calls that found their table cached, out[1] tables uploaded,
  * out[2] uploads that had to wait for a pending launch, out[3] cached
- * entries.  Errors: LEMA_ERR_NULL, LEMA_ERR_HIP.
+ * entries.  Launches whose table travels in the kernel arguments (fp32
+ * tables of at most 2048 bytes) count in none of them.  Errors:
+ * LEMA_ERR_NULL, LEMA_ERR_HIP.
  */
 lema_status lema_table_cache_stats(int64_t out[4]);
 

@@ -122,9 +122,35 @@ __device__ __forceinline__ void tile_st(__amdgpu_buffer_rsrc_t r, int lane, T v)
                                               kTileStorePolicy);
 }
 
+// Launch tables are read through the constant address space, whether they
+// sit in device memory or in the kernel arguments: their reads are uniform
+// over a wavefront and stay scalar loads.
+#define LEMA_CONST __attribute__((address_space(4)))
+typedef const LEMA_CONST unsigned char *ktable_t;
+
+// The launch table of a tile kernel: the device copy when `table` is set,
+// else the copy carried in the kernel arguments (a by-value kernel argument
+// lives in the kernel-argument segment, so `inl` is read in place there).
+__device__ __forceinline__ ktable_t launch_table(const void *table, const InlineTable &inl) {
+    return table != nullptr ? (ktable_t)table : (ktable_t)&inl;
+}
+
+// A record read from a launch table, one 8-byte word at a time.
+template <class Rec>
+__device__ __forceinline__ Rec table_record(ktable_t recs, int s) {
+    static_assert(sizeof(Rec) % 8 == 0, "records are whole 8-byte words");
+    struct Words {
+        uint64_t w[sizeof(Rec) / 8];
+    } out;
+    const LEMA_CONST uint64_t *src = (const LEMA_CONST uint64_t *)(recs + sizeof(Rec) * size_t(s));
+#pragma unroll
+    for (size_t i = 0; i < sizeof(Rec) / 8; ++i) out.w[i] = src[i];
+    return __builtin_bit_cast(Rec, out);
+}
+
 // The segment holding tile t: the last s with tile_begin[s] <= t.  The
 // table guarantees tile_begin[0] = 0 <= t < tile_begin[nseg].
-__device__ __forceinline__ int find_segment(const uint32_t *__restrict__ tile_begin, int nseg,
+__device__ __forceinline__ int find_segment(const LEMA_CONST uint32_t *tile_begin, int nseg,
                                             uint32_t t) {
     int lo = 0, hi = nseg;
     while (hi - lo > 1) {
@@ -141,14 +167,18 @@ __device__ __forceinline__ int find_segment(const uint32_t *__restrict__ tile_be
 // Table layout: uint32_t begin[nseg + 1] (prefix sums of blocks per segment),
 // padded to 64 bytes, then Rec[nseg].
 template <class Rec, class Fn>
-__device__ __forceinline__ void block_of_table(const void *table, int nseg, uint32_t block0,
+__device__ __forceinline__ void block_of_table(ktable_t table, int nseg, uint32_t block0,
                                                const Fn &fn) {
-    const uint32_t *begin = static_cast<const uint32_t *>(table);
-    const Rec *recs = reinterpret_cast<const Rec *>(static_cast<const char *>(table) +
-                                                    table_tiles_bytes(nseg));
+    const LEMA_CONST uint32_t *begin = (const LEMA_CONST uint32_t *)table;
     const uint32_t t = block0 + blockIdx.x;
     const int s = find_segment(begin, nseg, t);
-    fn(recs[s], t - begin[s]);
+    fn(table_record<Rec>(table + table_tiles_bytes(nseg), s), t - begin[s]);
+}
+
+template <class Rec, class Fn>
+__device__ __forceinline__ void block_of_table(const void *table, int nseg, uint32_t block0,
+                                               const Fn &fn) {
+    block_of_table<Rec>((ktable_t)table, nseg, block0, fn);
 }
 
 }  // namespace dev

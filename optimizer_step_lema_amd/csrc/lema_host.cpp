@@ -352,16 +352,45 @@ uint64_t count_tiles(const std::vector<SegRec> &recs) {
 
 }  // namespace
 
+namespace {
+
+// Launches are refused under stream capture: a captured graph would keep
+// using a table the cache may later reuse.  Tables that travel in the kernel
+// arguments are refused too, so that whether a call may be captured does
+// not depend on its segment count.
+lema_status refuse_capture(hipStream_t stream) {
+    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+    hipError_t ce = hipStreamIsCapturing(stream, &capture);
+    if (ce != hipSuccess) return hip_failed(ce);
+    return capture != hipStreamCaptureStatusNone ? LEMA_ERR_CAPTURE : LEMA_OK;
+}
+
+// An fp32 tile-kernel launch: a table of up to kInlineTableBytes goes in the
+// kernel arguments, with no cache entry and no event; a larger one goes
+// through the device cache.
+lema_status launch_tile_table(
+    const std::vector<unsigned char> &bytes, hipStream_t stream,
+    const std::function<hipError_t(const void *, const InlineTable *)> &launch) {
+    if (bytes.size() > kInlineTableBytes)
+        return launch_on_table(bytes, stream,
+                               [&](const void *table) { return launch(table, nullptr); });
+    lema_status st = refuse_capture(stream);
+    if (st != LEMA_OK) return st;
+    InlineTable inl = {};
+    std::memcpy(inl.w, bytes.data(), bytes.size());
+    const hipError_t e = launch(nullptr, &inl);   // the arguments are copied at the launch
+    return e == hipSuccess ? LEMA_OK : hip_failed(e);
+}
+
+}  // namespace
+
 lema_status launch_on_table(const std::vector<unsigned char> &bytes, hipStream_t stream,
                             const std::function<hipError_t(const void *)> &launch) {
     DeviceState *d = nullptr;
     lema_status st = device_state(&d, nullptr);
     if (st != LEMA_OK) return st;
-    // a captured graph would keep using a table the cache may later reuse
-    hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
-    hipError_t ce = hipStreamIsCapturing(stream, &capture);
-    if (ce != hipSuccess) return hip_failed(ce);
-    if (capture != hipStreamCaptureStatusNone) return LEMA_ERR_CAPTURE;
+    st = refuse_capture(stream);
+    if (st != LEMA_OK) return st;
     std::lock_guard<std::mutex> lock(d->mu);
     TableEntry *t = nullptr;
     st = acquire_table(*d, bytes, stream, &t);
@@ -488,8 +517,8 @@ lema_status launch_adamw_recs(const std::vector<SegRec> &recs, const AdamwConsts
     TableBuild tb;
     build_table(recs, &tb);
     const uint32_t lds = step_lds_bytes_for(grad_mode, with_delta, 0, tb.total_tiles);
-    return launch_on_table(tb.bytes, stream, [&](const void *table) {
-        return launch_adamw(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_mode,
+    return launch_tile_table(tb.bytes, stream, [&](const void *table, const InlineTable *inl) {
+        return launch_adamw(table, inl, tb.nseg, static_cast<uint32_t>(tb.total_tiles), grad_mode,
                             with_delta, c, stream, 0, lds);
     });
 }
@@ -509,9 +538,9 @@ lema_status launch_adamw_sum_recs(std::vector<SegRec> recs, const std::vector<ui
     const uint32_t lds = step_lds_bytes_for(kGradBf16Sum, with_delta, nmb, tb.total_tiles);
     tb.bytes.resize(table_bytes(n) + sizeof(uint64_t) * lists.size());
     std::memcpy(tb.bytes.data() + table_bytes(n), lists.data(), sizeof(uint64_t) * lists.size());
-    return launch_on_table(tb.bytes, stream, [&](const void *table) {
-        return launch_adamw(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), kGradBf16Sum,
-                            with_delta, c, stream, nmb, lds);
+    return launch_tile_table(tb.bytes, stream, [&](const void *table, const InlineTable *inl) {
+        return launch_adamw(table, inl, tb.nseg, static_cast<uint32_t>(tb.total_tiles),
+                            kGradBf16Sum, with_delta, c, stream, nmb, lds);
     });
 }
 
@@ -521,8 +550,8 @@ lema_status launch_accum_recs(const std::vector<SegRec> &recs, bool overwrite,
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
     TableBuild tb;
     build_table(recs, &tb);
-    return launch_on_table(tb.bytes, stream, [&](const void *table) {
-        return launch_accum(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), overwrite,
+    return launch_tile_table(tb.bytes, stream, [&](const void *table, const InlineTable *inl) {
+        return launch_accum(table, inl, tb.nseg, static_cast<uint32_t>(tb.total_tiles), overwrite,
                             stream);
     });
 }
@@ -532,8 +561,8 @@ lema_status launch_merge_recs(const std::vector<SegRec> &recs, hipStream_t strea
     if (count_tiles(recs) > kMaxTiles) return LEMA_ERR_SIZE;
     TableBuild tb;
     build_table(recs, &tb);
-    return launch_on_table(tb.bytes, stream, [&](const void *table) {
-        return launch_merge(table, tb.nseg, static_cast<uint32_t>(tb.total_tiles), stream);
+    return launch_tile_table(tb.bytes, stream, [&](const void *table, const InlineTable *inl) {
+        return launch_merge(table, inl, tb.nseg, static_cast<uint32_t>(tb.total_tiles), stream);
     });
 }
 

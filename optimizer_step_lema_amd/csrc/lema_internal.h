@@ -63,6 +63,18 @@ constexpr size_t table_bytes(int nseg) {
     return table_tiles_bytes(nseg) + sizeof(SegRec) * size_t(nseg);
 }
 
+// A launch table of at most kInlineTableBytes can travel by value in the
+// kernel arguments of the fp32 tile kernels (adamw, accum, merge) instead of
+// through a device copy: up to 24 segments, or a one-layer kGradBf16Sum
+// table with its micro-batch lists.  Such a launch needs no table upload,
+// no cache entry and no event recording when the cache may reuse the copy;
+// on MI355X that event alone cost about 3 us of GPU time per launch of
+// back-to-back steps.
+constexpr size_t kInlineTableBytes = 2048;
+struct InlineTable {
+    uint64_t w[kInlineTableBytes / 8];
+};
+
 // ------------------------------------------------ int8 rows with scales
 //
 // The int8 kernels give each row to a team of 2^team_log2 lanes of one
@@ -141,18 +153,20 @@ struct AdamwConsts {
     float b1, omb1, b2, omb2, eps, decay, step_size, inv_bc2_root;
 };
 
-// Kernel launches (asynchronous on `stream`).  `table` is the device copy of
-// the launch table; one workgroup runs per tile 0 .. total_tiles-1.
+// Kernel launches (asynchronous on `stream`).  The launch table is `table`,
+// a device copy, when that is not null, else `*inl`, copied into the kernel
+// arguments; one workgroup runs per tile 0 .. total_tiles-1.
 // `nmb` is the micro-batch count of kGradBf16Sum (ignored otherwise).
 // `lds_bytes` of LDS are reserved per workgroup of the AdamW kernel, which
 // itself uses none: the reservation caps how many of its workgroups share a
 // CU.
-hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles,
-                        GradMode grad_mode, bool with_delta, const AdamwConsts &c,
-                        hipStream_t stream, int nmb, uint32_t lds_bytes);
-hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles,
-                        bool overwrite, hipStream_t stream);
-hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream);
+hipError_t launch_adamw(const void *table, const InlineTable *inl, int nseg,
+                        uint32_t total_tiles, GradMode grad_mode, bool with_delta,
+                        const AdamwConsts &c, hipStream_t stream, int nmb, uint32_t lds_bytes);
+hipError_t launch_accum(const void *table, const InlineTable *inl, int nseg,
+                        uint32_t total_tiles, bool overwrite, hipStream_t stream);
+hipError_t launch_merge(const void *table, const InlineTable *inl, int nseg,
+                        uint32_t total_tiles, hipStream_t stream);
 
 // int8 kernels; `block` (kQBlock or kQBlockWide) is the workgroup size the
 // table's records were sized for, `rows` the kernel family of all its records

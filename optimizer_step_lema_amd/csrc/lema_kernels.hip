@@ -49,7 +49,7 @@ using namespace dev;
 template <GradMode kMode, bool kDelta, int kNmb>
 struct AdamwTile {
     AdamwConsts c;
-    const char *table;   // the launch table (micro-batch pointer lists live there)
+    ktable_t table;      // the launch table (micro-batch pointer lists live there)
 
     __device__ __forceinline__ void operator()(const SegRec &r, uint32_t local_tile) const {
         const uint64_t master = r.p[0], m = r.p[1], v = r.p[2], grad = r.p[3];
@@ -76,8 +76,8 @@ struct AdamwTile {
     }
 
     // The K micro-batch pointers of a kGradBf16Sum segment.
-    __device__ __forceinline__ const uint64_t *microbatches(uint64_t list_offset) const {
-        return reinterpret_cast<const uint64_t *>(table + list_offset);
+    __device__ __forceinline__ const LEMA_CONST uint64_t *microbatches(uint64_t list_offset) const {
+        return (const LEMA_CONST uint64_t *)(table + list_offset);
     }
 
     // The gradient of this lane's 4 elements of the tile whose first vector
@@ -93,7 +93,7 @@ struct AdamwTile {
         } else if constexpr (kMode == kGradBf16Sum) {
             // every micro-batch's loads first, then the fp32 sum in micro-batch
             // order, the first one widened exactly (lema_grad_accum's overwrite)
-            const uint64_t *mb = microbatches(grad);
+            const LEMA_CONST uint64_t *mb = microbatches(grad);
             u32x2 gb[kNmb];
 #pragma unroll
             for (int k = 0; k < kNmb; ++k) gb[k] = tile_ld<u32x2>(tile_rsrc<u32x2>(mb[k], q0, kBlock), lane);
@@ -180,7 +180,7 @@ struct AdamwTile {
                 else if constexpr (kMode == kGradF32)
                     g = as_global<gfloat>(grad)[e];
                 else if constexpr (kMode == kGradBf16Sum) {
-                    const uint64_t *mb = microbatches(grad);
+                    const LEMA_CONST uint64_t *mb = microbatches(grad);
                     g = bf16_one(as_global<gu16>(mb[0])[e]);
                     for (int j = 1; j < kNmb; ++j)
                         g = accum_elem(g, bf16_one(as_global<gu16>(mb[j])[e]), false);
@@ -202,9 +202,10 @@ struct AdamwTile {
 
 template <GradMode kMode, bool kDelta, int kNmb = 0>
 __global__ __launch_bounds__(kBlock) void adamw_tile_kernel(const void *table, int nseg,
-                                                            uint32_t tile0, AdamwConsts c) {
-    block_of_table<SegRec>(table, nseg, tile0,
-                           AdamwTile<kMode, kDelta, kNmb>{c, static_cast<const char *>(table)});
+                                                            uint32_t tile0, AdamwConsts c,
+                                                            InlineTable inl) {
+    const ktable_t t = launch_table(table, inl);
+    block_of_table<SegRec>(t, nseg, tile0, AdamwTile<kMode, kDelta, kNmb>{c, t});
 }
 
 template <int kNmb>
@@ -271,8 +272,8 @@ struct AccumTile {
 
 template <bool kOverwrite>
 __global__ __launch_bounds__(kBlock) void accum_tile_kernel(const void *table, int nseg,
-                                                            uint32_t tile0) {
-    block_of_table<SegRec>(table, nseg, tile0, AccumTile<kOverwrite>{});
+                                                            uint32_t tile0, InlineTable inl) {
+    block_of_table<SegRec>(launch_table(table, inl), nseg, tile0, AccumTile<kOverwrite>{});
 }
 
 // ------------------------------------------------------------ merge delta
@@ -319,8 +320,8 @@ struct MergeTile {
 };
 
 __global__ __launch_bounds__(kBlock) void merge_tile_kernel(const void *table, int nseg,
-                                                            uint32_t tile0) {
-    block_of_table<SegRec>(table, nseg, tile0, MergeTile{});
+                                                            uint32_t tile0, InlineTable inl) {
+    block_of_table<SegRec>(launch_table(table, inl), nseg, tile0, MergeTile{});
 }
 
 // ------------------------------------------------- measurement aids
@@ -384,6 +385,9 @@ __global__ __launch_bounds__(kBlock) void fp32_probe_kernel(const float *__restr
 // Launches go through hipLaunchKernel, which returns the launch status
 // directly instead of through the thread's sticky last-error slot.  Grids
 // larger than max_blocks_per_launch are split into consecutive launches.
+// The tile kernels always take an InlineTable argument; launches on a
+// device table pass this unused one.
+const InlineTable kNoInlineTable = {};
 const void *adamw_kernel_fn(GradMode grad_mode, bool with_delta, int nmb) {
 #define LEMA_PICK(M) with_delta ? reinterpret_cast<const void *>(&adamw_tile_kernel<M, true>) \
                                 : reinterpret_cast<const void *>(&adamw_tile_kernel<M, false>)
@@ -399,15 +403,16 @@ const void *adamw_kernel_fn(GradMode grad_mode, bool with_delta, int nmb) {
 #undef LEMA_PICK
 }
 
-hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradMode grad_mode,
-                        bool with_delta, const AdamwConsts &c, hipStream_t stream, int nmb,
-                        uint32_t lds_bytes) {
+hipError_t launch_adamw(const void *table, const InlineTable *inl, int nseg,
+                        uint32_t total_tiles, GradMode grad_mode, bool with_delta,
+                        const AdamwConsts &c, hipStream_t stream, int nmb, uint32_t lds_bytes) {
     const void *fn = adamw_kernel_fn(grad_mode, with_delta, nmb);
-    if (fn == nullptr) return hipErrorInvalidValue;
+    if (fn == nullptr || (table == nullptr) == (inl == nullptr)) return hipErrorInvalidValue;
     AdamwConsts consts = c;
+    void *inl_arg = const_cast<InlineTable *>(inl ? inl : &kNoInlineTable);
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
         const uint32_t n = std::min<uint32_t>(total_tiles - tile0, max_blocks_per_launch(kBlock));
-        void *args[] = {&table, &nseg, &tile0, &consts};
+        void *args[] = {&table, &nseg, &tile0, &consts, inl_arg};
         hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, lds_bytes, stream);
         if (e != hipSuccess) return e;
         tile0 += n;
@@ -415,13 +420,15 @@ hipError_t launch_adamw(const void *table, int nseg, uint32_t total_tiles, GradM
     return hipSuccess;
 }
 
-hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles, bool overwrite,
-                        hipStream_t stream) {
+hipError_t launch_accum(const void *table, const InlineTable *inl, int nseg,
+                        uint32_t total_tiles, bool overwrite, hipStream_t stream) {
+    if ((table == nullptr) == (inl == nullptr)) return hipErrorInvalidValue;
     const void *fn = overwrite ? reinterpret_cast<const void *>(&accum_tile_kernel<true>)
                                : reinterpret_cast<const void *>(&accum_tile_kernel<false>);
+    void *inl_arg = const_cast<InlineTable *>(inl ? inl : &kNoInlineTable);
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
         const uint32_t n = std::min<uint32_t>(total_tiles - tile0, max_blocks_per_launch(kBlock));
-        void *args[] = {&table, &nseg, &tile0};
+        void *args[] = {&table, &nseg, &tile0, inl_arg};
         hipError_t e = hipLaunchKernel(fn, dim3(n), dim3(kBlock), args, 0, stream);
         if (e != hipSuccess) return e;
         tile0 += n;
@@ -429,10 +436,13 @@ hipError_t launch_accum(const void *table, int nseg, uint32_t total_tiles, bool 
     return hipSuccess;
 }
 
-hipError_t launch_merge(const void *table, int nseg, uint32_t total_tiles, hipStream_t stream) {
+hipError_t launch_merge(const void *table, const InlineTable *inl, int nseg,
+                        uint32_t total_tiles, hipStream_t stream) {
+    if ((table == nullptr) == (inl == nullptr)) return hipErrorInvalidValue;
+    void *inl_arg = const_cast<InlineTable *>(inl ? inl : &kNoInlineTable);
     for (uint32_t tile0 = 0; tile0 < total_tiles;) {
         const uint32_t n = std::min<uint32_t>(total_tiles - tile0, max_blocks_per_launch(kBlock));
-        void *args[] = {&table, &nseg, &tile0};
+        void *args[] = {&table, &nseg, &tile0, inl_arg};
         hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&merge_tile_kernel), dim3(n),
                                        dim3(kBlock), args, 0, stream);
         if (e != hipSuccess) return e;

@@ -163,7 +163,7 @@ extern "C" lema_status lema_adamw_step_noalloc(const lema_adamw_seg *segs, int32
         if (e != hipSuccess) return hip_failed(e);
     }
     const GradMode mode = args->grad_dtype == LEMA_GRAD_FP32 ? kGradF32 : kGradBf16;
-    e = launch_adamw(table, nrec, static_cast<uint32_t>(tiles), mode, with_delta,
+    e = launch_adamw(table, nullptr, nrec, static_cast<uint32_t>(tiles), mode, with_delta,
                      derive_consts(args), stream, 0, step_lds_bytes_for(mode, with_delta, 0, tiles));
     return e == hipSuccess ? LEMA_OK : hip_failed(e);
 }

@@ -569,14 +569,28 @@ def test_plans_match_direct_calls(L):
             assert _same(a.delta, b.delta)
 
 
+# Tables of more than 2048 bytes go through the device cache; smaller ones
+# travel in the kernel arguments.  The cache tests pad every call with
+# PAD_SEGS one-element segments of their own tensor so that each table is
+# large enough for the cache.
+PAD_SEGS = 25
+
+
+def _pad_segments(L, pad):
+    return [L.AdamwSegment(pad.master[k:k + 1], pad.exp_avg[k:k + 1], pad.exp_avg_sq[k:k + 1],
+                           pad.grad[k:k + 1], pad.weight[k:k + 1]) for k in range(PAD_SEGS)]
+
+
 def test_table_cache_many_lists_and_streams(L):
     """More distinct segment lists than cached tables, alternating two streams.
 
     Call j steps a prefix of segment j % 3 whose length shrinks with j, so
     nearly every call has a table of its own and the cache must evict."""
     s2 = torch.cuda.Stream()
-    base, snaps = build_segments(L, [3000, 70001, 2048], 61)
+    base, snaps = build_segments(L, [3000, 70001, 2048, PAD_SEGS], 61)
+    pad = _pad_segments(L, base[3])
     calls = []
+    before = L.table_cache_stats()
     for j in range(48):
         i = j % 3
         n = base[i].master.numel() - (j % 24)
@@ -590,11 +604,13 @@ def test_table_cache_many_lists_and_streams(L):
                                                  base[(i + 1) % 3].weight[:7])]
         if j % 2:
             s2.wait_stream(torch.cuda.current_stream())
-            L.adamw_step([seg] + extra, step=j + 1, stream=s2, **HP)
+            L.adamw_step([seg] + extra + pad, step=j + 1, stream=s2, **HP)
             torch.cuda.current_stream().wait_stream(s2)
         else:
-            L.adamw_step([seg] + extra, step=j + 1, **HP)
-        calls.append(([(i, n)] + ([((i + 1) % 3, 7)] if extra else []), j + 1))
+            L.adamw_step([seg] + extra + pad, step=j + 1, **HP)
+        calls.append(([(i, n)] + ([((i + 1) % 3, 7)] if extra else []) + [(3, PAD_SEGS)], j + 1))
+    after = L.table_cache_stats()
+    assert after["hits"] + after["uploads"] - before["hits"] - before["uploads"] == 48
     torch.cuda.synchronize()
     state = [{k: h[k].copy() for k in ("master", "m", "v", "grad")} for h in snaps]
     for w in state:
@@ -620,22 +636,97 @@ def test_table_cache_beyond_capacity(L):
     calls on prefixes of one tensor, each its own table, with no host wait in
     between, so that the cache both grows and, at its cap, reuses entries whose
     launches have finished.  Results follow the oracle's sequence of steps."""
-    base, snaps = build_segments(L, [4096], 62)
+    base, snaps = build_segments(L, [4096, PAD_SEGS], 62)
     b = base[0]
+    pad = _pad_segments(L, base[1])
     lengths = [4096 - j for j in range(600)]
+    before = L.table_cache_stats()
     for j, n in enumerate(lengths):
         seg = L.AdamwSegment(b.master[:n], b.exp_avg[:n], b.exp_avg_sq[:n], b.grad[:n],
                              b.weight[:n])
-        L.adamw_step([seg], step=j + 1, **HP)
+        L.adamw_step([seg] + pad, step=j + 1, **HP)
     torch.cuda.synchronize()
-    st = {k: snaps[0][k].copy() for k in ("master", "m", "v", "grad")}
+    after = L.table_cache_stats()
+    assert after["hits"] + after["uploads"] - before["hits"] - before["uploads"] == 600
+    assert after["entries"] <= 512
+    sts = [{k: h[k].copy() for k in ("master", "m", "v", "grad")} for h in snaps]
     for j, n in enumerate(lengths):
-        out = oracle_segment(st["master"][:n], st["m"][:n], st["v"][:n], st["grad"][:n],
-                             oracle_consts(HP, j + 1))
-        st["master"][:n], st["m"][:n], st["v"][:n] = out["master"], out["m"], out["v"]
-    compare_f32(to_np(b.master), st["master"], "cache cap master")
-    compare_f32(to_np(b.exp_avg), st["m"], "cache cap m")
-    compare_f32(to_np(b.exp_avg_sq), st["v"], "cache cap v")
+        for st, k in ((sts[0], n), (sts[1], PAD_SEGS)):
+            out = oracle_segment(st["master"][:k], st["m"][:k], st["v"][:k], st["grad"][:k],
+                                 oracle_consts(HP, j + 1))
+            st["master"][:k], st["m"][:k], st["v"][:k] = out["master"], out["m"], out["v"]
+    for t, st, tag in ((b, sts[0], "cache cap"), (base[1], sts[1], "cache cap pad")):
+        compare_f32(to_np(t.master), st["master"], tag + " master")
+        compare_f32(to_np(t.exp_avg), st["m"], tag + " m")
+        compare_f32(to_np(t.exp_avg_sq), st["v"], tag + " v")
+
+
+# The largest launch table carried in the kernel arguments is 2048 bytes:
+# 24 segment records (a 128-byte tile prefix and 24 x 80 bytes), or, for the
+# step over 8 resident micro-batches, 13 records with their pointer lists.
+@pytest.mark.parametrize("nseg", [24, 25])
+def test_tables_in_kernel_arguments_and_in_cache(L, nseg):
+    """The step, the accumulation and the merge on 24 segments (table in the
+    kernel arguments, cache untouched) and on 25 (table through the cache):
+    every element equals the oracle's either way."""
+    rng = np.random.default_rng(90 + nseg)
+    sizes = [int(x) for x in rng.choice([1, 17, 255, 256, 2048, 5000, 40001], size=nseg)]
+    segs, snaps = build_segments(L, sizes, 90 + nseg, delta=set(range(0, nseg, 2)))
+    accs = [_empty(n, torch.float32) for n in sizes]
+    g1 = [_bf16(n, 1e-3, 9100 + i) for i, n in enumerate(sizes)]
+    g2 = [_bf16(n, 1e-3, 9200 + i) for i, n in enumerate(sizes)]
+    bases = [_bf16(n, 0.02, 9300 + i) for i, n in enumerate(sizes)]
+    deltas = [_f32(n, 1e-4, 9400 + i) for i, n in enumerate(sizes)]
+    merged = [_empty(n, torch.bfloat16) for n in sizes]
+    torch.cuda.synchronize()
+    before = L.table_cache_stats()
+    L.adamw_step(segs, step=9, **HP)
+    L.grad_accum([L.AccumSegment(a, g) for a, g in zip(accs, g1)], overwrite=True)
+    L.grad_accum([L.AccumSegment(a, g) for a, g in zip(accs, g2)], overwrite=False)
+    L.merge_delta([L.MergeSegment(b, d, o) for b, d, o in zip(bases, deltas, merged)])
+    torch.cuda.synchronize()
+    after = L.table_cache_stats()
+    cached = after["hits"] + after["uploads"] - before["hits"] - before["uploads"]
+    assert cached == (0 if nseg <= 24 else 4), (before, after)
+    check_segments(segs, snaps, oracle_consts(HP, 9), f"n{nseg}.")
+    for i, n in enumerate(sizes):
+        acc = np.empty(n, np.float32)
+        oracle.grad_accum(acc, to_np(g1[i]), overwrite=True)
+        oracle.grad_accum(acc, to_np(g2[i]), overwrite=False)
+        compare_f32(to_np(accs[i]), acc, f"n{nseg}.accum{i}")
+        compare_bf16(to_np(merged[i]), oracle.merge_delta(to_np(bases[i]), to_np(deltas[i])),
+                     f"n{nseg}.merge{i}")
+
+
+@pytest.mark.parametrize("nseg", [13, 14])
+def test_microbatch_tables_in_kernel_arguments_and_in_cache(L, nseg):
+    """8 resident micro-batches: 13 segments fit the kernel arguments with
+    their pointer lists, 14 go through the cache; both equal accumulate-then-
+    step on every element."""
+    nmb = 8
+    rng = np.random.default_rng(110 + nseg)
+    sizes = [int(x) for x in rng.choice([1, 255, 256, 4099, 30000], size=nseg)]
+    segs, snaps = build_segments(L, sizes, 110 + nseg, delta=set(range(1, nseg, 2)))
+    mbs = [[_bf16(n, 1e-3, 11000 + 100 * i + k) for k in range(nmb)] for i, n in enumerate(sizes)]
+    for seg in segs:
+        seg.grad = None
+    torch.cuda.synchronize()
+    before = L.table_cache_stats()
+    L.adamw_step(segs, step=4, microbatch_grads=mbs, **HP)
+    torch.cuda.synchronize()
+    after = L.table_cache_stats()
+    cached = after["hits"] + after["uploads"] - before["hits"] - before["uploads"]
+    assert cached == (0 if nseg <= 13 else 1), (before, after)
+    c = oracle_consts(HP, 4)
+    for i, (seg, h, gs) in enumerate(zip(segs, snaps, mbs)):
+        ref = _accumulate_then_step(h, [to_np(g) for g in gs], c, h["orig"])
+        tag = f"mb.n{nseg}.seg{i}"
+        compare_f32(to_np(seg.master), ref["master"], tag + ".master")
+        compare_f32(to_np(seg.exp_avg), ref["m"], tag + ".m")
+        compare_f32(to_np(seg.exp_avg_sq), ref["v"], tag + ".v")
+        compare_bf16(to_np(seg.weight), ref["weight"], tag + ".weight")
+        if seg.delta is not None:
+            compare_f32(to_np(seg.delta), ref["delta"], tag + ".delta")
 
 
 def _accumulate_then_step(snap, grads_np, consts, orig=None):
