@@ -698,6 +698,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     int32_t backs_enqueued = 0;     // layers whose write-backs are enqueued
     bool abort = false;
     lema_status out_status = LEMA_OK;
+    int32_t out_hip = 0;            // the write-back thread's HIP error, if it failed
     double h2d_bytes = 0, d2h_bytes = 0, in_ms = 0, out_ms = 0;
 
     auto fail = [&](lema_status s2) {
@@ -707,6 +708,10 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
     };
 
     auto outbound_work = [&] {
+        // HIP's current device is per thread: this one starts on device 0
+        lema_status s2 = LEMA_OK;
+        hipError_t err = hipSetDevice(pool->device);
+        if (err != hipSuccess) s2 = hip_failed(err);
         CopyWorkers workers(threads_out);
         struct Pending { hipEvent_t done; char *chunk; const Piece *piece; };
         std::deque<Pending> fifo;          // enqueued pieces not yet copied out, oldest first
@@ -728,7 +733,6 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
             out_ms += std::chrono::duration<double, std::milli>(clock::now() - t0).count();
             return LEMA_OK;
         };
-        lema_status s2 = LEMA_OK;
         for (int32_t j = 0; j < nlayers && s2 == LEMA_OK; ++j) {
             {
                 // the step of layer j enqueued, and on a single copy stream also
@@ -738,7 +742,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
                 cv.wait(lk, [&] { return abort || steps_enqueued >= need; });
                 if (abort) break;
             }
-            hipError_t err = hipStreamWaitEvent(d2h_stream, ev(j, EV_K_END), 0);
+            err = hipStreamWaitEvent(d2h_stream, ev(j, EV_K_END), 0);
             if (err == hipSuccess) err = hipEventRecord(ev(j, EV_D2H_BEGIN), d2h_stream);
             if (err != hipSuccess) { s2 = hip_failed(err); break; }
             char *slot = slot_of(j);
@@ -782,6 +786,7 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
             std::lock_guard<std::mutex> lk(m);
             abort = true;
             out_status = s2;
+            out_hip = lema_last_hip_error();   // this thread's; handed to the caller's below
         }
         cv.notify_all();
     };
@@ -868,7 +873,10 @@ lema_status run_staged(lema_slot_pool *pool, const std::vector<LayerPlan> &plans
         cv.notify_all();
     }
     outbound.join();
-    if (st == LEMA_OK) st = out_status;
+    if (st == LEMA_OK && out_status != LEMA_OK) {
+        st = out_status;
+        if (st == LEMA_ERR_HIP) hip_failed(static_cast<hipError_t>(out_hip));
+    }
     if (st != LEMA_OK) return drain(pool, st);
     e = hipEventSynchronize(ev(nlayers - 1, EV_D2H_END));
     if (e != hipSuccess) return drain(pool, hip_failed(e));

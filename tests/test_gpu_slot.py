@@ -7,6 +7,8 @@ copy and compute streams from the host must not change a single bit.
 """
 from __future__ import annotations
 
+import threading
+
 import numpy as np
 import pytest
 import torch
@@ -284,22 +286,44 @@ def test_injected_copy_failure_then_recovery(L, monkeypatch, staged, fail_at):
     pool.close()
 
 
+def _in_fresh_thread(fn):
+    """Runs fn on a new thread (whose last-HIP-error slot starts at 0) and
+    returns the exception it raised, or None."""
+    out = {}
+
+    def run():
+        try:
+            fn()
+        except BaseException as ex:    # handed to the test thread
+            out["e"] = ex
+
+    t = threading.Thread(target=run)
+    t.start()
+    t.join()
+    return out.get("e")
+
+
+HIP_ERROR_UNKNOWN = 999     # what the injected copy failure returns
+
+
 @pytest.mark.parametrize("duplex,fail_at", [(False, 40), (False, 125), (True, 60), (True, 130)])
 def test_staged_failure_mid_stream_then_recovery(L, monkeypatch, duplex, fail_at):
     """A copy that fails while a staged call over real Llama-2-7B layers is
     well under way (each direction of a layer moves in 45 pieces, so both
     rings are full and completion groups are pending in both threads):
-    LEMA_ERR_HIP once the streams have drained, then the same pool streams
-    the layers again and every element matches the oracle."""
+    LEMA_ERR_HIP once the streams have drained, with the injected failure's
+    raw HIP code on the calling thread whichever of the call's threads hit
+    it, then the same pool streams the layers again and every element
+    matches the oracle."""
     from optimizer_step_lema_amd import _native as N
     w = synth.WORKLOADS["llama7b_layer"]
     sizes = w.numels
     layers, snaps = zip(*[pageable_layer(sizes, 170 + i) for i in range(3)])
     pool = L.SlotPool(layer_bytes(sizes), nslots=2, duplex=duplex)
     monkeypatch.setenv("LEMA_FAULT_INJECT", f"copy:{fail_at}")
-    with pytest.raises(N.LemaError) as e:
-        pool.stream(layers, step=10, staged=True, **HP)
-    assert e.value.status == N.LEMA_ERR_HIP and e.value.hip_error != 0
+    err = _in_fresh_thread(lambda: pool.stream(layers, step=10, staged=True, **HP))
+    assert isinstance(err, N.LemaError), err
+    assert err.status == N.LEMA_ERR_HIP and err.hip_error == HIP_ERROR_UNKNOWN
     monkeypatch.delenv("LEMA_FAULT_INJECT")
     layers2, snaps2 = zip(*[pageable_layer(sizes, 180 + i) for i in range(3)])
     pool.stream(layers2, step=10, staged=True, **HP)
