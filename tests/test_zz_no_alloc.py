@@ -128,3 +128,17 @@ def test_interleaved_with_cached_calls():
     torch.cuda.synchronize()
     _assert_same(a_ref, a_got)
     _assert_same(b_ref, b_got)
+
+
+def test_fp32_gradient_matches():
+    # an fp32 accumulator as the gradient (LEMA_GRAD_FP32), ragged sizes
+    sizes = [202 * 1024 + 3, 4096, 17]
+    ref, got = _state(sizes, 2400)
+    for i, n in enumerate(sizes):
+        g = synth.normal(n, 1e-3, 2450 + i, "cuda")
+        ref[i].grad = g.clone()
+        got[i].grad = g.clone()
+    L.adamw_step(ref, step=9, **HP)
+    L.adamw_step_noalloc(got, step=9, **HP)
+    torch.cuda.synchronize()
+    _assert_same(ref, got)
