@@ -463,7 +463,10 @@ lema_status lema_slot_stream(lema_slot_pool *pool, const lema_layer *layers, int
  * the caller's memory and the rings, piece by piece, so that a layer's first
  * upload starts after one piece's host copy and a write-back's host copies
  * follow its DMA.  The calling thread enqueues the uploads and steps; a
- * second thread of the library enqueues the write-backs and copies them out.
+ * second thread of the library (on the pool's device) enqueues the
+ * write-backs and copies them out.  A HIP failure on either thread returns
+ * LEMA_ERR_HIP with its raw code in the calling thread's
+ * lema_last_hip_error().
  * On a single copy stream each layer's write-back is enqueued after the next
  * layer's uploads.  Blocks until every layer is written back.  In `stats`,
  * as for lema_slot_stream, copy times are per layer and direction (first
