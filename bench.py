@@ -97,6 +97,10 @@ def parse():
     ap.add_argument("--stagger", type=int, default=4096,
                     help="flat layout: the k-th array kind's buffer starts k * STAGGER bytes "
                          "into its allocation (a multiple of 256; 0 = no offsets)")
+    ap.add_argument("--state-sets", type=int, default=0,
+                    help="resident and int8 benches: rotate over N copies of the workload's "
+                         "state, one per timed launch in turn (0 = enough copies for 1 GiB of "
+                         "traffic per rotation, at least 1)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-gib", type=float, default=4.0, help="size of the copy-ceiling test")
@@ -291,6 +295,10 @@ def main():
     if a.slots < 2:
         print(f"bench.py: --slots {a.slots}: a slot pool needs at least 2 slots", file=sys.stderr)
         sys.exit(2)
+    if a.state_sets < 0:
+        print(f"bench.py: --state-sets {a.state_sets}: 0 (automatic) or a positive count is "
+              "needed", file=sys.stderr)
+        sys.exit(2)
 
     import torch
     import optimizer_step_lema_amd as L
@@ -334,7 +342,7 @@ def resident_bench(torch, L, synth, a):
 
     # state resident in HBM; small workloads get rotated copies so that the
     # working set exceeds the 256 MB last-level cache between launches
-    nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
+    nsets = a.state_sets or (max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1)
     t_setup = time.perf_counter()
     sets = [resident_state(torch, L, synth, w, a.layout, delta, grad_f32, resident_mb,
                            a.stagger)
@@ -666,7 +674,7 @@ def q8_bench(torch, L, synth, a):
                           for n, r in zip(w.numels, rows))
     per_step = step_bytes + accum_bytes
 
-    nsets = max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1
+    nsets = a.state_sets or (max(1, -(-(1 << 30) // per_step)) if per_step < (1 << 30) else 1)
     t_setup = time.perf_counter()
     sets = [q8_state(torch, L, synth, w, row_lens, a.layout, delta, a.stagger)
             for _ in range(nsets)]

@@ -466,35 +466,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(uint64_t array, const
         kRawBufferWord3);
 }
 
-// Vector v (elements 4v .. 4v+3) of a row's array.  The fp32 and bf16
-// arrays move nontemporal (gfx950 NT bit), like the global accesses of the
-// other int8 paths.  The one-byte code arrays are read with the default
-// policy, and written with it by the accumulation and conversion kernels;
-// the step writes its codes nontemporal.  Measured on MI355X (variant
-// builds, interleaved rounds on one box): code reads with the default
-// policy took the step over the Llama-2-7B attention projections from
-// 1.008-1.015 to 0.955-0.965 ms and eight int8 accumulations of one layer
-// from 1.064 to 1.013 ms, code writes with it the accumulations on to
-// 1.003-1.005 ms but the step alone to 1.026-1.037 ms; every array with
-// the default policy took the step to 1.094-1.099 ms.
+// Vector v (elements 4v .. 4v+3) of a row's array.  Accesses are
+// nontemporal (gfx950 NT bit), like the global accesses of the other int8
+// paths, except the reads of the one-byte code arrays in the separate
+// wave-row launches (the step's m and v codes, an int8 gradient, the
+// accumulator), which take the default policy.  Measured on MI355X with
+// variant builds, interleaved on one box, state rotated so that no code
+// array fits the last-level cache between its uses: the int8 step over the
+// Llama-2-7B attention projections went from 1.004-1.011 to 0.965-0.975 ms
+// (two boxes), eight int8 accumulations of one layer, each behind a 2 GiB
+// cache scrub, from 1.091 to 1.048-1.050 ms, the whole 7B step stayed at
+// 23.8-24.0 ms; in the mixed launch the rank-16 LoRA step lost 2% with it
+// (0.171-0.174 against 0.174-0.177 ms), and default-policy code writes or
+// fp32 reads gained nothing anywhere (every array on the default policy
+// took the attention step to 1.094-1.099 ms).
 constexpr int kRowPolicy = 2;
 constexpr int kCodeLoadPolicy = 0;
-constexpr int kStepCodeStorePolicy = kRowPolicy;
-constexpr int kRowsCodeStorePolicy = 0;
 
+template <int kPolicy>
 __device__ __forceinline__ uint32_t row_ld_codes(__amdgpu_buffer_rsrc_t r, uint32_t v) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, int(v * 4), 0, kCodeLoadPolicy);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, int(v * 4), 0, kPolicy);
 }
-template <int kPolicy = kRowPolicy>
 __device__ __forceinline__ u32x2 row_ld_bf16(__amdgpu_buffer_rsrc_t r, uint32_t v) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, int(v * 8), 0, kPolicy));
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, int(v * 8), 0, kRowPolicy));
 }
 __device__ __forceinline__ f32x4 row_ld_f32(__amdgpu_buffer_rsrc_t r, uint32_t v) {
     return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, int(v * 16), 0, kRowPolicy));
 }
-template <int kPolicy>
 __device__ __forceinline__ void row_st_codes(__amdgpu_buffer_rsrc_t r, uint32_t v, uint32_t w) {
-    __builtin_amdgcn_raw_buffer_store_b32(w, r, int(v * 4), 0, kPolicy);
+    __builtin_amdgcn_raw_buffer_store_b32(w, r, int(v * 4), 0, kRowPolicy);
 }
 __device__ __forceinline__ void row_st_bf16(__amdgpu_buffer_rsrc_t r, uint32_t v, f32x4 x) {
     const u32x2_t b = {to_bf16_pair(x.x, x.y), to_bf16_pair(x.z, x.w)};
@@ -757,12 +757,9 @@ struct AdamwRows {
     __device__ __forceinline__ void wave_rows(const Q8Rec &r, uint32_t local_block) const {
         constexpr int kMomBytes = kMomQ8 ? 1 : 4;
         constexpr int kGradBytes = kGrad == kQGradBf16 ? 2 : kGrad == kQGradF32 ? 4 : 1;
-        // bf16 reads of the mixed launch's wave rows take the default policy:
-        // on MI355X the rank-16 LoRA step went from 0.174-0.178 to
-        // 0.169-0.171 ms with it, while the separate wave-row launches lost
-        // (the attention step 0.954-0.956 -> 0.970-0.978 ms, eight
-        // accumulations of one layer 1.005 -> 1.19 ms)
-        constexpr int kBf16Policy = kRows == kQRowsMixed ? 0 : kRowPolicy;
+        // code reads: the default policy in the separate wave-row launches,
+        // nontemporal in the mixed one (see row_ld_codes)
+        constexpr int kCodePolicy = kRows == kQRowsMixed ? kRowPolicy : kCodeLoadPolicy;
         const WaveRow wr = wave_row_of<kThreads>(r, local_block);
         const bool has_delta = kDelta && r.p[9] != 0;
         const auto r_master = row_rsrc<4>(r.p[0], wr);
@@ -804,8 +801,8 @@ struct AdamwRows {
 #pragma unroll
             for (int g = 0; g < kG; ++g) {
                 if (4 * g + (j >> 4) >= wr.chunks) continue;
-                const u32x4_t qm = __builtin_amdgcn_raw_buffer_load_b128(r_m, wide_off(g), 0, kCodeLoadPolicy);
-                const u32x4_t qv = __builtin_amdgcn_raw_buffer_load_b128(r_v, wide_off(g), 0, kCodeLoadPolicy);
+                const u32x4_t qm = __builtin_amdgcn_raw_buffer_load_b128(r_m, wide_off(g), 0, kCodePolicy);
+                const u32x4_t qv = __builtin_amdgcn_raw_buffer_load_b128(r_v, wide_off(g), 0, kCodePolicy);
                 *reinterpret_cast<u32x4_t *>(stage + g * 256 + 4 * j) = qm;
                 *reinterpret_cast<u32x4_t *>(stage + (kStageGroups + g) * 256 + 4 * j) = qv;
             }
@@ -824,17 +821,17 @@ struct AdamwRows {
             in[ci].w = row_ld_f32(r_master, v);
             if constexpr (kMomQ8) {
                 if (!wide) {
-                    in[ci].mc = row_ld_codes(r_m, v);
-                    in[ci].vc = row_ld_codes(r_v, v);
+                    in[ci].mc = row_ld_codes<kCodePolicy>(r_m, v);
+                    in[ci].vc = row_ld_codes<kCodePolicy>(r_v, v);
                 }
             } else {
                 in[ci].mf = row_ld_f32(r_m, v);
                 in[ci].vf = row_ld_f32(r_v, v);
             }
-            if constexpr (kGrad == kQGradBf16) in[ci].gb = row_ld_bf16<kBf16Policy>(r_g, v);
+            if constexpr (kGrad == kQGradBf16) in[ci].gb = row_ld_bf16(r_g, v);
             if constexpr (kGrad == kQGradF32) in[ci].g4 = row_ld_f32(r_g, v);
-            if constexpr (kGrad == kQGradQ8) in[ci].gc = row_ld_codes(r_g, v);
-            if (has_delta) in[ci].o2 = row_ld_bf16<kBf16Policy>(r_o, v);
+            if constexpr (kGrad == kQGradQ8) in[ci].gc = row_ld_codes<kCodePolicy>(r_g, v);
+            if (has_delta) in[ci].o2 = row_ld_bf16(r_o, v);
         }
 
         f32x4 mf[kCW], vf[kCW];
@@ -880,16 +877,16 @@ struct AdamwRows {
                 const u32x4_t qm4 = *reinterpret_cast<const u32x4_t *>(stage + g * 256 + 4 * j);
                 const u32x4_t qv4 =
                     *reinterpret_cast<const u32x4_t *>(stage + (kStageGroups + g) * 256 + 4 * j);
-                __builtin_amdgcn_raw_buffer_store_b128(qm4, r_m, wide_off(g), 0, kStepCodeStorePolicy);
-                __builtin_amdgcn_raw_buffer_store_b128(qv4, r_v, wide_off(g), 0, kStepCodeStorePolicy);
+                __builtin_amdgcn_raw_buffer_store_b128(qm4, r_m, wide_off(g), 0, kRowPolicy);
+                __builtin_amdgcn_raw_buffer_store_b128(qv4, r_v, wide_off(g), 0, kRowPolicy);
             }
         } else {
 #pragma unroll
             for (int ci = 0; ci < kCW; ++ci) {
                 if (ci >= wr.chunks) continue;
                 const uint32_t v = uint32_t(ci * wr.width + wr.lane);
-                row_st_codes<kStepCodeStorePolicy>(r_m, v, cm[ci]);
-                row_st_codes<kStepCodeStorePolicy>(r_v, v, cv[ci]);
+                row_st_codes(r_m, v, cm[ci]);
+                row_st_codes(r_v, v, cv[ci]);
             }
         }
         if (wr.lane == 0) {
@@ -1107,7 +1104,7 @@ struct CodeRows {
         for (int ci = 0; ci < kC; ++ci) {
             if (ci >= wr.chunks) continue;
             const uint32_t v = uint32_t(ci * wr.width + wr.lane);
-            if constexpr (kReadsCodes) cw[ci] = row_ld_codes(rc, v);
+            if constexpr (kReadsCodes) cw[ci] = row_ld_codes<kCodeLoadPolicy>(rc, v);
             if constexpr (kAccum) gb[ci] = row_ld_bf16(rs, v);
             if constexpr (kOp == kQuantize) x[ci] = row_ld_f32(rs, v);
         }
@@ -1133,7 +1130,7 @@ struct CodeRows {
 #pragma unroll
         for (int ci = 0; ci < kC; ++ci) {
             if (ci >= wr.chunks) continue;
-            row_st_codes<kRowsCodeStorePolicy>(rc, uint32_t(ci * wr.width + wr.lane), w[ci]);
+            row_st_codes(rc, uint32_t(ci * wr.width + wr.lane), w[ci]);
         }
         if (wr.lane == 0) as_global<gfloat>(scale)[wr.row] = q.s;
     }

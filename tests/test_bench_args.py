@@ -1,5 +1,5 @@
 """bench.py's argument checks, which run before anything touches a GPU:
-one GPU only, and the layout and slot-pool options."""
+one GPU only, and the layout, rotation and slot-pool options."""
 import os
 import subprocess
 import sys
@@ -20,6 +20,7 @@ def bench(*args):
     (["--stagger", "100"], "--stagger 100"),
     (["--stagger", "-256"], "--stagger -256"),
     (["--slot-stream", "--slots", "1"], "--slots 1"),
+    (["--state-sets", "-1"], "--state-sets -1"),
 ])
 def test_refused_before_any_gpu_work(args, needle):
     r = bench(*args)
@@ -31,5 +32,6 @@ def test_refused_before_any_gpu_work(args, needle):
 def test_help_lists_the_workloads_and_options():
     r = bench("--help")
     assert r.returncode == 0
-    for word in ("--workload", "--stagger", "--slots", "--q8", "--slot-stream", "--merge"):
+    for word in ("--workload", "--stagger", "--slots", "--state-sets", "--q8", "--slot-stream",
+                 "--merge"):
         assert word in r.stdout
