@@ -97,8 +97,29 @@ bool any_conflict(Span *begin, Span *end) {
     return false;
 }
 
+// A training loop hands the same arrays to every step, and sorting a few
+// thousand spans costs more host time than a small step's kernel (448 LoRA
+// tensors: about 4,500 spans, 180 us to sort on a 2.7 GHz Xeon).  So each
+// thread keeps the last span list found free of conflicts, in the order it
+// was given; an identical list, compared field by field, has the same
+// answer without the sort.  A list with a conflict is never kept.
+static bool same_spans(const std::vector<Span> &a, const std::vector<Span> &b) {
+    if (a.size() != b.size()) return false;
+    for (size_t i = 0; i < a.size(); ++i)
+        if (a[i].lo != b[i].lo || a[i].hi != b[i].hi || a[i].written != b[i].written)
+            return false;
+    return true;
+}
+
 bool any_conflict(std::vector<Span> &spans) {
-    return any_conflict(spans.data(), spans.data() + spans.size());
+    constexpr size_t kRememberFrom = 64;   // below this the sort is cheaper than the copy
+    if (spans.size() < kRememberFrom) return any_conflict(spans.data(), spans.data() + spans.size());
+    thread_local std::vector<Span> last_clear;
+    if (same_spans(spans, last_clear)) return false;
+    std::vector<Span> given(spans);
+    if (any_conflict(spans.data(), spans.data() + spans.size())) return true;
+    last_clear.swap(given);
+    return false;
 }
 
 template <class Spans>

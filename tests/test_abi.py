@@ -153,6 +153,27 @@ def test_overlap_errors(lib):
     del b2
 
 
+def test_overlap_check_of_repeated_long_lists(lib):
+    """Long span lists (here 40 segments, 280 spans) are checked once per
+    thread and then recognized when repeated: a repeat of a clean list passes,
+    any change is checked again, and a list with a conflict is rejected every
+    time, also right after its clean twin."""
+    clean = [fake_seg((1 << 32) + i * (1 << 28), 1000, delta=True) for i in range(40)]
+    for _ in range(3):
+        assert call(lib, clean) != N.LEMA_ERR_OVERLAP
+    bad = [fake_seg((1 << 32) + i * (1 << 28), 1000, delta=True) for i in range(40)]
+    bad[17].exp_avg = bad[3].master + 4 * 500          # m of one tensor inside another's master
+    for _ in range(2):
+        assert call(lib, bad) == N.LEMA_ERR_OVERLAP
+    assert call(lib, clean) != N.LEMA_ERR_OVERLAP
+    assert call(lib, bad) == N.LEMA_ERR_OVERLAP
+    # same addresses, one length longer: the tensor now runs into the next array
+    longer = [fake_seg((1 << 32) + i * (1 << 28), 1000, delta=True) for i in range(40)]
+    longer[5].numel = (1 << 24) // 4 + 1
+    assert call(lib, longer) == N.LEMA_ERR_OVERLAP
+    assert call(lib, clean) != N.LEMA_ERR_OVERLAP
+
+
 def test_empty_calls_are_noops_without_gpu(lib):
     assert lib.lema_adamw_step(None, 0, ctypes.byref(args()), None) == N.LEMA_OK
     z = fake_seg(1 << 32, 0)
